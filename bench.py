@@ -1,0 +1,231 @@
+"""Benchmark of the gated delta rule hot path on one MI355X.
+
+One step = one pass of the whole path over one batch of synthetic input:
+  * gdn_chunk_fwd on the prefill workload (B=4, H=16, T=4096, d_k=d_v=128,
+    bf16 q/k/v, fp32 state, chunk 64): gate, intra-chunk WY, state scan and
+    output kernels, final state written;
+  * gdn_decode_step on the decode workload (B=256, H=32, d=128, one bf16 token
+    per sequence, fp32 state updated in place; the state comes from a
+    512-token chunked forward over the seeded warm-up tokens).
+
+Timing: W untimed warm-up steps, then exactly K steps bracketed by
+torch.cuda.synchronize(); each call is bracketed by HIP events on the stream
+it runs on.  Before each call a 512 MiB scratch write evicts the 256 MB
+last-level cache (outside the events), so inputs come from HBM.
+
+Prints ONE JSON line.  ``value`` is chunked-forward tokens/s (prefill tokens
+per second of gdn_chunk_fwd); decode steps/s ride along in ``decode``.
+``roofline`` is for the decode kernel, the dominant kernel of the step (one
+kernel per call, so its event time is its launch duration); ``chunk_roofline``
+gives the chunked forward's fractions of the HBM and bf16 MFMA peaks.
+``cpu_baseline`` is the float64 oracle timed on this host's cores over the
+whole prefill batch.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import statistics
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK = 8.0e12            # bytes/s, MI355X HBM3E
+MFMA_BF16_PEAK = 2.5e15      # flop/s, dense bf16 MFMA
+
+# Algorithmic work (per unit = (sequence, value head); per token-unit):
+# q, k, v, o in bf16 (4 x 128 x 2 bytes) + alpha, beta fp32 (8 bytes).
+PREFILL_BYTES_PER_TOKEN_UNIT = 4 * 128 * 2 + 8
+# Chunked delta-rule operations per token and head, C = 64, r = d = 128:
+# 4 C r + 3 C d + 6 r d ("Attention as Matrix Algebra", section 8 and 9).
+PREFILL_FLOPS_PER_TOKEN_UNIT = 4 * 64 * 128 + 3 * 64 * 128 + 6 * 128 * 128
+# Decode per unit: state read + write (2 x 128 x 128 x 4 bytes), q k v o
+# (4 x 128 x 2 bytes), alpha, beta (8 bytes).
+DECODE_BYTES_PER_UNIT = 2 * 128 * 128 * 4 + 4 * 128 * 2 + 8
+DECODE_FLOPS_PER_UNIT = 6 * 128 * 128
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def to_dev(a, torch, dev):
+    import numpy as np
+    if a.dtype == np.uint16:
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(dev).view(torch.bfloat16)
+    return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+
+
+def cpu_baseline(w):
+    """The oracle as it stands, on this host's cores, over the whole prefill batch."""
+    import oracle
+    threads = oracle.cpu_threads()
+    t0 = time.perf_counter()
+    oracle.forward(w.q, w.k, w.v, w.alpha, w.beta, return_o=True, threads=threads)
+    dt = time.perf_counter() - t0
+    tokens = w.B * w.T
+    return {"value": tokens / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": f"whole prefill batch (B={w.B}, T={w.T}, H={w.spec.H_v}, d=128; "
+                      f"{tokens * w.spec.H_v} token-units) in {dt:.2f} s, float64"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-flush", action="store_true", help="keep caches warm between calls")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
+              "(the path shards by (sequence, head) with no exchange; see the design notes)",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import gated_delta_rule_03_amd as gdn
+    import gdn_inputs as gi
+
+    dev = torch.device("cuda:0")
+    gdn.load()
+
+    # ---------------- inputs, resident in HBM before timing ----------------
+    log("bench: generating prefill inputs")
+    wp = gi.generate(gi.config(2))
+    P = {n: to_dev(getattr(wp, n), torch, dev) for n in ("q", "k", "v", "alpha", "beta")}
+    B, T, H, D = wp.B, wp.T, wp.spec.H_v, wp.spec.d_k
+    o_p = torch.empty((B, T, H, D), dtype=torch.bfloat16, device=dev)
+    hT_p = torch.empty((B, H, D, D), dtype=torch.float32, device=dev)
+    need = gdn.chunk_fwd_workspace_bytes(B, T, H, H, D, D, gdn.GDN_BF16, 64, 0)
+    ws = torch.empty(need, dtype=torch.uint8, device=dev)
+
+    log("bench: decode state from a 512-token chunked forward over the seeded warm-up")
+    spec3 = gi.config(3)
+    warm = gi.generate(gi.decode_warmup_spec(spec3))
+    Wd = {n: to_dev(getattr(warm, n), torch, dev) for n in ("q", "k", "v", "alpha", "beta")}
+    _, state = gdn.chunk_fwd(Wd["q"], Wd["k"], Wd["v"], Wd["alpha"], Wd["beta"], chunk=64)
+    del Wd, warm
+    wd = gi.generate(spec3)
+    Dd = {n: to_dev(getattr(wd, n), torch, dev) for n in ("q", "k", "v", "alpha", "beta")}
+    o_d = torch.empty((spec3.B, 1, spec3.H_v, spec3.d_v), dtype=torch.bfloat16, device=dev)
+    torch.cuda.synchronize()
+
+    flush = None if args.no_flush else torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream()
+
+    def chunk_call():
+        gdn.chunk_fwd(P["q"], P["k"], P["v"], P["alpha"], P["beta"], chunk=64, o=o_p, hT=hT_p,
+                      workspace=ws, stream=stream)
+
+    def decode_call():
+        gdn.decode_step(Dd["q"], Dd["k"], Dd["v"], Dd["alpha"], Dd["beta"], state, o=o_d,
+                        stream=stream)
+
+    def step(record):
+        if flush is not None:
+            flush.fill_(1)
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        chunk_call()
+        e1.record(stream)
+        if flush is not None:
+            flush.fill_(2)
+        e2 = torch.cuda.Event(enable_timing=True)
+        e3 = torch.cuda.Event(enable_timing=True)
+        e2.record(stream)
+        decode_call()
+        e3.record(stream)
+        record.append((e0, e1, e2, e3))
+
+    log(f"bench: {args.warmup} warm-up steps")
+    rec = []
+    for _ in range(args.warmup):
+        step(rec)
+    torch.cuda.synchronize()
+    rec = []
+    log(f"bench: {args.steps} timed steps")
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step(rec)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    chunk_ms = [a.elapsed_time(b) for a, b, _, _ in rec]
+    dec_ms = [c.elapsed_time(d) for _, _, c, d in rec]
+    chunk_s = statistics.median(chunk_ms) * 1e-3
+    dec_s = statistics.median(dec_ms) * 1e-3
+    dec_mean_s = statistics.fmean(dec_ms) * 1e-3
+
+    tokens = B * T
+    units = B * H
+    prefill_bytes = tokens * H * PREFILL_BYTES_PER_TOKEN_UNIT + units * D * D * 4
+    prefill_flops = tokens * H * PREFILL_FLOPS_PER_TOKEN_UNIT
+    dec_units = spec3.B * spec3.H_v
+    dec_bytes = dec_units * DECODE_BYTES_PER_UNIT
+
+    result = {
+        "metric": "GDN chunked-fwd tokens/s (H=16,d=128,T=4096) + decode steps/s; % roofline",
+        "value": tokens / chunk_s,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": (chunk_s + dec_s) * 1e3,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": "chunked forward B=4 H=16 T=4096 d_k=d_v=128 bf16 chunk 64 "
+                        "+ decode step B=256 H=32 d=128 (fp32 state in place)",
+            "global_batch": B, "seq_len": T, "heads": H, "head_dim": D, "chunk": 64,
+            "decode_batch": spec3.B, "decode_heads": spec3.H_v,
+            "cache": "warm" if args.no_flush else "cold (512 MiB flush before each call)",
+        },
+        "decode": {
+            "steps_per_s": 1.0 / dec_s,
+            "tokens_per_s": spec3.B / dec_s,
+            "us_per_step": dec_s * 1e6,
+            "hbm_frac": dec_bytes / dec_s / HBM_PEAK,
+        },
+        "chunk_fwd": {
+            "us_per_call": chunk_s * 1e6,
+            "us_p10": float(np.percentile(chunk_ms, 10)) * 1e3,
+            "us_p90": float(np.percentile(chunk_ms, 90)) * 1e3,
+        },
+        "roofline": {
+            "kernel": "decode_kernel<bf16>",
+            "bound": "hbm",
+            "achieved": dec_bytes / dec_mean_s / 1e9,
+            "peak": HBM_PEAK / 1e9,
+            "unit": "GB/s",
+            "frac": dec_bytes / dec_mean_s / HBM_PEAK,
+            "traffic": None,
+        },
+        "chunk_roofline": {
+            "algorithmic_bytes": prefill_bytes,
+            "algorithmic_flops": prefill_flops,
+            "hbm_frac": prefill_bytes / chunk_s / HBM_PEAK,
+            "mfma_frac": prefill_flops / chunk_s / MFMA_BF16_PEAK,
+            "achieved_GBps": prefill_bytes / chunk_s / 1e9,
+            "achieved_TFLOPs": prefill_flops / chunk_s / 1e12,
+        },
+        "wall_s_timed_region": wall,
+    }
+    if not args.no_cpu_baseline:
+        log("bench: cpu baseline (float64 oracle on host cores)")
+        result["cpu_baseline"] = cpu_baseline(wp)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

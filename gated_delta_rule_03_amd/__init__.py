@@ -1,0 +1,234 @@
+"""Python binding of libgdn (the gated delta rule on MI355X).
+
+Thin ctypes marshalling over the C ABI declared in ``include/gdn.h``: it checks
+tensor devices, dtypes, shapes and contiguity, passes raw device pointers and
+the current HIP stream, and raises ``GDNError`` on a non-zero status.  Every
+step of the computation runs in the HIP kernels of ``libgdn.so``; there is no
+other implementation here and no fallback.  PyTorch only provides device
+memory and streams.
+
+Names follow the C ABI: ``recurrent_fwd``, ``chunk_fwd`` (with
+``chunk_fwd_workspace_bytes``) and ``decode_step``.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Tuple
+
+__all__ = [
+    "GDNError", "lib_path", "load", "version", "status_string", "recurrent_fwd",
+    "chunk_fwd", "chunk_fwd_workspace_bytes", "decode_step", "GDN_F32", "GDN_BF16",
+]
+
+GDN_SUCCESS = 0
+GDN_F32 = 0
+GDN_BF16 = 1
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_HERE, "libgdn.so")
+_lib: Optional[ctypes.CDLL] = None
+
+EXPORTS = ["gdn_version", "gdn_status_string", "gdn_recurrent_fwd",
+           "gdn_chunk_fwd_workspace_bytes", "gdn_chunk_fwd", "gdn_decode_step"]
+
+
+class GDNError(RuntimeError):
+    """A libgdn call returned a non-zero status."""
+
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {status_string(status)} (status {status})")
+
+
+def lib_path() -> str:
+    return _LIB_PATH
+
+
+def load() -> ctypes.CDLL:
+    """Load libgdn.so from the package directory.  Raises if it was not built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB_PATH):
+        raise RuntimeError(
+            f"libgdn.so not found at {_LIB_PATH}: build it with "
+            "`python -m gated_delta_rule_03_amd.build` (there is no fallback implementation)")
+    lib = ctypes.CDLL(_LIB_PATH)
+    i32, vp, fp = ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p
+    lib.gdn_version.argtypes = []
+    lib.gdn_version.restype = i32
+    lib.gdn_status_string.argtypes = [i32]
+    lib.gdn_status_string.restype = ctypes.c_char_p
+    fwd = [i32] * 7 + [vp, vp, vp, fp, fp, vp, i32, fp, vp, fp]
+    lib.gdn_recurrent_fwd.argtypes = fwd + [vp]
+    lib.gdn_recurrent_fwd.restype = i32
+    lib.gdn_chunk_fwd_workspace_bytes.argtypes = [i32] * 9
+    lib.gdn_chunk_fwd_workspace_bytes.restype = ctypes.c_size_t
+    lib.gdn_chunk_fwd.argtypes = fwd + [i32, vp, ctypes.c_size_t, vp]
+    lib.gdn_chunk_fwd.restype = i32
+    lib.gdn_decode_step.argtypes = [i32] * 6 + [vp, vp, vp, fp, fp, fp, vp, vp]
+    lib.gdn_decode_step.restype = i32
+    _lib = lib
+    return lib
+
+
+def version() -> int:
+    return int(load().gdn_version())
+
+
+def status_string(status: int) -> str:
+    return load().gdn_status_string(int(status)).decode()
+
+
+# ---------------------------------------------------------------------------
+# argument marshalling
+# ---------------------------------------------------------------------------
+
+def _torch():
+    import torch
+    return torch
+
+
+def _dtype_code(t) -> int:
+    torch = _torch()
+    if t.dtype == torch.bfloat16:
+        return GDN_BF16
+    if t.dtype == torch.float32:
+        return GDN_F32
+    raise TypeError(f"q/k/v must be bfloat16 or float32, got {t.dtype}")
+
+
+def _check(t, name, shape, dtype=None, device=None):
+    torch = _torch()
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} has dtype {t.dtype}, expected {dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _ptr(t) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def _stream(stream) -> Optional[int]:
+    torch = _torch()
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return s.cuda_stream
+
+
+def _fwd_args(q, k, v, alpha, beta, cu_seqlens, h0, o, hT, output_final_state):
+    torch = _torch()
+    if q.dim() != 4 or k.dim() != 4 or v.dim() != 4:
+        raise ValueError("q, k, v must be [B, T, H, d]")
+    B, T, H_qk, d_k = q.shape
+    H_v, d_v = v.shape[2], v.shape[3]
+    dev = q.device
+    _check(q, "q", (B, T, H_qk, d_k), device=dev)
+    _check(k, "k", (B, T, H_qk, d_k), q.dtype, dev)
+    _check(v, "v", (B, T, H_v, d_v), q.dtype, dev)
+    _check(alpha, "alpha", (B, T, H_v), torch.float32, dev)
+    _check(beta, "beta", (B, T, H_v), torch.float32, dev)
+    code = _dtype_code(q)
+    if cu_seqlens is not None:
+        if B != 1:
+            raise ValueError("a packed batch (cu_seqlens) needs B == 1")
+        _check(cu_seqlens, "cu_seqlens", (cu_seqlens.numel(),), torch.int32, dev)
+        n_seqs = cu_seqlens.numel() - 1
+        if n_seqs < 0:
+            raise ValueError("cu_seqlens needs at least one element")
+        N = n_seqs
+    else:
+        n_seqs = 0
+        N = B
+    if h0 is not None:
+        _check(h0, "h0", (N, H_v, d_k, d_v), torch.float32, dev)
+    if o is None:
+        o = torch.empty((B, T, H_v, d_v), dtype=q.dtype, device=dev)
+    else:
+        _check(o, "o", (B, T, H_v, d_v), q.dtype, dev)
+    if hT is None and output_final_state:
+        hT = torch.empty((N, H_v, d_k, d_v), dtype=torch.float32, device=dev)
+    elif hT is not None:
+        _check(hT, "hT", (N, H_v, d_k, d_v), torch.float32, dev)
+    dims = (B, T, H_qk, H_v, d_k, d_v, code)
+    return dims, n_seqs, o, hT
+
+
+def recurrent_fwd(q, k, v, alpha, beta, *, cu_seqlens=None, h0=None, o=None, hT=None,
+                  output_final_state: bool = True, stream=None) -> Tuple:
+    """Token-by-token gated delta rule.  Returns (o, hT)."""
+    dims, n_seqs, o, hT = _fwd_args(q, k, v, alpha, beta, cu_seqlens, h0, o, hT,
+                                    output_final_state)
+    st = load().gdn_recurrent_fwd(*dims, _ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(beta),
+                                  _ptr(cu_seqlens), n_seqs, _ptr(h0), _ptr(o), _ptr(hT),
+                                  _stream(stream))
+    if st != GDN_SUCCESS:
+        raise GDNError(st, "gdn_recurrent_fwd")
+    return o, hT
+
+
+def chunk_fwd_workspace_bytes(B, T, H_qk, H_v, d_k, d_v, dtype_code, chunk=64, n_seqs=0) -> int:
+    return int(load().gdn_chunk_fwd_workspace_bytes(B, T, H_qk, H_v, d_k, d_v, dtype_code, chunk,
+                                                    n_seqs))
+
+
+def chunk_fwd(q, k, v, alpha, beta, *, chunk: int = 64, cu_seqlens=None, h0=None, o=None,
+              hT=None, workspace=None, output_final_state: bool = True, stream=None) -> Tuple:
+    """Chunked gated delta rule (WY/UT form).  Returns (o, hT).
+
+    ``workspace``: an optional uint8 device tensor of at least
+    ``chunk_fwd_workspace_bytes(...)`` bytes; allocated per call when omitted.
+    """
+    torch = _torch()
+    dims, n_seqs, o, hT = _fwd_args(q, k, v, alpha, beta, cu_seqlens, h0, o, hT,
+                                    output_final_state)
+    need = chunk_fwd_workspace_bytes(*dims, chunk, n_seqs)
+    if need == 0:
+        raise GDNError(2, "gdn_chunk_fwd_workspace_bytes")
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    elif workspace.numel() * workspace.element_size() < need:
+        raise ValueError(f"workspace holds {workspace.numel() * workspace.element_size()} "
+                         f"bytes, {need} needed")
+    st = load().gdn_chunk_fwd(*dims, _ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(beta),
+                              _ptr(cu_seqlens), n_seqs, _ptr(h0), _ptr(o), _ptr(hT), chunk,
+                              _ptr(workspace), workspace.numel() * workspace.element_size(),
+                              _stream(stream))
+    if st != GDN_SUCCESS:
+        raise GDNError(st, "gdn_chunk_fwd")
+    return o, hT
+
+
+def decode_step(q, k, v, alpha, beta, state, *, o=None, stream=None):
+    """One token per sequence; ``state`` [B, H_v, d_k, d_v] is updated in place.  Returns o."""
+    torch = _torch()
+    if q.dim() != 4 or q.shape[1] != 1:
+        raise ValueError("q must be [B, 1, H_qk, d_k]")
+    B, _, H_qk, d_k = q.shape
+    H_v, d_v = v.shape[2], v.shape[3]
+    dev = q.device
+    _check(q, "q", (B, 1, H_qk, d_k), device=dev)
+    _check(k, "k", (B, 1, H_qk, d_k), q.dtype, dev)
+    _check(v, "v", (B, 1, H_v, d_v), q.dtype, dev)
+    _check(alpha, "alpha", (B, 1, H_v), torch.float32, dev)
+    _check(beta, "beta", (B, 1, H_v), torch.float32, dev)
+    _check(state, "state", (B, H_v, d_k, d_v), torch.float32, dev)
+    if o is None:
+        o = torch.empty((B, 1, H_v, d_v), dtype=q.dtype, device=dev)
+    else:
+        _check(o, "o", (B, 1, H_v, d_v), q.dtype, dev)
+    st = load().gdn_decode_step(B, H_qk, H_v, d_k, d_v, _dtype_code(q), _ptr(q), _ptr(k),
+                                _ptr(v), _ptr(alpha), _ptr(beta), _ptr(state), _ptr(o),
+                                _stream(stream))
+    if st != GDN_SUCCESS:
+        raise GDNError(st, "gdn_decode_step")
+    return o

@@ -1,0 +1,195 @@
+// libgdn C ABI: argument checks, workspace layout and launch order.
+// The operation and the contract of every entry point are in include/gdn.h.
+#include "../../include/gdn.h"
+
+#include <limits>
+
+#include "launch.hpp"
+
+namespace gdn {
+
+static int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+static size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+int64_t chunk_slots(const Problem &p) {
+  if (p.cu_seqlens) return ceil_div(p.T, p.chunk) + p.n_seqs;
+  return int64_t(p.B) * ceil_div(p.T, p.chunk);
+}
+
+SeqGeom make_geom(const Problem &p, const Workspace *ws) {
+  SeqGeom g;
+  g.cu_seqlens = p.cu_seqlens;
+  g.chunk_off = ws ? ws->chunk_off : nullptr;
+  g.n_seqs = p.n_seqs;
+  g.T = p.T;
+  g.chunk = p.chunk > 0 ? p.chunk : 64;
+  g.chunks_per_seq = int32_t(ceil_div(p.T, g.chunk));
+  g.n_slots = int32_t(std::min<int64_t>(chunk_slots(p), std::numeric_limits<int32_t>::max()));
+  return g;
+}
+
+size_t workspace_layout(const Problem &p, void *base, Workspace *ws) {
+  const size_t elem = p.dtype == GDN_BF16 ? 2 : 4;
+  const size_t g_bytes = align256(size_t(p.n_tokens()) * p.H_v * sizeof(float));
+  const size_t off_bytes = align256(size_t(p.n_seqs + 1) * sizeof(int32_t));
+  const size_t ent_bytes = align256(size_t(chunk_slots(p)) * p.H_v * kEntryElems * elem);
+  if (ws) {
+    char *b = static_cast<char *>(base);
+    ws->g = reinterpret_cast<float *>(b);
+    ws->chunk_off = reinterpret_cast<int32_t *>(b + g_bytes);
+    ws->entries = b + g_bytes + off_bytes;
+  }
+  return g_bytes + off_bytes + ent_bytes;
+}
+
+static bool dim_ok(int32_t d) { return d == 16 || d == 32 || d == 64 || d == 128; }
+
+// Shape and dtype checks.  Returns GDN_SUCCESS or the error status.
+static int32_t check_shapes(int32_t B, int32_t T, int32_t H_qk, int32_t H_v, int32_t d_k,
+                            int32_t d_v, int32_t dtype) {
+  if (B < 0 || T < 0 || H_qk <= 0 || H_v <= 0 || d_k <= 0 || d_v <= 0)
+    return GDN_ERROR_INVALID_VALUE;
+  if (dtype != GDN_F32 && dtype != GDN_BF16) return GDN_ERROR_NOT_SUPPORTED;
+  if (!dim_ok(d_k) || !dim_ok(d_v)) return GDN_ERROR_NOT_SUPPORTED;
+  if (H_v % H_qk != 0) return GDN_ERROR_NOT_SUPPORTED;
+  const int64_t tokens = int64_t(B) * T;
+  if (tokens * std::max<int64_t>(H_v, H_qk) * std::max(d_k, d_v) > (int64_t(1) << 40))
+    return GDN_ERROR_NOT_SUPPORTED;
+  return GDN_SUCCESS;
+}
+
+// Shape checks plus the tensor pointers every non-empty call needs.
+static int32_t check_common(int32_t B, int32_t T, int32_t H_qk, int32_t H_v, int32_t d_k,
+                            int32_t d_v, int32_t dtype, const void *q, const void *k,
+                            const void *v, const float *alpha, const float *beta, const void *o) {
+  const int32_t st = check_shapes(B, T, H_qk, H_v, d_k, d_v, dtype);
+  if (st != GDN_SUCCESS) return st;
+  if (int64_t(B) * T > 0 && (!q || !k || !v || !alpha || !beta || !o))
+    return GDN_ERROR_INVALID_VALUE;
+  return GDN_SUCCESS;
+}
+
+static int32_t make_problem(int32_t B, int32_t T, int32_t H_qk, int32_t H_v, int32_t d_k,
+                            int32_t d_v, int32_t dtype, const void *q, const void *k,
+                            const void *v, const float *alpha, const float *beta,
+                            const int32_t *cu_seqlens, int32_t n_seqs, const float *h0,
+                            void *o, float *hT, Problem *p) {
+  int32_t st = check_common(B, T, H_qk, H_v, d_k, d_v, dtype, q, k, v, alpha, beta, o);
+  if (st != GDN_SUCCESS) return st;
+  if (cu_seqlens) {
+    if (B != 1 || n_seqs < 0) return GDN_ERROR_INVALID_VALUE;
+  } else {
+    if (n_seqs != 0 && n_seqs != B) return GDN_ERROR_INVALID_VALUE;
+    n_seqs = B;
+  }
+  *p = Problem{B, T, H_qk, H_v, d_k, d_v, dtype, q, k, v, alpha, beta,
+               cu_seqlens, n_seqs, h0, o, hT, 0};
+  return GDN_SUCCESS;
+}
+
+static int32_t status_of(hipError_t e) { return e == hipSuccess ? GDN_SUCCESS : GDN_ERROR_LAUNCH; }
+
+}  // namespace gdn
+
+using namespace gdn;
+
+extern "C" {
+
+int32_t gdn_version(void) { return 100; }
+
+const char *gdn_status_string(int32_t status) {
+  switch (status) {
+    case GDN_SUCCESS: return "success";
+    case GDN_ERROR_INVALID_VALUE: return "invalid value (null pointer or inconsistent size)";
+    case GDN_ERROR_NOT_SUPPORTED: return "not supported (size or dtype outside the supported set)";
+    case GDN_ERROR_WORKSPACE: return "workspace missing or too small";
+    case GDN_ERROR_LAUNCH: return "kernel launch failed";
+    default: return "unknown status";
+  }
+}
+
+int32_t gdn_recurrent_fwd(int32_t B, int32_t T, int32_t H_qk, int32_t H_v, int32_t d_k,
+                          int32_t d_v, int32_t dtype, const void *q, const void *k, const void *v,
+                          const float *alpha, const float *beta, const int32_t *cu_seqlens,
+                          int32_t n_seqs, const float *h0, void *o, float *hT, void *stream) {
+  Problem p;
+  int32_t st = make_problem(B, T, H_qk, H_v, d_k, d_v, dtype, q, k, v, alpha, beta, cu_seqlens,
+                            n_seqs, h0, o, hT, &p);
+  if (st != GDN_SUCCESS) return st;
+  return status_of(launch_recurrent(p, static_cast<hipStream_t>(stream)));
+}
+
+size_t gdn_chunk_fwd_workspace_bytes(int32_t B, int32_t T, int32_t H_qk, int32_t H_v,
+                                     int32_t d_k, int32_t d_v, int32_t dtype, int32_t chunk,
+                                     int32_t n_seqs) {
+  if (check_shapes(B, T, H_qk, H_v, d_k, d_v, dtype) != GDN_SUCCESS) return 0;
+  if (chunk != 16 && chunk != 32 && chunk != 64) return 0;
+  if (n_seqs < 0) return 0;
+  Problem p{};
+  p.B = B;
+  p.T = T;
+  p.H_qk = H_qk;
+  p.H_v = H_v;
+  p.d_k = d_k;
+  p.d_v = d_v;
+  p.dtype = dtype;
+  // A packed batch (B == 1, n_seqs > 0) reserves ceil(T / chunk) + n_seqs
+  // chunk slots, which also covers a single uniform sequence.
+  const bool packed = B == 1 && n_seqs > 0;
+  p.n_seqs = packed ? n_seqs : B;
+  static const int32_t kLayoutOnly = 0;
+  p.cu_seqlens = packed ? &kLayoutOnly : nullptr;  // selects the packed layout; never read
+  p.chunk = chunk;
+  return workspace_layout(p, nullptr, nullptr);
+}
+
+int32_t gdn_chunk_fwd(int32_t B, int32_t T, int32_t H_qk, int32_t H_v, int32_t d_k, int32_t d_v,
+                      int32_t dtype, const void *q, const void *k, const void *v,
+                      const float *alpha, const float *beta, const int32_t *cu_seqlens,
+                      int32_t n_seqs, const float *h0, void *o, float *hT, int32_t chunk,
+                      void *workspace, size_t workspace_bytes, void *stream) {
+  Problem p;
+  int32_t st = make_problem(B, T, H_qk, H_v, d_k, d_v, dtype, q, k, v, alpha, beta, cu_seqlens,
+                            n_seqs, h0, o, hT, &p);
+  if (st != GDN_SUCCESS) return st;
+  if (chunk != 16 && chunk != 32 && chunk != 64) return GDN_ERROR_NOT_SUPPORTED;
+  p.chunk = chunk;
+  const size_t need = workspace_layout(p, nullptr, nullptr);
+  if (!workspace || workspace_bytes < need) return GDN_ERROR_WORKSPACE;
+  if (reinterpret_cast<uintptr_t>(workspace) & 255) return GDN_ERROR_WORKSPACE;
+  Workspace ws;
+  workspace_layout(p, workspace, &ws);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e = launch_chunk_offsets(p, ws, s);
+  if (e == hipSuccess) e = launch_gate(p, ws, s);
+  if (e == hipSuccess) e = launch_prep(p, ws, s);
+  if (e == hipSuccess) e = launch_scan(p, ws, s);
+  return status_of(e);
+}
+
+int32_t gdn_decode_step(int32_t B, int32_t H_qk, int32_t H_v, int32_t d_k, int32_t d_v,
+                        int32_t dtype, const void *q, const void *k, const void *v,
+                        const float *alpha, const float *beta, float *state, void *o,
+                        void *stream) {
+  int32_t st = check_common(B, 1, H_qk, H_v, d_k, d_v, dtype, q, k, v, alpha, beta, o);
+  if (st != GDN_SUCCESS) return st;
+  if (B > 0 && !state) return GDN_ERROR_INVALID_VALUE;
+  Problem p{};
+  p.B = B;
+  p.T = 1;
+  p.H_qk = H_qk;
+  p.H_v = H_v;
+  p.d_k = d_k;
+  p.d_v = d_v;
+  p.dtype = dtype;
+  p.q = q;
+  p.k = k;
+  p.v = v;
+  p.alpha = alpha;
+  p.beta = beta;
+  p.o = o;
+  p.n_seqs = B;
+  return status_of(launch_decode(p, state, static_cast<hipStream_t>(stream)));
+}
+
+}  // extern "C"

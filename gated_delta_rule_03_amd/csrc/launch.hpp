@@ -1,0 +1,49 @@
+// Internal launchers of the libgdn kernels (host side).  Not part of the ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "device.hpp"
+
+namespace gdn {
+
+struct Problem {
+  int32_t B, T, H_qk, H_v, d_k, d_v, dtype;
+  const void *q, *k, *v;
+  const float *alpha, *beta;
+  const int32_t *cu_seqlens;
+  int32_t n_seqs;  // sequences (B for a uniform batch)
+  const float *h0;
+  void *o;
+  float *hT;
+  int32_t chunk;
+  int64_t n_tokens() const { return int64_t(B) * T; }
+};
+
+// Chunk slots reserved for a problem: an upper bound on the number of chunks
+// for any packed layout with the same totals.
+int64_t chunk_slots(const Problem &p);
+
+// Fragments per (chunk, value head) workspace entry: T (8), P (8), Ktilde^T (16).
+constexpr int kFragsPerEntry = 32;
+constexpr int kFragElems = 64 * 8;
+constexpr int64_t kEntryElems = int64_t(kFragsPerEntry) * kFragElems;
+
+struct Workspace {
+  float *g;          // [n_tokens, H_v] chunk-local cumulative log2 alpha
+  int32_t *chunk_off;  // [n_seqs + 1] (packed batches)
+  void *entries;     // [chunk_slots, H_v, kEntryElems] in the operand type
+};
+size_t workspace_layout(const Problem &p, void *base, Workspace *ws);
+
+hipError_t launch_chunk_offsets(const Problem &p, const Workspace &ws, hipStream_t st);
+hipError_t launch_gate(const Problem &p, const Workspace &ws, hipStream_t st);
+hipError_t launch_prep(const Problem &p, const Workspace &ws, hipStream_t st);
+hipError_t launch_scan(const Problem &p, const Workspace &ws, hipStream_t st);
+hipError_t launch_recurrent(const Problem &p, hipStream_t st);
+hipError_t launch_decode(const Problem &p, float *state, hipStream_t st);
+
+SeqGeom make_geom(const Problem &p, const Workspace *ws);
+
+}  // namespace gdn

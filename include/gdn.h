@@ -1,0 +1,148 @@
+/*
+ * libgdn -- the gated delta rule on AMD Instinct MI355X (gfx950).
+ *
+ * The operation (per unit = one sequence and one value head, state S of
+ * d_k x d_v, S_0 = h0 or 0), once per token t:
+ *
+ *   S'  = alpha_t S_{t-1}                    decay
+ *   vhat = S'^T k_t                          predict from the decayed state
+ *   S_t = S' + beta_t k_t (v_t - vhat)^T     correct along the key
+ *   o_t = S_t^T q_t                          read after the write
+ *
+ * Source: "Linear attention" (arsalanzafar.ai), section "How it works",
+ * Eqs. (1)-(4); the same update, transposed, is "The gated delta rule" of
+ * "How linear attention works: a small memory matrix and the gated delta rule"
+ * (joelfernandes.org).  There is no score scale and no normaliser: callers
+ * pre-scale and L2-normalise q and k themselves.
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * Tensors are dense, row-major and contiguous; there are no stride arguments.
+ *   q, k     [B, T, H_qk, d_k]   element type `dtype`
+ *   v, o     [B, T, H_v,  d_v]   element type `dtype`
+ *   alpha, beta [B, T, H_v]      float32 (one scalar per token and value head)
+ *   h0, hT, state [N, H_v, d_k, d_v] float32, d_v fastest (the state is
+ *                                stored as keys x values)
+ * Value head j reads query/key head (j * H_qk) / H_v: H_v must be a multiple
+ * of H_qk and each query/key head serves H_v / H_qk consecutive value heads.
+ * Packed (variable-length) batches: pass `cu_seqlens` (device pointer, int32,
+ * n_seqs + 1 non-decreasing offsets with cu_seqlens[0] = 0 and
+ * cu_seqlens[n_seqs] = T) with B == 1; the state restarts at every boundary
+ * and N = n_seqs.  Otherwise pass NULL and N = B.
+ * Supported sizes: d_k, d_v in {16, 32, 64, 128}; dtype GDN_F32 or GDN_BF16.
+ * The state and all accumulation are float32; o is written in `dtype`.
+ *
+ * Ownership: every buffer is allocated by the caller and lives on the current
+ * HIP device (device pointers).  The library allocates nothing, frees nothing
+ * and keeps no pointer after a call returns.  Calls are asynchronous on the
+ * given stream (NULL = the default stream); results are ready when the caller
+ * synchronises that stream.  o must not alias any input.
+ *
+ * Errors: arguments are checked before anything is launched.  On an error
+ * nothing is launched and no output is touched; the status says why.  A
+ * failed launch returns GDN_ERROR_LAUNCH.  Execution faults surface at the
+ * caller's next synchronisation.  No call keeps global mutable state; calls
+ * on different streams with disjoint buffers may run concurrently.
+ * Results are bitwise reproducible run to run (no atomics).
+ */
+#ifndef GDN_H_
+#define GDN_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Status codes. */
+#define GDN_SUCCESS 0
+#define GDN_ERROR_INVALID_VALUE 1 /* a null pointer, a negative or inconsistent size */
+#define GDN_ERROR_NOT_SUPPORTED 2 /* a size or dtype outside the supported set */
+#define GDN_ERROR_WORKSPACE 3     /* workspace missing or smaller than required */
+#define GDN_ERROR_LAUNCH 4        /* the HIP runtime rejected a kernel launch */
+
+/* Element types of q, k, v and o. */
+#define GDN_F32 0
+#define GDN_BF16 1
+
+/* Library version: major * 10000 + minor * 100 + patch. */
+int32_t gdn_version(void);
+
+/* A static, human-readable description of a status code (never NULL). */
+const char *gdn_status_string(int32_t status);
+
+/*
+ * gdn_recurrent_fwd -- the recurrence token by token.
+ *
+ * Evaluates Eqs. (1)-(4) of "Linear attention" ("How it works") one token at
+ * a time with the state held in registers: the direct form whose cost
+ * "How linear attention works" (section "Why it is called linear attention")
+ * puts at O(d_v d_k) per token.
+ *
+ *   h0  nullable: initial state per (sequence, value head); NULL = zeros.
+ *   hT  nullable: receives the final state.
+ *   cu_seqlens, n_seqs: see "Packed batches" above (NULL and 0 otherwise).
+ * T == 0 (or an empty packed sequence) is allowed: hT receives h0 (or zeros).
+ */
+int32_t gdn_recurrent_fwd(int32_t B, int32_t T, int32_t H_qk, int32_t H_v, int32_t d_k,
+                          int32_t d_v, int32_t dtype, const void *q, const void *k, const void *v,
+                          const float *alpha, const float *beta, const int32_t *cu_seqlens,
+                          int32_t n_seqs, const float *h0, void *o, float *hT, void *stream);
+
+/*
+ * Bytes of device workspace gdn_chunk_fwd needs for these sizes (0 when the
+ * arguments are unsupported).  The bound holds for every cu_seqlens with the
+ * given T and n_seqs.
+ */
+size_t gdn_chunk_fwd_workspace_bytes(int32_t B, int32_t T, int32_t H_qk, int32_t H_v,
+                                     int32_t d_k, int32_t d_v, int32_t dtype, int32_t chunk,
+                                     int32_t n_seqs);
+
+/*
+ * gdn_chunk_fwd -- the same result, computed chunk by chunk.
+ *
+ * Tokens are grouped into chunks of `chunk` tokens (16, 32 or 64; a
+ * sequence's last chunk may be shorter and chunks never cross a sequence
+ * boundary).  Inside a chunk one triangular solve turns the values into
+ * pseudo-values and the rest is chunked linear attention; only the boundary
+ * state passes from chunk to chunk ("Attention as Matrix Algebra: From
+ * Softmax to the Delta Rule", section 8 "Training the delta rule in chunks";
+ * "From KV Cache to a State Matrix: Linear Attention and DeltaNet", section
+ * "Chunkwise training for DeltaNet"), with the decay gate of "Linear
+ * attention", Eq. (1), carried as chunk-local cumulative log gates.
+ *
+ * Arguments as gdn_recurrent_fwd, plus:
+ *   chunk       16, 32 or 64.
+ *   workspace   device memory of at least gdn_chunk_fwd_workspace_bytes(...)
+ *               bytes, 256-byte aligned; its contents on entry do not matter
+ *               and are undefined on return.  Concurrent calls need separate
+ *               workspaces.
+ */
+int32_t gdn_chunk_fwd(int32_t B, int32_t T, int32_t H_qk, int32_t H_v, int32_t d_k, int32_t d_v,
+                      int32_t dtype, const void *q, const void *k, const void *v,
+                      const float *alpha, const float *beta, const int32_t *cu_seqlens,
+                      int32_t n_seqs, const float *h0, void *o, float *hT, int32_t chunk,
+                      void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * gdn_decode_step -- one new token per sequence, state updated in place.
+ *
+ * The generation step of "Attention as Matrix Algebra" (section 9: about 6rd
+ * operations and rd numbers of state per step and head) for the gated rule:
+ * with S the stored state, a = S^T k, b = S^T q, vhat = alpha a,
+ * u = beta (v - vhat), o = alpha b + (q^T k) u and S <- alpha S + k u^T.
+ *
+ *   q, k   [B, 1, H_qk, d_k];  v, o [B, 1, H_v, d_v];  alpha, beta [B, 1, H_v]
+ *   state  [B, H_v, d_k, d_v] float32, read and overwritten in place.
+ */
+int32_t gdn_decode_step(int32_t B, int32_t H_qk, int32_t H_v, int32_t d_k, int32_t d_v,
+                        int32_t dtype, const void *q, const void *k, const void *v,
+                        const float *alpha, const float *beta, float *state, void *o,
+                        void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GDN_H_ */

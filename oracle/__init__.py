@@ -130,7 +130,7 @@ def qk_head(j: int, H_qk: int, H_v: int) -> int:
 
 
 def forward(q, k, v, alpha, beta, *, cu_seqlens=None, h0=None, delta: bool = True,
-            units: Optional[Iterable[Tuple[int, int]]] = None,
+            units: Optional[Iterable[Tuple[int, int]]] = None, return_o: bool = True,
             threads: Optional[int] = None, lib: Optional[ctypes.CDLL] = None):
     """Oracle forward over a batch laid out as the library receives it.
 
@@ -141,6 +141,7 @@ def forward(q, k, v, alpha, beta, *, cu_seqlens=None, h0=None, delta: bool = Tru
     With ``units`` None, returns (o [B, T, H_v, d_v], hT [N, H_v, d_k, d_v]) in
     float64.  With ``units`` a list of (sequence, value head) pairs, returns a
     dict mapping each pair to (o [L, d_v], hT [d_k, d_v]) for that unit only.
+    ``return_o=False`` skips gathering o (the full result is then (None, hT)).
     """
     B, T, H_qk, dk = q.shape
     H_v, dv = v.shape[2], v.shape[3]
@@ -154,7 +155,7 @@ def forward(q, k, v, alpha, beta, *, cu_seqlens=None, h0=None, delta: bool = Tru
     N = len(seqs)
     if units is None:
         want = {i: list(range(H_v)) for i in range(N)}
-        o_full = np.zeros((B, T, H_v, dv), dtype=np.float64)
+        o_full = np.zeros((B, T, H_v, dv), dtype=np.float64) if return_o else None
         hT_full = np.zeros((N, H_v, dk, dv), dtype=np.float64)
     else:
         want: Dict[int, list] = {}
@@ -174,7 +175,8 @@ def forward(q, k, v, alpha, beta, *, cu_seqlens=None, h0=None, delta: bool = Tru
                                   threads=threads, lib=lib)
         for n, j in enumerate(heads):
             if units is None:
-                o_full[b, s:e, j] = o_u[n]
+                if return_o:
+                    o_full[b, s:e, j] = o_u[n]
                 hT_full[i, j] = hT_u[n]
             else:
                 out[(i, j)] = (o_u[n], hT_u[n])

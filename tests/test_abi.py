@@ -1,0 +1,87 @@
+"""The C ABI without a GPU: the library loads, exports every declared entry
+point, and rejects bad arguments before launching anything."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import gated_delta_rule_03_amd as gdn
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def declared_functions():
+    text = open(os.path.join(ROOT, "include", "gdn.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(gdn_[a-z_]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(gdn.lib_path()):
+        pytest.fail("libgdn.so is not built (run __graft_entry__.build())")
+    return gdn.load()
+
+
+def test_exports_every_declared_symbol(lib):
+    names = declared_functions()
+    assert set(names) == set(gdn.EXPORTS)
+    raw = ctypes.CDLL(gdn.lib_path())
+    for n in names:
+        assert hasattr(raw, n), n
+
+
+def test_version_and_status_strings(lib):
+    assert gdn.version() >= 100
+    for code in range(5):
+        assert gdn.status_string(code)
+    assert "unknown" in gdn.status_string(99)
+
+
+def test_workspace_query(lib):
+    w = gdn.chunk_fwd_workspace_bytes(4, 4096, 16, 16, 128, 128, gdn.GDN_BF16, 64, 0)
+    entries = 4 * 64 * 16 * 32 * 512 * 2
+    assert w >= entries + 4 * 4096 * 16 * 4
+    packed = gdn.chunk_fwd_workspace_bytes(1, 1000, 2, 4, 128, 128, gdn.GDN_BF16, 64, 5)
+    assert packed >= (16 + 5) * 4 * 32 * 512 * 2
+    assert gdn.chunk_fwd_workspace_bytes(1, 64, 1, 1, 48, 64, gdn.GDN_BF16, 64, 0) == 0
+    assert gdn.chunk_fwd_workspace_bytes(1, 64, 1, 1, 64, 64, gdn.GDN_BF16, 48, 0) == 0
+    assert gdn.chunk_fwd_workspace_bytes(1, 64, 1, 1, 64, 64, 7, 64, 0) == 0
+
+
+def fwd(lib, fn, B=1, T=8, H_qk=1, H_v=1, d_k=64, d_v=64, dtype=0, ptrs=True, cu=None, n=0,
+        extra=()):
+    p = ctypes.c_void_p(0x1000) if ptrs else None
+    args = [B, T, H_qk, H_v, d_k, d_v, dtype, p, p, p, p, p, cu, n, None, p, None]
+    return getattr(lib, fn)(*args, *extra)
+
+
+@pytest.mark.parametrize("fn,extra", [("gdn_recurrent_fwd", (None,)),
+                                      ("gdn_chunk_fwd", (64, None, 0, None))])
+def test_argument_errors_are_reported_before_launch(lib, fn, extra):
+    # every case below fails validation, so no kernel is launched
+    assert fwd(lib, fn, d_k=48, extra=extra) == 2
+    assert fwd(lib, fn, d_v=256, extra=extra) == 2
+    assert fwd(lib, fn, dtype=5, extra=extra) == 2
+    assert fwd(lib, fn, H_qk=3, H_v=4, extra=extra) == 2
+    assert fwd(lib, fn, B=-1, extra=extra) == 1
+    assert fwd(lib, fn, ptrs=False, extra=extra) == 1
+    assert fwd(lib, fn, B=2, cu=ctypes.c_void_p(0x1000), n=2, extra=extra) == 1
+    assert fwd(lib, fn, B=2, n=3, extra=extra) == 1
+
+
+def test_chunk_workspace_errors(lib):
+    p = ctypes.c_void_p(0x1000)
+    args = [1, 8, 1, 1, 64, 64, 0, p, p, p, p, p, None, 0, None, p, None]
+    assert lib.gdn_chunk_fwd(*args, 48, p, 1 << 30, None) == 2   # unsupported chunk
+    assert lib.gdn_chunk_fwd(*args, 64, None, 1 << 30, None) == 3  # no workspace
+    assert lib.gdn_chunk_fwd(*args, 64, p, 16, None) == 3          # too small
+    assert lib.gdn_chunk_fwd(*args, 64, ctypes.c_void_p(0x1001), 1 << 30, None) == 3  # misaligned
+
+
+def test_decode_argument_errors(lib):
+    p = ctypes.c_void_p(0x1000)
+    assert lib.gdn_decode_step(1, 1, 1, 48, 64, 0, p, p, p, p, p, p, p, None) == 2
+    assert lib.gdn_decode_step(1, 1, 1, 64, 64, 0, p, p, p, p, p, None, p, None) == 1
+    assert lib.gdn_decode_step(1, 2, 3, 64, 64, 0, p, p, p, p, p, p, p, None) == 2
