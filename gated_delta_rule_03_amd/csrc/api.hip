@@ -12,6 +12,7 @@ static int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 static size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
 int64_t chunk_slots(const Problem &p) {
+  if (p.chunk <= 0) return 0;  // the token-by-token path has no chunks
   if (p.cu_seqlens) return ceil_div(p.T, p.chunk) + p.n_seqs;
   return int64_t(p.B) * ceil_div(p.T, p.chunk);
 }

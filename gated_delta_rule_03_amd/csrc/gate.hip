@@ -44,28 +44,30 @@ __global__ __launch_bounds__(256) void chunk_offsets_kernel(SeqGeom geo, int32_t
   }
 }
 
-// One block per chunk slot; thread h walks the chunk's tokens for value head h.
-// Consecutive threads read consecutive heads of one token (coalesced).
+// One block per chunk slot; thread h owns value head h of the chunk.  All of
+// the chunk's alpha loads are issued before the prefix sum, and consecutive
+// threads touch consecutive heads of one token (coalesced).
+__device__ __forceinline__ float clamped_log2(float a) {
+  // log2 alpha, clamped below; alpha = 0 hits the floor, NaN and negative
+  // gates propagate as NaN.
+  if (a > 0.0f) return fmaxf(log2f(a), kLog2Floor);
+  if (a == 0.0f) return kLog2Floor;
+  return __builtin_nanf("");
+}
+
 __global__ __launch_bounds__(256) void gate_kernel(const float *__restrict__ alpha,
                                                    float *__restrict__ g, int H, SeqGeom geo) {
   int s, tok0, len;
   if (!geo.locate(blockIdx.x, s, tok0, len)) return;
   for (int h = threadIdx.x; h < H; h += blockDim.x) {
+    float l[64];
+#pragma unroll
+    for (int t = 0; t < 64; ++t) l[t] = t < len ? alpha[int64_t(tok0 + t) * H + h] : 1.0f;
     float acc = 0.0f;
-    for (int t = 0; t < len; ++t) {
-      const int64_t idx = int64_t(tok0 + t) * H + h;
-      const float a = alpha[idx];
-      // log2 alpha, clamped below; alpha = 0 hits the floor, NaN and negative
-      // gates propagate as NaN.
-      float l;
-      if (a > 0.0f)
-        l = fmaxf(log2f(a), kLog2Floor);
-      else if (a == 0.0f)
-        l = kLog2Floor;
-      else
-        l = __builtin_nanf("");
-      acc += l;
-      g[idx] = acc;
+#pragma unroll
+    for (int t = 0; t < 64; ++t) {
+      acc += clamped_log2(l[t]);
+      if (t < len) g[int64_t(tok0 + t) * H + h] = acc;
     }
   }
 }

@@ -15,14 +15,18 @@
 // This kernel computes everything that does not depend on the incoming state:
 // T, P and Ktilde^T for one (chunk, value head).  It writes them to the
 // workspace in MFMA fragment order, ready for the sequential state scan.
-// A chunk is padded to 64 token slots; padded slots have k = q = 0, beta = 0
-// and the chunk's last gate, so they contribute nothing.
+// A chunk is padded to 64 token slots.  Padded slots carry beta = 0 and the
+// chunk's last gate; their k and q rows (zero, or a copy of the chunk's last
+// row when staged) only ever meet exact zeros: rows and columns of A and T
+// vanish with beta, Ktilde^T columns are written as zeros, and P rows of
+// padded tokens only reach outputs that are never stored.
 //
 // MFMA: k k^T and k q^T are dense 64 x 64 x d_k contractions (bf16 MFMA for
 // bf16 inputs, fp32 MFMA for fp32 inputs).  The triangular inverse is fp32:
 // four 16 x 16 diagonal blocks by forward substitution (one lane per column),
 // then block forward substitution for the off-diagonal blocks.
 #include "launch.hpp"
+#include "stage.hpp"
 
 namespace gdn {
 
@@ -35,31 +39,54 @@ struct PrepArgs {
   SeqGeom geo;
 };
 
-template <typename T>
+// kStaged (bf16, d_k = 128): the chunk's k and q rows are first copied into
+// swizzled LDS row tiles with every load in flight at once, and all fragment
+// reads come from LDS.  Otherwise fragments are read from global memory.
+template <typename T, bool kStaged>
 __global__ __launch_bounds__(256) void prep_kernel(PrepArgs<T> a) {
   const int c = blockIdx.x;
   const int h = blockIdx.y;
   int s, tok0, len;
   if (!a.geo.locate(c, s, tok0, len)) return;
   const int hq = h / a.group;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
 
   __shared__ float sg[64], sb[64];
   __shared__ float sA[64][65];
   __shared__ float sM[64][65];
   __shared__ float sY[3][16][17];
+  __shared__ __attribute__((aligned(16))) bf16_t sK[kStaged ? 64 * 128 : 1];
+  __shared__ __attribute__((aligned(16))) bf16_t sQ[kStaged ? 64 * 128 : 1];
 
+  const int64_t stride = int64_t(a.H_qk) * a.d_k;
+  const T *kb = a.k + int64_t(tok0) * stride + int64_t(hq) * a.d_k;
+  const T *qb = a.q + int64_t(tok0) * stride + int64_t(hq) * a.d_k;
+  if constexpr (kStaged) {
+    // 16 one-KiB pieces per tile; each wave issues 4 of each.
+    stage_rowtile(sK, kb, stride, len, lane, 4 * wave, 4);
+    stage_rowtile(sQ, qb, stride, len, lane, 4 * wave, 4);
+  }
   if (tid < 64) {
     const int t = tid < len ? tid : len - 1;
     const int64_t idx = int64_t(tok0 + t) * a.H_v + h;
     sg[tid] = a.g[idx];
     sb[tid] = tid < len ? a.beta[idx] : 0.0f;
   }
+  if constexpr (kStaged) wait_vmem();
   __syncthreads();
 
-  const int64_t stride = int64_t(a.H_qk) * a.d_k;
-  const T *kb = a.k + int64_t(tok0) * stride + int64_t(hq) * a.d_k;
-  const T *qb = a.q + int64_t(tok0) * stride + int64_t(hq) * a.d_k;
+  // Row fragment of k (src 0) or q (src 1): rows 16 r + (lane & 15),
+  // contraction block kk.  Staged rows past the chunk repeat its last row;
+  // those rows and columns meet beta = 0 or are never stored.
+  auto frag = [&](int src, int r, int kk) -> Frag<T> {
+    if constexpr (kStaged) {
+      return rowtile_frag(src == 0 ? sK : sQ, r, kk, lane);
+    } else {
+      return load_row_frag(src == 0 ? kb : qb, stride, 16 * r + (lane & 15), len, 32 * kk,
+                           a.d_k, lane);
+    }
+  };
   T *entry = a.entries + (int64_t(c) * a.H_v + h) * kEntryElems;
   T *fragT = entry;
   T *fragP = entry + 8 * kFragElems;
@@ -77,12 +104,7 @@ __global__ __launch_bounds__(256) void prep_kernel(PrepArgs<T> a) {
       if (isA) { r = rr; cc = idx; } else { r = idx; cc = rr; }
     }
     f32x4_t acc = zero4();
-    const T *bsrc = isA ? kb : qb;
-    for (int kk = 0; kk < nkb; ++kk) {
-      Frag<T> fa = load_row_frag(kb, stride, 16 * r + (lane & 15), len, 32 * kk, a.d_k, lane);
-      Frag<T> fb = load_row_frag(bsrc, stride, 16 * cc + (lane & 15), len, 32 * kk, a.d_k, lane);
-      acc = mfma(fa, fb, acc);
-    }
+    for (int kk = 0; kk < nkb; ++kk) acc = mfma(frag(0, r, kk), frag(isA ? 0 : 1, cc, kk), acc);
     const int col = 16 * cc + (lane & 15);
     if (isA) {
       // rows t, column i: A_ti for i < t
@@ -173,14 +195,19 @@ __global__ __launch_bounds__(256) void prep_kernel(PrepArgs<T> a) {
     for (int j = 0; j < 8; ++j) {
       const int i = 32 * kk + kappa(lane, j);
       float x = 0.0f;
-      if (i < len && m < a.d_k) x = exp2f(g_last - sg[i]) * to_f32(kb[int64_t(i) * stride + m]);
+      if (i < len && m < a.d_k) {
+        float kv;
+        if constexpr (kStaged) kv = to_f32(sK[rowtile_off(i, m)]);
+        else kv = to_f32(kb[int64_t(i) * stride + m]);
+        x = exp2f(g_last - sg[i]) * kv;
+      }
       fr.set(j, x);
     }
     store_frag(fragK + f * kFragElems, lane, fr);
   }
 }
 
-template <typename T>
+template <typename T, bool kStaged>
 static hipError_t launch_prep_t(const Problem &p, const Workspace &ws, hipStream_t st) {
   PrepArgs<T> a;
   a.q = static_cast<const T *>(p.q);
@@ -194,13 +221,17 @@ static hipError_t launch_prep_t(const Problem &p, const Workspace &ws, hipStream
   a.group = p.H_v / p.H_qk;
   a.geo = make_geom(p, &ws);
   const int64_t slots = chunk_slots(p);
-  hipLaunchKernelGGL(prep_kernel<T>, dim3(unsigned(slots), unsigned(p.H_v)), dim3(256), 0, st, a);
+  hipLaunchKernelGGL((prep_kernel<T, kStaged>), dim3(unsigned(slots), unsigned(p.H_v)), dim3(256),
+                     0, st, a);
   return hipGetLastError();
 }
 
 hipError_t launch_prep(const Problem &p, const Workspace &ws, hipStream_t st) {
   if (chunk_slots(p) == 0) return hipSuccess;
-  return p.dtype == 1 ? launch_prep_t<bf16_t>(p, ws, st) : launch_prep_t<float>(p, ws, st);
+  if (p.dtype == 1)
+    return p.d_k == 128 ? launch_prep_t<bf16_t, true>(p, ws, st)
+                        : launch_prep_t<bf16_t, false>(p, ws, st);
+  return launch_prep_t<float, false>(p, ws, st);
 }
 
 }  // namespace gdn

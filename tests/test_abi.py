@@ -85,3 +85,24 @@ def test_decode_argument_errors(lib):
     assert lib.gdn_decode_step(1, 1, 1, 48, 64, 0, p, p, p, p, p, p, p, None) == 2
     assert lib.gdn_decode_step(1, 1, 1, 64, 64, 0, p, p, p, p, p, None, p, None) == 1
     assert lib.gdn_decode_step(1, 2, 3, 64, 64, 0, p, p, p, p, p, p, p, None) == 2
+
+
+def _gpu_visible():
+    try:
+        import torch
+        return torch.cuda.is_available()
+    except Exception:
+        return False
+
+
+@pytest.mark.skipif(_gpu_visible(), reason="drives launches with placeholder pointers: CPU-only hosts")
+def test_host_path_reaches_launch_without_gpu(lib):
+    """Valid arguments run the host-side geometry and launch sequencing; with no
+    GPU present the launch fails and is reported as GDN_ERROR_LAUNCH (4).
+    Regression: the token-by-token path once divided by its (zero) chunk size."""
+    p = ctypes.c_void_p(0x1000)
+    base = [1, 8, 1, 1, 64, 64, 0, p, p, p, p, p, None, 0, None, p, None]
+    assert lib.gdn_recurrent_fwd(*base, None) == 4
+    ws = ctypes.c_void_p(0x100000)
+    assert lib.gdn_chunk_fwd(*base, 64, ws, 1 << 30, None) == 4
+    assert lib.gdn_decode_step(2, 1, 1, 64, 64, 1, p, p, p, p, p, p, p, None) == 4
