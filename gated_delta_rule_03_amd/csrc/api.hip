@@ -30,17 +30,15 @@ SeqGeom make_geom(const Problem &p, const Workspace *ws) {
 }
 
 size_t workspace_layout(const Problem &p, void *base, Workspace *ws) {
-  const size_t elem = p.dtype == GDN_BF16 ? 2 : 4;
-  const size_t g_bytes = align256(size_t(p.n_tokens()) * p.H_v * sizeof(float));
+  const int64_t entry = p.dtype == GDN_BF16 ? entry_bytes<uint16_t>() : entry_bytes<float>();
   const size_t off_bytes = align256(size_t(p.n_seqs + 1) * sizeof(int32_t));
-  const size_t ent_bytes = align256(size_t(chunk_slots(p)) * p.H_v * kEntryElems * elem);
+  const size_t ent_bytes = align256(size_t(chunk_slots(p)) * p.H_v * size_t(entry));
   if (ws) {
     char *b = static_cast<char *>(base);
-    ws->g = reinterpret_cast<float *>(b);
-    ws->chunk_off = reinterpret_cast<int32_t *>(b + g_bytes);
-    ws->entries = b + g_bytes + off_bytes;
+    ws->chunk_off = reinterpret_cast<int32_t *>(b);
+    ws->entries = b + off_bytes;
   }
-  return g_bytes + off_bytes + ent_bytes;
+  return off_bytes + ent_bytes;
 }
 
 static bool dim_ok(int32_t d) { return d == 16 || d == 32 || d == 64 || d == 128; }
@@ -162,7 +160,6 @@ int32_t gdn_chunk_fwd(int32_t B, int32_t T, int32_t H_qk, int32_t H_v, int32_t d
   workspace_layout(p, workspace, &ws);
   hipStream_t s = static_cast<hipStream_t>(stream);
   hipError_t e = launch_chunk_offsets(p, ws, s);
-  if (e == hipSuccess) e = launch_gate(p, ws, s);
   if (e == hipSuccess) e = launch_prep(p, ws, s);
   if (e == hipSuccess) e = launch_scan(p, ws, s);
   return status_of(e);

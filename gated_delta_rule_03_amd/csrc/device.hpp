@@ -19,6 +19,19 @@ typedef uint16_t bf16_t;
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 
+// log2 alpha, clamped below at kLog2Floor; alpha = 0 hits the floor, NaN and
+// negative gates propagate as NaN.
+__device__ __forceinline__ float clamped_log2(float a) {
+  if (a > 0.0f) return fmaxf(log2f(a), kLog2Floor);
+  if (a == 0.0f) return kLog2Floor;
+  return __builtin_nanf("");
+}
+
+// 2^x with the hardware v_exp_f32 (about 1 ulp; results below the normal
+// range flush to zero).  The chunk kernels only take 2^x of non-positive
+// log-gate differences, where a flushed tiny factor is as good as exact.
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
 __device__ __forceinline__ float to_f32(float x) { return x; }
 __device__ __forceinline__ float to_f32(bf16_t x) { return __uint_as_float(uint32_t(x) << 16); }
 

@@ -25,20 +25,22 @@ struct Problem {
 // for any packed layout with the same totals.
 int64_t chunk_slots(const Problem &p);
 
-// Fragments per (chunk, value head) workspace entry: T (8), P (8), Ktilde^T (16).
-constexpr int kFragsPerEntry = 32;
+// One workspace entry per (chunk slot, value head): the intra-chunk factors
+// in MFMA fragment order -- T (8 fragments), P (8 fragments) of 64 lanes x 8
+// elements of the operand type -- followed by the chunk's 64 cumulative log2
+// gates (fp32).
 constexpr int kFragElems = 64 * 8;
-constexpr int64_t kEntryElems = int64_t(kFragsPerEntry) * kFragElems;
+template <typename T> constexpr int64_t entry_bytes() {
+  return int64_t(16) * kFragElems * sizeof(T) + 64 * sizeof(float);
+}
 
 struct Workspace {
-  float *g;          // [n_tokens, H_v] chunk-local cumulative log2 alpha
-  int32_t *chunk_off;  // [n_seqs + 1] (packed batches)
-  void *entries;     // [chunk_slots, H_v, kEntryElems] in the operand type
+  int32_t *chunk_off;  // [n_seqs + 1] chunk prefix sums (packed batches)
+  void *entries;       // [chunk_slots, H_v] entries
 };
 size_t workspace_layout(const Problem &p, void *base, Workspace *ws);
 
 hipError_t launch_chunk_offsets(const Problem &p, const Workspace &ws, hipStream_t st);
-hipError_t launch_gate(const Problem &p, const Workspace &ws, hipStream_t st);
 hipError_t launch_prep(const Problem &p, const Workspace &ws, hipStream_t st);
 hipError_t launch_scan(const Problem &p, const Workspace &ws, hipStream_t st);
 hipError_t launch_recurrent(const Problem &p, hipStream_t st);

@@ -2,25 +2,25 @@
 //
 // Only the boundary state passes from one chunk to the next ("From KV Cache
 // to a State Matrix", section "Chunkwise training for DeltaNet"; "Attention
-// as Matrix Algebra", section 5.1 and section 8).  For each chunk, from the
-// state S at its start and the intra-chunk factors T, P, Ktilde^T:
+// as Matrix Algebra", sections 5.1 and 8).  For each chunk, from the state S
+// at its start, the intra-chunk factors T and P and the chunk-local gates g
+// (gamma_t = 2^g_t, s_t = 2^(g_C - g_t)):
 //
 //   Y = K S                      (d_k contraction)
 //   U = T (V - diag(gamma) Y)    pseudo-values
 //   O = diag(gamma) (Q S) + P U  the chunk's outputs
-//   S <- gamma_C S + Ktilde^T U
+//   S <- gamma_C S + K^T (diag(s) U)
 //
-// One wavefront owns 16 columns of the state (a d_k x 16 slice, fp32, in
-// MFMA accumulator registers) for one (sequence, value head) and walks that
+// A wavefront owns 16 columns of the state (a d_k x 16 slice, fp32, in MFMA
+// accumulator registers) for one (sequence, value head) and walks that
 // sequence's chunks in order.  The delta-rule update acts on each value
 // column separately ("Attention as Matrix Algebra", section 7.2: each write
-// moves a column along the key only), so the column slices are independent.
-// The accumulator layout of two stacked 16 x 16 tiles is the B-fragment
-// layout, so Y, U and S feed the next product from registers.
+// moves a column along the key only), so column slices are independent.  The
+// accumulator layout of two stacked 16 x 16 tiles is the B-fragment layout,
+// so Y, U and S feed the next product from registers.
 //
-// Launch: one 64-lane block per (unit, 16-column block).  Blocks of one unit
-// are numbered so that they share blockIdx mod 8, i.e. they land on the same
-// XCD and share its L2 for K, Q, T, P and Ktilde^T.
+// Blocks of one unit are numbered so that they share blockIdx mod 8: they land
+// on the same XCD and share its L2 for the chunk's k, q, T and P.
 #include "launch.hpp"
 #include "stage.hpp"
 
@@ -29,8 +29,7 @@ namespace gdn {
 template <typename T>
 struct ScanArgs {
   const T *q, *k, *v;
-  const float *g;
-  const T *entries;
+  const char *entries;
   const float *h0;
   T *o;
   float *hT;
@@ -38,31 +37,38 @@ struct ScanArgs {
   SeqGeom geo;
 };
 
+// XCD-aware block decode: unit u's column blocks share bid % 8.
+__device__ __forceinline__ void decode_block(int bid, int n_colblk, int &u, int &cb) {
+  const int per_group = 8 * n_colblk;
+  const int grp = bid / per_group, rem = bid - grp * per_group;
+  cb = rem >> 3;
+  u = grp * 8 + (rem & 7);
+}
+
+// ---------------------------------------------------------------------------
+// General path: any supported d_k / d_v, fp32 or bf16.  One 64-lane block per
+// (unit, 16 columns); operands are read from global memory as needed.
+// ---------------------------------------------------------------------------
 template <typename T>
 __global__ __launch_bounds__(64) void scan_kernel(ScanArgs<T> a) {
   const int lane = threadIdx.x;
-  // XCD-aware decode: unit u's column blocks share bid % 8.
-  const int per_group = 8 * a.n_colblk;
-  const int bid = blockIdx.x;
-  const int grp = bid / per_group, rem = bid - grp * per_group;
-  const int cb = rem >> 3, u = grp * 8 + (rem & 7);
+  int u, cb;
+  decode_block(blockIdx.x, a.n_colblk, u, cb);
   if (u >= a.n_units) return;
   const int s = u / a.H_v, h = u - s * a.H_v, hq = h / a.group;
   const int col = 16 * cb + (lane & 15);  // this lane's state column
   const int nkt = a.d_k >> 4;             // 16-row tiles of the state
+  const int nkb = (a.d_k + 31) >> 5;      // 32-deep contraction blocks over d_k
 
-  // ---- state slice: S[rt] holds rows 16 rt + 4 (lane >> 4) + e, column col ----
+  // S[rt] holds state rows 16 rt + 4 (lane >> 4) + e of column col
   f32x4_t S[8];
   const int64_t st_base = (int64_t(s) * a.H_v + h) * a.d_k * a.d_v;
 #pragma unroll
   for (int rt = 0; rt < 8; ++rt) {
     S[rt] = zero4();
-    if (rt < nkt && a.h0) {
-      for (int e = 0; e < 4; ++e) {
-        const int m = 16 * rt + 4 * (lane >> 4) + e;
-        S[rt][e] = a.h0[st_base + int64_t(m) * a.d_v + col];
-      }
-    }
+    if (rt < nkt && a.h0)
+      for (int e = 0; e < 4; ++e)
+        S[rt][e] = a.h0[st_base + int64_t(16 * rt + 4 * (lane >> 4) + e) * a.d_v + col];
   }
 
   int start, end;
@@ -80,25 +86,28 @@ __global__ __launch_bounds__(64) void scan_kernel(ScanArgs<T> a) {
     const T *kb = a.k + int64_t(tok0) * qk_stride + int64_t(hq) * a.d_k;
     const T *qb = a.q + int64_t(tok0) * qk_stride + int64_t(hq) * a.d_k;
     const T *vb = a.v + int64_t(tok0) * v_stride + int64_t(h) * a.d_v + col;
-    const T *entry = a.entries + (int64_t(c) * a.H_v + h) * kEntryElems;
+    const T *entry = reinterpret_cast<const T *>(a.entries + (int64_t(c) * a.H_v + h) *
+                                                                 entry_bytes<T>());
+    const float *gent = reinterpret_cast<const float *>(entry + 16 * kFragElems);
 
-    // gate of slot `lane` (padded slots repeat the last token's gate)
-    const float gl = a.g[int64_t(tok0 + min(lane, len - 1)) * a.H_v + h];
+    const float gl = gent[lane];  // slot gates; padded slots hold the last gate
     const float g_last = __shfl(gl, 63);
-    const float gamma_C = exp2f(g_last);
-    float gam[4][4];  // gamma of the rows this lane holds in a 64-row tile set
+    const float gamma_C = fast_exp2(g_last);
+    float gam[4][4], sc[4][4];
 #pragma unroll
     for (int rt = 0; rt < 4; ++rt)
 #pragma unroll
-      for (int e = 0; e < 4; ++e) gam[rt][e] = exp2f(__shfl(gl, 16 * rt + 4 * (lane >> 4) + e));
+      for (int e = 0; e < 4; ++e) {
+        const float gt = __shfl(gl, 16 * rt + 4 * (lane >> 4) + e);
+        gam[rt][e] = fast_exp2(gt);
+        sc[rt][e] = fast_exp2(g_last - gt);
+      }
 
-    // state as B fragments (d_k contraction blocks of 32)
     Frag<T> Sf[4];
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk) Sf[kk] = frag_from_acc<T>(S[2 * kk], S[2 * kk + 1]);
-    const int nkb = (a.d_k + 31) >> 5;
 
-    // ---- Y = K S,  OQ = Q S ----
+    // Y = K S, OQ = Q S
     f32x4_t Y[4], OQ[4];
 #pragma unroll
     for (int rt = 0; rt < 4; ++rt) {
@@ -107,15 +116,14 @@ __global__ __launch_bounds__(64) void scan_kernel(ScanArgs<T> a) {
 #pragma unroll
       for (int kk = 0; kk < 4; ++kk) {
         if (kk < nkb) {
-          Frag<T> fk = load_row_frag(kb, qk_stride, 16 * rt + (lane & 15), len, 32 * kk, a.d_k, lane);
-          Frag<T> fq = load_row_frag(qb, qk_stride, 16 * rt + (lane & 15), len, 32 * kk, a.d_k, lane);
-          Y[rt] = mfma(fk, Sf[kk], Y[rt]);
-          OQ[rt] = mfma(fq, Sf[kk], OQ[rt]);
+          const int row = 16 * rt + (lane & 15);
+          Y[rt] = mfma(load_row_frag(kb, qk_stride, row, len, 32 * kk, a.d_k, lane), Sf[kk], Y[rt]);
+          OQ[rt] = mfma(load_row_frag(qb, qk_stride, row, len, 32 * kk, a.d_k, lane), Sf[kk],
+                        OQ[rt]);
         }
       }
     }
-
-    // ---- X = V - gamma Y ----
+    // X = V - gamma Y
     f32x4_t X[4];
 #pragma unroll
     for (int rt = 0; rt < 4; ++rt)
@@ -125,24 +133,18 @@ __global__ __launch_bounds__(64) void scan_kernel(ScanArgs<T> a) {
         const float vv = t < len ? to_f32(vb[int64_t(t) * v_stride]) : 0.0f;
         X[rt][e] = vv - gam[rt][e] * Y[rt][e];
       }
-
-    // ---- U = T X ----
-    Frag<T> Xf[2];
-    Xf[0] = frag_from_acc<T>(X[0], X[1]);
-    Xf[1] = frag_from_acc<T>(X[2], X[3]);
-    f32x4_t Uacc[4];
+    // U = T X
+    Frag<T> Xf[2] = {frag_from_acc<T>(X[0], X[1]), frag_from_acc<T>(X[2], X[3])};
+    f32x4_t Ua[4];
 #pragma unroll
     for (int rt = 0; rt < 4; ++rt) {
-      Uacc[rt] = zero4();
+      Ua[rt] = zero4();
 #pragma unroll
       for (int kk = 0; kk < 2; ++kk)
-        Uacc[rt] = mfma(load_frag(entry + (rt * 2 + kk) * kFragElems, lane), Xf[kk], Uacc[rt]);
+        Ua[rt] = mfma(load_frag(entry + (rt * 2 + kk) * kFragElems, lane), Xf[kk], Ua[rt]);
     }
-    Frag<T> Uf[2];
-    Uf[0] = frag_from_acc<T>(Uacc[0], Uacc[1]);
-    Uf[1] = frag_from_acc<T>(Uacc[2], Uacc[3]);
-
-    // ---- O = gamma (Q S) + P U ----
+    Frag<T> Uf[2] = {frag_from_acc<T>(Ua[0], Ua[1]), frag_from_acc<T>(Ua[2], Ua[3])};
+    // O = gamma (Q S) + P U
 #pragma unroll
     for (int rt = 0; rt < 4; ++rt) {
       f32x4_t acc;
@@ -152,73 +154,118 @@ __global__ __launch_bounds__(64) void scan_kernel(ScanArgs<T> a) {
         acc = mfma(load_frag(entry + (8 + rt * 2 + kk) * kFragElems, lane), Uf[kk], acc);
       for (int e = 0; e < 4; ++e) {
         const int t = 16 * rt + 4 * (lane >> 4) + e;
-        if (t < len) a.o[int64_t(tok0 + t) * v_stride + int64_t(h) * a.d_v + col] = from_f32<T>(acc[e]);
+        if (t < len)
+          a.o[int64_t(tok0 + t) * v_stride + int64_t(h) * a.d_v + col] = from_f32<T>(acc[e]);
       }
     }
-
-    // ---- S <- gamma_C S + Ktilde^T U ----
+    // S <- gamma_C S + K^T (s U); K^T fragments gathered from k
 #pragma unroll
-    for (int rt = 0; rt < 8; ++rt) {
-      if (rt < nkt) {
+    for (int rt = 0; rt < 4; ++rt)
+      for (int e = 0; e < 4; ++e) Ua[rt][e] *= sc[rt][e];
+    Frag<T> Usf[2] = {frag_from_acc<T>(Ua[0], Ua[1]), frag_from_acc<T>(Ua[2], Ua[3])};
+#pragma unroll
+    for (int rm = 0; rm < 8; ++rm) {
+      if (rm < nkt) {
+        const int m = 16 * rm + (lane & 15);
         f32x4_t acc;
-        for (int e = 0; e < 4; ++e) acc[e] = gamma_C * S[rt][e];
+        for (int e = 0; e < 4; ++e) acc[e] = gamma_C * S[rm][e];
 #pragma unroll
-        for (int kk = 0; kk < 2; ++kk)
-          acc = mfma(load_frag(entry + (16 + rt * 2 + kk) * kFragElems, lane), Uf[kk], acc);
-        S[rt] = acc;
+        for (int kk = 0; kk < 2; ++kk) {
+          Frag<T> kt;
+          for (int j = 0; j < 8; ++j) {
+            const int i = 32 * kk + kappa(lane, j);
+            kt.set(j, i < len ? to_f32(kb[int64_t(i) * qk_stride + m]) : 0.0f);
+          }
+          acc = mfma(kt, Usf[kk], acc);
+        }
+        S[rm] = acc;
       }
     }
   }
 
   if (a.hT) {
 #pragma unroll
-    for (int rt = 0; rt < 8; ++rt) {
-      if (rt < nkt) {
-        for (int e = 0; e < 4; ++e) {
-          const int m = 16 * rt + 4 * (lane >> 4) + e;
-          a.hT[st_base + int64_t(m) * a.d_v + col] = S[rt][e];
-        }
-      }
-    }
+    for (int rt = 0; rt < 8; ++rt)
+      if (rt < nkt)
+        for (int e = 0; e < 4; ++e)
+          a.hT[st_base + int64_t(16 * rt + 4 * (lane >> 4) + e) * a.d_v + col] = S[rt][e];
   }
 }
 
 // ---------------------------------------------------------------------------
-// Pipelined variant for bf16 with d_k = 128 and d_v a multiple of 32.
+// Pipelined path: bf16, d_k = 128, d_v a multiple of 32.
 //
 // Two waves per block own 32 state columns (16 each).  A chunk's operands --
-// the k and q rows (swizzled row tiles), the 32 fragments T, P, Ktilde^T, the
-// 64 x 32 block of v and the 64 gates -- are copied into an LDS stage with
-// global_load_lds while the previous chunk is computed from the other stage,
-// so the sequential chunk chain never waits on global memory.  Rows past a
-// partial chunk repeat its last row (finite filler that meets exact zeros).
+// its k and q rows (swizzled row tiles), the T and P fragments and gates of
+// its workspace entry, and its 64 x 32 block of v -- are copied into one of
+// three LDS stages with global_load_lds, two chunks ahead of the chunk being
+// computed.  K^T fragments for the state update and the v block come from the
+// staged tiles through transposed reads (ds_read_b64_tr_b16).  Every LDS and
+// global offset a lane uses is computed once; per chunk only wave-uniform
+// bases change.  The chunk's outputs are written over the wave's own columns
+// of the staged v block and leave in 16-byte stores.  Rows past a partial
+// chunk repeat its last row (finite filler that only meets exact zeros).
 // ---------------------------------------------------------------------------
-constexpr int kStageK = 0;                       // 64 x 128 bf16
-constexpr int kStageQ = 16384;                   // 64 x 128 bf16
-constexpr int kStageF = 32768;                   // 32 fragments x 1 KiB
-constexpr int kStageV = 65536;                   // 64 x 32 bf16
-constexpr int kStageG = 69632;                   // 64 fp32
-constexpr int kStageBytes = 69888;
+constexpr int kStK = 0;        // 64 x 128 bf16 row tile
+constexpr int kStQ = 16384;    // 64 x 128 bf16 row tile
+constexpr int kStF = 32768;    // T (8) and P (8) fragments, 1 KiB each
+constexpr int kStG = 49152;    // 64 fp32 gates
+constexpr int kStV = 49408;    // 64 x 32 bf16 (v, then the outputs)
+constexpr int kStBytes = 53504;
+constexpr int kStages = 3;
+// Load instructions one wave issues per stage (wave 0: k tile, T, v, gates;
+// wave 1: q tile, P, v).  The end-of-chunk wait leaves exactly the newest
+// stage's loads in flight; loads complete in issue order, and nothing else is
+// issued after them in the chunk (its output stores go out at the top of the
+// next chunk, before that chunk's prefetch).
+constexpr int kStageLoadsW0 = 27;
+constexpr int kStageLoadsW1 = 26;
 
-__device__ __forceinline__ int vtile_off(int row, int col) {
-  // 64 rows x 32 bf16 (64 B per row); 16-byte chunks swizzled by row / 4 so
-  // the four row groups of an accumulator tile read different banks.
-  return row * 32 + 8 * ((col >> 3) ^ ((row >> 2) & 3)) + (col & 7);
+// Byte offset of (row, col) in the staged 64 x 32 bf16 v block; 16-byte
+// chunks are swizzled by (row / 4) mod 4.
+__device__ __forceinline__ int vtile_byte(int row, int col) {
+  return 2 * (row * 32 + 8 * ((col >> 3) ^ ((row >> 2) & 3)) + (col & 7));
 }
 
 __global__ __launch_bounds__(128) void scan_kernel_staged(ScanArgs<bf16_t> a) {
-  __shared__ __attribute__((aligned(16))) char smem[2 * kStageBytes];
+  __shared__ __attribute__((aligned(16))) char smem[kStages * kStBytes];
+  lds_t *const lds = lds_ptr(smem);
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int per_group = 8 * a.n_colblk;  // n_colblk = d_v / 32
-  const int bid = blockIdx.x;
-  const int grp = bid / per_group, rem = bid - grp * per_group;
-  const int cb = rem >> 3, u = grp * 8 + (rem & 7);
+  const int r0 = lane & 15, g = lane >> 4;
+  int u, cb;
+  decode_block(blockIdx.x, a.n_colblk, u, cb);  // n_colblk = d_v / 32
   if (u >= a.n_units) return;
   const int s = u / a.H_v, h = u - s * a.H_v, hq = h / a.group;
-  const int wcol = 16 * wave + (lane & 15);  // column inside the block's 32
-  const int col = 32 * cb + wcol;            // state column
+  const int col = 32 * cb + 16 * wave + r0;  // this lane's state column
 
+  // ---- lane-invariant LDS byte offsets (relative to a stage) ----
+  // A fragments of k / q rows 16 rt + r0, columns 32 kk + 16 half + 4 g:
+  // offset = 4096 rt + kq_off[kk][half].
+  int kq_off[4][2];
+#pragma unroll
+  for (int kk = 0; kk < 4; ++kk)
+#pragma unroll
+    for (int hf = 0; hf < 2; ++hf)
+      kq_off[kk][hf] = 2 * rowtile_off(r0, 32 * kk + 16 * hf + 4 * g);
+  // transposed K^T fragments: lane a = r0 addresses token
+  // 32 kk + 16 half + 4 g + a / 4, columns 16 rm + 4 (a mod 4) .. + 3:
+  // offset = 8192 kk + 4096 half + kt_off[rm].
+  int kt_off[8];
+#pragma unroll
+  for (int rm = 0; rm < 8; ++rm) kt_off[rm] = 2 * rowtile_off(4 * g + (r0 >> 2), 16 * rm + 4 * (r0 & 3));
+  // transposed v tile rt (rows 16 rt + 4 g + a / 4, columns 16 w + 4 (a mod 4)):
+  // offset = 1024 rt + v_off.
+  const int v_off = vtile_byte(4 * g + (r0 >> 2), 16 * wave + 4 * (r0 & 3));
+  // outputs in accumulator layout (row 16 rt + 4 g + e, column 16 w + r0):
+  // offset = 1024 rt + 64 e + o_woff.
+  const int o_woff = vtile_byte(4 * g, 16 * wave + r0);
+  // outputs leaving in 16-byte pieces: piece p of 2 covers row 32 p + lane / 2,
+  // columns 16 w + 8 (lane mod 2) .. + 7.
+  const int o_row = lane >> 1, o_half = lane & 1;
+  const int o_roff = vtile_byte(o_row, 16 * wave + 8 * o_half);
+
+  // ---- state ----
   f32x4_t S[8];
   const int64_t st_base = (int64_t(s) * a.H_v + h) * 128 * a.d_v;
 #pragma unroll
@@ -226,73 +273,121 @@ __global__ __launch_bounds__(128) void scan_kernel_staged(ScanArgs<bf16_t> a) {
     S[rt] = zero4();
     if (a.h0)
       for (int e = 0; e < 4; ++e)
-        S[rt][e] = a.h0[st_base + int64_t(16 * rt + 4 * (lane >> 4) + e) * a.d_v + col];
+        S[rt][e] = a.h0[st_base + int64_t(16 * rt + 4 * g + e) * a.d_v + col];
   }
 
   int start, end;
   a.geo.seq_bounds(s, start, end);
   const int C = a.geo.chunk;
-  const int n_chunks = (end - start + C - 1) / C;
   const int c_first = a.geo.first_chunk(s);
+  const int n_chunks = max(0, min((end - start + C - 1) / C, a.geo.n_slots - c_first));
   const int64_t qk_stride = int64_t(a.H_qk) * 128;
   const int64_t v_stride = int64_t(a.H_v) * a.d_v;
+  const int64_t ebytes = entry_bytes<bf16_t>();
+  const char *kq_src = reinterpret_cast<const char *>(wave == 0 ? a.k : a.q) + int64_t(hq) * 256;
+  const char *v_src = reinterpret_cast<const char *>(a.v) + (int64_t(h) * a.d_v + 32 * cb) * 2;
 
-  auto stage = [&](int cc, int buf) {
-    const int c = c_first + cc;
+  // lane-invariant global byte offsets of a full chunk's row-tile and v pieces
+  int kq_goff[16];
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const int row = 4 * i + g;
+    kq_goff[i] = int(2 * (int64_t(row) * qk_stride + 8 * (r0 ^ (row & 15))));
+  }
+  int v_goff[2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int row = 16 * (2 * wave + i) + (lane >> 2);
+    v_goff[i] = int(2 * (int64_t(row) * v_stride + 8 * ((lane & 3) ^ ((row >> 2) & 3))));
+  }
+
+  auto stage = [&](int cc) {
     const int tok0 = start + cc * C;
     const int len = min(C, end - tok0);
-    char *base = smem + buf * kStageBytes;
-    const bf16_t *entry = a.entries + (int64_t(c) * a.H_v + h) * kEntryElems;
-    if (wave == 0) {
-      stage_rowtile(reinterpret_cast<bf16_t *>(base + kStageK),
-                    a.k + int64_t(tok0) * qk_stride + int64_t(hq) * 128, qk_stride, len, lane, 0,
-                    16);
-      for (int f = 0; f < 16; ++f)
-        copy16_to_lds(entry + f * kFragElems + 8 * lane, base + kStageF + 1024 * f);
-      copy4_to_lds(a.g + int64_t(tok0 + min(lane, len - 1)) * a.H_v + h, base + kStageG);
+    char *base = smem + (cc % kStages) * kStBytes;
+    const char *entry = a.entries + (int64_t(c_first + cc) * a.H_v + h) * ebytes;
+    const char *kq = kq_src + int64_t(tok0) * qk_stride * 2;
+    const char *vv = v_src + int64_t(tok0) * v_stride * 2;
+    char *tile = base + (wave == 0 ? kStK : kStQ);
+    if (len == 64) {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) copy16_to_lds(kq + kq_goff[i], tile + 1024 * i);
+#pragma unroll
+      for (int i = 0; i < 2; ++i) copy16_to_lds(vv + v_goff[i], base + kStV + 2048 * wave + 1024 * i);
     } else {
-      stage_rowtile(reinterpret_cast<bf16_t *>(base + kStageQ),
-                    a.q + int64_t(tok0) * qk_stride + int64_t(hq) * 128, qk_stride, len, lane, 0,
-                    16);
-      for (int f = 16; f < 32; ++f)
-        copy16_to_lds(entry + f * kFragElems + 8 * lane, base + kStageF + 1024 * f);
+      // partial chunk: rows at or past len repeat row len - 1
+      for (int i = 0; i < 16; ++i) {
+        const int row = 4 * i + g;
+        const int r = row < len ? row : len - 1;
+        copy16_to_lds(kq + 2 * (int64_t(r) * qk_stride + 8 * (r0 ^ (row & 15))), tile + 1024 * i);
+      }
+      for (int i = 0; i < 2; ++i) {
+        const int row = 16 * (2 * wave + i) + (lane >> 2);
+        const int r = row < len ? row : len - 1;
+        copy16_to_lds(vv + 2 * (int64_t(r) * v_stride + 8 * ((lane & 3) ^ ((row >> 2) & 3))),
+                      base + kStV + 2048 * wave + 1024 * i);
+      }
     }
-    // v block: 4 pieces of 16 rows x 32 columns, two per wave
-    for (int i = 2 * wave; i < 2 * wave + 2; ++i) {
-      const int row = 16 * i + (lane >> 2);
-      const int logical = (lane & 3) ^ ((row >> 2) & 3);
-      const int r = row < len ? row : len - 1;
-      copy16_to_lds(a.v + int64_t(tok0 + r) * v_stride + int64_t(h) * a.d_v + 32 * cb + 8 * logical,
-                    base + kStageV + 1024 * i);
+    const char *f = entry + 8192 * wave + 16 * lane;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) copy16_to_lds(f + 1024 * i, base + kStF + 8192 * wave + 1024 * i);
+    if (wave == 0) copy4_to_lds(entry + 16384 + 4 * lane, base + kStG);
+  };
+
+  auto wait_all_but_newest_stage = [&]() {
+    if (wave == 0)
+      wait_vmem_upto<kStageLoadsW0>();
+    else
+      wait_vmem_upto<kStageLoadsW1>();
+  };
+  // The outputs of chunk cc sit over this wave's v columns of stage cc % 3;
+  // they leave in two 16-byte pieces per lane.
+  auto store_outputs = [&](int cc) {
+    const int tok0 = start + cc * C;
+    const int len = min(C, end - tok0);
+    const lds_t *st = lds + (cc % kStages) * kStBytes;
+#pragma unroll
+    for (int p = 0; p < 2; ++p) {
+      const int row = 32 * p + o_row;
+      const u32x4_t piece = lds_load<u32x4_t>(st + kStV + 2048 * p + o_roff);
+      if (row < len)
+        *reinterpret_cast<u32x4_t *>(a.o + int64_t(tok0 + row) * v_stride + int64_t(h) * a.d_v +
+                                     32 * cb + 16 * wave + 8 * o_half) = piece;
     }
   };
 
-  const bool any = n_chunks > 0 && c_first < a.geo.n_slots;
-  if (any) stage(0, 0);
-  wait_vmem();
-  __syncthreads();
+  if (n_chunks > 0) stage(0);
+  if (n_chunks > 1) {
+    stage(1);
+    wait_all_but_newest_stage();
+  } else {
+    wait_vmem();
+  }
+  lds_barrier();
 
   for (int cc = 0; cc < n_chunks; ++cc) {
-    const int c = c_first + cc;
-    if (c >= a.geo.n_slots) break;
-    const int buf = cc & 1;
-    if (cc + 1 < n_chunks && c + 1 < a.geo.n_slots) stage(cc + 1, buf ^ 1);
+    const bool ahead = cc + 2 < n_chunks;
+    // the previous chunk's outputs leave before the prefetch that reuses
+    // their stage (stage (cc + 2) % 3 == (cc - 1) % 3)
+    if (cc > 0) store_outputs(cc - 1);
+    if (ahead) stage(cc + 2);
 
-    const char *base = smem + buf * kStageBytes;
-    const bf16_t *sK = reinterpret_cast<const bf16_t *>(base + kStageK);
-    const bf16_t *sQ = reinterpret_cast<const bf16_t *>(base + kStageQ);
-    const bf16_t *sF = reinterpret_cast<const bf16_t *>(base + kStageF);
-    const bf16_t *sV = reinterpret_cast<const bf16_t *>(base + kStageV);
-    const float *sG = reinterpret_cast<const float *>(base + kStageG);
-    const int tok0 = start + cc * C;
-    const int len = min(C, end - tok0);
+    lds_t *const st = lds + (cc % kStages) * kStBytes;
 
-    const float gamma_C = exp2f(sG[63]);
-    float gam[4][4];
+    // gates of this lane's rows (16 rt + 4 g + e) and of the last slot
+    const float g_last = lds_load<float>(st + kStG + 252);
+    const float gamma_C = fast_exp2(g_last);
+    float gam[4][4], sc[4][4];
 #pragma unroll
-    for (int rt = 0; rt < 4; ++rt)
+    for (int rt = 0; rt < 4; ++rt) {
+      const f32x4_t gv = lds_load<f32x4_t>(st + kStG + 64 * rt + 16 * g);
+      const float gg[4] = {gv[0], gv[1], gv[2], gv[3]};
 #pragma unroll
-      for (int e = 0; e < 4; ++e) gam[rt][e] = exp2f(sG[16 * rt + 4 * (lane >> 4) + e]);
+      for (int e = 0; e < 4; ++e) {
+        gam[rt][e] = fast_exp2(gg[e]);
+        sc[rt][e] = fast_exp2(g_last - gg[e]);
+      }
+    }
 
     Frag<bf16_t> Sf[4];
 #pragma unroll
@@ -304,80 +399,96 @@ __global__ __launch_bounds__(128) void scan_kernel_staged(ScanArgs<bf16_t> a) {
     for (int rt = 0; rt < 4; ++rt) {
       Y[rt] = zero4();
       OQ[rt] = zero4();
-#pragma unroll
-      for (int kk = 0; kk < 4; ++kk) {
-        Y[rt] = mfma(rowtile_frag(sK, rt, kk, lane), Sf[kk], Y[rt]);
-        OQ[rt] = mfma(rowtile_frag(sQ, rt, kk, lane), Sf[kk], OQ[rt]);
-      }
     }
-    // X = V - gamma Y
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk)
+#pragma unroll
+      for (int rt = 0; rt < 4; ++rt) {
+        const lds_t *pk = st + kStK + 4096 * rt;
+        const lds_t *pq = st + kStQ + 4096 * rt;
+        Y[rt] = mfma(frag_cat(lds_load<bf16x4_t>(pk + kq_off[kk][0]),
+                              lds_load<bf16x4_t>(pk + kq_off[kk][1])), Sf[kk], Y[rt]);
+        OQ[rt] = mfma(frag_cat(lds_load<bf16x4_t>(pq + kq_off[kk][0]),
+                               lds_load<bf16x4_t>(pq + kq_off[kk][1])), Sf[kk], OQ[rt]);
+      }
+    // X = V - gamma Y (v tile read transposed: four rows of this lane's column)
     f32x4_t X[4];
 #pragma unroll
-    for (int rt = 0; rt < 4; ++rt)
+    for (int rt = 0; rt < 4; ++rt) {
+      const bf16x4_t vv = lds_read_tr16(st + kStV + 1024 * rt + v_off);
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int t = 16 * rt + 4 * (lane >> 4) + e;
-        X[rt][e] = to_f32(sV[vtile_off(t, wcol)]) - gam[rt][e] * Y[rt][e];
-      }
+      for (int e = 0; e < 4; ++e) X[rt][e] = static_cast<float>(vv[e]) - gam[rt][e] * Y[rt][e];
+    }
     // U = T X
-    Frag<bf16_t> Xf[2];
-    Xf[0] = frag_from_acc<bf16_t>(X[0], X[1]);
-    Xf[1] = frag_from_acc<bf16_t>(X[2], X[3]);
+    Frag<bf16_t> Xf[2] = {frag_from_acc<bf16_t>(X[0], X[1]), frag_from_acc<bf16_t>(X[2], X[3])};
     f32x4_t Ua[4];
 #pragma unroll
     for (int rt = 0; rt < 4; ++rt) {
       Ua[rt] = zero4();
 #pragma unroll
-      for (int kk = 0; kk < 2; ++kk)
-        Ua[rt] = mfma(load_frag(sF + (rt * 2 + kk) * kFragElems, lane), Xf[kk], Ua[rt]);
+      for (int kk = 0; kk < 2; ++kk) {
+        Frag<bf16_t> tf;
+        tf.v = lds_load<bf16x8_t>(st + kStF + 1024 * (rt * 2 + kk) + 16 * lane);
+        Ua[rt] = mfma(tf, Xf[kk], Ua[rt]);
+      }
     }
-    Frag<bf16_t> Uf[2];
-    Uf[0] = frag_from_acc<bf16_t>(Ua[0], Ua[1]);
-    Uf[1] = frag_from_acc<bf16_t>(Ua[2], Ua[3]);
-    // O = gamma (Q S) + P U
+    Frag<bf16_t> Uf[2] = {frag_from_acc<bf16_t>(Ua[0], Ua[1]), frag_from_acc<bf16_t>(Ua[2], Ua[3])};
+    // O = gamma (Q S) + P U, written over this wave's v columns
 #pragma unroll
     for (int rt = 0; rt < 4; ++rt) {
       f32x4_t acc;
       for (int e = 0; e < 4; ++e) acc[e] = gam[rt][e] * OQ[rt][e];
 #pragma unroll
-      for (int kk = 0; kk < 2; ++kk)
-        acc = mfma(load_frag(sF + (8 + rt * 2 + kk) * kFragElems, lane), Uf[kk], acc);
-      for (int e = 0; e < 4; ++e) {
-        const int t = 16 * rt + 4 * (lane >> 4) + e;
-        if (t < len)
-          a.o[int64_t(tok0 + t) * v_stride + int64_t(h) * a.d_v + col] = from_f32<bf16_t>(acc[e]);
+      for (int kk = 0; kk < 2; ++kk) {
+        Frag<bf16_t> pf;
+        pf.v = lds_load<bf16x8_t>(st + kStF + 8192 + 1024 * (rt * 2 + kk) + 16 * lane);
+        acc = mfma(pf, Uf[kk], acc);
       }
-    }
-    // S <- gamma_C S + Ktilde^T U
 #pragma unroll
-    for (int rt = 0; rt < 8; ++rt) {
+      for (int e = 0; e < 4; ++e)
+        lds_store<bf16_t>(st + kStV + 1024 * rt + 64 * e + o_woff, from_f32<bf16_t>(acc[e]));
+    }
+    // S <- gamma_C S + K^T (s U), K^T read transposed from the k tile
+#pragma unroll
+    for (int rt = 0; rt < 4; ++rt)
+      for (int e = 0; e < 4; ++e) Ua[rt][e] *= sc[rt][e];
+    Frag<bf16_t> Usf[2] = {frag_from_acc<bf16_t>(Ua[0], Ua[1]),
+                           frag_from_acc<bf16_t>(Ua[2], Ua[3])};
+#pragma unroll
+    for (int rm = 0; rm < 8; ++rm) {
       f32x4_t acc;
-      for (int e = 0; e < 4; ++e) acc[e] = gamma_C * S[rt][e];
+      for (int e = 0; e < 4; ++e) acc[e] = gamma_C * S[rm][e];
 #pragma unroll
-      for (int kk = 0; kk < 2; ++kk)
-        acc = mfma(load_frag(sF + (16 + rt * 2 + kk) * kFragElems, lane), Uf[kk], acc);
-      S[rt] = acc;
+      for (int kk = 0; kk < 2; ++kk) {
+        const lds_t *p = st + kStK + 8192 * kk + kt_off[rm];
+        acc = mfma(frag_cat(lds_read_tr16(p), lds_read_tr16(p + 4096)), Usf[kk], acc);
+      }
+      S[rm] = acc;
     }
-    wait_vmem();
-    __syncthreads();
+    // the next chunk's stage must be complete and this stage free for reuse
+    if (ahead)
+      wait_all_but_newest_stage();
+    else
+      wait_vmem();
+    lds_barrier();
   }
+  if (n_chunks > 0) store_outputs(n_chunks - 1);
 
   if (a.hT) {
 #pragma unroll
     for (int rt = 0; rt < 8; ++rt)
       for (int e = 0; e < 4; ++e)
-        a.hT[st_base + int64_t(16 * rt + 4 * (lane >> 4) + e) * a.d_v + col] = S[rt][e];
+        a.hT[st_base + int64_t(16 * rt + 4 * g + e) * a.d_v + col] = S[rt][e];
   }
 }
 
 template <typename T>
-static hipError_t launch_scan_t(const Problem &p, const Workspace &ws, hipStream_t st) {
+static ScanArgs<T> scan_args(const Problem &p, const Workspace &ws, int colblk_width) {
   ScanArgs<T> a;
   a.q = static_cast<const T *>(p.q);
   a.k = static_cast<const T *>(p.k);
   a.v = static_cast<const T *>(p.v);
-  a.g = ws.g;
-  a.entries = static_cast<const T *>(ws.entries);
+  a.entries = static_cast<const char *>(ws.entries);
   a.h0 = p.h0;
   a.o = static_cast<T *>(p.o);
   a.hT = p.hT;
@@ -387,43 +498,27 @@ static hipError_t launch_scan_t(const Problem &p, const Workspace &ws, hipStream
   a.d_v = p.d_v;
   a.group = p.H_v / p.H_qk;
   a.n_units = p.n_seqs * p.H_v;
-  a.n_colblk = p.d_v / 16;
+  a.n_colblk = p.d_v / colblk_width;
   a.geo = make_geom(p, &ws);
-  const int64_t groups = (int64_t(a.n_units) + 7) / 8;
-  const int64_t blocks = groups * 8 * a.n_colblk;
-  if (blocks == 0) return hipSuccess;
-  hipLaunchKernelGGL(scan_kernel<T>, dim3(unsigned(blocks)), dim3(64), 0, st, a);
-  return hipGetLastError();
-}
-
-static hipError_t launch_scan_staged(const Problem &p, const Workspace &ws, hipStream_t st) {
-  ScanArgs<bf16_t> a;
-  a.q = static_cast<const bf16_t *>(p.q);
-  a.k = static_cast<const bf16_t *>(p.k);
-  a.v = static_cast<const bf16_t *>(p.v);
-  a.g = ws.g;
-  a.entries = static_cast<const bf16_t *>(ws.entries);
-  a.h0 = p.h0;
-  a.o = static_cast<bf16_t *>(p.o);
-  a.hT = p.hT;
-  a.H_qk = p.H_qk;
-  a.H_v = p.H_v;
-  a.d_k = p.d_k;
-  a.d_v = p.d_v;
-  a.group = p.H_v / p.H_qk;
-  a.n_units = p.n_seqs * p.H_v;
-  a.n_colblk = p.d_v / 32;
-  a.geo = make_geom(p, &ws);
-  const int64_t groups = (int64_t(a.n_units) + 7) / 8;
-  const int64_t blocks = groups * 8 * a.n_colblk;
-  if (blocks == 0) return hipSuccess;
-  hipLaunchKernelGGL(scan_kernel_staged, dim3(unsigned(blocks)), dim3(128), 0, st, a);
-  return hipGetLastError();
+  return a;
 }
 
 hipError_t launch_scan(const Problem &p, const Workspace &ws, hipStream_t st) {
-  if (p.dtype == 1 && p.d_k == 128 && p.d_v % 32 == 0) return launch_scan_staged(p, ws, st);
-  return p.dtype == 1 ? launch_scan_t<bf16_t>(p, ws, st) : launch_scan_t<float>(p, ws, st);
+  const bool staged = p.dtype == 1 && p.d_k == 128 && p.d_v % 32 == 0;
+  const int width = staged ? 32 : 16;
+  const int64_t blocks = (int64_t(p.n_seqs) * p.H_v + 7) / 8 * 8 * (p.d_v / width);
+  if (blocks == 0) return hipSuccess;
+  if (staged) {
+    hipLaunchKernelGGL(scan_kernel_staged, dim3(unsigned(blocks)), dim3(128), 0, st,
+                       scan_args<bf16_t>(p, ws, width));
+  } else if (p.dtype == 1) {
+    hipLaunchKernelGGL(scan_kernel<bf16_t>, dim3(unsigned(blocks)), dim3(64), 0, st,
+                       scan_args<bf16_t>(p, ws, width));
+  } else {
+    hipLaunchKernelGGL(scan_kernel<float>, dim3(unsigned(blocks)), dim3(64), 0, st,
+                       scan_args<float>(p, ws, width));
+  }
+  return hipGetLastError();
 }
 
 }  // namespace gdn

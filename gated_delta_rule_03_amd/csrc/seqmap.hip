@@ -1,0 +1,50 @@
+// Packed-batch chunk map: chunk_off[s] = number of chunks in sequences
+// 0..s-1, computed on the device from cu_seqlens (no host synchronisation).
+// Chunks never cross a sequence boundary and a sequence's last chunk may be
+// shorter ("Attention as Matrix Algebra", section 8: chunks of C tokens with a
+// shorter final chunk), so sequence s owns ceil(L_s / C) chunks.
+#include "launch.hpp"
+
+namespace gdn {
+
+// chunk_off[s] = number of chunks in sequences 0..s-1 (packed batches).
+__global__ __launch_bounds__(256) void chunk_offsets_kernel(SeqGeom geo, int32_t *off) {
+  __shared__ int32_t sh[256];
+  __shared__ int32_t carry;
+  const int tid = threadIdx.x;
+  if (tid == 0) {
+    off[0] = 0;
+    carry = 0;
+  }
+  __syncthreads();
+  for (int base = 0; base < geo.n_seqs; base += 256) {
+    const int s = base + tid;
+    int cnt = 0;
+    if (s < geo.n_seqs) {
+      int start, end;
+      geo.seq_bounds(s, start, end);
+      cnt = (end - start + geo.chunk - 1) / geo.chunk;
+    }
+    sh[tid] = cnt;
+    __syncthreads();
+    for (int d = 1; d < 256; d <<= 1) {
+      const int add = tid >= d ? sh[tid - d] : 0;
+      __syncthreads();
+      sh[tid] += add;
+      __syncthreads();
+    }
+    if (s < geo.n_seqs) off[s + 1] = carry + sh[tid];
+    __syncthreads();
+    if (tid == 255) carry += sh[255];
+    __syncthreads();
+  }
+}
+
+hipError_t launch_chunk_offsets(const Problem &p, const Workspace &ws, hipStream_t st) {
+  if (!p.cu_seqlens) return hipSuccess;
+  SeqGeom geo = make_geom(p, &ws);
+  hipLaunchKernelGGL(chunk_offsets_kernel, dim3(1), dim3(256), 0, st, geo, ws.chunk_off);
+  return hipGetLastError();
+}
+
+}  // namespace gdn

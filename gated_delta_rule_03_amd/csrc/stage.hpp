@@ -28,6 +28,22 @@ __device__ __forceinline__ void copy4_to_lds(const void *src, void *wave_base) {
 }
 // Waits for this wave's outstanding global loads (including LDS-bound ones).
 __device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0); }
+// Waits until at most N of this wave's vector memory operations are
+// outstanding (s_waitcnt vmcnt(N); expcnt and lgkmcnt untouched).  Loads
+// complete in issue order, so this leaves only the N newest loads in flight.
+template <int N> __device__ __forceinline__ void wait_vmem_upto() {
+  static_assert(N >= 0 && N < 64, "vmcnt is 6 bits");
+  __builtin_amdgcn_s_waitcnt((N & 0xF) | (0x7 << 4) | (0xF << 8) | ((N >> 4) << 14));
+}
+
+// Workgroup barrier without the memory fence of __syncthreads (whose release
+// fence waits for every outstanding global load, including prefetches).  The
+// caller orders LDS itself: its own LDS-bound loads by wait_vmem[_upto], and
+// its LDS reads are complete because their results have been consumed.
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_s_waitcnt((0x3F & 0xF) | (0x7 << 4) | (0x0 << 8) | ((0x3F >> 4) << 14));
+  __builtin_amdgcn_s_barrier();
+}
 
 // Element offset of (row, col) in a swizzled 64 x 128 bf16 row tile.
 __device__ __forceinline__ int rowtile_off(int row, int col) {
@@ -63,6 +79,55 @@ __device__ __forceinline__ Frag<bf16_t> rowtile_frag(const bf16_t *tile, int rt,
   const bf16x4_t hi = *reinterpret_cast<const bf16x4_t *>(tile + rowtile_off(row, c1));
   Frag<bf16_t> f;
   f.v = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+  return f;
+}
+
+// ---------------------------------------------------------------------------
+// Raw LDS access by byte offset (address space 3, so the compiler emits ds_*
+// instructions and folds constant offsets into them).
+// ---------------------------------------------------------------------------
+typedef __attribute__((address_space(3))) char lds_t;
+typedef short s16x4_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s16x4_t lds_s16x4_t;
+typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
+typedef unsigned u32x4_t __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ lds_t *lds_ptr(void *generic_shared) {
+  return (lds_t *)(generic_shared);
+}
+template <typename V> __device__ __forceinline__ V lds_load(const lds_t *p) {
+  return *(const __attribute__((address_space(3))) V *)(p);
+}
+template <typename V> __device__ __forceinline__ void lds_store(lds_t *p, V v) {
+  *(__attribute__((address_space(3))) V *)(p) = v;
+}
+// ds_read_b64_tr_b16: inside each group of 16 lanes, lane i receives for
+// j = 0..3 the (i mod 4)-th 16-bit element of the 8 bytes addressed by lane
+// (i / 4) + 4 j of the group.  Reads 4 rows x 16 columns of a row-major bf16
+// matrix as four values of one column per lane.
+__device__ __forceinline__ bf16x4_t lds_read_tr16(const lds_t *p) {
+  s16x4_t v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t *)(p));
+  return __builtin_bit_cast(bf16x4_t, v);
+}
+__device__ __forceinline__ Frag<bf16_t> frag_cat(bf16x4_t lo, bf16x4_t hi) {
+  Frag<bf16_t> f;
+  f.v = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+  return f;
+}
+
+// Transposed fragment of a swizzled row tile: lane l holds column
+// m = 16 rm + (l & 15) (an A-operand row of the transpose) and elements
+// j = 0..7 stand for tile rows 32 kk + kappa(l, j).  With the row swizzle the
+// 64 lanes of each 2-byte read spread over 32 banks without conflicts.
+__device__ __forceinline__ Frag<bf16_t> rowtile_colfrag(const bf16_t *tile, int rm, int kk,
+                                                        int lane) {
+  const int m = 16 * rm + (lane & 15);
+  Frag<bf16_t> f;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const int i = 32 * kk + kappa(lane, j);
+    f.v[j] = __builtin_bit_cast(__bf16, tile[rowtile_off(i, m)]);
+  }
   return f;
 }
 
