@@ -27,11 +27,14 @@ int64_t chunk_slots(const Problem &p);
 
 // One workspace entry per (chunk slot, value head): the intra-chunk factors
 // in MFMA fragment order -- T (8 fragments), P (8 fragments) of 64 lanes x 8
-// elements of the operand type -- followed by the chunk's 64 cumulative log2
-// gates (fp32).
+// elements of the operand type -- followed by a 1 KiB gate block of fp32:
+// gamma_t = 2^g_t for the 64 slots, then s_t = 2^(g_C - g_t), then padding.
+// (g_t is the chunk-local cumulative log2 gate; padded slots repeat the last
+// token's gate, so gamma_63 = gamma_C and s = 1 there.)
 constexpr int kFragElems = 64 * 8;
+constexpr int kGateBlockBytes = 1024;
 template <typename T> constexpr int64_t entry_bytes() {
-  return int64_t(16) * kFragElems * sizeof(T) + 64 * sizeof(float);
+  return int64_t(16) * kFragElems * sizeof(T) + kGateBlockBytes;
 }
 
 struct Workspace {

@@ -19,9 +19,10 @@
 //   O    = diag(gamma) Q S + P U,       P_ti = Gamma_ti q_t^T k_i  (i <= t)
 //   S   <- gamma_C S + K^T diag(2^(g_C - g)) U
 //
-// This kernel computes what does not depend on the incoming state -- g, T and
-// P for one (chunk, value head) -- and writes them to the workspace entry in
-// MFMA fragment order (T: 8 fragments, P: 8 fragments, then the 64 gates).
+// This kernel computes what does not depend on the incoming state -- T, P and
+// the gate factors gamma_t = 2^g_t and s_t = 2^(g_C - g_t) for one (chunk,
+// value head) -- and writes them to the workspace entry (T and P in MFMA
+// fragment order, then the gate block).
 //
 // MFMA: k k^T and k q^T are dense 64 x 64 x d_k contractions (bf16 MFMA for
 // bf16 inputs, fp32 MFMA for fp32 inputs).  The triangular inverse is fp32:
@@ -76,13 +77,13 @@ __global__ __launch_bounds__(256) void prep_kernel(PrepArgs<T> a) {
   const T *qb = a.q + int64_t(tok0) * stride + int64_t(hq) * a.d_k;
   if constexpr (kStaged) {
     static_assert(sizeof(T) == 2, "staged path is bf16");
-    stage_rowtile(sK, reinterpret_cast<const bf16_t *>(kb), stride, len, lane, 4 * wave, 4);
-    stage_rowtile(sQ, reinterpret_cast<const bf16_t *>(qb), stride, len, lane, 4 * wave, 4);
+    stage_rowtile(lds_ptr(sK), reinterpret_cast<const bf16_t *>(kb), stride, len, lane, 4 * wave, 4);
+    stage_rowtile(lds_ptr(sQ), reinterpret_cast<const bf16_t *>(qb), stride, len, lane, 4 * wave, 4);
   }
   char *entry = a.entries + (int64_t(c) * a.H_v + h) * entry_bytes<T>();
   T *fragT = reinterpret_cast<T *>(entry);
   T *fragP = fragT + 8 * kFragElems;
-  float *gout = reinterpret_cast<float *>(fragT + 16 * kFragElems);
+  float *gate_out = reinterpret_cast<float *>(fragT + 16 * kFragElems);
 
   // ---- cumulative gate (wave 0): g_t for slot t, padded slots hold g_last ----
   if (wave == 0) {
@@ -96,7 +97,9 @@ __global__ __launch_bounds__(256) void prep_kernel(PrepArgs<T> a) {
     }
     sg[t] = x;
     sb[t] = t < len ? a.beta[idx] : 0.0f;
-    gout[t] = x;
+    const float g_last = __shfl(x, 63);
+    gate_out[t] = exp2f(x);             // gamma_t
+    gate_out[64 + t] = exp2f(g_last - x);  // s_t
   }
   if constexpr (kStaged) wait_vmem();
   lds_barrier();

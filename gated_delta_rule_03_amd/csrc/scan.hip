@@ -90,17 +90,15 @@ __global__ __launch_bounds__(64) void scan_kernel(ScanArgs<T> a) {
                                                                  entry_bytes<T>());
     const float *gent = reinterpret_cast<const float *>(entry + 16 * kFragElems);
 
-    const float gl = gent[lane];  // slot gates; padded slots hold the last gate
-    const float g_last = __shfl(gl, 63);
-    const float gamma_C = fast_exp2(g_last);
+    const float gam_l = gent[lane], sc_l = gent[64 + lane];  // this lane's slot
+    const float gamma_C = __shfl(gam_l, 63);
     float gam[4][4], sc[4][4];
 #pragma unroll
     for (int rt = 0; rt < 4; ++rt)
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        const float gt = __shfl(gl, 16 * rt + 4 * (lane >> 4) + e);
-        gam[rt][e] = fast_exp2(gt);
-        sc[rt][e] = fast_exp2(g_last - gt);
+        gam[rt][e] = __shfl(gam_l, 16 * rt + 4 * (lane >> 4) + e);
+        sc[rt][e] = __shfl(sc_l, 16 * rt + 4 * (lane >> 4) + e);
       }
 
     Frag<T> Sf[4];
@@ -209,10 +207,9 @@ __global__ __launch_bounds__(64) void scan_kernel(ScanArgs<T> a) {
 constexpr int kStK = 0;        // 64 x 128 bf16 row tile
 constexpr int kStQ = 16384;    // 64 x 128 bf16 row tile
 constexpr int kStF = 32768;    // T (8) and P (8) fragments, 1 KiB each
-constexpr int kStG = 49152;    // 64 fp32 gates
-constexpr int kStV = 49408;    // 64 x 32 bf16 (v, then the outputs)
-constexpr int kStBytes = 53504;
-constexpr int kStages = 3;
+constexpr int kStG = 49152;    // gate block: gamma (64 fp32), s (64 fp32), padding
+constexpr int kStV = 50176;    // 64 x 32 bf16 (v, then the outputs)
+constexpr int kStBytes = 54272;
 // Load instructions one wave issues per stage (wave 0: k tile, T, v, gates;
 // wave 1: q tile, P, v).  The end-of-chunk wait leaves exactly the newest
 // stage's loads in flight; loads complete in issue order, and nothing else is
@@ -221,15 +218,15 @@ constexpr int kStages = 3;
 constexpr int kStageLoadsW0 = 27;
 constexpr int kStageLoadsW1 = 26;
 
-// Byte offset of (row, col) in the staged 64 x 32 bf16 v block; 16-byte
-// chunks are swizzled by (row / 4) mod 4.
-__device__ __forceinline__ int vtile_byte(int row, int col) {
-  return 2 * (row * 32 + 8 * ((col >> 3) ^ ((row >> 2) & 3)) + (col & 7));
-}
+// Three stages as distinct LDS objects: with the chunk loop unrolled by three,
+// every access names its stage at compile time, so the compiler can tell that
+// the in-flight global_load_lds copies never alias the stage being read and
+// does not wait for them before LDS reads.
+__shared__ __attribute__((aligned(16))) char scan_stage0[kStBytes];
+__shared__ __attribute__((aligned(16))) char scan_stage1[kStBytes];
+__shared__ __attribute__((aligned(16))) char scan_stage2[kStBytes];
 
 __global__ __launch_bounds__(128) void scan_kernel_staged(ScanArgs<bf16_t> a) {
-  __shared__ __attribute__((aligned(16))) char smem[kStages * kStBytes];
-  lds_t *const lds = lds_ptr(smem);
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int r0 = lane & 15, g = lane >> 4;
@@ -262,8 +259,7 @@ __global__ __launch_bounds__(128) void scan_kernel_staged(ScanArgs<bf16_t> a) {
   const int o_woff = vtile_byte(4 * g, 16 * wave + r0);
   // outputs leaving in 16-byte pieces: piece p of 2 covers row 32 p + lane / 2,
   // columns 16 w + 8 (lane mod 2) .. + 7.
-  const int o_row = lane >> 1, o_half = lane & 1;
-  const int o_roff = vtile_byte(o_row, 16 * wave + 8 * o_half);
+  const int o_roff = vtile_byte(out_piece_row(0, lane), out_piece_col(wave, lane));
 
   // ---- state ----
   f32x4_t S[8];
@@ -287,51 +283,41 @@ __global__ __launch_bounds__(128) void scan_kernel_staged(ScanArgs<bf16_t> a) {
   const char *kq_src = reinterpret_cast<const char *>(wave == 0 ? a.k : a.q) + int64_t(hq) * 256;
   const char *v_src = reinterpret_cast<const char *>(a.v) + (int64_t(h) * a.d_v + 32 * cb) * 2;
 
-  // lane-invariant global byte offsets of a full chunk's row-tile and v pieces
-  int kq_goff[16];
+  // lane parts of a full chunk's global offsets (tile_index.hpp): row-tile
+  // copy i adds the wave-uniform rowtile_copy_uniform(i) to kq_goff[i mod 4]
+  uint32_t kq_goff[4];
 #pragma unroll
-  for (int i = 0; i < 16; ++i) {
-    const int row = 4 * i + g;
-    kq_goff[i] = int(2 * (int64_t(row) * qk_stride + 8 * (r0 ^ (row & 15))));
-  }
-  int v_goff[2];
+  for (int i = 0; i < 4; ++i) kq_goff[i] = rowtile_copy_lane(i, lane, qk_stride);
+  uint32_t v_goff[2];
 #pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    const int row = 16 * (2 * wave + i) + (lane >> 2);
-    v_goff[i] = int(2 * (int64_t(row) * v_stride + 8 * ((lane & 3) ^ ((row >> 2) & 3))));
-  }
+  for (int i = 0; i < 2; ++i) v_goff[i] = uint32_t(vblock_copy_src(2 * wave + i, lane, 64, v_stride));
 
-  auto stage = [&](int cc) {
+  auto stage = [&](int cc, char *base_mem) {
     const int tok0 = start + cc * C;
     const int len = min(C, end - tok0);
-    char *base = smem + (cc % kStages) * kStBytes;
+    lds_t *const base = lds_ptr(base_mem);
     const char *entry = a.entries + (int64_t(c_first + cc) * a.H_v + h) * ebytes;
     const char *kq = kq_src + int64_t(tok0) * qk_stride * 2;
     const char *vv = v_src + int64_t(tok0) * v_stride * 2;
-    char *tile = base + (wave == 0 ? kStK : kStQ);
+    lds_t *const tile = base + (wave == 0 ? kStK : kStQ);
     if (len == 64) {
 #pragma unroll
-      for (int i = 0; i < 16; ++i) copy16_to_lds(kq + kq_goff[i], tile + 1024 * i);
+      for (int i = 0; i < 16; ++i)
+        dma16(kq + rowtile_copy_uniform(i, qk_stride), kq_goff[i & 3], tile + 1024 * i);
 #pragma unroll
-      for (int i = 0; i < 2; ++i) copy16_to_lds(vv + v_goff[i], base + kStV + 2048 * wave + 1024 * i);
+      for (int i = 0; i < 2; ++i) dma16(vv, v_goff[i], base + kStV + 2048 * wave + 1024 * i);
     } else {
       // partial chunk: rows at or past len repeat row len - 1
-      for (int i = 0; i < 16; ++i) {
-        const int row = 4 * i + g;
-        const int r = row < len ? row : len - 1;
-        copy16_to_lds(kq + 2 * (int64_t(r) * qk_stride + 8 * (r0 ^ (row & 15))), tile + 1024 * i);
-      }
-      for (int i = 0; i < 2; ++i) {
-        const int row = 16 * (2 * wave + i) + (lane >> 2);
-        const int r = row < len ? row : len - 1;
-        copy16_to_lds(vv + 2 * (int64_t(r) * v_stride + 8 * ((lane & 3) ^ ((row >> 2) & 3))),
-                      base + kStV + 2048 * wave + 1024 * i);
-      }
+      for (int i = 0; i < 16; ++i)
+        dma16(kq, uint32_t(rowtile_copy_src(i, lane, len, qk_stride)), tile + 1024 * i);
+      for (int i = 0; i < 2; ++i)
+        dma16(vv, uint32_t(vblock_copy_src(2 * wave + i, lane, len, v_stride)),
+              base + kStV + 2048 * wave + 1024 * i);
     }
-    const char *f = entry + 8192 * wave + 16 * lane;
+    const char *f = entry + 8192 * wave;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) copy16_to_lds(f + 1024 * i, base + kStF + 8192 * wave + 1024 * i);
-    if (wave == 0) copy4_to_lds(entry + 16384 + 4 * lane, base + kStG);
+    for (int i = 0; i < 8; ++i) dma16(f + 1024 * i, 16 * lane, base + kStF + 8192 * wave + 1024 * i);
+    if (wave == 0) dma16(entry + 16384, 16 * lane, base + kStG);
   };
 
   auto wait_all_but_newest_stage = [&]() {
@@ -342,137 +328,159 @@ __global__ __launch_bounds__(128) void scan_kernel_staged(ScanArgs<bf16_t> a) {
   };
   // The outputs of chunk cc sit over this wave's v columns of stage cc % 3;
   // they leave in two 16-byte pieces per lane.
-  auto store_outputs = [&](int cc) {
+  // (cc = -1 stores nothing: its row count is 0)
+  auto store_outputs = [&](int cc, const char *stage_mem) {
     const int tok0 = start + cc * C;
-    const int len = min(C, end - tok0);
-    const lds_t *st = lds + (cc % kStages) * kStBytes;
+    const int len = cc >= 0 ? min(C, end - tok0) : 0;
+    const lds_t *st = lds_ptr(const_cast<char *>(stage_mem));
 #pragma unroll
     for (int p = 0; p < 2; ++p) {
-      const int row = 32 * p + o_row;
+      const int row = out_piece_row(p, lane);
       const u32x4_t piece = lds_load<u32x4_t>(st + kStV + 2048 * p + o_roff);
       if (row < len)
         *reinterpret_cast<u32x4_t *>(a.o + int64_t(tok0 + row) * v_stride + int64_t(h) * a.d_v +
-                                     32 * cb + 16 * wave + 8 * o_half) = piece;
+                                     32 * cb + out_piece_col(wave, lane)) = piece;
     }
   };
 
-  if (n_chunks > 0) stage(0);
-  if (n_chunks > 1) {
-    stage(1);
+  if (n_chunks > 0) {
+    stage(0, scan_stage0);
+    stage(min(1, n_chunks - 1), scan_stage1);
     wait_all_but_newest_stage();
-  } else {
-    wait_vmem();
   }
   lds_barrier();
 
-  for (int cc = 0; cc < n_chunks; ++cc) {
-    const bool ahead = cc + 2 < n_chunks;
-    // the previous chunk's outputs leave before the prefetch that reuses
-    // their stage (stage (cc + 2) % 3 == (cc - 1) % 3)
-    if (cc > 0) store_outputs(cc - 1);
-    if (ahead) stage(cc + 2);
+  // One chunk: compute from `cur`; the previous chunk's outputs (in `prev`)
+  // leave before the prefetch of chunk cc + 2 reuses that stage.  The
+  // prefetch is issued every chunk (past the end it re-reads the last chunk),
+  // so each chunk issues the same loads and the waits below are exact.
+  auto chunk_step = [&](int cc, char *cur_mem, char *prev_mem) {
+    store_outputs(cc - 1, prev_mem);
+    stage(min(cc + 2, n_chunks - 1), prev_mem);
 
-    lds_t *const st = lds + (cc % kStages) * kStBytes;
+    lds_t *const st = lds_ptr(cur_mem);
 
-    // gates of this lane's rows (16 rt + 4 g + e) and of the last slot
-    const float g_last = lds_load<float>(st + kStG + 252);
-    const float gamma_C = fast_exp2(g_last);
-    float gam[4][4], sc[4][4];
+    // gate factors of this lane's rows (16 rt + 4 g + e) and of the last slot
+    const float gamma_C = lds_load<float>(st + kStG + 252);
+    f32x4_t gam[4], sc[4];
 #pragma unroll
     for (int rt = 0; rt < 4; ++rt) {
-      const f32x4_t gv = lds_load<f32x4_t>(st + kStG + 64 * rt + 16 * g);
-      const float gg[4] = {gv[0], gv[1], gv[2], gv[3]};
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        gam[rt][e] = fast_exp2(gg[e]);
-        sc[rt][e] = fast_exp2(g_last - gg[e]);
-      }
+      gam[rt] = lds_load<f32x4_t>(st + kStG + 64 * rt + 16 * g);
+      sc[rt] = lds_load<f32x4_t>(st + kStG + 256 + 64 * rt + 16 * g);
     }
 
-    Frag<bf16_t> Sf[4];
-#pragma unroll
-    for (int kk = 0; kk < 4; ++kk) Sf[kk] = frag_from_acc<bf16_t>(S[2 * kk], S[2 * kk + 1]);
-
-    // Y = K S, OQ = Q S
-    f32x4_t Y[4], OQ[4];
-#pragma unroll
-    for (int rt = 0; rt < 4; ++rt) {
-      Y[rt] = zero4();
-      OQ[rt] = zero4();
-    }
+    // Operands are read into registers one phase ahead of their use, so each
+    // phase's MFMAs do not wait on their own LDS reads.
+    Frag<bf16_t> kf[4][4];  // k rows: [contraction block][row tile]
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk)
 #pragma unroll
       for (int rt = 0; rt < 4; ++rt) {
         const lds_t *pk = st + kStK + 4096 * rt;
-        const lds_t *pq = st + kStQ + 4096 * rt;
-        Y[rt] = mfma(frag_cat(lds_load<bf16x4_t>(pk + kq_off[kk][0]),
-                              lds_load<bf16x4_t>(pk + kq_off[kk][1])), Sf[kk], Y[rt]);
-        OQ[rt] = mfma(frag_cat(lds_load<bf16x4_t>(pq + kq_off[kk][0]),
-                               lds_load<bf16x4_t>(pq + kq_off[kk][1])), Sf[kk], OQ[rt]);
+        kf[kk][rt] = frag_cat(lds_load<bf16x4_t>(pk + kq_off[kk][0]),
+                              lds_load<bf16x4_t>(pk + kq_off[kk][1]));
       }
-    // X = V - gamma Y (v tile read transposed: four rows of this lane's column)
+    bf16x4_t vt[4];  // v, transposed: four rows of this lane's column
+#pragma unroll
+    for (int rt = 0; rt < 4; ++rt) vt[rt] = lds_read_tr16(st + kStV + 1024 * rt + v_off);
+    Frag<bf16_t> tf[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) tf[i].v = lds_load<bf16x8_t>(st + kStF + 1024 * i + 16 * lane);
+
+    Frag<bf16_t> Sf[4];
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) Sf[kk] = frag_from_acc<bf16_t>(S[2 * kk], S[2 * kk + 1]);
+
+    // Y = K S
+    f32x4_t Y[4];
+#pragma unroll
+    for (int rt = 0; rt < 4; ++rt) Y[rt] = zero4();
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk)
+#pragma unroll
+      for (int rt = 0; rt < 4; ++rt) Y[rt] = mfma(kf[kk][rt], Sf[kk], Y[rt]);
+
+    // next: q rows, P and K^T fragments
+    Frag<bf16_t> qf[4][4];
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk)
+#pragma unroll
+      for (int rt = 0; rt < 4; ++rt) {
+        const lds_t *pq = st + kStQ + 4096 * rt;
+        qf[kk][rt] = frag_cat(lds_load<bf16x4_t>(pq + kq_off[kk][0]),
+                              lds_load<bf16x4_t>(pq + kq_off[kk][1]));
+      }
+
+    // X = V - gamma Y, then U = T X
     f32x4_t X[4];
 #pragma unroll
-    for (int rt = 0; rt < 4; ++rt) {
-      const bf16x4_t vv = lds_read_tr16(st + kStV + 1024 * rt + v_off);
+    for (int rt = 0; rt < 4; ++rt)
 #pragma unroll
-      for (int e = 0; e < 4; ++e) X[rt][e] = static_cast<float>(vv[e]) - gam[rt][e] * Y[rt][e];
-    }
-    // U = T X
+      for (int e = 0; e < 4; ++e) X[rt][e] = static_cast<float>(vt[rt][e]) - gam[rt][e] * Y[rt][e];
     Frag<bf16_t> Xf[2] = {frag_from_acc<bf16_t>(X[0], X[1]), frag_from_acc<bf16_t>(X[2], X[3])};
     f32x4_t Ua[4];
 #pragma unroll
     for (int rt = 0; rt < 4; ++rt) {
       Ua[rt] = zero4();
 #pragma unroll
-      for (int kk = 0; kk < 2; ++kk) {
-        Frag<bf16_t> tf;
-        tf.v = lds_load<bf16x8_t>(st + kStF + 1024 * (rt * 2 + kk) + 16 * lane);
-        Ua[rt] = mfma(tf, Xf[kk], Ua[rt]);
-      }
+      for (int kk = 0; kk < 2; ++kk) Ua[rt] = mfma(tf[rt * 2 + kk], Xf[kk], Ua[rt]);
     }
+
+    Frag<bf16_t> ktf[8][2];
+#pragma unroll
+    for (int rm = 0; rm < 8; ++rm)
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk) {
+        const lds_t *p = st + kStK + 8192 * kk + kt_off[rm];
+        ktf[rm][kk] = frag_cat(lds_read_tr16(p), lds_read_tr16(p + 4096));
+      }
+    Frag<bf16_t> pf[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) pf[i].v = lds_load<bf16x8_t>(st + kStF + 8192 + 1024 * i + 16 * lane);
+
     Frag<bf16_t> Uf[2] = {frag_from_acc<bf16_t>(Ua[0], Ua[1]), frag_from_acc<bf16_t>(Ua[2], Ua[3])};
-    // O = gamma (Q S) + P U, written over this wave's v columns
+#pragma unroll
+    for (int rt = 0; rt < 4; ++rt) Ua[rt] *= sc[rt];
+    Frag<bf16_t> Usf[2] = {frag_from_acc<bf16_t>(Ua[0], Ua[1]),
+                           frag_from_acc<bf16_t>(Ua[2], Ua[3])};
+
+    // S <- gamma_C S + K^T (s U): the state chain's last product
+#pragma unroll
+    for (int rm = 0; rm < 8; ++rm) {
+      f32x4_t acc = gamma_C * S[rm];
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk) acc = mfma(ktf[rm][kk], Usf[kk], acc);
+      S[rm] = acc;
+    }
+
+    // O = gamma (Q S) + P U (Sf still holds the chunk-start state), written
+    // over this wave's v columns
 #pragma unroll
     for (int rt = 0; rt < 4; ++rt) {
-      f32x4_t acc;
-      for (int e = 0; e < 4; ++e) acc[e] = gam[rt][e] * OQ[rt][e];
+      f32x4_t oq = zero4();
 #pragma unroll
-      for (int kk = 0; kk < 2; ++kk) {
-        Frag<bf16_t> pf;
-        pf.v = lds_load<bf16x8_t>(st + kStF + 8192 + 1024 * (rt * 2 + kk) + 16 * lane);
-        acc = mfma(pf, Uf[kk], acc);
-      }
+      for (int kk = 0; kk < 4; ++kk) oq = mfma(qf[kk][rt], Sf[kk], oq);
+      f32x4_t acc = gam[rt] * oq;
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk) acc = mfma(pf[rt * 2 + kk], Uf[kk], acc);
 #pragma unroll
       for (int e = 0; e < 4; ++e)
         lds_store<bf16_t>(st + kStV + 1024 * rt + 64 * e + o_woff, from_f32<bf16_t>(acc[e]));
     }
-    // S <- gamma_C S + K^T (s U), K^T read transposed from the k tile
-#pragma unroll
-    for (int rt = 0; rt < 4; ++rt)
-      for (int e = 0; e < 4; ++e) Ua[rt][e] *= sc[rt][e];
-    Frag<bf16_t> Usf[2] = {frag_from_acc<bf16_t>(Ua[0], Ua[1]),
-                           frag_from_acc<bf16_t>(Ua[2], Ua[3])};
-#pragma unroll
-    for (int rm = 0; rm < 8; ++rm) {
-      f32x4_t acc;
-      for (int e = 0; e < 4; ++e) acc[e] = gamma_C * S[rm][e];
-#pragma unroll
-      for (int kk = 0; kk < 2; ++kk) {
-        const lds_t *p = st + kStK + 8192 * kk + kt_off[rm];
-        acc = mfma(frag_cat(lds_read_tr16(p), lds_read_tr16(p + 4096)), Usf[kk], acc);
-      }
-      S[rm] = acc;
-    }
     // the next chunk's stage must be complete and this stage free for reuse
-    if (ahead)
-      wait_all_but_newest_stage();
-    else
-      wait_vmem();
+    wait_all_but_newest_stage();
     lds_barrier();
+  };
+  for (int cc = 0; cc < n_chunks; cc += 3) {
+    chunk_step(cc, scan_stage0, scan_stage2);
+    if (cc + 1 < n_chunks) chunk_step(cc + 1, scan_stage1, scan_stage0);
+    if (cc + 2 < n_chunks) chunk_step(cc + 2, scan_stage2, scan_stage1);
   }
-  if (n_chunks > 0) store_outputs(n_chunks - 1);
+  if (n_chunks > 0) {
+    const int last = (n_chunks - 1) % 3;
+    store_outputs(n_chunks - 1, last == 0 ? scan_stage0 : last == 1 ? scan_stage1 : scan_stage2);
+  }
+  wait_vmem();  // the trailing prefetches
 
   if (a.hT) {
 #pragma unroll

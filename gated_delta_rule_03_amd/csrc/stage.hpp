@@ -11,20 +11,27 @@
 #pragma once
 
 #include "device.hpp"
+#include "tile_index.hpp"
 
 namespace gdn {
 
-typedef __attribute__((address_space(3))) void lds_void_t;
-typedef __attribute__((address_space(1))) void glb_void_t;
+typedef __attribute__((address_space(3))) char lds_t;
 
-// 16 bytes per lane: global src (per lane) -> LDS wave_base + 16 * lane.
-// `wave_base` must be the same for every lane of the wave.
-__device__ __forceinline__ void copy16_to_lds(const void *src, void *wave_base) {
-  __builtin_amdgcn_global_load_lds((glb_void_t *)(src), (lds_void_t *)(wave_base), 16, 0, 0);
+__device__ __forceinline__ lds_t *lds_ptr(void *generic_shared) {
+  return (lds_t *)(generic_shared);
 }
-// 4 bytes per lane: global src -> LDS wave_base + 4 * lane.
-__device__ __forceinline__ void copy4_to_lds(const void *src, void *wave_base) {
-  __builtin_amdgcn_global_load_lds((glb_void_t *)(src), (lds_void_t *)(wave_base), 4, 0, 0);
+
+// 16 bytes per lane from global `base + voff` (base wave-uniform, voff per
+// lane) into LDS at dst + 16 * lane (dst wave-uniform).  Issued as inline
+// assembly on purpose: the compiler then adds no waits of its own for these
+// copies, and every user orders them explicitly (counted vmcnt waits followed
+// by a barrier) -- the compiler's own rule would wait for every in-flight
+// prefetch before any LDS read it cannot prove disjoint.
+__device__ __forceinline__ void dma16(const void *base, uint32_t voff, lds_t *dst) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2"
+               :
+               : "s"((uint32_t)(uintptr_t)dst), "v"(voff), "s"(base)
+               : "memory", "m0");
 }
 // Waits for this wave's outstanding global loads (including LDS-bound ones).
 __device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0); }
@@ -45,25 +52,15 @@ __device__ __forceinline__ void lds_barrier() {
   __builtin_amdgcn_s_barrier();
 }
 
-// Element offset of (row, col) in a swizzled 64 x 128 bf16 row tile.
-__device__ __forceinline__ int rowtile_off(int row, int col) {
-  return row * 128 + 8 * ((col >> 3) ^ (row & 15)) + (col & 7);
-}
 
 // Stages rows [0, 64) of a 128-wide bf16 row-major matrix (row stride
-// `stride` elements) into a swizzled row tile with 16 instructions.  Rows at
-// or beyond `len` repeat row len - 1 (in-bounds, finite filler that the chunk
-// algebra multiplies by exact zeros).  `inst0`/`ninst` select which of the 16
-// one-KiB pieces this wave issues.
-__device__ __forceinline__ void stage_rowtile(bf16_t *tile, const bf16_t *src, int64_t stride,
+// `stride` elements) into a swizzled row tile (copies as in tile_index.hpp).
+// Rows at or beyond `len` repeat row len - 1.  `inst0`/`ninst` select which
+// of the 16 copies this wave issues.
+__device__ __forceinline__ void stage_rowtile(lds_t *tile, const bf16_t *src, int64_t stride,
                                               int len, int lane, int inst0, int ninst) {
-  for (int i = inst0; i < inst0 + ninst; ++i) {
-    const int row = 4 * i + (lane >> 4);
-    const int phys = lane & 15;
-    const int logical = phys ^ (row & 15);
-    const int r = row < len ? row : len - 1;
-    copy16_to_lds(src + int64_t(r) * stride + 8 * logical, tile + 512 * i);
-  }
+  for (int i = inst0; i < inst0 + ninst; ++i)
+    dma16(src, uint32_t(rowtile_copy_src(i, lane, len, stride)), tile + 1024 * i);
 }
 
 // A (or B) fragment of rows [16 rt, 16 rt + 16), contraction columns
@@ -86,15 +83,11 @@ __device__ __forceinline__ Frag<bf16_t> rowtile_frag(const bf16_t *tile, int rt,
 // Raw LDS access by byte offset (address space 3, so the compiler emits ds_*
 // instructions and folds constant offsets into them).
 // ---------------------------------------------------------------------------
-typedef __attribute__((address_space(3))) char lds_t;
 typedef short s16x4_t __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) s16x4_t lds_s16x4_t;
 typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
 typedef unsigned u32x4_t __attribute__((ext_vector_type(4)));
 
-__device__ __forceinline__ lds_t *lds_ptr(void *generic_shared) {
-  return (lds_t *)(generic_shared);
-}
 template <typename V> __device__ __forceinline__ V lds_load(const lds_t *p) {
   return *(const __attribute__((address_space(3))) V *)(p);
 }

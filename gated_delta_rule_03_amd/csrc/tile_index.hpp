@@ -1,0 +1,74 @@
+// Index arithmetic of the LDS-staged chunk operands (bf16).  Pure functions,
+// used by the kernels and also compiled for the host, where a check walks
+// every copy, lane and chunk length and confirms that each global byte a
+// staging copy reads lies inside the chunk's rows and that the LDS tiles are
+// covered exactly once.
+//
+// Row tile: 64 token rows x 128 bf16 (256 B per row) in 16 copies of 1 KiB.
+// Copy i moves rows 4 i .. 4 i + 3; lane l moves row 4 i + l / 16 and writes
+// physical 16-byte block l mod 16 of that row, which holds source block
+// (l mod 16) ^ (row mod 16) -- the XOR swizzle that spreads an MFMA
+// fragment's 16 rows over distinct banks.
+//
+// v block: 64 token rows x 32 bf16 (64 B per row) in 4 copies of 1 KiB; copy
+// j moves rows 16 j .. 16 j + 15, lane l moves row 16 j + l / 4, physical
+// block l mod 4, source block (l mod 4) ^ ((row / 4) mod 4).
+//
+// Rows at or past a partial chunk's length repeat row len - 1 (finite,
+// in-bounds filler that the chunk algebra multiplies by exact zeros).
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+namespace gdn {
+
+__host__ __device__ constexpr int clamp_row(int row, int len) { return row < len ? row : len - 1; }
+
+// ---- row tile ----
+// Element offset of logical (row, col) in a swizzled row tile.
+__host__ __device__ constexpr int rowtile_off(int row, int col) {
+  return row * 128 + 8 * ((col >> 3) ^ (row & 15)) + (col & 7);
+}
+__host__ __device__ constexpr int rowtile_copy_row(int i, int lane) { return 4 * i + (lane >> 4); }
+__host__ __device__ constexpr int rowtile_copy_block(int i, int lane) {
+  return (lane & 15) ^ (rowtile_copy_row(i, lane) & 15);
+}
+// Source byte offset (from the chunk's first row) that lane `lane` of copy
+// `i` reads, rows clamped to `len`; `stride` is the row stride in elements.
+__host__ __device__ constexpr int64_t rowtile_copy_src(int i, int lane, int len, int64_t stride) {
+  return 2 * (int64_t(clamp_row(rowtile_copy_row(i, lane), len)) * stride +
+              8 * rowtile_copy_block(i, lane));
+}
+// A full chunk's offset split into a wave-uniform part for copy i ...
+__host__ __device__ constexpr int64_t rowtile_copy_uniform(int i, int64_t stride) {
+  return int64_t(8) * i * stride;  // 4 i rows of 2-byte elements
+}
+// ... and a lane part that depends on the copy only through i mod 4.
+__host__ __device__ constexpr uint32_t rowtile_copy_lane(int i, int lane, int64_t stride) {
+  return uint32_t(2 * (int64_t(lane >> 4) * stride + 8 * rowtile_copy_block(i, lane)));
+}
+
+// ---- v block ----
+__host__ __device__ constexpr int vblock_copy_row(int j, int lane) { return 16 * j + (lane >> 2); }
+__host__ __device__ constexpr int vblock_copy_block(int j, int lane) {
+  return (lane & 3) ^ ((vblock_copy_row(j, lane) >> 2) & 3);
+}
+__host__ __device__ constexpr int64_t vblock_copy_src(int j, int lane, int len, int64_t stride) {
+  return 2 * (int64_t(clamp_row(vblock_copy_row(j, lane), len)) * stride +
+              8 * vblock_copy_block(j, lane));
+}
+
+// Byte offset of logical (row, col) in the staged v block.
+__host__ __device__ constexpr int vtile_byte(int row, int col) {
+  return 2 * (row * 32 + 8 * ((col >> 3) ^ ((row >> 2) & 3)) + (col & 7));
+}
+
+// ---- outputs leaving the staged v block ----
+// Wave w, piece p (0..1): lane l stores row 32 p + l / 2, columns
+// 16 w + 8 (l mod 2) .. + 7 of the block (one 16-byte store).
+__host__ __device__ constexpr int out_piece_row(int p, int lane) { return 32 * p + (lane >> 1); }
+__host__ __device__ constexpr int out_piece_col(int wave, int lane) { return 16 * wave + 8 * (lane & 1); }
+
+}  // namespace gdn

@@ -1,0 +1,121 @@
+// Host check of the LDS-staging index arithmetic in tile_index.hpp (the same
+// functions the staged kernels call).  For every copy, lane, chunk length and
+// a range of row strides it confirms that
+//   * each global byte offset a copy reads lies inside the chunk's rows
+//     [0, len) and inside the 128 (row tile) or 32 (v block) columns it owns;
+//   * a full chunk's split into wave-uniform and lane parts adds up to the
+//     direct offset;
+//   * the bytes every lane writes into LDS are where the kernels' readers
+//     (rowtile_off, vtile_byte) look for them, and each tile is covered once;
+//   * the output pieces leaving the v block cover its 64 x 32 outputs once.
+// Prints "OK" and exits 0, or names the first violation and exits 1.
+#include <cstdio>
+#include <vector>
+
+#include "tile_index.hpp"
+
+using namespace gdn;
+
+static int fails = 0;
+#define CHECK(cond, ...)                    \
+  do {                                      \
+    if (!(cond)) {                          \
+      if (fails < 10) {                     \
+        std::printf("FAIL %s: ", #cond);    \
+        std::printf(__VA_ARGS__);           \
+        std::printf("\n");                  \
+      }                                     \
+      ++fails;                              \
+    }                                       \
+  } while (0)
+
+int main() {
+  const long long strides[] = {128, 256, 384, 2048, 4096, 128 * 64};
+  for (long long s : strides) {
+    // ---- row tile: 16 copies x 64 lanes ----
+    for (int len = 1; len <= 64; ++len) {
+      for (int i = 0; i < 16; ++i)
+        for (int l = 0; l < 64; ++l) {
+          const long long off = rowtile_copy_src(i, l, len, s);
+          CHECK(off % 16 == 0, "row tile copy %d lane %d: offset %lld not 16-byte aligned", i, l, off);
+          const long long e = off / 2, row = e / s, col = e % s;
+          CHECK(row >= 0 && row < len, "row tile copy %d lane %d len %d stride %lld reads row %lld",
+                i, l, len, s, row);
+          CHECK(col >= 0 && col + 8 <= 128, "row tile copy %d lane %d reads columns %lld..+7", i, l, col);
+          if (len == 64) {
+            const long long split = rowtile_copy_uniform(i, s) + rowtile_copy_lane(i & 3, l, s);
+            CHECK(split == off, "row tile copy %d lane %d stride %lld: uniform + lane = %lld, direct %lld",
+                  i, l, s, split, off);
+          }
+        }
+    }
+    // ---- v block: 4 copies x 64 lanes ----
+    for (int len = 1; len <= 64; ++len)
+      for (int j = 0; j < 4; ++j)
+        for (int l = 0; l < 64; ++l) {
+          const long long off = vblock_copy_src(j, l, len, s);
+          CHECK(off % 16 == 0, "v copy %d lane %d: offset %lld not aligned", j, l, off);
+          const long long e = off / 2, row = e / s, col = e % s;
+          CHECK(row >= 0 && row < len, "v copy %d lane %d len %d reads row %lld", j, l, len, row);
+          CHECK(col >= 0 && col + 8 <= 32, "v copy %d lane %d reads columns %lld..+7", j, l, col);
+        }
+  }
+
+  // ---- LDS placement: copy i, lane l writes bytes [1024 i + 16 l, +16) ----
+  {
+    std::vector<int> seen(64 * 128, 0);
+    for (int i = 0; i < 16; ++i)
+      for (int l = 0; l < 64; ++l) {
+        const int row = rowtile_copy_row(i, l), col = 8 * rowtile_copy_block(i, l);
+        const int at = 2 * rowtile_off(row, col);
+        CHECK(at == 1024 * i + 16 * l, "row tile (%d,%d) read at byte %d, written at %d", row, col, at,
+              1024 * i + 16 * l);
+        for (int c = 0; c < 8; ++c) {
+          CHECK(2 * rowtile_off(row, col + c) == at + 2 * c, "row tile (%d,%d) not contiguous", row, col + c);
+          seen[row * 128 + col + c]++;
+        }
+      }
+    for (int x = 0; x < 64 * 128; ++x) CHECK(seen[x] == 1, "row tile element %d copied %d times", x, seen[x]);
+  }
+  {
+    std::vector<int> seen(64 * 32, 0);
+    for (int j = 0; j < 4; ++j)
+      for (int l = 0; l < 64; ++l) {
+        const int row = vblock_copy_row(j, l), col = 8 * vblock_copy_block(j, l);
+        const int at = vtile_byte(row, col);
+        CHECK(at == 1024 * j + 16 * l, "v block (%d,%d) read at byte %d, written at %d", row, col, at,
+              1024 * j + 16 * l);
+        for (int c = 0; c < 8; ++c) {
+          CHECK(vtile_byte(row, col + c) == at + 2 * c, "v block (%d,%d) not contiguous", row, col + c);
+          seen[row * 32 + col + c]++;
+        }
+      }
+    for (int x = 0; x < 64 * 32; ++x) CHECK(seen[x] == 1, "v block element %d copied %d times", x, seen[x]);
+  }
+
+  // ---- outputs: 2 waves x 2 pieces x 64 lanes, 8 columns each ----
+  {
+    std::vector<int> seen(64 * 32, 0);
+    for (int w = 0; w < 2; ++w)
+      for (int p = 0; p < 2; ++p)
+        for (int l = 0; l < 64; ++l) {
+          const int row = out_piece_row(p, l), col = out_piece_col(w, l);
+          CHECK(row < 64 && col + 8 <= 32 && col % 8 == 0, "output piece %d lane %d at (%d,%d)", p, l, row, col);
+          const int base = vtile_byte(out_piece_row(0, l), out_piece_col(w, l));
+          CHECK(vtile_byte(row, col) == base + 2048 * p, "output piece %d lane %d LDS offset", p, l);
+          for (int c = 0; c < 8; ++c) {
+            CHECK(vtile_byte(row, col + c) == vtile_byte(row, col) + 2 * c, "output (%d,%d) not contiguous",
+                  row, col + c);
+            seen[row * 32 + col + c]++;
+          }
+        }
+    for (int x = 0; x < 64 * 32; ++x) CHECK(seen[x] == 1, "output element %d stored %d times", x, seen[x]);
+  }
+
+  if (fails) {
+    std::printf("%d violations\n", fails);
+    return 1;
+  }
+  std::printf("OK\n");
+  return 0;
+}

@@ -40,14 +40,15 @@ def test_version_and_status_strings(lib):
 
 
 def test_workspace_query(lib):
-    # one entry per (chunk slot, value head): 16 bf16 fragments of 1 KiB + 64 fp32 gates
-    entry = 16 * 1024 + 256
+    # one entry per (chunk slot, value head): 16 fragments of 512 elements
+    # (1 KiB in bf16, 2 KiB in fp32) + a 1 KiB gate block (gamma_t, s_t)
+    entry = 16 * 1024 + 1024
     w = gdn.chunk_fwd_workspace_bytes(4, 4096, 16, 16, 128, 128, gdn.GDN_BF16, 64, 0)
     assert w >= 4 * 64 * 16 * entry
     packed = gdn.chunk_fwd_workspace_bytes(1, 1000, 2, 4, 128, 128, gdn.GDN_BF16, 64, 5)
     assert packed >= (16 + 5) * 4 * entry
     f32 = gdn.chunk_fwd_workspace_bytes(1, 64, 1, 1, 16, 16, gdn.GDN_F32, 16, 0)
-    assert f32 >= 4 * (16 * 2048 + 256)
+    assert f32 >= 4 * (16 * 2048 + 1024)
     assert gdn.chunk_fwd_workspace_bytes(1, 64, 1, 1, 48, 64, gdn.GDN_BF16, 64, 0) == 0
     assert gdn.chunk_fwd_workspace_bytes(1, 64, 1, 1, 64, 64, gdn.GDN_BF16, 48, 0) == 0
     assert gdn.chunk_fwd_workspace_bytes(1, 64, 1, 1, 64, 64, 7, 64, 0) == 0
