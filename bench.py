@@ -20,10 +20,18 @@ kernel per call, so its event time is its launch duration); ``chunk_roofline``
 gives the chunked forward's fractions of the HBM and bf16 MFMA peaks.
 ``cpu_baseline`` is the float64 oracle timed on this host's cores over the
 whole prefill batch.
+
+``roofline.traffic`` is the decode kernel's HBM bytes per launch from the
+rocprofv3 FETCH_SIZE and WRITE_SIZE counters (profiles/decode_kernel.traffic.json),
+each scaled by what the counter reads for a plain 1 GiB read + 1 GiB write
+elementwise kernel; it is null when the decode source has changed since the
+counters were taken.  ``--calibrate-copy`` adds that plain kernel to the run
+(and reports its bandwidth) so a counter pass over this script sees both.
 """
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import os
 import statistics
@@ -47,6 +55,24 @@ PREFILL_FLOPS_PER_TOKEN_UNIT = 4 * 64 * 128 + 3 * 64 * 128 + 6 * 128 * 128
 # (4 x 128 x 2 bytes), alpha, beta (8 bytes).
 DECODE_BYTES_PER_UNIT = 2 * 128 * 128 * 4 + 4 * 128 * 2 + 8
 DECODE_FLOPS_PER_UNIT = 6 * 128 * 128
+
+
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_kernel.traffic.json")
+DECODE_SOURCE = os.path.join(ROOT, "gated_delta_rule_03_amd", "csrc", "decode.hip")
+
+
+def decode_traffic():
+    """Counter-measured HBM bytes per decode launch, if taken on this source."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            rec = json.load(f)
+        with open(DECODE_SOURCE, "rb") as f:
+            sha = hashlib.sha256(f.read()).hexdigest()
+    except (OSError, ValueError):
+        return None
+    if rec.get("source_sha256") != sha:
+        return None
+    return rec.get("hbm_bytes_per_launch")
 
 
 def log(msg):
@@ -80,6 +106,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-flush", action="store_true", help="keep caches warm between calls")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="also run a plain 1 GiB read + 1 GiB write kernel (counter calibration)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
@@ -164,6 +192,25 @@ def main():
     dec_s = statistics.median(dec_ms) * 1e-3
     dec_mean_s = statistics.fmean(dec_ms) * 1e-3
 
+    copy_gbps = None
+    if args.calibrate_copy:
+        log("bench: calibration copy, 1 GiB read + 1 GiB write")
+        c_src = torch.ones(256 << 20, dtype=torch.float32, device=dev)
+        c_dst = torch.empty_like(c_src)
+        cms = []
+        for _ in range(3):
+            if flush is not None:
+                flush.fill_(3)
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            torch.mul(c_src, 1.0, out=c_dst)
+            e1.record(stream)
+            torch.cuda.synchronize()
+            cms.append(e0.elapsed_time(e1))
+        copy_gbps = 2 * c_src.numel() * 4 / (statistics.median(cms) * 1e-3) / 1e9
+        del c_src, c_dst
+
     tokens = B * T
     units = B * H
     prefill_bytes = tokens * H * PREFILL_BYTES_PER_TOKEN_UNIT + units * D * D * 4
@@ -209,7 +256,7 @@ def main():
             "peak": HBM_PEAK / 1e9,
             "unit": "GB/s",
             "frac": dec_bytes / dec_mean_s / HBM_PEAK,
-            "traffic": None,
+            "traffic": decode_traffic(),
         },
         "chunk_roofline": {
             "algorithmic_bytes": prefill_bytes,
@@ -221,6 +268,8 @@ def main():
         },
         "wall_s_timed_region": wall,
     }
+    if copy_gbps is not None:
+        result["calibration_copy_GBps"] = copy_gbps
     if not args.no_cpu_baseline:
         log("bench: cpu baseline (float64 oracle on host cores)")
         result["cpu_baseline"] = cpu_baseline(wp)

@@ -9,11 +9,14 @@
 // The step reads and writes the state once: about rd numbers each way
 // ("Attention as Matrix Algebra", section 9), so it is bound by HBM bandwidth.
 //
-// Layout: one 256-thread block per (sequence, value head).  Thread tid owns
-// columns 4 (tid & 31) .. +3 of rows (tid >> 5) + 8 i: each wave instruction
-// moves two whole 512-byte rows (coalesced 16-byte accesses).  Column sums
-// over d_k reduce across the two row groups of a wave with a lane swap and
-// across the four waves through LDS.
+// Layout: one 512-thread block per (sequence, value head).  Thread tid owns
+// columns 4 (tid & 31) .. +3 of rows (tid >> 5) + 16 i: each wave instruction
+// moves two whole 512-byte rows (coalesced 16-byte accesses).  The state is
+// read and written with nontemporal accesses: it streams through once, and
+// keeping it out of the caches' normal replacement path is worth about a
+// quarter more achieved bandwidth here than plain loads and stores.  k and q
+// are staged once in LDS.  Column sums over d_k reduce across the two row
+// groups of a wave with a lane swap and across the eight waves through LDS.
 #include "launch.hpp"
 
 namespace gdn {
@@ -27,8 +30,12 @@ struct DecodeArgs {
   int H_qk, H_v, d_k, d_v, group;
 };
 
+constexpr int kDecodeThreads = 512;
+constexpr int kDecodeRowGroups = kDecodeThreads / 32;  // 16
+constexpr int kDecodeRows = 128 / kDecodeRowGroups;    // rows per thread (d_k <= 128)
+
 template <typename T>
-__global__ __launch_bounds__(256) void decode_kernel(DecodeArgs<T> a) {
+__global__ __launch_bounds__(kDecodeThreads) void decode_kernel(DecodeArgs<T> a) {
   const int u = blockIdx.x;  // b * H_v + h
   const int b = u / a.H_v, h = u - b * a.H_v, hq = h / a.group;
   const int tid = threadIdx.x, cg = tid & 31, rg = tid >> 5, wave = tid >> 6;
@@ -38,78 +45,81 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs<T> a) {
   const T *kp = a.k + (int64_t(b) * a.H_qk + hq) * a.d_k;
   const T *qp = a.q + (int64_t(b) * a.H_qk + hq) * a.d_k;
 
-  float4 s[16];
-  float kk[16], qq[16];
+  f32x4_t s[kDecodeRows];
 #pragma unroll
-  for (int i = 0; i < 16; ++i) {
-    const int r = rg + 8 * i;
-    const bool ok = r < a.d_k;
-    s[i] = (ok && col_ok) ? *reinterpret_cast<const float4 *>(S + int64_t(r) * a.d_v + 4 * cg)
-                          : make_float4(0.f, 0.f, 0.f, 0.f);
-    kk[i] = ok ? to_f32(kp[r]) : 0.0f;
-    qq[i] = ok ? to_f32(qp[r]) : 0.0f;
+  for (int i = 0; i < kDecodeRows; ++i) {
+    const int r = rg + kDecodeRowGroups * i;
+    s[i] = (r < a.d_k && col_ok)
+               ? __builtin_nontemporal_load(reinterpret_cast<const f32x4_t *>(S + int64_t(r) * a.d_v + 4 * cg))
+               : zero4();
   }
+  __shared__ float skq[2][128];
+  if (tid < a.d_k) skq[0][tid] = to_f32(kp[tid]);
+  else if (tid >= 128 && tid - 128 < a.d_k) skq[1][tid - 128] = to_f32(qp[tid - 128]);
+  __syncthreads();
 
-  float4 ak = make_float4(0.f, 0.f, 0.f, 0.f), bq = ak;
-  float qk = 0.0f;
+  float kk[kDecodeRows];
+  f32x4_t ak = zero4(), bq = zero4();
 #pragma unroll
-  for (int i = 0; i < 16; ++i) {
-    ak.x += s[i].x * kk[i]; ak.y += s[i].y * kk[i]; ak.z += s[i].z * kk[i]; ak.w += s[i].w * kk[i];
-    bq.x += s[i].x * qq[i]; bq.y += s[i].y * qq[i]; bq.z += s[i].z * qq[i]; bq.w += s[i].w * qq[i];
-    qk += kk[i] * qq[i];
+  for (int i = 0; i < kDecodeRows; ++i) {
+    const int r = rg + kDecodeRowGroups * i;
+    kk[i] = r < a.d_k ? skq[0][r] : 0.0f;
+    const float qq = r < a.d_k ? skq[1][r] : 0.0f;
+    ak += s[i] * kk[i];
+    bq += s[i] * qq;
+  }
+  // q^T k over d_k, in wave 0
+  float qk = 0.0f;
+  if (wave == 0) {
+    if (tid < a.d_k) qk = skq[0][tid] * skq[1][tid];
+    if (tid + 64 < a.d_k) qk += skq[0][tid + 64] * skq[1][tid + 64];
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1) qk += __shfl_xor(qk, m);
   }
   // reduce the two row groups of this wave (lanes l and l ^ 32)
-  ak.x += __shfl_xor(ak.x, 32); ak.y += __shfl_xor(ak.y, 32);
-  ak.z += __shfl_xor(ak.z, 32); ak.w += __shfl_xor(ak.w, 32);
-  bq.x += __shfl_xor(bq.x, 32); bq.y += __shfl_xor(bq.y, 32);
-  bq.z += __shfl_xor(bq.z, 32); bq.w += __shfl_xor(bq.w, 32);
-  qk += __shfl_xor(qk, 32);
-
-  __shared__ float4 red_a[4][32], red_b[4][32];
-  __shared__ float red_qk[4];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    ak[e] += __shfl_xor(ak[e], 32);
+    bq[e] += __shfl_xor(bq[e], 32);
+  }
+  __shared__ f32x4_t red_a[kDecodeThreads / 64][32], red_b[kDecodeThreads / 64][32];
+  __shared__ float red_qk;
   if ((tid & 32) == 0) {
     red_a[wave][cg] = ak;
     red_b[wave][cg] = bq;
   }
-  if ((tid & 63) == 0) red_qk[wave] = qk;
+  if (tid == 0) red_qk = qk;
   __syncthreads();
-  ak = red_a[0][cg]; bq = red_b[0][cg]; qk = red_qk[0];
+  ak = red_a[0][cg];
+  bq = red_b[0][cg];
+  qk = red_qk;
 #pragma unroll
-  for (int w = 1; w < 4; ++w) {
-    const float4 x = red_a[w][cg], y = red_b[w][cg];
-    ak.x += x.x; ak.y += x.y; ak.z += x.z; ak.w += x.w;
-    bq.x += y.x; bq.y += y.y; bq.z += y.z; bq.w += y.w;
-    qk += red_qk[w];
+  for (int w = 1; w < kDecodeThreads / 64; ++w) {
+    ak += red_a[w][cg];
+    bq += red_b[w][cg];
   }
 
   const int64_t vi = (int64_t(b) * a.H_v + h);
   const float al = a.alpha[vi], be = a.beta[vi];
-  float4 vv = make_float4(0.f, 0.f, 0.f, 0.f);
-  if (col_ok) vv = load4_f32(a.v + vi * a.d_v + 4 * cg);
-  float4 uu;
-  uu.x = be * (vv.x - al * ak.x);
-  uu.y = be * (vv.y - al * ak.y);
-  uu.z = be * (vv.z - al * ak.z);
-  uu.w = be * (vv.w - al * ak.w);
+  f32x4_t vv = zero4();
+  if (col_ok) {
+    const float4 x = load4_f32(a.v + vi * a.d_v + 4 * cg);
+    vv = f32x4_t{x.x, x.y, x.z, x.w};
+  }
+  const f32x4_t uu = be * (vv - al * ak);
 
   if (rg == 0 && col_ok) {
     T *op = a.o + vi * a.d_v + 4 * cg;
-    op[0] = from_f32<T>(al * bq.x + qk * uu.x);
-    op[1] = from_f32<T>(al * bq.y + qk * uu.y);
-    op[2] = from_f32<T>(al * bq.z + qk * uu.z);
-    op[3] = from_f32<T>(al * bq.w + qk * uu.w);
+    const f32x4_t ov = al * bq + qk * uu;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) op[e] = from_f32<T>(ov[e]);
   }
 #pragma unroll
-  for (int i = 0; i < 16; ++i) {
-    const int r = rg + 8 * i;
-    if (r < a.d_k && col_ok) {
-      float4 n;
-      n.x = al * s[i].x + kk[i] * uu.x;
-      n.y = al * s[i].y + kk[i] * uu.y;
-      n.z = al * s[i].z + kk[i] * uu.z;
-      n.w = al * s[i].w + kk[i] * uu.w;
-      *reinterpret_cast<float4 *>(S + int64_t(r) * a.d_v + 4 * cg) = n;
-    }
+  for (int i = 0; i < kDecodeRows; ++i) {
+    const int r = rg + kDecodeRowGroups * i;
+    if (r < a.d_k && col_ok)
+      __builtin_nontemporal_store(al * s[i] + kk[i] * uu,
+                                  reinterpret_cast<f32x4_t *>(S + int64_t(r) * a.d_v + 4 * cg));
   }
 }
 
@@ -130,7 +140,7 @@ static hipError_t launch_decode_t(const Problem &p, float *state, hipStream_t st
   a.group = p.H_v / p.H_qk;
   const int64_t blocks = int64_t(p.B) * p.H_v;
   if (blocks == 0) return hipSuccess;
-  hipLaunchKernelGGL(decode_kernel<T>, dim3(unsigned(blocks)), dim3(256), 0, st, a);
+  hipLaunchKernelGGL(decode_kernel<T>, dim3(unsigned(blocks)), dim3(kDecodeThreads), 0, st, a);
   return hipGetLastError();
 }
 
