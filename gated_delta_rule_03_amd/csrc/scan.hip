@@ -254,9 +254,9 @@ __global__ __launch_bounds__(128) void scan_kernel_staged(ScanArgs<bf16_t> a) {
   // transposed v tile rt (rows 16 rt + 4 g + a / 4, columns 16 w + 4 (a mod 4)):
   // offset = 1024 rt + v_off.
   const int v_off = vtile_byte(4 * g + (r0 >> 2), 16 * wave + 4 * (r0 & 3));
-  // outputs in accumulator layout (row 16 rt + 4 g + e, column 16 w + r0):
-  // offset = 1024 rt + 64 e + o_woff.
-  const int o_woff = vtile_byte(4 * g, 16 * wave + r0);
+  // outputs as computed (transposed tiles: token row 16 rt + r0, columns
+  // 16 w + 4 g .. + 3, one 8-byte piece): offset = 1024 rt + o_woff.
+  const int o_woff = vtile_byte(out_acc_row(0, lane), out_acc_col(wave, lane));
   // outputs leaving in 16-byte pieces: piece p of 2 covers row 32 p + lane / 2,
   // columns 16 w + 8 (lane mod 2) .. + 7.
   const int o_roff = vtile_byte(out_piece_row(0, lane), out_piece_col(wave, lane));
@@ -363,10 +363,12 @@ __global__ __launch_bounds__(128) void scan_kernel_staged(ScanArgs<bf16_t> a) {
     // gate factors of this lane's rows (16 rt + 4 g + e) and of the last slot
     const float gamma_C = lds_load<float>(st + kStG + 252);
     f32x4_t gam[4], sc[4];
+    float gam_tok[4];  // gamma of token 16 rt + r0 (the transposed output tiles)
 #pragma unroll
     for (int rt = 0; rt < 4; ++rt) {
       gam[rt] = lds_load<f32x4_t>(st + kStG + 64 * rt + 16 * g);
       sc[rt] = lds_load<f32x4_t>(st + kStG + 256 + 64 * rt + 16 * g);
+      gam_tok[rt] = lds_load<float>(st + kStG + 4 * out_acc_row(rt, lane));
     }
 
     // Operands are read into registers one phase ahead of their use, so each
@@ -453,19 +455,20 @@ __global__ __launch_bounds__(128) void scan_kernel_staged(ScanArgs<bf16_t> a) {
       S[rm] = acc;
     }
 
-    // O = gamma (Q S) + P U (Sf still holds the chunk-start state), written
-    // over this wave's v columns
+    // O = gamma (Q S) + P U (Sf still holds the chunk-start state), computed
+    // as O^T = S^T (gamma Q^T) + U^T P^T: with the kappa fragment convention
+    // Sf and Uf serve as A operands and the q rows and P fragments as B
+    // operands unchanged, and each lane ends with four consecutive columns of
+    // one token row, written over this wave's v columns in one 8-byte store.
 #pragma unroll
     for (int rt = 0; rt < 4; ++rt) {
       f32x4_t oq = zero4();
 #pragma unroll
-      for (int kk = 0; kk < 4; ++kk) oq = mfma(qf[kk][rt], Sf[kk], oq);
-      f32x4_t acc = gam[rt] * oq;
+      for (int kk = 0; kk < 4; ++kk) oq = mfma(Sf[kk], qf[kk][rt], oq);
+      f32x4_t acc = gam_tok[rt] * oq;
 #pragma unroll
-      for (int kk = 0; kk < 2; ++kk) acc = mfma(pf[rt * 2 + kk], Uf[kk], acc);
-#pragma unroll
-      for (int e = 0; e < 4; ++e)
-        lds_store<bf16_t>(st + kStV + 1024 * rt + 64 * e + o_woff, from_f32<bf16_t>(acc[e]));
+      for (int kk = 0; kk < 2; ++kk) acc = mfma(Uf[kk], pf[rt * 2 + kk], acc);
+      lds_store<bf16x4_t>(st + kStV + 1024 * rt + o_woff, __builtin_convertvector(acc, bf16x4_t));
     }
     // the next chunk's stage must be complete and this stage free for reuse
     wait_all_but_newest_stage();

@@ -65,6 +65,12 @@ __host__ __device__ constexpr int vtile_byte(int row, int col) {
   return 2 * (row * 32 + 8 * ((col >> 3) ^ ((row >> 2) & 3)) + (col & 7));
 }
 
+// ---- outputs as the MFMA leaves them (transposed tiles) ----
+// Output tile rt, lane l: token row 16 rt + l mod 16, columns
+// 16 w + 4 (l / 16) .. + 3 of wave w's half of the block.
+__host__ __device__ constexpr int out_acc_row(int rt, int lane) { return 16 * rt + (lane & 15); }
+__host__ __device__ constexpr int out_acc_col(int wave, int lane) { return 16 * wave + 4 * (lane >> 4); }
+
 // ---- outputs leaving the staged v block ----
 // Wave w, piece p (0..1): lane l stores row 32 p + l / 2, columns
 // 16 w + 8 (l mod 2) .. + 7 of the block (one 16-byte store).

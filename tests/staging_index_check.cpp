@@ -93,6 +93,24 @@ int main() {
     for (int x = 0; x < 64 * 32; ++x) CHECK(seen[x] == 1, "v block element %d copied %d times", x, seen[x]);
   }
 
+  // ---- outputs written from the transposed MFMA tiles: 2 waves x 4 tiles x 64 lanes, 4 columns ----
+  {
+    std::vector<int> seen(64 * 32, 0);
+    for (int w = 0; w < 2; ++w)
+      for (int rt = 0; rt < 4; ++rt)
+        for (int l = 0; l < 64; ++l) {
+          const int row = out_acc_row(rt, l), col = out_acc_col(w, l);
+          CHECK(row < 64 && col + 4 <= 32 && col % 4 == 0, "output tile %d lane %d at (%d,%d)", rt, l, row, col);
+          const int base = vtile_byte(out_acc_row(0, l), out_acc_col(w, l));
+          CHECK(vtile_byte(row, col) == base + 1024 * rt, "output tile %d lane %d LDS offset", rt, l);
+          for (int c = 0; c < 4; ++c) {
+            CHECK(vtile_byte(row, col + c) == vtile_byte(row, col) + 2 * c, "output (%d,%d) not contiguous", row, col + c);
+            seen[row * 32 + col + c]++;
+          }
+        }
+    for (int x = 0; x < 64 * 32; ++x) CHECK(seen[x] == 1, "output element %d written %d times", x, seen[x]);
+  }
+
   // ---- outputs: 2 waves x 2 pieces x 64 lanes, 8 columns each ----
   {
     std::vector<int> seen(64 * 32, 0);
