@@ -201,8 +201,8 @@ __global__ __launch_bounds__(64) void scan_kernel(ScanArgs<T> a) {
 // staged tiles through transposed reads (ds_read_b64_tr_b16).  Every LDS and
 // global offset a lane uses is computed once; per chunk only wave-uniform
 // bases change.  The chunk's outputs are written over the wave's own columns
-// of the staged v block and leave in 16-byte stores.  Rows past a partial
-// chunk repeat its last row (finite filler that only meets exact zeros).
+// of the staged v block and leave in 16-byte stores.  The k / q and v copies
+// are bounds-checked buffer loads: rows past a partial chunk read as zeros.
 // ---------------------------------------------------------------------------
 constexpr int kStK = 0;        // 64 x 128 bf16 row tile
 constexpr int kStQ = 16384;    // 64 x 128 bf16 row tile
@@ -279,41 +279,37 @@ __global__ __launch_bounds__(128) void scan_kernel_staged(ScanArgs<bf16_t> a) {
   const int n_chunks = max(0, min((end - start + C - 1) / C, a.geo.n_slots - c_first));
   const int64_t qk_stride = int64_t(a.H_qk) * 128;
   const int64_t v_stride = int64_t(a.H_v) * a.d_v;
+  const uint32_t kq_row_bytes = uint32_t(2 * qk_stride), v_row_bytes = uint32_t(2 * v_stride);
   const int64_t ebytes = entry_bytes<bf16_t>();
   const char *kq_src = reinterpret_cast<const char *>(wave == 0 ? a.k : a.q) + int64_t(hq) * 256;
   const char *v_src = reinterpret_cast<const char *>(a.v) + (int64_t(h) * a.d_v + 32 * cb) * 2;
 
-  // lane parts of a full chunk's global offsets (tile_index.hpp): row-tile
-  // copy i adds the wave-uniform rowtile_copy_uniform(i) to kq_goff[i mod 4]
-  uint32_t kq_goff[4];
+  // Per-lane byte offsets of every copy of a full chunk (tile_index.hpp),
+  // relative to the chunk's first row.  The k / q and v copies go through a
+  // buffer resource whose size ends at the chunk's last row, so rows past a
+  // partial chunk read as zeros (exact zeros that the chunk algebra only
+  // multiplies by zero) and no copy can leave the sequence.
+  uint32_t kq_voff[16];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) kq_goff[i] = rowtile_copy_lane(i, lane, qk_stride);
-  uint32_t v_goff[2];
+  for (int i = 0; i < 16; ++i) kq_voff[i] = uint32_t(rowtile_copy_src(i, lane, 64, qk_stride));
+  uint32_t v_voff[2];
 #pragma unroll
-  for (int i = 0; i < 2; ++i) v_goff[i] = uint32_t(vblock_copy_src(2 * wave + i, lane, 64, v_stride));
+  for (int i = 0; i < 2; ++i) v_voff[i] = uint32_t(vblock_copy_src(2 * wave + i, lane, 64, v_stride));
 
   auto stage = [&](int cc, char *base_mem) {
     const int tok0 = start + cc * C;
     const int len = min(C, end - tok0);
     lds_t *const base = lds_ptr(base_mem);
     const char *entry = a.entries + (int64_t(c_first + cc) * a.H_v + h) * ebytes;
-    const char *kq = kq_src + int64_t(tok0) * qk_stride * 2;
-    const char *vv = v_src + int64_t(tok0) * v_stride * 2;
+    const i32x4_t kq_res = buffer_rsrc(kq_src + int64_t(tok0) * kq_row_bytes,
+                                       rowtile_valid_bytes(len, kq_row_bytes));
+    const i32x4_t v_res = buffer_rsrc(v_src + int64_t(tok0) * v_row_bytes,
+                                      vblock_valid_bytes(len, v_row_bytes));
     lds_t *const tile = base + (wave == 0 ? kStK : kStQ);
-    if (len == 64) {
 #pragma unroll
-      for (int i = 0; i < 16; ++i)
-        dma16(kq + rowtile_copy_uniform(i, qk_stride), kq_goff[i & 3], tile + 1024 * i);
+    for (int i = 0; i < 16; ++i) dma16_buf(kq_res, kq_voff[i], tile + 1024 * i);
 #pragma unroll
-      for (int i = 0; i < 2; ++i) dma16(vv, v_goff[i], base + kStV + 2048 * wave + 1024 * i);
-    } else {
-      // partial chunk: rows at or past len repeat row len - 1
-      for (int i = 0; i < 16; ++i)
-        dma16(kq, uint32_t(rowtile_copy_src(i, lane, len, qk_stride)), tile + 1024 * i);
-      for (int i = 0; i < 2; ++i)
-        dma16(vv, uint32_t(vblock_copy_src(2 * wave + i, lane, len, v_stride)),
-              base + kStV + 2048 * wave + 1024 * i);
-    }
+    for (int i = 0; i < 2; ++i) dma16_buf(v_res, v_voff[i], base + kStV + 2048 * wave + 1024 * i);
     const char *f = entry + 8192 * wave;
 #pragma unroll
     for (int i = 0; i < 8; ++i) dma16(f + 1024 * i, 16 * lane, base + kStF + 8192 * wave + 1024 * i);
@@ -326,9 +322,9 @@ __global__ __launch_bounds__(128) void scan_kernel_staged(ScanArgs<bf16_t> a) {
     else
       wait_vmem_upto<kStageLoadsW1>();
   };
-  // The outputs of chunk cc sit over this wave's v columns of stage cc % 3;
-  // they leave in two 16-byte pieces per lane.
-  // (cc = -1 stores nothing: its row count is 0)
+  // The outputs of chunk cc sit over this wave's v columns of its stage; they
+  // leave in two 16-byte pieces per lane.  (cc = -1 stores nothing: its row
+  // count is 0.)
   auto store_outputs = [&](int cc, const char *stage_mem) {
     const int tok0 = start + cc * C;
     const int len = cc >= 0 ? min(C, end - tok0) : 0;
@@ -360,10 +356,11 @@ __global__ __launch_bounds__(128) void scan_kernel_staged(ScanArgs<bf16_t> a) {
 
     lds_t *const st = lds_ptr(cur_mem);
 
-    // gate factors of this lane's rows (16 rt + 4 g + e) and of the last slot
+    // gate factors: rows 16 rt + 4 g + e of this lane's column, the token of
+    // this lane's transposed output tiles, and the chunk's last slot
     const float gamma_C = lds_load<float>(st + kStG + 252);
     f32x4_t gam[4], sc[4];
-    float gam_tok[4];  // gamma of token 16 rt + r0 (the transposed output tiles)
+    float gam_tok[4];
 #pragma unroll
     for (int rt = 0; rt < 4; ++rt) {
       gam[rt] = lds_load<f32x4_t>(st + kStG + 64 * rt + 16 * g);
@@ -372,15 +369,17 @@ __global__ __launch_bounds__(128) void scan_kernel_staged(ScanArgs<bf16_t> a) {
     }
 
     // Operands are read into registers one phase ahead of their use, so each
-    // phase's MFMAs do not wait on their own LDS reads.
+    // phase's MFMAs do not wait on their own LDS reads.  Row fragments are two
+    // 8-byte reads each, kept single (not paired across tiles) so that they
+    // land in the fragment's registers directly.
     Frag<bf16_t> kf[4][4];  // k rows: [contraction block][row tile]
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk)
 #pragma unroll
       for (int rt = 0; rt < 4; ++rt) {
         const lds_t *pk = st + kStK + 4096 * rt;
-        kf[kk][rt] = frag_cat(lds_load<bf16x4_t>(pk + kq_off[kk][0]),
-                              lds_load<bf16x4_t>(pk + kq_off[kk][1]));
+        kf[kk][rt] = frag_cat(lds_load_single<bf16x4_t>(pk + kq_off[kk][0]),
+                              lds_load_single<bf16x4_t>(pk + kq_off[kk][1]));
       }
     bf16x4_t vt[4];  // v, transposed: four rows of this lane's column
 #pragma unroll
@@ -396,38 +395,33 @@ __global__ __launch_bounds__(128) void scan_kernel_staged(ScanArgs<bf16_t> a) {
     // Y = K S
     f32x4_t Y[4];
 #pragma unroll
-    for (int rt = 0; rt < 4; ++rt) Y[rt] = zero4();
-#pragma unroll
     for (int kk = 0; kk < 4; ++kk)
 #pragma unroll
-      for (int rt = 0; rt < 4; ++rt) Y[rt] = mfma(kf[kk][rt], Sf[kk], Y[rt]);
+      for (int rt = 0; rt < 4; ++rt) Y[rt] = mfma(kf[kk][rt], Sf[kk], kk == 0 ? zero4() : Y[rt]);
 
-    // next: q rows, P and K^T fragments
+    // next: q rows
     Frag<bf16_t> qf[4][4];
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk)
 #pragma unroll
       for (int rt = 0; rt < 4; ++rt) {
         const lds_t *pq = st + kStQ + 4096 * rt;
-        qf[kk][rt] = frag_cat(lds_load<bf16x4_t>(pq + kq_off[kk][0]),
-                              lds_load<bf16x4_t>(pq + kq_off[kk][1]));
+        qf[kk][rt] = frag_cat(lds_load_single<bf16x4_t>(pq + kq_off[kk][0]),
+                              lds_load_single<bf16x4_t>(pq + kq_off[kk][1]));
       }
 
     // X = V - gamma Y, then U = T X
     f32x4_t X[4];
 #pragma unroll
-    for (int rt = 0; rt < 4; ++rt)
-#pragma unroll
-      for (int e = 0; e < 4; ++e) X[rt][e] = static_cast<float>(vt[rt][e]) - gam[rt][e] * Y[rt][e];
-    Frag<bf16_t> Xf[2] = {frag_from_acc<bf16_t>(X[0], X[1]), frag_from_acc<bf16_t>(X[2], X[3])};
+    for (int rt = 0; rt < 4; ++rt) X[rt] = __builtin_convertvector(vt[rt], f32x4_t) - gam[rt] * Y[rt];
+    const Frag<bf16_t> Xf[2] = {frag_from_acc<bf16_t>(X[0], X[1]), frag_from_acc<bf16_t>(X[2], X[3])};
     f32x4_t Ua[4];
 #pragma unroll
-    for (int rt = 0; rt < 4; ++rt) {
-      Ua[rt] = zero4();
+    for (int rt = 0; rt < 4; ++rt)
 #pragma unroll
-      for (int kk = 0; kk < 2; ++kk) Ua[rt] = mfma(tf[rt * 2 + kk], Xf[kk], Ua[rt]);
-    }
+      for (int kk = 0; kk < 2; ++kk) Ua[rt] = mfma(tf[rt * 2 + kk], Xf[kk], kk == 0 ? zero4() : Ua[rt]);
 
+    // next: K^T fragments (transposed reads of the k tile) and P
     Frag<bf16_t> ktf[8][2];
 #pragma unroll
     for (int rm = 0; rm < 8; ++rm)
@@ -440,13 +434,14 @@ __global__ __launch_bounds__(128) void scan_kernel_staged(ScanArgs<bf16_t> a) {
 #pragma unroll
     for (int i = 0; i < 8; ++i) pf[i].v = lds_load<bf16x8_t>(st + kStF + 8192 + 1024 * i + 16 * lane);
 
-    Frag<bf16_t> Uf[2] = {frag_from_acc<bf16_t>(Ua[0], Ua[1]), frag_from_acc<bf16_t>(Ua[2], Ua[3])};
+    const Frag<bf16_t> Uf[2] = {frag_from_acc<bf16_t>(Ua[0], Ua[1]), frag_from_acc<bf16_t>(Ua[2], Ua[3])};
 #pragma unroll
     for (int rt = 0; rt < 4; ++rt) Ua[rt] *= sc[rt];
-    Frag<bf16_t> Usf[2] = {frag_from_acc<bf16_t>(Ua[0], Ua[1]),
-                           frag_from_acc<bf16_t>(Ua[2], Ua[3])};
+    const Frag<bf16_t> Usf[2] = {frag_from_acc<bf16_t>(Ua[0], Ua[1]), frag_from_acc<bf16_t>(Ua[2], Ua[3])};
 
-    // S <- gamma_C S + K^T (s U): the state chain's last product
+    // S <- gamma_C S + K^T (s U): the state chain's last product, issued
+    // before the output products so that the next chunk's state is not
+    // queued behind them
 #pragma unroll
     for (int rm = 0; rm < 8; ++rm) {
       f32x4_t acc = gamma_C * S[rm];
@@ -455,21 +450,22 @@ __global__ __launch_bounds__(128) void scan_kernel_staged(ScanArgs<bf16_t> a) {
       S[rm] = acc;
     }
 
-    // O = gamma (Q S) + P U (Sf still holds the chunk-start state), computed
-    // as O^T = S^T (gamma Q^T) + U^T P^T: with the kappa fragment convention
-    // Sf and Uf serve as A operands and the q rows and P fragments as B
-    // operands unchanged, and each lane ends with four consecutive columns of
-    // one token row, written over this wave's v columns in one 8-byte store.
+    // O = gamma (Q S) + P U with the chunk-start state, computed as
+    // O^T = S^T (gamma Q^T) + U^T P^T: with the kappa fragment convention Sf
+    // and Uf serve as A operands and the q rows and P fragments as B operands
+    // unchanged, and each lane ends with four consecutive columns of one
+    // token row, written over this wave's v columns in one 8-byte store.
 #pragma unroll
     for (int rt = 0; rt < 4; ++rt) {
-      f32x4_t oq = zero4();
+      f32x4_t oq;
 #pragma unroll
-      for (int kk = 0; kk < 4; ++kk) oq = mfma(Sf[kk], qf[kk][rt], oq);
+      for (int kk = 0; kk < 4; ++kk) oq = mfma(Sf[kk], qf[kk][rt], kk == 0 ? zero4() : oq);
       f32x4_t acc = gam_tok[rt] * oq;
 #pragma unroll
       for (int kk = 0; kk < 2; ++kk) acc = mfma(Uf[kk], pf[rt * 2 + kk], acc);
       lds_store<bf16x4_t>(st + kStV + 1024 * rt + o_woff, __builtin_convertvector(acc, bf16x4_t));
     }
+
     // the next chunk's stage must be complete and this stage free for reuse
     wait_all_but_newest_stage();
     lds_barrier();

@@ -33,6 +33,25 @@ __device__ __forceinline__ void dma16(const void *base, uint32_t voff, lds_t *ds
                : "s"((uint32_t)(uintptr_t)dst), "v"(voff), "s"(base)
                : "memory", "m0");
 }
+// Buffer resource (V#) for a raw byte buffer of `bytes` bytes at `base`
+// (wave-uniform): stride 0, so a lane's access is out of range, and reads as
+// zero, once its offset + size exceeds `bytes`.
+typedef int i32x4_t __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ i32x4_t buffer_rsrc(const void *base, uint32_t bytes) {
+  const uint64_t p = reinterpret_cast<uint64_t>(base);
+  return i32x4_t{int(uint32_t(p)), int(uint32_t(p >> 32) & 0xffff), int(bytes), 0x00020000};
+}
+
+// Bounds-checked form of dma16: 16 bytes per lane from byte offset `voff` of
+// the buffer `rsrc` into LDS at dst + 16 * lane; lanes whose 16 bytes are not
+// wholly inside the buffer write zeros.  Same ordering rules as dma16.
+__device__ __forceinline__ void dma16_buf(i32x4_t rsrc, uint32_t voff, lds_t *dst) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+               :
+               : "s"((uint32_t)(uintptr_t)dst), "v"(voff), "s"(rsrc)
+               : "memory", "m0");
+}
+
 // Waits for this wave's outstanding global loads (including LDS-bound ones).
 __device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0); }
 // Waits until at most N of this wave's vector memory operations are
@@ -90,6 +109,12 @@ typedef unsigned u32x4_t __attribute__((ext_vector_type(4)));
 
 template <typename V> __device__ __forceinline__ V lds_load(const lds_t *p) {
   return *(const __attribute__((address_space(3))) V *)(p);
+}
+// Volatile form: never merged with a neighbouring read into a paired
+// ds_read2 (whose results would then have to be moved apart again to form
+// MFMA operands).
+template <typename V> __device__ __forceinline__ V lds_load_single(const lds_t *p) {
+  return *(const volatile __attribute__((address_space(3))) V *)(p);
 }
 template <typename V> __device__ __forceinline__ void lds_store(lds_t *p, V v) {
   *(__attribute__((address_space(3))) V *)(p) = v;

@@ -50,6 +50,13 @@ __host__ __device__ constexpr uint32_t rowtile_copy_lane(int i, int lane, int64_
   return uint32_t(2 * (int64_t(lane >> 4) * stride + 8 * rowtile_copy_block(i, lane)));
 }
 
+// Bytes of a chunk's row-tile source that are valid when it has `len` rows
+// (row stride `row_bytes` >= 256): rows below len lie wholly inside, and every
+// copy of a row at or past len starts at or beyond the end.
+__host__ __device__ constexpr uint32_t rowtile_valid_bytes(int len, uint32_t row_bytes) {
+  return uint32_t(len - 1) * row_bytes + 256;
+}
+
 // ---- v block ----
 __host__ __device__ constexpr int vblock_copy_row(int j, int lane) { return 16 * j + (lane >> 2); }
 __host__ __device__ constexpr int vblock_copy_block(int j, int lane) {
@@ -58,6 +65,11 @@ __host__ __device__ constexpr int vblock_copy_block(int j, int lane) {
 __host__ __device__ constexpr int64_t vblock_copy_src(int j, int lane, int len, int64_t stride) {
   return 2 * (int64_t(clamp_row(vblock_copy_row(j, lane), len)) * stride +
               8 * vblock_copy_block(j, lane));
+}
+
+// Same for a v block source (row stride `row_bytes` >= 64).
+__host__ __device__ constexpr uint32_t vblock_valid_bytes(int len, uint32_t row_bytes) {
+  return uint32_t(len - 1) * row_bytes + 64;
 }
 
 // Byte offset of logical (row, col) in the staged v block.

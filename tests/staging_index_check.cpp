@@ -49,6 +49,31 @@ int main() {
           }
         }
     }
+    // ---- bounds-checked copies: full-chunk offsets against the valid size ----
+    for (int len = 1; len <= 64; ++len) {
+      const uint32_t row_bytes = uint32_t(2 * s);
+      const uint32_t valid = rowtile_valid_bytes(len, row_bytes);
+      for (int i = 0; i < 16; ++i)
+        for (int l = 0; l < 64; ++l) {
+          const long long off = rowtile_copy_src(i, l, 64, s);
+          const bool in = rowtile_copy_row(i, l) < len;
+          CHECK(in ? off + 16 <= valid : off >= valid,
+                "row tile copy %d lane %d len %d stride %lld: offset %lld vs valid %u", i, l, len, s, off, valid);
+        }
+    }
+  }
+  // v rows can be as narrow as one 32-column block (64 bytes)
+  for (long long s : {32LL, 64LL, 96LL, 128LL, 4096LL}) {
+    for (int len = 1; len <= 64; ++len) {
+      const uint32_t vvalid = vblock_valid_bytes(len, uint32_t(2 * s));
+      for (int j = 0; j < 4; ++j)
+        for (int l = 0; l < 64; ++l) {
+          const long long off = vblock_copy_src(j, l, 64, s);
+          const bool in = vblock_copy_row(j, l) < len;
+          CHECK(in ? off + 16 <= vvalid : off >= vvalid,
+                "v copy %d lane %d len %d stride %lld: offset %lld vs valid %u", j, l, len, s, off, vvalid);
+        }
+    }
     // ---- v block: 4 copies x 64 lanes ----
     for (int len = 1; len <= 64; ++len)
       for (int j = 0; j < 4; ++j)
