@@ -103,6 +103,18 @@ __device__ __forceinline__ f32x4_t mfma(const Frag<float> &a, const Frag<float> 
   return c;
 }
 
+// XCD-aware block numbering for the per-(unit, column block) kernels: the
+// launch hands out block ids round-robin over the 8 XCDs (bid % 8), so giving
+// all column blocks of a unit the same bid % 8 puts them on one XCD, where
+// they share that XCD's L2 copy of the unit's k, q and v.  Blocks come in
+// groups of 8 units x n_colblk column blocks.
+__device__ __forceinline__ void decode_block(int bid, int n_colblk, int &u, int &cb) {
+  const int per_group = 8 * n_colblk;
+  const int grp = bid / per_group, rem = bid - grp * per_group;
+  cb = rem >> 3;
+  u = grp * 8 + (rem & 7);
+}
+
 __device__ __forceinline__ f32x4_t zero4() { return f32x4_t{0.0f, 0.0f, 0.0f, 0.0f}; }
 
 // B fragment from two stacked accumulator tiles (rows 0-15 and 16-31 of a

@@ -48,10 +48,9 @@ struct PrepArgs {
   SeqGeom geo;
 };
 
-// kStaged (bf16, d_k = 128): the chunk's k and q rows are first copied into
-// swizzled LDS row tiles with every load in flight at once, and fragment reads
-// come from LDS.  Otherwise fragments are read from global memory.
-template <typename T, bool kStaged>
+// General path (fp32, or d_k != 128): fragments are read from global memory,
+// A and M = (I + A)^-1 live in LDS.
+template <typename T>
 __global__ __launch_bounds__(256) void prep_kernel(PrepArgs<T> a) {
   const int c = blockIdx.x;
   const int h = blockIdx.y;
@@ -61,25 +60,16 @@ __global__ __launch_bounds__(256) void prep_kernel(PrepArgs<T> a) {
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
 
-  // LDS: the staged k/q tiles (32 KiB) are dead once the tiles are in
-  // registers; A and M = (I + A)^-1 then reuse the same bytes.
   constexpr int kLdsMain = 2 * 64 * 65 * 4;
   __shared__ __attribute__((aligned(16))) char smem[kLdsMain];
   __shared__ float sY[3][16][17];
   __shared__ float sg[64], sb[64];
-  bf16_t *sK = reinterpret_cast<bf16_t *>(smem);
-  bf16_t *sQ = sK + 64 * 128;
   float(*sA)[65] = reinterpret_cast<float(*)[65]>(smem);
   float(*sM)[65] = reinterpret_cast<float(*)[65]>(smem + 64 * 65 * 4);
 
   const int64_t stride = int64_t(a.H_qk) * a.d_k;
   const T *kb = a.k + int64_t(tok0) * stride + int64_t(hq) * a.d_k;
   const T *qb = a.q + int64_t(tok0) * stride + int64_t(hq) * a.d_k;
-  if constexpr (kStaged) {
-    static_assert(sizeof(T) == 2, "staged path is bf16");
-    stage_rowtile(lds_ptr(sK), reinterpret_cast<const bf16_t *>(kb), stride, len, lane, 4 * wave, 4);
-    stage_rowtile(lds_ptr(sQ), reinterpret_cast<const bf16_t *>(qb), stride, len, lane, 4 * wave, 4);
-  }
   char *entry = a.entries + (int64_t(c) * a.H_v + h) * entry_bytes<T>();
   T *fragT = reinterpret_cast<T *>(entry);
   T *fragP = fragT + 8 * kFragElems;
@@ -101,16 +91,11 @@ __global__ __launch_bounds__(256) void prep_kernel(PrepArgs<T> a) {
     gate_out[t] = exp2f(x);             // gamma_t
     gate_out[64 + t] = exp2f(g_last - x);  // s_t
   }
-  if constexpr (kStaged) wait_vmem();
   lds_barrier();
 
   auto frag = [&](int src, int r, int kk) -> Frag<T> {
-    if constexpr (kStaged) {
-      return rowtile_frag(src == 0 ? sK : sQ, r, kk, lane);
-    } else {
-      return load_row_frag(src == 0 ? kb : qb, stride, 16 * r + (lane & 15), len, 32 * kk,
-                           a.d_k, lane);
-    }
+    return load_row_frag(src == 0 ? kb : qb, stride, 16 * r + (lane & 15), len, 32 * kk, a.d_k,
+                         lane);
   };
   const int nkb = (a.d_k + 31) / 32;
 
@@ -130,7 +115,6 @@ __global__ __launch_bounds__(256) void prep_kernel(PrepArgs<T> a) {
     for (int kk = 0; kk < nkb; ++kk)
       acc[n] = mfma(frag(0, tr[n], kk), frag(isA ? 0 : 1, tc[n], kk), acc[n]);
   }
-  lds_barrier();  // the k/q tiles are dead from here on
 
 #pragma unroll
   for (int n = 0; n < 5; ++n) {
@@ -218,7 +202,248 @@ __global__ __launch_bounds__(256) void prep_kernel(PrepArgs<T> a) {
   }
 }
 
-template <typename T, bool kStaged>
+// ---------------------------------------------------------------------------
+// bf16, d_k = 128: the factor kernel.  One workgroup per (chunk slot, value
+// head); its k and q rows and gates are copied into LDS with bounds-checked
+// buffer loads (rows past the chunk's end read as zeros, padded slots get
+// beta = 0 and add nothing to the gate).
+//
+// M = (I + A)^-1 in 16 x 16 blocks: D_b = (I + A_bb)^-1 by forward
+// substitution and M_bc = -D_b sum_{j=c}^{b-1} A_bj M_jc for b > c, the
+// products on fp32 MFMA.  The block columns of M are independent: wave 0
+// forms columns 0 and 2, wave 1 columns 1 and 3; the part both need (gates,
+// A, the D_b) runs as one code path in both, so their shared LDS writes carry
+// identical values.  A stays in registers: by the symmetry of K K^T the tile
+// K_j K_b^T holds row t = 16 b + r of A_bj in lane (r, g) (columns
+// 16 j + 4 g .. + 3), the left-operand layout of the block products.  Waves 2
+// and 3 form P (t-blocks 0-2 and 3) and the gate factors.  T is assembled in
+// LDS and leaves in 16-byte stores; P and the gates go out directly.
+// ---------------------------------------------------------------------------
+namespace {
+constexpr int kXK = 0;         // k rows, 64 x 128 bf16 row tile
+constexpr int kXQ = 16384;     // q rows
+constexpr int kXAlpha = 32768; // alpha, 64 fp32
+constexpr int kXBeta = 33024;  // beta, 64 fp32
+constexpr int kXT = 33280;     // T, 8 fragments of 1 KiB, assembled here
+// fp32 16 x 16 blocks (1 KiB, row-major) and gate vectors
+constexpr int kXAd = 41472;    // A_bb, b = 0..3
+constexpr int kXD = 45568;     // D_b
+constexpr int kXDt = 49664;    // D_b^T
+constexpr int kXM10 = 53760;   // M_10^T (wave 0)
+constexpr int kXM20 = 54784;   // M_20^T (wave 0)
+constexpr int kXM21 = 55808;   // M_21^T (wave 1)
+constexpr int kXG = 56832;     // g_t, 64 fp32
+constexpr int kXB = 57088;     // beta_t, 64 fp32 (0 past the chunk's end)
+constexpr int kXBytes = 57344;
+}  // namespace
+
+__global__ __launch_bounds__(256) void factors_kernel(PrepArgs<bf16_t> a) {
+  const int c = blockIdx.x, h = blockIdx.y;
+  int s, tok0, len;
+  if (!a.geo.locate(c, s, tok0, len)) return;
+  const int hq = h / a.group;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int r0 = lane & 15, g = lane >> 4;
+  __shared__ __attribute__((aligned(16))) char factors_smem[kXBytes];
+  lds_t *const sm = lds_ptr(factors_smem);
+
+  // ---- copies: wave 0 the k rows, wave 1 the q rows, wave 2 alpha and beta ----
+  const uint32_t row_bytes = uint32_t(a.H_qk) * 256;
+  if (wave < 2) {
+    const char *src = reinterpret_cast<const char *>(wave == 0 ? a.k : a.q) +
+                      (int64_t(tok0) * a.H_qk + hq) * 256;
+    const i32x4_t res = buffer_rsrc(src, rowtile_valid_bytes(len, row_bytes));
+    lds_t *const tile = sm + (wave == 0 ? kXK : kXQ);
+#pragma unroll
+    for (int i = 0; i < 16; ++i)
+      dma16_buf(res, uint32_t(rowtile_copy_src(i, lane, 64, int64_t(a.H_qk) * 128)), tile + 1024 * i);
+  } else if (wave == 2) {
+    const uint32_t gate_bytes = uint32_t(len - 1) * uint32_t(a.H_v) * 4 + 4;
+    const int64_t first = int64_t(tok0) * a.H_v + h;
+    const uint32_t voff = uint32_t(lane) * uint32_t(a.H_v) * 4;
+    dma4_buf(buffer_rsrc(a.alpha + first, gate_bytes), voff, sm + kXAlpha);
+    dma4_buf(buffer_rsrc(a.beta + first, gate_bytes), voff, sm + kXBeta);
+  }
+  wait_vmem();
+  lds_barrier();
+
+  char *const entry = a.entries + (int64_t(c) * a.H_v + h) * entry_bytes<bf16_t>();
+  // chunk-local cumulative log2 gate of slot `lane` (slots past len add 0)
+  const float gl =
+      wave_prefix_sum(lane < len ? clamped_log2(lds_load<float>(sm + kXAlpha + 4 * lane)) : 0.0f);
+  int kq_off[4][2];
+#pragma unroll
+  for (int kk = 0; kk < 4; ++kk)
+#pragma unroll
+    for (int hf = 0; hf < 2; ++hf) kq_off[kk][hf] = 2 * rowtile_off(r0, 32 * kk + 16 * hf + 4 * g);
+  auto row_frag = [&](int tile, int rt, int kk) -> Frag<bf16_t> {
+    const lds_t *p = sm + tile + 4096 * rt;
+    return frag_cat(lds_load_single<bf16x4_t>(p + kq_off[kk][0]),
+                    lds_load_single<bf16x4_t>(p + kq_off[kk][1]));
+  };
+
+  if (wave < 2) {
+    // ---- T: gates and betas of all slots for broadcast reads ----
+    const float bl = lane < len ? lds_load<float>(sm + kXBeta + 4 * lane) : 0.0f;
+    lds_store<float>(sm + kXG + 4 * lane, gl);
+    lds_store<float>(sm + kXB + 4 * lane, bl);
+    Frag<bf16_t> kf[4][4];
+#pragma unroll
+    for (int rt = 0; rt < 4; ++rt)
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk) kf[rt][kk] = row_frag(kXK, rt, kk);
+    // A_bj rows (wave 1 does not need A_b0, b > 0)
+    f32x4_t At[4][4];
+#pragma unroll
+    for (int b = 0; b < 4; ++b)
+#pragma unroll
+      for (int j = 0; j <= b; ++j) {
+        if (wave == 1 && j == 0 && b > 0) continue;
+        f32x4_t acc = zero4();
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) acc = mfma(kf[j][kk], kf[b][kk], acc);
+        const int t = 16 * b + r0;
+        const float gt = lds_load<float>(sm + kXG + 4 * t), bt = lds_load<float>(sm + kXB + 4 * t);
+        const f32x4_t gi = lds_load<f32x4_t>(sm + kXG + 4 * (16 * j + 4 * g));
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int i = 16 * j + 4 * g + e;
+          At[b][j][e] = i < t ? bt * fast_exp2(gt - gi[e]) * acc[e] : 0.0f;
+        }
+        if (j == b) lds_store<f32x4_t>(sm + kXAd + 1024 * b + 64 * r0 + 16 * g, At[b][b]);
+      }
+    // D_b by forward substitution: lane (b = g, column r0) solves for column
+    // r0 of D_b; then D_b row-major and D_b^T (this lane's column as a row)
+    float x[16];
+    {
+      const lds_t *ab = sm + kXAd + 1024 * g;
+#pragma unroll
+      for (int t = 0; t < 16; ++t) {
+        float v = t == r0 ? 1.0f : 0.0f;
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4) {
+          if (4 * q4 < t) {
+            const f32x4_t arow = lds_load<f32x4_t>(ab + 64 * t + 16 * q4);
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+              if (4 * q4 + e < t) v -= arow[e] * x[4 * q4 + e];
+          }
+        }
+        x[t] = v;
+      }
+#pragma unroll
+      for (int t = 0; t < 16; ++t) lds_store<float>(sm + kXD + 1024 * g + 64 * t + 4 * r0, x[t]);
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4)
+        lds_store<f32x4_t>(sm + kXDt + 1024 * g + 64 * r0 + 16 * q4,
+                           f32x4_t{x[4 * q4], x[4 * q4 + 1], x[4 * q4 + 2], x[4 * q4 + 3]});
+    }
+    lds_t *const tf = sm + kXT;
+    auto rowv = [&](int off) { return lds_load<f32x4_t>(sm + off + 64 * r0 + 16 * g); };
+    // T entries of an off-diagonal block from its accumulator (rows 4 g + e,
+    // column r0): T[16 b + 4 g + e][16 c + r0] = M beta_(16 c + r0), in
+    // fragment (b, c / 2), lane 4 g + e + 16 (r0 / 4), element 4 (c mod 2) + r0 mod 4
+    auto put_t = [&](int b, int cb, f32x4_t m) {
+      const float bc = lds_load<float>(sm + kXB + 4 * (16 * cb + r0));
+      const int f = 2 * b + (cb >> 1);
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        lds_store<bf16_t>(tf + 1024 * f + 16 * ((4 * g + e) + 16 * (r0 >> 2)) + 2 * (4 * (cb & 1) + (r0 & 3)),
+                          from_f32<bf16_t>(m[e] * bc));
+    };
+    // T entries of this lane's column of its diagonal block (b = g):
+    // T[16 b + t][16 b + r0] = x[t] beta_(16 b + r0), fragment (b, b / 2),
+    // lane t + 16 (r0 / 4), element 4 (b mod 2) + r0 mod 4
+    auto put_diag = [&]() {
+      const int b = g, f = 2 * b + (b >> 1);
+#pragma unroll
+      for (int t = 0; t < 16; ++t)
+        lds_store<bf16_t>(tf + 1024 * f + 16 * (t + 16 * (r0 >> 2)) + 2 * (4 * (b & 1) + (r0 & 3)),
+                          from_f32<bf16_t>(x[t] * bl));
+    };
+    if (wave == 0) {
+      // block columns 0 and 2
+      if ((g & 1) == 0) put_diag();
+      const f32x4_t M10 = -mm16(rowv(kXD + 1024 * 1), mm16(At[1][0], rowv(kXDt + 1024 * 0), zero4()), zero4());
+      lds_store<f32x4_t>(sm + kXM10 + 64 * r0 + 16 * g, M10);
+      const f32x4_t M32 = -mm16(rowv(kXD + 1024 * 3), mm16(At[3][2], rowv(kXDt + 1024 * 2), zero4()), zero4());
+      put_t(1, 0, M10);
+      put_t(3, 2, M32);
+      const f32x4_t Y20 = mm16(At[2][1], rowv(kXM10), mm16(At[2][0], rowv(kXDt + 1024 * 0), zero4()));
+      const f32x4_t M20 = -mm16(rowv(kXD + 1024 * 2), Y20, zero4());
+      lds_store<f32x4_t>(sm + kXM20 + 64 * r0 + 16 * g, M20);
+      put_t(2, 0, M20);
+      const f32x4_t Y30 =
+          mm16(At[3][2], rowv(kXM20), mm16(At[3][1], rowv(kXM10), mm16(At[3][0], rowv(kXDt + 1024 * 0), zero4())));
+      put_t(3, 0, -mm16(rowv(kXD + 1024 * 3), Y30, zero4()));
+      // blocks above the diagonal: fragments (0, 1) and (1, 1) whole, the
+      // upper halves of (0, 0) and (2, 1)
+      lds_store<u32x4_t>(tf + 1024 * 1 + 16 * lane, u32x4_t{0, 0, 0, 0});
+      lds_store<u32x4_t>(tf + 1024 * 3 + 16 * lane, u32x4_t{0, 0, 0, 0});
+      lds_store<uint64_t>(tf + 1024 * 0 + 16 * lane + 8, uint64_t(0));
+      lds_store<uint64_t>(tf + 1024 * 5 + 16 * lane + 8, uint64_t(0));
+    } else {
+      // block columns 1 and 3
+      if (g & 1) put_diag();
+      const f32x4_t M21 = -mm16(rowv(kXD + 1024 * 2), mm16(At[2][1], rowv(kXDt + 1024 * 1), zero4()), zero4());
+      lds_store<f32x4_t>(sm + kXM21 + 64 * r0 + 16 * g, M21);
+      put_t(2, 1, M21);
+      const f32x4_t Y31 = mm16(At[3][2], rowv(kXM21), mm16(At[3][1], rowv(kXDt + 1024 * 1), zero4()));
+      put_t(3, 1, -mm16(rowv(kXD + 1024 * 3), Y31, zero4()));
+    }
+  } else {
+    // ---- P and the gate factors: wave 2 t-blocks 0-2, wave 3 t-block 3 ----
+    // P^T tile (i-block r, t-block cb), r <= cb: its lane layout is the A
+    // fragment layout of P (row t, contraction i), so its four values are half
+    // of fragment (cb, r / 2).
+    bf16_t *const fragP = reinterpret_cast<bf16_t *>(entry) + 8 * kFragElems;
+    auto p_tile = [&](int r, int cb) {
+      f32x4_t acc = zero4();
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk) acc = mfma(row_frag(kXK, r, kk), row_frag(kXQ, cb, kk), acc);
+      const int t = 16 * cb + r0;
+      const float gt = __shfl(gl, t);
+      f32x4_t pv;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int i = 16 * r + 4 * g + e;
+        const float gi = __shfl(gl, i);  // every lane takes part in the shuffle
+        pv[e] = i <= t ? fast_exp2(gt - gi) * acc[e] : 0.0f;
+      }
+      *reinterpret_cast<bf16x4_t *>(fragP + kFragElems * (2 * cb + (r >> 1)) + 8 * lane + 4 * (r & 1)) =
+          __builtin_convertvector(pv, bf16x4_t);
+    };
+    if (wave == 2) {
+#pragma unroll
+      for (int cb = 0; cb < 3; ++cb)
+#pragma unroll
+        for (int r = 0; r <= cb; ++r) p_tile(r, cb);
+      // halves above the diagonal in t-blocks 0-2
+      *reinterpret_cast<uint64_t *>(fragP + kFragElems * 0 + 8 * lane + 4) = 0;
+      *reinterpret_cast<u32x4_t *>(fragP + kFragElems * 1 + 8 * lane) = u32x4_t{0, 0, 0, 0};
+      *reinterpret_cast<u32x4_t *>(fragP + kFragElems * 3 + 8 * lane) = u32x4_t{0, 0, 0, 0};
+      *reinterpret_cast<uint64_t *>(fragP + kFragElems * 5 + 8 * lane + 4) = 0;
+    } else {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) p_tile(r, 3);
+      // gate factors: gamma_t = 2^g_t, s_t = 2^(g_C - g_t)
+      float *gate_out = reinterpret_cast<float *>(entry + 16 * kFragElems * sizeof(bf16_t));
+      const float g_last = __shfl(gl, 63);
+      gate_out[lane] = exp2f(gl);
+      gate_out[64 + lane] = exp2f(g_last - gl);
+    }
+  }
+  lds_barrier();
+  // ---- T leaves in 16-byte stores (8 KiB, 32 bytes per thread) ----
+#pragma unroll
+  for (int q2 = 0; q2 < 2; ++q2) {
+    const int off = 16 * (tid + 256 * q2);
+    *reinterpret_cast<u32x4_t *>(entry + off) = lds_load<u32x4_t>(sm + kXT + off);
+  }
+}
+
+template <typename T>
 static hipError_t launch_prep_t(const Problem &p, const Workspace &ws, hipStream_t st) {
   PrepArgs<T> a;
   a.q = static_cast<const T *>(p.q);
@@ -232,17 +457,20 @@ static hipError_t launch_prep_t(const Problem &p, const Workspace &ws, hipStream
   a.group = p.H_v / p.H_qk;
   a.geo = make_geom(p, &ws);
   const int64_t slots = chunk_slots(p);
-  hipLaunchKernelGGL((prep_kernel<T, kStaged>), dim3(unsigned(slots), unsigned(p.H_v)), dim3(256),
-                     0, st, a);
+  if constexpr (sizeof(T) == 2) {
+    if (p.d_k == 128) {
+      hipLaunchKernelGGL(factors_kernel, dim3(unsigned(slots), unsigned(p.H_v)), dim3(256), 0, st, a);
+      return hipGetLastError();
+    }
+  }
+  hipLaunchKernelGGL((prep_kernel<T>), dim3(unsigned(slots), unsigned(p.H_v)), dim3(256), 0, st, a);
   return hipGetLastError();
 }
 
 hipError_t launch_prep(const Problem &p, const Workspace &ws, hipStream_t st) {
   if (chunk_slots(p) == 0) return hipSuccess;
-  if (p.dtype == 1)
-    return p.d_k == 128 ? launch_prep_t<bf16_t, true>(p, ws, st)
-                        : launch_prep_t<bf16_t, false>(p, ws, st);
-  return launch_prep_t<float, false>(p, ws, st);
+  if (p.dtype == 1) return launch_prep_t<bf16_t>(p, ws, st);
+  return launch_prep_t<float>(p, ws, st);
 }
 
 }  // namespace gdn

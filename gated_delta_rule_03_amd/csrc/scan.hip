@@ -37,13 +37,6 @@ struct ScanArgs {
   SeqGeom geo;
 };
 
-// XCD-aware block decode: unit u's column blocks share bid % 8.
-__device__ __forceinline__ void decode_block(int bid, int n_colblk, int &u, int &cb) {
-  const int per_group = 8 * n_colblk;
-  const int grp = bid / per_group, rem = bid - grp * per_group;
-  cb = rem >> 3;
-  u = grp * 8 + (rem & 7);
-}
 
 // ---------------------------------------------------------------------------
 // General path: any supported d_k / d_v, fp32 or bf16.  One 64-lane block per

@@ -52,6 +52,14 @@ __device__ __forceinline__ void dma16_buf(i32x4_t rsrc, uint32_t voff, lds_t *ds
                : "memory", "m0");
 }
 
+// Bounds-checked 4-byte-per-lane form: lane l's 4 bytes land at dst + 4 * l.
+__device__ __forceinline__ void dma4_buf(i32x4_t rsrc, uint32_t voff, lds_t *dst) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dword %1, %2, 0 offen lds"
+               :
+               : "s"((uint32_t)(uintptr_t)dst), "v"(voff), "s"(rsrc)
+               : "memory", "m0");
+}
+
 // Waits for this wave's outstanding global loads (including LDS-bound ones).
 __device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0); }
 // Waits until at most N of this wave's vector memory operations are
@@ -147,6 +155,32 @@ __device__ __forceinline__ Frag<bf16_t> rowtile_colfrag(const bf16_t *tile, int 
     f.v[j] = __builtin_bit_cast(__bf16, tile[rowtile_off(i, m)]);
   }
   return f;
+}
+
+// Inclusive prefix sum over the 64 lanes of a wave: shifts within rows of 16
+// lanes, then the last lane of rows 0 and 2 into rows 1 and 3, then lane 31
+// into rows 2 and 3 (DPP row_shr and row_bcast).
+__device__ __forceinline__ float wave_prefix_sum(float x) {
+#define GDN_ADD_DPP(ctrl, rows, bound) \
+  x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), ctrl, rows, 0xf, bound))
+  GDN_ADD_DPP(0x111, 0xf, true);   // row_shr:1 (lanes without a source add 0)
+  GDN_ADD_DPP(0x112, 0xf, true);   // row_shr:2
+  GDN_ADD_DPP(0x114, 0xf, true);   // row_shr:4
+  GDN_ADD_DPP(0x118, 0xf, true);   // row_shr:8
+  GDN_ADD_DPP(0x142, 0xa, false);  // row_bcast:15 into rows 1 and 3
+  GDN_ADD_DPP(0x143, 0xc, false);  // row_bcast:31 into rows 2 and 3
+#undef GDN_ADD_DPP
+  return x;
+}
+
+// 16 x 16 x 16 fp32 product, acc += X Y: `xr` holds X[r][4g .. 4g + 3] and
+// `yt` holds Y^T[r][4g .. 4g + 3] (r = lane mod 16, g = lane / 16); the
+// result is in accumulator layout (rows 4g + e, column r).  Contraction slot
+// j of each of the four MFMAs is k = 4g + j.
+__device__ __forceinline__ f32x4_t mm16(f32x4_t xr, f32x4_t yt, f32x4_t acc) {
+#pragma unroll
+  for (int j = 0; j < 4; ++j) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(xr[j], yt[j], acc, 0, 0, 0);
+  return acc;
 }
 
 }  // namespace gdn
