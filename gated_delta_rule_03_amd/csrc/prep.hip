@@ -216,25 +216,26 @@ __global__ __launch_bounds__(256) void prep_kernel(PrepArgs<T> a) {
 // identical values.  A stays in registers: by the symmetry of K K^T the tile
 // K_j K_b^T holds row t = 16 b + r of A_bj in lane (r, g) (columns
 // 16 j + 4 g .. + 3), the left-operand layout of the block products.  Waves 2
-// and 3 form P (t-blocks 0-2 and 3) and the gate factors.  T is assembled in
-// LDS and leaves in 16-byte stores; P and the gates go out directly.
+// and 3 form P (t-blocks 0-2 and 3) and the gate factors, which go out
+// directly.  T stays in registers until P is formed; it is then assembled
+// over the dead q tile and leaves in 16-byte stores (48 KiB of LDS: three
+// workgroups per CU).
 // ---------------------------------------------------------------------------
 namespace {
-constexpr int kXK = 0;         // k rows, 64 x 128 bf16 row tile
-constexpr int kXQ = 16384;     // q rows
-constexpr int kXAlpha = 32768; // alpha, 64 fp32
-constexpr int kXBeta = 33024;  // beta, 64 fp32
-constexpr int kXT = 33280;     // T, 8 fragments of 1 KiB, assembled here
+constexpr int kXK = 0;          // k rows, 64 x 128 bf16 row tile
+constexpr int kXQ = 16384;      // q rows; once P is formed, T is assembled here
+constexpr int kXAlpha = 32768;  // alpha, 64 fp32
+constexpr int kXBeta = 33024;   // beta, 64 fp32
 // fp32 16 x 16 blocks (1 KiB, row-major) and gate vectors
-constexpr int kXAd = 41472;    // A_bb, b = 0..3
-constexpr int kXD = 45568;     // D_b
-constexpr int kXDt = 49664;    // D_b^T
-constexpr int kXM10 = 53760;   // M_10^T (wave 0)
-constexpr int kXM20 = 54784;   // M_20^T (wave 0)
-constexpr int kXM21 = 55808;   // M_21^T (wave 1)
-constexpr int kXG = 56832;     // g_t, 64 fp32
-constexpr int kXB = 57088;     // beta_t, 64 fp32 (0 past the chunk's end)
-constexpr int kXBytes = 57344;
+constexpr int kXAd = 33280;     // A_bb, b = 0..3
+constexpr int kXD = 37376;      // D_b
+constexpr int kXDt = 41472;     // D_b^T
+constexpr int kXM10 = 45568;    // M_10^T (wave 0)
+constexpr int kXM20 = 46592;    // M_20^T (wave 0)
+constexpr int kXM21 = 47616;    // M_21^T (wave 1)
+constexpr int kXG = 48640;      // g_t, 64 fp32
+constexpr int kXB = 48896;      // beta_t, 64 fp32 (0 past the chunk's end)
+constexpr int kXBytes = 49152;  // three workgroups per CU
 }  // namespace
 
 __global__ __launch_bounds__(256) void factors_kernel(PrepArgs<bf16_t> a) {
@@ -283,9 +284,15 @@ __global__ __launch_bounds__(256) void factors_kernel(PrepArgs<bf16_t> a) {
                     lds_load_single<bf16x4_t>(p + kq_off[kk][1]));
   };
 
+  // T results kept in registers until the q tile is dead: this lane's column
+  // of its diagonal block (x, scaled by beta of slot `lane`) and up to four
+  // off-diagonal blocks in accumulator layout
+  float x[16];
+  f32x4_t mt[4];
+  float bl = 0.0f;
   if (wave < 2) {
     // ---- T: gates and betas of all slots for broadcast reads ----
-    const float bl = lane < len ? lds_load<float>(sm + kXBeta + 4 * lane) : 0.0f;
+    bl = lane < len ? lds_load<float>(sm + kXBeta + 4 * lane) : 0.0f;
     lds_store<float>(sm + kXG + 4 * lane, gl);
     lds_store<float>(sm + kXB + 4 * lane, bl);
     Frag<bf16_t> kf[4][4];
@@ -315,7 +322,6 @@ __global__ __launch_bounds__(256) void factors_kernel(PrepArgs<bf16_t> a) {
       }
     // D_b by forward substitution: lane (b = g, column r0) solves for column
     // r0 of D_b; then D_b row-major and D_b^T (this lane's column as a row)
-    float x[16];
     {
       const lds_t *ab = sm + kXAd + 1024 * g;
 #pragma unroll
@@ -339,58 +345,24 @@ __global__ __launch_bounds__(256) void factors_kernel(PrepArgs<bf16_t> a) {
         lds_store<f32x4_t>(sm + kXDt + 1024 * g + 64 * r0 + 16 * q4,
                            f32x4_t{x[4 * q4], x[4 * q4 + 1], x[4 * q4 + 2], x[4 * q4 + 3]});
     }
-    lds_t *const tf = sm + kXT;
     auto rowv = [&](int off) { return lds_load<f32x4_t>(sm + off + 64 * r0 + 16 * g); };
-    // T entries of an off-diagonal block from its accumulator (rows 4 g + e,
-    // column r0): T[16 b + 4 g + e][16 c + r0] = M beta_(16 c + r0), in
-    // fragment (b, c / 2), lane 4 g + e + 16 (r0 / 4), element 4 (c mod 2) + r0 mod 4
-    auto put_t = [&](int b, int cb, f32x4_t m) {
-      const float bc = lds_load<float>(sm + kXB + 4 * (16 * cb + r0));
-      const int f = 2 * b + (cb >> 1);
-#pragma unroll
-      for (int e = 0; e < 4; ++e)
-        lds_store<bf16_t>(tf + 1024 * f + 16 * ((4 * g + e) + 16 * (r0 >> 2)) + 2 * (4 * (cb & 1) + (r0 & 3)),
-                          from_f32<bf16_t>(m[e] * bc));
-    };
-    // T entries of this lane's column of its diagonal block (b = g):
-    // T[16 b + t][16 b + r0] = x[t] beta_(16 b + r0), fragment (b, b / 2),
-    // lane t + 16 (r0 / 4), element 4 (b mod 2) + r0 mod 4
-    auto put_diag = [&]() {
-      const int b = g, f = 2 * b + (b >> 1);
-#pragma unroll
-      for (int t = 0; t < 16; ++t)
-        lds_store<bf16_t>(tf + 1024 * f + 16 * (t + 16 * (r0 >> 2)) + 2 * (4 * (b & 1) + (r0 & 3)),
-                          from_f32<bf16_t>(x[t] * bl));
-    };
     if (wave == 0) {
-      // block columns 0 and 2
-      if ((g & 1) == 0) put_diag();
-      const f32x4_t M10 = -mm16(rowv(kXD + 1024 * 1), mm16(At[1][0], rowv(kXDt + 1024 * 0), zero4()), zero4());
-      lds_store<f32x4_t>(sm + kXM10 + 64 * r0 + 16 * g, M10);
-      const f32x4_t M32 = -mm16(rowv(kXD + 1024 * 3), mm16(At[3][2], rowv(kXDt + 1024 * 2), zero4()), zero4());
-      put_t(1, 0, M10);
-      put_t(3, 2, M32);
+      // block columns 0 and 2: M10, M32, M20, M30
+      mt[0] = -mm16(rowv(kXD + 1024 * 1), mm16(At[1][0], rowv(kXDt + 1024 * 0), zero4()), zero4());
+      lds_store<f32x4_t>(sm + kXM10 + 64 * r0 + 16 * g, mt[0]);
+      mt[1] = -mm16(rowv(kXD + 1024 * 3), mm16(At[3][2], rowv(kXDt + 1024 * 2), zero4()), zero4());
       const f32x4_t Y20 = mm16(At[2][1], rowv(kXM10), mm16(At[2][0], rowv(kXDt + 1024 * 0), zero4()));
-      const f32x4_t M20 = -mm16(rowv(kXD + 1024 * 2), Y20, zero4());
-      lds_store<f32x4_t>(sm + kXM20 + 64 * r0 + 16 * g, M20);
-      put_t(2, 0, M20);
+      mt[2] = -mm16(rowv(kXD + 1024 * 2), Y20, zero4());
+      lds_store<f32x4_t>(sm + kXM20 + 64 * r0 + 16 * g, mt[2]);
       const f32x4_t Y30 =
           mm16(At[3][2], rowv(kXM20), mm16(At[3][1], rowv(kXM10), mm16(At[3][0], rowv(kXDt + 1024 * 0), zero4())));
-      put_t(3, 0, -mm16(rowv(kXD + 1024 * 3), Y30, zero4()));
-      // blocks above the diagonal: fragments (0, 1) and (1, 1) whole, the
-      // upper halves of (0, 0) and (2, 1)
-      lds_store<u32x4_t>(tf + 1024 * 1 + 16 * lane, u32x4_t{0, 0, 0, 0});
-      lds_store<u32x4_t>(tf + 1024 * 3 + 16 * lane, u32x4_t{0, 0, 0, 0});
-      lds_store<uint64_t>(tf + 1024 * 0 + 16 * lane + 8, uint64_t(0));
-      lds_store<uint64_t>(tf + 1024 * 5 + 16 * lane + 8, uint64_t(0));
+      mt[3] = -mm16(rowv(kXD + 1024 * 3), Y30, zero4());
     } else {
-      // block columns 1 and 3
-      if (g & 1) put_diag();
-      const f32x4_t M21 = -mm16(rowv(kXD + 1024 * 2), mm16(At[2][1], rowv(kXDt + 1024 * 1), zero4()), zero4());
-      lds_store<f32x4_t>(sm + kXM21 + 64 * r0 + 16 * g, M21);
-      put_t(2, 1, M21);
+      // block columns 1 and 3: M21, M31
+      mt[0] = -mm16(rowv(kXD + 1024 * 2), mm16(At[2][1], rowv(kXDt + 1024 * 1), zero4()), zero4());
+      lds_store<f32x4_t>(sm + kXM21 + 64 * r0 + 16 * g, mt[0]);
       const f32x4_t Y31 = mm16(At[3][2], rowv(kXM21), mm16(At[3][1], rowv(kXDt + 1024 * 1), zero4()));
-      put_t(3, 1, -mm16(rowv(kXD + 1024 * 3), Y31, zero4()));
+      mt[1] = -mm16(rowv(kXD + 1024 * 3), Y31, zero4());
     }
   } else {
     // ---- P and the gate factors: wave 2 t-blocks 0-2, wave 3 t-block 3 ----
@@ -434,12 +406,54 @@ __global__ __launch_bounds__(256) void factors_kernel(PrepArgs<bf16_t> a) {
       gate_out[64 + lane] = exp2f(g_last - gl);
     }
   }
+  lds_barrier();  // every factor is formed: the q tile is dead
+  if (wave < 2) {
+    lds_t *const tf = sm + kXQ;
+    // T entries of an off-diagonal block from its accumulator (rows 4 g + e,
+    // column r0): T[16 b + 4 g + e][16 c + r0] = M beta_(16 c + r0), in
+    // fragment (b, c / 2), lane 4 g + e + 16 (r0 / 4), element 4 (c mod 2) + r0 mod 4
+    auto put_t = [&](int b, int cb, f32x4_t m) {
+      const float bc = lds_load<float>(sm + kXB + 4 * (16 * cb + r0));
+      const int f = 2 * b + (cb >> 1);
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        lds_store<bf16_t>(tf + 1024 * f + 16 * ((4 * g + e) + 16 * (r0 >> 2)) + 2 * (4 * (cb & 1) + (r0 & 3)),
+                          from_f32<bf16_t>(m[e] * bc));
+    };
+    // T entries of this lane's column of its diagonal block (b = g):
+    // T[16 b + t][16 b + r0] = x[t] beta_(16 b + r0), fragment (b, b / 2),
+    // lane t + 16 (r0 / 4), element 4 (b mod 2) + r0 mod 4
+    auto put_diag = [&]() {
+      const int b = g, f = 2 * b + (b >> 1);
+#pragma unroll
+      for (int t = 0; t < 16; ++t)
+        lds_store<bf16_t>(tf + 1024 * f + 16 * (t + 16 * (r0 >> 2)) + 2 * (4 * (b & 1) + (r0 & 3)),
+                          from_f32<bf16_t>(x[t] * bl));
+    };
+    if (wave == 0) {
+      if ((g & 1) == 0) put_diag();
+      put_t(1, 0, mt[0]);
+      put_t(3, 2, mt[1]);
+      put_t(2, 0, mt[2]);
+      put_t(3, 0, mt[3]);
+      // blocks above the diagonal: fragments (0, 1) and (1, 1) whole, the
+      // upper halves of (0, 0) and (2, 1)
+      lds_store<u32x4_t>(tf + 1024 * 1 + 16 * lane, u32x4_t{0, 0, 0, 0});
+      lds_store<u32x4_t>(tf + 1024 * 3 + 16 * lane, u32x4_t{0, 0, 0, 0});
+      lds_store<uint64_t>(tf + 1024 * 0 + 16 * lane + 8, uint64_t(0));
+      lds_store<uint64_t>(tf + 1024 * 5 + 16 * lane + 8, uint64_t(0));
+    } else {
+      if (g & 1) put_diag();
+      put_t(2, 1, mt[0]);
+      put_t(3, 1, mt[1]);
+    }
+  }
   lds_barrier();
   // ---- T leaves in 16-byte stores (8 KiB, 32 bytes per thread) ----
 #pragma unroll
   for (int q2 = 0; q2 < 2; ++q2) {
     const int off = 16 * (tid + 256 * q2);
-    *reinterpret_cast<u32x4_t *>(entry + off) = lds_load<u32x4_t>(sm + kXT + off);
+    *reinterpret_cast<u32x4_t *>(entry + off) = lds_load<u32x4_t>(sm + kXQ + off);
   }
 }
 
