@@ -211,7 +211,7 @@ __global__ __launch_bounds__(256) void prep_kernel(PrepArgs<T> a) {
 // M = (I + A)^-1 in 16 x 16 blocks: D_b = (I + A_bb)^-1 by forward
 // substitution and M_bc = -D_b sum_{j=c}^{b-1} A_bj M_jc for b > c, the
 // products on fp32 MFMA.  The block columns of M are independent: wave 0
-// forms columns 0 and 2, wave 1 columns 1 and 3; the part both need (gates,
+// forms column 0 (9 products), wave 1 columns 1-3 (7); the part both need (gates,
 // A, the D_b) runs as one code path in both, so their shared LDS writes carry
 // identical values.  A stays in registers: by the symmetry of K K^T the tile
 // K_j K_b^T holds row t = 16 b + r of A_bj in lane (r, g) (columns
@@ -347,20 +347,20 @@ __global__ __launch_bounds__(256) void factors_kernel(PrepArgs<bf16_t> a) {
     }
     auto rowv = [&](int off) { return lds_load<f32x4_t>(sm + off + 64 * r0 + 16 * g); };
     if (wave == 0) {
-      // block columns 0 and 2: M10, M32, M20, M30
+      // block column 0 (the longest dependency chain): M10, M20, M30
       mt[0] = -mm16(rowv(kXD + 1024 * 1), mm16(At[1][0], rowv(kXDt + 1024 * 0), zero4()), zero4());
       lds_store<f32x4_t>(sm + kXM10 + 64 * r0 + 16 * g, mt[0]);
-      mt[1] = -mm16(rowv(kXD + 1024 * 3), mm16(At[3][2], rowv(kXDt + 1024 * 2), zero4()), zero4());
       const f32x4_t Y20 = mm16(At[2][1], rowv(kXM10), mm16(At[2][0], rowv(kXDt + 1024 * 0), zero4()));
-      mt[2] = -mm16(rowv(kXD + 1024 * 2), Y20, zero4());
-      lds_store<f32x4_t>(sm + kXM20 + 64 * r0 + 16 * g, mt[2]);
+      mt[1] = -mm16(rowv(kXD + 1024 * 2), Y20, zero4());
+      lds_store<f32x4_t>(sm + kXM20 + 64 * r0 + 16 * g, mt[1]);
       const f32x4_t Y30 =
           mm16(At[3][2], rowv(kXM20), mm16(At[3][1], rowv(kXM10), mm16(At[3][0], rowv(kXDt + 1024 * 0), zero4())));
-      mt[3] = -mm16(rowv(kXD + 1024 * 3), Y30, zero4());
+      mt[2] = -mm16(rowv(kXD + 1024 * 3), Y30, zero4());
     } else {
-      // block columns 1 and 3: M21, M31
+      // block columns 1 to 3: M21, M31, M32
       mt[0] = -mm16(rowv(kXD + 1024 * 2), mm16(At[2][1], rowv(kXDt + 1024 * 1), zero4()), zero4());
       lds_store<f32x4_t>(sm + kXM21 + 64 * r0 + 16 * g, mt[0]);
+      mt[2] = -mm16(rowv(kXD + 1024 * 3), mm16(At[3][2], rowv(kXDt + 1024 * 2), zero4()), zero4());
       const f32x4_t Y31 = mm16(At[3][2], rowv(kXM21), mm16(At[3][1], rowv(kXDt + 1024 * 1), zero4()));
       mt[1] = -mm16(rowv(kXD + 1024 * 3), Y31, zero4());
     }
@@ -431,11 +431,10 @@ __global__ __launch_bounds__(256) void factors_kernel(PrepArgs<bf16_t> a) {
                           from_f32<bf16_t>(x[t] * bl));
     };
     if (wave == 0) {
-      if ((g & 1) == 0) put_diag();
+      if (g == 0) put_diag();
       put_t(1, 0, mt[0]);
-      put_t(3, 2, mt[1]);
-      put_t(2, 0, mt[2]);
-      put_t(3, 0, mt[3]);
+      put_t(2, 0, mt[1]);
+      put_t(3, 0, mt[2]);
       // blocks above the diagonal: fragments (0, 1) and (1, 1) whole, the
       // upper halves of (0, 0) and (2, 1)
       lds_store<u32x4_t>(tf + 1024 * 1 + 16 * lane, u32x4_t{0, 0, 0, 0});
@@ -443,9 +442,10 @@ __global__ __launch_bounds__(256) void factors_kernel(PrepArgs<bf16_t> a) {
       lds_store<uint64_t>(tf + 1024 * 0 + 16 * lane + 8, uint64_t(0));
       lds_store<uint64_t>(tf + 1024 * 5 + 16 * lane + 8, uint64_t(0));
     } else {
-      if (g & 1) put_diag();
+      if (g > 0) put_diag();
       put_t(2, 1, mt[0]);
       put_t(3, 1, mt[1]);
+      put_t(3, 2, mt[2]);
     }
   }
   lds_barrier();
