@@ -289,24 +289,37 @@ __global__ __launch_bounds__(128) void scan_kernel_staged(ScanArgs<bf16_t> a) {
 #pragma unroll
   for (int i = 0; i < 2; ++i) v_voff[i] = uint32_t(vblock_copy_src(2 * wave + i, lane, 64, v_stride));
 
-  auto stage = [&](int cc, char *base_mem) {
+  // A stage's copies come in two parts, issued at different points of a
+  // chunk so that the vector-memory queue never holds all of them at once:
+  // the k or q row tile (16 copies), then the v block, the entry's fragments
+  // and (wave 0) its gate block.
+  auto stage_rows = [&](int cc, char *base_mem) {
+    const int tok0 = start + cc * C;
+    const int len = min(C, end - tok0);
+    lds_t *const base = lds_ptr(base_mem);
+    const i32x4_t kq_res = buffer_rsrc(kq_src + int64_t(tok0) * kq_row_bytes,
+                                       rowtile_valid_bytes(len, kq_row_bytes));
+    lds_t *const tile = base + (wave == 0 ? kStK : kStQ);
+#pragma unroll
+    for (int i = 0; i < 16; ++i) dma16_buf(kq_res, kq_voff[i], tile + 1024 * i);
+  };
+  auto stage_rest = [&](int cc, char *base_mem) {
     const int tok0 = start + cc * C;
     const int len = min(C, end - tok0);
     lds_t *const base = lds_ptr(base_mem);
     const char *entry = a.entries + (int64_t(c_first + cc) * a.H_v + h) * ebytes;
-    const i32x4_t kq_res = buffer_rsrc(kq_src + int64_t(tok0) * kq_row_bytes,
-                                       rowtile_valid_bytes(len, kq_row_bytes));
     const i32x4_t v_res = buffer_rsrc(v_src + int64_t(tok0) * v_row_bytes,
                                       vblock_valid_bytes(len, v_row_bytes));
-    lds_t *const tile = base + (wave == 0 ? kStK : kStQ);
-#pragma unroll
-    for (int i = 0; i < 16; ++i) dma16_buf(kq_res, kq_voff[i], tile + 1024 * i);
 #pragma unroll
     for (int i = 0; i < 2; ++i) dma16_buf(v_res, v_voff[i], base + kStV + 2048 * wave + 1024 * i);
     const char *f = entry + 8192 * wave;
 #pragma unroll
     for (int i = 0; i < 8; ++i) dma16(f + 1024 * i, 16 * lane, base + kStF + 8192 * wave + 1024 * i);
     if (wave == 0) dma16(entry + 16384, 16 * lane, base + kStG);
+  };
+  auto stage = [&](int cc, char *base_mem) {
+    stage_rows(cc, base_mem);
+    stage_rest(cc, base_mem);
   };
 
   auto wait_all_but_newest_stage = [&]() {
@@ -332,40 +345,27 @@ __global__ __launch_bounds__(128) void scan_kernel_staged(ScanArgs<bf16_t> a) {
     }
   };
 
-  if (n_chunks > 0) {
-    stage(0, scan_stage0);
-    stage(min(1, n_chunks - 1), scan_stage1);
-    wait_all_but_newest_stage();
-  }
-  lds_barrier();
-
-  // One chunk: compute from `cur`; the previous chunk's outputs (in `prev`)
-  // leave before the prefetch of chunk cc + 2 reuses that stage.  The
-  // prefetch is issued every chunk (past the end it re-reads the last chunk),
-  // so each chunk issues the same loads and the waits below are exact.
-  auto chunk_step = [&](int cc, char *cur_mem, char *prev_mem) {
-    store_outputs(cc - 1, prev_mem);
-    stage(min(cc + 2, n_chunks - 1), prev_mem);
-
-    lds_t *const st = lds_ptr(cur_mem);
-
-    // gate factors: rows 16 rt + 4 g + e of this lane's column, the token of
-    // this lane's transposed output tiles, and the chunk's last slot
-    const float gamma_C = lds_load<float>(st + kStG + 252);
-    f32x4_t gam[4], sc[4];
-    float gam_tok[4];
+  // Operands of the chunk about to run, read from its stage right after the
+  // barrier that completes it: gate factors (rows 16 rt + 4 g + e of this
+  // lane's column, the token of this lane's transposed output tiles, the
+  // chunk's last slot), k row fragments, v transposed, T fragments.  Row
+  // fragments are two 8-byte reads each, kept single (not paired across
+  // tiles) so that they land in the fragment's registers directly.
+  float gamma_C;
+  f32x4_t gam[4], sc[4];
+  float gam_tok[4];
+  Frag<bf16_t> kf[4][4];  // k rows: [contraction block][row tile]
+  bf16x4_t vt[4];         // v, transposed: four rows of this lane's column
+  Frag<bf16_t> tf[8];
+  auto read_operands = [&](const char *stage_mem) {
+    const lds_t *st = lds_ptr(const_cast<char *>(stage_mem));
+    gamma_C = lds_load<float>(st + kStG + 252);
 #pragma unroll
     for (int rt = 0; rt < 4; ++rt) {
       gam[rt] = lds_load<f32x4_t>(st + kStG + 64 * rt + 16 * g);
       sc[rt] = lds_load<f32x4_t>(st + kStG + 256 + 64 * rt + 16 * g);
       gam_tok[rt] = lds_load<float>(st + kStG + 4 * out_acc_row(rt, lane));
     }
-
-    // Operands are read into registers one phase ahead of their use, so each
-    // phase's MFMAs do not wait on their own LDS reads.  Row fragments are two
-    // 8-byte reads each, kept single (not paired across tiles) so that they
-    // land in the fragment's registers directly.
-    Frag<bf16_t> kf[4][4];  // k rows: [contraction block][row tile]
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk)
 #pragma unroll
@@ -374,12 +374,33 @@ __global__ __launch_bounds__(128) void scan_kernel_staged(ScanArgs<bf16_t> a) {
         kf[kk][rt] = frag_cat(lds_load_single<bf16x4_t>(pk + kq_off[kk][0]),
                               lds_load_single<bf16x4_t>(pk + kq_off[kk][1]));
       }
-    bf16x4_t vt[4];  // v, transposed: four rows of this lane's column
 #pragma unroll
     for (int rt = 0; rt < 4; ++rt) vt[rt] = lds_read_tr16(st + kStV + 1024 * rt + v_off);
-    Frag<bf16_t> tf[8];
 #pragma unroll
     for (int i = 0; i < 8; ++i) tf[i].v = lds_load<bf16x8_t>(st + kStF + 1024 * i + 16 * lane);
+  };
+
+  if (n_chunks > 0) {
+    stage(0, scan_stage0);
+    stage(min(1, n_chunks - 1), scan_stage1);
+    wait_all_but_newest_stage();
+  }
+  lds_barrier();
+  read_operands(scan_stage0);
+
+  // One chunk, software-pipelined: the state chain runs from the operands
+  // read after the previous barrier; the q rows, K^T and P are read from the
+  // stage during the chain.  The barrier follows the state update, and the
+  // chunk's output products run after it, behind the reads of the next
+  // chunk's operands.  The previous chunk's outputs (in `prev`) leave before
+  // the prefetch of chunk cc + 2 reuses that stage.  The prefetch is issued
+  // every chunk (past the end it re-reads the last chunk), so each chunk
+  // issues the same loads, and no other vector-memory operation follows them
+  // in the chunk: the waits below are exact.
+  auto chunk_step = [&](int cc, char *cur_mem, char *prev_mem, char *next_mem) {
+    store_outputs(cc - 1, prev_mem);
+    const int pf_chunk = min(cc + 2, n_chunks - 1);
+    lds_t *const st = lds_ptr(cur_mem);
 
     Frag<bf16_t> Sf[4];
 #pragma unroll
@@ -391,8 +412,9 @@ __global__ __launch_bounds__(128) void scan_kernel_staged(ScanArgs<bf16_t> a) {
     for (int kk = 0; kk < 4; ++kk)
 #pragma unroll
       for (int rt = 0; rt < 4; ++rt) Y[rt] = mfma(kf[kk][rt], Sf[kk], kk == 0 ? zero4() : Y[rt]);
+    stage_rows(pf_chunk, prev_mem);  // prefetch, part 1 (behind the Y products)
 
-    // next: q rows
+    // q rows, for the output products after the barrier
     Frag<bf16_t> qf[4][4];
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk)
@@ -413,8 +435,9 @@ __global__ __launch_bounds__(128) void scan_kernel_staged(ScanArgs<bf16_t> a) {
     for (int rt = 0; rt < 4; ++rt)
 #pragma unroll
       for (int kk = 0; kk < 2; ++kk) Ua[rt] = mfma(tf[rt * 2 + kk], Xf[kk], kk == 0 ? zero4() : Ua[rt]);
+    stage_rest(pf_chunk, prev_mem);  // prefetch, part 2 (behind the U products)
 
-    // next: K^T fragments (transposed reads of the k tile) and P
+    // K^T fragments (transposed reads of the k tile) and P
     Frag<bf16_t> ktf[8][2];
 #pragma unroll
     for (int rm = 0; rm < 8; ++rm)
@@ -432,9 +455,7 @@ __global__ __launch_bounds__(128) void scan_kernel_staged(ScanArgs<bf16_t> a) {
     for (int rt = 0; rt < 4; ++rt) Ua[rt] *= sc[rt];
     const Frag<bf16_t> Usf[2] = {frag_from_acc<bf16_t>(Ua[0], Ua[1]), frag_from_acc<bf16_t>(Ua[2], Ua[3])};
 
-    // S <- gamma_C S + K^T (s U): the state chain's last product, issued
-    // before the output products so that the next chunk's state is not
-    // queued behind them
+    // S <- gamma_C S + K^T (s U)
 #pragma unroll
     for (int rm = 0; rm < 8; ++rm) {
       f32x4_t acc = gamma_C * S[rm];
@@ -442,6 +463,16 @@ __global__ __launch_bounds__(128) void scan_kernel_staged(ScanArgs<bf16_t> a) {
       for (int kk = 0; kk < 2; ++kk) acc = mfma(ktf[rm][kk], Usf[kk], acc);
       S[rm] = acc;
     }
+    float gt_o[4];
+#pragma unroll
+    for (int rt = 0; rt < 4; ++rt) gt_o[rt] = gam_tok[rt];
+
+    // the next chunk's stage must be complete and this chunk's k, q, T and P
+    // reads done before the other wave may prefetch over this stage; then the
+    // next chunk's operands are read
+    wait_all_but_newest_stage();
+    lds_barrier();
+    read_operands(next_mem);
 
     // O = gamma (Q S) + P U with the chunk-start state, computed as
     // O^T = S^T (gamma Q^T) + U^T P^T: with the kappa fragment convention Sf
@@ -453,20 +484,16 @@ __global__ __launch_bounds__(128) void scan_kernel_staged(ScanArgs<bf16_t> a) {
       f32x4_t oq;
 #pragma unroll
       for (int kk = 0; kk < 4; ++kk) oq = mfma(Sf[kk], qf[kk][rt], kk == 0 ? zero4() : oq);
-      f32x4_t acc = gam_tok[rt] * oq;
+      f32x4_t acc = gt_o[rt] * oq;
 #pragma unroll
       for (int kk = 0; kk < 2; ++kk) acc = mfma(Uf[kk], pf[rt * 2 + kk], acc);
       lds_store<bf16x4_t>(st + kStV + 1024 * rt + o_woff, __builtin_convertvector(acc, bf16x4_t));
     }
-
-    // the next chunk's stage must be complete and this stage free for reuse
-    wait_all_but_newest_stage();
-    lds_barrier();
   };
   for (int cc = 0; cc < n_chunks; cc += 3) {
-    chunk_step(cc, scan_stage0, scan_stage2);
-    if (cc + 1 < n_chunks) chunk_step(cc + 1, scan_stage1, scan_stage0);
-    if (cc + 2 < n_chunks) chunk_step(cc + 2, scan_stage2, scan_stage1);
+    chunk_step(cc, scan_stage0, scan_stage2, scan_stage1);
+    if (cc + 1 < n_chunks) chunk_step(cc + 1, scan_stage1, scan_stage0, scan_stage2);
+    if (cc + 2 < n_chunks) chunk_step(cc + 2, scan_stage2, scan_stage1, scan_stage0);
   }
   if (n_chunks > 0) {
     const int last = (n_chunks - 1) % 3;
