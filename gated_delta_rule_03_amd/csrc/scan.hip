@@ -186,47 +186,127 @@ __global__ __launch_bounds__(64) void scan_kernel(ScanArgs<T> a) {
 // ---------------------------------------------------------------------------
 // Pipelined path: bf16, d_k = 128, d_v a multiple of 32.
 //
-// Two waves per block own 32 state columns (16 each).  A chunk's operands --
+// A block of four waves owns 32 state columns of one unit.  Waves 0 and 1
+// compute (16 columns each); waves 2 and 3 only copy.  A chunk's operands --
 // its k and q rows (swizzled row tiles), the T and P fragments and gates of
 // its workspace entry, and its 64 x 32 block of v -- are copied into one of
 // three LDS stages with global_load_lds, two chunks ahead of the chunk being
-// computed.  K^T fragments for the state update and the v block come from the
-// staged tiles through transposed reads (ds_read_b64_tr_b16).  Every LDS and
-// global offset a lane uses is computed once; per chunk only wave-uniform
-// bases change.  The chunk's outputs are written over the wave's own columns
-// of the staged v block and leave in 16-byte stores.  The k / q and v copies
-// are bounds-checked buffer loads: rows past a partial chunk read as zeros.
+// computed.  A copy moves 1 KiB and the memory pipeline accepts one from a
+// wave only every few dozen cycles, so the copies are issued by the two
+// copy waves, on SIMDs the compute waves leave idle, and the compute waves'
+// instruction streams hold only LDS reads, MFMAs and their output stores.
+// One barrier per chunk keeps the roles in step.  K^T fragments for the state
+// update and the v block come from the staged tiles through transposed reads
+// (ds_read_b64_tr_b16).  Every LDS and global offset a lane uses is computed
+// once; per chunk only wave-uniform bases change.  The k / q and v copies are
+// bounds-checked buffer loads: rows past a partial chunk read as zeros.
 // ---------------------------------------------------------------------------
 constexpr int kStK = 0;        // 64 x 128 bf16 row tile
 constexpr int kStQ = 16384;    // 64 x 128 bf16 row tile
 constexpr int kStF = 32768;    // T (8) and P (8) fragments, 1 KiB each
 constexpr int kStG = 49152;    // gate block: gamma (64 fp32), s (64 fp32), padding
-constexpr int kStV = 50176;    // 64 x 32 bf16 (v, then the outputs)
+constexpr int kStV = 50176;    // 64 x 32 bf16 v block
 constexpr int kStBytes = 54272;
-// Load instructions one wave issues per stage (wave 0: k tile, T, v, gates;
-// wave 1: q tile, P, v).  The end-of-chunk wait leaves exactly the newest
-// stage's loads in flight; loads complete in issue order, and nothing else is
-// issued after them in the chunk (its output stores go out at the top of the
-// next chunk, before that chunk's prefetch).
-constexpr int kStageLoadsW0 = 27;
-constexpr int kStageLoadsW1 = 26;
+// Copies one copy wave issues per stage (wave 2: k tile, T, gates, v columns
+// 0-15; wave 3: q tile, P, v columns 16-31).  A copy wave issues nothing but
+// these loads, and loads complete in issue order, so waiting until only the
+// newest stage's copies are outstanding completes every older stage.
+constexpr int kStageLoadsW2 = 27;
+constexpr int kStageLoadsW3 = 26;
 
 // Three stages as distinct LDS objects: with the chunk loop unrolled by three,
-// every access names its stage at compile time, so the compiler can tell that
-// the in-flight global_load_lds copies never alias the stage being read and
-// does not wait for them before LDS reads.
+// every access names its stage at compile time.
 __shared__ __attribute__((aligned(16))) char scan_stage0[kStBytes];
 __shared__ __attribute__((aligned(16))) char scan_stage1[kStBytes];
 __shared__ __attribute__((aligned(16))) char scan_stage2[kStBytes];
 
-__global__ __launch_bounds__(128) void scan_kernel_staged(ScanArgs<bf16_t> a) {
+__global__ __launch_bounds__(256) void scan_kernel_staged(ScanArgs<bf16_t> a) {
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int r0 = lane & 15, g = lane >> 4;
   int u, cb;
   decode_block(blockIdx.x, a.n_colblk, u, cb);  // n_colblk = d_v / 32
-  if (u >= a.n_units) return;
+  if (u >= a.n_units) return;  // the whole block
   const int s = u / a.H_v, h = u - s * a.H_v, hq = h / a.group;
+
+  int start, end;
+  a.geo.seq_bounds(s, start, end);
+  const int C = a.geo.chunk;
+  const int c_first = a.geo.first_chunk(s);
+  const int n_chunks = max(0, min((end - start + C - 1) / C, a.geo.n_slots - c_first));
+  const int64_t qk_stride = int64_t(a.H_qk) * 128;
+  const int64_t v_stride = int64_t(a.H_v) * a.d_v;
+
+  if (wave >= 2) {
+    // ---- copy waves ----
+    const int cw = wave - 2;  // 0: k tile, T, gates; 1: q tile, P
+    const uint32_t kq_row_bytes = uint32_t(2 * qk_stride), v_row_bytes = uint32_t(2 * v_stride);
+    const int64_t ebytes = entry_bytes<bf16_t>();
+    const char *kq_src = reinterpret_cast<const char *>(cw == 0 ? a.k : a.q) + int64_t(hq) * 256;
+    const char *v_src = reinterpret_cast<const char *>(a.v) + (int64_t(h) * a.d_v + 32 * cb) * 2;
+    // Per-lane byte offsets of every copy of a full chunk (tile_index.hpp),
+    // relative to the chunk's first row.  The k / q and v copies go through a
+    // buffer resource whose size ends at the chunk's last row, so rows past a
+    // partial chunk read as zeros (exact zeros that the chunk algebra only
+    // multiplies by zero) and no copy can leave the sequence.
+    uint32_t kq_voff[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) kq_voff[i] = uint32_t(rowtile_copy_src(i, lane, 64, qk_stride));
+    uint32_t v_voff[2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i) v_voff[i] = uint32_t(vblock_copy_src(2 * cw + i, lane, 64, v_stride));
+
+    auto stage = [&](int cc, char *base_mem) {
+      const int tok0 = start + cc * C;
+      const int len = min(C, end - tok0);
+      lds_t *const base = lds_ptr(base_mem);
+      const i32x4_t kq_res = buffer_rsrc(kq_src + int64_t(tok0) * kq_row_bytes,
+                                         rowtile_valid_bytes(len, kq_row_bytes));
+      lds_t *const tile = base + (cw == 0 ? kStK : kStQ);
+#pragma unroll
+      for (int i = 0; i < 16; ++i) dma16_buf(kq_res, kq_voff[i], tile + 1024 * i);
+      const char *entry = a.entries + (int64_t(c_first + cc) * a.H_v + h) * ebytes;
+      const char *f = entry + 8192 * cw;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) dma16(f + 1024 * i, 16 * lane, base + kStF + 8192 * cw + 1024 * i);
+      if (cw == 0) dma16(entry + 16384, 16 * lane, base + kStG);
+      const i32x4_t v_res = buffer_rsrc(v_src + int64_t(tok0) * v_row_bytes,
+                                        vblock_valid_bytes(len, v_row_bytes));
+#pragma unroll
+      for (int i = 0; i < 2; ++i) dma16_buf(v_res, v_voff[i], base + kStV + 2048 * cw + 1024 * i);
+    };
+    auto wait_all_but_newest_stage = [&]() {
+      if (cw == 0)
+        wait_vmem_upto<kStageLoadsW2>();
+      else
+        wait_vmem_upto<kStageLoadsW3>();
+    };
+    if (n_chunks > 0) {
+      stage(0, scan_stage0);
+      stage(min(1, n_chunks - 1), scan_stage1);
+      wait_all_but_newest_stage();
+    }
+    lds_barrier();
+    // In the phase of chunk cc (between the barriers that open chunks cc and
+    // cc + 1) the stage of chunk cc - 1 is free: the compute waves read it
+    // before the barrier that opened chunk cc.  Chunk cc + 2 goes there (past
+    // the end the last chunk is copied again, so every phase issues the same
+    // loads), then chunk cc + 1's stage must be complete.
+    auto phase = [&](int cc, char *dst) {
+      stage(min(cc + 2, n_chunks - 1), dst);
+      wait_all_but_newest_stage();
+      lds_barrier();
+    };
+    for (int cc = 0; cc < n_chunks; cc += 3) {
+      phase(cc, scan_stage2);
+      if (cc + 1 < n_chunks) phase(cc + 1, scan_stage0);
+      if (cc + 2 < n_chunks) phase(cc + 2, scan_stage1);
+    }
+    wait_vmem();  // the trailing copies
+    return;
+  }
+
+  // ---- compute waves ----
   const int col = 32 * cb + 16 * wave + r0;  // this lane's state column
 
   // ---- lane-invariant LDS byte offsets (relative to a stage) ----
@@ -247,12 +327,10 @@ __global__ __launch_bounds__(128) void scan_kernel_staged(ScanArgs<bf16_t> a) {
   // transposed v tile rt (rows 16 rt + 4 g + a / 4, columns 16 w + 4 (a mod 4)):
   // offset = 1024 rt + v_off.
   const int v_off = vtile_byte(4 * g + (r0 >> 2), 16 * wave + 4 * (r0 & 3));
-  // outputs as computed (transposed tiles: token row 16 rt + r0, columns
-  // 16 w + 4 g .. + 3, one 8-byte piece): offset = 1024 rt + o_woff.
-  const int o_woff = vtile_byte(out_acc_row(0, lane), out_acc_col(wave, lane));
-  // outputs leaving in 16-byte pieces: piece p of 2 covers row 32 p + lane / 2,
-  // columns 16 w + 8 (lane mod 2) .. + 7.
-  const int o_roff = vtile_byte(out_piece_row(0, lane), out_piece_col(wave, lane));
+  // outputs as computed (transposed tiles): token row 16 rt + r0, columns
+  // 16 w + 4 g .. + 3 of the block, one 8-byte store per tile
+  bf16_t *const o_lane = a.o + int64_t(start + out_acc_row(0, lane)) * v_stride + int64_t(h) * a.d_v +
+                         32 * cb + out_acc_col(wave, lane);
 
   // ---- state ----
   f32x4_t S[8];
@@ -264,86 +342,6 @@ __global__ __launch_bounds__(128) void scan_kernel_staged(ScanArgs<bf16_t> a) {
       for (int e = 0; e < 4; ++e)
         S[rt][e] = a.h0[st_base + int64_t(16 * rt + 4 * g + e) * a.d_v + col];
   }
-
-  int start, end;
-  a.geo.seq_bounds(s, start, end);
-  const int C = a.geo.chunk;
-  const int c_first = a.geo.first_chunk(s);
-  const int n_chunks = max(0, min((end - start + C - 1) / C, a.geo.n_slots - c_first));
-  const int64_t qk_stride = int64_t(a.H_qk) * 128;
-  const int64_t v_stride = int64_t(a.H_v) * a.d_v;
-  const uint32_t kq_row_bytes = uint32_t(2 * qk_stride), v_row_bytes = uint32_t(2 * v_stride);
-  const int64_t ebytes = entry_bytes<bf16_t>();
-  const char *kq_src = reinterpret_cast<const char *>(wave == 0 ? a.k : a.q) + int64_t(hq) * 256;
-  const char *v_src = reinterpret_cast<const char *>(a.v) + (int64_t(h) * a.d_v + 32 * cb) * 2;
-
-  // Per-lane byte offsets of every copy of a full chunk (tile_index.hpp),
-  // relative to the chunk's first row.  The k / q and v copies go through a
-  // buffer resource whose size ends at the chunk's last row, so rows past a
-  // partial chunk read as zeros (exact zeros that the chunk algebra only
-  // multiplies by zero) and no copy can leave the sequence.
-  uint32_t kq_voff[16];
-#pragma unroll
-  for (int i = 0; i < 16; ++i) kq_voff[i] = uint32_t(rowtile_copy_src(i, lane, 64, qk_stride));
-  uint32_t v_voff[2];
-#pragma unroll
-  for (int i = 0; i < 2; ++i) v_voff[i] = uint32_t(vblock_copy_src(2 * wave + i, lane, 64, v_stride));
-
-  // A stage's copies come in two parts, issued at different points of a
-  // chunk so that the vector-memory queue never holds all of them at once:
-  // the k or q row tile (16 copies), then the v block, the entry's fragments
-  // and (wave 0) its gate block.
-  auto stage_rows = [&](int cc, char *base_mem) {
-    const int tok0 = start + cc * C;
-    const int len = min(C, end - tok0);
-    lds_t *const base = lds_ptr(base_mem);
-    const i32x4_t kq_res = buffer_rsrc(kq_src + int64_t(tok0) * kq_row_bytes,
-                                       rowtile_valid_bytes(len, kq_row_bytes));
-    lds_t *const tile = base + (wave == 0 ? kStK : kStQ);
-#pragma unroll
-    for (int i = 0; i < 16; ++i) dma16_buf(kq_res, kq_voff[i], tile + 1024 * i);
-  };
-  auto stage_rest = [&](int cc, char *base_mem) {
-    const int tok0 = start + cc * C;
-    const int len = min(C, end - tok0);
-    lds_t *const base = lds_ptr(base_mem);
-    const char *entry = a.entries + (int64_t(c_first + cc) * a.H_v + h) * ebytes;
-    const i32x4_t v_res = buffer_rsrc(v_src + int64_t(tok0) * v_row_bytes,
-                                      vblock_valid_bytes(len, v_row_bytes));
-#pragma unroll
-    for (int i = 0; i < 2; ++i) dma16_buf(v_res, v_voff[i], base + kStV + 2048 * wave + 1024 * i);
-    const char *f = entry + 8192 * wave;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) dma16(f + 1024 * i, 16 * lane, base + kStF + 8192 * wave + 1024 * i);
-    if (wave == 0) dma16(entry + 16384, 16 * lane, base + kStG);
-  };
-  auto stage = [&](int cc, char *base_mem) {
-    stage_rows(cc, base_mem);
-    stage_rest(cc, base_mem);
-  };
-
-  auto wait_all_but_newest_stage = [&]() {
-    if (wave == 0)
-      wait_vmem_upto<kStageLoadsW0>();
-    else
-      wait_vmem_upto<kStageLoadsW1>();
-  };
-  // The outputs of chunk cc sit over this wave's v columns of its stage; they
-  // leave in two 16-byte pieces per lane.  (cc = -1 stores nothing: its row
-  // count is 0.)
-  auto store_outputs = [&](int cc, const char *stage_mem) {
-    const int tok0 = start + cc * C;
-    const int len = cc >= 0 ? min(C, end - tok0) : 0;
-    const lds_t *st = lds_ptr(const_cast<char *>(stage_mem));
-#pragma unroll
-    for (int p = 0; p < 2; ++p) {
-      const int row = out_piece_row(p, lane);
-      const u32x4_t piece = lds_load<u32x4_t>(st + kStV + 2048 * p + o_roff);
-      if (row < len)
-        *reinterpret_cast<u32x4_t *>(a.o + int64_t(tok0 + row) * v_stride + int64_t(h) * a.d_v +
-                                     32 * cb + out_piece_col(wave, lane)) = piece;
-    }
-  };
 
   // Operands of the chunk about to run, read from its stage right after the
   // barrier that completes it: gate factors (rows 16 rt + 4 g + e of this
@@ -380,27 +378,32 @@ __global__ __launch_bounds__(128) void scan_kernel_staged(ScanArgs<bf16_t> a) {
     for (int i = 0; i < 8; ++i) tf[i].v = lds_load<bf16x8_t>(st + kStF + 1024 * i + 16 * lane);
   };
 
-  if (n_chunks > 0) {
-    stage(0, scan_stage0);
-    stage(min(1, n_chunks - 1), scan_stage1);
-    wait_all_but_newest_stage();
-  }
-  lds_barrier();
-  read_operands(scan_stage0);
+  lds_barrier();  // the first two stages are complete
+  if (n_chunks > 0) read_operands(scan_stage0);
+
+  // A chunk's outputs wait in registers and leave after the next chunk's Y
+  // products: right after the barrier the copy waves fill the memory
+  // pipeline, and a store issued then would hold up this wave behind them.
+  bf16x4_t o_pend[4];
+  int o_chunk_pend = -1;
+  auto store_pending = [&]() {
+    if (o_chunk_pend < 0) return;
+    const int len = min(C, end - (start + o_chunk_pend * C));
+    bf16_t *const o_chunk = o_lane + int64_t(o_chunk_pend) * C * v_stride;
+#pragma unroll
+    for (int rt = 0; rt < 4; ++rt)
+      if (out_acc_row(rt, lane) < len)
+        *reinterpret_cast<bf16x4_t *>(o_chunk + int64_t(16 * rt) * v_stride) = o_pend[rt];
+  };
 
   // One chunk, software-pipelined: the state chain runs from the operands
   // read after the previous barrier; the q rows, K^T and P are read from the
-  // stage during the chain.  The barrier follows the state update, and the
-  // chunk's output products run after it, behind the reads of the next
-  // chunk's operands.  The previous chunk's outputs (in `prev`) leave before
-  // the prefetch of chunk cc + 2 reuses that stage.  The prefetch is issued
-  // every chunk (past the end it re-reads the last chunk), so each chunk
-  // issues the same loads, and no other vector-memory operation follows them
-  // in the chunk: the waits below are exact.
-  auto chunk_step = [&](int cc, char *cur_mem, char *prev_mem, char *next_mem) {
-    store_outputs(cc - 1, prev_mem);
-    const int pf_chunk = min(cc + 2, n_chunks - 1);
-    lds_t *const st = lds_ptr(cur_mem);
+  // stage during the chain.  The barrier follows the state update (after it
+  // the copy waves may reuse the previous chunk's stage), and the chunk's
+  // output products run after it, behind the reads of the next chunk's
+  // operands, and leave straight from their accumulators.
+  auto chunk_step = [&](int cc, char *cur_mem, char *next_mem) {
+    const lds_t *const st = lds_ptr(cur_mem);
 
     Frag<bf16_t> Sf[4];
 #pragma unroll
@@ -412,7 +415,7 @@ __global__ __launch_bounds__(128) void scan_kernel_staged(ScanArgs<bf16_t> a) {
     for (int kk = 0; kk < 4; ++kk)
 #pragma unroll
       for (int rt = 0; rt < 4; ++rt) Y[rt] = mfma(kf[kk][rt], Sf[kk], kk == 0 ? zero4() : Y[rt]);
-    stage_rows(pf_chunk, prev_mem);  // prefetch, part 1 (behind the Y products)
+    store_pending();  // the previous chunk's outputs
 
     // q rows, for the output products after the barrier
     Frag<bf16_t> qf[4][4];
@@ -435,7 +438,6 @@ __global__ __launch_bounds__(128) void scan_kernel_staged(ScanArgs<bf16_t> a) {
     for (int rt = 0; rt < 4; ++rt)
 #pragma unroll
       for (int kk = 0; kk < 2; ++kk) Ua[rt] = mfma(tf[rt * 2 + kk], Xf[kk], kk == 0 ? zero4() : Ua[rt]);
-    stage_rest(pf_chunk, prev_mem);  // prefetch, part 2 (behind the U products)
 
     // K^T fragments (transposed reads of the k tile) and P
     Frag<bf16_t> ktf[8][2];
@@ -467,18 +469,16 @@ __global__ __launch_bounds__(128) void scan_kernel_staged(ScanArgs<bf16_t> a) {
 #pragma unroll
     for (int rt = 0; rt < 4; ++rt) gt_o[rt] = gam_tok[rt];
 
-    // the next chunk's stage must be complete and this chunk's k, q, T and P
-    // reads done before the other wave may prefetch over this stage; then the
-    // next chunk's operands are read
-    wait_all_but_newest_stage();
+    // this chunk's stage reads are done (the copy waves may now refill the
+    // previous chunk's stage) and the next chunk's stage is complete
     lds_barrier();
-    read_operands(next_mem);
+    if (cc + 1 < n_chunks) read_operands(next_mem);
 
     // O = gamma (Q S) + P U with the chunk-start state, computed as
     // O^T = S^T (gamma Q^T) + U^T P^T: with the kappa fragment convention Sf
     // and Uf serve as A operands and the q rows and P fragments as B operands
     // unchanged, and each lane ends with four consecutive columns of one
-    // token row, written over this wave's v columns in one 8-byte store.
+    // token row, one 8-byte piece of the output.
 #pragma unroll
     for (int rt = 0; rt < 4; ++rt) {
       f32x4_t oq;
@@ -487,19 +487,16 @@ __global__ __launch_bounds__(128) void scan_kernel_staged(ScanArgs<bf16_t> a) {
       f32x4_t acc = gt_o[rt] * oq;
 #pragma unroll
       for (int kk = 0; kk < 2; ++kk) acc = mfma(Uf[kk], pf[rt * 2 + kk], acc);
-      lds_store<bf16x4_t>(st + kStV + 1024 * rt + o_woff, __builtin_convertvector(acc, bf16x4_t));
+      o_pend[rt] = __builtin_convertvector(acc, bf16x4_t);
     }
+    o_chunk_pend = cc;
   };
   for (int cc = 0; cc < n_chunks; cc += 3) {
-    chunk_step(cc, scan_stage0, scan_stage2, scan_stage1);
-    if (cc + 1 < n_chunks) chunk_step(cc + 1, scan_stage1, scan_stage0, scan_stage2);
-    if (cc + 2 < n_chunks) chunk_step(cc + 2, scan_stage2, scan_stage1, scan_stage0);
+    chunk_step(cc, scan_stage0, scan_stage1);
+    if (cc + 1 < n_chunks) chunk_step(cc + 1, scan_stage1, scan_stage2);
+    if (cc + 2 < n_chunks) chunk_step(cc + 2, scan_stage2, scan_stage0);
   }
-  if (n_chunks > 0) {
-    const int last = (n_chunks - 1) % 3;
-    store_outputs(n_chunks - 1, last == 0 ? scan_stage0 : last == 1 ? scan_stage1 : scan_stage2);
-  }
-  wait_vmem();  // the trailing prefetches
+  store_pending();
 
   if (a.hT) {
 #pragma unroll
@@ -536,7 +533,7 @@ hipError_t launch_scan(const Problem &p, const Workspace &ws, hipStream_t st) {
   const int64_t blocks = (int64_t(p.n_seqs) * p.H_v + 7) / 8 * 8 * (p.d_v / width);
   if (blocks == 0) return hipSuccess;
   if (staged) {
-    hipLaunchKernelGGL(scan_kernel_staged, dim3(unsigned(blocks)), dim3(128), 0, st,
+    hipLaunchKernelGGL(scan_kernel_staged, dim3(unsigned(blocks)), dim3(256), 0, st,
                        scan_args<bf16_t>(p, ws, width));
   } else if (p.dtype == 1) {
     hipLaunchKernelGGL(scan_kernel<bf16_t>, dim3(unsigned(blocks)), dim3(64), 0, st,
