@@ -208,34 +208,48 @@ __global__ __launch_bounds__(256) void prep_kernel(PrepArgs<T> a) {
 // buffer loads (rows past the chunk's end read as zeros, padded slots get
 // beta = 0 and add nothing to the gate).
 //
-// M = (I + A)^-1 in 16 x 16 blocks: D_b = (I + A_bb)^-1 by forward
-// substitution and M_bc = -D_b sum_{j=c}^{b-1} A_bj M_jc for b > c, the
-// products on fp32 MFMA.  The block columns of M are independent: wave 0
-// forms column 0 (9 products), wave 1 columns 1-3 (7); the part both need (gates,
-// A, the D_b) runs as one code path in both, so their shared LDS writes carry
-// identical values.  A stays in registers: by the symmetry of K K^T the tile
-// K_j K_b^T holds row t = 16 b + r of A_bj in lane (r, g) (columns
-// 16 j + 4 g .. + 3), the left-operand layout of the block products.  Waves 2
-// and 3 form P (t-blocks 0-2 and 3) and the gate factors, which go out
-// directly.  T stays in registers until P is formed; it is then assembled
-// over the dead q tile and leaves in 16-byte stores (48 KiB of LDS: three
-// workgroups per CU).
+// M = (I + A)^-1 in 16 x 16 blocks.  Wave 1 forms the diagonal blocks A_bb
+// and solves D_b = (I + A_bb)^-1 for all four b at once (lane 16 b + c owns
+// column c of D_b) by right-looking substitution: once x_j is final it is
+// subtracted from every later row, so the dependent chain is one FMA per step.
+// Wave 0 forms the six off-diagonal A_bj.  The off-diagonal blocks of M then
+// follow in two levels from 2 x 2 block inversion of the two 32 x 32 halves:
+//   M10 = -D1 A10 D0,  M32 = -D3 A32 D2,
+//   X20 = A20 D0 + A21 M10,  X21 = A21 D1,  X30 = A30 D0 + A31 M10,  X31 = A31 D1,
+//   M20 = -D2 X20,  M21 = -D2 X21,  M30 = -(D3 X30 + M32 X20),  M31 = -(D3 X31 + M32 X21)
+// (wave 0: M10, M20, M30; wave 1: M21, M31, M32), on fp32 MFMA.  A product
+// is formed in either orientation: with X in row layout (lane (r, g) holds
+// X[r][4g..4g+3]) and Y in column layout (lane (c, g) holds Y[4g..4g+3][c]),
+// one MFMA sequence gives XY in column layout and the same operands swapped
+// give XY in row layout -- the layout of a T fragment, so each block of T
+// leaves in one 8-byte store (two blocks side by side in one 16-byte store).
+// A stays in registers: the tile K_j K_b^T holds row 16 b + c of A_bj in lane
+// (c, g) (columns 16 j + 4 g .. + 3), i.e. A_bj in row layout; a diagonal tile
+// is symmetric, so the same tile read as A_bb in column layout stores the
+// transposed block the substitution reads.  Waves 2 and 3 form P (t-blocks
+// 0-2 and 3) and the gate factors.  Every factor goes straight from registers
+// to the workspace entry.
+//
+// LDS: fp32 16 x 16 blocks use 80-byte rows, and the block strides are chosen
+// so that the broadcast row reads of the substitution (one address per block)
+// and its column stores fall in distinct banks.
 // ---------------------------------------------------------------------------
 namespace {
 constexpr int kXK = 0;          // k rows, 64 x 128 bf16 row tile
-constexpr int kXQ = 16384;      // q rows; once P is formed, T is assembled here
+constexpr int kXQ = 16384;      // q rows
 constexpr int kXAlpha = 32768;  // alpha, 64 fp32
 constexpr int kXBeta = 33024;   // beta, 64 fp32
-// fp32 16 x 16 blocks (1 KiB, row-major) and gate vectors
-constexpr int kXAd = 33280;     // A_bb, b = 0..3
-constexpr int kXD = 37376;      // D_b
-constexpr int kXDt = 41472;     // D_b^T
-constexpr int kXM10 = 45568;    // M_10^T (wave 0)
-constexpr int kXM20 = 46592;    // M_20^T (wave 0)
-constexpr int kXM21 = 47616;    // M_21^T (wave 1)
-constexpr int kXG = 48640;      // g_t, 64 fp32
-constexpr int kXB = 48896;      // beta_t, 64 fp32 (0 past the chunk's end)
-constexpr int kXBytes = 49152;  // three workgroups per CU
+constexpr int kXG = 33280;      // g_t, 64 fp32
+constexpr int kXB = 33536;      // beta_t, 64 fp32 (0 past the chunk's end)
+constexpr int kXRow = 80;       // row stride of an fp32 16 x 16 block
+constexpr int kXAdT = 33792;    // A_bb^T (row j = column j of A_bb)
+constexpr int kXAdTBlk = 1296;  // 324 dwords: 4 mod 32
+constexpr int kXD = kXAdT + 4 * kXAdTBlk;  // D_b, row-major
+constexpr int kXDBlk = 1344;               // 336 dwords: 16 mod 32
+constexpr int kXDt = kXD + 4 * kXDBlk;     // D_b^T
+constexpr int kXDtBlk = 1296;
+constexpr int kXBytes = kXDt + 4 * kXDtBlk;  // 49536: three workgroups per CU
+static_assert(kXBytes <= 160 * 1024 / 3, "three factor workgroups per CU");
 }  // namespace
 
 __global__ __launch_bounds__(256) void factors_kernel(PrepArgs<bf16_t> a) {
@@ -284,87 +298,167 @@ __global__ __launch_bounds__(256) void factors_kernel(PrepArgs<bf16_t> a) {
                     lds_load_single<bf16x4_t>(p + kq_off[kk][1]));
   };
 
-  // T results kept in registers until the q tile is dead: this lane's column
-  // of its diagonal block (x, scaled by beta of slot `lane`) and up to four
-  // off-diagonal blocks in accumulator layout
-  float x[16];
-  f32x4_t mt[4];
-  float bl = 0.0f;
+  // fp32 16 x 16 block operands from LDS: row layout of a row-major block
+  // (lane (r, g) reads row r, columns 4 g .. + 3)
+  auto rowv = [&](int off) { return lds_load<f32x4_t>(sm + off + kXRow * r0 + 16 * g); };
+  // T block (b, cb) in row layout leaves as one half of fragment (b, cb / 2),
+  // scaled by beta of its columns 16 cb + 4 g .. + 3
+  bf16_t *const fragT = reinterpret_cast<bf16_t *>(entry);
+  auto t_half = [&](int cb, f32x4_t m) -> bf16x4_t {
+    const f32x4_t bc = lds_load<f32x4_t>(sm + kXB + 4 * (16 * cb + 4 * g));
+    return __builtin_convertvector(m * bc, bf16x4_t);
+  };
+  auto put_frag = [&](int f, bf16x4_t lo, bf16x4_t hi) {
+    *reinterpret_cast<bf16x8_t *>(fragT + kFragElems * f + 8 * lane) = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+  };
+  auto put_half = [&](int f, int hf, bf16x4_t v) {
+    *reinterpret_cast<bf16x4_t *>(fragT + kFragElems * f + 8 * lane + 4 * hf) = v;
+  };
+  const bf16x4_t zero_h = {0, 0, 0, 0};
+
   if (wave < 2) {
-    // ---- T: gates and betas of all slots for broadcast reads ----
-    bl = lane < len ? lds_load<float>(sm + kXBeta + 4 * lane) : 0.0f;
+    // gates and betas of all slots for broadcast reads (both waves write the
+    // same values and read only after their own writes)
+    const float bl = lane < len ? lds_load<float>(sm + kXBeta + 4 * lane) : 0.0f;
     lds_store<float>(sm + kXG + 4 * lane, gl);
     lds_store<float>(sm + kXB + 4 * lane, bl);
-    Frag<bf16_t> kf[4][4];
+    // gated tile: (K_j K_b^T)[4 g + e][c] read as row 16 b + c of A_bj, or, for
+    // j == b, as row 16 b + 4 g + e, column 16 b + c of A_bb (column layout)
+    auto k_tile = [&](int j, int b) {
+      f32x4_t acc = zero4();
 #pragma unroll
-    for (int rt = 0; rt < 4; ++rt)
+      for (int kk = 0; kk < 4; ++kk) acc = mfma(row_frag(kXK, j, kk), row_frag(kXK, b, kk), acc);
+      return acc;
+    };
+    if (wave == 0) {
+      // ---- off-diagonal A_bj (j < b) in row layout: row t = 16 b + r0 ----
+      f32x4_t At[4][3];
 #pragma unroll
-      for (int kk = 0; kk < 4; ++kk) kf[rt][kk] = row_frag(kXK, rt, kk);
-    // A_bj rows (wave 1 does not need A_b0, b > 0)
-    f32x4_t At[4][4];
+      for (int b = 1; b < 4; ++b)
 #pragma unroll
-    for (int b = 0; b < 4; ++b)
+        for (int j = 0; j < b; ++j) {
+          const f32x4_t acc = k_tile(j, b);
+          const int t = 16 * b + r0;
+          const float gt = lds_load<float>(sm + kXG + 4 * t), bt = lds_load<float>(sm + kXB + 4 * t);
+          const f32x4_t gi = lds_load<f32x4_t>(sm + kXG + 4 * (16 * j + 4 * g));
 #pragma unroll
-      for (int j = 0; j <= b; ++j) {
-        if (wave == 1 && j == 0 && b > 0) continue;
-        f32x4_t acc = zero4();
-#pragma unroll
-        for (int kk = 0; kk < 4; ++kk) acc = mfma(kf[j][kk], kf[b][kk], acc);
-        const int t = 16 * b + r0;
-        const float gt = lds_load<float>(sm + kXG + 4 * t), bt = lds_load<float>(sm + kXB + 4 * t);
-        const f32x4_t gi = lds_load<f32x4_t>(sm + kXG + 4 * (16 * j + 4 * g));
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int i = 16 * j + 4 * g + e;
-          At[b][j][e] = i < t ? bt * fast_exp2(gt - gi[e]) * acc[e] : 0.0f;
+          for (int e = 0; e < 4; ++e) At[b][j][e] = bt * fast_exp2(gt - gi[e]) * acc[e];
         }
-        if (j == b) lds_store<f32x4_t>(sm + kXAd + 1024 * b + 64 * r0 + 16 * g, At[b][b]);
+      Split16 As[4][3];
+#pragma unroll
+      for (int b = 1; b < 4; ++b)
+#pragma unroll
+        for (int j = 0; j < b; ++j) As[b][j] = split16(At[b][j]);
+      lds_barrier();  // D_b and D_b^T are in LDS
+      f32x4_t D[4];  // D_b, row layout
+      Split16 Drs[4], Dcs[3];
+#pragma unroll
+      for (int b = 0; b < 4; ++b) D[b] = rowv(kXD + kXDBlk * b);
+#pragma unroll
+      for (int b = 0; b < 3; ++b) Dcs[b] = split16(rowv(kXDt + kXDtBlk * b));  // column layout
+#pragma unroll
+      for (int b = 1; b < 4; ++b) Drs[b] = split16(D[b]);
+      const Split16 Y10c = split16(mm16x3(As[1][0], Dcs[0], zero4()));
+      const Split16 M10c = split16(-mm16x3(Drs[1], Y10c, zero4()));
+      const f32x4_t M10r = -mm16x3(Y10c, Drs[1], zero4());
+      const Split16 M32r = split16(-mm16x3(split16(mm16x3(As[3][2], Dcs[2], zero4())), Drs[3], zero4()));
+      const Split16 X20c = split16(mm16x3(As[2][1], M10c, mm16x3(As[2][0], Dcs[0], zero4())));
+      const Split16 X30c = split16(mm16x3(As[3][1], M10c, mm16x3(As[3][0], Dcs[0], zero4())));
+      const f32x4_t M20r = -mm16x3(X20c, Drs[2], zero4());
+      const f32x4_t M30r = -mm16x3(X20c, M32r, mm16x3(X30c, Drs[3], zero4()));
+      auto Dr = [&](int b) { return D[b]; };
+      // fragments (0, 0) = [D0 | 0], (0, 1) = 0, (1, 0) = [M10 | D1], (1, 1) = 0,
+      // and the left halves of (2, 0) and (3, 0)
+      put_frag(0, t_half(0, Dr(0)), zero_h);
+      put_frag(1, zero_h, zero_h);
+      put_frag(2, t_half(0, M10r), t_half(1, Dr(1)));
+      put_frag(3, zero_h, zero_h);
+      put_half(4, 0, t_half(0, M20r));
+      put_half(6, 0, t_half(0, M30r));
+    } else {
+      // ---- diagonal blocks, stored transposed: A_bb^T[c][4 g + e] ----
+#pragma unroll
+      for (int b = 0; b < 4; ++b) {
+        const f32x4_t acc = k_tile(b, b);
+        const int i = 16 * b + r0;  // column of A (the tile's c)
+        const float gi = lds_load<float>(sm + kXG + 4 * i);
+        const f32x4_t gt = lds_load<f32x4_t>(sm + kXG + 4 * (16 * b + 4 * g));
+        const f32x4_t bt = lds_load<f32x4_t>(sm + kXB + 4 * (16 * b + 4 * g));
+        f32x4_t v;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v[e] = 4 * g + e > r0 ? bt[e] * fast_exp2(gt[e] - gi) * acc[e] : 0.0f;
+        lds_store<f32x4_t>(sm + kXAdT + kXAdTBlk * b + kXRow * r0 + 16 * g, v);
       }
-    // D_b by forward substitution: lane (b = g, column r0) solves for column
-    // r0 of D_b; then D_b row-major and D_b^T (this lane's column as a row)
-    {
-      const lds_t *ab = sm + kXAd + 1024 * g;
+      // ---- D_b = (I + A_bb)^-1: lane (b = g, column r0), right-looking ----
+      {
+        const lds_t *ab = sm + kXAdT + kXAdTBlk * g;
+        float x[16];
 #pragma unroll
-      for (int t = 0; t < 16; ++t) {
-        float v = t == r0 ? 1.0f : 0.0f;
+        for (int t = 0; t < 16; ++t) x[t] = t == r0 ? 1.0f : 0.0f;
+        // column j of A_bb (rows t > j) is row j of A_bb^T; rows are read
+        // two steps ahead of their use
+        f32x4_t col[3][4];
+        auto read_col = [&](int j, f32x4_t *dst) {
 #pragma unroll
-        for (int q4 = 0; q4 < 4; ++q4) {
-          if (4 * q4 < t) {
-            const f32x4_t arow = lds_load<f32x4_t>(ab + 64 * t + 16 * q4);
+          for (int q4 = (j + 1) / 4; q4 < 4; ++q4) dst[q4] = lds_load<f32x4_t>(ab + kXRow * j + 16 * q4);
+        };
+        read_col(0, col[0]);
+        read_col(1, col[1]);
+#pragma unroll
+        for (int j = 0; j < 15; ++j) {
+          if (j + 2 < 15) read_col(j + 2, col[(j + 2) % 3]);
+#pragma unroll
+          for (int q4 = (j + 1) / 4; q4 < 4; ++q4)
 #pragma unroll
             for (int e = 0; e < 4; ++e)
-              if (4 * q4 + e < t) v -= arow[e] * x[4 * q4 + e];
-          }
+              if (4 * q4 + e > j) x[4 * q4 + e] -= col[j % 3][q4][e] * x[j];
         }
-        x[t] = v;
+        // D_b row-major (this lane's column) and D_b^T (this lane's column as a row)
+#pragma unroll
+        for (int t = 0; t < 16; ++t) lds_store<float>(sm + kXD + kXDBlk * g + kXRow * t + 4 * r0, x[t]);
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4)
+          lds_store<f32x4_t>(sm + kXDt + kXDtBlk * g + kXRow * r0 + 16 * q4,
+                             f32x4_t{x[4 * q4], x[4 * q4 + 1], x[4 * q4 + 2], x[4 * q4 + 3]});
       }
+      // ---- A21, A31, A32 in row layout ----
+      f32x4_t At[4][3];
 #pragma unroll
-      for (int t = 0; t < 16; ++t) lds_store<float>(sm + kXD + 1024 * g + 64 * t + 4 * r0, x[t]);
+      for (int b = 2; b < 4; ++b)
 #pragma unroll
-      for (int q4 = 0; q4 < 4; ++q4)
-        lds_store<f32x4_t>(sm + kXDt + 1024 * g + 64 * r0 + 16 * q4,
-                           f32x4_t{x[4 * q4], x[4 * q4 + 1], x[4 * q4 + 2], x[4 * q4 + 3]});
-    }
-    auto rowv = [&](int off) { return lds_load<f32x4_t>(sm + off + 64 * r0 + 16 * g); };
-    if (wave == 0) {
-      // block column 0 (the longest dependency chain): M10, M20, M30
-      mt[0] = -mm16(rowv(kXD + 1024 * 1), mm16(At[1][0], rowv(kXDt + 1024 * 0), zero4()), zero4());
-      lds_store<f32x4_t>(sm + kXM10 + 64 * r0 + 16 * g, mt[0]);
-      const f32x4_t Y20 = mm16(At[2][1], rowv(kXM10), mm16(At[2][0], rowv(kXDt + 1024 * 0), zero4()));
-      mt[1] = -mm16(rowv(kXD + 1024 * 2), Y20, zero4());
-      lds_store<f32x4_t>(sm + kXM20 + 64 * r0 + 16 * g, mt[1]);
-      const f32x4_t Y30 =
-          mm16(At[3][2], rowv(kXM20), mm16(At[3][1], rowv(kXM10), mm16(At[3][0], rowv(kXDt + 1024 * 0), zero4())));
-      mt[2] = -mm16(rowv(kXD + 1024 * 3), Y30, zero4());
-    } else {
-      // block columns 1 to 3: M21, M31, M32
-      mt[0] = -mm16(rowv(kXD + 1024 * 2), mm16(At[2][1], rowv(kXDt + 1024 * 1), zero4()), zero4());
-      lds_store<f32x4_t>(sm + kXM21 + 64 * r0 + 16 * g, mt[0]);
-      mt[2] = -mm16(rowv(kXD + 1024 * 3), mm16(At[3][2], rowv(kXDt + 1024 * 2), zero4()), zero4());
-      const f32x4_t Y31 = mm16(At[3][2], rowv(kXM21), mm16(At[3][1], rowv(kXDt + 1024 * 1), zero4()));
-      mt[1] = -mm16(rowv(kXD + 1024 * 3), Y31, zero4());
+        for (int j = 1; j < b; ++j) {
+          const f32x4_t acc = k_tile(j, b);
+          const int t = 16 * b + r0;
+          const float gt = lds_load<float>(sm + kXG + 4 * t), bt = lds_load<float>(sm + kXB + 4 * t);
+          const f32x4_t gi = lds_load<f32x4_t>(sm + kXG + 4 * (16 * j + 4 * g));
+#pragma unroll
+          for (int e = 0; e < 4; ++e) At[b][j][e] = bt * fast_exp2(gt - gi[e]) * acc[e];
+        }
+      const Split16 A21 = split16(At[2][1]), A31 = split16(At[3][1]), A32 = split16(At[3][2]);
+      lds_barrier();  // D_b and D_b^T are in LDS
+      f32x4_t D[4];  // D_b, row layout (b >= 1)
+      Split16 Drs[4], Dcs[3];
+#pragma unroll
+      for (int b = 1; b < 4; ++b) D[b] = rowv(kXD + kXDBlk * b);
+#pragma unroll
+      for (int b = 1; b < 3; ++b) Dcs[b] = split16(rowv(kXDt + kXDtBlk * b));  // column layout
+#pragma unroll
+      for (int b = 2; b < 4; ++b) Drs[b] = split16(D[b]);
+      const f32x4_t M32 = -mm16x3(split16(mm16x3(A32, Dcs[2], zero4())), Drs[3], zero4());
+      const Split16 M32r = split16(M32);
+      const Split16 X21c = split16(mm16x3(A21, Dcs[1], zero4()));
+      const f32x4_t M21r = -mm16x3(X21c, Drs[2], zero4());
+      const Split16 X31c = split16(mm16x3(A31, Dcs[1], zero4()));
+      const f32x4_t M31r = -mm16x3(X21c, M32r, mm16x3(X31c, Drs[3], zero4()));
+      auto Dr = [&](int b) { return D[b]; };
+      // the right halves of (2, 0) and (3, 0); (2, 1) = [D2 | 0], (3, 1) = [M32 | D3]
+      put_half(4, 1, t_half(1, M21r));
+      put_half(6, 1, t_half(1, M31r));
+      put_frag(5, t_half(2, Dr(2)), zero_h);
+      put_frag(7, t_half(2, M32), t_half(3, Dr(3)));
     }
   } else {
+    lds_barrier();  // pairs with the barrier of waves 0 and 1, which only they need
     // ---- P and the gate factors: wave 2 t-blocks 0-2, wave 3 t-block 3 ----
     // P^T tile (i-block r, t-block cb), r <= cb: its lane layout is the A
     // fragment layout of P (row t, contraction i), so its four values are half
@@ -405,55 +499,6 @@ __global__ __launch_bounds__(256) void factors_kernel(PrepArgs<bf16_t> a) {
       gate_out[lane] = exp2f(gl);
       gate_out[64 + lane] = exp2f(g_last - gl);
     }
-  }
-  lds_barrier();  // every factor is formed: the q tile is dead
-  if (wave < 2) {
-    lds_t *const tf = sm + kXQ;
-    // T entries of an off-diagonal block from its accumulator (rows 4 g + e,
-    // column r0): T[16 b + 4 g + e][16 c + r0] = M beta_(16 c + r0), in
-    // fragment (b, c / 2), lane 4 g + e + 16 (r0 / 4), element 4 (c mod 2) + r0 mod 4
-    auto put_t = [&](int b, int cb, f32x4_t m) {
-      const float bc = lds_load<float>(sm + kXB + 4 * (16 * cb + r0));
-      const int f = 2 * b + (cb >> 1);
-#pragma unroll
-      for (int e = 0; e < 4; ++e)
-        lds_store<bf16_t>(tf + 1024 * f + 16 * ((4 * g + e) + 16 * (r0 >> 2)) + 2 * (4 * (cb & 1) + (r0 & 3)),
-                          from_f32<bf16_t>(m[e] * bc));
-    };
-    // T entries of this lane's column of its diagonal block (b = g):
-    // T[16 b + t][16 b + r0] = x[t] beta_(16 b + r0), fragment (b, b / 2),
-    // lane t + 16 (r0 / 4), element 4 (b mod 2) + r0 mod 4
-    auto put_diag = [&]() {
-      const int b = g, f = 2 * b + (b >> 1);
-#pragma unroll
-      for (int t = 0; t < 16; ++t)
-        lds_store<bf16_t>(tf + 1024 * f + 16 * (t + 16 * (r0 >> 2)) + 2 * (4 * (b & 1) + (r0 & 3)),
-                          from_f32<bf16_t>(x[t] * bl));
-    };
-    if (wave == 0) {
-      if (g == 0) put_diag();
-      put_t(1, 0, mt[0]);
-      put_t(2, 0, mt[1]);
-      put_t(3, 0, mt[2]);
-      // blocks above the diagonal: fragments (0, 1) and (1, 1) whole, the
-      // upper halves of (0, 0) and (2, 1)
-      lds_store<u32x4_t>(tf + 1024 * 1 + 16 * lane, u32x4_t{0, 0, 0, 0});
-      lds_store<u32x4_t>(tf + 1024 * 3 + 16 * lane, u32x4_t{0, 0, 0, 0});
-      lds_store<uint64_t>(tf + 1024 * 0 + 16 * lane + 8, uint64_t(0));
-      lds_store<uint64_t>(tf + 1024 * 5 + 16 * lane + 8, uint64_t(0));
-    } else {
-      if (g > 0) put_diag();
-      put_t(2, 1, mt[0]);
-      put_t(3, 1, mt[1]);
-      put_t(3, 2, mt[2]);
-    }
-  }
-  lds_barrier();
-  // ---- T leaves in 16-byte stores (8 KiB, 32 bytes per thread) ----
-#pragma unroll
-  for (int q2 = 0; q2 < 2; ++q2) {
-    const int off = 16 * (tid + 256 * q2);
-    *reinterpret_cast<u32x4_t *>(entry + off) = lds_load<u32x4_t>(sm + kXQ + off);
   }
 }
 

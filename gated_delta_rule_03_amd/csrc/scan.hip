@@ -220,7 +220,12 @@ __shared__ __attribute__((aligned(16))) char scan_stage0[kStBytes];
 __shared__ __attribute__((aligned(16))) char scan_stage1[kStBytes];
 __shared__ __attribute__((aligned(16))) char scan_stage2[kStBytes];
 
-__global__ __launch_bounds__(256) void scan_kernel_staged(ScanArgs<bf16_t> a) {
+// NG = 16-column groups per compute wave: 2 compute waves of one group, or
+// one compute wave of two groups (which reads each k, q, T and P fragment
+// once for both).  The copy waves follow the compute waves.
+template <int NG>
+__global__ __launch_bounds__(64 * (2 / NG + 2)) void scan_kernel_staged(ScanArgs<bf16_t> a) {
+  constexpr int kCompute = 2 / NG;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int r0 = lane & 15, g = lane >> 4;
@@ -237,9 +242,9 @@ __global__ __launch_bounds__(256) void scan_kernel_staged(ScanArgs<bf16_t> a) {
   const int64_t qk_stride = int64_t(a.H_qk) * 128;
   const int64_t v_stride = int64_t(a.H_v) * a.d_v;
 
-  if (wave >= 2) {
+  if (wave >= kCompute) {
     // ---- copy waves ----
-    const int cw = wave - 2;  // 0: k tile, T, gates; 1: q tile, P
+    const int cw = wave - kCompute;  // 0: k tile, T, gates; 1: q tile, P
     const uint32_t kq_row_bytes = uint32_t(2 * qk_stride), v_row_bytes = uint32_t(2 * v_stride);
     const int64_t ebytes = entry_bytes<bf16_t>();
     const char *kq_src = reinterpret_cast<const char *>(cw == 0 ? a.k : a.q) + int64_t(hq) * 256;
@@ -306,9 +311,7 @@ __global__ __launch_bounds__(256) void scan_kernel_staged(ScanArgs<bf16_t> a) {
     return;
   }
 
-  // ---- compute waves ----
-  const int col = 32 * cb + 16 * wave + r0;  // this lane's state column
-
+  // ---- compute waves: 16-column groups grp = NG wave + cg of the block ----
   // ---- lane-invariant LDS byte offsets (relative to a stage) ----
   // A fragments of k / q rows 16 rt + r0, columns 32 kk + 16 half + 4 g:
   // offset = 4096 rt + kq_off[kk][half].
@@ -324,24 +327,34 @@ __global__ __launch_bounds__(256) void scan_kernel_staged(ScanArgs<bf16_t> a) {
   int kt_off[8];
 #pragma unroll
   for (int rm = 0; rm < 8; ++rm) kt_off[rm] = 2 * rowtile_off(4 * g + (r0 >> 2), 16 * rm + 4 * (r0 & 3));
-  // transposed v tile rt (rows 16 rt + 4 g + a / 4, columns 16 w + 4 (a mod 4)):
-  // offset = 1024 rt + v_off.
-  const int v_off = vtile_byte(4 * g + (r0 >> 2), 16 * wave + 4 * (r0 & 3));
+  // transposed v tile rt of group grp (rows 16 rt + 4 g + a / 4, columns
+  // 16 grp + 4 (a mod 4)): offset = 1024 rt + v_off[cg].
+  int v_off[NG];
   // outputs as computed (transposed tiles): token row 16 rt + r0, columns
-  // 16 w + 4 g .. + 3 of the block, one 8-byte store per tile
-  bf16_t *const o_lane = a.o + int64_t(start + out_acc_row(0, lane)) * v_stride + int64_t(h) * a.d_v +
-                         32 * cb + out_acc_col(wave, lane);
+  // 16 grp + 4 g .. + 3 of the block, one 8-byte store per tile
+  bf16_t *o_lane[NG];
+  int col[NG];  // this lane's state column in each group
+#pragma unroll
+  for (int cg = 0; cg < NG; ++cg) {
+    const int grp = NG * wave + cg;
+    v_off[cg] = vtile_byte(4 * g + (r0 >> 2), 16 * grp + 4 * (r0 & 3));
+    o_lane[cg] = a.o + int64_t(start + out_acc_row(0, lane)) * v_stride + int64_t(h) * a.d_v + 32 * cb +
+                 out_acc_col(grp, lane);
+    col[cg] = 32 * cb + 16 * grp + r0;
+  }
 
   // ---- state ----
-  f32x4_t S[8];
+  f32x4_t S[NG][8];
   const int64_t st_base = (int64_t(s) * a.H_v + h) * 128 * a.d_v;
 #pragma unroll
-  for (int rt = 0; rt < 8; ++rt) {
-    S[rt] = zero4();
-    if (a.h0)
-      for (int e = 0; e < 4; ++e)
-        S[rt][e] = a.h0[st_base + int64_t(16 * rt + 4 * g + e) * a.d_v + col];
-  }
+  for (int cg = 0; cg < NG; ++cg)
+#pragma unroll
+    for (int rt = 0; rt < 8; ++rt) {
+      S[cg][rt] = zero4();
+      if (a.h0)
+        for (int e = 0; e < 4; ++e)
+          S[cg][rt][e] = a.h0[st_base + int64_t(16 * rt + 4 * g + e) * a.d_v + col[cg]];
+    }
 
   // Operands of the chunk about to run, read from its stage right after the
   // barrier that completes it: gate factors (rows 16 rt + 4 g + e of this
@@ -353,7 +366,7 @@ __global__ __launch_bounds__(256) void scan_kernel_staged(ScanArgs<bf16_t> a) {
   f32x4_t gam[4], sc[4];
   float gam_tok[4];
   Frag<bf16_t> kf[4][4];  // k rows: [contraction block][row tile]
-  bf16x4_t vt[4];         // v, transposed: four rows of this lane's column
+  bf16x4_t vt[NG][4];     // v, transposed: four rows of this lane's column
   Frag<bf16_t> tf[8];
   auto read_operands = [&](const char *stage_mem) {
     const lds_t *st = lds_ptr(const_cast<char *>(stage_mem));
@@ -373,7 +386,9 @@ __global__ __launch_bounds__(256) void scan_kernel_staged(ScanArgs<bf16_t> a) {
                               lds_load_single<bf16x4_t>(pk + kq_off[kk][1]));
       }
 #pragma unroll
-    for (int rt = 0; rt < 4; ++rt) vt[rt] = lds_read_tr16(st + kStV + 1024 * rt + v_off);
+    for (int cg = 0; cg < NG; ++cg)
+#pragma unroll
+      for (int rt = 0; rt < 4; ++rt) vt[cg][rt] = lds_read_tr16(st + kStV + 1024 * rt + v_off[cg]);
 #pragma unroll
     for (int i = 0; i < 8; ++i) tf[i].v = lds_load<bf16x8_t>(st + kStF + 1024 * i + 16 * lane);
   };
@@ -384,16 +399,19 @@ __global__ __launch_bounds__(256) void scan_kernel_staged(ScanArgs<bf16_t> a) {
   // A chunk's outputs wait in registers and leave after the next chunk's Y
   // products: right after the barrier the copy waves fill the memory
   // pipeline, and a store issued then would hold up this wave behind them.
-  bf16x4_t o_pend[4];
+  bf16x4_t o_pend[NG][4];
   int o_chunk_pend = -1;
   auto store_pending = [&]() {
     if (o_chunk_pend < 0) return;
     const int len = min(C, end - (start + o_chunk_pend * C));
-    bf16_t *const o_chunk = o_lane + int64_t(o_chunk_pend) * C * v_stride;
 #pragma unroll
-    for (int rt = 0; rt < 4; ++rt)
-      if (out_acc_row(rt, lane) < len)
-        *reinterpret_cast<bf16x4_t *>(o_chunk + int64_t(16 * rt) * v_stride) = o_pend[rt];
+    for (int cg = 0; cg < NG; ++cg) {
+      bf16_t *const o_chunk = o_lane[cg] + int64_t(o_chunk_pend) * C * v_stride;
+#pragma unroll
+      for (int rt = 0; rt < 4; ++rt)
+        if (out_acc_row(rt, lane) < len)
+          *reinterpret_cast<bf16x4_t *>(o_chunk + int64_t(16 * rt) * v_stride) = o_pend[cg][rt];
+    }
   };
 
   // One chunk, software-pipelined: the state chain runs from the operands
@@ -401,20 +419,25 @@ __global__ __launch_bounds__(256) void scan_kernel_staged(ScanArgs<bf16_t> a) {
   // stage during the chain.  The barrier follows the state update (after it
   // the copy waves may reuse the previous chunk's stage), and the chunk's
   // output products run after it, behind the reads of the next chunk's
-  // operands, and leave straight from their accumulators.
+  // operands.  With two groups each operand fragment serves both.
   auto chunk_step = [&](int cc, char *cur_mem, char *next_mem) {
     const lds_t *const st = lds_ptr(cur_mem);
 
-    Frag<bf16_t> Sf[4];
+    Frag<bf16_t> Sf[NG][4];
 #pragma unroll
-    for (int kk = 0; kk < 4; ++kk) Sf[kk] = frag_from_acc<bf16_t>(S[2 * kk], S[2 * kk + 1]);
+    for (int cg = 0; cg < NG; ++cg)
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk) Sf[cg][kk] = frag_from_acc<bf16_t>(S[cg][2 * kk], S[cg][2 * kk + 1]);
 
     // Y = K S
-    f32x4_t Y[4];
+    f32x4_t Y[NG][4];
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk)
 #pragma unroll
-      for (int rt = 0; rt < 4; ++rt) Y[rt] = mfma(kf[kk][rt], Sf[kk], kk == 0 ? zero4() : Y[rt]);
+      for (int rt = 0; rt < 4; ++rt)
+#pragma unroll
+        for (int cg = 0; cg < NG; ++cg)
+          Y[cg][rt] = mfma(kf[kk][rt], Sf[cg][kk], kk == 0 ? zero4() : Y[cg][rt]);
     store_pending();  // the previous chunk's outputs
 
     // q rows, for the output products after the barrier
@@ -429,15 +452,23 @@ __global__ __launch_bounds__(256) void scan_kernel_staged(ScanArgs<bf16_t> a) {
       }
 
     // X = V - gamma Y, then U = T X
-    f32x4_t X[4];
+    Frag<bf16_t> Xf[NG][2];
 #pragma unroll
-    for (int rt = 0; rt < 4; ++rt) X[rt] = __builtin_convertvector(vt[rt], f32x4_t) - gam[rt] * Y[rt];
-    const Frag<bf16_t> Xf[2] = {frag_from_acc<bf16_t>(X[0], X[1]), frag_from_acc<bf16_t>(X[2], X[3])};
-    f32x4_t Ua[4];
+    for (int cg = 0; cg < NG; ++cg) {
+      f32x4_t X[4];
+#pragma unroll
+      for (int rt = 0; rt < 4; ++rt) X[rt] = __builtin_convertvector(vt[cg][rt], f32x4_t) - gam[rt] * Y[cg][rt];
+      Xf[cg][0] = frag_from_acc<bf16_t>(X[0], X[1]);
+      Xf[cg][1] = frag_from_acc<bf16_t>(X[2], X[3]);
+    }
+    f32x4_t Ua[NG][4];
 #pragma unroll
     for (int rt = 0; rt < 4; ++rt)
 #pragma unroll
-      for (int kk = 0; kk < 2; ++kk) Ua[rt] = mfma(tf[rt * 2 + kk], Xf[kk], kk == 0 ? zero4() : Ua[rt]);
+      for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+        for (int cg = 0; cg < NG; ++cg)
+          Ua[cg][rt] = mfma(tf[rt * 2 + kk], Xf[cg][kk], kk == 0 ? zero4() : Ua[cg][rt]);
 
     // K^T fragments (transposed reads of the k tile) and P
     Frag<bf16_t> ktf[8][2];
@@ -452,19 +483,27 @@ __global__ __launch_bounds__(256) void scan_kernel_staged(ScanArgs<bf16_t> a) {
 #pragma unroll
     for (int i = 0; i < 8; ++i) pf[i].v = lds_load<bf16x8_t>(st + kStF + 8192 + 1024 * i + 16 * lane);
 
-    const Frag<bf16_t> Uf[2] = {frag_from_acc<bf16_t>(Ua[0], Ua[1]), frag_from_acc<bf16_t>(Ua[2], Ua[3])};
+    Frag<bf16_t> Uf[NG][2], Usf[NG][2];
 #pragma unroll
-    for (int rt = 0; rt < 4; ++rt) Ua[rt] *= sc[rt];
-    const Frag<bf16_t> Usf[2] = {frag_from_acc<bf16_t>(Ua[0], Ua[1]), frag_from_acc<bf16_t>(Ua[2], Ua[3])};
+    for (int cg = 0; cg < NG; ++cg) {
+      Uf[cg][0] = frag_from_acc<bf16_t>(Ua[cg][0], Ua[cg][1]);
+      Uf[cg][1] = frag_from_acc<bf16_t>(Ua[cg][2], Ua[cg][3]);
+#pragma unroll
+      for (int rt = 0; rt < 4; ++rt) Ua[cg][rt] *= sc[rt];
+      Usf[cg][0] = frag_from_acc<bf16_t>(Ua[cg][0], Ua[cg][1]);
+      Usf[cg][1] = frag_from_acc<bf16_t>(Ua[cg][2], Ua[cg][3]);
+    }
 
     // S <- gamma_C S + K^T (s U)
 #pragma unroll
-    for (int rm = 0; rm < 8; ++rm) {
-      f32x4_t acc = gamma_C * S[rm];
+    for (int rm = 0; rm < 8; ++rm)
 #pragma unroll
-      for (int kk = 0; kk < 2; ++kk) acc = mfma(ktf[rm][kk], Usf[kk], acc);
-      S[rm] = acc;
-    }
+      for (int cg = 0; cg < NG; ++cg) {
+        f32x4_t acc = gamma_C * S[cg][rm];
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk) acc = mfma(ktf[rm][kk], Usf[cg][kk], acc);
+        S[cg][rm] = acc;
+      }
     float gt_o[4];
 #pragma unroll
     for (int rt = 0; rt < 4; ++rt) gt_o[rt] = gam_tok[rt];
@@ -480,15 +519,17 @@ __global__ __launch_bounds__(256) void scan_kernel_staged(ScanArgs<bf16_t> a) {
     // unchanged, and each lane ends with four consecutive columns of one
     // token row, one 8-byte piece of the output.
 #pragma unroll
-    for (int rt = 0; rt < 4; ++rt) {
-      f32x4_t oq;
+    for (int rt = 0; rt < 4; ++rt)
 #pragma unroll
-      for (int kk = 0; kk < 4; ++kk) oq = mfma(Sf[kk], qf[kk][rt], kk == 0 ? zero4() : oq);
-      f32x4_t acc = gt_o[rt] * oq;
+      for (int cg = 0; cg < NG; ++cg) {
+        f32x4_t oq;
 #pragma unroll
-      for (int kk = 0; kk < 2; ++kk) acc = mfma(Uf[kk], pf[rt * 2 + kk], acc);
-      o_pend[rt] = __builtin_convertvector(acc, bf16x4_t);
-    }
+        for (int kk = 0; kk < 4; ++kk) oq = mfma(Sf[cg][kk], qf[kk][rt], kk == 0 ? zero4() : oq);
+        f32x4_t acc = gt_o[rt] * oq;
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk) acc = mfma(Uf[cg][kk], pf[rt * 2 + kk], acc);
+        o_pend[cg][rt] = __builtin_convertvector(acc, bf16x4_t);
+      }
     o_chunk_pend = cc;
   };
   for (int cc = 0; cc < n_chunks; cc += 3) {
@@ -500,11 +541,17 @@ __global__ __launch_bounds__(256) void scan_kernel_staged(ScanArgs<bf16_t> a) {
 
   if (a.hT) {
 #pragma unroll
-    for (int rt = 0; rt < 8; ++rt)
-      for (int e = 0; e < 4; ++e)
-        a.hT[st_base + int64_t(16 * rt + 4 * g + e) * a.d_v + col] = S[rt][e];
+    for (int cg = 0; cg < NG; ++cg)
+#pragma unroll
+      for (int rt = 0; rt < 8; ++rt)
+        for (int e = 0; e < 4; ++e)
+          a.hT[st_base + int64_t(16 * rt + 4 * g + e) * a.d_v + col[cg]] = S[cg][rt][e];
   }
 }
+
+#ifndef SCAN_GROUPS
+#define SCAN_GROUPS 1
+#endif
 
 template <typename T>
 static ScanArgs<T> scan_args(const Problem &p, const Workspace &ws, int colblk_width) {
@@ -533,7 +580,7 @@ hipError_t launch_scan(const Problem &p, const Workspace &ws, hipStream_t st) {
   const int64_t blocks = (int64_t(p.n_seqs) * p.H_v + 7) / 8 * 8 * (p.d_v / width);
   if (blocks == 0) return hipSuccess;
   if (staged) {
-    hipLaunchKernelGGL(scan_kernel_staged, dim3(unsigned(blocks)), dim3(256), 0, st,
+    hipLaunchKernelGGL(scan_kernel_staged<SCAN_GROUPS>, dim3(unsigned(blocks)), dim3(64 * (2 / SCAN_GROUPS + 2)), 0, st,
                        scan_args<bf16_t>(p, ws, width));
   } else if (p.dtype == 1) {
     hipLaunchKernelGGL(scan_kernel<bf16_t>, dim3(unsigned(blocks)), dim3(64), 0, st,

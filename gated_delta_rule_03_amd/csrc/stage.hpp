@@ -183,4 +183,29 @@ __device__ __forceinline__ f32x4_t mm16(f32x4_t xr, f32x4_t yt, f32x4_t acc) {
   return acc;
 }
 
+// The same 16 x 16 x 16 product from bf16 MFMAs with each fp32 operand split
+// as x = hi + lo (hi = bf16(x), lo = bf16(x - hi)): hi*hi + lo*hi + hi*lo
+// carries about 16 significant bits (the dropped lo*lo term is ~2^-16
+// relative).  One 16 x 16 x 32 MFMA takes [x_hi | x_lo] against
+// [y_hi ; y_hi] (the operand's contraction index 4 g + j sits in elements
+// j and 4 + j of the kappa fragment), a second [x_hi | x_lo] against
+// [y_lo ; 0].
+struct Split16 {
+  bf16x4_t hi, lo;
+};
+__device__ __forceinline__ Split16 split16(f32x4_t x) {
+  Split16 s;
+  s.hi = __builtin_convertvector(x, bf16x4_t);
+  s.lo = __builtin_convertvector(x - __builtin_convertvector(s.hi, f32x4_t), bf16x4_t);
+  return s;
+}
+__device__ __forceinline__ f32x4_t mm16x3(const Split16 &x, const Split16 &y, f32x4_t acc) {
+  const bf16x4_t z = {0, 0, 0, 0};
+  const bf16x8_t a = __builtin_shufflevector(x.hi, x.lo, 0, 1, 2, 3, 4, 5, 6, 7);
+  const bf16x8_t b1 = __builtin_shufflevector(y.hi, y.hi, 0, 1, 2, 3, 4, 5, 6, 7);
+  const bf16x8_t b2 = __builtin_shufflevector(y.lo, z, 0, 1, 2, 3, 4, 5, 6, 7);
+  acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b1, acc, 0, 0, 0);
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b2, acc, 0, 0, 0);
+}
+
 }  // namespace gdn
