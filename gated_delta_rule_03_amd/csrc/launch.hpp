@@ -28,14 +28,21 @@ int64_t chunk_slots(const Problem &p);
 // One workspace entry per (chunk slot, value head): the intra-chunk factors
 // in MFMA fragment order -- T (8 fragments), P (8 fragments) of 64 lanes x 8
 // elements of the operand type -- followed by a 1 KiB gate block of fp32:
-// gamma_t = 2^g_t for the 64 slots, then s_t = 2^(g_C - g_t), then padding.
+// gamma_t = 2^g_t for the 64 slots, then s_t = 2^(g_C - g_t), then g_t.
 // (g_t is the chunk-local cumulative log2 gate; padded slots repeat the last
-// token's gate, so gamma_63 = gamma_C and s = 1 there.)
+// token's gate, so gamma_63 = gamma_C and s = 1 there.)  On the staged path
+// the scan forms P itself: its entries hold T and the gate block only, and
+// the two all-zero T fragments (rows 0-31, columns 32-63) are never written
+// or read.
 constexpr int kFragElems = 64 * 8;
 constexpr int kGateBlockBytes = 1024;
 template <typename T> constexpr int64_t entry_bytes() {
   return int64_t(16) * kFragElems * sizeof(T) + kGateBlockBytes;
 }
+
+// The staged path: bf16 operands, d_k = 128, d_v a multiple of 32 (the factor
+// kernel and the staged scan, which share the reduced entry contents).
+inline bool staged_path(const Problem &p) { return p.dtype == 1 && p.d_k == 128 && p.d_v % 32 == 0; }
 
 struct Workspace {
   int32_t *chunk_off;  // [n_seqs + 1] chunk prefix sums (packed batches)

@@ -203,10 +203,12 @@ __global__ __launch_bounds__(256) void prep_kernel(PrepArgs<T> a) {
 }
 
 // ---------------------------------------------------------------------------
-// bf16, d_k = 128: the factor kernel.  One workgroup per (chunk slot, value
-// head); its k and q rows and gates are copied into LDS with bounds-checked
-// buffer loads (rows past the chunk's end read as zeros, padded slots get
-// beta = 0 and add nothing to the gate).
+// Staged path (bf16, d_k = 128, d_v % 32 = 0): the factor kernel.  One
+// workgroup of two waves per (chunk slot, value head); its k rows and gates
+// are copied into LDS with bounds-checked buffer loads (rows past the chunk's
+// end read as zeros, padded slots get beta = 0 and add nothing to the gate).
+// It writes T and the gate block; the staged scan forms P from the q and k
+// rows it stages anyway.
 //
 // M = (I + A)^-1 in 16 x 16 blocks.  Wave 1 forms the diagonal blocks A_bb
 // and solves D_b = (I + A_bb)^-1 for all four b at once (lane 16 b + c owns
@@ -226,9 +228,8 @@ __global__ __launch_bounds__(256) void prep_kernel(PrepArgs<T> a) {
 // A stays in registers: the tile K_j K_b^T holds row 16 b + c of A_bj in lane
 // (c, g) (columns 16 j + 4 g .. + 3), i.e. A_bj in row layout; a diagonal tile
 // is symmetric, so the same tile read as A_bb in column layout stores the
-// transposed block the substitution reads.  Waves 2 and 3 form P (t-blocks
-// 0-2 and 3) and the gate factors.  Every factor goes straight from registers
-// to the workspace entry.
+// transposed block the substitution reads.  Every factor goes straight from
+// registers to the workspace entry.
 //
 // LDS: fp32 16 x 16 blocks use 80-byte rows, and the block strides are chosen
 // so that the broadcast row reads of the substitution (one address per block)
@@ -236,23 +237,22 @@ __global__ __launch_bounds__(256) void prep_kernel(PrepArgs<T> a) {
 // ---------------------------------------------------------------------------
 namespace {
 constexpr int kXK = 0;          // k rows, 64 x 128 bf16 row tile
-constexpr int kXQ = 16384;      // q rows
-constexpr int kXAlpha = 32768;  // alpha, 64 fp32
-constexpr int kXBeta = 33024;   // beta, 64 fp32
-constexpr int kXG = 33280;      // g_t, 64 fp32
-constexpr int kXB = 33536;      // beta_t, 64 fp32 (0 past the chunk's end)
+constexpr int kXAlpha = 16384;  // alpha, 64 fp32
+constexpr int kXBeta = 16640;   // beta, 64 fp32
+constexpr int kXG = 16896;      // g_t, 64 fp32
+constexpr int kXB = 17152;      // beta_t, 64 fp32 (0 past the chunk's end)
 constexpr int kXRow = 80;       // row stride of an fp32 16 x 16 block
-constexpr int kXAdT = 33792;    // A_bb^T (row j = column j of A_bb)
+constexpr int kXAdT = 17408;    // A_bb^T (row j = column j of A_bb)
 constexpr int kXAdTBlk = 1296;  // 324 dwords: 4 mod 32
 constexpr int kXD = kXAdT + 4 * kXAdTBlk;  // D_b, row-major
 constexpr int kXDBlk = 1344;               // 336 dwords: 16 mod 32
 constexpr int kXDt = kXD + 4 * kXDBlk;     // D_b^T
 constexpr int kXDtBlk = 1296;
-constexpr int kXBytes = kXDt + 4 * kXDtBlk;  // 49536: three workgroups per CU
-static_assert(kXBytes <= 160 * 1024 / 3, "three factor workgroups per CU");
+constexpr int kXBytes = kXDt + 4 * kXDtBlk;  // 33152: four workgroups per CU
+static_assert(kXBytes <= 160 * 1024 / 4, "four factor workgroups per CU");
 }  // namespace
 
-__global__ __launch_bounds__(256) void factors_kernel(PrepArgs<bf16_t> a) {
+__global__ __launch_bounds__(128) void factors_kernel(PrepArgs<bf16_t> a) {
   const int c = blockIdx.x, h = blockIdx.y;
   int s, tok0, len;
   if (!a.geo.locate(c, s, tok0, len)) return;
@@ -263,17 +263,15 @@ __global__ __launch_bounds__(256) void factors_kernel(PrepArgs<bf16_t> a) {
   __shared__ __attribute__((aligned(16))) char factors_smem[kXBytes];
   lds_t *const sm = lds_ptr(factors_smem);
 
-  // ---- copies: wave 0 the k rows, wave 1 the q rows, wave 2 alpha and beta ----
+  // ---- copies: wave 0 the k rows, wave 1 alpha and beta ----
   const uint32_t row_bytes = uint32_t(a.H_qk) * 256;
-  if (wave < 2) {
-    const char *src = reinterpret_cast<const char *>(wave == 0 ? a.k : a.q) +
-                      (int64_t(tok0) * a.H_qk + hq) * 256;
+  if (wave == 0) {
+    const char *src = reinterpret_cast<const char *>(a.k) + (int64_t(tok0) * a.H_qk + hq) * 256;
     const i32x4_t res = buffer_rsrc(src, rowtile_valid_bytes(len, row_bytes));
-    lds_t *const tile = sm + (wave == 0 ? kXK : kXQ);
 #pragma unroll
     for (int i = 0; i < 16; ++i)
-      dma16_buf(res, uint32_t(rowtile_copy_src(i, lane, 64, int64_t(a.H_qk) * 128)), tile + 1024 * i);
-  } else if (wave == 2) {
+      dma16_buf(res, uint32_t(rowtile_copy_src(i, lane, 64, int64_t(a.H_qk) * 128)), sm + kXK + 1024 * i);
+  } else {
     const uint32_t gate_bytes = uint32_t(len - 1) * uint32_t(a.H_v) * 4 + 4;
     const int64_t first = int64_t(tok0) * a.H_v + h;
     const uint32_t voff = uint32_t(lane) * uint32_t(a.H_v) * 4;
@@ -316,7 +314,7 @@ __global__ __launch_bounds__(256) void factors_kernel(PrepArgs<bf16_t> a) {
   };
   const bf16x4_t zero_h = {0, 0, 0, 0};
 
-  if (wave < 2) {
+  {
     // gates and betas of all slots for broadcast reads (both waves write the
     // same values and read only after their own writes)
     const float bl = lane < len ? lds_load<float>(sm + kXBeta + 4 * lane) : 0.0f;
@@ -367,15 +365,19 @@ __global__ __launch_bounds__(256) void factors_kernel(PrepArgs<bf16_t> a) {
       const f32x4_t M20r = -mm16x3(X20c, Drs[2], zero4());
       const f32x4_t M30r = -mm16x3(X20c, M32r, mm16x3(X30c, Drs[3], zero4()));
       auto Dr = [&](int b) { return D[b]; };
-      // fragments (0, 0) = [D0 | 0], (0, 1) = 0, (1, 0) = [M10 | D1], (1, 1) = 0,
-      // and the left halves of (2, 0) and (3, 0)
+      // fragments (0, 0) = [D0 | 0], (1, 0) = [M10 | D1] and the left halves of
+      // (2, 0) and (3, 0); (0, 1) and (1, 1) are zero and not stored
       put_frag(0, t_half(0, Dr(0)), zero_h);
-      put_frag(1, zero_h, zero_h);
       put_frag(2, t_half(0, M10r), t_half(1, Dr(1)));
-      put_frag(3, zero_h, zero_h);
       put_half(4, 0, t_half(0, M20r));
       put_half(6, 0, t_half(0, M30r));
     } else {
+      // gate block: gamma_t = 2^g_t, s_t = 2^(g_C - g_t), g_t
+      float *gate_out = reinterpret_cast<float *>(entry + 16 * kFragElems * sizeof(bf16_t));
+      const float g_last = __shfl(gl, 63);
+      gate_out[lane] = exp2f(gl);
+      gate_out[64 + lane] = exp2f(g_last - gl);
+      gate_out[128 + lane] = gl;
       // ---- diagonal blocks, stored transposed: A_bb^T[c][4 g + e] ----
 #pragma unroll
       for (int b = 0; b < 4; ++b) {
@@ -457,48 +459,6 @@ __global__ __launch_bounds__(256) void factors_kernel(PrepArgs<bf16_t> a) {
       put_frag(5, t_half(2, Dr(2)), zero_h);
       put_frag(7, t_half(2, M32), t_half(3, Dr(3)));
     }
-  } else {
-    lds_barrier();  // pairs with the barrier of waves 0 and 1, which only they need
-    // ---- P and the gate factors: wave 2 t-blocks 0-2, wave 3 t-block 3 ----
-    // P^T tile (i-block r, t-block cb), r <= cb: its lane layout is the A
-    // fragment layout of P (row t, contraction i), so its four values are half
-    // of fragment (cb, r / 2).
-    bf16_t *const fragP = reinterpret_cast<bf16_t *>(entry) + 8 * kFragElems;
-    auto p_tile = [&](int r, int cb) {
-      f32x4_t acc = zero4();
-#pragma unroll
-      for (int kk = 0; kk < 4; ++kk) acc = mfma(row_frag(kXK, r, kk), row_frag(kXQ, cb, kk), acc);
-      const int t = 16 * cb + r0;
-      const float gt = __shfl(gl, t);
-      f32x4_t pv;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int i = 16 * r + 4 * g + e;
-        const float gi = __shfl(gl, i);  // every lane takes part in the shuffle
-        pv[e] = i <= t ? fast_exp2(gt - gi) * acc[e] : 0.0f;
-      }
-      *reinterpret_cast<bf16x4_t *>(fragP + kFragElems * (2 * cb + (r >> 1)) + 8 * lane + 4 * (r & 1)) =
-          __builtin_convertvector(pv, bf16x4_t);
-    };
-    if (wave == 2) {
-#pragma unroll
-      for (int cb = 0; cb < 3; ++cb)
-#pragma unroll
-        for (int r = 0; r <= cb; ++r) p_tile(r, cb);
-      // halves above the diagonal in t-blocks 0-2
-      *reinterpret_cast<uint64_t *>(fragP + kFragElems * 0 + 8 * lane + 4) = 0;
-      *reinterpret_cast<u32x4_t *>(fragP + kFragElems * 1 + 8 * lane) = u32x4_t{0, 0, 0, 0};
-      *reinterpret_cast<u32x4_t *>(fragP + kFragElems * 3 + 8 * lane) = u32x4_t{0, 0, 0, 0};
-      *reinterpret_cast<uint64_t *>(fragP + kFragElems * 5 + 8 * lane + 4) = 0;
-    } else {
-#pragma unroll
-      for (int r = 0; r < 4; ++r) p_tile(r, 3);
-      // gate factors: gamma_t = 2^g_t, s_t = 2^(g_C - g_t)
-      float *gate_out = reinterpret_cast<float *>(entry + 16 * kFragElems * sizeof(bf16_t));
-      const float g_last = __shfl(gl, 63);
-      gate_out[lane] = exp2f(gl);
-      gate_out[64 + lane] = exp2f(g_last - gl);
-    }
   }
 }
 
@@ -517,8 +477,8 @@ static hipError_t launch_prep_t(const Problem &p, const Workspace &ws, hipStream
   a.geo = make_geom(p, &ws);
   const int64_t slots = chunk_slots(p);
   if constexpr (sizeof(T) == 2) {
-    if (p.d_k == 128) {
-      hipLaunchKernelGGL(factors_kernel, dim3(unsigned(slots), unsigned(p.H_v)), dim3(256), 0, st, a);
+    if (staged_path(p)) {
+      hipLaunchKernelGGL(factors_kernel, dim3(unsigned(slots), unsigned(p.H_v)), dim3(128), 0, st, a);
       return hipGetLastError();
     }
   }

@@ -187,15 +187,20 @@ __global__ __launch_bounds__(64) void scan_kernel(ScanArgs<T> a) {
 // Pipelined path: bf16, d_k = 128, d_v a multiple of 32.
 //
 // A block of four waves owns 32 state columns of one unit.  Waves 0 and 1
-// compute (16 columns each); waves 2 and 3 only copy.  A chunk's operands --
-// its k and q rows (swizzled row tiles), the T and P fragments and gates of
-// its workspace entry, and its 64 x 32 block of v -- are copied into one of
-// three LDS stages with global_load_lds, two chunks ahead of the chunk being
-// computed.  A copy moves 1 KiB and the memory pipeline accepts one from a
-// wave only every few dozen cycles, so the copies are issued by the two
-// copy waves, on SIMDs the compute waves leave idle, and the compute waves'
-// instruction streams hold only LDS reads, MFMAs and their output stores.
-// One barrier per chunk keeps the roles in step.  K^T fragments for the state
+// compute (16 columns each); waves 2 and 3 copy and form P.  A chunk's
+// operands -- its k and q rows (swizzled row tiles), the T fragments and gates
+// of its workspace entry, and its 64 x 32 block of v -- are copied into one
+// of three LDS stages with global_load_lds, two chunks ahead of the chunk
+// being computed.  A copy moves 1 KiB and the memory pipeline accepts one
+// from a wave only every few dozen cycles, so the copies are issued by the
+// two copy waves, on SIMDs the compute waves leave idle, and the compute
+// waves' instruction streams hold only LDS reads, MFMAs and their output
+// stores.  While the compute waves run chunk c, the copy waves also form P
+// of chunk c (P_ti = 2^(g_t - g_i) q_t . k_i, i <= t) from its staged q and
+// k rows into one of two P buffers; the compute waves read it after the next
+// barrier, for chunk c's outputs.  One barrier per chunk keeps the roles in
+// step.  T and P are lower triangular: their two all-zero fragments (rows
+// 0-31, columns 32-63) are neither copied nor formed nor multiplied.  K^T fragments for the state
 // update and the v block come from the staged tiles through transposed reads
 // (ds_read_b64_tr_b16).  Every LDS and global offset a lane uses is computed
 // once; per chunk only wave-uniform bases change.  The k / q and v copies are
@@ -203,22 +208,70 @@ __global__ __launch_bounds__(64) void scan_kernel(ScanArgs<T> a) {
 // ---------------------------------------------------------------------------
 constexpr int kStK = 0;        // 64 x 128 bf16 row tile
 constexpr int kStQ = 16384;    // 64 x 128 bf16 row tile
-constexpr int kStF = 32768;    // T (8) and P (8) fragments, 1 KiB each
-constexpr int kStG = 49152;    // gate block: gamma (64 fp32), s (64 fp32), padding
-constexpr int kStV = 50176;    // 64 x 32 bf16 v block
-constexpr int kStBytes = 54272;
-// Copies one copy wave issues per stage (wave 2: k tile, T, gates, v columns
-// 0-15; wave 3: q tile, P, v columns 16-31).  A copy wave issues nothing but
-// these loads, and loads complete in issue order, so waiting until only the
-// newest stage's copies are outstanding completes every older stage.
-constexpr int kStageLoadsW2 = 27;
-constexpr int kStageLoadsW3 = 26;
+constexpr int kStT = 32768;    // T fragments, 1 KiB each (1 and 3 unused)
+constexpr int kStG = 40960;    // gate block: gamma, s, g (64 fp32 each), padding
+constexpr int kStV = 41984;    // 64 x 32 bf16 v block
+constexpr int kStBytes = 46080;
+constexpr int kPBytes = 8192;  // P fragments, 1 KiB each (1 and 3 unused)
+// Copies one copy wave issues per stage (wave 2: k tile, T fragments 0, 2, 4,
+// gates, v columns 0-15; wave 3: q tile, T fragments 5, 6, 7, v columns
+// 16-31).  A copy wave issues no other vector-memory operation, and loads
+// complete in issue order, so waiting until only the newest stage's copies
+// are outstanding completes every older stage.
+constexpr int kStageLoadsW2 = 22;
+constexpr int kStageLoadsW3 = 21;
 
-// Three stages as distinct LDS objects: with the chunk loop unrolled by three,
-// every access names its stage at compile time.
+// Three stages and two P buffers as distinct LDS objects: with the chunk loop
+// unrolled by three, every stage access names its stage at compile time.
 __shared__ __attribute__((aligned(16))) char scan_stage0[kStBytes];
 __shared__ __attribute__((aligned(16))) char scan_stage1[kStBytes];
 __shared__ __attribute__((aligned(16))) char scan_stage2[kStBytes];
+__shared__ __attribute__((aligned(16))) char scan_p0[kPBytes];
+__shared__ __attribute__((aligned(16))) char scan_p1[kPBytes];
+
+// P of one chunk from its staged q and k rows and gate block, by one copy
+// wave: tiles (i-block r, t-block cb), r <= cb, five per wave (wave CW = 0:
+// (0,0) (0,1) (1,1) (0,2) (1,2); CW = 1: (2,2) (0,3) (1,3) (2,3) (3,3)).  The
+// P^T tile K_r Q_cb^T has the A-fragment layout of P (row t, contraction i),
+// so its four values per lane are half of fragment (cb, r / 2).  All operand
+// reads are issued first and the five tiles' MFMAs interleave.
+template <int CW>
+__device__ __forceinline__ void scan_p_tiles(const lds_t *st, lds_t *pb, const int (&kq_off)[4][2], int lane) {
+  constexpr int R[2][5] = {{0, 0, 1, 0, 1}, {2, 0, 1, 2, 3}};
+  constexpr int CB[2][5] = {{0, 1, 1, 2, 2}, {2, 3, 3, 3, 3}};
+  constexpr int KLO = CW == 0 ? 0 : 0, KHI = CW == 0 ? 2 : 4;  // k blocks used
+  constexpr int QLO = CW == 0 ? 0 : 2, QHI = CW == 0 ? 3 : 4;  // q blocks used
+  const int r0 = lane & 15, g = lane >> 4;
+  auto frag = [&](int tile, int rt, int kk) -> Frag<bf16_t> {
+    const lds_t *p = st + tile + 4096 * rt;
+    return frag_cat(lds_load_single<bf16x4_t>(p + kq_off[kk][0]), lds_load_single<bf16x4_t>(p + kq_off[kk][1]));
+  };
+  Frag<bf16_t> kf[4][4], qf[4][4];
+#pragma unroll
+  for (int b = KLO; b < KHI; ++b)
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) kf[b][kk] = frag(kStK, b, kk);
+#pragma unroll
+  for (int b = QLO; b < QHI; ++b)
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) qf[b][kk] = frag(kStQ, b, kk);
+  f32x4_t acc[5];
+#pragma unroll
+  for (int kk = 0; kk < 4; ++kk)
+#pragma unroll
+    for (int n = 0; n < 5; ++n) acc[n] = mfma(kf[R[CW][n]][kk], qf[CB[CW][n]][kk], kk == 0 ? zero4() : acc[n]);
+#pragma unroll
+  for (int n = 0; n < 5; ++n) {
+    const int r = R[CW][n], cb = CB[CW][n];
+    const int t = 16 * cb + r0;
+    const float gt = lds_load<float>(st + kStG + 512 + 4 * t);
+    const f32x4_t gi = lds_load<f32x4_t>(st + kStG + 512 + 4 * (16 * r + 4 * g));
+    f32x4_t pv;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) pv[e] = 16 * r + 4 * g + e <= t ? fast_exp2(gt - gi[e]) * acc[n][e] : 0.0f;
+    lds_store<bf16x4_t>(pb + 1024 * (2 * cb + (r >> 1)) + 16 * lane + 8 * (r & 1), __builtin_convertvector(pv, bf16x4_t));
+  }
+}
 
 // NG = 16-column groups per compute wave: 2 compute waves of one group, or
 // one compute wave of two groups (which reads each k, q, T and P fragment
@@ -271,9 +324,11 @@ __global__ __launch_bounds__(64 * (2 / NG + 2)) void scan_kernel_staged(ScanArgs
 #pragma unroll
       for (int i = 0; i < 16; ++i) dma16_buf(kq_res, kq_voff[i], tile + 1024 * i);
       const char *entry = a.entries + (int64_t(c_first + cc) * a.H_v + h) * ebytes;
-      const char *f = entry + 8192 * cw;
 #pragma unroll
-      for (int i = 0; i < 8; ++i) dma16(f + 1024 * i, 16 * lane, base + kStF + 8192 * cw + 1024 * i);
+      for (int i = 0; i < 3; ++i) {
+        const int f = cw == 0 ? 2 * i : 5 + i;  // T fragments 0, 2, 4 / 5, 6, 7
+        dma16(entry + 1024 * f, 16 * lane, base + kStT + 1024 * f);
+      }
       if (cw == 0) dma16(entry + 16384, 16 * lane, base + kStG);
       const i32x4_t v_res = buffer_rsrc(v_src + int64_t(tok0) * v_row_bytes,
                                         vblock_valid_bytes(len, v_row_bytes));
@@ -286,6 +341,27 @@ __global__ __launch_bounds__(64 * (2 / NG + 2)) void scan_kernel_staged(ScanArgs
       else
         wait_vmem_upto<kStageLoadsW3>();
     };
+    // P of the chunk in stage `stage_mem` into `p_mem`.
+    int kq_off[4][2];
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk)
+#pragma unroll
+      for (int hf = 0; hf < 2; ++hf) kq_off[kk][hf] = 2 * rowtile_off(r0, 32 * kk + 16 * hf + 4 * g);
+    auto p_tiles = [&](const char *stage_mem, char *p_mem) {
+      if (cw == 0)
+        scan_p_tiles<0>(lds_ptr(const_cast<char *>(stage_mem)), lds_ptr(p_mem), kq_off, lane);
+      else
+        scan_p_tiles<1>(lds_ptr(const_cast<char *>(stage_mem)), lds_ptr(p_mem), kq_off, lane);
+    };
+    // the zero halves of fragments 0 and 5 (tiles r = 1, cb = 0 and r = 3,
+    // cb = 2) never change
+    if (cw == 0) {
+      const bf16x4_t z = {0, 0, 0, 0};
+      lds_store<bf16x4_t>(lds_ptr(scan_p0) + 1024 * 0 + 16 * lane + 8, z);
+      lds_store<bf16x4_t>(lds_ptr(scan_p0) + 1024 * 5 + 16 * lane + 8, z);
+      lds_store<bf16x4_t>(lds_ptr(scan_p1) + 1024 * 0 + 16 * lane + 8, z);
+      lds_store<bf16x4_t>(lds_ptr(scan_p1) + 1024 * 5 + 16 * lane + 8, z);
+    }
     if (n_chunks > 0) {
       stage(0, scan_stage0);
       stage(min(1, n_chunks - 1), scan_stage1);
@@ -296,16 +372,22 @@ __global__ __launch_bounds__(64 * (2 / NG + 2)) void scan_kernel_staged(ScanArgs
     // cc + 1) the stage of chunk cc - 1 is free: the compute waves read it
     // before the barrier that opened chunk cc.  Chunk cc + 2 goes there (past
     // the end the last chunk is copied again, so every phase issues the same
-    // loads), then chunk cc + 1's stage must be complete.
-    auto phase = [&](int cc, char *dst) {
+    // loads); P of chunk cc is formed from its stage into P buffer cc mod 2
+    // (read by the compute waves in the next phase, and free again by the
+    // phase after); then chunk cc + 1's stage must be complete.
+    auto phase = [&](int cc, char *dst, const char *cur, char *p_mem) {
       stage(min(cc + 2, n_chunks - 1), dst);
+      p_tiles(cur, p_mem);
       wait_all_but_newest_stage();
       lds_barrier();
     };
-    for (int cc = 0; cc < n_chunks; cc += 3) {
-      phase(cc, scan_stage2);
-      if (cc + 1 < n_chunks) phase(cc + 1, scan_stage0);
-      if (cc + 2 < n_chunks) phase(cc + 2, scan_stage1);
+    for (int cc = 0; cc < n_chunks; cc += 6) {
+      phase(cc, scan_stage2, scan_stage0, scan_p0);
+      if (cc + 1 < n_chunks) phase(cc + 1, scan_stage0, scan_stage1, scan_p1);
+      if (cc + 2 < n_chunks) phase(cc + 2, scan_stage1, scan_stage2, scan_p0);
+      if (cc + 3 < n_chunks) phase(cc + 3, scan_stage2, scan_stage0, scan_p1);
+      if (cc + 4 < n_chunks) phase(cc + 4, scan_stage0, scan_stage1, scan_p0);
+      if (cc + 5 < n_chunks) phase(cc + 5, scan_stage1, scan_stage2, scan_p1);
     }
     wait_vmem();  // the trailing copies
     return;
@@ -390,7 +472,8 @@ __global__ __launch_bounds__(64 * (2 / NG + 2)) void scan_kernel_staged(ScanArgs
 #pragma unroll
       for (int rt = 0; rt < 4; ++rt) vt[cg][rt] = lds_read_tr16(st + kStV + 1024 * rt + v_off[cg]);
 #pragma unroll
-    for (int i = 0; i < 8; ++i) tf[i].v = lds_load<bf16x8_t>(st + kStF + 1024 * i + 16 * lane);
+    for (int i = 0; i < 8; ++i)
+      if (i != 1 && i != 3) tf[i].v = lds_load<bf16x8_t>(st + kStT + 1024 * i + 16 * lane);
   };
 
   lds_barrier();  // the first two stages are complete
@@ -420,7 +503,7 @@ __global__ __launch_bounds__(64 * (2 / NG + 2)) void scan_kernel_staged(ScanArgs
   // the copy waves may reuse the previous chunk's stage), and the chunk's
   // output products run after it, behind the reads of the next chunk's
   // operands.  With two groups each operand fragment serves both.
-  auto chunk_step = [&](int cc, char *cur_mem, char *next_mem) {
+  auto chunk_step = [&](int cc, char *cur_mem, char *next_mem, const char *p_mem) {
     const lds_t *const st = lds_ptr(cur_mem);
 
     Frag<bf16_t> Sf[NG][4];
@@ -465,12 +548,12 @@ __global__ __launch_bounds__(64 * (2 / NG + 2)) void scan_kernel_staged(ScanArgs
 #pragma unroll
     for (int rt = 0; rt < 4; ++rt)
 #pragma unroll
-      for (int kk = 0; kk < 2; ++kk)
+      for (int kk = 0; kk < (rt < 2 ? 1 : 2); ++kk)  // T rows 0-31 end at column 31
 #pragma unroll
         for (int cg = 0; cg < NG; ++cg)
           Ua[cg][rt] = mfma(tf[rt * 2 + kk], Xf[cg][kk], kk == 0 ? zero4() : Ua[cg][rt]);
 
-    // K^T fragments (transposed reads of the k tile) and P
+    // K^T fragments (transposed reads of the k tile)
     Frag<bf16_t> ktf[8][2];
 #pragma unroll
     for (int rm = 0; rm < 8; ++rm)
@@ -479,9 +562,6 @@ __global__ __launch_bounds__(64 * (2 / NG + 2)) void scan_kernel_staged(ScanArgs
         const lds_t *p = st + kStK + 8192 * kk + kt_off[rm];
         ktf[rm][kk] = frag_cat(lds_read_tr16(p), lds_read_tr16(p + 4096));
       }
-    Frag<bf16_t> pf[8];
-#pragma unroll
-    for (int i = 0; i < 8; ++i) pf[i].v = lds_load<bf16x8_t>(st + kStF + 8192 + 1024 * i + 16 * lane);
 
     Frag<bf16_t> Uf[NG][2], Usf[NG][2];
 #pragma unroll
@@ -512,6 +592,13 @@ __global__ __launch_bounds__(64 * (2 / NG + 2)) void scan_kernel_staged(ScanArgs
     // previous chunk's stage) and the next chunk's stage is complete
     lds_barrier();
     if (cc + 1 < n_chunks) read_operands(next_mem);
+    Frag<bf16_t> pf[8];  // P of this chunk, formed by the copy waves
+    {
+      const lds_t *pb = lds_ptr(const_cast<char *>(p_mem));
+#pragma unroll
+      for (int i = 0; i < 8; ++i)
+        if (i != 1 && i != 3) pf[i].v = lds_load<bf16x8_t>(pb + 1024 * i + 16 * lane);
+    }
 
     // O = gamma (Q S) + P U with the chunk-start state, computed as
     // O^T = S^T (gamma Q^T) + U^T P^T: with the kappa fragment convention Sf
@@ -527,15 +614,18 @@ __global__ __launch_bounds__(64 * (2 / NG + 2)) void scan_kernel_staged(ScanArgs
         for (int kk = 0; kk < 4; ++kk) oq = mfma(Sf[cg][kk], qf[kk][rt], kk == 0 ? zero4() : oq);
         f32x4_t acc = gt_o[rt] * oq;
 #pragma unroll
-        for (int kk = 0; kk < 2; ++kk) acc = mfma(Uf[cg][kk], pf[rt * 2 + kk], acc);
+        for (int kk = 0; kk < (rt < 2 ? 1 : 2); ++kk) acc = mfma(Uf[cg][kk], pf[rt * 2 + kk], acc);
         o_pend[cg][rt] = __builtin_convertvector(acc, bf16x4_t);
       }
     o_chunk_pend = cc;
   };
-  for (int cc = 0; cc < n_chunks; cc += 3) {
-    chunk_step(cc, scan_stage0, scan_stage1);
-    if (cc + 1 < n_chunks) chunk_step(cc + 1, scan_stage1, scan_stage2);
-    if (cc + 2 < n_chunks) chunk_step(cc + 2, scan_stage2, scan_stage0);
+  for (int cc = 0; cc < n_chunks; cc += 6) {
+    chunk_step(cc, scan_stage0, scan_stage1, scan_p0);
+    if (cc + 1 < n_chunks) chunk_step(cc + 1, scan_stage1, scan_stage2, scan_p1);
+    if (cc + 2 < n_chunks) chunk_step(cc + 2, scan_stage2, scan_stage0, scan_p0);
+    if (cc + 3 < n_chunks) chunk_step(cc + 3, scan_stage0, scan_stage1, scan_p1);
+    if (cc + 4 < n_chunks) chunk_step(cc + 4, scan_stage1, scan_stage2, scan_p0);
+    if (cc + 5 < n_chunks) chunk_step(cc + 5, scan_stage2, scan_stage0, scan_p1);
   }
   store_pending();
 
@@ -575,7 +665,7 @@ static ScanArgs<T> scan_args(const Problem &p, const Workspace &ws, int colblk_w
 }
 
 hipError_t launch_scan(const Problem &p, const Workspace &ws, hipStream_t st) {
-  const bool staged = p.dtype == 1 && p.d_k == 128 && p.d_v % 32 == 0;
+  const bool staged = staged_path(p);
   const int width = staged ? 32 : 16;
   const int64_t blocks = (int64_t(p.n_seqs) * p.H_v + 7) / 8 * 8 * (p.d_v / width);
   if (blocks == 0) return hipSuccess;
