@@ -479,17 +479,61 @@ __global__ __launch_bounds__(64 * (2 / NG + 2)) void scan_kernel_staged(ScanArgs
   lds_barrier();  // the first two stages are complete
   if (n_chunks > 0) read_operands(scan_stage0);
 
-  // A chunk's outputs wait in registers and leave after the next chunk's Y
-  // products: right after the barrier the copy waves fill the memory
-  // pipeline, and a store issued then would hold up this wave behind them.
+  // Chunk c's output products run inside chunk c + 1's state chain, where the
+  // MFMA pipe would otherwise wait on the chain's VALU work: they need the
+  // chunk-start state and U of chunk c (o_Sf, o_Uf), its q rows (read during
+  // chunk c) and its P (read after the barrier that follows chunk c).  The
+  // outputs leave at the end of the next chain, when the copy waves' burst
+  // of copies after the barrier has drained from the memory pipeline.
+  Frag<bf16_t> o_Sf[NG][4], o_Uf[NG][2], o_qf[4][4], o_pf[8];
+  float o_gt[4];
   bf16x4_t o_pend[NG][4];
-  int o_chunk_pend = -1;
-  auto store_pending = [&]() {
-    if (o_chunk_pend < 0) return;
-    const int len = min(C, end - (start + o_chunk_pend * C));
+#pragma unroll
+  for (int i = 0; i < 8; ++i) o_pf[i].zero();
+#pragma unroll
+  for (int kk = 0; kk < 4; ++kk)
+#pragma unroll
+    for (int rt = 0; rt < 4; ++rt) o_qf[kk][rt].zero();
+#pragma unroll
+  for (int cg = 0; cg < NG; ++cg) {
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) o_Sf[cg][kk].zero();
+    o_Uf[cg][0].zero();
+    o_Uf[cg][1].zero();
+  }
+#pragma unroll
+  for (int rt = 0; rt < 4; ++rt) o_gt[rt] = 0.0f;
+
+  // O = gamma (Q S) + P U with the chunk-start state, computed as
+  // O^T = S^T (gamma Q^T) + U^T P^T: with the kappa fragment convention Sf
+  // and Uf serve as A operands and the q rows and P fragments as B operands
+  // unchanged, and each lane ends with four consecutive columns of one token
+  // row, one 8-byte piece of the output.  (T and P rows 0-31 end at column 31.)
+  f32x4_t oq[NG][4];
+  auto out_qs = [&]() {
+#pragma unroll
+    for (int rt = 0; rt < 4; ++rt)
+#pragma unroll
+      for (int cg = 0; cg < NG; ++cg)
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) oq[cg][rt] = mfma(o_Sf[cg][kk], o_qf[kk][rt], kk == 0 ? zero4() : oq[cg][rt]);
+  };
+  auto out_pu = [&]() {
+#pragma unroll
+    for (int rt = 0; rt < 4; ++rt)
+#pragma unroll
+      for (int cg = 0; cg < NG; ++cg) {
+        f32x4_t acc = o_gt[rt] * oq[cg][rt];
+#pragma unroll
+        for (int kk = 0; kk < (rt < 2 ? 1 : 2); ++kk) acc = mfma(o_Uf[cg][kk], o_pf[rt * 2 + kk], acc);
+        o_pend[cg][rt] = __builtin_convertvector(acc, bf16x4_t);
+      }
+  };
+  auto store_out = [&](int oc) {
+    const int len = min(C, end - (start + oc * C));
 #pragma unroll
     for (int cg = 0; cg < NG; ++cg) {
-      bf16_t *const o_chunk = o_lane[cg] + int64_t(o_chunk_pend) * C * v_stride;
+      bf16_t *const o_chunk = o_lane[cg] + int64_t(oc) * C * v_stride;
 #pragma unroll
       for (int rt = 0; rt < 4; ++rt)
         if (out_acc_row(rt, lane) < len)
@@ -498,11 +542,12 @@ __global__ __launch_bounds__(64 * (2 / NG + 2)) void scan_kernel_staged(ScanArgs
   };
 
   // One chunk, software-pipelined: the state chain runs from the operands
-  // read after the previous barrier; the q rows, K^T and P are read from the
-  // stage during the chain.  The barrier follows the state update (after it
-  // the copy waves may reuse the previous chunk's stage), and the chunk's
-  // output products run after it, behind the reads of the next chunk's
-  // operands.  With two groups each operand fragment serves both.
+  // read after the previous barrier, with the previous chunk's output
+  // products interleaved; the q rows and K^T are read from the stage during
+  // the chain.  The barrier follows the state update (after it the copy
+  // waves may reuse the previous chunk's stage); then the next chunk's
+  // operands and this chunk's P are read.  With two groups each operand
+  // fragment serves both.
   auto chunk_step = [&](int cc, char *cur_mem, char *next_mem, const char *p_mem) {
     const lds_t *const st = lds_ptr(cur_mem);
 
@@ -521,18 +566,7 @@ __global__ __launch_bounds__(64 * (2 / NG + 2)) void scan_kernel_staged(ScanArgs
 #pragma unroll
         for (int cg = 0; cg < NG; ++cg)
           Y[cg][rt] = mfma(kf[kk][rt], Sf[cg][kk], kk == 0 ? zero4() : Y[cg][rt]);
-    store_pending();  // the previous chunk's outputs
-
-    // q rows, for the output products after the barrier
-    Frag<bf16_t> qf[4][4];
-#pragma unroll
-    for (int kk = 0; kk < 4; ++kk)
-#pragma unroll
-      for (int rt = 0; rt < 4; ++rt) {
-        const lds_t *pq = st + kStQ + 4096 * rt;
-        qf[kk][rt] = frag_cat(lds_load_single<bf16x4_t>(pq + kq_off[kk][0]),
-                              lds_load_single<bf16x4_t>(pq + kq_off[kk][1]));
-      }
+    out_qs();  // previous chunk: S^T (Q^T)
 
     // X = V - gamma Y, then U = T X
     Frag<bf16_t> Xf[NG][2];
@@ -552,6 +586,17 @@ __global__ __launch_bounds__(64 * (2 / NG + 2)) void scan_kernel_staged(ScanArgs
 #pragma unroll
         for (int cg = 0; cg < NG; ++cg)
           Ua[cg][rt] = mfma(tf[rt * 2 + kk], Xf[cg][kk], kk == 0 ? zero4() : Ua[cg][rt]);
+    out_pu();  // previous chunk: + U^T P^T
+
+    // this chunk's q rows, for its output products in the next chunk
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk)
+#pragma unroll
+      for (int rt = 0; rt < 4; ++rt) {
+        const lds_t *pq = st + kStQ + 4096 * rt;
+        o_qf[kk][rt] = frag_cat(lds_load_single<bf16x4_t>(pq + kq_off[kk][0]),
+                                lds_load_single<bf16x4_t>(pq + kq_off[kk][1]));
+      }
 
     // K^T fragments (transposed reads of the k tile)
     Frag<bf16_t> ktf[8][2];
@@ -563,11 +608,11 @@ __global__ __launch_bounds__(64 * (2 / NG + 2)) void scan_kernel_staged(ScanArgs
         ktf[rm][kk] = frag_cat(lds_read_tr16(p), lds_read_tr16(p + 4096));
       }
 
-    Frag<bf16_t> Uf[NG][2], Usf[NG][2];
+    Frag<bf16_t> Usf[NG][2];
 #pragma unroll
     for (int cg = 0; cg < NG; ++cg) {
-      Uf[cg][0] = frag_from_acc<bf16_t>(Ua[cg][0], Ua[cg][1]);
-      Uf[cg][1] = frag_from_acc<bf16_t>(Ua[cg][2], Ua[cg][3]);
+      o_Uf[cg][0] = frag_from_acc<bf16_t>(Ua[cg][0], Ua[cg][1]);
+      o_Uf[cg][1] = frag_from_acc<bf16_t>(Ua[cg][2], Ua[cg][3]);
 #pragma unroll
       for (int rt = 0; rt < 4; ++rt) Ua[cg][rt] *= sc[rt];
       Usf[cg][0] = frag_from_acc<bf16_t>(Ua[cg][0], Ua[cg][1]);
@@ -584,40 +629,24 @@ __global__ __launch_bounds__(64 * (2 / NG + 2)) void scan_kernel_staged(ScanArgs
         for (int kk = 0; kk < 2; ++kk) acc = mfma(ktf[rm][kk], Usf[cg][kk], acc);
         S[cg][rm] = acc;
       }
-    float gt_o[4];
+    if (cc > 0) store_out(cc - 1);
 #pragma unroll
-    for (int rt = 0; rt < 4; ++rt) gt_o[rt] = gam_tok[rt];
+    for (int cg = 0; cg < NG; ++cg)
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk) o_Sf[cg][kk] = Sf[cg][kk];
+#pragma unroll
+    for (int rt = 0; rt < 4; ++rt) o_gt[rt] = gam_tok[rt];
 
     // this chunk's stage reads are done (the copy waves may now refill the
     // previous chunk's stage) and the next chunk's stage is complete
     lds_barrier();
     if (cc + 1 < n_chunks) read_operands(next_mem);
-    Frag<bf16_t> pf[8];  // P of this chunk, formed by the copy waves
-    {
+    {  // P of this chunk, formed by the copy waves
       const lds_t *pb = lds_ptr(const_cast<char *>(p_mem));
 #pragma unroll
       for (int i = 0; i < 8; ++i)
-        if (i != 1 && i != 3) pf[i].v = lds_load<bf16x8_t>(pb + 1024 * i + 16 * lane);
+        if (i != 1 && i != 3) o_pf[i].v = lds_load<bf16x8_t>(pb + 1024 * i + 16 * lane);
     }
-
-    // O = gamma (Q S) + P U with the chunk-start state, computed as
-    // O^T = S^T (gamma Q^T) + U^T P^T: with the kappa fragment convention Sf
-    // and Uf serve as A operands and the q rows and P fragments as B operands
-    // unchanged, and each lane ends with four consecutive columns of one
-    // token row, one 8-byte piece of the output.
-#pragma unroll
-    for (int rt = 0; rt < 4; ++rt)
-#pragma unroll
-      for (int cg = 0; cg < NG; ++cg) {
-        f32x4_t oq;
-#pragma unroll
-        for (int kk = 0; kk < 4; ++kk) oq = mfma(Sf[cg][kk], qf[kk][rt], kk == 0 ? zero4() : oq);
-        f32x4_t acc = gt_o[rt] * oq;
-#pragma unroll
-        for (int kk = 0; kk < (rt < 2 ? 1 : 2); ++kk) acc = mfma(Uf[cg][kk], pf[rt * 2 + kk], acc);
-        o_pend[cg][rt] = __builtin_convertvector(acc, bf16x4_t);
-      }
-    o_chunk_pend = cc;
   };
   for (int cc = 0; cc < n_chunks; cc += 6) {
     chunk_step(cc, scan_stage0, scan_stage1, scan_p0);
@@ -627,7 +656,11 @@ __global__ __launch_bounds__(64 * (2 / NG + 2)) void scan_kernel_staged(ScanArgs
     if (cc + 4 < n_chunks) chunk_step(cc + 4, scan_stage1, scan_stage2, scan_p0);
     if (cc + 5 < n_chunks) chunk_step(cc + 5, scan_stage2, scan_stage0, scan_p1);
   }
-  store_pending();
+  if (n_chunks > 0) {  // the last chunk's outputs
+    out_qs();
+    out_pu();
+    store_out(n_chunks - 1);
+  }
 
   if (a.hT) {
 #pragma unroll
