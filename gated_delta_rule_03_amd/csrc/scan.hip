@@ -568,6 +568,17 @@ __global__ __launch_bounds__(64 * (2 / NG + 2)) void scan_kernel_staged(ScanArgs
           Y[cg][rt] = mfma(kf[kk][rt], Sf[cg][kk], kk == 0 ? zero4() : Y[cg][rt]);
     out_qs();  // previous chunk: S^T (Q^T)
 
+    // K^T fragments for the state update (transposed reads of the k tile),
+    // issued early so that they have landed when the update starts
+    Frag<bf16_t> ktf[8][2];
+#pragma unroll
+    for (int rm = 0; rm < 8; ++rm)
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk) {
+        const lds_t *p = st + kStK + 8192 * kk + kt_off[rm];
+        ktf[rm][kk] = frag_cat(lds_read_tr16(p), lds_read_tr16(p + 4096));
+      }
+
     // X = V - gamma Y, then U = T X
     Frag<bf16_t> Xf[NG][2];
 #pragma unroll
@@ -596,16 +607,6 @@ __global__ __launch_bounds__(64 * (2 / NG + 2)) void scan_kernel_staged(ScanArgs
         const lds_t *pq = st + kStQ + 4096 * rt;
         o_qf[kk][rt] = frag_cat(lds_load_single<bf16x4_t>(pq + kq_off[kk][0]),
                                 lds_load_single<bf16x4_t>(pq + kq_off[kk][1]));
-      }
-
-    // K^T fragments (transposed reads of the k tile)
-    Frag<bf16_t> ktf[8][2];
-#pragma unroll
-    for (int rm = 0; rm < 8; ++rm)
-#pragma unroll
-      for (int kk = 0; kk < 2; ++kk) {
-        const lds_t *p = st + kStK + 8192 * kk + kt_off[rm];
-        ktf[rm][kk] = frag_cat(lds_read_tr16(p), lds_read_tr16(p + 4096));
       }
 
     Frag<bf16_t> Usf[NG][2];
