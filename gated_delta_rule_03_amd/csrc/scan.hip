@@ -187,21 +187,28 @@ __global__ __launch_bounds__(64) void scan_kernel(ScanArgs<T> a) {
 // Pipelined path: bf16, d_k = 128, d_v a multiple of 32.
 //
 // A block of four waves owns 32 state columns of one unit.  Waves 0 and 1
-// compute (16 columns each); waves 2 and 3 copy and form P.  A chunk's
-// operands -- its k and q rows (swizzled row tiles), the T fragments and gates
-// of its workspace entry, and its 64 x 32 block of v -- are copied into one
-// of three LDS stages with global_load_lds, two chunks ahead of the chunk
-// being computed.  A copy moves 1 KiB and the memory pipeline accepts one
-// from a wave only every few dozen cycles, so the copies are issued by the
-// two copy waves, on SIMDs the compute waves leave idle, and the compute
-// waves' instruction streams hold only LDS reads, MFMAs and their output
-// stores.  While the compute waves run chunk c, the copy waves also form P
-// of chunk c (P_ti = 2^(g_t - g_i) q_t . k_i, i <= t) from its staged q and
-// k rows into one of two P buffers; the compute waves read it after the next
-// barrier, for chunk c's outputs.  One barrier per chunk keeps the roles in
-// step.  T and P are lower triangular: their two all-zero fragments (rows
-// 0-31, columns 32-63) are neither copied nor formed nor multiplied.  K^T fragments for the state
-// update and the v block come from the staged tiles through transposed reads
+// run the state chain (16 columns each); waves 2 and 3 copy operands, form P
+// and compute the outputs.  A chunk's operands -- its k and q rows (swizzled
+// row tiles), the T fragments and gates of its workspace entry, and its
+// 64 x 32 block of v -- are copied into one of three LDS stages with
+// buffer/global loads straight to LDS, two chunks ahead of the chunk being
+// computed.  A copy moves 1 KiB and the memory pipeline accepts one from a
+// wave only every few dozen cycles, so the copies are issued by the copy
+// waves, on SIMDs the chain waves leave idle.
+//
+// The chain waves' instruction stream is the whole cost of a chunk, so it
+// holds the state chain only: Y = K S, U = T (V - gamma Y), the state update.
+// Each chain wave leaves the chunk-start state (as the bf16 fragments it
+// multiplies anyway) and U in one of two exchange buffers.  In the next phase
+// each copy wave computes the outputs of two of the chunk's four 16-token row
+// blocks for both column groups, O^T = S^T (gamma Q^T) + U^T P^T, from that
+// exchange, the q rows and the rows of P it formed itself in the previous
+// phase (kept in registers), and stores them.
+//
+// One barrier per chunk keeps the roles in step.  T and P are lower
+// triangular: their all-zero fragments (rows 0-31, columns 32-63) are neither
+// copied nor formed nor multiplied.  K^T fragments for the state update and
+// the v block come from the staged tiles through transposed reads
 // (ds_read_b64_tr_b16).  Every LDS and global offset a lane uses is computed
 // once; per chunk only wave-uniform bases change.  The k / q and v copies are
 // bounds-checked buffer loads: rows past a partial chunk read as zeros.
@@ -212,73 +219,233 @@ constexpr int kStT = 32768;    // T fragments, 1 KiB each (1 and 3 unused)
 constexpr int kStG = 40960;    // gate block: gamma, s, g (64 fp32 each), padding
 constexpr int kStV = 41984;    // 64 x 32 bf16 v block
 constexpr int kStBytes = 46080;
-constexpr int kPBytes = 8192;  // P fragments, 1 KiB each (1 and 3 unused)
+// Exchange buffer: per chain wave w, at 6144 w, the chunk-start state as four
+// bf16 A fragments of S^T (fragment kk: state rows 32 kk + kappa) and then U
+// as two fragments (tokens 32 kk + kappa), 1 KiB each in fragment order.
+constexpr int kExS = 0, kExU = 4096, kExWave = 6144;
+constexpr int kExBytes = 2 * kExWave;
 // Copies one copy wave issues per stage (wave 2: k tile, T fragments 0, 2, 4,
 // gates, v columns 0-15; wave 3: q tile, T fragments 5, 6, 7, v columns
-// 16-31).  A copy wave issues no other vector-memory operation, and loads
-// complete in issue order, so waiting until only the newest stage's copies
-// are outstanding completes every older stage.
+// 16-31).  Loads complete in issue order, and the only other vector-memory
+// operations of a copy wave are its output stores; so waiting until at most
+// this many of its operations are outstanding completes every load issued
+// before the newest stage's copies, whatever the stores do.
 constexpr int kStageLoadsW2 = 22;
 constexpr int kStageLoadsW3 = 21;
 
-// Three stages and two P buffers as distinct LDS objects: with the chunk loop
-// unrolled by three, every stage access names its stage at compile time.
+// Three stages and two exchange buffers as distinct LDS objects: with the
+// chunk loop unrolled by six, every access names its buffer at compile time.
 __shared__ __attribute__((aligned(16))) char scan_stage0[kStBytes];
 __shared__ __attribute__((aligned(16))) char scan_stage1[kStBytes];
 __shared__ __attribute__((aligned(16))) char scan_stage2[kStBytes];
-__shared__ __attribute__((aligned(16))) char scan_p0[kPBytes];
-__shared__ __attribute__((aligned(16))) char scan_p1[kPBytes];
+__shared__ __attribute__((aligned(16))) char scan_ex0[kExBytes];
+__shared__ __attribute__((aligned(16))) char scan_ex1[kExBytes];
 
-// P of one chunk from its staged q and k rows and gate block, by one copy
-// wave: tiles (i-block r, t-block cb), r <= cb, five per wave (wave CW = 0:
-// (0,0) (0,1) (1,1) (0,2) (1,2); CW = 1: (2,2) (0,3) (1,3) (2,3) (3,3)).  The
-// P^T tile K_r Q_cb^T has the A-fragment layout of P (row t, contraction i),
-// so its four values per lane are half of fragment (cb, r / 2).  All operand
-// reads are issued first and the five tiles' MFMAs interleave.
-template <int CW>
-__device__ __forceinline__ void scan_p_tiles(const lds_t *st, lds_t *pb, const int (&kq_off)[4][2], int lane) {
-  constexpr int R[2][5] = {{0, 0, 1, 0, 1}, {2, 0, 1, 2, 3}};
-  constexpr int CB[2][5] = {{0, 1, 1, 2, 2}, {2, 3, 3, 3, 3}};
-  constexpr int KLO = CW == 0 ? 0 : 0, KHI = CW == 0 ? 2 : 4;  // k blocks used
-  constexpr int QLO = CW == 0 ? 0 : 2, QHI = CW == 0 ? 3 : 4;  // q blocks used
+// Token row blocks of P and of the outputs that copy wave CW owns:
+// copy_rows(CW, 0..1) (tile_index.hpp), five 16 x 16 tiles of P each.
+template <int CW> __device__ constexpr int own_rt(int a) { return copy_rows(CW, a); }
+
+// What a copy wave keeps from one phase to the next for a chunk's outputs.
+struct OutOperands {
+  Frag<bf16_t> q[2][4];  // q rows of its two row blocks, [block][contraction block]
+  Frag<bf16_t> p[2][2];  // P fragments of those rows (row t, contraction i)
+  float gam[2];          // gamma_t of this lane's token (16 rt + lane mod 16) in each block
+};
+
+// Copy wave CW's rows of P = Gamma . (Q K^T) (i <= t) for the chunk staged at
+// `st`.  The tile K_r Q_rt^T leaves, in accumulator layout, the values
+// P[16 rt + lane mod 16][16 r + 4 (lane / 16) + e] -- half of the P fragment
+// (rt, r / 2) -- so P stays in registers.  `between` runs after the operand
+// reads are issued.
+template <int CW, typename Between>
+__device__ __forceinline__ void scan_form_p(const lds_t *st, const int (&kq_off)[4][2], int lane, OutOperands &op,
+                                            Between &&between) {
+  constexpr int KB = CW == 0 ? 4 : 3;  // k row blocks used (up to the largest own row block)
   const int r0 = lane & 15, g = lane >> 4;
   auto frag = [&](int tile, int rt, int kk) -> Frag<bf16_t> {
     const lds_t *p = st + tile + 4096 * rt;
     return frag_cat(lds_load_single<bf16x4_t>(p + kq_off[kk][0]), lds_load_single<bf16x4_t>(p + kq_off[kk][1]));
   };
-  Frag<bf16_t> kf[4][4], qf[4][4];
+  Frag<bf16_t> kf[4][4];
 #pragma unroll
-  for (int b = KLO; b < KHI; ++b)
+  for (int a = 0; a < 2; ++a)
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) op.q[a][kk] = frag(kStQ, own_rt<CW>(a), kk);
+#pragma unroll
+  for (int b = 0; b < KB; ++b)
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk) kf[b][kk] = frag(kStK, b, kk);
-#pragma unroll
-  for (int b = QLO; b < QHI; ++b)
-#pragma unroll
-    for (int kk = 0; kk < 4; ++kk) qf[b][kk] = frag(kStQ, b, kk);
-  f32x4_t acc[5];
+  between();
+  f32x4_t acc[2][4];
 #pragma unroll
   for (int kk = 0; kk < 4; ++kk)
 #pragma unroll
-    for (int n = 0; n < 5; ++n) acc[n] = mfma(kf[R[CW][n]][kk], qf[CB[CW][n]][kk], kk == 0 ? zero4() : acc[n]);
+    for (int a = 0; a < 2; ++a)
 #pragma unroll
-  for (int n = 0; n < 5; ++n) {
-    const int r = R[CW][n], cb = CB[CW][n];
-    const int t = 16 * cb + r0;
+      for (int r = 0; r <= own_rt<CW>(a); ++r) acc[a][r] = mfma(kf[r][kk], op.q[a][kk], kk == 0 ? zero4() : acc[a][r]);
+  const bf16x4_t z = {0, 0, 0, 0};
+#pragma unroll
+  for (int a = 0; a < 2; ++a) {
+    const int rt = own_rt<CW>(a), t = 16 * rt + r0;
     const float gt = lds_load<float>(st + kStG + 512 + 4 * t);
-    const f32x4_t gi = lds_load<f32x4_t>(st + kStG + 512 + 4 * (16 * r + 4 * g));
-    f32x4_t pv;
+    op.gam[a] = lds_load<float>(st + kStG + 4 * t);
+    bf16x4_t pv[4];
 #pragma unroll
-    for (int e = 0; e < 4; ++e) pv[e] = 16 * r + 4 * g + e <= t ? fast_exp2(gt - gi[e]) * acc[n][e] : 0.0f;
-    lds_store<bf16x4_t>(pb + 1024 * (2 * cb + (r >> 1)) + 16 * lane + 8 * (r & 1), __builtin_convertvector(pv, bf16x4_t));
+    for (int r = 0; r < 4; ++r) {
+      if (r > rt) {
+        pv[r] = z;
+        continue;
+      }
+      const f32x4_t gi = lds_load<f32x4_t>(st + kStG + 512 + 4 * (16 * r + 4 * g));
+      f32x4_t x;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float val = fast_exp2(gt - gi[e]) * acc[a][r][e];
+        x[e] = (r < rt || 4 * g + e <= r0) ? val : 0.0f;
+      }
+      pv[r] = __builtin_convertvector(x, bf16x4_t);
+    }
+    op.p[a][0] = frag_cat(pv[0], pv[1]);
+    op.p[a][1] = frag_cat(pv[2], pv[3]);
   }
 }
 
-// NG = 16-column groups per compute wave: 2 compute waves of one group, or
-// one compute wave of two groups (which reads each k, q, T and P fragment
-// once for both).  The copy waves follow the compute waves.
-template <int NG>
-__global__ __launch_bounds__(64 * (2 / NG + 2)) void scan_kernel_staged(ScanArgs<bf16_t> a) {
-  constexpr int kCompute = 2 / NG;
+template <int CW>
+__device__ __forceinline__ void scan_copy_waves(const ScanArgs<bf16_t> &a, int lane, int h, int hq, int cb,
+                                                int start, int end, int c_first, int n_chunks) {
+  const int r0 = lane & 15, g = lane >> 4;
+  const int C = a.geo.chunk;
+  const int64_t qk_stride = int64_t(a.H_qk) * 128;
+  const int64_t v_stride = int64_t(a.H_v) * a.d_v;
+  const uint32_t kq_row_bytes = uint32_t(2 * qk_stride), v_row_bytes = uint32_t(2 * v_stride);
+  const int64_t ebytes = entry_bytes<bf16_t>();
+  const char *kq_src = reinterpret_cast<const char *>(CW == 0 ? a.k : a.q) + int64_t(hq) * 256;
+  const char *v_src = reinterpret_cast<const char *>(a.v) + (int64_t(h) * a.d_v + 32 * cb) * 2;
+  // Per-lane byte offsets of every copy of a full chunk (tile_index.hpp),
+  // relative to the chunk's first row.  The k / q and v copies go through a
+  // buffer resource whose size ends at the chunk's last row, so rows past a
+  // partial chunk read as zeros (exact zeros that the chunk algebra only
+  // multiplies by zero) and no copy can leave the sequence.
+  uint32_t kq_voff[16];
+#pragma unroll
+  for (int i = 0; i < 16; ++i) kq_voff[i] = uint32_t(rowtile_copy_src(i, lane, 64, qk_stride));
+  uint32_t v_voff[2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) v_voff[i] = uint32_t(vblock_copy_src(2 * CW + i, lane, 64, v_stride));
+
+  // A stage's copies in three groups: the k (or q) tile copies 0-7 and
+  // 8-15, then T, gates and v.
+  auto stage_part = [&](int part, int cc, char *base_mem) {
+    const int tok0 = start + cc * C;
+    const int len = min(C, end - tok0);
+    lds_t *const base = lds_ptr(base_mem);
+    if (part < 2) {
+      const i32x4_t kq_res = buffer_rsrc(kq_src + int64_t(tok0) * kq_row_bytes, rowtile_valid_bytes(len, kq_row_bytes));
+      lds_t *const tile = base + (CW == 0 ? kStK : kStQ);
+#pragma unroll
+      for (int i = 8 * part; i < 8 * part + 8; ++i) dma16_buf(kq_res, kq_voff[i], tile + 1024 * i);
+      return;
+    }
+    const char *entry = a.entries + (int64_t(c_first + cc) * a.H_v + h) * ebytes;
+#pragma unroll
+    for (int i = 0; i < 3; ++i) {
+      const int f = CW == 0 ? 2 * i : 5 + i;  // T fragments 0, 2, 4 / 5, 6, 7
+      dma16(entry + 1024 * f, 16 * lane, base + kStT + 1024 * f);
+    }
+    if (CW == 0) dma16(entry + 16384, 16 * lane, base + kStG);
+    const i32x4_t v_res = buffer_rsrc(v_src + int64_t(tok0) * v_row_bytes, vblock_valid_bytes(len, v_row_bytes));
+#pragma unroll
+    for (int i = 0; i < 2; ++i) dma16_buf(v_res, v_voff[i], base + kStV + 2048 * CW + 1024 * i);
+  };
+  auto stage = [&](int cc, char *base_mem) {
+    stage_part(0, cc, base_mem);
+    stage_part(1, cc, base_mem);
+    stage_part(2, cc, base_mem);
+  };
+  auto wait_all_but_newest_stage = [&]() {
+    if (CW == 0)
+      wait_vmem_upto<kStageLoadsW2>();
+    else
+      wait_vmem_upto<kStageLoadsW3>();
+  };
+  int kq_off[4][2];
+#pragma unroll
+  for (int kk = 0; kk < 4; ++kk)
+#pragma unroll
+    for (int hf = 0; hf < 2; ++hf) kq_off[kk][hf] = 2 * rowtile_off(r0, 32 * kk + 16 * hf + 4 * g);
+
+  // Outputs of chunk oc from exchange buffer `ex_mem` and the operands kept
+  // from its phase: transposed tiles, lane = token row 16 rt + lane mod 16,
+  // columns 16 cg + 4 (lane / 16) .. + 3 of the block, one 8-byte store each.
+  OutOperands op;
+  bf16_t *const o_lane = a.o + int64_t(start + out_acc_row(0, lane)) * v_stride + int64_t(h) * a.d_v + 32 * cb +
+                         out_acc_col(0, lane);
+  auto outputs = [&](int oc, const char *ex_mem) {
+    const lds_t *ex = lds_ptr(const_cast<char *>(ex_mem));
+    Frag<bf16_t> sx[2][4], ux[2][2];
+#pragma unroll
+    for (int cg = 0; cg < 2; ++cg) {
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk) sx[cg][kk].v = lds_load<bf16x8_t>(ex + kExWave * cg + kExS + 1024 * kk + 16 * lane);
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk) ux[cg][kk].v = lds_load<bf16x8_t>(ex + kExWave * cg + kExU + 1024 * kk + 16 * lane);
+    }
+    const int len = min(C, end - (start + oc * C));
+    bf16_t *const o_chunk = o_lane + int64_t(oc) * C * v_stride;
+#pragma unroll
+    for (int b = 0; b < 2; ++b) {
+      const int rt = own_rt<CW>(b);
+#pragma unroll
+      for (int cg = 0; cg < 2; ++cg) {
+        f32x4_t acc = zero4();
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) acc = mfma(sx[cg][kk], op.q[b][kk], acc);
+        acc = op.gam[b] * acc;
+#pragma unroll
+        for (int kk = 0; kk < (rt < 2 ? 1 : 2); ++kk) acc = mfma(ux[cg][kk], op.p[b][kk], acc);
+        if (out_acc_row(rt, lane) < len)
+          *reinterpret_cast<bf16x4_t *>(o_chunk + int64_t(16 * rt) * v_stride + out_acc_col(cg, 0)) =
+              __builtin_convertvector(acc, bf16x4_t);
+      }
+    }
+  };
+
+  if (n_chunks > 0) {
+    stage(0, scan_stage0);
+    stage(min(1, n_chunks - 1), scan_stage1);
+    wait_all_but_newest_stage();
+  }
+  lds_barrier();
+  // In the phase of chunk cc (between the barriers that open chunks cc and
+  // cc + 1): the outputs of chunk cc - 1 (its exchange buffer was written
+  // before this phase's barrier); the stage of chunk cc - 1 is free (the chain
+  // waves read it before that barrier), and chunk cc + 2 goes there (past the
+  // end the last chunk is copied again, so every phase issues the same
+  // loads); the rows of P of chunk cc from its stage; then chunk cc + 1's
+  // stage must be complete.
+  auto phase = [&](int cc, char *dst, const char *cur, const char *ex_prev) {
+    const int pf = min(cc + 2, n_chunks - 1);
+    stage_part(0, pf, dst);
+    if (cc > 0) outputs(cc - 1, ex_prev);
+    stage_part(1, pf, dst);
+    scan_form_p<CW>(lds_ptr(const_cast<char *>(cur)), kq_off, lane, op, [&]() { stage_part(2, pf, dst); });
+    wait_all_but_newest_stage();
+    lds_barrier();
+  };
+  for (int cc = 0; cc < n_chunks; cc += 6) {
+    phase(cc, scan_stage2, scan_stage0, scan_ex1);
+    if (cc + 1 < n_chunks) phase(cc + 1, scan_stage0, scan_stage1, scan_ex0);
+    if (cc + 2 < n_chunks) phase(cc + 2, scan_stage1, scan_stage2, scan_ex1);
+    if (cc + 3 < n_chunks) phase(cc + 3, scan_stage2, scan_stage0, scan_ex0);
+    if (cc + 4 < n_chunks) phase(cc + 4, scan_stage0, scan_stage1, scan_ex1);
+    if (cc + 5 < n_chunks) phase(cc + 5, scan_stage1, scan_stage2, scan_ex0);
+  }
+  // the last chunk's exchange was written before the last barrier
+  if (n_chunks > 0) outputs(n_chunks - 1, (n_chunks - 1) % 2 == 0 ? scan_ex0 : scan_ex1);
+  wait_vmem();  // the trailing copies and stores
+}
+
+__global__ __launch_bounds__(256) void scan_kernel_staged(ScanArgs<bf16_t> a) {
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int r0 = lane & 15, g = lane >> 4;
@@ -292,163 +459,57 @@ __global__ __launch_bounds__(64 * (2 / NG + 2)) void scan_kernel_staged(ScanArgs
   const int C = a.geo.chunk;
   const int c_first = a.geo.first_chunk(s);
   const int n_chunks = max(0, min((end - start + C - 1) / C, a.geo.n_slots - c_first));
-  const int64_t qk_stride = int64_t(a.H_qk) * 128;
-  const int64_t v_stride = int64_t(a.H_v) * a.d_v;
 
-  if (wave >= kCompute) {
-    // ---- copy waves ----
-    const int cw = wave - kCompute;  // 0: k tile, T, gates; 1: q tile, P
-    const uint32_t kq_row_bytes = uint32_t(2 * qk_stride), v_row_bytes = uint32_t(2 * v_stride);
-    const int64_t ebytes = entry_bytes<bf16_t>();
-    const char *kq_src = reinterpret_cast<const char *>(cw == 0 ? a.k : a.q) + int64_t(hq) * 256;
-    const char *v_src = reinterpret_cast<const char *>(a.v) + (int64_t(h) * a.d_v + 32 * cb) * 2;
-    // Per-lane byte offsets of every copy of a full chunk (tile_index.hpp),
-    // relative to the chunk's first row.  The k / q and v copies go through a
-    // buffer resource whose size ends at the chunk's last row, so rows past a
-    // partial chunk read as zeros (exact zeros that the chunk algebra only
-    // multiplies by zero) and no copy can leave the sequence.
-    uint32_t kq_voff[16];
-#pragma unroll
-    for (int i = 0; i < 16; ++i) kq_voff[i] = uint32_t(rowtile_copy_src(i, lane, 64, qk_stride));
-    uint32_t v_voff[2];
-#pragma unroll
-    for (int i = 0; i < 2; ++i) v_voff[i] = uint32_t(vblock_copy_src(2 * cw + i, lane, 64, v_stride));
-
-    auto stage = [&](int cc, char *base_mem) {
-      const int tok0 = start + cc * C;
-      const int len = min(C, end - tok0);
-      lds_t *const base = lds_ptr(base_mem);
-      const i32x4_t kq_res = buffer_rsrc(kq_src + int64_t(tok0) * kq_row_bytes,
-                                         rowtile_valid_bytes(len, kq_row_bytes));
-      lds_t *const tile = base + (cw == 0 ? kStK : kStQ);
-#pragma unroll
-      for (int i = 0; i < 16; ++i) dma16_buf(kq_res, kq_voff[i], tile + 1024 * i);
-      const char *entry = a.entries + (int64_t(c_first + cc) * a.H_v + h) * ebytes;
-#pragma unroll
-      for (int i = 0; i < 3; ++i) {
-        const int f = cw == 0 ? 2 * i : 5 + i;  // T fragments 0, 2, 4 / 5, 6, 7
-        dma16(entry + 1024 * f, 16 * lane, base + kStT + 1024 * f);
-      }
-      if (cw == 0) dma16(entry + 16384, 16 * lane, base + kStG);
-      const i32x4_t v_res = buffer_rsrc(v_src + int64_t(tok0) * v_row_bytes,
-                                        vblock_valid_bytes(len, v_row_bytes));
-#pragma unroll
-      for (int i = 0; i < 2; ++i) dma16_buf(v_res, v_voff[i], base + kStV + 2048 * cw + 1024 * i);
-    };
-    auto wait_all_but_newest_stage = [&]() {
-      if (cw == 0)
-        wait_vmem_upto<kStageLoadsW2>();
-      else
-        wait_vmem_upto<kStageLoadsW3>();
-    };
-    // P of the chunk in stage `stage_mem` into `p_mem`.
-    int kq_off[4][2];
-#pragma unroll
-    for (int kk = 0; kk < 4; ++kk)
-#pragma unroll
-      for (int hf = 0; hf < 2; ++hf) kq_off[kk][hf] = 2 * rowtile_off(r0, 32 * kk + 16 * hf + 4 * g);
-    auto p_tiles = [&](const char *stage_mem, char *p_mem) {
-      if (cw == 0)
-        scan_p_tiles<0>(lds_ptr(const_cast<char *>(stage_mem)), lds_ptr(p_mem), kq_off, lane);
-      else
-        scan_p_tiles<1>(lds_ptr(const_cast<char *>(stage_mem)), lds_ptr(p_mem), kq_off, lane);
-    };
-    // the zero halves of fragments 0 and 5 (tiles r = 1, cb = 0 and r = 3,
-    // cb = 2) never change
-    if (cw == 0) {
-      const bf16x4_t z = {0, 0, 0, 0};
-      lds_store<bf16x4_t>(lds_ptr(scan_p0) + 1024 * 0 + 16 * lane + 8, z);
-      lds_store<bf16x4_t>(lds_ptr(scan_p0) + 1024 * 5 + 16 * lane + 8, z);
-      lds_store<bf16x4_t>(lds_ptr(scan_p1) + 1024 * 0 + 16 * lane + 8, z);
-      lds_store<bf16x4_t>(lds_ptr(scan_p1) + 1024 * 5 + 16 * lane + 8, z);
-    }
-    if (n_chunks > 0) {
-      stage(0, scan_stage0);
-      stage(min(1, n_chunks - 1), scan_stage1);
-      wait_all_but_newest_stage();
-    }
-    lds_barrier();
-    // In the phase of chunk cc (between the barriers that open chunks cc and
-    // cc + 1) the stage of chunk cc - 1 is free: the compute waves read it
-    // before the barrier that opened chunk cc.  Chunk cc + 2 goes there (past
-    // the end the last chunk is copied again, so every phase issues the same
-    // loads); P of chunk cc is formed from its stage into P buffer cc mod 2
-    // (read by the compute waves in the next phase, and free again by the
-    // phase after); then chunk cc + 1's stage must be complete.
-    auto phase = [&](int cc, char *dst, const char *cur, char *p_mem) {
-      stage(min(cc + 2, n_chunks - 1), dst);
-      p_tiles(cur, p_mem);
-      wait_all_but_newest_stage();
-      lds_barrier();
-    };
-    for (int cc = 0; cc < n_chunks; cc += 6) {
-      phase(cc, scan_stage2, scan_stage0, scan_p0);
-      if (cc + 1 < n_chunks) phase(cc + 1, scan_stage0, scan_stage1, scan_p1);
-      if (cc + 2 < n_chunks) phase(cc + 2, scan_stage1, scan_stage2, scan_p0);
-      if (cc + 3 < n_chunks) phase(cc + 3, scan_stage2, scan_stage0, scan_p1);
-      if (cc + 4 < n_chunks) phase(cc + 4, scan_stage0, scan_stage1, scan_p0);
-      if (cc + 5 < n_chunks) phase(cc + 5, scan_stage1, scan_stage2, scan_p1);
-    }
-    wait_vmem();  // the trailing copies
+  if (wave == 2) {
+    scan_copy_waves<0>(a, lane, h, hq, cb, start, end, c_first, n_chunks);
+    return;
+  }
+  if (wave == 3) {
+    scan_copy_waves<1>(a, lane, h, hq, cb, start, end, c_first, n_chunks);
     return;
   }
 
-  // ---- compute waves: 16-column groups grp = NG wave + cg of the block ----
+  // ---- chain waves: wave w owns columns 32 cb + 16 w .. + 15 ----
   // ---- lane-invariant LDS byte offsets (relative to a stage) ----
-  // A fragments of k / q rows 16 rt + r0, columns 32 kk + 16 half + 4 g:
+  // A fragments of k rows 16 rt + r0, columns 32 kk + 16 half + 4 g:
   // offset = 4096 rt + kq_off[kk][half].
   int kq_off[4][2];
 #pragma unroll
   for (int kk = 0; kk < 4; ++kk)
 #pragma unroll
-    for (int hf = 0; hf < 2; ++hf)
-      kq_off[kk][hf] = 2 * rowtile_off(r0, 32 * kk + 16 * hf + 4 * g);
+    for (int hf = 0; hf < 2; ++hf) kq_off[kk][hf] = 2 * rowtile_off(r0, 32 * kk + 16 * hf + 4 * g);
   // transposed K^T fragments: lane a = r0 addresses token
   // 32 kk + 16 half + 4 g + a / 4, columns 16 rm + 4 (a mod 4) .. + 3:
   // offset = 8192 kk + 4096 half + kt_off[rm].
   int kt_off[8];
 #pragma unroll
   for (int rm = 0; rm < 8; ++rm) kt_off[rm] = 2 * rowtile_off(4 * g + (r0 >> 2), 16 * rm + 4 * (r0 & 3));
-  // transposed v tile rt of group grp (rows 16 rt + 4 g + a / 4, columns
-  // 16 grp + 4 (a mod 4)): offset = 1024 rt + v_off[cg].
-  int v_off[NG];
-  // outputs as computed (transposed tiles): token row 16 rt + r0, columns
-  // 16 grp + 4 g .. + 3 of the block, one 8-byte store per tile
-  bf16_t *o_lane[NG];
-  int col[NG];  // this lane's state column in each group
-#pragma unroll
-  for (int cg = 0; cg < NG; ++cg) {
-    const int grp = NG * wave + cg;
-    v_off[cg] = vtile_byte(4 * g + (r0 >> 2), 16 * grp + 4 * (r0 & 3));
-    o_lane[cg] = a.o + int64_t(start + out_acc_row(0, lane)) * v_stride + int64_t(h) * a.d_v + 32 * cb +
-                 out_acc_col(grp, lane);
-    col[cg] = 32 * cb + 16 * grp + r0;
-  }
+  // transposed v tile rt of this wave's columns (rows 16 rt + 4 g + a / 4,
+  // columns 16 w + 4 (a mod 4)): offset = 1024 rt + v_off.
+  const int v_off = vtile_byte(4 * g + (r0 >> 2), 16 * wave + 4 * (r0 & 3));
+  const int col = 32 * cb + 16 * wave + r0;  // this lane's state column
+  const int ex_off = kExWave * wave + 16 * lane;
 
   // ---- state ----
-  f32x4_t S[NG][8];
+  f32x4_t S[8];
   const int64_t st_base = (int64_t(s) * a.H_v + h) * 128 * a.d_v;
 #pragma unroll
-  for (int cg = 0; cg < NG; ++cg)
-#pragma unroll
-    for (int rt = 0; rt < 8; ++rt) {
-      S[cg][rt] = zero4();
-      if (a.h0)
-        for (int e = 0; e < 4; ++e)
-          S[cg][rt][e] = a.h0[st_base + int64_t(16 * rt + 4 * g + e) * a.d_v + col[cg]];
-    }
+  for (int rt = 0; rt < 8; ++rt) {
+    S[rt] = zero4();
+    if (a.h0)
+      for (int e = 0; e < 4; ++e) S[rt][e] = a.h0[st_base + int64_t(16 * rt + 4 * g + e) * a.d_v + col];
+  }
 
   // Operands of the chunk about to run, read from its stage right after the
   // barrier that completes it: gate factors (rows 16 rt + 4 g + e of this
-  // lane's column, the token of this lane's transposed output tiles, the
-  // chunk's last slot), k row fragments, v transposed, T fragments.  Row
-  // fragments are two 8-byte reads each, kept single (not paired across
-  // tiles) so that they land in the fragment's registers directly.
+  // lane's column, the chunk's last slot), k row fragments, v transposed, T
+  // fragments.  Row fragments are two 8-byte reads each, kept single (not
+  // paired across tiles) so that they land in the fragment's registers
+  // directly.
   float gamma_C;
   f32x4_t gam[4], sc[4];
-  float gam_tok[4];
   Frag<bf16_t> kf[4][4];  // k rows: [contraction block][row tile]
-  bf16x4_t vt[NG][4];     // v, transposed: four rows of this lane's column
+  bf16x4_t vt[4];         // v, transposed: four rows of this lane's column
   Frag<bf16_t> tf[8];
   auto read_operands = [&](const char *stage_mem) {
     const lds_t *st = lds_ptr(const_cast<char *>(stage_mem));
@@ -457,7 +518,6 @@ __global__ __launch_bounds__(64 * (2 / NG + 2)) void scan_kernel_staged(ScanArgs
     for (int rt = 0; rt < 4; ++rt) {
       gam[rt] = lds_load<f32x4_t>(st + kStG + 64 * rt + 16 * g);
       sc[rt] = lds_load<f32x4_t>(st + kStG + 256 + 64 * rt + 16 * g);
-      gam_tok[rt] = lds_load<float>(st + kStG + 4 * out_acc_row(rt, lane));
     }
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk)
@@ -468,9 +528,7 @@ __global__ __launch_bounds__(64 * (2 / NG + 2)) void scan_kernel_staged(ScanArgs
                               lds_load_single<bf16x4_t>(pk + kq_off[kk][1]));
       }
 #pragma unroll
-    for (int cg = 0; cg < NG; ++cg)
-#pragma unroll
-      for (int rt = 0; rt < 4; ++rt) vt[cg][rt] = lds_read_tr16(st + kStV + 1024 * rt + v_off[cg]);
+    for (int rt = 0; rt < 4; ++rt) vt[rt] = lds_read_tr16(st + kStV + 1024 * rt + v_off);
 #pragma unroll
     for (int i = 0; i < 8; ++i)
       if (i != 1 && i != 3) tf[i].v = lds_load<bf16x8_t>(st + kStT + 1024 * i + 16 * lane);
@@ -479,94 +537,27 @@ __global__ __launch_bounds__(64 * (2 / NG + 2)) void scan_kernel_staged(ScanArgs
   lds_barrier();  // the first two stages are complete
   if (n_chunks > 0) read_operands(scan_stage0);
 
-  // Chunk c's output products run inside chunk c + 1's state chain, where the
-  // MFMA pipe would otherwise wait on the chain's VALU work: they need the
-  // chunk-start state and U of chunk c (o_Sf, o_Uf), its q rows (read during
-  // chunk c) and its P (read after the barrier that follows chunk c).  The
-  // outputs leave at the end of the next chain, when the copy waves' burst
-  // of copies after the barrier has drained from the memory pipeline.
-  Frag<bf16_t> o_Sf[NG][4], o_Uf[NG][2], o_qf[4][4], o_pf[8];
-  float o_gt[4];
-  bf16x4_t o_pend[NG][4];
-#pragma unroll
-  for (int i = 0; i < 8; ++i) o_pf[i].zero();
-#pragma unroll
-  for (int kk = 0; kk < 4; ++kk)
-#pragma unroll
-    for (int rt = 0; rt < 4; ++rt) o_qf[kk][rt].zero();
-#pragma unroll
-  for (int cg = 0; cg < NG; ++cg) {
-#pragma unroll
-    for (int kk = 0; kk < 4; ++kk) o_Sf[cg][kk].zero();
-    o_Uf[cg][0].zero();
-    o_Uf[cg][1].zero();
-  }
-#pragma unroll
-  for (int rt = 0; rt < 4; ++rt) o_gt[rt] = 0.0f;
-
-  // O = gamma (Q S) + P U with the chunk-start state, computed as
-  // O^T = S^T (gamma Q^T) + U^T P^T: with the kappa fragment convention Sf
-  // and Uf serve as A operands and the q rows and P fragments as B operands
-  // unchanged, and each lane ends with four consecutive columns of one token
-  // row, one 8-byte piece of the output.  (T and P rows 0-31 end at column 31.)
-  f32x4_t oq[NG][4];
-  auto out_qs = [&]() {
-#pragma unroll
-    for (int rt = 0; rt < 4; ++rt)
-#pragma unroll
-      for (int cg = 0; cg < NG; ++cg)
-#pragma unroll
-        for (int kk = 0; kk < 4; ++kk) oq[cg][rt] = mfma(o_Sf[cg][kk], o_qf[kk][rt], kk == 0 ? zero4() : oq[cg][rt]);
-  };
-  auto out_pu = [&]() {
-#pragma unroll
-    for (int rt = 0; rt < 4; ++rt)
-#pragma unroll
-      for (int cg = 0; cg < NG; ++cg) {
-        f32x4_t acc = o_gt[rt] * oq[cg][rt];
-#pragma unroll
-        for (int kk = 0; kk < (rt < 2 ? 1 : 2); ++kk) acc = mfma(o_Uf[cg][kk], o_pf[rt * 2 + kk], acc);
-        o_pend[cg][rt] = __builtin_convertvector(acc, bf16x4_t);
-      }
-  };
-  auto store_out = [&](int oc) {
-    const int len = min(C, end - (start + oc * C));
-#pragma unroll
-    for (int cg = 0; cg < NG; ++cg) {
-      bf16_t *const o_chunk = o_lane[cg] + int64_t(oc) * C * v_stride;
-#pragma unroll
-      for (int rt = 0; rt < 4; ++rt)
-        if (out_acc_row(rt, lane) < len)
-          *reinterpret_cast<bf16x4_t *>(o_chunk + int64_t(16 * rt) * v_stride) = o_pend[cg][rt];
-    }
-  };
-
-  // One chunk, software-pipelined: the state chain runs from the operands
-  // read after the previous barrier, with the previous chunk's output
-  // products interleaved; the q rows and K^T are read from the stage during
-  // the chain.  The barrier follows the state update (after it the copy
-  // waves may reuse the previous chunk's stage); then the next chunk's
-  // operands and this chunk's P are read.  With two groups each operand
-  // fragment serves both.
-  auto chunk_step = [&](int cc, char *cur_mem, char *next_mem, const char *p_mem) {
+  // One chunk: the state chain from the operands read after the previous
+  // barrier, the chunk-start state and U handed to the copy waves through
+  // exchange buffer `ex_mem`, K^T read from the stage during the chain.  The
+  // barrier follows the state update (after it the copy waves may reuse this
+  // chunk's stage); then the next chunk's operands are read.
+  auto chunk_step = [&](int cc, char *cur_mem, char *next_mem, char *ex_mem) {
     const lds_t *const st = lds_ptr(cur_mem);
+    lds_t *const ex = lds_ptr(ex_mem) + ex_off;
 
-    Frag<bf16_t> Sf[NG][4];
+    Frag<bf16_t> Sf[4];
 #pragma unroll
-    for (int cg = 0; cg < NG; ++cg)
-#pragma unroll
-      for (int kk = 0; kk < 4; ++kk) Sf[cg][kk] = frag_from_acc<bf16_t>(S[cg][2 * kk], S[cg][2 * kk + 1]);
+    for (int kk = 0; kk < 4; ++kk) Sf[kk] = frag_from_acc<bf16_t>(S[2 * kk], S[2 * kk + 1]);
 
     // Y = K S
-    f32x4_t Y[NG][4];
+    f32x4_t Y[4];
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk)
 #pragma unroll
-      for (int rt = 0; rt < 4; ++rt)
+      for (int rt = 0; rt < 4; ++rt) Y[rt] = mfma(kf[kk][rt], Sf[kk], kk == 0 ? zero4() : Y[rt]);
 #pragma unroll
-        for (int cg = 0; cg < NG; ++cg)
-          Y[cg][rt] = mfma(kf[kk][rt], Sf[cg][kk], kk == 0 ? zero4() : Y[cg][rt]);
-    out_qs();  // previous chunk: S^T (Q^T)
+    for (int kk = 0; kk < 4; ++kk) lds_store<bf16x8_t>(ex + kExS + 1024 * kk, Sf[kk].v);
 
     // K^T fragments for the state update (transposed reads of the k tile),
     // issued early so that they have landed when the update starts
@@ -580,102 +571,60 @@ __global__ __launch_bounds__(64 * (2 / NG + 2)) void scan_kernel_staged(ScanArgs
       }
 
     // X = V - gamma Y, then U = T X
-    Frag<bf16_t> Xf[NG][2];
-#pragma unroll
-    for (int cg = 0; cg < NG; ++cg) {
+    Frag<bf16_t> Xf[2];
+    {
       f32x4_t X[4];
 #pragma unroll
-      for (int rt = 0; rt < 4; ++rt) X[rt] = __builtin_convertvector(vt[cg][rt], f32x4_t) - gam[rt] * Y[cg][rt];
-      Xf[cg][0] = frag_from_acc<bf16_t>(X[0], X[1]);
-      Xf[cg][1] = frag_from_acc<bf16_t>(X[2], X[3]);
+      for (int rt = 0; rt < 4; ++rt) X[rt] = __builtin_convertvector(vt[rt], f32x4_t) - gam[rt] * Y[rt];
+      Xf[0] = frag_from_acc<bf16_t>(X[0], X[1]);
+      Xf[1] = frag_from_acc<bf16_t>(X[2], X[3]);
     }
-    f32x4_t Ua[NG][4];
+    f32x4_t Ua[4];
 #pragma unroll
     for (int rt = 0; rt < 4; ++rt)
 #pragma unroll
       for (int kk = 0; kk < (rt < 2 ? 1 : 2); ++kk)  // T rows 0-31 end at column 31
-#pragma unroll
-        for (int cg = 0; cg < NG; ++cg)
-          Ua[cg][rt] = mfma(tf[rt * 2 + kk], Xf[cg][kk], kk == 0 ? zero4() : Ua[cg][rt]);
-    out_pu();  // previous chunk: + U^T P^T
+        Ua[rt] = mfma(tf[rt * 2 + kk], Xf[kk], kk == 0 ? zero4() : Ua[rt]);
 
-    // this chunk's q rows, for its output products in the next chunk
+    Frag<bf16_t> Usf[2];
 #pragma unroll
-    for (int kk = 0; kk < 4; ++kk)
+    for (int kk = 0; kk < 2; ++kk)
+      lds_store<bf16x8_t>(ex + kExU + 1024 * kk, frag_from_acc<bf16_t>(Ua[2 * kk], Ua[2 * kk + 1]).v);
 #pragma unroll
-      for (int rt = 0; rt < 4; ++rt) {
-        const lds_t *pq = st + kStQ + 4096 * rt;
-        o_qf[kk][rt] = frag_cat(lds_load_single<bf16x4_t>(pq + kq_off[kk][0]),
-                                lds_load_single<bf16x4_t>(pq + kq_off[kk][1]));
-      }
-
-    Frag<bf16_t> Usf[NG][2];
-#pragma unroll
-    for (int cg = 0; cg < NG; ++cg) {
-      o_Uf[cg][0] = frag_from_acc<bf16_t>(Ua[cg][0], Ua[cg][1]);
-      o_Uf[cg][1] = frag_from_acc<bf16_t>(Ua[cg][2], Ua[cg][3]);
-#pragma unroll
-      for (int rt = 0; rt < 4; ++rt) Ua[cg][rt] *= sc[rt];
-      Usf[cg][0] = frag_from_acc<bf16_t>(Ua[cg][0], Ua[cg][1]);
-      Usf[cg][1] = frag_from_acc<bf16_t>(Ua[cg][2], Ua[cg][3]);
-    }
+    for (int rt = 0; rt < 4; ++rt) Ua[rt] *= sc[rt];
+    Usf[0] = frag_from_acc<bf16_t>(Ua[0], Ua[1]);
+    Usf[1] = frag_from_acc<bf16_t>(Ua[2], Ua[3]);
 
     // S <- gamma_C S + K^T (s U)
 #pragma unroll
-    for (int rm = 0; rm < 8; ++rm)
+    for (int rm = 0; rm < 8; ++rm) {
+      f32x4_t acc = gamma_C * S[rm];
 #pragma unroll
-      for (int cg = 0; cg < NG; ++cg) {
-        f32x4_t acc = gamma_C * S[cg][rm];
-#pragma unroll
-        for (int kk = 0; kk < 2; ++kk) acc = mfma(ktf[rm][kk], Usf[cg][kk], acc);
-        S[cg][rm] = acc;
-      }
-    if (cc > 0) store_out(cc - 1);
-#pragma unroll
-    for (int cg = 0; cg < NG; ++cg)
-#pragma unroll
-      for (int kk = 0; kk < 4; ++kk) o_Sf[cg][kk] = Sf[cg][kk];
-#pragma unroll
-    for (int rt = 0; rt < 4; ++rt) o_gt[rt] = gam_tok[rt];
+      for (int kk = 0; kk < 2; ++kk) acc = mfma(ktf[rm][kk], Usf[kk], acc);
+      S[rm] = acc;
+    }
 
     // this chunk's stage reads are done (the copy waves may now refill the
-    // previous chunk's stage) and the next chunk's stage is complete
+    // previous chunk's stage), the exchange is written, and the next chunk's
+    // stage is complete
     lds_barrier();
     if (cc + 1 < n_chunks) read_operands(next_mem);
-    {  // P of this chunk, formed by the copy waves
-      const lds_t *pb = lds_ptr(const_cast<char *>(p_mem));
-#pragma unroll
-      for (int i = 0; i < 8; ++i)
-        if (i != 1 && i != 3) o_pf[i].v = lds_load<bf16x8_t>(pb + 1024 * i + 16 * lane);
-    }
   };
   for (int cc = 0; cc < n_chunks; cc += 6) {
-    chunk_step(cc, scan_stage0, scan_stage1, scan_p0);
-    if (cc + 1 < n_chunks) chunk_step(cc + 1, scan_stage1, scan_stage2, scan_p1);
-    if (cc + 2 < n_chunks) chunk_step(cc + 2, scan_stage2, scan_stage0, scan_p0);
-    if (cc + 3 < n_chunks) chunk_step(cc + 3, scan_stage0, scan_stage1, scan_p1);
-    if (cc + 4 < n_chunks) chunk_step(cc + 4, scan_stage1, scan_stage2, scan_p0);
-    if (cc + 5 < n_chunks) chunk_step(cc + 5, scan_stage2, scan_stage0, scan_p1);
-  }
-  if (n_chunks > 0) {  // the last chunk's outputs
-    out_qs();
-    out_pu();
-    store_out(n_chunks - 1);
+    chunk_step(cc, scan_stage0, scan_stage1, scan_ex0);
+    if (cc + 1 < n_chunks) chunk_step(cc + 1, scan_stage1, scan_stage2, scan_ex1);
+    if (cc + 2 < n_chunks) chunk_step(cc + 2, scan_stage2, scan_stage0, scan_ex0);
+    if (cc + 3 < n_chunks) chunk_step(cc + 3, scan_stage0, scan_stage1, scan_ex1);
+    if (cc + 4 < n_chunks) chunk_step(cc + 4, scan_stage1, scan_stage2, scan_ex0);
+    if (cc + 5 < n_chunks) chunk_step(cc + 5, scan_stage2, scan_stage0, scan_ex1);
   }
 
   if (a.hT) {
 #pragma unroll
-    for (int cg = 0; cg < NG; ++cg)
-#pragma unroll
-      for (int rt = 0; rt < 8; ++rt)
-        for (int e = 0; e < 4; ++e)
-          a.hT[st_base + int64_t(16 * rt + 4 * g + e) * a.d_v + col[cg]] = S[cg][rt][e];
+    for (int rt = 0; rt < 8; ++rt)
+      for (int e = 0; e < 4; ++e) a.hT[st_base + int64_t(16 * rt + 4 * g + e) * a.d_v + col] = S[rt][e];
   }
 }
-
-#ifndef SCAN_GROUPS
-#define SCAN_GROUPS 1
-#endif
 
 template <typename T>
 static ScanArgs<T> scan_args(const Problem &p, const Workspace &ws, int colblk_width) {
@@ -704,8 +653,7 @@ hipError_t launch_scan(const Problem &p, const Workspace &ws, hipStream_t st) {
   const int64_t blocks = (int64_t(p.n_seqs) * p.H_v + 7) / 8 * 8 * (p.d_v / width);
   if (blocks == 0) return hipSuccess;
   if (staged) {
-    hipLaunchKernelGGL(scan_kernel_staged<SCAN_GROUPS>, dim3(unsigned(blocks)), dim3(64 * (2 / SCAN_GROUPS + 2)), 0, st,
-                       scan_args<bf16_t>(p, ws, width));
+    hipLaunchKernelGGL(scan_kernel_staged, dim3(unsigned(blocks)), dim3(256), 0, st, scan_args<bf16_t>(p, ws, width));
   } else if (p.dtype == 1) {
     hipLaunchKernelGGL(scan_kernel<bf16_t>, dim3(unsigned(blocks)), dim3(64), 0, st,
                        scan_args<bf16_t>(p, ws, width));

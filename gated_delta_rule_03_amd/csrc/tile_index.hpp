@@ -79,14 +79,13 @@ __host__ __device__ constexpr int vtile_byte(int row, int col) {
 
 // ---- outputs as the MFMA leaves them (transposed tiles) ----
 // Output tile rt, lane l: token row 16 rt + l mod 16, columns
-// 16 w + 4 (l / 16) .. + 3 of wave w's half of the block.
+// 16 cg + 4 (l / 16) .. + 3 of column group cg of the block.
 __host__ __device__ constexpr int out_acc_row(int rt, int lane) { return 16 * rt + (lane & 15); }
-__host__ __device__ constexpr int out_acc_col(int wave, int lane) { return 16 * wave + 4 * (lane >> 4); }
+__host__ __device__ constexpr int out_acc_col(int cg, int lane) { return 16 * cg + 4 * (lane >> 4); }
 
-// ---- outputs leaving the staged v block ----
-// Wave w, piece p (0..1): lane l stores row 32 p + l / 2, columns
-// 16 w + 8 (l mod 2) .. + 7 of the block (one 16-byte store).
-__host__ __device__ constexpr int out_piece_row(int p, int lane) { return 32 * p + (lane >> 1); }
-__host__ __device__ constexpr int out_piece_col(int wave, int lane) { return 16 * wave + 8 * (lane & 1); }
+// Token row blocks (of P and of the outputs) that copy wave cw = 0, 1 owns:
+// {0, 3} and {1, 2}.  Row block rt of the lower-triangular P has rt + 1
+// tiles of 16 x 16, so each copy wave forms five.
+__host__ __device__ constexpr int copy_rows(int cw, int a) { return cw == 0 ? (a == 0 ? 0 : 3) : (a == 0 ? 1 : 2); }
 
 }  // namespace gdn

@@ -118,41 +118,25 @@ int main() {
     for (int x = 0; x < 64 * 32; ++x) CHECK(seen[x] == 1, "v block element %d copied %d times", x, seen[x]);
   }
 
-  // ---- outputs written from the transposed MFMA tiles: 2 waves x 4 tiles x 64 lanes, 4 columns ----
+  // ---- outputs: 2 copy waves x 2 row blocks x 2 column groups x 64 lanes, 4 columns each ----
   {
-    std::vector<int> seen(64 * 32, 0);
-    for (int w = 0; w < 2; ++w)
-      for (int rt = 0; rt < 4; ++rt)
-        for (int l = 0; l < 64; ++l) {
-          const int row = out_acc_row(rt, l), col = out_acc_col(w, l);
-          CHECK(row < 64 && col + 4 <= 32 && col % 4 == 0, "output tile %d lane %d at (%d,%d)", rt, l, row, col);
-          const int base = vtile_byte(out_acc_row(0, l), out_acc_col(w, l));
-          CHECK(vtile_byte(row, col) == base + 1024 * rt, "output tile %d lane %d LDS offset", rt, l);
-          for (int c = 0; c < 4; ++c) {
-            CHECK(vtile_byte(row, col + c) == vtile_byte(row, col) + 2 * c, "output (%d,%d) not contiguous", row, col + c);
-            seen[row * 32 + col + c]++;
+    std::vector<int> seen(64 * 32, 0), p_tiles(2, 0);
+    for (int cw = 0; cw < 2; ++cw)
+      for (int a = 0; a < 2; ++a) {
+        const int rt = copy_rows(cw, a);
+        CHECK(rt >= 0 && rt < 4, "copy wave %d row block %d", cw, rt);
+        p_tiles[cw] += rt + 1;
+        for (int cg = 0; cg < 2; ++cg)
+          for (int l = 0; l < 64; ++l) {
+            const int row = out_acc_row(rt, l), col = out_acc_col(cg, l);
+            CHECK(row < 64 && col + 4 <= 32 && col % 4 == 0, "output tile %d lane %d at (%d,%d)", rt, l, row, col);
+            CHECK(row == out_acc_row(0, l) + 16 * rt && col == out_acc_col(0, l) + 16 * cg,
+                  "output tile %d lane %d offset", rt, l);
+            for (int c = 0; c < 4; ++c) seen[row * 32 + col + c]++;
           }
-        }
+      }
     for (int x = 0; x < 64 * 32; ++x) CHECK(seen[x] == 1, "output element %d written %d times", x, seen[x]);
-  }
-
-  // ---- outputs: 2 waves x 2 pieces x 64 lanes, 8 columns each ----
-  {
-    std::vector<int> seen(64 * 32, 0);
-    for (int w = 0; w < 2; ++w)
-      for (int p = 0; p < 2; ++p)
-        for (int l = 0; l < 64; ++l) {
-          const int row = out_piece_row(p, l), col = out_piece_col(w, l);
-          CHECK(row < 64 && col + 8 <= 32 && col % 8 == 0, "output piece %d lane %d at (%d,%d)", p, l, row, col);
-          const int base = vtile_byte(out_piece_row(0, l), out_piece_col(w, l));
-          CHECK(vtile_byte(row, col) == base + 2048 * p, "output piece %d lane %d LDS offset", p, l);
-          for (int c = 0; c < 8; ++c) {
-            CHECK(vtile_byte(row, col + c) == vtile_byte(row, col) + 2 * c, "output (%d,%d) not contiguous",
-                  row, col + c);
-            seen[row * 32 + col + c]++;
-          }
-        }
-    for (int x = 0; x < 64 * 32; ++x) CHECK(seen[x] == 1, "output element %d stored %d times", x, seen[x]);
+    CHECK(p_tiles[0] == 5 && p_tiles[1] == 5, "P tiles per copy wave %d / %d", p_tiles[0], p_tiles[1]);
   }
 
   if (fails) {
