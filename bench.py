@@ -10,8 +10,11 @@ One step = one pass of the whole path over one batch of synthetic input:
 
 Timing: W untimed warm-up steps, then exactly K steps bracketed by
 torch.cuda.synchronize(); each call is bracketed by HIP events on the stream
-it runs on.  Before each call a 512 MiB scratch write evicts the 256 MB
-last-level cache (outside the events), so inputs come from HBM.
+it runs on.  Before each call a 512 MiB scratch read evicts the 256 MB
+last-level cache (outside the events), so inputs come from HBM.  The flush
+reads rather than writes: a write flush leaves up to 256 MB of dirty lines in
+the memory-side cache, and their write-back lands on whichever kernel runs
+next (``--flush write`` measures that case, ``--flush none`` warm caches).
 
 Prints ONE JSON line.  ``value`` is chunked-forward tokens/s (prefill tokens
 per second of gdn_chunk_fwd); decode steps/s ride along in ``decode``.
@@ -105,7 +108,8 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--no-flush", action="store_true", help="keep caches warm between calls")
+    ap.add_argument("--flush", choices=("read", "write", "none"), default="read",
+                    help="what runs before each call to evict the last-level cache")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run a plain 1 GiB read + 1 GiB write kernel (counter calibration)")
     args = ap.parse_args()
@@ -145,8 +149,17 @@ def main():
     o_d = torch.empty((spec3.B, 1, spec3.H_v, spec3.d_v), dtype=torch.bfloat16, device=dev)
     torch.cuda.synchronize()
 
-    flush = None if args.no_flush else torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+    flush = None if args.flush == "none" else torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+    flush_sink = torch.zeros(1, dtype=torch.int64, device=dev)
     stream = torch.cuda.current_stream()
+
+    def evict(tag):
+        if flush is None:
+            return
+        if args.flush == "write":
+            flush.fill_(tag)
+        else:
+            torch.sum(flush.view(torch.int64), dim=0, keepdim=True, out=flush_sink)
 
     def chunk_call():
         gdn.chunk_fwd(P["q"], P["k"], P["v"], P["alpha"], P["beta"], chunk=64, o=o_p, hT=hT_p,
@@ -157,15 +170,13 @@ def main():
                         stream=stream)
 
     def step(record):
-        if flush is not None:
-            flush.fill_(1)
+        evict(1)
         e0 = torch.cuda.Event(enable_timing=True)
         e1 = torch.cuda.Event(enable_timing=True)
         e0.record(stream)
         chunk_call()
         e1.record(stream)
-        if flush is not None:
-            flush.fill_(2)
+        evict(2)
         e2 = torch.cuda.Event(enable_timing=True)
         e3 = torch.cuda.Event(enable_timing=True)
         e2.record(stream)
@@ -199,8 +210,7 @@ def main():
         c_dst = torch.empty_like(c_src)
         cms = []
         for _ in range(3):
-            if flush is not None:
-                flush.fill_(3)
+            evict(3)
             e0 = torch.cuda.Event(enable_timing=True)
             e1 = torch.cuda.Event(enable_timing=True)
             e0.record(stream)
@@ -236,7 +246,8 @@ def main():
                         "+ decode step B=256 H=32 d=128 (fp32 state in place)",
             "global_batch": B, "seq_len": T, "heads": H, "head_dim": D, "chunk": 64,
             "decode_batch": spec3.B, "decode_heads": spec3.H_v,
-            "cache": "warm" if args.no_flush else "cold (512 MiB flush before each call)",
+            "cache": {"none": "warm", "read": "cold (512 MiB read before each call)",
+                      "write": "cold (512 MiB write before each call)"}[args.flush],
         },
         "decode": {
             "steps_per_s": 1.0 / dec_s,

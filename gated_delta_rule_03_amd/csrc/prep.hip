@@ -236,23 +236,25 @@ __global__ __launch_bounds__(256) void prep_kernel(PrepArgs<T> a) {
 // and its column stores fall in distinct banks.
 // ---------------------------------------------------------------------------
 namespace {
-constexpr int kXK = 0;          // k rows, 64 x 128 bf16 row tile
+constexpr int kXK = 0;          // k rows, 64 x 128 bf16 row tile (dead once in registers)
 constexpr int kXAlpha = 16384;  // alpha, 64 fp32
 constexpr int kXBeta = 16640;   // beta, 64 fp32
 constexpr int kXG = 16896;      // g_t, 64 fp32
 constexpr int kXB = 17152;      // beta_t, 64 fp32 (0 past the chunk's end)
 constexpr int kXRow = 80;       // row stride of an fp32 16 x 16 block
-constexpr int kXAdT = 17408;    // A_bb^T (row j = column j of A_bb)
+// The inverse's blocks reuse the k tile's bytes (both waves hold their k
+// fragments in registers before either writes them).
+constexpr int kXAdT = 0;        // A_bb^T (row j = column j of A_bb)
 constexpr int kXAdTBlk = 1296;  // 324 dwords: 4 mod 32
 constexpr int kXD = kXAdT + 4 * kXAdTBlk;  // D_b, row-major
 constexpr int kXDBlk = 1344;               // 336 dwords: 16 mod 32
 constexpr int kXDt = kXD + 4 * kXDBlk;     // D_b^T
 constexpr int kXDtBlk = 1296;
-constexpr int kXBytes = kXDt + 4 * kXDtBlk;  // 33152: four workgroups per CU
-static_assert(kXBytes <= 160 * 1024 / 4, "four factor workgroups per CU");
+static_assert(kXDt + 4 * kXDtBlk <= kXAlpha, "the inverse's blocks fit in the k tile");
+constexpr int kXBytes = 17408;
 }  // namespace
 
-__global__ __launch_bounds__(128) void factors_kernel(PrepArgs<bf16_t> a) {
+__global__ __launch_bounds__(128, 4) void factors_kernel(PrepArgs<bf16_t> a) {
   const int c = blockIdx.x, h = blockIdx.y;
   int s, tok0, len;
   if (!a.geo.locate(c, s, tok0, len)) return;
@@ -320,12 +322,20 @@ __global__ __launch_bounds__(128) void factors_kernel(PrepArgs<bf16_t> a) {
     const float bl = lane < len ? lds_load<float>(sm + kXBeta + 4 * lane) : 0.0f;
     lds_store<float>(sm + kXG + 4 * lane, gl);
     lds_store<float>(sm + kXB + 4 * lane, bl);
+    // k row fragments of the four 16-row blocks, read once; then the k tile's
+    // bytes are free for the inverse's blocks
+    Frag<bf16_t> kfr[4][4];
+#pragma unroll
+    for (int b = 0; b < 4; ++b)
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk) kfr[b][kk] = row_frag(kXK, b, kk);
+    lds_barrier();
     // gated tile: (K_j K_b^T)[4 g + e][c] read as row 16 b + c of A_bj, or, for
     // j == b, as row 16 b + 4 g + e, column 16 b + c of A_bb (column layout)
     auto k_tile = [&](int j, int b) {
       f32x4_t acc = zero4();
 #pragma unroll
-      for (int kk = 0; kk < 4; ++kk) acc = mfma(row_frag(kXK, j, kk), row_frag(kXK, b, kk), acc);
+      for (int kk = 0; kk < 4; ++kk) acc = mfma(kfr[j][kk], kfr[b][kk], acc);
       return acc;
     };
     if (wave == 0) {
