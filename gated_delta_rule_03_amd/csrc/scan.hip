@@ -224,6 +224,7 @@ constexpr int kStBytes = 46080;
 // as two fragments (tokens 32 kk + kappa), 1 KiB each in fragment order.
 constexpr int kExS = 0, kExU = 4096, kExWave = 6144;
 constexpr int kExBytes = 2 * kExWave;
+typedef unsigned u32x2_t __attribute__((ext_vector_type(2)));
 // Copies one copy wave issues per stage (wave 2: k tile, T fragments 0, 2, 4,
 // gates, v columns 0-15; wave 3: q tile, T fragments 5, 6, 7, v columns
 // 16-31).  Loads complete in issue order, and the only other vector-memory
@@ -377,9 +378,18 @@ __device__ __forceinline__ void scan_copy_waves(const ScanArgs<bf16_t> &a, int l
   // Outputs of chunk oc from exchange buffer `ex_mem` and the operands kept
   // from its phase: transposed tiles, lane = token row 16 rt + lane mod 16,
   // columns 16 cg + 4 (lane / 16) .. + 3 of the block, one 8-byte store each.
+  // The four tiles' products are independent and issue interleaved; the
+  // stores go through a buffer resource that ends at the chunk's last row, so
+  // rows past a partial chunk are dropped without a branch.
   OutOperands op;
-  bf16_t *const o_lane = a.o + int64_t(start + out_acc_row(0, lane)) * v_stride + int64_t(h) * a.d_v + 32 * cb +
-                         out_acc_col(0, lane);
+  const uint32_t o_row_bytes = uint32_t(2 * v_stride);
+  const char *const o_base = reinterpret_cast<const char *>(a.o + int64_t(h) * a.d_v + 32 * cb);
+  uint32_t o_voff[2][2];
+#pragma unroll
+  for (int b = 0; b < 2; ++b)
+#pragma unroll
+    for (int cg = 0; cg < 2; ++cg)
+      o_voff[b][cg] = uint32_t(out_acc_row(own_rt<CW>(b), lane)) * o_row_bytes + 2 * out_acc_col(cg, lane);
   auto outputs = [&](int oc, const char *ex_mem) {
     const lds_t *ex = lds_ptr(const_cast<char *>(ex_mem));
     Frag<bf16_t> sx[2][4], ux[2][2];
@@ -390,24 +400,34 @@ __device__ __forceinline__ void scan_copy_waves(const ScanArgs<bf16_t> &a, int l
 #pragma unroll
       for (int kk = 0; kk < 2; ++kk) ux[cg][kk].v = lds_load<bf16x8_t>(ex + kExWave * cg + kExU + 1024 * kk + 16 * lane);
     }
-    const int len = min(C, end - (start + oc * C));
-    bf16_t *const o_chunk = o_lane + int64_t(oc) * C * v_stride;
+    f32x4_t acc[2][2];
 #pragma unroll
-    for (int b = 0; b < 2; ++b) {
-      const int rt = own_rt<CW>(b);
+    for (int kk = 0; kk < 4; ++kk)
 #pragma unroll
-      for (int cg = 0; cg < 2; ++cg) {
-        f32x4_t acc = zero4();
+      for (int b = 0; b < 2; ++b)
 #pragma unroll
-        for (int kk = 0; kk < 4; ++kk) acc = mfma(sx[cg][kk], op.q[b][kk], acc);
-        acc = op.gam[b] * acc;
+        for (int cg = 0; cg < 2; ++cg) acc[b][cg] = mfma(sx[cg][kk], op.q[b][kk], kk == 0 ? zero4() : acc[b][cg]);
 #pragma unroll
-        for (int kk = 0; kk < (rt < 2 ? 1 : 2); ++kk) acc = mfma(ux[cg][kk], op.p[b][kk], acc);
-        if (out_acc_row(rt, lane) < len)
-          *reinterpret_cast<bf16x4_t *>(o_chunk + int64_t(16 * rt) * v_stride + out_acc_col(cg, 0)) =
-              __builtin_convertvector(acc, bf16x4_t);
-      }
-    }
+    for (int b = 0; b < 2; ++b)
+#pragma unroll
+      for (int cg = 0; cg < 2; ++cg) acc[b][cg] = op.gam[b] * acc[b][cg];
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+      for (int b = 0; b < 2; ++b)
+#pragma unroll
+        for (int cg = 0; cg < 2; ++cg)
+          if (kk < (own_rt<CW>(b) < 2 ? 1 : 2)) acc[b][cg] = mfma(ux[cg][kk], op.p[b][kk], acc[b][cg]);
+    const int tok0 = start + oc * C;
+    const int len = min(C, end - tok0);
+    const __amdgpu_buffer_rsrc_t o_res = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<char *>(o_base + int64_t(tok0) * o_row_bytes), 0, int((len - 1) * o_row_bytes + 64), 0x00020000);
+#pragma unroll
+    for (int b = 0; b < 2; ++b)
+#pragma unroll
+      for (int cg = 0; cg < 2; ++cg)
+        __builtin_amdgcn_raw_buffer_store_b64(
+            __builtin_bit_cast(u32x2_t, __builtin_convertvector(acc[b][cg], bf16x4_t)), o_res, o_voff[b][cg], 0, 0);
   };
 
   if (n_chunks > 0) {
