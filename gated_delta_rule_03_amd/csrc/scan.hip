@@ -193,8 +193,8 @@ __global__ __launch_bounds__(64) void scan_kernel(ScanArgs<T> a) {
 // 64 x 32 block of v -- are copied into one of three LDS stages with
 // buffer/global loads straight to LDS, two chunks ahead of the chunk being
 // computed.  A copy moves 1 KiB and the memory pipeline accepts one from a
-// wave only every few dozen cycles, so the copies are issued by the copy
-// waves, on SIMDs the chain waves leave idle.
+// wave only every few dozen cycles, so the copies are spread over the waves:
+// the copy waves issue the k and q tiles, the chain waves the small rest.
 //
 // The chain waves' instruction stream is the whole cost of a chunk, so it
 // holds the state chain only: Y = K S, U = T (V - gamma Y), the state update.
@@ -215,24 +215,27 @@ __global__ __launch_bounds__(64) void scan_kernel(ScanArgs<T> a) {
 // ---------------------------------------------------------------------------
 constexpr int kStK = 0;        // 64 x 128 bf16 row tile
 constexpr int kStQ = 16384;    // 64 x 128 bf16 row tile
-constexpr int kStT = 32768;    // T fragments, 1 KiB each (1 and 3 unused)
-constexpr int kStG = 40960;    // gate block: gamma, s, g (64 fp32 each), padding
-constexpr int kStV = 41984;    // 64 x 32 bf16 v block
-constexpr int kStBytes = 46080;
+constexpr int kStT = 32768;    // T's six non-zero fragments, 1 KiB each (t_slot, tile_index.hpp)
+constexpr int kStG = 38912;    // gate block: gamma, s, g (64 fp32 each), padding
+constexpr int kStV = 39936;    // 64 x 32 bf16 v block
+constexpr int kStBytes = 44032;
+
 // Exchange buffer: per chain wave w, at 6144 w, the chunk-start state as four
 // bf16 A fragments of S^T (fragment kk: state rows 32 kk + kappa) and then U
 // as two fragments (tokens 32 kk + kappa), 1 KiB each in fragment order.
 constexpr int kExS = 0, kExU = 4096, kExWave = 6144;
 constexpr int kExBytes = 2 * kExWave;
 typedef unsigned u32x2_t __attribute__((ext_vector_type(2)));
-// Copies one copy wave issues per stage (wave 2: k tile, T fragments 0, 2, 4,
-// gates, v columns 0-15; wave 3: q tile, T fragments 5, 6, 7, v columns
-// 16-31).  Loads complete in issue order, and the only other vector-memory
-// operations of a copy wave are its output stores; so waiting until at most
-// this many of its operations are outstanding completes every load issued
-// before the newest stage's copies, whatever the stores do.
-constexpr int kStageLoadsW2 = 22;
-constexpr int kStageLoadsW3 = 21;
+// Copies each wave issues per stage: copy wave 2 the k tile, copy wave 3 the
+// q tile (16 each); chain wave 0 T fragments 0, 2, 4, the gates and v rows
+// 0-31, chain wave 1 T fragments 5, 6, 7 and v rows 32-63.  Loads complete in
+// issue order, and the only other vector-memory operations in a wave's loop
+// are a copy wave's output stores; so waiting until at most this many of its
+// operations are outstanding completes every load it issued before the
+// newest stage's copies, whatever the stores do.
+constexpr int kStageLoadsCopy = 16;
+constexpr int kStageLoadsChain0 = 6;
+constexpr int kStageLoadsChain1 = 5;
 
 // Three stages and two exchange buffers as distinct LDS objects: with the
 // chunk loop unrolled by six, every access names its buffer at compile time.
@@ -241,6 +244,10 @@ __shared__ __attribute__((aligned(16))) char scan_stage1[kStBytes];
 __shared__ __attribute__((aligned(16))) char scan_stage2[kStBytes];
 __shared__ __attribute__((aligned(16))) char scan_ex0[kExBytes];
 __shared__ __attribute__((aligned(16))) char scan_ex1[kExBytes];
+// A chunk's outputs on their way out (64 token rows x 32 bf16, out_stage_byte
+// in tile_index.hpp): each copy wave writes and reads back only its own rows,
+// so that every store covers whole 64-byte rows of the block.
+__shared__ __attribute__((aligned(16))) char scan_ostage[4096];
 
 // Token row blocks of P and of the outputs that copy wave CW owns:
 // copy_rows(CW, 0..1) (tile_index.hpp), five 16 x 16 tiles of P each.
@@ -311,17 +318,19 @@ __device__ __forceinline__ void scan_form_p(const lds_t *st, const int (&kq_off)
   }
 }
 
-template <int CW>
+// ROLE 0: copy wave CW issues the k (CW = 0) or q (CW = 1) tile copies and
+// also forms its rows of P and computes their outputs; ROLE 1: P and outputs
+// only; ROLE 2: tile copies only.
+template <int CW, int ROLE>
 __device__ __forceinline__ void scan_copy_waves(const ScanArgs<bf16_t> &a, int lane, int h, int hq, int cb,
-                                                int start, int end, int c_first, int n_chunks) {
+                                                int start, int end, int n_chunks) {
+  constexpr bool kCopies = ROLE != 1, kOutputs = ROLE != 2;
   const int r0 = lane & 15, g = lane >> 4;
   const int C = a.geo.chunk;
   const int64_t qk_stride = int64_t(a.H_qk) * 128;
   const int64_t v_stride = int64_t(a.H_v) * a.d_v;
-  const uint32_t kq_row_bytes = uint32_t(2 * qk_stride), v_row_bytes = uint32_t(2 * v_stride);
-  const int64_t ebytes = entry_bytes<bf16_t>();
+  const uint32_t kq_row_bytes = uint32_t(2 * qk_stride);
   const char *kq_src = reinterpret_cast<const char *>(CW == 0 ? a.k : a.q) + int64_t(hq) * 256;
-  const char *v_src = reinterpret_cast<const char *>(a.v) + (int64_t(h) * a.d_v + 32 * cb) * 2;
   // Per-lane byte offsets of every copy of a full chunk (tile_index.hpp),
   // relative to the chunk's first row.  The k / q and v copies go through a
   // buffer resource whose size ends at the chunk's last row, so rows past a
@@ -330,45 +339,21 @@ __device__ __forceinline__ void scan_copy_waves(const ScanArgs<bf16_t> &a, int l
   uint32_t kq_voff[16];
 #pragma unroll
   for (int i = 0; i < 16; ++i) kq_voff[i] = uint32_t(rowtile_copy_src(i, lane, 64, qk_stride));
-  uint32_t v_voff[2];
-#pragma unroll
-  for (int i = 0; i < 2; ++i) v_voff[i] = uint32_t(vblock_copy_src(2 * CW + i, lane, 64, v_stride));
 
-  // A stage's copies in three groups: the k (or q) tile copies 0-7 and
-  // 8-15, then T, gates and v.
+  // A stage's k (or q) tile copies in two halves: copies 0-7 and 8-15.
   auto stage_part = [&](int part, int cc, char *base_mem) {
     const int tok0 = start + cc * C;
     const int len = min(C, end - tok0);
-    lds_t *const base = lds_ptr(base_mem);
-    if (part < 2) {
-      const i32x4_t kq_res = buffer_rsrc(kq_src + int64_t(tok0) * kq_row_bytes, rowtile_valid_bytes(len, kq_row_bytes));
-      lds_t *const tile = base + (CW == 0 ? kStK : kStQ);
+    const i32x4_t kq_res = buffer_rsrc(kq_src + int64_t(tok0) * kq_row_bytes, rowtile_valid_bytes(len, kq_row_bytes));
+    lds_t *const tile = lds_ptr(base_mem) + (CW == 0 ? kStK : kStQ);
 #pragma unroll
-      for (int i = 8 * part; i < 8 * part + 8; ++i) dma16_buf(kq_res, kq_voff[i], tile + 1024 * i);
-      return;
-    }
-    const char *entry = a.entries + (int64_t(c_first + cc) * a.H_v + h) * ebytes;
-#pragma unroll
-    for (int i = 0; i < 3; ++i) {
-      const int f = CW == 0 ? 2 * i : 5 + i;  // T fragments 0, 2, 4 / 5, 6, 7
-      dma16(entry + 1024 * f, 16 * lane, base + kStT + 1024 * f);
-    }
-    if (CW == 0) dma16(entry + 16384, 16 * lane, base + kStG);
-    const i32x4_t v_res = buffer_rsrc(v_src + int64_t(tok0) * v_row_bytes, vblock_valid_bytes(len, v_row_bytes));
-#pragma unroll
-    for (int i = 0; i < 2; ++i) dma16_buf(v_res, v_voff[i], base + kStV + 2048 * CW + 1024 * i);
+    for (int i = 8 * part; i < 8 * part + 8; ++i) dma16_buf(kq_res, kq_voff[i], tile + 1024 * i);
   };
   auto stage = [&](int cc, char *base_mem) {
     stage_part(0, cc, base_mem);
     stage_part(1, cc, base_mem);
-    stage_part(2, cc, base_mem);
   };
-  auto wait_all_but_newest_stage = [&]() {
-    if (CW == 0)
-      wait_vmem_upto<kStageLoadsW2>();
-    else
-      wait_vmem_upto<kStageLoadsW3>();
-  };
+  auto wait_all_but_newest_stage = [&]() { wait_vmem_upto<kStageLoadsCopy>(); };
   int kq_off[4][2];
 #pragma unroll
   for (int kk = 0; kk < 4; ++kk)
@@ -377,19 +362,27 @@ __device__ __forceinline__ void scan_copy_waves(const ScanArgs<bf16_t> &a, int l
 
   // Outputs of chunk oc from exchange buffer `ex_mem` and the operands kept
   // from its phase: transposed tiles, lane = token row 16 rt + lane mod 16,
-  // columns 16 cg + 4 (lane / 16) .. + 3 of the block, one 8-byte store each.
-  // The four tiles' products are independent and issue interleaved; the
-  // stores go through a buffer resource that ends at the chunk's last row, so
-  // rows past a partial chunk are dropped without a branch.
+  // columns 16 cg + 4 (lane / 16) .. + 3 of the block.  The four tiles'
+  // products are independent and issue interleaved.  The tiles pass through
+  // the output staging buffer so that each store writes whole 64-byte rows
+  // (16 bytes per lane); the stores go through a buffer resource that ends at
+  // the chunk's last row, so rows past a partial chunk are dropped without a
+  // branch.
   OutOperands op;
   const uint32_t o_row_bytes = uint32_t(2 * v_stride);
   const char *const o_base = reinterpret_cast<const char *>(a.o + int64_t(h) * a.d_v + 32 * cb);
-  uint32_t o_voff[2][2];
+  // this lane's output pieces: written as the MFMA leaves them (row block b,
+  // column group cg), read back as 16-byte row pieces (row block b)
+  int os_w[2][2], os_r[2];
+  uint32_t o_voff[2];
 #pragma unroll
-  for (int b = 0; b < 2; ++b)
+  for (int b = 0; b < 2; ++b) {
+    const int rt = own_rt<CW>(b);
 #pragma unroll
-    for (int cg = 0; cg < 2; ++cg)
-      o_voff[b][cg] = uint32_t(out_acc_row(own_rt<CW>(b), lane)) * o_row_bytes + 2 * out_acc_col(cg, lane);
+    for (int cg = 0; cg < 2; ++cg) os_w[b][cg] = out_stage_byte(out_acc_row(rt, lane), out_acc_col(cg, lane));
+    os_r[b] = out_stage_byte(out_piece_row(rt, lane), out_piece_col(lane));
+    o_voff[b] = uint32_t(out_piece_row(rt, lane)) * o_row_bytes + 2 * out_piece_col(lane);
+  }
   auto outputs = [&](int oc, const char *ex_mem) {
     const lds_t *ex = lds_ptr(const_cast<char *>(ex_mem));
     Frag<bf16_t> sx[2][4], ux[2][2];
@@ -418,19 +411,21 @@ __device__ __forceinline__ void scan_copy_waves(const ScanArgs<bf16_t> &a, int l
 #pragma unroll
         for (int cg = 0; cg < 2; ++cg)
           if (kk < (own_rt<CW>(b) < 2 ? 1 : 2)) acc[b][cg] = mfma(ux[cg][kk], op.p[b][kk], acc[b][cg]);
+    lds_t *const os = lds_ptr(scan_ostage);
+#pragma unroll
+    for (int b = 0; b < 2; ++b)
+#pragma unroll
+      for (int cg = 0; cg < 2; ++cg) lds_store<bf16x4_t>(os + os_w[b][cg], __builtin_convertvector(acc[b][cg], bf16x4_t));
     const int tok0 = start + oc * C;
     const int len = min(C, end - tok0);
     const __amdgpu_buffer_rsrc_t o_res = __builtin_amdgcn_make_buffer_rsrc(
         const_cast<char *>(o_base + int64_t(tok0) * o_row_bytes), 0, int((len - 1) * o_row_bytes + 64), 0x00020000);
 #pragma unroll
     for (int b = 0; b < 2; ++b)
-#pragma unroll
-      for (int cg = 0; cg < 2; ++cg)
-        __builtin_amdgcn_raw_buffer_store_b64(
-            __builtin_bit_cast(u32x2_t, __builtin_convertvector(acc[b][cg], bf16x4_t)), o_res, o_voff[b][cg], 0, 0);
+      __builtin_amdgcn_raw_buffer_store_b128(lds_load<u32x4_t>(os + os_r[b]), o_res, o_voff[b], 0, 0);
   };
 
-  if (n_chunks > 0) {
+  if (kCopies && n_chunks > 0) {
     stage(0, scan_stage0);
     stage(min(1, n_chunks - 1), scan_stage1);
     wait_all_but_newest_stage();
@@ -445,11 +440,15 @@ __device__ __forceinline__ void scan_copy_waves(const ScanArgs<bf16_t> &a, int l
   // stage must be complete.
   auto phase = [&](int cc, char *dst, const char *cur, const char *ex_prev) {
     const int pf = min(cc + 2, n_chunks - 1);
-    stage_part(0, pf, dst);
-    if (cc > 0) outputs(cc - 1, ex_prev);
-    stage_part(1, pf, dst);
-    scan_form_p<CW>(lds_ptr(const_cast<char *>(cur)), kq_off, lane, op, [&]() { stage_part(2, pf, dst); });
-    wait_all_but_newest_stage();
+    if (kCopies) stage_part(0, pf, dst);
+    if (kOutputs && cc > 0) outputs(cc - 1, ex_prev);
+    if (kOutputs)
+      scan_form_p<CW>(lds_ptr(const_cast<char *>(cur)), kq_off, lane, op, [&]() {
+        if (kCopies) stage_part(1, pf, dst);
+      });
+    else
+      stage_part(1, pf, dst);
+    if (kCopies) wait_all_but_newest_stage();
     lds_barrier();
   };
   for (int cc = 0; cc < n_chunks; cc += 6) {
@@ -461,11 +460,16 @@ __device__ __forceinline__ void scan_copy_waves(const ScanArgs<bf16_t> &a, int l
     if (cc + 5 < n_chunks) phase(cc + 5, scan_stage1, scan_stage2, scan_ex0);
   }
   // the last chunk's exchange was written before the last barrier
-  if (n_chunks > 0) outputs(n_chunks - 1, (n_chunks - 1) % 2 == 0 ? scan_ex0 : scan_ex1);
+  if (kOutputs && n_chunks > 0) outputs(n_chunks - 1, (n_chunks - 1) % 2 == 0 ? scan_ex0 : scan_ex1);
   wait_vmem();  // the trailing copies and stores
 }
 
-__global__ __launch_bounds__(256) void scan_kernel_staged(ScanArgs<bf16_t> a) {
+// NW = 4: waves 2 and 3 copy the k / q tiles and form P and the outputs.
+// NW = 6: waves 2 and 3 form P and the outputs, waves 4 and 5 (which share
+// SIMDs with the chain waves but issue only scalar and memory instructions)
+// copy the tiles, so no wave that computes ever waits to issue a copy.
+template <int NW>
+__global__ __launch_bounds__(64 * NW) void scan_kernel_staged(ScanArgs<bf16_t> a) {
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int r0 = lane & 15, g = lane >> 4;
@@ -480,13 +484,32 @@ __global__ __launch_bounds__(256) void scan_kernel_staged(ScanArgs<bf16_t> a) {
   const int c_first = a.geo.first_chunk(s);
   const int n_chunks = max(0, min((end - start + C - 1) / C, a.geo.n_slots - c_first));
 
-  if (wave == 2) {
-    scan_copy_waves<0>(a, lane, h, hq, cb, start, end, c_first, n_chunks);
-    return;
-  }
-  if (wave == 3) {
-    scan_copy_waves<1>(a, lane, h, hq, cb, start, end, c_first, n_chunks);
-    return;
+  if (NW == 4) {
+    if (wave == 2) {
+      scan_copy_waves<0, 0>(a, lane, h, hq, cb, start, end, n_chunks);
+      return;
+    }
+    if (wave == 3) {
+      scan_copy_waves<1, 0>(a, lane, h, hq, cb, start, end, n_chunks);
+      return;
+    }
+  } else {
+    if (wave == 2) {
+      scan_copy_waves<0, 1>(a, lane, h, hq, cb, start, end, n_chunks);
+      return;
+    }
+    if (wave == 3) {
+      scan_copy_waves<1, 1>(a, lane, h, hq, cb, start, end, n_chunks);
+      return;
+    }
+    if (wave == 4) {
+      scan_copy_waves<0, 2>(a, lane, h, hq, cb, start, end, n_chunks);
+      return;
+    }
+    if (wave == 5) {
+      scan_copy_waves<1, 2>(a, lane, h, hq, cb, start, end, n_chunks);
+      return;
+    }
   }
 
   // ---- chain waves: wave w owns columns 32 cb + 16 w .. + 15 ----
@@ -509,6 +532,38 @@ __global__ __launch_bounds__(256) void scan_kernel_staged(ScanArgs<bf16_t> a) {
   const int v_off = vtile_byte(4 * g + (r0 >> 2), 16 * wave + 4 * (r0 & 3));
   const int col = 32 * cb + 16 * wave + r0;  // this lane's state column
   const int ex_off = kExWave * wave + 16 * lane;
+
+  // This wave's copies of a stage: T fragments (0, 2, 4 / 5, 6, 7), the gate
+  // block (wave 0), and v rows 32 w .. 32 w + 31 of the block (two copies,
+  // through a buffer resource that ends at the chunk's last row).
+  const int64_t ebytes = entry_bytes<bf16_t>();
+  const char *const v_src = reinterpret_cast<const char *>(a.v) + (int64_t(h) * a.d_v + 32 * cb) * 2;
+  const int64_t v_stride = int64_t(a.H_v) * a.d_v;
+  const uint32_t v_row_bytes = uint32_t(2 * v_stride);
+  uint32_t v_voff[2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) v_voff[i] = uint32_t(vblock_copy_src(2 * wave + i, lane, 64, v_stride));
+  auto chain_stage = [&](int cc, char *base_mem) {
+    const int tok0 = start + cc * C;
+    const int len = min(C, end - tok0);
+    lds_t *const base = lds_ptr(base_mem);
+    const char *entry = a.entries + (int64_t(c_first + cc) * a.H_v + h) * ebytes;
+#pragma unroll
+    for (int i = 0; i < 3; ++i) {
+      const int f = wave == 0 ? 2 * i : 5 + i;
+      dma16(entry + 1024 * f, 16 * lane, base + kStT + 1024 * t_slot(f));
+    }
+    if (wave == 0) dma16(entry + 16384, 16 * lane, base + kStG);
+    const i32x4_t v_res = buffer_rsrc(v_src + int64_t(tok0) * v_row_bytes, vblock_valid_bytes(len, v_row_bytes));
+#pragma unroll
+    for (int i = 0; i < 2; ++i) dma16_buf(v_res, v_voff[i], base + kStV + 2048 * wave + 1024 * i);
+  };
+  auto chain_wait_all_but_newest_stage = [&]() {
+    if (wave == 0)
+      wait_vmem_upto<kStageLoadsChain0>();
+    else
+      wait_vmem_upto<kStageLoadsChain1>();
+  };
 
   // ---- state ----
   f32x4_t S[8];
@@ -551,9 +606,14 @@ __global__ __launch_bounds__(256) void scan_kernel_staged(ScanArgs<bf16_t> a) {
     for (int rt = 0; rt < 4; ++rt) vt[rt] = lds_read_tr16(st + kStV + 1024 * rt + v_off);
 #pragma unroll
     for (int i = 0; i < 8; ++i)
-      if (i != 1 && i != 3) tf[i].v = lds_load<bf16x8_t>(st + kStT + 1024 * i + 16 * lane);
+      if (i != 1 && i != 3) tf[i].v = lds_load<bf16x8_t>(st + kStT + 1024 * t_slot(i) + 16 * lane);
   };
 
+  if (n_chunks > 0) {
+    chain_stage(0, scan_stage0);
+    chain_stage(min(1, n_chunks - 1), scan_stage1);
+    chain_wait_all_but_newest_stage();
+  }
   lds_barrier();  // the first two stages are complete
   if (n_chunks > 0) read_operands(scan_stage0);
 
@@ -562,7 +622,7 @@ __global__ __launch_bounds__(256) void scan_kernel_staged(ScanArgs<bf16_t> a) {
   // exchange buffer `ex_mem`, K^T read from the stage during the chain.  The
   // barrier follows the state update (after it the copy waves may reuse this
   // chunk's stage); then the next chunk's operands are read.
-  auto chunk_step = [&](int cc, char *cur_mem, char *next_mem, char *ex_mem) {
+  auto chunk_step = [&](int cc, char *cur_mem, char *next_mem, char *prev_mem, char *ex_mem) {
     const lds_t *const st = lds_ptr(cur_mem);
     lds_t *const ex = lds_ptr(ex_mem) + ex_off;
 
@@ -578,6 +638,9 @@ __global__ __launch_bounds__(256) void scan_kernel_staged(ScanArgs<bf16_t> a) {
       for (int rt = 0; rt < 4; ++rt) Y[rt] = mfma(kf[kk][rt], Sf[kk], kk == 0 ? zero4() : Y[rt]);
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk) lds_store<bf16x8_t>(ex + kExS + 1024 * kk, Sf[kk].v);
+    // chunk cc + 2 into the previous chunk's stage (free since the barrier
+    // that opened this chunk; past the end the last chunk is copied again)
+    chain_stage(min(cc + 2, n_chunks - 1), prev_mem);
 
     // K^T fragments for the state update (transposed reads of the k tile),
     // issued early so that they have landed when the update starts
@@ -627,17 +690,19 @@ __global__ __launch_bounds__(256) void scan_kernel_staged(ScanArgs<bf16_t> a) {
     // this chunk's stage reads are done (the copy waves may now refill the
     // previous chunk's stage), the exchange is written, and the next chunk's
     // stage is complete
+    chain_wait_all_but_newest_stage();
     lds_barrier();
     if (cc + 1 < n_chunks) read_operands(next_mem);
   };
   for (int cc = 0; cc < n_chunks; cc += 6) {
-    chunk_step(cc, scan_stage0, scan_stage1, scan_ex0);
-    if (cc + 1 < n_chunks) chunk_step(cc + 1, scan_stage1, scan_stage2, scan_ex1);
-    if (cc + 2 < n_chunks) chunk_step(cc + 2, scan_stage2, scan_stage0, scan_ex0);
-    if (cc + 3 < n_chunks) chunk_step(cc + 3, scan_stage0, scan_stage1, scan_ex1);
-    if (cc + 4 < n_chunks) chunk_step(cc + 4, scan_stage1, scan_stage2, scan_ex0);
-    if (cc + 5 < n_chunks) chunk_step(cc + 5, scan_stage2, scan_stage0, scan_ex1);
+    chunk_step(cc, scan_stage0, scan_stage1, scan_stage2, scan_ex0);
+    if (cc + 1 < n_chunks) chunk_step(cc + 1, scan_stage1, scan_stage2, scan_stage0, scan_ex1);
+    if (cc + 2 < n_chunks) chunk_step(cc + 2, scan_stage2, scan_stage0, scan_stage1, scan_ex0);
+    if (cc + 3 < n_chunks) chunk_step(cc + 3, scan_stage0, scan_stage1, scan_stage2, scan_ex1);
+    if (cc + 4 < n_chunks) chunk_step(cc + 4, scan_stage1, scan_stage2, scan_stage0, scan_ex0);
+    if (cc + 5 < n_chunks) chunk_step(cc + 5, scan_stage2, scan_stage0, scan_stage1, scan_ex1);
   }
+  wait_vmem();  // the trailing copies
 
   if (a.hT) {
 #pragma unroll
@@ -645,6 +710,10 @@ __global__ __launch_bounds__(256) void scan_kernel_staged(ScanArgs<bf16_t> a) {
       for (int e = 0; e < 4; ++e) a.hT[st_base + int64_t(16 * rt + 4 * g + e) * a.d_v + col] = S[rt][e];
   }
 }
+
+#ifndef SCAN_WAVES
+#define SCAN_WAVES 6
+#endif
 
 template <typename T>
 static ScanArgs<T> scan_args(const Problem &p, const Workspace &ws, int colblk_width) {
@@ -673,7 +742,8 @@ hipError_t launch_scan(const Problem &p, const Workspace &ws, hipStream_t st) {
   const int64_t blocks = (int64_t(p.n_seqs) * p.H_v + 7) / 8 * 8 * (p.d_v / width);
   if (blocks == 0) return hipSuccess;
   if (staged) {
-    hipLaunchKernelGGL(scan_kernel_staged, dim3(unsigned(blocks)), dim3(256), 0, st, scan_args<bf16_t>(p, ws, width));
+    hipLaunchKernelGGL(scan_kernel_staged<SCAN_WAVES>, dim3(unsigned(blocks)), dim3(64 * SCAN_WAVES), 0, st,
+                       scan_args<bf16_t>(p, ws, width));
   } else if (p.dtype == 1) {
     hipLaunchKernelGGL(scan_kernel<bf16_t>, dim3(unsigned(blocks)), dim3(64), 0, st,
                        scan_args<bf16_t>(p, ws, width));

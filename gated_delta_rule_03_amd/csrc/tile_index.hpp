@@ -83,6 +83,23 @@ __host__ __device__ constexpr int vtile_byte(int row, int col) {
 __host__ __device__ constexpr int out_acc_row(int rt, int lane) { return 16 * rt + (lane & 15); }
 __host__ __device__ constexpr int out_acc_col(int cg, int lane) { return 16 * cg + 4 * (lane >> 4); }
 
+// ---- T fragments in a stage ----
+// LDS slot of T fragment f: fragments 1 and 3 (rows 0-31 x columns 32-63 of
+// the lower-triangular T) are zero and not staged; the other six fill slots
+// 0-5.
+__host__ __device__ constexpr int t_slot(int f) { return f < 4 ? f / 2 : f - 2; }
+
+// ---- outputs leaving through the output staging buffer ----
+// 64 token rows x 32 bf16 (64 bytes per row), 16-byte pieces XOR-swizzled by
+// the row: physical piece = piece ^ ((row / 4) mod 4).
+__host__ __device__ constexpr int out_stage_byte(int row, int col) {
+  return row * 64 + 16 * (((col >> 3) ^ (row >> 2)) & 3) + 2 * (col & 7);
+}
+// Read-back piece of lane l in row block rt: row 16 rt + l / 4, columns
+// 8 (l mod 4) .. + 7 (one 16-byte piece; 16 rows x 64 bytes per instruction).
+__host__ __device__ constexpr int out_piece_row(int rt, int lane) { return 16 * rt + (lane >> 2); }
+__host__ __device__ constexpr int out_piece_col(int lane) { return 8 * (lane & 3); }
+
 // Token row blocks (of P and of the outputs) that copy wave cw = 0, 1 owns:
 // {0, 3} and {1, 2}.  Row block rt of the lower-triangular P has rt + 1
 // tiles of 16 x 16, so each copy wave forms five.

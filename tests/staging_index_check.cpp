@@ -139,6 +139,58 @@ int main() {
     CHECK(p_tiles[0] == 5 && p_tiles[1] == 5, "P tiles per copy wave %d / %d", p_tiles[0], p_tiles[1]);
   }
 
+  // ---- T fragments: the six non-zero ones fill six distinct slots ----
+  {
+    std::vector<int> seen(6, 0);
+    for (int f = 0; f < 8; ++f) {
+      if (f == 1 || f == 3) continue;
+      const int sl = t_slot(f);
+      CHECK(sl >= 0 && sl < 6, "T fragment %d slot %d", f, sl);
+      if (sl >= 0 && sl < 6) seen[sl]++;
+    }
+    for (int sl = 0; sl < 6; ++sl) CHECK(seen[sl] == 1, "T slot %d used %d times", sl, seen[sl]);
+  }
+
+  // ---- output staging: each copy wave writes its two row blocks as 8-byte
+  // tile pieces and reads them back as 16-byte row pieces; every element is
+  // written once and read back once, each wave reads only what it wrote, and
+  // the staging buffer's 4 KiB hold the whole block ----
+  {
+    std::vector<int> wrote(64 * 32, -1), read(64 * 32, 0), at(64 * 32, -1);
+    for (int cw = 0; cw < 2; ++cw)
+      for (int a = 0; a < 2; ++a) {
+        const int rt = copy_rows(cw, a);
+        for (int cg = 0; cg < 2; ++cg)
+          for (int l = 0; l < 64; ++l) {
+            const int row = out_acc_row(rt, l), col = out_acc_col(cg, l);
+            const int base = out_stage_byte(row, col);
+            CHECK(base % 8 == 0 && base + 8 <= 4096, "staging write (%d,%d) at %d", row, col, base);
+            for (int c = 0; c < 4; ++c) {
+              CHECK(out_stage_byte(row, col + c) == base + 2 * c, "staging write (%d,%d) not contiguous", row, col + c);
+              CHECK(wrote[row * 32 + col + c] == -1, "output (%d,%d) staged twice", row, col + c);
+              wrote[row * 32 + col + c] = cw;
+              at[row * 32 + col + c] = out_stage_byte(row, col + c);
+            }
+          }
+        for (int l = 0; l < 64; ++l) {
+          const int row = out_piece_row(rt, l), col = out_piece_col(l);
+          const int base = out_stage_byte(row, col);
+          CHECK(base % 16 == 0 && base + 16 <= 4096, "staging read (%d,%d) at %d", row, col, base);
+          CHECK(row / 16 == rt, "read-back row %d outside row block %d", row, rt);
+          for (int c = 0; c < 8; ++c) {
+            CHECK(out_stage_byte(row, col + c) == base + 2 * c, "staging read (%d,%d) not contiguous", row, col + c);
+            read[row * 32 + col + c]++;
+          }
+        }
+      }
+    std::vector<int> bytes(4096, 0);
+    for (int x = 0; x < 64 * 32; ++x) {
+      CHECK(wrote[x] >= 0 && read[x] == 1, "output element %d staged %d / read %d times", x, wrote[x] >= 0, read[x]);
+      if (at[x] >= 0) bytes[at[x]]++;
+    }
+    for (int b = 0; b < 4096; b += 2) CHECK(bytes[b] == 1, "staging byte %d holds %d elements", b, bytes[b]);
+  }
+
   if (fails) {
     std::printf("%d violations\n", fails);
     return 1;
