@@ -93,6 +93,29 @@ def test_small_uniform(gdn, case, path):
     check(gdn, path, w, h0=h0, chunk=chunk)
 
 
+# bf16 with d_k = 128 and d_v a multiple of 32 runs the staged kernels: value
+# widths of one and two 32-column blocks, unit counts that are not a
+# multiple of the eight-unit block groups, a single partial chunk, one token,
+# and the small chunk sizes.
+STAGED = [
+    # B, T, H_qk, H_v, d_v, chunk
+    (3, 150, 3, 3, 32, 64),
+    (1, 333, 1, 3, 64, 64),
+    (3, 50, 1, 1, 128, 64),
+    (2, 1, 2, 2, 128, 64),
+    (1, 200, 1, 2, 64, 16),
+    (1, 97, 2, 2, 128, 32),
+]
+
+
+@pytest.mark.parametrize("case", STAGED, ids=[f"B{c[0]}T{c[1]}H{c[2]}_{c[3]}dv{c[4]}C{c[5]}" for c in STAGED])
+def test_staged_shapes(gdn, case):
+    B, T, H_qk, H_v, d_v, chunk = case
+    w = small("bf16", B, T, H_qk, H_v, 128, d_v, chunk, seed=200 + STAGED.index(case))
+    check(gdn, "chunk", w, chunk=chunk)
+    check(gdn, "chunk", w, h0=gi.random_state((B, H_v, 128, d_v), seed=11, scale=0.3), chunk=chunk)
+
+
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
 @pytest.mark.parametrize("path,chunk", [("chunk", 64), ("chunk", 32), ("recurrent", None)])
 def test_small_packed_grouped_heads(gdn, dtype, path, chunk):
