@@ -248,6 +248,11 @@ __shared__ __attribute__((aligned(16))) char scan_ex1[kExBytes];
 // in tile_index.hpp): each copy wave writes and reads back only its own rows,
 // so that every store covers whole 64-byte rows of the block.
 __shared__ __attribute__((aligned(16))) char scan_ostage[4096];
+// s_sleep units (64 cycles each) the tile copy waves wait after a barrier, so
+// that the output waves' stores enter the memory pipeline ahead of the copies.
+#ifndef SCAN_COPY_DELAY
+#define SCAN_COPY_DELAY 2
+#endif
 
 // Token row blocks of P and of the outputs that copy wave CW owns:
 // copy_rows(CW, 0..1) (tile_index.hpp), five 16 x 16 tiles of P each.
@@ -383,6 +388,8 @@ __device__ __forceinline__ void scan_copy_waves(const ScanArgs<bf16_t> &a, int l
     os_r[b] = out_stage_byte(out_piece_row(rt, lane), out_piece_col(lane));
     o_voff[b] = uint32_t(out_piece_row(rt, lane)) * o_row_bytes + 2 * out_piece_col(lane);
   }
+  u32x4_t o_pend[2];
+  int o_pend_chunk = -1;
   auto outputs = [&](int oc, const char *ex_mem) {
     const lds_t *ex = lds_ptr(const_cast<char *>(ex_mem));
     Frag<bf16_t> sx[2][4], ux[2][2];
@@ -416,13 +423,22 @@ __device__ __forceinline__ void scan_copy_waves(const ScanArgs<bf16_t> &a, int l
     for (int b = 0; b < 2; ++b)
 #pragma unroll
       for (int cg = 0; cg < 2; ++cg) lds_store<bf16x4_t>(os + os_w[b][cg], __builtin_convertvector(acc[b][cg], bf16x4_t));
-    const int tok0 = start + oc * C;
+#pragma unroll
+    for (int b = 0; b < 2; ++b) o_pend[b] = lds_load<u32x4_t>(os + os_r[b]);
+    o_pend_chunk = oc;
+  };
+  // The stores of the outputs computed in the previous phase, issued first
+  // thing in a phase, before the copy waves' burst of copies fills the
+  // memory pipeline (stores issued behind it wait for it to drain).
+  auto store_pending = [&]() {
+    if (o_pend_chunk < 0) return;
+    const int tok0 = start + o_pend_chunk * C;
     const int len = min(C, end - tok0);
     const __amdgpu_buffer_rsrc_t o_res = __builtin_amdgcn_make_buffer_rsrc(
         const_cast<char *>(o_base + int64_t(tok0) * o_row_bytes), 0, int((len - 1) * o_row_bytes + 64), 0x00020000);
 #pragma unroll
-    for (int b = 0; b < 2; ++b)
-      __builtin_amdgcn_raw_buffer_store_b128(lds_load<u32x4_t>(os + os_r[b]), o_res, o_voff[b], 0, 0);
+    for (int b = 0; b < 2; ++b) __builtin_amdgcn_raw_buffer_store_b128(o_pend[b], o_res, o_voff[b], 0, 0);
+    o_pend_chunk = -1;
   };
 
   if (kCopies && n_chunks > 0) {
@@ -440,6 +456,8 @@ __device__ __forceinline__ void scan_copy_waves(const ScanArgs<bf16_t> &a, int l
   // stage must be complete.
   auto phase = [&](int cc, char *dst, const char *cur, const char *ex_prev) {
     const int pf = min(cc + 2, n_chunks - 1);
+    if (kOutputs) store_pending();
+    if (ROLE == 2) __builtin_amdgcn_s_sleep(SCAN_COPY_DELAY);
     if (kCopies) stage_part(0, pf, dst);
     if (kOutputs && cc > 0) outputs(cc - 1, ex_prev);
     if (kOutputs)
@@ -460,7 +478,11 @@ __device__ __forceinline__ void scan_copy_waves(const ScanArgs<bf16_t> &a, int l
     if (cc + 5 < n_chunks) phase(cc + 5, scan_stage1, scan_stage2, scan_ex0);
   }
   // the last chunk's exchange was written before the last barrier
-  if (kOutputs && n_chunks > 0) outputs(n_chunks - 1, (n_chunks - 1) % 2 == 0 ? scan_ex0 : scan_ex1);
+  if (kOutputs && n_chunks > 0) {
+    store_pending();
+    outputs(n_chunks - 1, (n_chunks - 1) % 2 == 0 ? scan_ex0 : scan_ex1);
+    store_pending();
+  }
   wait_vmem();  // the trailing copies and stores
 }
 
