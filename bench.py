@@ -24,6 +24,14 @@ gives the chunked forward's fractions of the HBM and bf16 MFMA peaks.
 ``cpu_baseline`` is the float64 oracle timed on this host's cores over the
 whole prefill batch.
 
+``long_context`` and ``varlen`` report the chunked forward's throughput on the
+long-context workload (B=1, H=16, T=65536, log alpha / 64) and the packed
+variable-length workload (32 sequences, the generator's lengths, 16 query/key
+heads serving 32 value heads), timed the same way.  Their inputs are drawn on
+the device from a seed with the generator's shapes and distributions (the
+kernels' time does not depend on the values; the parity tests run these
+workloads on the generator's exact inputs).
+
 ``roofline.traffic`` is the decode kernel's HBM bytes per launch from the
 rocprofv3 FETCH_SIZE and WRITE_SIZE counters (profiles/decode_kernel.traffic.json),
 each scaled by what the counter reads for a plain 1 GiB read + 1 GiB write
@@ -35,6 +43,7 @@ from __future__ import annotations
 
 import argparse
 import hashlib
+import itertools
 import json
 import os
 import statistics
@@ -102,6 +111,77 @@ def cpu_baseline(w):
                       f"{tokens * w.spec.H_v} token-units) in {dt:.2f} s, float64"}
 
 
+def device_inputs(torch, dev, spec, n_tokens, B, seed):
+    """Inputs with ``spec``'s shapes and distributions, drawn on the device.
+
+    q, k ~ N(0, 1) scaled to unit length per token and head (q then by
+    1/sqrt(d_k)), v ~ N(0, 1), rounded to bf16; log alpha = -softplus(N(0, 1))
+    * A_h * s with A_h = exp(U(-4, 0)) per value head, beta = sigmoid(N(0, 1)).
+    """
+    g = torch.Generator(device=dev)
+    g.manual_seed(seed)
+    T = n_tokens // B
+    q = torch.randn((B, T, spec.H_qk, spec.d_k), generator=g, device=dev)
+    q = (torch.nn.functional.normalize(q, dim=-1) / spec.d_k ** 0.5).bfloat16()
+    k = torch.nn.functional.normalize(torch.randn((B, T, spec.H_qk, spec.d_k), generator=g, device=dev),
+                                      dim=-1).bfloat16()
+    v = torch.randn((B, T, spec.H_v, spec.d_v), generator=g, device=dev).bfloat16()
+    A_h = torch.exp(torch.rand((spec.H_v,), generator=g, device=dev) * 4.0 - 4.0)
+    z_a = torch.randn((B, T, spec.H_v), generator=g, device=dev)
+    alpha = torch.exp(-torch.nn.functional.softplus(z_a) * A_h * spec.log_alpha_scale)
+    beta = torch.sigmoid(torch.randn((B, T, spec.H_v), generator=g, device=dev))
+    return q, k, v, alpha.float().contiguous(), beta.float().contiguous()
+
+
+def extra_workloads(args, gi, gdn, torch, dev, stream, evict):
+    """Chunked-forward throughput on the long-context and variable-length workloads."""
+    out = {}
+    for key, idx in (("long_context", 4), ("varlen", 5)):
+        spec = gi.config(idx)
+        if spec.packed_seqs:
+            lengths = gi.packed_lengths(spec)
+            n_tokens, B = int(sum(lengths)), 1
+            cu = torch.tensor([0] + list(itertools.accumulate(lengths)), dtype=torch.int32, device=dev)
+            n_seqs = len(lengths)
+        else:
+            n_tokens, B, cu, n_seqs = spec.B * spec.T, spec.B, None, spec.B
+        log(f"bench: {spec.name} workload, {n_tokens} tokens")
+        q, k, v, alpha, beta = device_inputs(torch, dev, spec, n_tokens, B, seed=spec.seed)
+        o = torch.empty_like(v)
+        hT = torch.empty((n_seqs, spec.H_v, spec.d_k, spec.d_v), dtype=torch.float32, device=dev)
+        need = gdn.chunk_fwd_workspace_bytes(B, n_tokens // B, spec.H_qk, spec.H_v, spec.d_k, spec.d_v,
+                                             gdn.GDN_BF16, spec.chunk, n_seqs if cu is not None else 0)
+        ws = torch.empty(need, dtype=torch.uint8, device=dev)
+
+        def call():
+            gdn.chunk_fwd(q, k, v, alpha, beta, chunk=spec.chunk, cu_seqlens=cu, o=o, hT=hT, workspace=ws,
+                          stream=stream)
+
+        ms = []
+        for i in range(2 + max(3, args.steps // 4)):
+            evict(4)
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            call()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            if i >= 2:
+                ms.append(e0.elapsed_time(e1))
+        t = statistics.median(ms) * 1e-3
+        units = n_seqs * spec.H_v
+        flops = n_tokens * spec.H_v * PREFILL_FLOPS_PER_TOKEN_UNIT
+        byts = n_tokens * (2 * spec.H_qk * spec.d_k * 2 + 2 * spec.H_v * spec.d_v * 2 + 8 * spec.H_v) + \
+            units * spec.d_k * spec.d_v * 4
+        out[key] = {"workload": f"{spec.name}: B={B} tokens={n_tokens} sequences={n_seqs} H_qk={spec.H_qk} "
+                                f"H_v={spec.H_v} d={spec.d_k} bf16 chunk {spec.chunk}",
+                    "tokens_per_s": n_tokens / t, "us_per_call": t * 1e6,
+                    "hbm_frac": byts / t / HBM_PEAK, "mfma_frac": flops / t / MFMA_BF16_PEAK,
+                    "inputs": "drawn on the device with the generator's shapes and distributions"}
+        del q, k, v, alpha, beta, o, hT, ws
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -110,6 +190,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--flush", choices=("read", "write", "none"), default="read",
                     help="what runs before each call to evict the last-level cache")
+    ap.add_argument("--no-extra", action="store_true",
+                    help="skip the long-context and variable-length throughput lines")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run a plain 1 GiB read + 1 GiB write kernel (counter calibration)")
     args = ap.parse_args()
@@ -221,6 +303,10 @@ def main():
         copy_gbps = 2 * c_src.numel() * 4 / (statistics.median(cms) * 1e-3) / 1e9
         del c_src, c_dst
 
+    extra = {}
+    if not args.no_extra:
+        extra = extra_workloads(args, gi, gdn, torch, dev, stream, evict)
+
     tokens = B * T
     units = B * H
     prefill_bytes = tokens * H * PREFILL_BYTES_PER_TOKEN_UNIT + units * D * D * 4
@@ -279,6 +365,7 @@ def main():
         },
         "wall_s_timed_region": wall,
     }
+    result.update(extra)
     if copy_gbps is not None:
         result["calibration_copy_GBps"] = copy_gbps
     if not args.no_cpu_baseline:

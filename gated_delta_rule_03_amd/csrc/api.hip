@@ -21,6 +21,7 @@ SeqGeom make_geom(const Problem &p, const Workspace *ws) {
   SeqGeom g;
   g.cu_seqlens = p.cu_seqlens;
   g.chunk_off = ws ? ws->chunk_off : nullptr;
+  g.seq_order = ws && p.cu_seqlens ? ws->seq_order : nullptr;
   g.n_seqs = p.n_seqs;
   g.T = p.T;
   g.chunk = p.chunk > 0 ? p.chunk : 64;
@@ -31,11 +32,12 @@ SeqGeom make_geom(const Problem &p, const Workspace *ws) {
 
 size_t workspace_layout(const Problem &p, void *base, Workspace *ws) {
   const int64_t entry = p.dtype == GDN_BF16 ? entry_bytes<uint16_t>() : entry_bytes<float>();
-  const size_t off_bytes = align256(size_t(p.n_seqs + 1) * sizeof(int32_t));
+  const size_t off_bytes = align256(size_t(2 * int64_t(p.n_seqs) + 1) * sizeof(int32_t));
   const size_t ent_bytes = align256(size_t(chunk_slots(p)) * p.H_v * size_t(entry));
   if (ws) {
     char *b = static_cast<char *>(base);
     ws->chunk_off = reinterpret_cast<int32_t *>(b);
+    ws->seq_order = ws->chunk_off + p.n_seqs + 1;
     ws->entries = b + off_bytes;
   }
   return off_bytes + ent_bytes;

@@ -185,6 +185,7 @@ __device__ __forceinline__ void store_frag(float *p, int lane, const Frag<float>
 struct SeqGeom {
   const int32_t *cu_seqlens;  // device; nullptr for a uniform batch
   const int32_t *chunk_off;   // device, n_seqs + 1 prefix sums of chunk counts (packed only)
+  const int32_t *seq_order;   // device, sequences by chunk count, most first (packed only)
   int32_t n_seqs;
   int32_t T;                  // tokens per sequence (uniform) / total tokens (packed)
   int32_t chunk;
@@ -202,6 +203,9 @@ struct SeqGeom {
       end = start + T;
     }
   }
+  // The i-th sequence in scheduling order: packed batches are walked longest
+  // first, so the longest sequential scans start in the first wave of blocks.
+  __device__ __forceinline__ int ordered(int i) const { return seq_order ? seq_order[i] : i; }
   __device__ __forceinline__ int first_chunk(int s) const {
     return cu_seqlens ? chunk_off[s] : s * chunks_per_seq;
   }

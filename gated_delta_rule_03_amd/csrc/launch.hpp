@@ -46,6 +46,7 @@ inline bool staged_path(const Problem &p) { return p.dtype == 1 && p.d_k == 128 
 
 struct Workspace {
   int32_t *chunk_off;  // [n_seqs + 1] chunk prefix sums (packed batches)
+  int32_t *seq_order;  // [n_seqs] sequences, most chunks first (packed batches)
   void *entries;       // [chunk_slots, H_v] entries
 };
 size_t workspace_layout(const Problem &p, void *base, Workspace *ws);

@@ -48,7 +48,7 @@ __global__ __launch_bounds__(64) void scan_kernel(ScanArgs<T> a) {
   int u, cb;
   decode_block(blockIdx.x, a.n_colblk, u, cb);
   if (u >= a.n_units) return;
-  const int s = u / a.H_v, h = u - s * a.H_v, hq = h / a.group;
+  const int s = a.geo.ordered(u / a.H_v), h = u % a.H_v, hq = h / a.group;
   const int col = 16 * cb + (lane & 15);  // this lane's state column
   const int nkt = a.d_k >> 4;             // 16-row tiles of the state
   const int nkb = (a.d_k + 31) >> 5;      // 32-deep contraction blocks over d_k
@@ -498,7 +498,7 @@ __global__ __launch_bounds__(64 * NW) void scan_kernel_staged(ScanArgs<bf16_t> a
   int u, cb;
   decode_block(blockIdx.x, a.n_colblk, u, cb);  // n_colblk = d_v / 32
   if (u >= a.n_units) return;  // the whole block
-  const int s = u / a.H_v, h = u - s * a.H_v, hq = h / a.group;
+  const int s = a.geo.ordered(u / a.H_v), h = u % a.H_v, hq = h / a.group;
 
   int start, end;
   a.geo.seq_bounds(s, start, end);

@@ -7,8 +7,17 @@
 
 namespace gdn {
 
-// chunk_off[s] = number of chunks in sequences 0..s-1 (packed batches).
-__global__ __launch_bounds__(256) void chunk_offsets_kernel(SeqGeom geo, int32_t *off) {
+// Sequences ranked for scheduling: order[r] = the sequence with the r-th most
+// chunks (ties by index).  The per-(sequence, head) scans take time in
+// proportion to their chunk counts, so starting the longest first shortens
+// the tail of a packed batch.  Ranked directly up to kMaxRanked sequences;
+// beyond that the order is the identity.
+constexpr int kMaxRanked = 1024;
+
+// chunk_off[s] = number of chunks in sequences 0..s-1, and the scheduling
+// order (packed batches).
+__global__ __launch_bounds__(256) void chunk_offsets_kernel(SeqGeom geo, int32_t *off, int32_t *order) {
+  __shared__ int32_t cnt_sh[kMaxRanked];
   __shared__ int32_t sh[256];
   __shared__ int32_t carry;
   const int tid = threadIdx.x;
@@ -24,6 +33,7 @@ __global__ __launch_bounds__(256) void chunk_offsets_kernel(SeqGeom geo, int32_t
       int start, end;
       geo.seq_bounds(s, start, end);
       cnt = (end - start + geo.chunk - 1) / geo.chunk;
+      if (s < kMaxRanked) cnt_sh[s] = cnt;
     }
     sh[tid] = cnt;
     __syncthreads();
@@ -38,12 +48,25 @@ __global__ __launch_bounds__(256) void chunk_offsets_kernel(SeqGeom geo, int32_t
     if (tid == 255) carry += sh[255];
     __syncthreads();
   }
+  if (geo.n_seqs > kMaxRanked) {
+    for (int s = tid; s < geo.n_seqs; s += 256) order[s] = s;
+    return;
+  }
+  for (int s = tid; s < geo.n_seqs; s += 256) {
+    const int c = cnt_sh[s];
+    int rank = 0;
+    for (int j = 0; j < geo.n_seqs; ++j) {
+      const int cj = cnt_sh[j];
+      rank += (cj > c) || (cj == c && j < s);
+    }
+    order[rank] = s;
+  }
 }
 
 hipError_t launch_chunk_offsets(const Problem &p, const Workspace &ws, hipStream_t st) {
   if (!p.cu_seqlens) return hipSuccess;
   SeqGeom geo = make_geom(p, &ws);
-  hipLaunchKernelGGL(chunk_offsets_kernel, dim3(1), dim3(256), 0, st, geo, ws.chunk_off);
+  hipLaunchKernelGGL(chunk_offsets_kernel, dim3(1), dim3(256), 0, st, geo, ws.chunk_off, ws.seq_order);
   return hipGetLastError();
 }
 
