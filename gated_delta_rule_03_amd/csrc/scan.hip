@@ -323,13 +323,14 @@ __device__ __forceinline__ void scan_form_p(const lds_t *st, const int (&kq_off)
   }
 }
 
-// ROLE 0: copy wave CW issues the k (CW = 0) or q (CW = 1) tile copies and
-// also forms its rows of P and computes their outputs; ROLE 1: P and outputs
-// only; ROLE 2: tile copies only.
-template <int CW, int ROLE>
+// ROLE 1: output wave CW forms its rows of P and computes their outputs for
+// the block's NCH column groups; ROLE 2: copy wave CW issues the k (CW = 0)
+// or q (CW = 1) tile copies.
+template <int CW, int ROLE, int NCH>
 __device__ __forceinline__ void scan_copy_waves(const ScanArgs<bf16_t> &a, int lane, int h, int hq, int cb,
                                                 int start, int end, int n_chunks) {
-  constexpr bool kCopies = ROLE != 1, kOutputs = ROLE != 2;
+  constexpr bool kCopies = ROLE == 2, kOutputs = ROLE == 1;
+  constexpr int W = 16 * NCH;  // columns of the block
   const int r0 = lane & 15, g = lane >> 4;
   const int C = a.geo.chunk;
   const int64_t qk_stride = int64_t(a.H_qk) * 128;
@@ -375,56 +376,65 @@ __device__ __forceinline__ void scan_copy_waves(const ScanArgs<bf16_t> &a, int l
   // branch.
   OutOperands op;
   const uint32_t o_row_bytes = uint32_t(2 * v_stride);
-  const char *const o_base = reinterpret_cast<const char *>(a.o + int64_t(h) * a.d_v + 32 * cb);
+  const char *const o_base = reinterpret_cast<const char *>(a.o + int64_t(h) * a.d_v + W * cb);
   // this lane's output pieces: written as the MFMA leaves them (row block b,
-  // column group cg), read back as 16-byte row pieces (row block b)
-  int os_w[2][2], os_r[2];
-  uint32_t o_voff[2];
+  // column group cg), read back as 16-byte row pieces -- one per row block
+  // for 32-column blocks, one for both row blocks for 16-column blocks
+  constexpr int kPieces = NCH == 2 ? 2 : 1;
+  int os_w[2][NCH], os_r[kPieces];
+  uint32_t o_voff[kPieces];
 #pragma unroll
   for (int b = 0; b < 2; ++b) {
     const int rt = own_rt<CW>(b);
 #pragma unroll
-    for (int cg = 0; cg < 2; ++cg) os_w[b][cg] = out_stage_byte(out_acc_row(rt, lane), out_acc_col(cg, lane));
-    os_r[b] = out_stage_byte(out_piece_row(rt, lane), out_piece_col(lane));
-    o_voff[b] = uint32_t(out_piece_row(rt, lane)) * o_row_bytes + 2 * out_piece_col(lane);
+    for (int cg = 0; cg < NCH; ++cg)
+      os_w[b][cg] = NCH == 2 ? out_stage_byte(out_acc_row(rt, lane), out_acc_col(cg, lane))
+                             : out_stage16_byte(out_acc_row(rt, lane), out_acc_col(cg, lane));
   }
-  u32x4_t o_pend[2];
+#pragma unroll
+  for (int b = 0; b < kPieces; ++b) {
+    const int row = NCH == 2 ? out_piece_row(own_rt<CW>(b), lane) : out_piece16_row(own_rt<CW>(lane >> 5), lane);
+    const int col = NCH == 2 ? out_piece_col(lane) : out_piece16_col(lane);
+    os_r[b] = NCH == 2 ? out_stage_byte(row, col) : out_stage16_byte(row, col);
+    o_voff[b] = uint32_t(row) * o_row_bytes + 2 * col;
+  }
+  u32x4_t o_pend[kPieces];
   int o_pend_chunk = -1;
   auto outputs = [&](int oc, const char *ex_mem) {
     const lds_t *ex = lds_ptr(const_cast<char *>(ex_mem));
-    Frag<bf16_t> sx[2][4], ux[2][2];
+    Frag<bf16_t> sx[NCH][4], ux[NCH][2];
 #pragma unroll
-    for (int cg = 0; cg < 2; ++cg) {
+    for (int cg = 0; cg < NCH; ++cg) {
 #pragma unroll
       for (int kk = 0; kk < 4; ++kk) sx[cg][kk].v = lds_load<bf16x8_t>(ex + kExWave * cg + kExS + 1024 * kk + 16 * lane);
 #pragma unroll
       for (int kk = 0; kk < 2; ++kk) ux[cg][kk].v = lds_load<bf16x8_t>(ex + kExWave * cg + kExU + 1024 * kk + 16 * lane);
     }
-    f32x4_t acc[2][2];
+    f32x4_t acc[2][NCH];
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk)
 #pragma unroll
       for (int b = 0; b < 2; ++b)
 #pragma unroll
-        for (int cg = 0; cg < 2; ++cg) acc[b][cg] = mfma(sx[cg][kk], op.q[b][kk], kk == 0 ? zero4() : acc[b][cg]);
+        for (int cg = 0; cg < NCH; ++cg) acc[b][cg] = mfma(sx[cg][kk], op.q[b][kk], kk == 0 ? zero4() : acc[b][cg]);
 #pragma unroll
     for (int b = 0; b < 2; ++b)
 #pragma unroll
-      for (int cg = 0; cg < 2; ++cg) acc[b][cg] = op.gam[b] * acc[b][cg];
+      for (int cg = 0; cg < NCH; ++cg) acc[b][cg] = op.gam[b] * acc[b][cg];
 #pragma unroll
     for (int kk = 0; kk < 2; ++kk)
 #pragma unroll
       for (int b = 0; b < 2; ++b)
 #pragma unroll
-        for (int cg = 0; cg < 2; ++cg)
+        for (int cg = 0; cg < NCH; ++cg)
           if (kk < (own_rt<CW>(b) < 2 ? 1 : 2)) acc[b][cg] = mfma(ux[cg][kk], op.p[b][kk], acc[b][cg]);
     lds_t *const os = lds_ptr(scan_ostage);
 #pragma unroll
     for (int b = 0; b < 2; ++b)
 #pragma unroll
-      for (int cg = 0; cg < 2; ++cg) lds_store<bf16x4_t>(os + os_w[b][cg], __builtin_convertvector(acc[b][cg], bf16x4_t));
+      for (int cg = 0; cg < NCH; ++cg) lds_store<bf16x4_t>(os + os_w[b][cg], __builtin_convertvector(acc[b][cg], bf16x4_t));
 #pragma unroll
-    for (int b = 0; b < 2; ++b) o_pend[b] = lds_load<u32x4_t>(os + os_r[b]);
+    for (int b = 0; b < kPieces; ++b) o_pend[b] = lds_load<u32x4_t>(os + os_r[b]);
     o_pend_chunk = oc;
   };
   // The stores of the outputs computed in the previous phase, issued first
@@ -435,9 +445,9 @@ __device__ __forceinline__ void scan_copy_waves(const ScanArgs<bf16_t> &a, int l
     const int tok0 = start + o_pend_chunk * C;
     const int len = min(C, end - tok0);
     const __amdgpu_buffer_rsrc_t o_res = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<char *>(o_base + int64_t(tok0) * o_row_bytes), 0, int((len - 1) * o_row_bytes + 64), 0x00020000);
+        const_cast<char *>(o_base + int64_t(tok0) * o_row_bytes), 0, int((len - 1) * o_row_bytes + 2 * W), 0x00020000);
 #pragma unroll
-    for (int b = 0; b < 2; ++b) __builtin_amdgcn_raw_buffer_store_b128(o_pend[b], o_res, o_voff[b], 0, 0);
+    for (int b = 0; b < kPieces; ++b) __builtin_amdgcn_raw_buffer_store_b128(o_pend[b], o_res, o_voff[b], 0, 0);
     o_pend_chunk = -1;
   };
 
@@ -461,9 +471,7 @@ __device__ __forceinline__ void scan_copy_waves(const ScanArgs<bf16_t> &a, int l
     if (kCopies) stage_part(0, pf, dst);
     if (kOutputs && cc > 0) outputs(cc - 1, ex_prev);
     if (kOutputs)
-      scan_form_p<CW>(lds_ptr(const_cast<char *>(cur)), kq_off, lane, op, [&]() {
-        if (kCopies) stage_part(1, pf, dst);
-      });
+      scan_form_p<CW>(lds_ptr(const_cast<char *>(cur)), kq_off, lane, op, [&]() {});
     else
       stage_part(1, pf, dst);
     if (kCopies) wait_all_but_newest_stage();
@@ -486,17 +494,20 @@ __device__ __forceinline__ void scan_copy_waves(const ScanArgs<bf16_t> &a, int l
   wait_vmem();  // the trailing copies and stores
 }
 
-// NW = 4: waves 2 and 3 copy the k / q tiles and form P and the outputs.
-// NW = 6: waves 2 and 3 form P and the outputs, waves 4 and 5 (which share
-// SIMDs with the chain waves but issue only scalar and memory instructions)
-// copy the tiles, so no wave that computes ever waits to issue a copy.
-template <int NW>
-__global__ __launch_bounds__(64 * NW) void scan_kernel_staged(ScanArgs<bf16_t> a) {
+// NCH chain waves (one per 16-column group; a block of 16 NCH columns), then
+// two output waves, which form P and the outputs, and two copy waves, which
+// copy the k and q tiles (they share SIMDs with the other waves but issue
+// only scalar and memory instructions, so no wave that computes waits to
+// issue a copy).  One chain wave per block doubles the blocks of a problem
+// with few units (a long single sequence) at the same per-block traffic.
+template <int NCH>
+__global__ __launch_bounds__(64 * (NCH + 4)) void scan_kernel_staged(ScanArgs<bf16_t> a) {
+  constexpr int W = 16 * NCH;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int r0 = lane & 15, g = lane >> 4;
   int u, cb;
-  decode_block(blockIdx.x, a.n_colblk, u, cb);  // n_colblk = d_v / 32
+  decode_block(blockIdx.x, a.n_colblk, u, cb);  // n_colblk = d_v / W
   if (u >= a.n_units) return;  // the whole block
   const int s = a.geo.ordered(u / a.H_v), h = u % a.H_v, hq = h / a.group;
 
@@ -506,35 +517,24 @@ __global__ __launch_bounds__(64 * NW) void scan_kernel_staged(ScanArgs<bf16_t> a
   const int c_first = a.geo.first_chunk(s);
   const int n_chunks = max(0, min((end - start + C - 1) / C, a.geo.n_slots - c_first));
 
-  if (NW == 4) {
-    if (wave == 2) {
-      scan_copy_waves<0, 0>(a, lane, h, hq, cb, start, end, n_chunks);
-      return;
-    }
-    if (wave == 3) {
-      scan_copy_waves<1, 0>(a, lane, h, hq, cb, start, end, n_chunks);
-      return;
-    }
-  } else {
-    if (wave == 2) {
-      scan_copy_waves<0, 1>(a, lane, h, hq, cb, start, end, n_chunks);
-      return;
-    }
-    if (wave == 3) {
-      scan_copy_waves<1, 1>(a, lane, h, hq, cb, start, end, n_chunks);
-      return;
-    }
-    if (wave == 4) {
-      scan_copy_waves<0, 2>(a, lane, h, hq, cb, start, end, n_chunks);
-      return;
-    }
-    if (wave == 5) {
-      scan_copy_waves<1, 2>(a, lane, h, hq, cb, start, end, n_chunks);
-      return;
-    }
+  if (wave == NCH) {
+    scan_copy_waves<0, 1, NCH>(a, lane, h, hq, cb, start, end, n_chunks);
+    return;
+  }
+  if (wave == NCH + 1) {
+    scan_copy_waves<1, 1, NCH>(a, lane, h, hq, cb, start, end, n_chunks);
+    return;
+  }
+  if (wave == NCH + 2) {
+    scan_copy_waves<0, 2, NCH>(a, lane, h, hq, cb, start, end, n_chunks);
+    return;
+  }
+  if (wave == NCH + 3) {
+    scan_copy_waves<1, 2, NCH>(a, lane, h, hq, cb, start, end, n_chunks);
+    return;
   }
 
-  // ---- chain waves: wave w owns columns 32 cb + 16 w .. + 15 ----
+  // ---- chain waves: wave w owns columns W cb + 16 w .. + 15 ----
   // ---- lane-invariant LDS byte offsets (relative to a stage) ----
   // A fragments of k rows 16 rt + r0, columns 32 kk + 16 half + 4 g:
   // offset = 4096 rt + kq_off[kk][half].
@@ -550,38 +550,48 @@ __global__ __launch_bounds__(64 * NW) void scan_kernel_staged(ScanArgs<bf16_t> a
 #pragma unroll
   for (int rm = 0; rm < 8; ++rm) kt_off[rm] = 2 * rowtile_off(4 * g + (r0 >> 2), 16 * rm + 4 * (r0 & 3));
   // transposed v tile rt of this wave's columns (rows 16 rt + 4 g + a / 4,
-  // columns 16 w + 4 (a mod 4)): offset = 1024 rt + v_off.
-  const int v_off = vtile_byte(4 * g + (r0 >> 2), 16 * wave + 4 * (r0 & 3));
-  const int col = 32 * cb + 16 * wave + r0;  // this lane's state column
+  // columns 16 w + 4 (a mod 4)): offset = kVTile rt + v_off (32- or
+  // 16-column v block).
+  constexpr int kVTile = NCH == 2 ? 1024 : 512;
+  const int v_off = NCH == 2 ? vtile_byte(4 * g + (r0 >> 2), 16 * wave + 4 * (r0 & 3))
+                             : vtile16_byte(4 * g + (r0 >> 2), 4 * (r0 & 3));
+  const int col = W * cb + 16 * wave + r0;  // this lane's state column
   const int ex_off = kExWave * wave + 16 * lane;
 
-  // This wave's copies of a stage: T fragments (0, 2, 4 / 5, 6, 7), the gate
-  // block (wave 0), and v rows 32 w .. 32 w + 31 of the block (two copies,
-  // through a buffer resource that ends at the chunk's last row).
+  // This wave's copies of a stage (two chain waves: T fragments 0, 2, 4 and
+  // the gate block / T fragments 5, 6, 7, and v rows 32 w .. 32 w + 31; one
+  // chain wave: all of them), the v copies through a buffer resource that
+  // ends at the chunk's last row.
   const int64_t ebytes = entry_bytes<bf16_t>();
-  const char *const v_src = reinterpret_cast<const char *>(a.v) + (int64_t(h) * a.d_v + 32 * cb) * 2;
+  const char *const v_src = reinterpret_cast<const char *>(a.v) + (int64_t(h) * a.d_v + W * cb) * 2;
   const int64_t v_stride = int64_t(a.H_v) * a.d_v;
   const uint32_t v_row_bytes = uint32_t(2 * v_stride);
   uint32_t v_voff[2];
 #pragma unroll
-  for (int i = 0; i < 2; ++i) v_voff[i] = uint32_t(vblock_copy_src(2 * wave + i, lane, 64, v_stride));
+  for (int i = 0; i < 2; ++i)
+    v_voff[i] = uint32_t(NCH == 2 ? vblock_copy_src(2 * wave + i, lane, 64, v_stride)
+                                  : vblock16_copy_src(i, lane, 64, v_stride));
   auto chain_stage = [&](int cc, char *base_mem) {
     const int tok0 = start + cc * C;
     const int len = min(C, end - tok0);
     lds_t *const base = lds_ptr(base_mem);
     const char *entry = a.entries + (int64_t(c_first + cc) * a.H_v + h) * ebytes;
 #pragma unroll
-    for (int i = 0; i < 3; ++i) {
-      const int f = wave == 0 ? 2 * i : 5 + i;
-      dma16(entry + 1024 * f, 16 * lane, base + kStT + 1024 * t_slot(f));
+    for (int i = 0; i < 6; ++i) {
+      const int f = i < 3 ? 2 * i : 2 + i;  // 0, 2, 4, 5, 6, 7
+      if (NCH == 1 || (wave == 0) == (i < 3)) dma16(entry + 1024 * f, 16 * lane, base + kStT + 1024 * t_slot(f));
     }
     if (wave == 0) dma16(entry + 16384, 16 * lane, base + kStG);
-    const i32x4_t v_res = buffer_rsrc(v_src + int64_t(tok0) * v_row_bytes, vblock_valid_bytes(len, v_row_bytes));
+    const i32x4_t v_res = buffer_rsrc(v_src + int64_t(tok0) * v_row_bytes,
+                                      NCH == 2 ? vblock_valid_bytes(len, v_row_bytes)
+                                               : vblock16_valid_bytes(len, v_row_bytes));
 #pragma unroll
     for (int i = 0; i < 2; ++i) dma16_buf(v_res, v_voff[i], base + kStV + 2048 * wave + 1024 * i);
   };
   auto chain_wait_all_but_newest_stage = [&]() {
-    if (wave == 0)
+    if (NCH == 1)
+      wait_vmem_upto<kStageLoadsChain0 + 3>();
+    else if (wave == 0)
       wait_vmem_upto<kStageLoadsChain0>();
     else
       wait_vmem_upto<kStageLoadsChain1>();
@@ -625,7 +635,7 @@ __global__ __launch_bounds__(64 * NW) void scan_kernel_staged(ScanArgs<bf16_t> a
                               lds_load_single<bf16x4_t>(pk + kq_off[kk][1]));
       }
 #pragma unroll
-    for (int rt = 0; rt < 4; ++rt) vt[rt] = lds_read_tr16(st + kStV + 1024 * rt + v_off);
+    for (int rt = 0; rt < 4; ++rt) vt[rt] = lds_read_tr16(st + kStV + kVTile * rt + v_off);
 #pragma unroll
     for (int i = 0; i < 8; ++i)
       if (i != 1 && i != 3) tf[i].v = lds_load<bf16x8_t>(st + kStT + 1024 * t_slot(i) + 16 * lane);
@@ -733,9 +743,10 @@ __global__ __launch_bounds__(64 * NW) void scan_kernel_staged(ScanArgs<bf16_t> a
   }
 }
 
-#ifndef SCAN_WAVES
-#define SCAN_WAVES 6
-#endif
+// Below this many 32-column blocks (half the CUs of an MI355X) the staged
+// scan uses 16-column blocks, one chain wave each, so that a problem with few
+// (sequence, head) units spreads over twice as many CUs.
+constexpr int64_t kNarrowBelowBlocks = 128;
 
 template <typename T>
 static ScanArgs<T> scan_args(const Problem &p, const Workspace &ws, int colblk_width) {
@@ -760,11 +771,16 @@ static ScanArgs<T> scan_args(const Problem &p, const Workspace &ws, int colblk_w
 
 hipError_t launch_scan(const Problem &p, const Workspace &ws, hipStream_t st) {
   const bool staged = staged_path(p);
-  const int width = staged ? 32 : 16;
-  const int64_t blocks = (int64_t(p.n_seqs) * p.H_v + 7) / 8 * 8 * (p.d_v / width);
+  const int64_t units8 = (int64_t(p.n_seqs) * p.H_v + 7) / 8 * 8;
+  const bool narrow = staged && units8 * (p.d_v / 32) < kNarrowBelowBlocks;
+  const int width = staged && !narrow ? 32 : 16;
+  const int64_t blocks = units8 * (p.d_v / width);
   if (blocks == 0) return hipSuccess;
-  if (staged) {
-    hipLaunchKernelGGL(scan_kernel_staged<SCAN_WAVES>, dim3(unsigned(blocks)), dim3(64 * SCAN_WAVES), 0, st,
+  if (staged && narrow) {
+    hipLaunchKernelGGL(scan_kernel_staged<1>, dim3(unsigned(blocks)), dim3(64 * 5), 0, st,
+                       scan_args<bf16_t>(p, ws, width));
+  } else if (staged) {
+    hipLaunchKernelGGL(scan_kernel_staged<2>, dim3(unsigned(blocks)), dim3(64 * 6), 0, st,
                        scan_args<bf16_t>(p, ws, width));
   } else if (p.dtype == 1) {
     hipLaunchKernelGGL(scan_kernel<bf16_t>, dim3(unsigned(blocks)), dim3(64), 0, st,

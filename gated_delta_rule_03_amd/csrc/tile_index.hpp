@@ -77,6 +77,25 @@ __host__ __device__ constexpr int vtile_byte(int row, int col) {
   return 2 * (row * 32 + 8 * ((col >> 3) ^ ((row >> 2) & 3)) + (col & 7));
 }
 
+// ---- v block, 16 columns (a block of one column group) ----
+// 64 token rows x 16 bf16 (32 B per row) in 2 copies of 1 KiB; copy j moves
+// rows 32 j .. 32 j + 31, lane l moves row 32 j + l / 2, physical block
+// l mod 2, source block (l mod 2) ^ ((row / 4) mod 2).
+__host__ __device__ constexpr int vblock16_copy_row(int j, int lane) { return 32 * j + (lane >> 1); }
+__host__ __device__ constexpr int vblock16_copy_block(int j, int lane) {
+  return (lane & 1) ^ ((vblock16_copy_row(j, lane) >> 2) & 1);
+}
+__host__ __device__ constexpr int64_t vblock16_copy_src(int j, int lane, int len, int64_t stride) {
+  return 2 * (int64_t(clamp_row(vblock16_copy_row(j, lane), len)) * stride + 8 * vblock16_copy_block(j, lane));
+}
+__host__ __device__ constexpr uint32_t vblock16_valid_bytes(int len, uint32_t row_bytes) {
+  return uint32_t(len - 1) * row_bytes + 32;
+}
+// Byte offset of logical (row, col) in the staged 16-column v block.
+__host__ __device__ constexpr int vtile16_byte(int row, int col) {
+  return 2 * (row * 16 + 8 * ((col >> 3) ^ ((row >> 2) & 1)) + (col & 7));
+}
+
 // ---- outputs as the MFMA leaves them (transposed tiles) ----
 // Output tile rt, lane l: token row 16 rt + l mod 16, columns
 // 16 cg + 4 (l / 16) .. + 3 of column group cg of the block.
@@ -99,6 +118,16 @@ __host__ __device__ constexpr int out_stage_byte(int row, int col) {
 // 8 (l mod 4) .. + 7 (one 16-byte piece; 16 rows x 64 bytes per instruction).
 __host__ __device__ constexpr int out_piece_row(int rt, int lane) { return 16 * rt + (lane >> 2); }
 __host__ __device__ constexpr int out_piece_col(int lane) { return 8 * (lane & 3); }
+
+// The same for a 16-column block (32 bytes per row; physical piece =
+// piece ^ ((row / 4) mod 2)).  Read-back: lane l stores row
+// 16 rt + (l mod 32) / 2 of row block rt = copy_rows(cw, l / 32), columns
+// 8 (l mod 2) .. + 7 -- both row blocks of a copy wave in one instruction.
+__host__ __device__ constexpr int out_stage16_byte(int row, int col) {
+  return row * 32 + 16 * (((col >> 3) ^ (row >> 2)) & 1) + 2 * (col & 7);
+}
+__host__ __device__ constexpr int out_piece16_row(int rt, int lane) { return 16 * rt + ((lane & 31) >> 1); }
+__host__ __device__ constexpr int out_piece16_col(int lane) { return 8 * (lane & 1); }
 
 // Token row blocks (of P and of the outputs) that copy wave cw = 0, 1 owns:
 // {0, 3} and {1, 2}.  Row block rt of the lower-triangular P has rt + 1

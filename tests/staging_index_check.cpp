@@ -139,6 +139,68 @@ int main() {
     CHECK(p_tiles[0] == 5 && p_tiles[1] == 5, "P tiles per copy wave %d / %d", p_tiles[0], p_tiles[1]);
   }
 
+  // ---- 16-column v block: 2 copies x 64 lanes cover 64 rows x 16 columns once ----
+  for (int len = 1; len <= 64; ++len) {
+    const int64_t stride = 32 * 128;  // elements between token rows (32 heads x 128)
+    for (int j = 0; j < 2; ++j)
+      for (int l = 0; l < 64; ++l) {
+        const int64_t src = vblock16_copy_src(j, l, len, stride);
+        const int row = vblock16_copy_row(j, l);
+        CHECK(src >= 0 && src + 16 <= int64_t(vblock16_valid_bytes(len, uint32_t(2 * stride))),
+              "v16 copy %d lane %d len %d reads past the chunk", j, l, len);
+        CHECK(src / (2 * stride) == (row < len ? row : len - 1), "v16 copy %d lane %d row", j, l);
+      }
+  }
+  {
+    std::vector<int> seen(64 * 16, 0);
+    for (int j = 0; j < 2; ++j)
+      for (int l = 0; l < 64; ++l) {
+        const int row = vblock16_copy_row(j, l), col = 8 * vblock16_copy_block(j, l);
+        const int at = vtile16_byte(row, col);
+        CHECK(at == 1024 * j + 16 * l, "v16 block (%d,%d) read at byte %d, written at %d", row, col, at, 1024 * j + 16 * l);
+        for (int c = 0; c < 8; ++c) {
+          CHECK(vtile16_byte(row, col + c) == at + 2 * c, "v16 block (%d,%d) not contiguous", row, col + c);
+          seen[row * 16 + col + c]++;
+        }
+      }
+    for (int x = 0; x < 64 * 16; ++x) CHECK(seen[x] == 1, "v16 block element %d copied %d times", x, seen[x]);
+  }
+
+  // ---- output staging, 16-column blocks: each copy wave writes its two row
+  // blocks as 8-byte tile pieces and reads both back with one 16-byte piece
+  // per lane ----
+  {
+    std::vector<int> wrote(64 * 16, -1), read(64 * 16, 0);
+    for (int cw = 0; cw < 2; ++cw) {
+      for (int a = 0; a < 2; ++a) {
+        const int rt = copy_rows(cw, a);
+        for (int l = 0; l < 64; ++l) {
+          const int row = out_acc_row(rt, l), col = out_acc_col(0, l);
+          const int base = out_stage16_byte(row, col);
+          CHECK(base % 8 == 0 && base + 8 <= 2048, "staging16 write (%d,%d) at %d", row, col, base);
+          for (int c = 0; c < 4; ++c) {
+            CHECK(out_stage16_byte(row, col + c) == base + 2 * c, "staging16 write (%d,%d) not contiguous", row, col + c);
+            CHECK(wrote[row * 16 + col + c] == -1, "output16 (%d,%d) staged twice", row, col + c);
+            wrote[row * 16 + col + c] = cw;
+          }
+        }
+      }
+      for (int l = 0; l < 64; ++l) {
+        const int rt = copy_rows(cw, l >> 5);
+        const int row = out_piece16_row(rt, l), col = out_piece16_col(l);
+        const int base = out_stage16_byte(row, col);
+        CHECK(base % 16 == 0 && base + 16 <= 2048, "staging16 read (%d,%d) at %d", row, col, base);
+        CHECK(row / 16 == rt, "read-back16 row %d outside row block %d", row, rt);
+        for (int c = 0; c < 8; ++c) {
+          CHECK(out_stage16_byte(row, col + c) == base + 2 * c, "staging16 read (%d,%d) not contiguous", row, col + c);
+          CHECK(wrote[row * 16 + col + c] == cw, "output16 (%d,%d) read back by the other wave", row, col + c);
+          read[row * 16 + col + c]++;
+        }
+      }
+    }
+    for (int x = 0; x < 64 * 16; ++x) CHECK(wrote[x] >= 0 && read[x] == 1, "output16 element %d", x);
+  }
+
   // ---- T fragments: the six non-zero ones fill six distinct slots ----
   {
     std::vector<int> seen(6, 0);
