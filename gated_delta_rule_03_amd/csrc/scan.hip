@@ -186,15 +186,20 @@ __global__ __launch_bounds__(64) void scan_kernel(ScanArgs<T> a) {
 // ---------------------------------------------------------------------------
 // Pipelined path: bf16, d_k = 128, d_v a multiple of 32.
 //
-// A block of four waves owns 32 state columns of one unit.  Waves 0 and 1
-// run the state chain (16 columns each); waves 2 and 3 copy operands, form P
-// and compute the outputs.  A chunk's operands -- its k and q rows (swizzled
-// row tiles), the T fragments and gates of its workspace entry, and its
-// 64 x 32 block of v -- are copied into one of three LDS stages with
-// buffer/global loads straight to LDS, two chunks ahead of the chunk being
-// computed.  A copy moves 1 KiB and the memory pipeline accepts one from a
-// wave only every few dozen cycles, so the copies are spread over the waves:
-// the copy waves issue the k and q tiles, the chain waves the small rest.
+// A block of NCH + 4 waves owns 16 NCH state columns of one unit.  Waves
+// 0 .. NCH - 1 run the state chain (16 columns each); waves NCH and NCH + 1
+// form P and compute the outputs; waves NCH + 2 and NCH + 3 copy operands.
+// A chunk's operands -- its k and q rows (swizzled row tiles), the T
+// fragments and gates of its workspace entry, and its 64 x 16 NCH block of v
+// -- are copied into one of three LDS stages with buffer/global loads
+// straight to LDS, two chunks ahead of the chunk being computed.  The copy
+// waves issue every copy (one the k tile, T fragments 0, 2, 4 and the gate
+// block, the other the q tile and T fragments 5, 6, 7; each half of the v
+// block, with the nontemporal hint: v is read once, and its lines should
+// leave the L2 before the k and q lines that the unit's other column blocks
+// still read).  A copy moves 1 KiB and the memory pipeline accepts one only
+// every few dozen cycles; the copy waves share SIMDs with the chain waves
+// but issue no arithmetic, so no wave that computes waits to issue a copy.
 //
 // The chain waves' instruction stream is the whole cost of a chunk, so it
 // holds the state chain only: Y = K S, U = T (V - gamma Y), the state update.
@@ -226,16 +231,10 @@ constexpr int kStBytes = 44032;
 constexpr int kExS = 0, kExU = 4096, kExWave = 6144;
 constexpr int kExBytes = 2 * kExWave;
 typedef unsigned u32x2_t __attribute__((ext_vector_type(2)));
-// Copies each wave issues per stage: copy wave 2 the k tile, copy wave 3 the
-// q tile (16 each); chain wave 0 T fragments 0, 2, 4, the gates and v rows
-// 0-31, chain wave 1 T fragments 5, 6, 7 and v rows 32-63.  Loads complete in
-// issue order, and the only other vector-memory operations in a wave's loop
-// are a copy wave's output stores; so waiting until at most this many of its
-// operations are outstanding completes every load it issued before the
-// newest stage's copies, whatever the stores do.
+// k (or q) tile copies per stage.  A copy wave issues nothing but copies,
+// and loads complete in issue order, so waiting until at most one stage's
+// copies are outstanding completes every earlier stage.
 constexpr int kStageLoadsCopy = 16;
-constexpr int kStageLoadsChain0 = 6;
-constexpr int kStageLoadsChain1 = 5;
 
 // Three stages and two exchange buffers as distinct LDS objects: with the
 // chunk loop unrolled by six, every access names its buffer at compile time.
@@ -325,10 +324,11 @@ __device__ __forceinline__ void scan_form_p(const lds_t *st, const int (&kq_off)
 
 // ROLE 1: output wave CW forms its rows of P and computes their outputs for
 // the block's NCH column groups; ROLE 2: copy wave CW issues the k (CW = 0)
-// or q (CW = 1) tile copies.
+// or q (CW = 1) tile copies, half the T fragments (and, CW = 0, the gate
+// block) and half the v block of each stage.
 template <int CW, int ROLE, int NCH>
 __device__ __forceinline__ void scan_copy_waves(const ScanArgs<bf16_t> &a, int lane, int h, int hq, int cb,
-                                                int start, int end, int n_chunks) {
+                                                int start, int end, int c_first, int n_chunks) {
   constexpr bool kCopies = ROLE == 2, kOutputs = ROLE == 1;
   constexpr int W = 16 * NCH;  // columns of the block
   const int r0 = lane & 15, g = lane >> 4;
@@ -355,11 +355,42 @@ __device__ __forceinline__ void scan_copy_waves(const ScanArgs<bf16_t> &a, int l
 #pragma unroll
     for (int i = 8 * part; i < 8 * part + 8; ++i) dma16_buf(kq_res, kq_voff[i], tile + 1024 * i);
   };
+  // The rest of a stage: copy wave 0 T fragments 0, 2, 4 and the gate block,
+  // copy wave 1 T fragments 5, 6, 7; each half of the v rows.
+  const int64_t ebytes = entry_bytes<bf16_t>();
+  const char *const v_src = reinterpret_cast<const char *>(a.v) + (int64_t(h) * a.d_v + W * cb) * 2;
+  const uint32_t v_row_bytes = uint32_t(2 * v_stride);
+  constexpr int kVCopies = NCH == 2 ? 2 : 1;
+  uint32_t v_voff[kVCopies];
+#pragma unroll
+  for (int i = 0; i < kVCopies; ++i)
+    v_voff[i] = uint32_t(NCH == 2 ? vblock_copy_src(2 * CW + i, lane, 64, v_stride)
+                                  : vblock16_copy_src(CW, lane, 64, v_stride));
+  auto stage_rest = [&](int cc, char *base_mem) {
+    const int tok0 = start + cc * C;
+    const int len = min(C, end - tok0);
+    lds_t *const base = lds_ptr(base_mem);
+    const char *entry = a.entries + (int64_t(c_first + cc) * a.H_v + h) * ebytes;
+#pragma unroll
+    for (int i = 0; i < 3; ++i) {
+      const int f = CW == 0 ? 2 * i : 5 + i;  // 0, 2, 4 / 5, 6, 7
+      dma16(entry + 1024 * f, 16 * lane, base + kStT + 1024 * t_slot(f));
+    }
+    if (CW == 0) dma16(entry + 16384, 16 * lane, base + kStG);
+    const i32x4_t v_res = buffer_rsrc(v_src + int64_t(tok0) * v_row_bytes,
+                                      NCH == 2 ? vblock_valid_bytes(len, v_row_bytes)
+                                               : vblock16_valid_bytes(len, v_row_bytes));
+#pragma unroll
+    for (int i = 0; i < kVCopies; ++i)
+      dma16_buf_nt(v_res, v_voff[i], base + kStV + (NCH == 2 ? 2048 * CW + 1024 * i : 1024 * CW));
+  };
   auto stage = [&](int cc, char *base_mem) {
+    stage_rest(cc, base_mem);
     stage_part(0, cc, base_mem);
     stage_part(1, cc, base_mem);
   };
-  auto wait_all_but_newest_stage = [&]() { wait_vmem_upto<kStageLoadsCopy>(); };
+  constexpr int kLoads = kStageLoadsCopy + 3 + (CW == 0 ? 1 : 0) + kVCopies;
+  auto wait_all_but_newest_stage = [&]() { wait_vmem_upto<kLoads>(); };
   int kq_off[4][2];
 #pragma unroll
   for (int kk = 0; kk < 4; ++kk)
@@ -468,7 +499,10 @@ __device__ __forceinline__ void scan_copy_waves(const ScanArgs<bf16_t> &a, int l
     const int pf = min(cc + 2, n_chunks - 1);
     if (kOutputs) store_pending();
     if (ROLE == 2) __builtin_amdgcn_s_sleep(SCAN_COPY_DELAY);
-    if (kCopies) stage_part(0, pf, dst);
+    if (kCopies) {
+      stage_rest(pf, dst);
+      stage_part(0, pf, dst);
+    }
     if (kOutputs && cc > 0) outputs(cc - 1, ex_prev);
     if (kOutputs)
       scan_form_p<CW>(lds_ptr(const_cast<char *>(cur)), kq_off, lane, op, [&]() {});
@@ -496,10 +530,9 @@ __device__ __forceinline__ void scan_copy_waves(const ScanArgs<bf16_t> &a, int l
 
 // NCH chain waves (one per 16-column group; a block of 16 NCH columns), then
 // two output waves, which form P and the outputs, and two copy waves, which
-// copy the k and q tiles (they share SIMDs with the other waves but issue
-// only scalar and memory instructions, so no wave that computes waits to
-// issue a copy).  One chain wave per block doubles the blocks of a problem
-// with few units (a long single sequence) at the same per-block traffic.
+// issue every copy of a stage.  One chain wave per block doubles the blocks
+// of a problem with few units (a long single sequence) at the same per-block
+// traffic.
 template <int NCH>
 __global__ __launch_bounds__(64 * (NCH + 4)) void scan_kernel_staged(ScanArgs<bf16_t> a) {
   constexpr int W = 16 * NCH;
@@ -518,19 +551,19 @@ __global__ __launch_bounds__(64 * (NCH + 4)) void scan_kernel_staged(ScanArgs<bf
   const int n_chunks = max(0, min((end - start + C - 1) / C, a.geo.n_slots - c_first));
 
   if (wave == NCH) {
-    scan_copy_waves<0, 1, NCH>(a, lane, h, hq, cb, start, end, n_chunks);
+    scan_copy_waves<0, 1, NCH>(a, lane, h, hq, cb, start, end, c_first, n_chunks);
     return;
   }
   if (wave == NCH + 1) {
-    scan_copy_waves<1, 1, NCH>(a, lane, h, hq, cb, start, end, n_chunks);
+    scan_copy_waves<1, 1, NCH>(a, lane, h, hq, cb, start, end, c_first, n_chunks);
     return;
   }
   if (wave == NCH + 2) {
-    scan_copy_waves<0, 2, NCH>(a, lane, h, hq, cb, start, end, n_chunks);
+    scan_copy_waves<0, 2, NCH>(a, lane, h, hq, cb, start, end, c_first, n_chunks);
     return;
   }
   if (wave == NCH + 3) {
-    scan_copy_waves<1, 2, NCH>(a, lane, h, hq, cb, start, end, n_chunks);
+    scan_copy_waves<1, 2, NCH>(a, lane, h, hq, cb, start, end, c_first, n_chunks);
     return;
   }
 
@@ -557,45 +590,6 @@ __global__ __launch_bounds__(64 * (NCH + 4)) void scan_kernel_staged(ScanArgs<bf
                              : vtile16_byte(4 * g + (r0 >> 2), 4 * (r0 & 3));
   const int col = W * cb + 16 * wave + r0;  // this lane's state column
   const int ex_off = kExWave * wave + 16 * lane;
-
-  // This wave's copies of a stage (two chain waves: T fragments 0, 2, 4 and
-  // the gate block / T fragments 5, 6, 7, and v rows 32 w .. 32 w + 31; one
-  // chain wave: all of them), the v copies through a buffer resource that
-  // ends at the chunk's last row.
-  const int64_t ebytes = entry_bytes<bf16_t>();
-  const char *const v_src = reinterpret_cast<const char *>(a.v) + (int64_t(h) * a.d_v + W * cb) * 2;
-  const int64_t v_stride = int64_t(a.H_v) * a.d_v;
-  const uint32_t v_row_bytes = uint32_t(2 * v_stride);
-  uint32_t v_voff[2];
-#pragma unroll
-  for (int i = 0; i < 2; ++i)
-    v_voff[i] = uint32_t(NCH == 2 ? vblock_copy_src(2 * wave + i, lane, 64, v_stride)
-                                  : vblock16_copy_src(i, lane, 64, v_stride));
-  auto chain_stage = [&](int cc, char *base_mem) {
-    const int tok0 = start + cc * C;
-    const int len = min(C, end - tok0);
-    lds_t *const base = lds_ptr(base_mem);
-    const char *entry = a.entries + (int64_t(c_first + cc) * a.H_v + h) * ebytes;
-#pragma unroll
-    for (int i = 0; i < 6; ++i) {
-      const int f = i < 3 ? 2 * i : 2 + i;  // 0, 2, 4, 5, 6, 7
-      if (NCH == 1 || (wave == 0) == (i < 3)) dma16(entry + 1024 * f, 16 * lane, base + kStT + 1024 * t_slot(f));
-    }
-    if (wave == 0) dma16(entry + 16384, 16 * lane, base + kStG);
-    const i32x4_t v_res = buffer_rsrc(v_src + int64_t(tok0) * v_row_bytes,
-                                      NCH == 2 ? vblock_valid_bytes(len, v_row_bytes)
-                                               : vblock16_valid_bytes(len, v_row_bytes));
-#pragma unroll
-    for (int i = 0; i < 2; ++i) dma16_buf(v_res, v_voff[i], base + kStV + 2048 * wave + 1024 * i);
-  };
-  auto chain_wait_all_but_newest_stage = [&]() {
-    if (NCH == 1)
-      wait_vmem_upto<kStageLoadsChain0 + 3>();
-    else if (wave == 0)
-      wait_vmem_upto<kStageLoadsChain0>();
-    else
-      wait_vmem_upto<kStageLoadsChain1>();
-  };
 
   // ---- state ----
   f32x4_t S[8];
@@ -641,11 +635,6 @@ __global__ __launch_bounds__(64 * (NCH + 4)) void scan_kernel_staged(ScanArgs<bf
       if (i != 1 && i != 3) tf[i].v = lds_load<bf16x8_t>(st + kStT + 1024 * t_slot(i) + 16 * lane);
   };
 
-  if (n_chunks > 0) {
-    chain_stage(0, scan_stage0);
-    chain_stage(min(1, n_chunks - 1), scan_stage1);
-    chain_wait_all_but_newest_stage();
-  }
   lds_barrier();  // the first two stages are complete
   if (n_chunks > 0) read_operands(scan_stage0);
 
@@ -670,9 +659,6 @@ __global__ __launch_bounds__(64 * (NCH + 4)) void scan_kernel_staged(ScanArgs<bf
       for (int rt = 0; rt < 4; ++rt) Y[rt] = mfma(kf[kk][rt], Sf[kk], kk == 0 ? zero4() : Y[rt]);
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk) lds_store<bf16x8_t>(ex + kExS + 1024 * kk, Sf[kk].v);
-    // chunk cc + 2 into the previous chunk's stage (free since the barrier
-    // that opened this chunk; past the end the last chunk is copied again)
-    chain_stage(min(cc + 2, n_chunks - 1), prev_mem);
 
     // K^T fragments for the state update (transposed reads of the k tile),
     // issued early so that they have landed when the update starts
@@ -722,7 +708,6 @@ __global__ __launch_bounds__(64 * (NCH + 4)) void scan_kernel_staged(ScanArgs<bf
     // this chunk's stage reads are done (the copy waves may now refill the
     // previous chunk's stage), the exchange is written, and the next chunk's
     // stage is complete
-    chain_wait_all_but_newest_stage();
     lds_barrier();
     if (cc + 1 < n_chunks) read_operands(next_mem);
   };

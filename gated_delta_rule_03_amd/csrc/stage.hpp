@@ -52,6 +52,15 @@ __device__ __forceinline__ void dma16_buf(i32x4_t rsrc, uint32_t voff, lds_t *ds
                : "memory", "m0");
 }
 
+// dma16_buf with the nontemporal hint, for data that is read exactly once:
+// its lines leave the L2 first, ahead of tiles that other blocks still read.
+__device__ __forceinline__ void dma16_buf_nt(i32x4_t rsrc, uint32_t voff, lds_t *dst) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen nt lds"
+               :
+               : "s"((uint32_t)(uintptr_t)dst), "v"(voff), "s"(rsrc)
+               : "memory", "m0");
+}
+
 // Bounds-checked 4-byte-per-lane form: lane l's 4 bytes land at dst + 4 * l.
 __device__ __forceinline__ void dma4_buf(i32x4_t rsrc, uint32_t voff, lds_t *dst) {
   asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dword %1, %2, 0 offen lds"
