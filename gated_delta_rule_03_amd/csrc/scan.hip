@@ -542,7 +542,13 @@ __global__ __launch_bounds__(64 * (NCH + 4)) void scan_kernel_staged(ScanArgs<bf
   int u, cb;
   decode_block(blockIdx.x, a.n_colblk, u, cb);  // n_colblk = d_v / W
   if (u >= a.n_units) return;  // the whole block
-  const int s = a.geo.ordered(u / a.H_v), h = u % a.H_v, hq = h / a.group;
+  // The block's unit runs on XCD u mod 8.  Heads rotate by three per
+  // sequence, so that an XCD serves eight different heads rather than the two
+  // with h = u mod 8 (when H_v is a multiple of 8): the slices of some heads
+  // in every k, q, v and o row are served more slowly than others, and
+  // spread over all XCDs they delay the last blocks less.
+  const int s_idx = u / a.H_v;
+  const int s = a.geo.ordered(s_idx), h = (u + 3 * s_idx) % a.H_v, hq = h / a.group;
 
   int start, end;
   a.geo.seq_bounds(s, start, end);
