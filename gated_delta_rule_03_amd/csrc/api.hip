@@ -31,7 +31,7 @@ SeqGeom make_geom(const Problem &p, const Workspace *ws) {
 }
 
 size_t workspace_layout(const Problem &p, void *base, Workspace *ws) {
-  const int64_t entry = p.dtype == GDN_BF16 ? entry_bytes<uint16_t>() : entry_bytes<float>();
+  const int64_t entry = entry_stride(p);
   const size_t off_bytes = align256(size_t(2 * int64_t(p.n_seqs) + 1) * sizeof(int32_t));
   const size_t ent_bytes = align256(size_t(chunk_slots(p)) * p.H_v * size_t(entry));
   if (ws) {

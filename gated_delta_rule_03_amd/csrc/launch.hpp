@@ -30,10 +30,7 @@ int64_t chunk_slots(const Problem &p);
 // elements of the operand type -- followed by a 1 KiB gate block of fp32:
 // gamma_t = 2^g_t for the 64 slots, then s_t = 2^(g_C - g_t), then g_t.
 // (g_t is the chunk-local cumulative log2 gate; padded slots repeat the last
-// token's gate, so gamma_63 = gamma_C and s = 1 there.)  On the staged path
-// the scan forms P itself: its entries hold T and the gate block only, and
-// the two all-zero T fragments (rows 0-31, columns 32-63) are never written
-// or read.
+// token's gate, so gamma_63 = gamma_C and s = 1 there.)
 constexpr int kFragElems = 64 * 8;
 constexpr int kGateBlockBytes = 1024;
 template <typename T> constexpr int64_t entry_bytes() {
@@ -41,8 +38,17 @@ template <typename T> constexpr int64_t entry_bytes() {
 }
 
 // The staged path: bf16 operands, d_k = 128, d_v a multiple of 32 (the factor
-// kernel and the staged scan, which share the reduced entry contents).
+// kernel and the staged scan).  The scan forms P itself, and the two all-zero
+// T fragments (rows 0-31, columns 32-63) are neither stored nor read, so an
+// entry is 7 KiB: T's six other bf16 fragments in t_slot order
+// (tile_index.hpp), then the gate block.
 inline bool staged_path(const Problem &p) { return p.dtype == 1 && p.d_k == 128 && p.d_v % 32 == 0; }
+constexpr int kStagedGateOffset = 6 * kFragElems * 2;
+constexpr int64_t kStagedEntryBytes = kStagedGateOffset + kGateBlockBytes;
+inline int64_t entry_stride(const Problem &p) {
+  if (staged_path(p)) return kStagedEntryBytes;
+  return p.dtype == 1 ? entry_bytes<uint16_t>() : entry_bytes<float>();
+}
 
 struct Workspace {
   int32_t *chunk_off;  // [n_seqs + 1] chunk prefix sums (packed batches)

@@ -207,8 +207,8 @@ __global__ __launch_bounds__(256) void prep_kernel(PrepArgs<T> a) {
 // workgroup of two waves per (chunk slot, value head); its k rows and gates
 // are copied into LDS with bounds-checked buffer loads (rows past the chunk's
 // end read as zeros, padded slots get beta = 0 and add nothing to the gate).
-// It writes T and the gate block; the staged scan forms P from the q and k
-// rows it stages anyway.
+// It writes T and the gate block into a 7 KiB entry (launch.hpp); the staged
+// scan forms P from the q and k rows it stages anyway.
 //
 // M = (I + A)^-1 in 16 x 16 blocks.  Wave 1 forms the diagonal blocks A_bb
 // and solves D_b = (I + A_bb)^-1 for all four b at once (lane 16 b + c owns
@@ -283,7 +283,7 @@ __global__ __launch_bounds__(128, 4) void factors_kernel(PrepArgs<bf16_t> a) {
   wait_vmem();
   lds_barrier();
 
-  char *const entry = a.entries + (int64_t(c) * a.H_v + h) * entry_bytes<bf16_t>();
+  char *const entry = a.entries + (int64_t(c) * a.H_v + h) * kStagedEntryBytes;
   // chunk-local cumulative log2 gate of slot `lane` (slots past len add 0)
   const float gl =
       wave_prefix_sum(lane < len ? clamped_log2(lds_load<float>(sm + kXAlpha + 4 * lane)) : 0.0f);
@@ -309,10 +309,10 @@ __global__ __launch_bounds__(128, 4) void factors_kernel(PrepArgs<bf16_t> a) {
     return __builtin_convertvector(m * bc, bf16x4_t);
   };
   auto put_frag = [&](int f, bf16x4_t lo, bf16x4_t hi) {
-    *reinterpret_cast<bf16x8_t *>(fragT + kFragElems * f + 8 * lane) = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+    *reinterpret_cast<bf16x8_t *>(fragT + kFragElems * t_slot(f) + 8 * lane) = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
   };
   auto put_half = [&](int f, int hf, bf16x4_t v) {
-    *reinterpret_cast<bf16x4_t *>(fragT + kFragElems * f + 8 * lane + 4 * hf) = v;
+    *reinterpret_cast<bf16x4_t *>(fragT + kFragElems * t_slot(f) + 8 * lane + 4 * hf) = v;
   };
   const bf16x4_t zero_h = {0, 0, 0, 0};
 
@@ -383,7 +383,7 @@ __global__ __launch_bounds__(128, 4) void factors_kernel(PrepArgs<bf16_t> a) {
       put_half(6, 0, t_half(0, M30r));
     } else {
       // gate block: gamma_t = 2^g_t, s_t = 2^(g_C - g_t), g_t
-      float *gate_out = reinterpret_cast<float *>(entry + 16 * kFragElems * sizeof(bf16_t));
+      float *gate_out = reinterpret_cast<float *>(entry + kStagedGateOffset);
       const float g_last = __shfl(gl, 63);
       gate_out[lane] = exp2f(gl);
       gate_out[64 + lane] = exp2f(g_last - gl);

@@ -357,7 +357,7 @@ __device__ __forceinline__ void scan_copy_waves(const ScanArgs<bf16_t> &a, int l
   };
   // The rest of a stage: copy wave 0 T fragments 0, 2, 4 and the gate block,
   // copy wave 1 T fragments 5, 6, 7; each half of the v rows.
-  const int64_t ebytes = entry_bytes<bf16_t>();
+  const int64_t ebytes = kStagedEntryBytes;
   const char *const v_src = reinterpret_cast<const char *>(a.v) + (int64_t(h) * a.d_v + W * cb) * 2;
   const uint32_t v_row_bytes = uint32_t(2 * v_stride);
   constexpr int kVCopies = NCH == 2 ? 2 : 1;
@@ -374,9 +374,9 @@ __device__ __forceinline__ void scan_copy_waves(const ScanArgs<bf16_t> &a, int l
 #pragma unroll
     for (int i = 0; i < 3; ++i) {
       const int f = CW == 0 ? 2 * i : 5 + i;  // 0, 2, 4 / 5, 6, 7
-      dma16(entry + 1024 * f, 16 * lane, base + kStT + 1024 * t_slot(f));
+      dma16(entry + 1024 * t_slot(f), 16 * lane, base + kStT + 1024 * t_slot(f));
     }
-    if (CW == 0) dma16(entry + 16384, 16 * lane, base + kStG);
+    if (CW == 0) dma16(entry + kStagedGateOffset, 16 * lane, base + kStG);
     const i32x4_t v_res = buffer_rsrc(v_src + int64_t(tok0) * v_row_bytes,
                                       NCH == 2 ? vblock_valid_bytes(len, v_row_bytes)
                                                : vblock16_valid_bytes(len, v_row_bytes));
