@@ -127,6 +127,16 @@ def test_small_packed_grouped_heads(gdn, dtype, path, chunk):
 
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_many_packed_sequences(gdn, dtype):
+    """1,100 ragged sequences of 0-40 tokens: more than the 1,024 the device
+    ranks by length (beyond that the scan walks them in index order)."""
+    rng = np.random.default_rng(77)
+    lengths = tuple(int(x) for x in rng.integers(0, 41, size=1100))
+    w = small(dtype, 1, 0, 1, 2, 128, 64 if dtype == "bf16" else 32, 64, seed=78, lengths=lengths)
+    check(gdn, "chunk", w)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
 def test_small_decode(gdn, dtype):
     import torch
     w = small(dtype, 5, 1, 2, 4, 128, 64, 64, seed=41)
