@@ -201,14 +201,14 @@ __global__ __launch_bounds__(64) void scan_kernel(ScanArgs<T> a) {
 // every few dozen cycles; the copy waves share SIMDs with the chain waves
 // but issue no arithmetic, so no wave that computes waits to issue a copy.
 //
-// The chain waves' instruction stream is the whole cost of a chunk, so it
-// holds the state chain only: Y = K S, U = T (V - gamma Y), the state update.
-// Each chain wave leaves the chunk-start state (as the bf16 fragments it
-// multiplies anyway) and U in one of two exchange buffers.  In the next phase
-// each copy wave computes the outputs of two of the chunk's four 16-token row
-// blocks for both column groups, O^T = S^T (gamma Q^T) + U^T P^T, from that
-// exchange, the q rows and the rows of P it formed itself in the previous
-// phase (kept in registers), and stores them.
+// The chain waves run the state chain only (Y = K S, U = T (V - gamma Y), the
+// state update) and issue no memory instruction.  Each chain wave leaves the
+// chunk-start state (as the bf16 fragments it multiplies anyway) and U in one
+// of two exchange buffers.  In the next phase each output wave computes the
+// outputs of two of the chunk's four 16-token row blocks for every column
+// group, O^T = S^T (gamma Q^T) + U^T P^T, from that exchange, the q rows and
+// the rows of P it formed itself in the previous phase (kept in registers),
+// and stores them.
 //
 // One barrier per chunk keeps the roles in step.  T and P are lower
 // triangular: their all-zero fragments (rows 0-31, columns 32-63) are neither
@@ -222,7 +222,7 @@ constexpr int kStK = 0;        // 64 x 128 bf16 row tile
 constexpr int kStQ = 16384;    // 64 x 128 bf16 row tile
 constexpr int kStT = 32768;    // T's six non-zero fragments, 1 KiB each (t_slot, tile_index.hpp)
 constexpr int kStG = 38912;    // gate block: gamma, s, g (64 fp32 each), padding
-constexpr int kStV = 39936;    // 64 x 32 bf16 v block
+constexpr int kStV = 39936;    // 64 x 16 NCH bf16 v block (4 KiB)
 constexpr int kStBytes = 44032;
 
 // Exchange buffer: per chain wave w, at 6144 w, the chunk-start state as four
@@ -244,27 +244,27 @@ __shared__ __attribute__((aligned(16))) char scan_stage2[kStBytes];
 __shared__ __attribute__((aligned(16))) char scan_ex0[kExBytes];
 __shared__ __attribute__((aligned(16))) char scan_ex1[kExBytes];
 // A chunk's outputs on their way out (64 token rows x 32 bf16, out_stage_byte
-// in tile_index.hpp): each copy wave writes and reads back only its own rows,
-// so that every store covers whole 64-byte rows of the block.
+// in tile_index.hpp): each output wave writes and reads back only its own
+// rows, so that every store covers whole rows of the block.
 __shared__ __attribute__((aligned(16))) char scan_ostage[4096];
-// s_sleep units (64 cycles each) the tile copy waves wait after a barrier, so
-// that the output waves' stores enter the memory pipeline ahead of the copies.
+// s_sleep units (64 cycles each) the copy waves wait after a barrier, so that
+// the output waves' stores enter the memory pipeline ahead of the copies.
 #ifndef SCAN_COPY_DELAY
 #define SCAN_COPY_DELAY 2
 #endif
 
-// Token row blocks of P and of the outputs that copy wave CW owns:
+// Token row blocks of P and of the outputs that output wave CW owns:
 // copy_rows(CW, 0..1) (tile_index.hpp), five 16 x 16 tiles of P each.
 template <int CW> __device__ constexpr int own_rt(int a) { return copy_rows(CW, a); }
 
-// What a copy wave keeps from one phase to the next for a chunk's outputs.
+// What an output wave keeps from one phase to the next for a chunk's outputs.
 struct OutOperands {
   Frag<bf16_t> q[2][4];  // q rows of its two row blocks, [block][contraction block]
   Frag<bf16_t> p[2][2];  // P fragments of those rows (row t, contraction i)
   float gam[2];          // gamma_t of this lane's token (16 rt + lane mod 16) in each block
 };
 
-// Copy wave CW's rows of P = Gamma . (Q K^T) (i <= t) for the chunk staged at
+// Output wave CW's rows of P = Gamma . (Q K^T) (i <= t) for the chunk staged at
 // `st`.  The tile K_r Q_rt^T leaves, in accumulator layout, the values
 // P[16 rt + lane mod 16][16 r + 4 (lane / 16) + e] -- half of the P fragment
 // (rt, r / 2) -- so P stays in registers.  `between` runs after the operand
@@ -645,7 +645,7 @@ __global__ __launch_bounds__(64 * (NCH + 4)) void scan_kernel_staged(ScanArgs<bf
   if (n_chunks > 0) read_operands(scan_stage0);
 
   // One chunk: the state chain from the operands read after the previous
-  // barrier, the chunk-start state and U handed to the copy waves through
+  // barrier, the chunk-start state and U handed to the output waves through
   // exchange buffer `ex_mem`, K^T read from the stage during the chain.  The
   // barrier follows the state update (after it the copy waves may reuse this
   // chunk's stage); then the next chunk's operands are read.
