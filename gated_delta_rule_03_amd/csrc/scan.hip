@@ -186,20 +186,21 @@ __global__ __launch_bounds__(64) void scan_kernel(ScanArgs<T> a) {
 // ---------------------------------------------------------------------------
 // Pipelined path: bf16, d_k = 128, d_v a multiple of 32.
 //
-// A block of NCH + 4 waves owns 16 NCH state columns of one unit.  Waves
+// A block of NCH + 6 waves owns 16 NCH state columns of one unit.  Waves
 // 0 .. NCH - 1 run the state chain (16 columns each); waves NCH and NCH + 1
-// form P and compute the outputs; waves NCH + 2 and NCH + 3 copy operands.
+// form P and compute the outputs; waves NCH + 2 .. NCH + 5 copy operands.
 // A chunk's operands -- its k and q rows (swizzled row tiles), the T
 // fragments and gates of its workspace entry, and its 64 x 16 NCH block of v
 // -- are copied into one of three LDS stages with buffer/global loads
 // straight to LDS, two chunks ahead of the chunk being computed.  The copy
-// waves issue every copy (one the k tile, T fragments 0, 2, 4 and the gate
-// block, the other the q tile and T fragments 5, 6, 7; each half of the v
-// block, with the nontemporal hint: v is read once, and its lines should
-// leave the L2 before the k and q lines that the unit's other column blocks
-// still read).  A copy moves 1 KiB and the memory pipeline accepts one only
-// every few dozen cycles; the copy waves share SIMDs with the chain waves
-// but issue no arithmetic, so no wave that computes waits to issue a copy.
+// waves issue every copy: each half of the k or q tile, and copy wave 0 T
+// fragments 0, 2, 4, the gate block and half the v block, copy wave 1 T
+// fragments 5, 6, 7 and the other half (v with the nontemporal hint: it is
+// read once, and its lines should leave the L2 before the k and q lines that
+// the unit's other column blocks still read).  A copy moves 1 KiB and
+// one wave gets one accepted only every few dozen cycles, so four waves
+// issue them; they share SIMDs with the other waves but issue no
+// arithmetic, so no wave that computes waits to issue a copy.
 //
 // The chain waves run the state chain only (Y = K S, U = T (V - gamma Y), the
 // state update) and issue no memory instruction.  Each chain wave leaves the
@@ -231,10 +232,10 @@ constexpr int kStBytes = 44032;
 constexpr int kExS = 0, kExU = 4096, kExWave = 6144;
 constexpr int kExBytes = 2 * kExWave;
 typedef unsigned u32x2_t __attribute__((ext_vector_type(2)));
-// k (or q) tile copies per stage.  A copy wave issues nothing but copies,
-// and loads complete in issue order, so waiting until at most one stage's
-// copies are outstanding completes every earlier stage.
-constexpr int kStageLoadsCopy = 16;
+// k (or q) tile copies per stage and copy wave.  A copy wave issues nothing
+// but copies, and loads complete in issue order, so waiting until at most
+// one stage's copies are outstanding completes every earlier stage.
+constexpr int kStageLoadsCopy = 8;
 
 // Three stages and two exchange buffers as distinct LDS objects: with the
 // chunk loop unrolled by six, every access names its buffer at compile time.
@@ -322,10 +323,11 @@ __device__ __forceinline__ void scan_form_p(const lds_t *st, const int (&kq_off)
   }
 }
 
-// ROLE 1: output wave CW forms its rows of P and computes their outputs for
-// the block's NCH column groups; ROLE 2: copy wave CW issues the k (CW = 0)
-// or q (CW = 1) tile copies, half the T fragments (and, CW = 0, the gate
-// block) and half the v block of each stage.
+// ROLE 1: output wave CW (0, 1) forms its rows of P and computes their
+// outputs for the block's NCH column groups; ROLE 2: copy wave CW (0 .. 3)
+// issues half the k (CW even) or q (CW odd) tile copies of each stage; copy
+// waves 0 and 1 also half the T fragments and half the v block each, and copy
+// wave 0 the gate block.
 template <int CW, int ROLE, int NCH>
 __device__ __forceinline__ void scan_copy_waves(const ScanArgs<bf16_t> &a, int lane, int h, int hq, int cb,
                                                 int start, int end, int c_first, int n_chunks) {
@@ -336,7 +338,7 @@ __device__ __forceinline__ void scan_copy_waves(const ScanArgs<bf16_t> &a, int l
   const int64_t qk_stride = int64_t(a.H_qk) * 128;
   const int64_t v_stride = int64_t(a.H_v) * a.d_v;
   const uint32_t kq_row_bytes = uint32_t(2 * qk_stride);
-  const char *kq_src = reinterpret_cast<const char *>(CW == 0 ? a.k : a.q) + int64_t(hq) * 256;
+  const char *kq_src = reinterpret_cast<const char *>((CW & 1) == 0 ? a.k : a.q) + int64_t(hq) * 256;
   // Per-lane byte offsets of every copy of a full chunk (tile_index.hpp),
   // relative to the chunk's first row.  The k / q and v copies go through a
   // buffer resource whose size ends at the chunk's last row, so rows past a
@@ -346,17 +348,20 @@ __device__ __forceinline__ void scan_copy_waves(const ScanArgs<bf16_t> &a, int l
 #pragma unroll
   for (int i = 0; i < 16; ++i) kq_voff[i] = uint32_t(rowtile_copy_src(i, lane, 64, qk_stride));
 
-  // A stage's k (or q) tile copies in two halves: copies 0-7 and 8-15.
+  // A copy wave's share of a stage's k (or q) tile, 32 rows (copies
+  // 8 (CW / 2) .. + 7), in two halves of four copies.
   auto stage_part = [&](int part, int cc, char *base_mem) {
     const int tok0 = start + cc * C;
     const int len = min(C, end - tok0);
     const i32x4_t kq_res = buffer_rsrc(kq_src + int64_t(tok0) * kq_row_bytes, rowtile_valid_bytes(len, kq_row_bytes));
-    lds_t *const tile = lds_ptr(base_mem) + (CW == 0 ? kStK : kStQ);
+    lds_t *const tile = lds_ptr(base_mem) + ((CW & 1) == 0 ? kStK : kStQ);
 #pragma unroll
-    for (int i = 8 * part; i < 8 * part + 8; ++i) dma16_buf(kq_res, kq_voff[i], tile + 1024 * i);
+    for (int i = 8 * (CW >> 1) + 4 * part; i < 8 * (CW >> 1) + 4 * part + 4; ++i)
+      dma16_buf(kq_res, kq_voff[i], tile + 1024 * i);
   };
-  // The rest of a stage: copy wave 0 T fragments 0, 2, 4 and the gate block,
-  // copy wave 1 T fragments 5, 6, 7; each half of the v rows.
+  // The rest of a stage: copy wave 0 T fragments 0, 2, 4, the gate block
+  // and v rows of the first half, copy wave 1 T fragments 5, 6, 7 and the
+  // second half (copy waves 2 and 3 issue tile copies only).
   const int64_t ebytes = kStagedEntryBytes;
   const char *const v_src = reinterpret_cast<const char *>(a.v) + (int64_t(h) * a.d_v + W * cb) * 2;
   const uint32_t v_row_bytes = uint32_t(2 * v_stride);
@@ -364,12 +369,14 @@ __device__ __forceinline__ void scan_copy_waves(const ScanArgs<bf16_t> &a, int l
   uint32_t v_voff[kVCopies];
 #pragma unroll
   for (int i = 0; i < kVCopies; ++i)
-    v_voff[i] = uint32_t(NCH == 2 ? vblock_copy_src(2 * CW + i, lane, 64, v_stride)
-                                  : vblock16_copy_src(CW, lane, 64, v_stride));
+    v_voff[i] = CW >= 2 ? 0u
+                        : uint32_t(NCH == 2 ? vblock_copy_src(2 * CW + i, lane, 64, v_stride)
+                                            : vblock16_copy_src(CW, lane, 64, v_stride));
   auto stage_rest = [&](int cc, char *base_mem) {
     const int tok0 = start + cc * C;
     const int len = min(C, end - tok0);
     lds_t *const base = lds_ptr(base_mem);
+    if (CW >= 2) return;
     const char *entry = a.entries + (int64_t(c_first + cc) * a.H_v + h) * ebytes;
 #pragma unroll
     for (int i = 0; i < 3; ++i) {
@@ -389,7 +396,7 @@ __device__ __forceinline__ void scan_copy_waves(const ScanArgs<bf16_t> &a, int l
     stage_part(0, cc, base_mem);
     stage_part(1, cc, base_mem);
   };
-  constexpr int kLoads = kStageLoadsCopy + 3 + (CW == 0 ? 1 : 0) + kVCopies;
+  constexpr int kLoads = kStageLoadsCopy + (CW >= 2 ? 0 : 3 + (CW == 0 ? 1 : 0) + kVCopies);
   auto wait_all_but_newest_stage = [&]() { wait_vmem_upto<kLoads>(); };
   int kq_off[4][2];
 #pragma unroll
@@ -529,12 +536,12 @@ __device__ __forceinline__ void scan_copy_waves(const ScanArgs<bf16_t> &a, int l
 }
 
 // NCH chain waves (one per 16-column group; a block of 16 NCH columns), then
-// two output waves, which form P and the outputs, and two copy waves, which
+// two output waves, which form P and the outputs, and four copy waves, which
 // issue every copy of a stage.  One chain wave per block doubles the blocks
 // of a problem with few units (a long single sequence) at the same per-block
 // traffic.
 template <int NCH>
-__global__ __launch_bounds__(64 * (NCH + 4)) void scan_kernel_staged(ScanArgs<bf16_t> a) {
+__global__ __launch_bounds__(64 * (NCH + 6)) void scan_kernel_staged(ScanArgs<bf16_t> a) {
   constexpr int W = 16 * NCH;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -570,6 +577,14 @@ __global__ __launch_bounds__(64 * (NCH + 4)) void scan_kernel_staged(ScanArgs<bf
   }
   if (wave == NCH + 3) {
     scan_copy_waves<1, 2, NCH>(a, lane, h, hq, cb, start, end, c_first, n_chunks);
+    return;
+  }
+  if (wave == NCH + 4) {
+    scan_copy_waves<2, 2, NCH>(a, lane, h, hq, cb, start, end, c_first, n_chunks);
+    return;
+  }
+  if (wave == NCH + 5) {
+    scan_copy_waves<3, 2, NCH>(a, lane, h, hq, cb, start, end, c_first, n_chunks);
     return;
   }
 
@@ -768,10 +783,10 @@ hipError_t launch_scan(const Problem &p, const Workspace &ws, hipStream_t st) {
   const int64_t blocks = units8 * (p.d_v / width);
   if (blocks == 0) return hipSuccess;
   if (staged && narrow) {
-    hipLaunchKernelGGL(scan_kernel_staged<1>, dim3(unsigned(blocks)), dim3(64 * 5), 0, st,
+    hipLaunchKernelGGL(scan_kernel_staged<1>, dim3(unsigned(blocks)), dim3(64 * 7), 0, st,
                        scan_args<bf16_t>(p, ws, width));
   } else if (staged) {
-    hipLaunchKernelGGL(scan_kernel_staged<2>, dim3(unsigned(blocks)), dim3(64 * 6), 0, st,
+    hipLaunchKernelGGL(scan_kernel_staged<2>, dim3(unsigned(blocks)), dim3(64 * 8), 0, st,
                        scan_args<bf16_t>(p, ws, width));
   } else if (p.dtype == 1) {
     hipLaunchKernelGGL(scan_kernel<bf16_t>, dim3(unsigned(blocks)), dim3(64), 0, st,
