@@ -30,7 +30,8 @@ _LIB_PATH = os.path.join(_HERE, "libgdn.so")
 _lib: Optional[ctypes.CDLL] = None
 
 EXPORTS = ["gdn_version", "gdn_status_string", "gdn_recurrent_fwd",
-           "gdn_chunk_fwd_workspace_bytes", "gdn_chunk_fwd", "gdn_decode_step"]
+           "gdn_chunk_fwd_workspace_bytes", "gdn_chunk_fwd", "gdn_decode_step",
+           "gdn_block_prologue", "gdn_block_epilogue"]
 
 
 class GDNError(RuntimeError):
@@ -69,6 +70,12 @@ def load() -> ctypes.CDLL:
     lib.gdn_chunk_fwd.restype = i32
     lib.gdn_decode_step.argtypes = [i32] * 6 + [vp, vp, vp, fp, fp, fp, vp, vp]
     lib.gdn_decode_step.restype = i32
+    f32 = ctypes.c_float
+    lib.gdn_block_prologue.argtypes = ([i32] * 7 + [vp] * 3 + [fp] * 10 + [f32, f32, vp, i32]
+                                       + [vp] * 3 + [fp, fp, vp])
+    lib.gdn_block_prologue.restype = i32
+    lib.gdn_block_epilogue.argtypes = [i32] * 5 + [vp, vp, fp, f32, vp, vp]
+    lib.gdn_block_epilogue.restype = i32
     _lib = lib
     return lib
 
@@ -232,3 +239,76 @@ def decode_step(q, k, v, alpha, beta, state, *, o=None, stream=None):
     if st != GDN_SUCCESS:
         raise GDNError(st, "gdn_decode_step")
     return o
+
+
+def block_prologue(q_raw, k_raw, v_raw, conv_q, conv_k, conv_v, a_raw, b_raw, log_A, *,
+                   conv_q_bias=None, conv_k_bias=None, conv_v_bias=None, v_norm_weight=None,
+                   eps: float = 1e-6, q_scale: float = 1.0, cu_seqlens=None, out=None, stream=None):
+    """The GDN block's steps before the recurrence (causal conv + SiLU, unit q/k,
+    RMS-normalised v, gate maps) in one kernel.  Returns (q, k, v, alpha, beta),
+    the inputs of ``chunk_fwd``; ``out`` may supply those five tensors."""
+    torch = _torch()
+    if q_raw.dim() != 4 or v_raw.dim() != 4:
+        raise ValueError("q_raw, k_raw, v_raw must be [B, T, H, d]")
+    B, T, H_qk, d_k = q_raw.shape
+    H_v, d_v = v_raw.shape[2], v_raw.shape[3]
+    dev, dt = q_raw.device, q_raw.dtype
+    f32 = torch.float32
+    _check(q_raw, "q_raw", (B, T, H_qk, d_k), device=dev)
+    _check(k_raw, "k_raw", (B, T, H_qk, d_k), dt, dev)
+    _check(v_raw, "v_raw", (B, T, H_v, d_v), dt, dev)
+    _check(conv_q, "conv_q", (H_qk * d_k, 4), f32, dev)
+    _check(conv_k, "conv_k", (H_qk * d_k, 4), f32, dev)
+    _check(conv_v, "conv_v", (H_v * d_v, 4), f32, dev)
+    for t, n, c in ((conv_q_bias, "conv_q_bias", H_qk * d_k), (conv_k_bias, "conv_k_bias", H_qk * d_k),
+                    (conv_v_bias, "conv_v_bias", H_v * d_v), (v_norm_weight, "v_norm_weight", d_v)):
+        if t is not None:
+            _check(t, n, (c,), f32, dev)
+    _check(a_raw, "a_raw", (B, T, H_v), f32, dev)
+    _check(b_raw, "b_raw", (B, T, H_v), f32, dev)
+    _check(log_A, "log_A", (H_v,), f32, dev)
+    n_seqs = 0
+    if cu_seqlens is not None:
+        if B != 1:
+            raise ValueError("a packed batch (cu_seqlens) needs B == 1")
+        _check(cu_seqlens, "cu_seqlens", (cu_seqlens.numel(),), torch.int32, dev)
+        n_seqs = cu_seqlens.numel() - 1
+    if out is None:
+        out = (torch.empty_like(q_raw), torch.empty_like(k_raw), torch.empty_like(v_raw),
+               torch.empty((B, T, H_v), dtype=f32, device=dev), torch.empty((B, T, H_v), dtype=f32, device=dev))
+    q, k, v, alpha, beta = out
+    for t, n, ref in ((q, "q", q_raw), (k, "k", k_raw), (v, "v", v_raw)):
+        _check(t, n, tuple(ref.shape), dt, dev)
+    _check(alpha, "alpha", (B, T, H_v), f32, dev)
+    _check(beta, "beta", (B, T, H_v), f32, dev)
+    st = load().gdn_block_prologue(B, T, H_qk, H_v, d_k, d_v, _dtype_code(q_raw), _ptr(q_raw), _ptr(k_raw),
+                                   _ptr(v_raw), _ptr(conv_q), _ptr(conv_k), _ptr(conv_v), _ptr(conv_q_bias),
+                                   _ptr(conv_k_bias), _ptr(conv_v_bias), _ptr(a_raw), _ptr(b_raw), _ptr(log_A),
+                                   _ptr(v_norm_weight), float(eps), float(q_scale), _ptr(cu_seqlens), n_seqs,
+                                   _ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(beta), _stream(stream))
+    if st != GDN_SUCCESS:
+        raise GDNError(st, "gdn_block_prologue")
+    return q, k, v, alpha, beta
+
+
+def block_epilogue(o, g, *, o_norm_weight=None, eps: float = 1e-6, y=None, stream=None):
+    """The GDN block's steps after the recurrence: RMS normalisation of each
+    head's output times SiLU of the output gate's projection ``g``.  Returns y."""
+    torch = _torch()
+    if o.dim() != 4:
+        raise ValueError("o must be [B, T, H_v, d_v]")
+    B, T, H_v, d_v = o.shape
+    dev = o.device
+    _check(o, "o", (B, T, H_v, d_v), device=dev)
+    _check(g, "g", (B, T, H_v, d_v), o.dtype, dev)
+    if o_norm_weight is not None:
+        _check(o_norm_weight, "o_norm_weight", (d_v,), torch.float32, dev)
+    if y is None:
+        y = torch.empty_like(o)
+    else:
+        _check(y, "y", (B, T, H_v, d_v), o.dtype, dev)
+    st = load().gdn_block_epilogue(B, T, H_v, d_v, _dtype_code(o), _ptr(o), _ptr(g), _ptr(o_norm_weight),
+                                   float(eps), _ptr(y), _stream(stream))
+    if st != GDN_SUCCESS:
+        raise GDNError(st, "gdn_block_epilogue")
+    return y

@@ -2,6 +2,7 @@
 // The operation and the contract of every entry point are in include/gdn.h.
 #include "../../include/gdn.h"
 
+#include <cmath>
 #include <limits>
 
 #include "launch.hpp"
@@ -190,6 +191,82 @@ int32_t gdn_decode_step(int32_t B, int32_t H_qk, int32_t H_v, int32_t d_k, int32
   p.o = o;
   p.n_seqs = B;
   return status_of(launch_decode(p, state, static_cast<hipStream_t>(stream)));
+}
+
+int32_t gdn_block_prologue(int32_t B, int32_t T, int32_t H_qk, int32_t H_v, int32_t d_k,
+                           int32_t d_v, int32_t dtype, const void *q_raw, const void *k_raw,
+                           const void *v_raw, const float *conv_q, const float *conv_k,
+                           const float *conv_v, const float *conv_q_bias,
+                           const float *conv_k_bias, const float *conv_v_bias,
+                           const float *a_raw, const float *b_raw, const float *log_A,
+                           const float *v_norm_weight, float eps, float q_scale,
+                           const int32_t *cu_seqlens, int32_t n_seqs, void *q, void *k, void *v,
+                           float *alpha, float *beta, void *stream) {
+  int32_t st = check_shapes(B, T, H_qk, H_v, d_k, d_v, dtype);
+  if (st != GDN_SUCCESS) return st;
+  if (2 * int64_t(H_qk) + H_v > 65535) return GDN_ERROR_NOT_SUPPORTED;
+  if (!(eps >= 0.0f) || !std::isfinite(eps) || !std::isfinite(q_scale)) return GDN_ERROR_INVALID_VALUE;
+  const int64_t tokens = int64_t(B) * T;
+  if (cu_seqlens) {
+    if (B != 1 || n_seqs < 0 || (tokens > 0 && n_seqs < 1)) return GDN_ERROR_INVALID_VALUE;
+  } else if (n_seqs != 0 && n_seqs != B) {
+    return GDN_ERROR_INVALID_VALUE;
+  }
+  if (tokens > 0 && (!q_raw || !k_raw || !v_raw || !conv_q || !conv_k || !conv_v || !a_raw || !b_raw ||
+                     !log_A || !q || !k || !v || !alpha || !beta))
+    return GDN_ERROR_INVALID_VALUE;
+  BlockProblem p{};
+  p.B = B;
+  p.T = T;
+  p.H_qk = H_qk;
+  p.H_v = H_v;
+  p.d_k = d_k;
+  p.d_v = d_v;
+  p.dtype = dtype;
+  p.raw[0] = q_raw;
+  p.raw[1] = k_raw;
+  p.raw[2] = v_raw;
+  p.out[0] = q;
+  p.out[1] = k;
+  p.out[2] = v;
+  p.conv[0] = conv_q;
+  p.conv[1] = conv_k;
+  p.conv[2] = conv_v;
+  p.bias[0] = conv_q_bias;
+  p.bias[1] = conv_k_bias;
+  p.bias[2] = conv_v_bias;
+  p.a_raw = a_raw;
+  p.b_raw = b_raw;
+  p.log_A = log_A;
+  p.norm_w = v_norm_weight;
+  p.alpha = alpha;
+  p.beta = beta;
+  p.cu_seqlens = cu_seqlens;
+  p.n_seqs = cu_seqlens ? n_seqs : B;
+  p.eps = eps;
+  p.q_scale = q_scale;
+  return status_of(launch_block_prologue(p, static_cast<hipStream_t>(stream)));
+}
+
+int32_t gdn_block_epilogue(int32_t B, int32_t T, int32_t H_v, int32_t d_v, int32_t dtype,
+                           const void *o, const void *g, const float *o_norm_weight, float eps,
+                           void *y, void *stream) {
+  int32_t st = check_shapes(B, T, 1, H_v, 16, d_v, dtype);
+  if (st != GDN_SUCCESS) return st;
+  if (!(eps >= 0.0f) || !std::isfinite(eps)) return GDN_ERROR_INVALID_VALUE;
+  if (int64_t(B) * T > 0 && (!o || !g || !y)) return GDN_ERROR_INVALID_VALUE;
+  BlockProblem p{};
+  p.B = B;
+  p.T = T;
+  p.H_v = H_v;
+  p.d_v = d_v;
+  p.dtype = dtype;
+  p.raw[0] = o;
+  p.raw[1] = g;
+  p.out[0] = y;
+  p.norm_w = o_norm_weight;
+  p.eps = eps;
+  return status_of(launch_block_epilogue(p, static_cast<hipStream_t>(stream)));
 }
 
 }  // extern "C"

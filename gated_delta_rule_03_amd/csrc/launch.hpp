@@ -61,6 +61,23 @@ hipError_t launch_chunk_offsets(const Problem &p, const Workspace &ws, hipStream
 hipError_t launch_prep(const Problem &p, const Workspace &ws, hipStream_t st);
 hipError_t launch_scan(const Problem &p, const Workspace &ws, hipStream_t st);
 hipError_t launch_recurrent(const Problem &p, hipStream_t st);
+
+// The block prologue and epilogue (block.hip).  Prologue: raw = q_raw, k_raw,
+// v_raw and out = q, k, v; epilogue: raw[0] = o, raw[1] = the output gate's
+// projection, out[0] = y.
+struct BlockProblem {
+  int32_t B, T, H_qk, H_v, d_k, d_v, dtype;
+  const void *raw[3];
+  void *out[3];
+  const float *conv[3], *bias[3];
+  const float *a_raw, *b_raw, *log_A, *norm_w;
+  float *alpha, *beta;
+  const int32_t *cu_seqlens;
+  int32_t n_seqs;
+  float eps, q_scale;
+};
+hipError_t launch_block_prologue(const BlockProblem &p, hipStream_t st);
+hipError_t launch_block_epilogue(const BlockProblem &p, hipStream_t st);
 hipError_t launch_decode(const Problem &p, float *state, hipStream_t st);
 
 SeqGeom make_geom(const Problem &p, const Workspace *ws);

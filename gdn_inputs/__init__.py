@@ -40,7 +40,7 @@ import math
 import os
 from concurrent.futures import ThreadPoolExecutor
 from dataclasses import dataclass, field
-from typing import List, Optional
+from typing import List, Optional, Sequence
 
 import numpy as np
 
@@ -276,3 +276,33 @@ def random_state(shape, seed: int, scale: float = 1.0) -> np.ndarray:
     """A seeded float32 N(0, scale^2) array (for initial states h0)."""
     rng = np.random.default_rng(np.random.SeedSequence(seed))
     return (scale * rng.standard_normal(shape, dtype=np.float32)).astype(np.float32)
+
+
+def block_inputs(B: int, T: int, H_qk: int, H_v: int, d_k: int, d_v: int, dtype: str, seed: int,
+                 lengths: Optional[Sequence[int]] = None) -> dict:
+    """Seeded raw inputs of a GDN block's prologue and epilogue: the q, k, v and
+    output-gate projections (N(0, 1), stored as ``dtype``), depthwise
+    convolution taps (N(0, 0.5^2)) and biases (N(0, 0.1^2)), gate projections
+    a, b (N(0, 1)), log A = log U(0.5, 16) per value head, and RMS-norm
+    weights 1 + N(0, 0.1^2).  With ``lengths`` the batch is packed (B == 1,
+    T = sum of lengths) and ``cu_seqlens`` is included."""
+    if lengths is not None:
+        B, T = 1, int(sum(lengths))
+    rng = np.random.default_rng(np.random.SeedSequence(seed))
+    f = lambda *shape: rng.standard_normal(shape, dtype=np.float32)
+    out = {
+        "q_raw": _store(f(B, T, H_qk, d_k), dtype), "k_raw": _store(f(B, T, H_qk, d_k), dtype),
+        "v_raw": _store(f(B, T, H_v, d_v), dtype), "g_raw": _store(f(B, T, H_v, d_v), dtype),
+        "conv_q": 0.5 * f(H_qk * d_k, 4), "conv_k": 0.5 * f(H_qk * d_k, 4), "conv_v": 0.5 * f(H_v * d_v, 4),
+        "conv_q_bias": 0.1 * f(H_qk * d_k), "conv_k_bias": 0.1 * f(H_qk * d_k),
+        "conv_v_bias": 0.1 * f(H_v * d_v),
+        "a_raw": f(B, T, H_v), "b_raw": f(B, T, H_v),
+        "log_A": np.log(rng.uniform(0.5, 16.0, H_v)).astype(np.float32),
+        "v_norm": (1.0 + 0.1 * f(d_v)).astype(np.float32), "o_norm": (1.0 + 0.1 * f(d_v)).astype(np.float32),
+        "cu_seqlens": None, "B": B, "T": T,
+    }
+    if lengths is not None:
+        cu = np.zeros(len(lengths) + 1, dtype=np.int32)
+        cu[1:] = np.cumsum(lengths)
+        out["cu_seqlens"] = cu
+    return out

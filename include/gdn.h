@@ -141,6 +141,56 @@ int32_t gdn_decode_step(int32_t B, int32_t H_qk, int32_t H_v, int32_t d_k, int32
                         const float *alpha, const float *beta, float *state, void *o,
                         void *stream);
 
+/*
+ * gdn_block_prologue -- the GDN block's steps between the projections and
+ * the recurrence, fused ("Linear attention", section "A naive PyTorch
+ * implementation"):
+ *   x <- SiLU(bias + sum_j w[c][j] x[t - 3 + j])   per channel c of q, k and v
+ *       (a causal depthwise convolution of width 4; tokens before the start
+ *       of t's sequence count as zeros);
+ *   q <- q_scale * q / max(|q|, 1e-12),  k <- k / max(|k|, 1e-12)   per head;
+ *   v <- v / sqrt(mean(v^2) + eps) * v_norm_weight                 per head;
+ *   alpha = exp(-exp(log_A[h]) * log(1 + exp(a_raw))),  beta = 1 / (1 + exp(-b_raw)).
+ *
+ *   q_raw, k_raw   [B, T, H_qk, d_k];  v_raw [B, T, H_v, d_v]   (dtype; the
+ *                  projections of the block's input)
+ *   conv_q, conv_k [H_qk * d_k, 4];  conv_v [H_v * d_v, 4]      float32 taps of
+ *                  each channel, oldest token first (channel = head * d + i)
+ *   conv_*_bias    [H * d] float32, or NULL for none
+ *   a_raw, b_raw   [B, T, H_v] float32 gate projections;  log_A [H_v] float32
+ *   v_norm_weight  [d_v] float32, or NULL for ones;  eps >= 0;  q_scale finite
+ *                  (1 on the page; 1/sqrt(d_k) folds the attention scale in)
+ *   cu_seqlens, n_seqs   as gdn_recurrent_fwd (a packed batch needs n_seqs >= 1
+ *                  when T > 0); the convolution restarts at every sequence
+ *   q, k, v        outputs shaped like q_raw, k_raw, v_raw (dtype);
+ *   alpha, beta    outputs [B, T, H_v] float32 -- the inputs of gdn_chunk_fwd.
+ * Outputs must not alias inputs.  Errors as gdn_recurrent_fwd.
+ */
+int32_t gdn_block_prologue(int32_t B, int32_t T, int32_t H_qk, int32_t H_v, int32_t d_k,
+                           int32_t d_v, int32_t dtype, const void *q_raw, const void *k_raw,
+                           const void *v_raw, const float *conv_q, const float *conv_k,
+                           const float *conv_v, const float *conv_q_bias,
+                           const float *conv_k_bias, const float *conv_v_bias,
+                           const float *a_raw, const float *b_raw, const float *log_A,
+                           const float *v_norm_weight, float eps, float q_scale,
+                           const int32_t *cu_seqlens, int32_t n_seqs, void *q, void *k, void *v,
+                           float *alpha, float *beta, void *stream);
+
+/*
+ * gdn_block_epilogue -- the GDN block's steps after the recurrence, fused
+ * ("Linear attention", section "A naive PyTorch implementation"): each
+ * head's output RMS-normalised, times a weight, times SiLU of the output
+ * gate's projection:
+ *   y = o / sqrt(mean(o^2) + eps) * o_norm_weight * g / (1 + exp(-g)).
+ *
+ *   o, g, y        [B, T, H_v, d_v] (dtype); g is the output gate's projection
+ *   o_norm_weight  [d_v] float32, or NULL for ones;  eps >= 0
+ * y must not alias o or g.  Errors as gdn_recurrent_fwd.
+ */
+int32_t gdn_block_epilogue(int32_t B, int32_t T, int32_t H_v, int32_t d_v, int32_t dtype,
+                           const void *o, const void *g, const float *o_norm_weight, float eps,
+                           void *y, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -95,6 +95,31 @@ def test_decode_argument_errors(lib):
     assert lib.gdn_decode_step(1, 2, 3, 64, 64, 0, p, p, p, p, p, p, p, None) == 2
 
 
+def prologue(lib, B=1, T=8, H_qk=1, H_v=1, d_k=64, d_v=64, dtype=0, ptrs=True, cu=None, n=0, eps=1e-6,
+             q_scale=1.0):
+    p = ctypes.c_void_p(0x1000) if ptrs else None
+    return lib.gdn_block_prologue(B, T, H_qk, H_v, d_k, d_v, dtype, p, p, p, p, p, p, None, None, None, p, p, p,
+                                  None, eps, q_scale, cu, n, p, p, p, p, p, None)
+
+
+def test_block_argument_errors(lib):
+    p = ctypes.c_void_p(0x1000)
+    assert prologue(lib, d_k=48) == 2
+    assert prologue(lib, H_qk=3, H_v=4) == 2
+    assert prologue(lib, dtype=5) == 2
+    assert prologue(lib, ptrs=False) == 1
+    assert prologue(lib, eps=-1.0) == 1
+    assert prologue(lib, eps=float("nan")) == 1
+    assert prologue(lib, q_scale=float("inf")) == 1
+    assert prologue(lib, B=2, cu=p, n=2) == 1      # a packed batch has B == 1
+    assert prologue(lib, cu=p, n=0) == 1           # ... and at least one sequence
+    assert prologue(lib, H_qk=30000, H_v=30000) == 2  # grid rows 2 H_qk + H_v
+    assert lib.gdn_block_epilogue(1, 8, 1, 48, 0, p, p, None, 1e-6, p, None) == 2
+    assert lib.gdn_block_epilogue(1, 8, 1, 64, 0, p, None, None, 1e-6, p, None) == 1
+    assert lib.gdn_block_epilogue(1, 8, 1, 64, 0, p, p, None, -1.0, p, None) == 1
+    assert lib.gdn_block_epilogue(0, 8, 1, 64, 0, None, None, None, 1e-6, None, None) == 0  # nothing to do
+
+
 def _gpu_visible():
     try:
         import torch
@@ -114,3 +139,5 @@ def test_host_path_reaches_launch_without_gpu(lib):
     ws = ctypes.c_void_p(0x100000)
     assert lib.gdn_chunk_fwd(*base, 64, ws, 1 << 30, None) == 4
     assert lib.gdn_decode_step(2, 1, 1, 64, 64, 1, p, p, p, p, p, p, p, None) == 4
+    assert prologue(lib) == 4
+    assert lib.gdn_block_epilogue(1, 8, 1, 64, 0, p, p, None, 1e-6, p, None) == 4
