@@ -32,6 +32,12 @@ the device from a seed with the generator's shapes and distributions (the
 kernels' time does not depend on the values; the parity tests run these
 workloads on the generator's exact inputs).
 
+``block`` times the GDN block's prologue and epilogue kernels and a whole
+block (prologue, chunked forward, epilogue) on the prefill shape with bf16
+projections drawn on the device, and gives each kernel's algorithmic bytes
+(every input read once, every output written once) as a fraction of HBM
+peak.
+
 ``roofline.traffic`` is the decode kernel's HBM bytes per launch from the
 rocprofv3 FETCH_SIZE and WRITE_SIZE counters (profiles/decode_kernel.traffic.json),
 each scaled by what the counter reads for a plain 1 GiB read + 1 GiB write
@@ -182,6 +188,69 @@ def extra_workloads(args, gi, gdn, torch, dev, stream, evict):
     return out
 
 
+def block_workload(args, gdn, torch, dev, stream, evict):
+    """The block prologue and epilogue kernels, and a whole block (prologue,
+    chunked forward, epilogue), on the prefill shape with bf16 projections."""
+    B, T, H, D = 4, 4096, 16, 128
+    g = torch.Generator(device=dev)
+    g.manual_seed(77)
+    rn = lambda *shape: torch.randn(shape, generator=g, device=dev)
+    q_raw, k_raw, v_raw, g_raw = (rn(B, T, H, D).bfloat16() for _ in range(4))
+    conv = [0.5 * rn(H * D, 4) for _ in range(3)]
+    bias = [0.1 * rn(H * D) for _ in range(3)]
+    a_raw, b_raw = rn(B, T, H), rn(B, T, H)
+    log_A = torch.log(torch.rand(H, generator=g, device=dev) * 15.5 + 0.5)
+    nw = 1.0 + 0.1 * rn(D)
+    outs = (torch.empty_like(q_raw), torch.empty_like(k_raw), torch.empty_like(v_raw),
+            torch.empty((B, T, H), device=dev), torch.empty((B, T, H), device=dev))
+    o = torch.empty_like(v_raw)
+    y = torch.empty_like(v_raw)
+    hT = torch.empty((B, H, D, D), dtype=torch.float32, device=dev)
+    ws = torch.empty(gdn.chunk_fwd_workspace_bytes(B, T, H, H, D, D, gdn.GDN_BF16, 64, 0), dtype=torch.uint8,
+                     device=dev)
+
+    def prologue():
+        gdn.block_prologue(q_raw, k_raw, v_raw, *conv, a_raw, b_raw, log_A, conv_q_bias=bias[0],
+                           conv_k_bias=bias[1], conv_v_bias=bias[2], v_norm_weight=nw, q_scale=D ** -0.5,
+                           out=outs, stream=stream)
+
+    def epilogue():
+        gdn.block_epilogue(o, g_raw, o_norm_weight=nw, y=y, stream=stream)
+
+    def whole():
+        prologue()
+        q, k, v, al, be = outs
+        gdn.chunk_fwd(q, k, v, al, be, chunk=64, o=o, hT=hT, workspace=ws, stream=stream)
+        epilogue()
+
+    def timed(fn):
+        ms = []
+        for i in range(2 + max(3, args.steps // 2)):
+            evict(5)
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            fn()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            if i >= 2:
+                ms.append(e0.elapsed_time(e1))
+        return statistics.median(ms) * 1e-3
+
+    tokens = B * T
+    row = H * D * 2  # one token's projections of one tensor, bf16
+    pro_bytes = tokens * (3 * row * 2 + H * 4 * 4)  # q, k, v in and out; a, b in; alpha, beta out
+    epi_bytes = tokens * 3 * row                    # o, g in; y out
+    t_pro, t_epi, t_all = timed(prologue), timed(epilogue), timed(whole)
+    return {"block": {
+        "workload": f"B={B} T={T} H={H} d={D} bf16 projections (q/k/v convolution width 4)",
+        "prologue_us": t_pro * 1e6, "prologue_GBps": pro_bytes / t_pro / 1e9,
+        "prologue_hbm_frac": pro_bytes / t_pro / HBM_PEAK, "prologue_bytes": pro_bytes,
+        "epilogue_us": t_epi * 1e6, "epilogue_GBps": epi_bytes / t_epi / 1e9,
+        "epilogue_hbm_frac": epi_bytes / t_epi / HBM_PEAK, "epilogue_bytes": epi_bytes,
+        "whole_block_us": t_all * 1e6, "whole_block_tokens_per_s": tokens / t_all,
+    }}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -306,6 +375,7 @@ def main():
     extra = {}
     if not args.no_extra:
         extra = extra_workloads(args, gi, gdn, torch, dev, stream, evict)
+        extra.update(block_workload(args, gdn, torch, dev, stream, evict))
 
     tokens = B * T
     units = B * H

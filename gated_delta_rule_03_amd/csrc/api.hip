@@ -204,9 +204,11 @@ int32_t gdn_block_prologue(int32_t B, int32_t T, int32_t H_qk, int32_t H_v, int3
                            float *alpha, float *beta, void *stream) {
   int32_t st = check_shapes(B, T, H_qk, H_v, d_k, d_v, dtype);
   if (st != GDN_SUCCESS) return st;
-  if (2 * int64_t(H_qk) + H_v > 65535) return GDN_ERROR_NOT_SUPPORTED;
   if (!(eps >= 0.0f) || !std::isfinite(eps) || !std::isfinite(q_scale)) return GDN_ERROR_INVALID_VALUE;
   const int64_t tokens = int64_t(B) * T;
+  // one wave per (32 tokens, head) in a one-dimensional grid
+  if ((tokens + kPrologueTokens - 1) / kPrologueTokens > INT32_MAX / (2 * int64_t(H_qk) + H_v))
+    return GDN_ERROR_NOT_SUPPORTED;
   if (cu_seqlens) {
     if (B != 1 || n_seqs < 0 || (tokens > 0 && n_seqs < 1)) return GDN_ERROR_INVALID_VALUE;
   } else if (n_seqs != 0 && n_seqs != B) {

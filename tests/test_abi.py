@@ -113,7 +113,8 @@ def test_block_argument_errors(lib):
     assert prologue(lib, q_scale=float("inf")) == 1
     assert prologue(lib, B=2, cu=p, n=2) == 1      # a packed batch has B == 1
     assert prologue(lib, cu=p, n=0) == 1           # ... and at least one sequence
-    assert prologue(lib, H_qk=30000, H_v=30000) == 2  # grid rows 2 H_qk + H_v
+    # one wave per (32 tokens, head): 2^16 token ranges x 3 * 2^15 heads exceeds a 32-bit grid
+    assert prologue(lib, B=1, T=1 << 21, H_qk=1 << 15, H_v=1 << 15, d_k=16, d_v=16) == 2
     assert lib.gdn_block_epilogue(1, 8, 1, 48, 0, p, p, None, 1e-6, p, None) == 2
     assert lib.gdn_block_epilogue(1, 8, 1, 64, 0, p, None, None, 1e-6, p, None) == 1
     assert lib.gdn_block_epilogue(1, 8, 1, 64, 0, p, p, None, -1.0, p, None) == 1
