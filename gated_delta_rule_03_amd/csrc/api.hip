@@ -60,6 +60,9 @@ static int32_t check_shapes(int32_t B, int32_t T, int32_t H_qk, int32_t H_v, int
   return GDN_SUCCESS;
 }
 
+// Token-major tensors are read and written 16 bytes per lane.
+static bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
+
 // Shape checks plus the tensor pointers every non-empty call needs.
 static int32_t check_common(int32_t B, int32_t T, int32_t H_qk, int32_t H_v, int32_t d_k,
                             int32_t d_v, int32_t dtype, const void *q, const void *k,
@@ -68,6 +71,7 @@ static int32_t check_common(int32_t B, int32_t T, int32_t H_qk, int32_t H_v, int
   if (st != GDN_SUCCESS) return st;
   if (int64_t(B) * T > 0 && (!q || !k || !v || !alpha || !beta || !o))
     return GDN_ERROR_INVALID_VALUE;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o)) return GDN_ERROR_INVALID_VALUE;
   return GDN_SUCCESS;
 }
 
@@ -84,6 +88,7 @@ static int32_t make_problem(int32_t B, int32_t T, int32_t H_qk, int32_t H_v, int
     if (n_seqs != 0 && n_seqs != B) return GDN_ERROR_INVALID_VALUE;
     n_seqs = B;
   }
+  if (!aligned16(h0) || !aligned16(hT)) return GDN_ERROR_INVALID_VALUE;
   *p = Problem{B, T, H_qk, H_v, d_k, d_v, dtype, q, k, v, alpha, beta,
                cu_seqlens, n_seqs, h0, o, hT, 0};
   return GDN_SUCCESS;
@@ -174,7 +179,7 @@ int32_t gdn_decode_step(int32_t B, int32_t H_qk, int32_t H_v, int32_t d_k, int32
                         void *stream) {
   int32_t st = check_common(B, 1, H_qk, H_v, d_k, d_v, dtype, q, k, v, alpha, beta, o);
   if (st != GDN_SUCCESS) return st;
-  if (B > 0 && !state) return GDN_ERROR_INVALID_VALUE;
+  if ((B > 0 && !state) || !aligned16(state)) return GDN_ERROR_INVALID_VALUE;
   Problem p{};
   p.B = B;
   p.T = 1;
@@ -206,8 +211,12 @@ int32_t gdn_block_prologue(int32_t B, int32_t T, int32_t H_qk, int32_t H_v, int3
   if (st != GDN_SUCCESS) return st;
   if (!(eps >= 0.0f) || !std::isfinite(eps) || !std::isfinite(q_scale)) return GDN_ERROR_INVALID_VALUE;
   const int64_t tokens = int64_t(B) * T;
-  // one wave per (32 tokens, head) in a one-dimensional grid
-  if ((tokens + kPrologueTokens - 1) / kPrologueTokens > INT32_MAX / (2 * int64_t(H_qk) + H_v))
+  // at most one wave per (16 tokens, head) in a one-dimensional grid, and a
+  // token's row of one tensor below 2^24 bytes (32-bit buffer offsets)
+  if ((tokens + kPrologueMinTokens - 1) / kPrologueMinTokens > INT32_MAX / (2 * int64_t(H_qk) + H_v))
+    return GDN_ERROR_NOT_SUPPORTED;
+  const int64_t elem = dtype == GDN_BF16 ? 2 : 4;
+  if (int64_t(H_qk) * d_k * elem >= (1 << 24) || int64_t(H_v) * d_v * elem >= (1 << 24))
     return GDN_ERROR_NOT_SUPPORTED;
   if (cu_seqlens) {
     if (B != 1 || n_seqs < 0 || (tokens > 0 && n_seqs < 1)) return GDN_ERROR_INVALID_VALUE;
@@ -217,6 +226,9 @@ int32_t gdn_block_prologue(int32_t B, int32_t T, int32_t H_qk, int32_t H_v, int3
   if (tokens > 0 && (!q_raw || !k_raw || !v_raw || !conv_q || !conv_k || !conv_v || !a_raw || !b_raw ||
                      !log_A || !q || !k || !v || !alpha || !beta))
     return GDN_ERROR_INVALID_VALUE;
+  for (const void *t : {q_raw, k_raw, v_raw, static_cast<const void *>(q), static_cast<const void *>(k),
+                        static_cast<const void *>(v)})
+    if (!aligned16(t)) return GDN_ERROR_INVALID_VALUE;
   BlockProblem p{};
   p.B = B;
   p.T = T;
@@ -257,6 +269,7 @@ int32_t gdn_block_epilogue(int32_t B, int32_t T, int32_t H_v, int32_t d_v, int32
   if (st != GDN_SUCCESS) return st;
   if (!(eps >= 0.0f) || !std::isfinite(eps)) return GDN_ERROR_INVALID_VALUE;
   if (int64_t(B) * T > 0 && (!o || !g || !y)) return GDN_ERROR_INVALID_VALUE;
+  if (!aligned16(o) || !aligned16(g) || !aligned16(y)) return GDN_ERROR_INVALID_VALUE;
   BlockProblem p{};
   p.B = B;
   p.T = T;

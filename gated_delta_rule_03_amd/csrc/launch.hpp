@@ -76,7 +76,7 @@ struct BlockProblem {
   int32_t n_seqs;
   float eps, q_scale;
 };
-constexpr int kPrologueTokens = 32;  // tokens per prologue wave
+constexpr int kPrologueMinTokens = 16;  // tokens per prologue wave, at least (a bound for the grid size)
 hipError_t launch_block_prologue(const BlockProblem &p, hipStream_t st);
 hipError_t launch_block_epilogue(const BlockProblem &p, hipStream_t st);
 hipError_t launch_decode(const Problem &p, float *state, hipStream_t st);

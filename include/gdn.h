@@ -32,6 +32,12 @@
  * Supported sizes: d_k, d_v in {16, 32, 64, 128}; dtype GDN_F32 or GDN_BF16.
  * The state and all accumulation are float32; o is written in `dtype`.
  *
+ * Alignment: q, k, v, o, h0, hT, state and the block entry points' token-major
+ * tensors (q_raw, k_raw, v_raw, g, y) start at 16-byte aligned addresses
+ * (they are accessed 16 bytes per lane); other pointers need only the
+ * alignment of their element type.  A misaligned tensor is rejected with
+ * GDN_ERROR_INVALID_VALUE.
+ *
  * Ownership: every buffer is allocated by the caller and lives on the current
  * HIP device (device pointers).  The library allocates nothing, frees nothing
  * and keeps no pointer after a call returns.  Calls are asynchronous on the

@@ -77,6 +77,9 @@ def test_argument_errors_are_reported_before_launch(lib, fn, extra):
     assert fwd(lib, fn, ptrs=False, extra=extra) == 1
     assert fwd(lib, fn, B=2, cu=ctypes.c_void_p(0x1000), n=2, extra=extra) == 1
     assert fwd(lib, fn, B=2, n=3, extra=extra) == 1
+    # a tensor that does not start on a 16-byte boundary
+    args = [1, 8, 1, 1, 64, 64, 0] + [ctypes.c_void_p(0x1000)] * 5 + [None, 0, None, ctypes.c_void_p(0x1008), None]
+    assert getattr(lib, fn)(*args, *extra) == 1
 
 
 def test_chunk_workspace_errors(lib):
@@ -93,6 +96,7 @@ def test_decode_argument_errors(lib):
     assert lib.gdn_decode_step(1, 1, 1, 48, 64, 0, p, p, p, p, p, p, p, None) == 2
     assert lib.gdn_decode_step(1, 1, 1, 64, 64, 0, p, p, p, p, p, None, p, None) == 1
     assert lib.gdn_decode_step(1, 2, 3, 64, 64, 0, p, p, p, p, p, p, p, None) == 2
+    assert lib.gdn_decode_step(1, 1, 1, 64, 64, 0, p, p, p, p, p, ctypes.c_void_p(0x1008), p, None) == 1
 
 
 def prologue(lib, B=1, T=8, H_qk=1, H_v=1, d_k=64, d_v=64, dtype=0, ptrs=True, cu=None, n=0, eps=1e-6,
@@ -115,9 +119,15 @@ def test_block_argument_errors(lib):
     assert prologue(lib, cu=p, n=0) == 1           # ... and at least one sequence
     # one wave per (32 tokens, head): 2^16 token ranges x 3 * 2^15 heads exceeds a 32-bit grid
     assert prologue(lib, B=1, T=1 << 21, H_qk=1 << 15, H_v=1 << 15, d_k=16, d_v=16) == 2
+    # a token's row of one tensor must stay below 2^24 bytes: 2^15 heads x 128 x 4 bytes = 2^24
+    assert prologue(lib, B=1, T=8, H_qk=1 << 15, H_v=1 << 15, d_k=128, d_v=128) == 2
     assert lib.gdn_block_epilogue(1, 8, 1, 48, 0, p, p, None, 1e-6, p, None) == 2
     assert lib.gdn_block_epilogue(1, 8, 1, 64, 0, p, None, None, 1e-6, p, None) == 1
     assert lib.gdn_block_epilogue(1, 8, 1, 64, 0, p, p, None, -1.0, p, None) == 1
+    assert lib.gdn_block_epilogue(1, 8, 1, 64, 0, p, ctypes.c_void_p(0x1004), None, 1e-6, p, None) == 1
+    q = ctypes.c_void_p(0x1002)
+    assert lib.gdn_block_prologue(1, 8, 1, 1, 64, 64, 0, p, q, p, p, p, p, None, None, None, p, p, p,
+                                  None, 1e-6, 1.0, None, 0, p, p, p, p, p, None) == 1
     assert lib.gdn_block_epilogue(0, 8, 1, 64, 0, None, None, None, 1e-6, None, None) == 0  # nothing to do
 
 
