@@ -170,7 +170,9 @@ int32_t gdn_decode_step(int32_t B, int32_t H_qk, int32_t H_v, int32_t d_k, int32
  *                  when T > 0); the convolution restarts at every sequence
  *   q, k, v        outputs shaped like q_raw, k_raw, v_raw (dtype);
  *   alpha, beta    outputs [B, T, H_v] float32 -- the inputs of gdn_chunk_fwd.
- * Outputs must not alias inputs.  Errors as gdn_recurrent_fwd.
+ * Outputs must not alias inputs.  Errors as gdn_recurrent_fwd, plus
+ * GDN_ERROR_NOT_SUPPORTED when one token's row of q, k or v (H * d elements)
+ * takes 2^24 bytes or more, or the batch needs more than 2^31 waves.
  */
 int32_t gdn_block_prologue(int32_t B, int32_t T, int32_t H_qk, int32_t H_v, int32_t d_k,
                            int32_t d_v, int32_t dtype, const void *q_raw, const void *k_raw,
