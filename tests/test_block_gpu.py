@@ -122,3 +122,42 @@ def test_whole_block(gdn, dtype, lengths):
     err = rel_err(host_f64(y), ref, slices(x))
     log(f"    max rel err y={err:.3e}")
     assert np.all(np.isfinite(host_f64(y))) and err <= TOL[dtype]
+
+
+def test_block_full_prefill_shape(gdn):
+    """Prologue and epilogue at the bench's shape (B=4, T=4096, H=16, d=128,
+    bf16), in the launch configuration the bench times, against the float64
+    oracle on every output."""
+    x = gi.block_inputs(4, 4096, 16, 16, 128, 128, "bf16", seed=360)
+    log("[block full] B=4 T=4096 H=16 d=128 bf16")
+    (q, k, v, alpha, beta), _ = run_prologue(gdn, x, 128 ** -0.5)
+    y = gdn.block_epilogue(dev_tensor(x["v_raw"]), dev_tensor(x["g_raw"]), o_norm_weight=dev_tensor(x["o_norm"]),
+                           eps=1e-6)
+    import torch
+    torch.cuda.synchronize()
+    ref = oracle_prologue(x, 128 ** -0.5)
+    sl = slices(x)
+    errs = [rel_err(host_f64(t), r, sl) for t, r in zip((q, k, v), ref[:3])]
+    errs += [rel_err(host_f64(t)[..., None], r[..., None], sl) for t, r in zip((alpha, beta), ref[3:])]
+    ey = rel_err(host_f64(y), ob.epilogue(x["v_raw"], x["g_raw"], x["o_norm"], 1e-6), sl)
+    log(f"    max rel err q={errs[0]:.3e} k={errs[1]:.3e} v={errs[2]:.3e} alpha={errs[3]:.3e} "
+        f"beta={errs[4]:.3e} y={ey:.3e}")
+    assert max(errs[:3] + [ey]) <= TOL["bf16"] and max(errs[3:]) <= TOL["f32"]
+
+
+def test_block_prologue_many_short_sequences(gdn):
+    """A packed batch of 700 sequences of 0 to 40 tokens: many sequence starts
+    inside each 64-token run, empty sequences and sequences shorter than the
+    convolution."""
+    rng = np.random.default_rng(370)
+    lengths = tuple(int(v) for v in rng.integers(0, 41, 700))
+    x = gi.block_inputs(1, 0, 2, 4, 64, 128, "f32", seed=371, lengths=lengths)
+    log(f"[prologue packed] {len(lengths)} sequences, {sum(lengths)} tokens")
+    (q, k, v, alpha, beta), _ = run_prologue(gdn, x, 1.0)
+    import torch
+    torch.cuda.synchronize()
+    ref = oracle_prologue(x, 1.0)
+    sl = slices(x)
+    errs = [rel_err(host_f64(t), r, sl) for t, r in zip((q, k, v), ref[:3])]
+    log(f"    max rel err q={errs[0]:.3e} k={errs[1]:.3e} v={errs[2]:.3e}")
+    assert max(errs) <= TOL["f32"]
