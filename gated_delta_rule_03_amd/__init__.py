@@ -8,7 +8,9 @@ other implementation here and no fallback.  PyTorch only provides device
 memory and streams.
 
 Names follow the C ABI: ``recurrent_fwd``, ``chunk_fwd`` (with
-``chunk_fwd_workspace_bytes``) and ``decode_step``.
+``chunk_fwd_workspace_bytes``), ``decode_step``, the GDN block's
+``block_prologue`` and ``block_epilogue``, and the per-channel-gate
+``kda_recurrent_fwd`` and ``kda_decode_step``.
 """
 from __future__ import annotations
 
@@ -18,7 +20,8 @@ from typing import Optional, Tuple
 
 __all__ = [
     "GDNError", "lib_path", "load", "version", "status_string", "recurrent_fwd",
-    "chunk_fwd", "chunk_fwd_workspace_bytes", "decode_step", "GDN_F32", "GDN_BF16",
+    "chunk_fwd", "chunk_fwd_workspace_bytes", "decode_step", "block_prologue", "block_epilogue",
+    "kda_recurrent_fwd", "kda_decode_step", "GDN_F32", "GDN_BF16",
 ]
 
 GDN_SUCCESS = 0
@@ -31,7 +34,7 @@ _lib: Optional[ctypes.CDLL] = None
 
 EXPORTS = ["gdn_version", "gdn_status_string", "gdn_recurrent_fwd",
            "gdn_chunk_fwd_workspace_bytes", "gdn_chunk_fwd", "gdn_decode_step",
-           "gdn_block_prologue", "gdn_block_epilogue"]
+           "gdn_block_prologue", "gdn_block_epilogue", "gdn_kda_recurrent_fwd", "gdn_kda_decode_step"]
 
 
 class GDNError(RuntimeError):
@@ -69,6 +72,10 @@ def load() -> ctypes.CDLL:
     lib.gdn_chunk_fwd.argtypes = fwd + [i32, vp, ctypes.c_size_t, vp]
     lib.gdn_chunk_fwd.restype = i32
     lib.gdn_decode_step.argtypes = [i32] * 6 + [vp, vp, vp, fp, fp, fp, vp, vp]
+    lib.gdn_kda_recurrent_fwd.argtypes = fwd + [vp]
+    lib.gdn_kda_recurrent_fwd.restype = i32
+    lib.gdn_kda_decode_step.argtypes = [i32] * 6 + [vp, vp, vp, fp, fp, fp, vp, vp]
+    lib.gdn_kda_decode_step.restype = i32
     lib.gdn_decode_step.restype = i32
     f32 = ctypes.c_float
     lib.gdn_block_prologue.argtypes = ([i32] * 7 + [vp] * 3 + [fp] * 10 + [f32, f32, vp, i32]
@@ -132,7 +139,7 @@ def _stream(stream) -> Optional[int]:
     return s.cuda_stream
 
 
-def _fwd_args(q, k, v, alpha, beta, cu_seqlens, h0, o, hT, output_final_state):
+def _fwd_args(q, k, v, alpha, beta, cu_seqlens, h0, o, hT, output_final_state, per_channel=False):
     torch = _torch()
     if q.dim() != 4 or k.dim() != 4 or v.dim() != 4:
         raise ValueError("q, k, v must be [B, T, H, d]")
@@ -142,7 +149,7 @@ def _fwd_args(q, k, v, alpha, beta, cu_seqlens, h0, o, hT, output_final_state):
     _check(q, "q", (B, T, H_qk, d_k), device=dev)
     _check(k, "k", (B, T, H_qk, d_k), q.dtype, dev)
     _check(v, "v", (B, T, H_v, d_v), q.dtype, dev)
-    _check(alpha, "alpha", (B, T, H_v), torch.float32, dev)
+    _check(alpha, "alpha", (B, T, H_v, d_k) if per_channel else (B, T, H_v), torch.float32, dev)
     _check(beta, "beta", (B, T, H_v), torch.float32, dev)
     code = _dtype_code(q)
     if cu_seqlens is not None:
@@ -238,6 +245,47 @@ def decode_step(q, k, v, alpha, beta, state, *, o=None, stream=None):
                                 _stream(stream))
     if st != GDN_SUCCESS:
         raise GDNError(st, "gdn_decode_step")
+    return o
+
+
+def kda_recurrent_fwd(q, k, v, alpha, beta, *, cu_seqlens=None, h0=None, o=None, hT=None,
+                      output_final_state: bool = True, stream=None) -> Tuple:
+    """Token-by-token delta rule with one decay rate per key channel: alpha is
+    [B, T, H_v, d_k] float32.  Returns (o, hT)."""
+    dims, n_seqs, o, hT = _fwd_args(q, k, v, alpha, beta, cu_seqlens, h0, o, hT,
+                                    output_final_state, per_channel=True)
+    st = load().gdn_kda_recurrent_fwd(*dims, _ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(beta),
+                                      _ptr(cu_seqlens), n_seqs, _ptr(h0), _ptr(o), _ptr(hT),
+                                      _stream(stream))
+    if st != GDN_SUCCESS:
+        raise GDNError(st, "gdn_kda_recurrent_fwd")
+    return o, hT
+
+
+def kda_decode_step(q, k, v, alpha, beta, state, *, o=None, stream=None):
+    """One token per sequence with one decay rate per key channel (alpha
+    [B, 1, H_v, d_k] float32); ``state`` is updated in place.  Returns o."""
+    torch = _torch()
+    if q.dim() != 4 or q.shape[1] != 1:
+        raise ValueError("q must be [B, 1, H_qk, d_k]")
+    B, _, H_qk, d_k = q.shape
+    H_v, d_v = v.shape[2], v.shape[3]
+    dev = q.device
+    _check(q, "q", (B, 1, H_qk, d_k), device=dev)
+    _check(k, "k", (B, 1, H_qk, d_k), q.dtype, dev)
+    _check(v, "v", (B, 1, H_v, d_v), q.dtype, dev)
+    _check(alpha, "alpha", (B, 1, H_v, d_k), torch.float32, dev)
+    _check(beta, "beta", (B, 1, H_v), torch.float32, dev)
+    _check(state, "state", (B, H_v, d_k, d_v), torch.float32, dev)
+    if o is None:
+        o = torch.empty((B, 1, H_v, d_v), dtype=q.dtype, device=dev)
+    else:
+        _check(o, "o", (B, 1, H_v, d_v), q.dtype, dev)
+    st = load().gdn_kda_decode_step(B, H_qk, H_v, d_k, d_v, _dtype_code(q), _ptr(q), _ptr(k),
+                                    _ptr(v), _ptr(alpha), _ptr(beta), _ptr(state), _ptr(o),
+                                    _stream(stream))
+    if st != GDN_SUCCESS:
+        raise GDNError(st, "gdn_kda_decode_step")
     return o
 
 

@@ -198,6 +198,45 @@ int32_t gdn_decode_step(int32_t B, int32_t H_qk, int32_t H_v, int32_t d_k, int32
   return status_of(launch_decode(p, state, static_cast<hipStream_t>(stream)));
 }
 
+int32_t gdn_kda_recurrent_fwd(int32_t B, int32_t T, int32_t H_qk, int32_t H_v, int32_t d_k,
+                              int32_t d_v, int32_t dtype, const void *q, const void *k, const void *v,
+                              const float *alpha, const float *beta, const int32_t *cu_seqlens,
+                              int32_t n_seqs, const float *h0, void *o, float *hT, void *stream) {
+  Problem p;
+  int32_t st = make_problem(B, T, H_qk, H_v, d_k, d_v, dtype, q, k, v, alpha, beta, cu_seqlens,
+                            n_seqs, h0, o, hT, &p);
+  if (st != GDN_SUCCESS) return st;
+  if (!aligned16(alpha)) return GDN_ERROR_INVALID_VALUE;
+  p.per_channel = 1;
+  return status_of(launch_recurrent(p, static_cast<hipStream_t>(stream)));
+}
+
+int32_t gdn_kda_decode_step(int32_t B, int32_t H_qk, int32_t H_v, int32_t d_k, int32_t d_v,
+                            int32_t dtype, const void *q, const void *k, const void *v,
+                            const float *alpha, const float *beta, float *state, void *o,
+                            void *stream) {
+  int32_t st = check_common(B, 1, H_qk, H_v, d_k, d_v, dtype, q, k, v, alpha, beta, o);
+  if (st != GDN_SUCCESS) return st;
+  if ((B > 0 && !state) || !aligned16(state) || !aligned16(alpha)) return GDN_ERROR_INVALID_VALUE;
+  Problem p{};
+  p.B = B;
+  p.T = 1;
+  p.H_qk = H_qk;
+  p.H_v = H_v;
+  p.d_k = d_k;
+  p.d_v = d_v;
+  p.dtype = dtype;
+  p.q = q;
+  p.k = k;
+  p.v = v;
+  p.alpha = alpha;
+  p.beta = beta;
+  p.o = o;
+  p.n_seqs = B;
+  p.per_channel = 1;
+  return status_of(launch_decode(p, state, static_cast<hipStream_t>(stream)));
+}
+
 int32_t gdn_block_prologue(int32_t B, int32_t T, int32_t H_qk, int32_t H_v, int32_t d_k,
                            int32_t d_v, int32_t dtype, const void *q_raw, const void *k_raw,
                            const void *v_raw, const float *conv_q, const float *conv_k,

@@ -9,6 +9,10 @@
 // The step reads and writes the state once: about rd numbers each way
 // ("Attention as Matrix Algebra", section 9), so it is bound by HBM bandwidth.
 //
+// With a per-channel gate (alpha_t a vector over the key channels, i.e. the
+// state's rows) the decay is diag(alpha): a = S^T (alpha . k),
+// b = S^T (alpha . q), and row r is written back as alpha_r S_r + k_r u.
+//
 // Layout: one 512-thread block per (sequence, value head).  Thread tid owns
 // columns 4 (tid & 31) .. +3 of rows (tid >> 5) + 16 i: each wave instruction
 // moves two whole 512-byte rows (coalesced 16-byte accesses).  The state is
@@ -34,7 +38,7 @@ constexpr int kDecodeThreads = 512;
 constexpr int kDecodeRowGroups = kDecodeThreads / 32;  // 16
 constexpr int kDecodeRows = 128 / kDecodeRowGroups;    // rows per thread (d_k <= 128)
 
-template <typename T>
+template <typename T, bool PER_CHANNEL>
 __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(DecodeArgs<T> a) {
   const int u = blockIdx.x;  // b * H_v + h
   const int b = u / a.H_v, h = u - b * a.H_v, hq = h / a.group;
@@ -58,15 +62,22 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(DecodeArgs<T> a)
   else if (tid >= 128 && tid - 128 < a.d_k) skq[1][tid - 128] = to_f32(qp[tid - 128]);
   __syncthreads();
 
-  float kk[kDecodeRows];
+  const int64_t vi = (int64_t(b) * a.H_v + h);
+  float kk[kDecodeRows], ar[kDecodeRows];  // ar: per-channel rates of this thread's rows
   f32x4_t ak = zero4(), bq = zero4();
 #pragma unroll
   for (int i = 0; i < kDecodeRows; ++i) {
     const int r = rg + kDecodeRowGroups * i;
     kk[i] = r < a.d_k ? skq[0][r] : 0.0f;
     const float qq = r < a.d_k ? skq[1][r] : 0.0f;
-    ak += s[i] * kk[i];
-    bq += s[i] * qq;
+    if constexpr (PER_CHANNEL) {
+      ar[i] = r < a.d_k ? a.alpha[vi * a.d_k + r] : 0.0f;
+      ak += s[i] * (ar[i] * kk[i]);
+      bq += s[i] * (ar[i] * qq);
+    } else {
+      ak += s[i] * kk[i];
+      bq += s[i] * qq;
+    }
   }
   // q^T k over d_k, in wave 0
   float qk = 0.0f;
@@ -99,8 +110,7 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(DecodeArgs<T> a)
     bq += red_b[w][cg];
   }
 
-  const int64_t vi = (int64_t(b) * a.H_v + h);
-  const float al = a.alpha[vi], be = a.beta[vi];
+  const float al = PER_CHANNEL ? 1.0f : a.alpha[vi], be = a.beta[vi];  // per-channel: rates already applied
   f32x4_t vv = zero4();
   if (col_ok) {
     const float4 x = load4_f32(a.v + vi * a.d_v + 4 * cg);
@@ -118,7 +128,7 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(DecodeArgs<T> a)
   for (int i = 0; i < kDecodeRows; ++i) {
     const int r = rg + kDecodeRowGroups * i;
     if (r < a.d_k && col_ok)
-      __builtin_nontemporal_store(al * s[i] + kk[i] * uu,
+      __builtin_nontemporal_store((PER_CHANNEL ? ar[i] : al) * s[i] + kk[i] * uu,
                                   reinterpret_cast<f32x4_t *>(S + int64_t(r) * a.d_v + 4 * cg));
   }
 }
@@ -140,7 +150,10 @@ static hipError_t launch_decode_t(const Problem &p, float *state, hipStream_t st
   a.group = p.H_v / p.H_qk;
   const int64_t blocks = int64_t(p.B) * p.H_v;
   if (blocks == 0) return hipSuccess;
-  hipLaunchKernelGGL(decode_kernel<T>, dim3(unsigned(blocks)), dim3(kDecodeThreads), 0, st, a);
+  if (p.per_channel)
+    hipLaunchKernelGGL((decode_kernel<T, true>), dim3(unsigned(blocks)), dim3(kDecodeThreads), 0, st, a);
+  else
+    hipLaunchKernelGGL((decode_kernel<T, false>), dim3(unsigned(blocks)), dim3(kDecodeThreads), 0, st, a);
   return hipGetLastError();
 }
 

@@ -18,6 +18,7 @@ struct Problem {
   void *o;
   float *hT;
   int32_t chunk;
+  int32_t per_channel = 0;  // alpha holds one rate per key channel: [.., H_v, d_k]
   int64_t n_tokens() const { return int64_t(B) * T; }
 };
 

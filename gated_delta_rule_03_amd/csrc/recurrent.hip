@@ -3,6 +3,11 @@
 // read after the write -- a matrix-vector read and a rank-one write per token
 // ("How linear attention works", section "Why it is called linear attention").
 //
+// With a per-channel gate (one rate per key channel, the channels being the
+// state's rows: "Attention as Matrix Algebra", section 10, names the
+// variant) the decay is diag(alpha_t) instead of a scalar; each lane owns
+// whole rows, so it scales its rows by their own rates.
+//
 // Layout: one wavefront per (sequence, value head, 16-column block).  Lane l
 // owns column 16 cb + (l & 15) and the contiguous row block
 // [(l >> 4) d_k/4, (l >> 4 + 1) d_k/4) of the state, in registers.  Column sums
@@ -25,10 +30,11 @@ struct RecArgs {
 
 struct TokenOps {
   float k[32], q[32];
+  float ar[32];  // per-channel gate: the rates of this lane's rows
   float v, al, be;
 };
 
-template <typename T>
+template <typename T, bool PER_CHANNEL>
 __device__ __forceinline__ void fetch_token(const RecArgs<T> &a, int tok, int hq, int h, int col,
                                             int r0, int nrow, TokenOps &x) {
   const int64_t qk_off = (int64_t(tok) * a.H_qk + hq) * a.d_k + r0;
@@ -46,11 +52,21 @@ __device__ __forceinline__ void fetch_token(const RecArgs<T> &a, int tok, int hq
   }
   const int64_t gi = int64_t(tok) * a.H_v + h;
   x.v = to_f32(a.v[gi * a.d_v + col]);
-  x.al = a.alpha[gi];
+  if constexpr (PER_CHANNEL) {
+    const float *ap = a.alpha + gi * a.d_k + r0;  // alpha [.., H_v, d_k]
+#pragma unroll
+    for (int i = 0; i < 32; i += 4) {
+      const float4 r = i < nrow ? *reinterpret_cast<const float4 *>(ap + i) : make_float4(0.f, 0.f, 0.f, 0.f);
+      x.ar[i] = r.x; x.ar[i + 1] = r.y; x.ar[i + 2] = r.z; x.ar[i + 3] = r.w;
+    }
+    x.al = 1.0f;
+  } else {
+    x.al = a.alpha[gi];
+  }
   x.be = a.beta[gi];
 }
 
-template <typename T>
+template <typename T, bool PER_CHANNEL>
 __global__ __launch_bounds__(64) void recurrent_kernel(RecArgs<T> a) {
   const int lane = threadIdx.x;
   const int u = blockIdx.x / a.n_colblk, cb = blockIdx.x - u * a.n_colblk;
@@ -69,13 +85,13 @@ __global__ __launch_bounds__(64) void recurrent_kernel(RecArgs<T> a) {
   int start, end;
   a.geo.seq_bounds(s, start, end);
   TokenOps cur, nxt;
-  if (start < end) fetch_token(a, start, hq, h, col, r0, nrow, cur);
+  if (start < end) fetch_token<T, PER_CHANNEL>(a, start, hq, h, col, r0, nrow, cur);
   for (int tok = start; tok < end; ++tok) {
-    if (tok + 1 < end) fetch_token(a, tok + 1, hq, h, col, r0, nrow, nxt);
-    // predict: vhat = (alpha S)^T k
+    if (tok + 1 < end) fetch_token<T, PER_CHANNEL>(a, tok + 1, hq, h, col, r0, nrow, nxt);
+    // predict: vhat = (alpha S)^T k  (per-channel: (diag(a) S)^T k)
     float p = 0.0f;
 #pragma unroll
-    for (int i = 0; i < 32; ++i) p += S[i] * cur.k[i];
+    for (int i = 0; i < 32; ++i) p += S[i] * (PER_CHANNEL ? cur.ar[i] * cur.k[i] : cur.k[i]);
     p += __shfl_xor(p, 16);
     p += __shfl_xor(p, 32);
     const float w = cur.be * (cur.v - cur.al * p);
@@ -83,7 +99,7 @@ __global__ __launch_bounds__(64) void recurrent_kernel(RecArgs<T> a) {
     float r = 0.0f;
 #pragma unroll
     for (int i = 0; i < 32; ++i) {
-      S[i] = cur.al * S[i] + cur.k[i] * w;
+      S[i] = (PER_CHANNEL ? cur.ar[i] : cur.al) * S[i] + cur.k[i] * w;
       r += S[i] * cur.q[i];
     }
     r += __shfl_xor(r, 16);
@@ -119,7 +135,10 @@ static hipError_t launch_recurrent_t(const Problem &p, hipStream_t st) {
   a.geo = make_geom(p, nullptr);
   const int64_t blocks = int64_t(a.n_units) * a.n_colblk;
   if (blocks == 0) return hipSuccess;
-  hipLaunchKernelGGL(recurrent_kernel<T>, dim3(unsigned(blocks)), dim3(64), 0, st, a);
+  if (p.per_channel)
+    hipLaunchKernelGGL((recurrent_kernel<T, true>), dim3(unsigned(blocks)), dim3(64), 0, st, a);
+  else
+    hipLaunchKernelGGL((recurrent_kernel<T, false>), dim3(unsigned(blocks)), dim3(64), 0, st, a);
   return hipGetLastError();
 }
 

@@ -278,6 +278,13 @@ def random_state(shape, seed: int, scale: float = 1.0) -> np.ndarray:
     return (scale * rng.standard_normal(shape, dtype=np.float32)).astype(np.float32)
 
 
+def channel_rates(B: int, T: int, H_v: int, d_k: int, seed: int, lo: float = 0.8) -> np.ndarray:
+    """Seeded float32 decay rates, one per token, value head and key channel,
+    uniform in [lo, 1) (the per-channel gate's alpha, [B, T, H_v, d_k])."""
+    rng = np.random.default_rng(np.random.SeedSequence(seed))
+    return rng.uniform(lo, 1.0, (B, T, H_v, d_k)).astype(np.float32)
+
+
 def block_inputs(B: int, T: int, H_qk: int, H_v: int, d_k: int, d_v: int, dtype: str, seed: int,
                  lengths: Optional[Sequence[int]] = None) -> dict:
     """Seeded raw inputs of a GDN block's prologue and epilogue: the q, k, v and

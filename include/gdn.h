@@ -148,6 +148,33 @@ int32_t gdn_decode_step(int32_t B, int32_t H_qk, int32_t H_v, int32_t d_k, int32
                         void *stream);
 
 /*
+ * Per-channel gate (Kimi Delta Attention: "Attention as Matrix Algebra",
+ * section 10, gives each feature channel its own forget rate).  The channels
+ * are the key features, the rows of the keys x values state, so the decay of
+ * step t is diag(alpha_t) with alpha_t in R^{d_k}; the rest of the update is
+ * unchanged:
+ *
+ *   S' = diag(alpha_t) S_{t-1};  vhat = S'^T k_t;
+ *   S_t = S' + beta_t k_t (v_t - vhat)^T;  o_t = S_t^T q_t
+ *
+ * gdn_kda_recurrent_fwd takes the arguments of gdn_recurrent_fwd, with
+ *   alpha  [B, T, H_v, d_k] float32 (one rate per token, value head and key
+ *          channel), 16-byte aligned.
+ * gdn_kda_decode_step takes the arguments of gdn_decode_step, with
+ *   alpha  [B, 1, H_v, d_k] float32, 16-byte aligned.
+ * Errors, ownership and the state layout as for the scalar-gate entry points.
+ * Equal rates across the channels give the scalar-gate results.
+ */
+int32_t gdn_kda_recurrent_fwd(int32_t B, int32_t T, int32_t H_qk, int32_t H_v, int32_t d_k,
+                              int32_t d_v, int32_t dtype, const void *q, const void *k, const void *v,
+                              const float *alpha, const float *beta, const int32_t *cu_seqlens,
+                              int32_t n_seqs, const float *h0, void *o, float *hT, void *stream);
+int32_t gdn_kda_decode_step(int32_t B, int32_t H_qk, int32_t H_v, int32_t d_k, int32_t d_v,
+                            int32_t dtype, const void *q, const void *k, const void *v,
+                            const float *alpha, const float *beta, float *state, void *o,
+                            void *stream);
+
+/*
  * gdn_block_prologue -- the GDN block's steps between the projections and
  * the recurrence, fused ("Linear attention", section "A naive PyTorch
  * implementation"):

@@ -66,6 +66,7 @@ def fwd(lib, fn, B=1, T=8, H_qk=1, H_v=1, d_k=64, d_v=64, dtype=0, ptrs=True, cu
 
 
 @pytest.mark.parametrize("fn,extra", [("gdn_recurrent_fwd", (None,)),
+                                      ("gdn_kda_recurrent_fwd", (None,)),
                                       ("gdn_chunk_fwd", (64, None, 0, None))])
 def test_argument_errors_are_reported_before_launch(lib, fn, extra):
     # every case below fails validation, so no kernel is launched
@@ -97,6 +98,13 @@ def test_decode_argument_errors(lib):
     assert lib.gdn_decode_step(1, 1, 1, 64, 64, 0, p, p, p, p, p, None, p, None) == 1
     assert lib.gdn_decode_step(1, 2, 3, 64, 64, 0, p, p, p, p, p, p, p, None) == 2
     assert lib.gdn_decode_step(1, 1, 1, 64, 64, 0, p, p, p, p, p, ctypes.c_void_p(0x1008), p, None) == 1
+    for fn in (lib.gdn_decode_step, lib.gdn_kda_decode_step):
+        assert fn(1, 1, 1, 48, 64, 0, p, p, p, p, p, p, p, None) == 2
+        assert fn(1, 2, 3, 64, 64, 0, p, p, p, p, p, p, p, None) == 2
+    # the per-channel rates are read 16 bytes at a time
+    assert lib.gdn_kda_decode_step(1, 1, 1, 64, 64, 0, p, p, p, ctypes.c_void_p(0x1004), p, p, p, None) == 1
+    args = [1, 8, 1, 1, 64, 64, 0, p, p, p, ctypes.c_void_p(0x1004), p, None, 0, None, p, None, None]
+    assert lib.gdn_kda_recurrent_fwd(*args) == 1
 
 
 def prologue(lib, B=1, T=8, H_qk=1, H_v=1, d_k=64, d_v=64, dtype=0, ptrs=True, cu=None, n=0, eps=1e-6,
@@ -150,5 +158,7 @@ def test_host_path_reaches_launch_without_gpu(lib):
     ws = ctypes.c_void_p(0x100000)
     assert lib.gdn_chunk_fwd(*base, 64, ws, 1 << 30, None) == 4
     assert lib.gdn_decode_step(2, 1, 1, 64, 64, 1, p, p, p, p, p, p, p, None) == 4
+    assert lib.gdn_kda_recurrent_fwd(*base, None) == 4
+    assert lib.gdn_kda_decode_step(2, 1, 1, 64, 64, 1, p, p, p, p, p, p, p, None) == 4
     assert prologue(lib) == 4
     assert lib.gdn_block_epilogue(1, 8, 1, 64, 0, p, p, None, 1e-6, p, None) == 4

@@ -1,0 +1,103 @@
+"""GPU parity of the per-channel-gate entry points (gdn_kda_recurrent_fwd,
+gdn_kda_decode_step) against the float64 oracle ``oracle/kda.py``, through the
+C ABI.  Metric as the other parity tests: per (sequence, head) and tensor,
+max |X - X_ref| / max |X_ref|; bars 1e-4 (float32 inputs) and 2e-2 (bf16)."""
+import numpy as np
+import pytest
+
+import gdn_inputs as gi
+from oracle import kda
+from gpu_util import TOL, dev_tensor, host_f64, log
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def gdn():
+    import torch
+    import gated_delta_rule_03_amd as g
+    assert torch.cuda.is_available()
+    g.load()
+    return g
+
+
+def rel_err(got, ref):
+    """Max over the leading (unit) slices of max |got - ref| / max |ref|."""
+    g = got.reshape(-1, *got.shape[-2:]) if got.ndim > 3 else got
+    r = ref.reshape(-1, *ref.shape[-2:]) if ref.ndim > 3 else ref
+    worst = 0.0
+    for a, b in zip(g, r):
+        den = max(float(np.max(np.abs(b))), 1e-30)
+        worst = max(worst, float(np.max(np.abs(a - b))) / den)
+    return worst
+
+
+CASES = [
+    # dtype, B, T, H_qk, H_v, d_k, d_v, lengths
+    ("f32", 2, 40, 1, 2, 16, 16, None),
+    ("f32", 1, 0, 2, 4, 64, 128, (17, 0, 1, 30)),
+    ("f32", 2, 33, 2, 2, 128, 64, None),
+    ("bf16", 2, 64, 2, 4, 128, 128, None),
+]
+
+
+@pytest.mark.parametrize("case", CASES, ids=[f"{c[0]}-B{c[1]}T{c[2]}H{c[3]}_{c[4]}d{c[5]}_{c[6]}"
+                                             + ("-packed" if c[7] else "") for c in CASES])
+def test_kda_recurrent(gdn, case):
+    import torch
+    dtype, B, T, H_qk, H_v, d_k, d_v, lengths = case
+    seed = 400 + CASES.index(case)
+    w = gi.generate(gi.Spec("kda", B=B, T=T, H_qk=H_qk, H_v=H_v, d_k=d_k, d_v=d_v, dtype=dtype, chunk=64,
+                            lengths=lengths, seed=seed))
+    B, T = w.q.shape[0], w.q.shape[1]
+    a = gi.channel_rates(B, T, H_v, d_k, seed + 50)
+    cu = w.cu_seqlens
+    N = B if cu is None else len(cu) - 1
+    h0 = gi.random_state((N, H_v, d_k, d_v), seed=seed + 60, scale=0.3)
+    log(f"[kda recurrent] {case}")
+    o, hT = gdn.kda_recurrent_fwd(dev_tensor(w.q), dev_tensor(w.k), dev_tensor(w.v), dev_tensor(a),
+                                  dev_tensor(w.beta), cu_seqlens=None if cu is None else dev_tensor(cu),
+                                  h0=dev_tensor(h0))
+    torch.cuda.synchronize()
+    ro, rh = kda.forward(w.q, w.k, w.v, a, w.beta, cu_seqlens=cu, h0=h0)
+    eo = max(rel_err(host_f64(o)[b, s:e].transpose(1, 0, 2), ro[b, s:e].transpose(1, 0, 2))
+             for b, s, e in ([(b, 0, T) for b in range(B)] if cu is None else
+                             [(0, int(cu[i]), int(cu[i + 1])) for i in range(N) if cu[i + 1] > cu[i]]))
+    eh = rel_err(host_f64(hT), rh)
+    log(f"    max rel err o={eo:.3e} hT={eh:.3e}")
+    assert eo <= TOL[dtype] and eh <= TOL[dtype]
+
+
+def test_kda_equal_rates_match_scalar_gate(gdn):
+    """Every channel at one rate: the per-channel path gives the scalar-gate
+    kernel's results (to rounding)."""
+    import torch
+    w = gi.generate(gi.Spec("kda-eq", B=2, T=50, H_qk=2, H_v=2, d_k=64, d_v=64, dtype="f32", chunk=64, seed=420))
+    a = np.repeat(w.alpha[..., None], 64, axis=-1).astype(np.float32)
+    args = [dev_tensor(x) for x in (w.q, w.k, w.v)]
+    o1, h1 = gdn.kda_recurrent_fwd(*args, dev_tensor(a), dev_tensor(w.beta))
+    o2, h2 = gdn.recurrent_fwd(*args, dev_tensor(w.alpha), dev_tensor(w.beta))
+    torch.cuda.synchronize()
+    e = max(rel_err(host_f64(o1), host_f64(o2)), rel_err(host_f64(h1), host_f64(h2)))
+    log(f"[kda equal rates] max rel diff vs scalar gate {e:.3e}")
+    assert e <= 1e-5
+
+
+@pytest.mark.parametrize("dtype,B,H_qk,H_v,d", [("f32", 3, 1, 2, 32), ("bf16", 256, 32, 32, 128)])
+def test_kda_decode(gdn, dtype, B, H_qk, H_v, d):
+    """One decode step from a random state; the bf16 case is the decode bench
+    shape (B=256, H=32, d=128), every unit checked."""
+    import torch
+    w = gi.generate(gi.Spec("kda-dec", B=B, T=1, H_qk=H_qk, H_v=H_v, d_k=d, d_v=d, dtype=dtype, chunk=64,
+                            seed=430 + B))
+    a = gi.channel_rates(B, 1, H_v, d, 431 + B)
+    state = gi.random_state((B, H_v, d, d), seed=432 + B, scale=0.3)
+    log(f"[kda decode] {dtype} B={B} H={H_v} d={d}")
+    st = dev_tensor(state)
+    o = gdn.kda_decode_step(dev_tensor(w.q), dev_tensor(w.k), dev_tensor(w.v), dev_tensor(a), dev_tensor(w.beta), st)
+    torch.cuda.synchronize()
+    ro, rs = kda.decode(state, w.q, w.k, w.v, a, w.beta)
+    eo = rel_err(host_f64(o)[:, 0], ro[:, 0])
+    es = rel_err(host_f64(st), rs)
+    log(f"    max rel err o={eo:.3e} state={es:.3e}")
+    assert eo <= TOL[dtype] and es <= TOL["f32"]
