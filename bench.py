@@ -38,6 +38,9 @@ projections drawn on the device, and gives each kernel's algorithmic bytes
 (every input read once, every output written once) as a fraction of HBM
 peak.
 
+``kda_decode`` times the per-channel-gate decode step (one decay rate per key
+channel) on the decode shape, with its HBM fraction.
+
 ``roofline.traffic`` is the decode kernel's HBM bytes per launch from the
 rocprofv3 FETCH_SIZE and WRITE_SIZE counters (profiles/decode_kernel.traffic.json),
 each scaled by what the counter reads for a plain 1 GiB read + 1 GiB write
@@ -186,6 +189,34 @@ def extra_workloads(args, gi, gdn, torch, dev, stream, evict):
                     "inputs": "drawn on the device with the generator's shapes and distributions"}
         del q, k, v, alpha, beta, o, hT, ws
     return out
+
+
+def kda_decode_workload(args, gdn, torch, dev, stream, evict, Dd, state):
+    """The per-channel-gate decode step on the decode shape: the same q, k, v,
+    beta and a copy of the state, with one decay rate per key channel."""
+    B, _, H, D = Dd["v"].shape
+    g = torch.Generator(device=dev)
+    g.manual_seed(91)
+    alpha = 0.8 + 0.2 * torch.rand((B, 1, H, D), generator=g, device=dev)
+    st = state.clone()
+    o = torch.empty_like(Dd["v"])
+    ms = []
+    for i in range(2 + max(3, args.steps // 2)):
+        evict(6)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        gdn.kda_decode_step(Dd["q"], Dd["k"], Dd["v"], alpha, Dd["beta"], st, o=o, stream=stream)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        if i >= 2:
+            ms.append(e0.elapsed_time(e1))
+    t = statistics.median(ms) * 1e-3
+    nbytes = B * H * (DECODE_BYTES_PER_UNIT + (D - 1) * 4)  # + the rates beyond one scalar
+    del st
+    return {"kda_decode": {
+        "workload": f"per-channel gate decode step B={B} H={H} d={D} bf16, fp32 state in place",
+        "us_per_step": t * 1e6, "bytes": nbytes, "GBps": nbytes / t / 1e9, "hbm_frac": nbytes / t / HBM_PEAK,
+    }}
 
 
 def block_workload(args, gdn, torch, dev, stream, evict):
@@ -376,6 +407,7 @@ def main():
     if not args.no_extra:
         extra = extra_workloads(args, gi, gdn, torch, dev, stream, evict)
         extra.update(block_workload(args, gdn, torch, dev, stream, evict))
+        extra.update(kda_decode_workload(args, gdn, torch, dev, stream, evict, Dd, state))
 
     tokens = B * T
     units = B * H

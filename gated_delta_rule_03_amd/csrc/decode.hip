@@ -38,8 +38,9 @@ constexpr int kDecodeThreads = 512;
 constexpr int kDecodeRowGroups = kDecodeThreads / 32;  // 16
 constexpr int kDecodeRows = 128 / kDecodeRowGroups;    // rows per thread (d_k <= 128)
 
+// (four waves per SIMD, so two blocks fit a CU: at most 128 VGPRs)
 template <typename T, bool PER_CHANNEL>
-__global__ __launch_bounds__(kDecodeThreads) void decode_kernel(DecodeArgs<T> a) {
+__global__ __launch_bounds__(kDecodeThreads, 4) void decode_kernel(DecodeArgs<T> a) {
   const int u = blockIdx.x;  // b * H_v + h
   const int b = u / a.H_v, h = u - b * a.H_v, hq = h / a.group;
   const int tid = threadIdx.x, cg = tid & 31, rg = tid >> 5, wave = tid >> 6;
@@ -57,13 +58,17 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(DecodeArgs<T> a)
                ? __builtin_nontemporal_load(reinterpret_cast<const f32x4_t *>(S + int64_t(r) * a.d_v + 4 * cg))
                : zero4();
   }
-  __shared__ float skq[2][128];
+  const int64_t vi = (int64_t(b) * a.H_v + h);
+  // k, q and (per-channel gate) the rates, staged once in LDS
+  __shared__ float skq[PER_CHANNEL ? 3 : 2][128];
   if (tid < a.d_k) skq[0][tid] = to_f32(kp[tid]);
   else if (tid >= 128 && tid - 128 < a.d_k) skq[1][tid - 128] = to_f32(qp[tid - 128]);
+  else if (PER_CHANNEL && tid >= 256 && tid - 256 < a.d_k) skq[PER_CHANNEL ? 2 : 0][tid - 256] = a.alpha[vi * a.d_k + tid - 256];
   __syncthreads();
 
-  const int64_t vi = (int64_t(b) * a.H_v + h);
-  float kk[kDecodeRows], ar[kDecodeRows];  // ar: per-channel rates of this thread's rows
+  // per-channel rate of row r (read from LDS where used, not held in registers)
+  auto rate = [&](int r) -> float { return r < a.d_k ? skq[PER_CHANNEL ? 2 : 0][r] : 0.0f; };
+  float kk[kDecodeRows];
   f32x4_t ak = zero4(), bq = zero4();
 #pragma unroll
   for (int i = 0; i < kDecodeRows; ++i) {
@@ -71,9 +76,9 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(DecodeArgs<T> a)
     kk[i] = r < a.d_k ? skq[0][r] : 0.0f;
     const float qq = r < a.d_k ? skq[1][r] : 0.0f;
     if constexpr (PER_CHANNEL) {
-      ar[i] = r < a.d_k ? a.alpha[vi * a.d_k + r] : 0.0f;
-      ak += s[i] * (ar[i] * kk[i]);
-      bq += s[i] * (ar[i] * qq);
+      const float ar = rate(r);
+      ak += s[i] * (ar * kk[i]);
+      bq += s[i] * (ar * qq);
     } else {
       ak += s[i] * kk[i];
       bq += s[i] * qq;
@@ -128,7 +133,7 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(DecodeArgs<T> a)
   for (int i = 0; i < kDecodeRows; ++i) {
     const int r = rg + kDecodeRowGroups * i;
     if (r < a.d_k && col_ok)
-      __builtin_nontemporal_store((PER_CHANNEL ? ar[i] : al) * s[i] + kk[i] * uu,
+      __builtin_nontemporal_store((PER_CHANNEL ? rate(r) : al) * s[i] + kk[i] * uu,
                                   reinterpret_cast<f32x4_t *>(S + int64_t(r) * a.d_v + 4 * cg));
   }
 }
