@@ -255,7 +255,9 @@ constexpr int kXBytes = 17408;
 }  // namespace
 
 __global__ __launch_bounds__(128, 4) void factors_kernel(PrepArgs<bf16_t> a) {
-  const int c = blockIdx.x, h = blockIdx.y;
+  // heads vary fastest across blocks: the blocks in flight at once read
+  // whole tokens' k rows, contiguous in memory
+  const int c = blockIdx.x / unsigned(a.H_v), h = blockIdx.x - c * a.H_v;
   int s, tok0, len;
   if (!a.geo.locate(c, s, tok0, len)) return;
   const int hq = h / a.group;
@@ -488,7 +490,8 @@ static hipError_t launch_prep_t(const Problem &p, const Workspace &ws, hipStream
   const int64_t slots = chunk_slots(p);
   if constexpr (sizeof(T) == 2) {
     if (staged_path(p)) {
-      hipLaunchKernelGGL(factors_kernel, dim3(unsigned(slots), unsigned(p.H_v)), dim3(128), 0, st, a);
+      if (slots * p.H_v > 0x7fffffff) return hipErrorInvalidConfiguration;
+      hipLaunchKernelGGL(factors_kernel, dim3(unsigned(slots * p.H_v)), dim3(128), 0, st, a);
       return hipGetLastError();
     }
   }
