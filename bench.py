@@ -41,6 +41,9 @@ peak.
 ``kda_decode`` times the per-channel-gate decode step (one decay rate per key
 channel) on the decode shape, with its HBM fraction.
 
+``decode_graph`` times a 64-step batch-1 decode loop launched eagerly and
+replayed as one captured HIP graph (host wall time per step).
+
 ``roofline.traffic`` is the decode kernel's HBM bytes per launch from the
 rocprofv3 FETCH_SIZE and WRITE_SIZE counters (profiles/decode_kernel.traffic.json),
 each scaled by what the counter reads for a plain 1 GiB read + 1 GiB write
@@ -216,6 +219,56 @@ def kda_decode_workload(args, gdn, torch, dev, stream, evict, Dd, state):
     return {"kda_decode": {
         "workload": f"per-channel gate decode step B={B} H={H} d={D} bf16, fp32 state in place",
         "us_per_step": t * 1e6, "bytes": nbytes, "GBps": nbytes / t / 1e9, "hbm_frac": nbytes / t / HBM_PEAK,
+    }}
+
+
+def decode_graph_workload(args, gdn, torch, dev, stream):
+    """A serving loop of 64 decode steps at batch 1 (H=32, d=128, bf16), launched
+    eagerly and as one captured HIP graph: the per-step time shows the launch
+    overhead that a graph removes at this size."""
+    steps, B, H, D = 64, 1, 32, 128
+    g = torch.Generator(device=dev)
+    g.manual_seed(93)
+    ops = []
+    for _ in range(steps):
+        q = torch.randn((B, 1, H, D), generator=g, device=dev)
+        k = torch.nn.functional.normalize(torch.randn((B, 1, H, D), generator=g, device=dev), dim=-1)
+        ops.append(((q * D ** -0.5).bfloat16(), k.bfloat16(), torch.randn((B, 1, H, D), generator=g, device=dev).bfloat16(),
+                    0.9 + 0.1 * torch.rand((B, 1, H), generator=g, device=dev),
+                    torch.rand((B, 1, H), generator=g, device=dev)))
+    state = torch.zeros((B, H, D, D), device=dev)
+    outs = [torch.empty((B, 1, H, D), dtype=torch.bfloat16, device=dev) for _ in range(steps)]
+
+    def loop():
+        for s_ in range(steps):
+            gdn.decode_step(*ops[s_], state, o=outs[s_])
+
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        loop()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        loop()
+    torch.cuda.synchronize()
+
+    def timed(fn, reps=5):
+        ts = []
+        for _ in range(reps):
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            fn()
+            torch.cuda.synchronize()
+            ts.append(time.perf_counter() - t0)
+        return statistics.median(ts) / steps
+    loop()
+    t_eager = timed(loop)
+    t_graph = timed(graph.replay)
+    return {"decode_graph": {
+        "workload": f"{steps} decode steps, B={B} H={H} d={D} bf16, host wall time per step",
+        "eager_us_per_step": t_eager * 1e6, "graph_us_per_step": t_graph * 1e6,
     }}
 
 
@@ -408,6 +461,7 @@ def main():
         extra = extra_workloads(args, gi, gdn, torch, dev, stream, evict)
         extra.update(block_workload(args, gdn, torch, dev, stream, evict))
         extra.update(kda_decode_workload(args, gdn, torch, dev, stream, evict, Dd, state))
+        extra.update(decode_graph_workload(args, gdn, torch, dev, stream))
 
     tokens = B * T
     units = B * H
