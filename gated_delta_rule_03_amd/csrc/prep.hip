@@ -255,9 +255,12 @@ constexpr int kXBytes = 17408;
 }  // namespace
 
 __global__ __launch_bounds__(128, 4) void factors_kernel(PrepArgs<bf16_t> a) {
-  // heads vary fastest across blocks: the blocks in flight at once read
-  // whole tokens' k rows, contiguous in memory
-  const int c = blockIdx.x / unsigned(a.H_v), h = blockIdx.x - c * a.H_v;
+  // Block b runs on XCD b % 8.  XCD x takes chunks x, x + 8, x + 16, ..., and
+  // each chunk's heads one after another: heads vary fastest in time (the
+  // blocks in flight read whole tokens' k rows, contiguous in memory), and a
+  // chunk's alpha and beta lines are fetched into one XCD's L2 only.
+  const unsigned j = blockIdx.x >> 3;
+  const int c = int(8u * (j / unsigned(a.H_v)) + (blockIdx.x & 7u)), h = int(j % unsigned(a.H_v));
   int s, tok0, len;
   if (!a.geo.locate(c, s, tok0, len)) return;
   const int hq = h / a.group;
@@ -490,8 +493,9 @@ static hipError_t launch_prep_t(const Problem &p, const Workspace &ws, hipStream
   const int64_t slots = chunk_slots(p);
   if constexpr (sizeof(T) == 2) {
     if (staged_path(p)) {
-      if (slots * p.H_v > 0x7fffffff) return hipErrorInvalidConfiguration;
-      hipLaunchKernelGGL(factors_kernel, dim3(unsigned(slots * p.H_v)), dim3(128), 0, st, a);
+      const int64_t blocks = 8 * ((slots + 7) / 8) * p.H_v;  // chunk slots rounded up to the XCD count
+      if (blocks > 0x7fffffff) return hipErrorInvalidConfiguration;
+      hipLaunchKernelGGL(factors_kernel, dim3(unsigned(blocks)), dim3(128), 0, st, a);
       return hipGetLastError();
     }
   }
