@@ -102,7 +102,7 @@ using namespace gdn;
 
 extern "C" {
 
-int32_t gdn_version(void) { return 100; }
+int32_t gdn_version(void) { return 200; }  // 0.2.0: block prologue/epilogue, per-channel gate
 
 const char *gdn_status_string(int32_t status) {
   switch (status) {
