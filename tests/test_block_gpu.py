@@ -161,3 +161,22 @@ def test_block_prologue_many_short_sequences(gdn):
     errs = [rel_err(host_f64(t), r, sl) for t, r in zip((q, k, v), ref[:3])]
     log(f"    max rel err q={errs[0]:.3e} k={errs[1]:.3e} v={errs[2]:.3e}")
     assert max(errs) <= TOL["f32"]
+
+
+def test_whole_block_unequal_head_dims(gdn):
+    """Prologue (two launches: q/k at d_k = 64, v at d_v = 128) -> chunked
+    recurrence on the general path -> epilogue, packed, float32, against the
+    float64 oracle of the same composition."""
+    import torch
+    x = gi.block_inputs(1, 0, 2, 4, 64, 128, "f32", seed=380, lengths=(90, 1, 0, 130))
+    log("[block] f32 d_k=64 d_v=128 packed")
+    (q, k, v, alpha, beta), cu = run_prologue(gdn, x, 0.125)
+    o, _ = gdn.chunk_fwd(q, k, v, alpha, beta, chunk=32, cu_seqlens=cu)
+    y = gdn.block_epilogue(o, dev_tensor(x["g_raw"]), o_norm_weight=dev_tensor(x["o_norm"]), eps=1e-6)
+    torch.cuda.synchronize()
+    rq, rk, rv, ra, rb = oracle_prologue(x, 0.125)
+    ro, _ = oracle.forward(rq, rk, rv, ra, rb, cu_seqlens=x["cu_seqlens"])
+    ref = ob.epilogue(ro, x["g_raw"], x["o_norm"], 1e-6)
+    err = rel_err(host_f64(y), ref, slices(x))
+    log(f"    max rel err y={err:.3e}")
+    assert np.all(np.isfinite(host_f64(y))) and err <= TOL["f32"]

@@ -38,6 +38,7 @@ CASES = [
     ("f32", 1, 0, 2, 4, 64, 128, (17, 0, 1, 30)),
     ("f32", 2, 33, 2, 2, 128, 64, None),
     ("bf16", 2, 64, 2, 4, 128, 128, None),
+    ("bf16", 1, 0, 1, 4, 64, 32, (40, 3, 0, 77)),
 ]
 
 
@@ -83,7 +84,8 @@ def test_kda_equal_rates_match_scalar_gate(gdn):
     assert e <= 1e-5
 
 
-@pytest.mark.parametrize("dtype,B,H_qk,H_v,d", [("f32", 3, 1, 2, 32), ("bf16", 256, 32, 32, 128)])
+@pytest.mark.parametrize("dtype,B,H_qk,H_v,d", [("f32", 3, 1, 2, 32), ("f32", 5, 2, 8, 64),
+                                               ("bf16", 256, 32, 32, 128)])
 def test_kda_decode(gdn, dtype, B, H_qk, H_v, d):
     """One decode step from a random state; the bf16 case is the decode bench
     shape (B=256, H=32, d=128), every unit checked."""
