@@ -39,12 +39,12 @@ template <typename T> constexpr int64_t entry_bytes() {
 }
 
 // The staged path: bf16 operands, d_k = 128, d_v a multiple of 32 (the factor
-// kernel and the staged scan).  The scan forms P itself, and the two all-zero
-// T fragments (rows 0-31, columns 32-63) are neither stored nor read, so an
-// entry is 7 KiB: T's six other bf16 fragments in t_slot order
-// (tile_index.hpp), then the gate block.
+// kernel and the staged scan).  The scan forms P itself, and T's zeros are
+// left out: the two all-zero fragments (rows 0-31, columns 32-63) entirely,
+// and the zero halves of the two diagonal fragments 0 and 5 (t_entry_byte,
+// tile_index.hpp).  An entry is 6 KiB: 5 KiB of T, then the gate block.
 inline bool staged_path(const Problem &p) { return p.dtype == 1 && p.d_k == 128 && p.d_v % 32 == 0; }
-constexpr int kStagedGateOffset = 6 * kFragElems * 2;
+constexpr int kStagedGateOffset = 5 * 1024;
 constexpr int64_t kStagedEntryBytes = kStagedGateOffset + kGateBlockBytes;
 inline int64_t entry_stride(const Problem &p) {
   if (staged_path(p)) return kStagedEntryBytes;

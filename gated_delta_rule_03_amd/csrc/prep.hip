@@ -207,7 +207,7 @@ __global__ __launch_bounds__(256) void prep_kernel(PrepArgs<T> a) {
 // workgroup of two waves per (chunk slot, value head); its k rows and gates
 // are copied into LDS with bounds-checked buffer loads (rows past the chunk's
 // end read as zeros, padded slots get beta = 0 and add nothing to the gate).
-// It writes T and the gate block into a 7 KiB entry (launch.hpp); the staged
+// It writes T and the gate block into a 6 KiB entry (launch.hpp); the staged
 // scan forms P from the q and k rows it stages anyway.
 //
 // M = (I + A)^-1 in 16 x 16 blocks.  Wave 1 forms the diagonal blocks A_bb
@@ -313,13 +313,17 @@ __global__ __launch_bounds__(128, 4) void factors_kernel(PrepArgs<bf16_t> a) {
     const f32x4_t bc = lds_load<f32x4_t>(sm + kXB + 4 * (16 * cb + 4 * g));
     return __builtin_convertvector(m * bc, bf16x4_t);
   };
+  // (fragments 0 and 5 keep elements 0-3 only: their upper halves are zero)
   auto put_frag = [&](int f, bf16x4_t lo, bf16x4_t hi) {
-    *reinterpret_cast<bf16x8_t *>(fragT + kFragElems * t_slot(f) + 8 * lane) = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+    if (t_compact(f))
+      *reinterpret_cast<bf16x4_t *>(fragT + t_entry_byte(f) / 2 + 4 * lane) = lo;
+    else
+      *reinterpret_cast<bf16x8_t *>(fragT + t_entry_byte(f) / 2 + 8 * lane) = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
   };
   auto put_half = [&](int f, int hf, bf16x4_t v) {
-    *reinterpret_cast<bf16x4_t *>(fragT + kFragElems * t_slot(f) + 8 * lane + 4 * hf) = v;
+    *reinterpret_cast<bf16x4_t *>(fragT + t_entry_byte(f) / 2 + 8 * lane + 4 * hf) = v;
   };
-  const bf16x4_t zero_h = {0, 0, 0, 0};
+  const bf16x4_t zero_h = {0, 0, 0, 0};  // the zero half of fragments 0 and 5 (not stored)
 
   {
     // gates and betas of all slots for broadcast reads (both waves write the

@@ -221,7 +221,7 @@ __global__ __launch_bounds__(64) void scan_kernel(ScanArgs<T> a) {
 // ---------------------------------------------------------------------------
 constexpr int kStK = 0;        // 64 x 128 bf16 row tile
 constexpr int kStQ = 16384;    // 64 x 128 bf16 row tile
-constexpr int kStT = 32768;    // T's six non-zero fragments, 1 KiB each (t_slot, tile_index.hpp)
+constexpr int kStT = 32768;    // T's six non-zero fragments, a 1 KiB slot each (t_slot, tile_index.hpp)
 constexpr int kStG = 38912;    // gate block: gamma, s, g (64 fp32 each), padding
 constexpr int kStV = 39936;    // 64 x 16 NCH bf16 v block (4 KiB)
 constexpr int kStBytes = 44032;
@@ -381,7 +381,10 @@ __device__ __forceinline__ void scan_copy_waves(const ScanArgs<bf16_t> &a, int l
 #pragma unroll
     for (int i = 0; i < 3; ++i) {
       const int f = CW == 0 ? 2 * i : 5 + i;  // 0, 2, 4 / 5, 6, 7
-      dma16(entry + 1024 * t_slot(f), 16 * lane, base + kStT + 1024 * t_slot(f));
+      // (fragments 0 and 5 are 512 bytes in the entry: lanes 0-31 bring them
+      // to the first half of their slot, lanes 32-63 the start of the next
+      // fragment, which the chain does not read)
+      dma16(entry + t_entry_byte(f), 16 * lane, base + kStT + 1024 * t_slot(f));
     }
     if (CW == 0) dma16(entry + kStagedGateOffset, 16 * lane, base + kStG);
     const i32x4_t v_res = buffer_rsrc(v_src + int64_t(tok0) * v_row_bytes,
@@ -653,7 +656,12 @@ __global__ __launch_bounds__(64 * (NCH + 6)) void scan_kernel_staged(ScanArgs<bf
     for (int rt = 0; rt < 4; ++rt) vt[rt] = lds_read_tr16(st + kStV + kVTile * rt + v_off);
 #pragma unroll
     for (int i = 0; i < 8; ++i)
-      if (i != 1 && i != 3) tf[i].v = lds_load<bf16x8_t>(st + kStT + 1024 * t_slot(i) + 16 * lane);
+      if (t_compact(i)) {  // elements 0-3 staged, 4-7 zero
+        const bf16x4_t lo = lds_load<bf16x4_t>(st + kStT + 1024 * t_slot(i) + 8 * lane);
+        tf[i].v = __builtin_shufflevector(lo, bf16x4_t{0, 0, 0, 0}, 0, 1, 2, 3, 4, 5, 6, 7);
+      } else if (i != 1 && i != 3) {
+        tf[i].v = lds_load<bf16x8_t>(st + kStT + 1024 * t_slot(i) + 16 * lane);
+      }
   };
 
   lds_barrier();  // the first two stages are complete

@@ -108,6 +108,17 @@ __host__ __device__ constexpr int out_acc_col(int cg, int lane) { return 16 * cg
 // 0-5.
 __host__ __device__ constexpr int t_slot(int f) { return f < 4 ? f / 2 : f - 2; }
 
+// ---- T fragments in a staged workspace entry ----
+// Fragments 0 and 5 (rows 0-15 x columns 0-31 and rows 32-47 x columns
+// 32-63) lie on T's diagonal: their elements 4-7 in every lane (contraction
+// indices 16-31 of the fragment, above the diagonal) are zero.  The entry
+// keeps only elements 0-3 of those two, 64 lanes x 8 bytes; the other four
+// are whole, 64 lanes x 16 bytes.  Byte offset of fragment f in the entry:
+__host__ __device__ constexpr bool t_compact(int f) { return f == 0 || f == 5; }
+__host__ __device__ constexpr int t_entry_byte(int f) {
+  return f == 0 ? 0 : f == 2 ? 512 : f == 4 ? 1536 : f == 5 ? 2560 : f == 6 ? 3072 : 4096;
+}
+
 // ---- outputs leaving through the output staging buffer ----
 // 64 token rows x 32 bf16 (64 bytes per row), 16-byte pieces XOR-swizzled by
 // the row: physical piece = piece ^ ((row / 4) mod 4).
