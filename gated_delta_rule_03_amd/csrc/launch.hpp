@@ -42,10 +42,12 @@ template <typename T> constexpr int64_t entry_bytes() {
 // kernel and the staged scan).  The scan forms P itself, and T's zeros are
 // left out: the two all-zero fragments (rows 0-31, columns 32-63) entirely,
 // and the zero halves of the two diagonal fragments 0 and 5 (t_entry_byte,
-// tile_index.hpp).  An entry is 6 KiB: 5 KiB of T, then the gate block.
+// tile_index.hpp).  An entry is 5,888 bytes: 5 KiB of T, then the gate
+// block without its padding (gamma, s, g: 768 bytes; 23 x 256 bytes in all).
 inline bool staged_path(const Problem &p) { return p.dtype == 1 && p.d_k == 128 && p.d_v % 32 == 0; }
 constexpr int kStagedGateOffset = 5 * 1024;
-constexpr int64_t kStagedEntryBytes = kStagedGateOffset + kGateBlockBytes;
+constexpr int kStagedGateBytes = 3 * 64 * 4;
+constexpr int64_t kStagedEntryBytes = kStagedGateOffset + kStagedGateBytes;
 inline int64_t entry_stride(const Problem &p) {
   if (staged_path(p)) return kStagedEntryBytes;
   return p.dtype == 1 ? entry_bytes<uint16_t>() : entry_bytes<float>();

@@ -386,7 +386,9 @@ __device__ __forceinline__ void scan_copy_waves(const ScanArgs<bf16_t> &a, int l
       // fragment, which the chain does not read)
       dma16(entry + t_entry_byte(f), 16 * lane, base + kStT + 1024 * t_slot(f));
     }
-    if (CW == 0) dma16(entry + kStagedGateOffset, 16 * lane, base + kStG);
+    // the gate block is 768 bytes: lanes 48-63 fall out of the resource's
+    // range and write zeros into the slot's padding
+    if (CW == 0) dma16_buf(buffer_rsrc(entry + kStagedGateOffset, kStagedGateBytes), 16 * lane, base + kStG);
     const i32x4_t v_res = buffer_rsrc(v_src + int64_t(tok0) * v_row_bytes,
                                       NCH == 2 ? vblock_valid_bytes(len, v_row_bytes)
                                                : vblock16_valid_bytes(len, v_row_bytes));

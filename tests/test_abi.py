@@ -43,8 +43,8 @@ def test_workspace_query(lib):
     # one entry per (chunk slot, value head).  General path: 16 fragments of
     # 512 elements (1 KiB in bf16, 2 KiB in fp32) + a 1 KiB gate block.
     # Staged path (bf16, d_k = 128, d_v a multiple of 32): T's non-zero
-    # bf16 fragments (four whole, two half) + the gate block, 6 KiB.
-    entry, staged = 16 * 1024 + 1024, 5 * 1024 + 1024
+    # bf16 fragments (four whole, two half) + gamma, s, g: 5,888 bytes.
+    entry, staged = 16 * 1024 + 1024, 5 * 1024 + 768
     w = gdn.chunk_fwd_workspace_bytes(4, 4096, 16, 16, 128, 128, gdn.GDN_BF16, 64, 0)
     assert 4 * 64 * 16 * staged <= w < 4 * 64 * 16 * staged + 4096
     packed = gdn.chunk_fwd_workspace_bytes(1, 1000, 2, 4, 128, 128, gdn.GDN_BF16, 64, 5)
