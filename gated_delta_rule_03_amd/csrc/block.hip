@@ -14,14 +14,16 @@
 // times SiLU(g).
 //
 // Both are HBM-bound: each reads its inputs once and writes its outputs
-// once, and each wave issues all its loads before any arithmetic (a wave
-// that waited for one row at a time would leave HBM mostly idle).
-// Both lay a (token, head) row over one DPP row of 16 lanes, d / 16 channels
-// per lane (16 bytes for bf16 at d = 128), so a row's sum of squares is a DPP
-// sum and one load instruction moves four rows, adjacent in memory.
-// Prologue: a wave takes 32 tokens (16 for float32) of four heads and holds
-// their raw rows and the 3 rows before them in registers; waves over value
-// heads also form alpha and beta.  Epilogue: 16 rows per wave.
+// once, and keeps many loads in flight (a wave that waited for one row at a
+// time would leave HBM mostly idle).  Both lay a (token, head) row over one
+// DPP row of 16 lanes, d / 16 channels per lane (16 bytes for bf16 at
+// d = 128), so a row's sum of squares is a DPP sum and one load instruction
+// moves four rows, adjacent in memory.
+// Prologue: a wave takes 64 tokens of four heads of one tensor and streams
+// their raw rows through a ring of 16 register sets, loading each row 13
+// tokens before it is needed; waves over value heads also form alpha and
+// beta.  Epilogue: 16 rows per wave, every load issued before any
+// arithmetic.
 #include "launch.hpp"
 
 namespace gdn {
