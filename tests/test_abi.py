@@ -125,7 +125,7 @@ def test_block_argument_errors(lib):
     assert prologue(lib, q_scale=float("inf")) == 1
     assert prologue(lib, B=2, cu=p, n=2) == 1      # a packed batch has B == 1
     assert prologue(lib, cu=p, n=0) == 1           # ... and at least one sequence
-    # one wave per (32 tokens, head): 2^16 token ranges x 3 * 2^15 heads exceeds a 32-bit grid
+    # the grid bound (one wave per 16 tokens and head at most): 2^17 x 3 * 2^15 exceeds 32 bits
     assert prologue(lib, B=1, T=1 << 21, H_qk=1 << 15, H_v=1 << 15, d_k=16, d_v=16) == 2
     # a token's row of one tensor must stay below 2^24 bytes: 2^15 heads x 128 x 4 bytes = 2^24
     assert prologue(lib, B=1, T=8, H_qk=1 << 15, H_v=1 << 15, d_k=128, d_v=128) == 2
