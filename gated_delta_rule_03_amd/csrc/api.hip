@@ -54,7 +54,9 @@ static int32_t check_shapes(int32_t B, int32_t T, int32_t H_qk, int32_t H_v, int
   if (dtype != GDN_F32 && dtype != GDN_BF16) return GDN_ERROR_NOT_SUPPORTED;
   if (!dim_ok(d_k) || !dim_ok(d_v)) return GDN_ERROR_NOT_SUPPORTED;
   if (H_v % H_qk != 0) return GDN_ERROR_NOT_SUPPORTED;
+  // Token and chunk indices are 32-bit in the kernels.
   const int64_t tokens = int64_t(B) * T;
+  if (tokens > std::numeric_limits<int32_t>::max()) return GDN_ERROR_NOT_SUPPORTED;
   if (tokens * std::max<int64_t>(H_v, H_qk) * std::max(d_k, d_v) > (int64_t(1) << 40))
     return GDN_ERROR_NOT_SUPPORTED;
   return GDN_SUCCESS;
@@ -83,7 +85,8 @@ static int32_t make_problem(int32_t B, int32_t T, int32_t H_qk, int32_t H_v, int
   int32_t st = check_common(B, T, H_qk, H_v, d_k, d_v, dtype, q, k, v, alpha, beta, o);
   if (st != GDN_SUCCESS) return st;
   if (cu_seqlens) {
-    if (B != 1 || n_seqs < 0) return GDN_ERROR_INVALID_VALUE;
+    // a packed batch with tokens must hold at least one sequence
+    if (B != 1 || n_seqs < 0 || (n_seqs == 0 && T > 0)) return GDN_ERROR_INVALID_VALUE;
   } else {
     if (n_seqs != 0 && n_seqs != B) return GDN_ERROR_INVALID_VALUE;
     n_seqs = B;

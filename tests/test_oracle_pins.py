@@ -385,3 +385,58 @@ def test_pins_catch_planted_mistakes(mutant):
     results = [check_walkthrough(lib), check_figure6(lib), check_additive_brute_force(lib),
                check_whole_sequence_solve(lib)]
     assert not all(results), f"mutant {mutant} passed every pin"
+
+
+# ---------------------------------------------------------------------------
+# The bf16 widening the oracle applies to uint16 bit patterns
+# ---------------------------------------------------------------------------
+
+def test_bf16_widening_exact_values():
+    """bf16 is the top half of an IEEE binary32: sign, 8 exponent bits, 7
+    mantissa bits.  Bit patterns with known values: 1, -2.5, the smallest
+    subnormal 2^-133, the largest finite value (2 - 2^-7) 2^127, infinities
+    and a NaN."""
+    bits = np.array([0x3F80, 0xC020, 0x0001, 0x8001, 0x7F7F, 0x7F80, 0xFF80, 0x0000, 0x8000,
+                     0x3E80, 0x4049], dtype=np.uint16)
+    want = np.array([1.0, -2.5, 2.0 ** -133, -(2.0 ** -133), (2.0 - 2.0 ** -7) * 2.0 ** 127,
+                     np.inf, -np.inf, 0.0, -0.0, 0.25, 3.140625])
+    got = oracle._as_f64(bits)
+    assert got.dtype == np.float64
+    assert np.array_equal(got, want)
+    assert np.signbit(got[8]) and not np.signbit(got[7])
+    assert np.isnan(oracle._as_f64(np.array([0x7FC0], dtype=np.uint16)))[0]
+
+
+def test_bf16_widening_matches_torch_on_every_pattern():
+    """Every one of the 65,536 patterns widens as torch's bfloat16 -> float64."""
+    import torch
+    bits = np.arange(1 << 16, dtype=np.uint32).astype(np.uint16)
+    ours = oracle._as_f64(bits)
+    ref = torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).to(torch.float64).numpy()
+    nan = np.isnan(ref)
+    assert np.array_equal(np.isnan(ours), nan)
+    assert np.array_equal(ours[~nan], ref[~nan])
+    assert np.array_equal(np.signbit(ours[~nan]), np.signbit(ref[~nan]))
+
+
+def test_forward_on_bf16_bits_equals_forward_on_their_values():
+    """A batch handed over as bf16 bit patterns gives the result of the same
+    batch handed over as the float64 values torch assigns those patterns."""
+    import torch
+    rng = np.random.default_rng(11)
+    B, T, H_qk, H_v, dk, dv = 2, 9, 1, 2, 8, 4
+    def bf16(shape, scale=1.0):
+        x = torch.from_numpy((rng.standard_normal(shape) * scale).astype(np.float32))
+        return x.to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    q, k, v = bf16((B, T, H_qk, dk), 0.3), bf16((B, T, H_qk, dk), 0.3), bf16((B, T, H_v, dv))
+    alpha = rng.uniform(0.5, 1.0, (B, T, H_v))
+    beta = rng.uniform(0.0, 1.0, (B, T, H_v))
+    def widen(a):
+        return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to(torch.float64).numpy()
+    o_bits, h_bits = oracle.forward(q, k, v, alpha, beta)
+    o_vals, h_vals = oracle.forward(widen(q), widen(k), widen(v), alpha, beta)
+    assert np.array_equal(o_bits, o_vals) and np.array_equal(h_bits, h_vals)
+    # and the bits are not read as integers: the result differs from that reading
+    o_int, _ = oracle.forward(q.astype(np.float64), k.astype(np.float64), v.astype(np.float64),
+                              alpha, beta)
+    assert not np.allclose(o_int, o_bits)

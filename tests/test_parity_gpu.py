@@ -10,7 +10,7 @@ import pytest
 
 import gdn_inputs as gi
 import oracle
-from gpu_util import TOL, host_f64, log, to_device, unit_rel_errors, dev_tensor
+from gpu_util import ELEM_TOL, TOL, dev_tensor, host_f64, local_errors, log, to_device, unit_rel_errors
 
 pytestmark = pytest.mark.gpu
 
@@ -46,10 +46,13 @@ def check(gdn, path, w, h0=None, chunk=None, tol=None, units=None):
     o_ref, hT_ref = oracle.forward(w.q, w.k, w.v, w.alpha, w.beta, cu_seqlens=w.cu_seqlens,
                                    h0=h0)
     eo, eh, unit = unit_rel_errors(o, hT, o_ref, hT_ref, w.seq_slices(), w.spec.H_v)
+    ew, ee = local_errors(o, o_ref, w.seq_slices(), w.spec.H_v)
     bar = tol or TOL[w.spec.dtype]
-    log(f"    max rel err o={eo:.3e} hT={eh:.3e} (worst unit {unit}) bar={bar}")
+    log(f"    max rel err o={eo:.3e} hT={eh:.3e} (worst unit {unit}) bar={bar}; "
+        f"64-token windows o={ew:.3e}; elementwise o={ee:.3e} bar={ELEM_TOL[w.spec.dtype]}")
     assert np.all(np.isfinite(o)) and np.all(np.isfinite(hT))
     assert eo <= bar and eh <= bar
+    assert ew <= bar and ee <= ELEM_TOL[w.spec.dtype]
     return o, hT
 
 
@@ -234,5 +237,6 @@ def test_config3_decode_full(gdn):
     torch.cuda.synchronize()
     o_ref, s_ref = oracle.decode(state, w.q, w.k, w.v, w.alpha, w.beta)
     eo, eh, unit = unit_rel_errors(host_f64(o), host_f64(st), o_ref, s_ref, w.seq_slices(), 32)
-    log(f"    max rel err o={eo:.3e} state={eh:.3e} (worst unit {unit})")
-    assert eo <= TOL["bf16"] and eh <= TOL["bf16"]
+    _, ee = local_errors(host_f64(o), o_ref, w.seq_slices(), 32)
+    log(f"    max rel err o={eo:.3e} state={eh:.3e} (worst unit {unit}); elementwise o={ee:.3e}")
+    assert eo <= TOL["bf16"] and eh <= TOL["bf16"] and ee <= ELEM_TOL["bf16"]
