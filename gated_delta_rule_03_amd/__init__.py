@@ -8,7 +8,9 @@ other implementation here and no fallback.  PyTorch only provides device
 memory and streams.
 
 Names follow the C ABI: ``recurrent_fwd``, ``chunk_fwd`` (with
-``chunk_fwd_workspace_bytes``), ``decode_step``, the GDN block's
+``chunk_fwd_workspace_bytes``; ``seg_chunks`` selects the segment-parallel
+form of ``gdn_chunk_fwd_segmented``, with ``chunk_fwd_plan_segments`` and
+``chunk_fwd_segmented_workspace_bytes``), ``decode_step``, the GDN block's
 ``block_prologue`` and ``block_epilogue``, and the per-channel-gate
 ``kda_recurrent_fwd`` and ``kda_decode_step``.
 """
@@ -20,7 +22,8 @@ from typing import Optional, Tuple
 
 __all__ = [
     "GDNError", "lib_path", "load", "version", "status_string", "recurrent_fwd",
-    "chunk_fwd", "chunk_fwd_workspace_bytes", "decode_step", "block_prologue", "block_epilogue",
+    "chunk_fwd", "chunk_fwd_workspace_bytes", "chunk_fwd_plan_segments",
+    "chunk_fwd_segmented_workspace_bytes", "decode_step", "block_prologue", "block_epilogue",
     "kda_recurrent_fwd", "kda_decode_step", "GDN_F32", "GDN_BF16",
 ]
 
@@ -33,7 +36,8 @@ _LIB_PATH = os.path.join(_HERE, "libgdn.so")
 _lib: Optional[ctypes.CDLL] = None
 
 EXPORTS = ["gdn_version", "gdn_status_string", "gdn_recurrent_fwd",
-           "gdn_chunk_fwd_workspace_bytes", "gdn_chunk_fwd", "gdn_decode_step",
+           "gdn_chunk_fwd_workspace_bytes", "gdn_chunk_fwd", "gdn_chunk_fwd_plan_segments",
+           "gdn_chunk_fwd_segmented_workspace_bytes", "gdn_chunk_fwd_segmented", "gdn_decode_step",
            "gdn_block_prologue", "gdn_block_epilogue", "gdn_kda_recurrent_fwd", "gdn_kda_decode_step"]
 
 
@@ -71,6 +75,12 @@ def load() -> ctypes.CDLL:
     lib.gdn_chunk_fwd_workspace_bytes.restype = ctypes.c_size_t
     lib.gdn_chunk_fwd.argtypes = fwd + [i32, vp, ctypes.c_size_t, vp]
     lib.gdn_chunk_fwd.restype = i32
+    lib.gdn_chunk_fwd_plan_segments.argtypes = [i32] * 9
+    lib.gdn_chunk_fwd_plan_segments.restype = i32
+    lib.gdn_chunk_fwd_segmented_workspace_bytes.argtypes = [i32] * 10
+    lib.gdn_chunk_fwd_segmented_workspace_bytes.restype = ctypes.c_size_t
+    lib.gdn_chunk_fwd_segmented.argtypes = fwd + [i32, i32, vp, ctypes.c_size_t, vp]
+    lib.gdn_chunk_fwd_segmented.restype = i32
     lib.gdn_decode_step.argtypes = [i32] * 6 + [vp, vp, vp, fp, fp, fp, vp, vp]
     lib.gdn_kda_recurrent_fwd.argtypes = fwd + [vp]
     lib.gdn_kda_recurrent_fwd.restype = i32
@@ -195,30 +205,58 @@ def chunk_fwd_workspace_bytes(B, T, H_qk, H_v, d_k, d_v, dtype_code, chunk=64, n
                                                     n_seqs))
 
 
+def chunk_fwd_plan_segments(B, T, H_qk, H_v, d_k, d_v, dtype_code, chunk=64, n_seqs=0) -> int:
+    """Chunks per segment that gdn_chunk_fwd uses for these sizes (0: one pass)."""
+    n = int(load().gdn_chunk_fwd_plan_segments(B, T, H_qk, H_v, d_k, d_v, dtype_code, chunk, n_seqs))
+    if n < 0:
+        raise GDNError(2, "gdn_chunk_fwd_plan_segments")
+    return n
+
+
+def chunk_fwd_segmented_workspace_bytes(B, T, H_qk, H_v, d_k, d_v, dtype_code, chunk=64, n_seqs=0,
+                                        seg_chunks=0) -> int:
+    return int(load().gdn_chunk_fwd_segmented_workspace_bytes(B, T, H_qk, H_v, d_k, d_v, dtype_code,
+                                                              chunk, n_seqs, seg_chunks))
+
+
 def chunk_fwd(q, k, v, alpha, beta, *, chunk: int = 64, cu_seqlens=None, h0=None, o=None,
-              hT=None, workspace=None, output_final_state: bool = True, stream=None) -> Tuple:
+              hT=None, workspace=None, output_final_state: bool = True, seg_chunks=None,
+              stream=None) -> Tuple:
     """Chunked gated delta rule (WY/UT form).  Returns (o, hT).
 
-    ``workspace``: an optional uint8 device tensor of at least
-    ``chunk_fwd_workspace_bytes(...)`` bytes; allocated per call when omitted.
+    ``seg_chunks``: None lets gdn_chunk_fwd choose between one pass and the
+    segment-parallel form; 0 forces one pass, n > 0 segments of n chunks
+    (gdn_chunk_fwd_segmented).
+    ``workspace``: an optional uint8 device tensor of at least the queried
+    workspace bytes; allocated per call when omitted.
     """
     torch = _torch()
     dims, n_seqs, o, hT = _fwd_args(q, k, v, alpha, beta, cu_seqlens, h0, o, hT,
                                     output_final_state)
-    need = chunk_fwd_workspace_bytes(*dims, chunk, n_seqs)
+    if seg_chunks is None:
+        need = chunk_fwd_workspace_bytes(*dims, chunk, n_seqs)
+        where = "gdn_chunk_fwd_workspace_bytes"
+    else:
+        need = chunk_fwd_segmented_workspace_bytes(*dims, chunk, n_seqs, int(seg_chunks))
+        where = "gdn_chunk_fwd_segmented_workspace_bytes"
     if need == 0:
-        raise GDNError(2, "gdn_chunk_fwd_workspace_bytes")
+        raise GDNError(2, where)
     if workspace is None:
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
     elif workspace.numel() * workspace.element_size() < need:
         raise ValueError(f"workspace holds {workspace.numel() * workspace.element_size()} "
                          f"bytes, {need} needed")
-    st = load().gdn_chunk_fwd(*dims, _ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(beta),
-                              _ptr(cu_seqlens), n_seqs, _ptr(h0), _ptr(o), _ptr(hT), chunk,
-                              _ptr(workspace), workspace.numel() * workspace.element_size(),
-                              _stream(stream))
+    args = (*dims, _ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(beta), _ptr(cu_seqlens), n_seqs,
+            _ptr(h0), _ptr(o), _ptr(hT), chunk)
+    ws = (_ptr(workspace), workspace.numel() * workspace.element_size(), _stream(stream))
+    if seg_chunks is None:
+        st = load().gdn_chunk_fwd(*args, *ws)
+        where = "gdn_chunk_fwd"
+    else:
+        st = load().gdn_chunk_fwd_segmented(*args, int(seg_chunks), *ws)
+        where = "gdn_chunk_fwd_segmented"
     if st != GDN_SUCCESS:
-        raise GDNError(st, "gdn_chunk_fwd")
+        raise GDNError(st, where)
     return o, hT
 
 

@@ -99,6 +99,146 @@ static int32_t make_problem(int32_t B, int32_t T, int32_t H_qk, int32_t H_v, int
 
 static int32_t status_of(hipError_t e) { return e == hipSuccess ? GDN_SUCCESS : GDN_ERROR_LAUNCH; }
 
+// ---------------------------------------------------------------------------
+// Segment-parallel chunked forward.  A sequence scan visits its chunks in
+// order, so a problem with few (sequence, value head) units leaves most of the
+// GPU idle however long the sequences are.  Cutting every sequence into
+// segments of seg_chunks chunks gives more, shorter units: one transition-mode
+// scan over the segments (each segment's affine map), a fold of the maps in
+// sequence order (the state entering every segment, and the final state), and
+// the ordinary scan over the segments from those states (the outputs).
+// ---------------------------------------------------------------------------
+
+// Chunks per segment for a problem (0: one pass).  Segments pay off when the
+// one-pass scan would keep fewer than half of the 256 compute units busy
+// (units x d_v / 16 blocks of 16 columns); then the segment length is chosen
+// so that the output pass has about 256 blocks of 32 columns, with at least
+// four chunks per segment.
+static int32_t plan_segment_chunks(const Problem &p) {
+  const int64_t units = int64_t(p.n_seqs) * p.H_v;
+  const int64_t max_chunks = ceil_div(p.T, p.chunk);  // the longest sequence's chunks, at most
+  if (units == 0 || units * (p.d_v / 16) >= 128 || max_chunks < 16) return 0;
+  const int64_t blocks32 = units * std::max(1, p.d_v / 32);
+  const int64_t segs = std::max<int64_t>(2, ceil_div(256, blocks32));
+  const int64_t seg = std::max<int64_t>(4, ceil_div(max_chunks, segs));
+  return seg >= max_chunks ? 0 : int32_t(seg);
+}
+
+struct SegWorkspace {
+  int32_t *seg_cu, *seg_first;
+  void *base;          // the segment batch's own workspace
+  float *mb, *s_in;
+};
+
+// The segment batch: one packed batch over the whole token axis, one
+// sequence per segment, started from the fold's states.
+static int32_t n_seg_bound(const Problem &p, int32_t seg_chunks) {
+  const int64_t seg_tokens = int64_t(seg_chunks) * p.chunk;
+  if (p.cu_seqlens) return int32_t(ceil_div(p.T, seg_tokens) + p.n_seqs);
+  return int32_t(int64_t(p.B) * ceil_div(p.T, seg_tokens));
+}
+static Problem segment_problem(const Problem &p, int32_t seg_chunks, const SegWorkspace *sw) {
+  Problem ps = p;
+  ps.B = 1;
+  ps.T = int32_t(p.n_tokens());
+  ps.n_seqs = n_seg_bound(p, seg_chunks);
+  static const int32_t kLayoutOnly = 0;
+  ps.cu_seqlens = sw ? sw->seg_cu : &kLayoutOnly;  // selects the packed layout
+  ps.h0 = sw ? sw->s_in : nullptr;
+  ps.hT = nullptr;  // the fold writes the final states
+  return ps;
+}
+static size_t seg_workspace_layout(const Problem &p, int32_t seg_chunks, void *base, SegWorkspace *sw) {
+  const Problem ps = segment_problem(p, seg_chunks, nullptr);
+  const int64_t nseg = ps.n_seqs;
+  const size_t cu_bytes = align256(size_t(nseg + 1) * sizeof(int32_t));
+  const size_t first_bytes = align256(size_t(p.n_seqs + 1) * sizeof(int32_t));
+  const size_t ws_bytes = workspace_layout(ps, nullptr, nullptr);
+  const size_t mb_bytes = align256(size_t(nseg) * p.H_v * p.d_k * (p.d_k + p.d_v) * sizeof(float));
+  const size_t sin_bytes = align256(size_t(nseg) * p.H_v * p.d_k * p.d_v * sizeof(float));
+  if (sw) {
+    char *b = static_cast<char *>(base);
+    sw->seg_cu = reinterpret_cast<int32_t *>(b);
+    sw->seg_first = reinterpret_cast<int32_t *>(b + cu_bytes);
+    sw->base = b + cu_bytes + first_bytes;
+    sw->mb = reinterpret_cast<float *>(b + cu_bytes + first_bytes + ws_bytes);
+    sw->s_in = reinterpret_cast<float *>(b + cu_bytes + first_bytes + ws_bytes + mb_bytes);
+  }
+  return cu_bytes + first_bytes + ws_bytes + mb_bytes + sin_bytes;
+}
+
+static size_t chunk_workspace_bytes(const Problem &p, int32_t seg_chunks) {
+  return seg_chunks > 0 ? seg_workspace_layout(p, seg_chunks, nullptr, nullptr)
+                        : workspace_layout(p, nullptr, nullptr);
+}
+
+// Problem for the workspace queries (no tensors).
+static Problem query_problem(int32_t B, int32_t T, int32_t H_qk, int32_t H_v, int32_t d_k, int32_t d_v,
+                             int32_t dtype, int32_t chunk, int32_t n_seqs) {
+  Problem p{};
+  p.B = B;
+  p.T = T;
+  p.H_qk = H_qk;
+  p.H_v = H_v;
+  p.d_k = d_k;
+  p.d_v = d_v;
+  p.dtype = dtype;
+  // A packed batch (B == 1, n_seqs > 0) reserves ceil(T / chunk) + n_seqs
+  // chunk slots, which also covers a single uniform sequence.
+  const bool packed = B == 1 && n_seqs > 0;
+  p.n_seqs = packed ? n_seqs : B;
+  static const int32_t kLayoutOnly = 0;
+  p.cu_seqlens = packed ? &kLayoutOnly : nullptr;  // selects the packed layout; never read
+  p.chunk = chunk;
+  return p;
+}
+
+static bool query_ok(int32_t B, int32_t T, int32_t H_qk, int32_t H_v, int32_t d_k, int32_t d_v, int32_t dtype,
+                     int32_t chunk, int32_t n_seqs) {
+  return check_shapes(B, T, H_qk, H_v, d_k, d_v, dtype) == GDN_SUCCESS &&
+         (chunk == 16 || chunk == 32 || chunk == 64) && n_seqs >= 0;
+}
+
+// Segment lengths that keep every index in range: segments of at most 2^31
+// tokens, a segment count that fits a 32-bit sequence count.
+static bool seg_chunks_ok(const Problem &p, int32_t seg_chunks) {
+  if (seg_chunks < 0) return false;
+  if (seg_chunks == 0) return true;
+  if (int64_t(seg_chunks) * p.chunk > std::numeric_limits<int32_t>::max()) return false;
+  const int64_t seg_tokens = int64_t(seg_chunks) * p.chunk;
+  const int64_t bound = p.cu_seqlens ? ceil_div(p.T, seg_tokens) + p.n_seqs
+                                     : int64_t(p.B) * ceil_div(p.T, seg_tokens);
+  return bound < (int64_t(1) << 30) && bound * p.H_v * std::max(p.d_v, 32) / 16 < 0x7fffffff;
+}
+
+static int32_t run_chunk_fwd(Problem p, int32_t seg_chunks, void *workspace, size_t workspace_bytes,
+                             hipStream_t s) {
+  const size_t need = chunk_workspace_bytes(p, seg_chunks);
+  if (!workspace || workspace_bytes < need) return GDN_ERROR_WORKSPACE;
+  if (reinterpret_cast<uintptr_t>(workspace) & 255) return GDN_ERROR_WORKSPACE;
+  if (seg_chunks == 0) {
+    Workspace ws;
+    workspace_layout(p, workspace, &ws);
+    hipError_t e = launch_chunk_offsets(p, ws, s);
+    if (e == hipSuccess) e = launch_prep(p, ws, s);
+    if (e == hipSuccess) e = launch_scan(p, ws, s);
+    return status_of(e);
+  }
+  SegWorkspace sw;
+  seg_workspace_layout(p, seg_chunks, workspace, &sw);
+  const Problem ps = segment_problem(p, seg_chunks, &sw);
+  Workspace ws;
+  workspace_layout(ps, sw.base, &ws);
+  hipError_t e = launch_segment_map(p, seg_chunks * p.chunk, ps.n_seqs, sw.seg_cu, sw.seg_first, s);
+  if (e == hipSuccess) e = launch_chunk_offsets(ps, ws, s);
+  if (e == hipSuccess) e = launch_prep(ps, ws, s);
+  if (e == hipSuccess) e = launch_scan(ps, ws, s, sw.mb);
+  if (e == hipSuccess) e = launch_fold(sw.mb, p.h0, sw.s_in, p.hT, sw.seg_first, p.n_seqs, ps.n_seqs, p.H_v, p.d_k,
+                                       p.d_v, s);
+  if (e == hipSuccess) e = launch_scan(ps, ws, s);
+  return status_of(e);
+}
+
 }  // namespace gdn
 
 using namespace gdn;
@@ -132,25 +272,24 @@ int32_t gdn_recurrent_fwd(int32_t B, int32_t T, int32_t H_qk, int32_t H_v, int32
 size_t gdn_chunk_fwd_workspace_bytes(int32_t B, int32_t T, int32_t H_qk, int32_t H_v,
                                      int32_t d_k, int32_t d_v, int32_t dtype, int32_t chunk,
                                      int32_t n_seqs) {
-  if (check_shapes(B, T, H_qk, H_v, d_k, d_v, dtype) != GDN_SUCCESS) return 0;
-  if (chunk != 16 && chunk != 32 && chunk != 64) return 0;
-  if (n_seqs < 0) return 0;
-  Problem p{};
-  p.B = B;
-  p.T = T;
-  p.H_qk = H_qk;
-  p.H_v = H_v;
-  p.d_k = d_k;
-  p.d_v = d_v;
-  p.dtype = dtype;
-  // A packed batch (B == 1, n_seqs > 0) reserves ceil(T / chunk) + n_seqs
-  // chunk slots, which also covers a single uniform sequence.
-  const bool packed = B == 1 && n_seqs > 0;
-  p.n_seqs = packed ? n_seqs : B;
-  static const int32_t kLayoutOnly = 0;
-  p.cu_seqlens = packed ? &kLayoutOnly : nullptr;  // selects the packed layout; never read
-  p.chunk = chunk;
-  return workspace_layout(p, nullptr, nullptr);
+  if (!query_ok(B, T, H_qk, H_v, d_k, d_v, dtype, chunk, n_seqs)) return 0;
+  const Problem p = query_problem(B, T, H_qk, H_v, d_k, d_v, dtype, chunk, n_seqs);
+  return chunk_workspace_bytes(p, plan_segment_chunks(p));
+}
+
+int32_t gdn_chunk_fwd_plan_segments(int32_t B, int32_t T, int32_t H_qk, int32_t H_v, int32_t d_k,
+                                    int32_t d_v, int32_t dtype, int32_t chunk, int32_t n_seqs) {
+  if (!query_ok(B, T, H_qk, H_v, d_k, d_v, dtype, chunk, n_seqs)) return -1;
+  return plan_segment_chunks(query_problem(B, T, H_qk, H_v, d_k, d_v, dtype, chunk, n_seqs));
+}
+
+size_t gdn_chunk_fwd_segmented_workspace_bytes(int32_t B, int32_t T, int32_t H_qk, int32_t H_v,
+                                               int32_t d_k, int32_t d_v, int32_t dtype, int32_t chunk,
+                                               int32_t n_seqs, int32_t seg_chunks) {
+  if (!query_ok(B, T, H_qk, H_v, d_k, d_v, dtype, chunk, n_seqs)) return 0;
+  const Problem p = query_problem(B, T, H_qk, H_v, d_k, d_v, dtype, chunk, n_seqs);
+  if (!seg_chunks_ok(p, seg_chunks)) return 0;
+  return chunk_workspace_bytes(p, seg_chunks);
 }
 
 int32_t gdn_chunk_fwd(int32_t B, int32_t T, int32_t H_qk, int32_t H_v, int32_t d_k, int32_t d_v,
@@ -164,16 +303,23 @@ int32_t gdn_chunk_fwd(int32_t B, int32_t T, int32_t H_qk, int32_t H_v, int32_t d
   if (st != GDN_SUCCESS) return st;
   if (chunk != 16 && chunk != 32 && chunk != 64) return GDN_ERROR_NOT_SUPPORTED;
   p.chunk = chunk;
-  const size_t need = workspace_layout(p, nullptr, nullptr);
-  if (!workspace || workspace_bytes < need) return GDN_ERROR_WORKSPACE;
-  if (reinterpret_cast<uintptr_t>(workspace) & 255) return GDN_ERROR_WORKSPACE;
-  Workspace ws;
-  workspace_layout(p, workspace, &ws);
-  hipStream_t s = static_cast<hipStream_t>(stream);
-  hipError_t e = launch_chunk_offsets(p, ws, s);
-  if (e == hipSuccess) e = launch_prep(p, ws, s);
-  if (e == hipSuccess) e = launch_scan(p, ws, s);
-  return status_of(e);
+  return run_chunk_fwd(p, plan_segment_chunks(p), workspace, workspace_bytes, static_cast<hipStream_t>(stream));
+}
+
+int32_t gdn_chunk_fwd_segmented(int32_t B, int32_t T, int32_t H_qk, int32_t H_v, int32_t d_k, int32_t d_v,
+                                int32_t dtype, const void *q, const void *k, const void *v,
+                                const float *alpha, const float *beta, const int32_t *cu_seqlens,
+                                int32_t n_seqs, const float *h0, void *o, float *hT, int32_t chunk,
+                                int32_t seg_chunks, void *workspace, size_t workspace_bytes, void *stream) {
+  Problem p;
+  int32_t st = make_problem(B, T, H_qk, H_v, d_k, d_v, dtype, q, k, v, alpha, beta, cu_seqlens,
+                            n_seqs, h0, o, hT, &p);
+  if (st != GDN_SUCCESS) return st;
+  if (chunk != 16 && chunk != 32 && chunk != 64) return GDN_ERROR_NOT_SUPPORTED;
+  p.chunk = chunk;
+  if (seg_chunks < 0) return GDN_ERROR_INVALID_VALUE;
+  if (!seg_chunks_ok(p, seg_chunks)) return GDN_ERROR_NOT_SUPPORTED;
+  return run_chunk_fwd(p, seg_chunks, workspace, workspace_bytes, static_cast<hipStream_t>(stream));
 }
 
 int32_t gdn_decode_step(int32_t B, int32_t H_qk, int32_t H_v, int32_t d_k, int32_t d_v,

@@ -62,8 +62,13 @@ size_t workspace_layout(const Problem &p, void *base, Workspace *ws);
 
 hipError_t launch_chunk_offsets(const Problem &p, const Workspace &ws, hipStream_t st);
 hipError_t launch_prep(const Problem &p, const Workspace &ws, hipStream_t st);
-hipError_t launch_scan(const Problem &p, const Workspace &ws, hipStream_t st);
+hipError_t launch_scan(const Problem &p, const Workspace &ws, hipStream_t st, float *mb = nullptr);
 hipError_t launch_recurrent(const Problem &p, hipStream_t st);
+// Segment-parallel path (seqmap.hip, fold.hip).
+hipError_t launch_segment_map(const Problem &p, int seg_tokens, int n_seg_bound, int32_t *seg_cu,
+                              int32_t *seg_first, hipStream_t st);
+hipError_t launch_fold(const float *mb, const float *h0, float *s_in, float *hT, const int32_t *seg_first,
+                       int n_seqs, int n_segs, int H_v, int d_k, int d_v, hipStream_t st);
 
 // The block prologue and epilogue (block.hip).  Prologue: raw = q_raw, k_raw,
 // v_raw and out = q, k, v; epilogue: raw[0] = o, raw[1] = the output gate's

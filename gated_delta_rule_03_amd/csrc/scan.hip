@@ -21,6 +21,15 @@
 //
 // Blocks of one unit are numbered so that they share blockIdx mod 8: they land
 // on the same XCD and share its L2 for the chunk's k, q, T and P.
+//
+// Transition mode (mode 1) serves the segment-parallel path: a sequence is cut
+// into segments that are scanned as independent units, and each segment's
+// effect on the state is the affine map S_out = M S_in + B.  The delta rule is
+// linear in (S, v) ("From KV Cache to a State Matrix", section "Chunkwise
+// training for DeltaNet": the chunk updates compose), so B is the segment's
+// final state from S_in = 0, and M (d_k x d_k) is the final state of the same
+// scan over d_k extra columns started from the identity with v = 0.  Mode 1
+// computes both, as d_v + d_k state columns, and writes no outputs.
 #include "launch.hpp"
 #include "stage.hpp"
 
@@ -35,7 +44,19 @@ struct ScanArgs {
   float *hT;
   int H_qk, H_v, d_k, d_v, group, n_units, n_colblk;
   SeqGeom geo;
+  // transition mode: column blocks cb >= n_colblk_v carry M; the result goes
+  // to mb [n_seqs, H_v, d_k, d_v + d_k] (B in columns 0 .. d_v - 1, M after)
+  int mode, n_colblk_v;
+  float *mb;
 };
+
+// Initial state of column `col` of a block: h0 (mode 0), zero (mode 1, the
+// columns of B) or the identity (mode 1, the columns of M).
+__device__ __forceinline__ float initial_state(const float *h0, int64_t st_base, int row, int col,
+                                               int d_v, int mode, bool is_m) {
+  if (mode == 1) return is_m && row == col ? 1.0f : 0.0f;
+  return h0 ? h0[st_base + int64_t(row) * d_v + col] : 0.0f;
+}
 
 
 // ---------------------------------------------------------------------------
@@ -49,7 +70,9 @@ __global__ __launch_bounds__(64) void scan_kernel(ScanArgs<T> a) {
   decode_block(blockIdx.x, a.n_colblk, u, cb);
   if (u >= a.n_units) return;
   const int s = a.geo.ordered(u / a.H_v), h = u % a.H_v, hq = h / a.group;
-  const int col = 16 * cb + (lane & 15);  // this lane's state column
+  const bool is_m = a.mode == 1 && cb >= a.n_colblk_v;       // a column block of M
+  const int col = 16 * (is_m ? cb - a.n_colblk_v : cb) + (lane & 15);  // this lane's state column
+  const int vcol = is_m ? (lane & 15) : col;                  // v column read (M blocks: v = 0)
   const int nkt = a.d_k >> 4;             // 16-row tiles of the state
   const int nkb = (a.d_k + 31) >> 5;      // 32-deep contraction blocks over d_k
 
@@ -59,9 +82,9 @@ __global__ __launch_bounds__(64) void scan_kernel(ScanArgs<T> a) {
 #pragma unroll
   for (int rt = 0; rt < 8; ++rt) {
     S[rt] = zero4();
-    if (rt < nkt && a.h0)
+    if (rt < nkt)
       for (int e = 0; e < 4; ++e)
-        S[rt][e] = a.h0[st_base + int64_t(16 * rt + 4 * (lane >> 4) + e) * a.d_v + col];
+        S[rt][e] = initial_state(a.h0, st_base, 16 * rt + 4 * (lane >> 4) + e, col, a.d_v, a.mode, is_m);
   }
 
   int start, end;
@@ -78,7 +101,7 @@ __global__ __launch_bounds__(64) void scan_kernel(ScanArgs<T> a) {
     const int len = min(a.geo.chunk, end - tok0);
     const T *kb = a.k + int64_t(tok0) * qk_stride + int64_t(hq) * a.d_k;
     const T *qb = a.q + int64_t(tok0) * qk_stride + int64_t(hq) * a.d_k;
-    const T *vb = a.v + int64_t(tok0) * v_stride + int64_t(h) * a.d_v + col;
+    const T *vb = a.v + int64_t(tok0) * v_stride + int64_t(h) * a.d_v + vcol;
     const T *entry = reinterpret_cast<const T *>(a.entries + (int64_t(c) * a.H_v + h) *
                                                                  entry_bytes<T>());
     const float *gent = reinterpret_cast<const float *>(entry + 16 * kFragElems);
@@ -121,7 +144,7 @@ __global__ __launch_bounds__(64) void scan_kernel(ScanArgs<T> a) {
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int t = 16 * rt + 4 * (lane >> 4) + e;
-        const float vv = t < len ? to_f32(vb[int64_t(t) * v_stride]) : 0.0f;
+        const float vv = t < len && !is_m ? to_f32(vb[int64_t(t) * v_stride]) : 0.0f;
         X[rt][e] = vv - gam[rt][e] * Y[rt][e];
       }
     // U = T X
@@ -138,6 +161,7 @@ __global__ __launch_bounds__(64) void scan_kernel(ScanArgs<T> a) {
     // O = gamma (Q S) + P U
 #pragma unroll
     for (int rt = 0; rt < 4; ++rt) {
+      if (a.mode == 1) break;
       f32x4_t acc;
       for (int e = 0; e < 4; ++e) acc[e] = gam[rt][e] * OQ[rt][e];
 #pragma unroll
@@ -174,7 +198,14 @@ __global__ __launch_bounds__(64) void scan_kernel(ScanArgs<T> a) {
     }
   }
 
-  if (a.hT) {
+  if (a.mode == 1) {
+    const int ld = a.d_v + a.d_k;
+    float *dst = a.mb + (int64_t(s) * a.H_v + h) * a.d_k * ld + (is_m ? a.d_v : 0) + col;
+#pragma unroll
+    for (int rt = 0; rt < 8; ++rt)
+      if (rt < nkt)
+        for (int e = 0; e < 4; ++e) dst[int64_t(16 * rt + 4 * (lane >> 4) + e) * ld] = S[rt][e];
+  } else if (a.hT) {
 #pragma unroll
     for (int rt = 0; rt < 8; ++rt)
       if (rt < nkt)
@@ -327,11 +358,14 @@ __device__ __forceinline__ void scan_form_p(const lds_t *st, const int (&kq_off)
 // outputs for the block's NCH column groups; ROLE 2: copy wave CW (0 .. 3)
 // issues half the k (CW even) or q (CW odd) tile copies of each stage; copy
 // waves 0 and 1 also half the T fragments and half the v block each, and copy
-// wave 0 the gate block.
-template <int CW, int ROLE, int NCH>
+// wave 0 the gate block.  In transition mode (MODE 1) nothing reads q or the
+// outputs: the output waves only keep step at the barriers and the q copies
+// are not issued.  `cbv` is the column block whose v is staged.
+template <int CW, int ROLE, int NCH, int MODE>
 __device__ __forceinline__ void scan_copy_waves(const ScanArgs<bf16_t> &a, int lane, int h, int hq, int cb,
-                                                int start, int end, int c_first, int n_chunks) {
-  constexpr bool kCopies = ROLE == 2, kOutputs = ROLE == 1;
+                                                int cbv, int start, int end, int c_first, int n_chunks) {
+  constexpr bool kCopies = ROLE == 2, kOutputs = ROLE == 1 && MODE == 0;
+  constexpr bool kTileCopies = kCopies && !(MODE == 1 && (CW & 1));
   constexpr int W = 16 * NCH;  // columns of the block
   const int r0 = lane & 15, g = lane >> 4;
   const int C = a.geo.chunk;
@@ -351,6 +385,7 @@ __device__ __forceinline__ void scan_copy_waves(const ScanArgs<bf16_t> &a, int l
   // A copy wave's share of a stage's k (or q) tile, 32 rows (copies
   // 8 (CW / 2) .. + 7), in two halves of four copies.
   auto stage_part = [&](int part, int cc, char *base_mem) {
+    if (!kTileCopies) return;
     const int tok0 = start + cc * C;
     const int len = min(C, end - tok0);
     const i32x4_t kq_res = buffer_rsrc(kq_src + int64_t(tok0) * kq_row_bytes, rowtile_valid_bytes(len, kq_row_bytes));
@@ -363,7 +398,7 @@ __device__ __forceinline__ void scan_copy_waves(const ScanArgs<bf16_t> &a, int l
   // and v rows of the first half, copy wave 1 T fragments 5, 6, 7 and the
   // second half (copy waves 2 and 3 issue tile copies only).
   const int64_t ebytes = kStagedEntryBytes;
-  const char *const v_src = reinterpret_cast<const char *>(a.v) + (int64_t(h) * a.d_v + W * cb) * 2;
+  const char *const v_src = reinterpret_cast<const char *>(a.v) + (int64_t(h) * a.d_v + W * cbv) * 2;
   const uint32_t v_row_bytes = uint32_t(2 * v_stride);
   constexpr int kVCopies = NCH == 2 ? 2 : 1;
   uint32_t v_voff[kVCopies];
@@ -401,7 +436,7 @@ __device__ __forceinline__ void scan_copy_waves(const ScanArgs<bf16_t> &a, int l
     stage_part(0, cc, base_mem);
     stage_part(1, cc, base_mem);
   };
-  constexpr int kLoads = kStageLoadsCopy + (CW >= 2 ? 0 : 3 + (CW == 0 ? 1 : 0) + kVCopies);
+  constexpr int kLoads = (kTileCopies ? kStageLoadsCopy : 0) + (CW >= 2 ? 0 : 3 + (CW == 0 ? 1 : 0) + kVCopies);
   auto wait_all_but_newest_stage = [&]() { wait_vmem_upto<kLoads>(); };
   int kq_off[4][2];
 #pragma unroll
@@ -518,8 +553,7 @@ __device__ __forceinline__ void scan_copy_waves(const ScanArgs<bf16_t> &a, int l
     if (kOutputs && cc > 0) outputs(cc - 1, ex_prev);
     if (kOutputs)
       scan_form_p<CW>(lds_ptr(const_cast<char *>(cur)), kq_off, lane, op, [&]() {});
-    else
-      stage_part(1, pf, dst);
+    if (kCopies) stage_part(1, pf, dst);
     if (kCopies) wait_all_but_newest_stage();
     lds_barrier();
   };
@@ -545,7 +579,7 @@ __device__ __forceinline__ void scan_copy_waves(const ScanArgs<bf16_t> &a, int l
 // issue every copy of a stage.  One chain wave per block doubles the blocks
 // of a problem with few units (a long single sequence) at the same per-block
 // traffic.
-template <int NCH>
+template <int NCH, int MODE>
 __global__ __launch_bounds__(64 * (NCH + 6)) void scan_kernel_staged(ScanArgs<bf16_t> a) {
   constexpr int W = 16 * NCH;
   const int tid = threadIdx.x, lane = tid & 63;
@@ -567,29 +601,34 @@ __global__ __launch_bounds__(64 * (NCH + 6)) void scan_kernel_staged(ScanArgs<bf
   const int C = a.geo.chunk;
   const int c_first = a.geo.first_chunk(s);
   const int n_chunks = max(0, min((end - start + C - 1) / C, a.geo.n_slots - c_first));
+  // transition mode: blocks past the value columns carry M (v = 0; the v of
+  // column block 0 is staged so that every copy stays inside v)
+  const bool is_m = MODE == 1 && cb >= a.n_colblk_v;
+  const int cbv = is_m ? 0 : cb;
+  const int cbs = is_m ? cb - a.n_colblk_v : cb;  // column block within B or M
 
   if (wave == NCH) {
-    scan_copy_waves<0, 1, NCH>(a, lane, h, hq, cb, start, end, c_first, n_chunks);
+    scan_copy_waves<0, 1, NCH, MODE>(a, lane, h, hq, cb, cbv, start, end, c_first, n_chunks);
     return;
   }
   if (wave == NCH + 1) {
-    scan_copy_waves<1, 1, NCH>(a, lane, h, hq, cb, start, end, c_first, n_chunks);
+    scan_copy_waves<1, 1, NCH, MODE>(a, lane, h, hq, cb, cbv, start, end, c_first, n_chunks);
     return;
   }
   if (wave == NCH + 2) {
-    scan_copy_waves<0, 2, NCH>(a, lane, h, hq, cb, start, end, c_first, n_chunks);
+    scan_copy_waves<0, 2, NCH, MODE>(a, lane, h, hq, cb, cbv, start, end, c_first, n_chunks);
     return;
   }
   if (wave == NCH + 3) {
-    scan_copy_waves<1, 2, NCH>(a, lane, h, hq, cb, start, end, c_first, n_chunks);
+    scan_copy_waves<1, 2, NCH, MODE>(a, lane, h, hq, cb, cbv, start, end, c_first, n_chunks);
     return;
   }
   if (wave == NCH + 4) {
-    scan_copy_waves<2, 2, NCH>(a, lane, h, hq, cb, start, end, c_first, n_chunks);
+    scan_copy_waves<2, 2, NCH, MODE>(a, lane, h, hq, cb, cbv, start, end, c_first, n_chunks);
     return;
   }
   if (wave == NCH + 5) {
-    scan_copy_waves<3, 2, NCH>(a, lane, h, hq, cb, start, end, c_first, n_chunks);
+    scan_copy_waves<3, 2, NCH, MODE>(a, lane, h, hq, cb, cbv, start, end, c_first, n_chunks);
     return;
   }
 
@@ -614,18 +653,16 @@ __global__ __launch_bounds__(64 * (NCH + 6)) void scan_kernel_staged(ScanArgs<bf
   constexpr int kVTile = NCH == 2 ? 1024 : 512;
   const int v_off = NCH == 2 ? vtile_byte(4 * g + (r0 >> 2), 16 * wave + 4 * (r0 & 3))
                              : vtile16_byte(4 * g + (r0 >> 2), 4 * (r0 & 3));
-  const int col = W * cb + 16 * wave + r0;  // this lane's state column
+  const int col = W * cbs + 16 * wave + r0;  // this lane's state column
   const int ex_off = kExWave * wave + 16 * lane;
 
   // ---- state ----
   f32x4_t S[8];
   const int64_t st_base = (int64_t(s) * a.H_v + h) * 128 * a.d_v;
 #pragma unroll
-  for (int rt = 0; rt < 8; ++rt) {
-    S[rt] = zero4();
-    if (a.h0)
-      for (int e = 0; e < 4; ++e) S[rt][e] = a.h0[st_base + int64_t(16 * rt + 4 * g + e) * a.d_v + col];
-  }
+  for (int rt = 0; rt < 8; ++rt)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) S[rt][e] = initial_state(a.h0, st_base, 16 * rt + 4 * g + e, col, a.d_v, MODE, is_m);
 
   // Operands of the chunk about to run, read from its stage right after the
   // barrier that completes it: gate factors (rows 16 rt + 4 g + e of this
@@ -655,7 +692,7 @@ __global__ __launch_bounds__(64 * (NCH + 6)) void scan_kernel_staged(ScanArgs<bf
                               lds_load_single<bf16x4_t>(pk + kq_off[kk][1]));
       }
 #pragma unroll
-    for (int rt = 0; rt < 4; ++rt) vt[rt] = lds_read_tr16(st + kStV + kVTile * rt + v_off);
+    for (int rt = 0; rt < 4; ++rt) vt[rt] = is_m ? bf16x4_t{0, 0, 0, 0} : lds_read_tr16(st + kStV + kVTile * rt + v_off);
 #pragma unroll
     for (int i = 0; i < 8; ++i)
       if (t_compact(i)) {  // elements 0-3 staged, 4-7 zero
@@ -688,8 +725,9 @@ __global__ __launch_bounds__(64 * (NCH + 6)) void scan_kernel_staged(ScanArgs<bf
     for (int kk = 0; kk < 4; ++kk)
 #pragma unroll
       for (int rt = 0; rt < 4; ++rt) Y[rt] = mfma(kf[kk][rt], Sf[kk], kk == 0 ? zero4() : Y[rt]);
+    if (MODE == 0)
 #pragma unroll
-    for (int kk = 0; kk < 4; ++kk) lds_store<bf16x8_t>(ex + kExS + 1024 * kk, Sf[kk].v);
+      for (int kk = 0; kk < 4; ++kk) lds_store<bf16x8_t>(ex + kExS + 1024 * kk, Sf[kk].v);
 
     // K^T fragments for the state update (transposed reads of the k tile),
     // issued early so that they have landed when the update starts
@@ -719,9 +757,10 @@ __global__ __launch_bounds__(64 * (NCH + 6)) void scan_kernel_staged(ScanArgs<bf
         Ua[rt] = mfma(tf[rt * 2 + kk], Xf[kk], kk == 0 ? zero4() : Ua[rt]);
 
     Frag<bf16_t> Usf[2];
+    if (MODE == 0)
 #pragma unroll
-    for (int kk = 0; kk < 2; ++kk)
-      lds_store<bf16x8_t>(ex + kExU + 1024 * kk, frag_from_acc<bf16_t>(Ua[2 * kk], Ua[2 * kk + 1]).v);
+      for (int kk = 0; kk < 2; ++kk)
+        lds_store<bf16x8_t>(ex + kExU + 1024 * kk, frag_from_acc<bf16_t>(Ua[2 * kk], Ua[2 * kk + 1]).v);
 #pragma unroll
     for (int rt = 0; rt < 4; ++rt) Ua[rt] *= sc[rt];
     Usf[0] = frag_from_acc<bf16_t>(Ua[0], Ua[1]);
@@ -752,7 +791,13 @@ __global__ __launch_bounds__(64 * (NCH + 6)) void scan_kernel_staged(ScanArgs<bf
   }
   wait_vmem();  // the trailing copies
 
-  if (a.hT) {
+  if (MODE == 1) {
+    const int ld = a.d_v + 128;
+    float *dst = a.mb + (int64_t(s) * a.H_v + h) * 128 * ld + (is_m ? a.d_v : 0) + col;
+#pragma unroll
+    for (int rt = 0; rt < 8; ++rt)
+      for (int e = 0; e < 4; ++e) dst[int64_t(16 * rt + 4 * g + e) * ld] = S[rt][e];
+  } else if (a.hT) {
 #pragma unroll
     for (int rt = 0; rt < 8; ++rt)
       for (int e = 0; e < 4; ++e) a.hT[st_base + int64_t(16 * rt + 4 * g + e) * a.d_v + col] = S[rt][e];
@@ -765,7 +810,7 @@ __global__ __launch_bounds__(64 * (NCH + 6)) void scan_kernel_staged(ScanArgs<bf
 constexpr int64_t kNarrowBelowBlocks = 128;
 
 template <typename T>
-static ScanArgs<T> scan_args(const Problem &p, const Workspace &ws, int colblk_width) {
+static ScanArgs<T> scan_args(const Problem &p, const Workspace &ws, int colblk_width, float *mb) {
   ScanArgs<T> a;
   a.q = static_cast<const T *>(p.q);
   a.k = static_cast<const T *>(p.k);
@@ -780,30 +825,34 @@ static ScanArgs<T> scan_args(const Problem &p, const Workspace &ws, int colblk_w
   a.d_v = p.d_v;
   a.group = p.H_v / p.H_qk;
   a.n_units = p.n_seqs * p.H_v;
-  a.n_colblk = p.d_v / colblk_width;
+  a.n_colblk_v = p.d_v / colblk_width;
+  a.mode = mb ? 1 : 0;
+  a.mb = mb;
+  a.n_colblk = a.n_colblk_v + (mb ? p.d_k / colblk_width : 0);
   a.geo = make_geom(p, &ws);
   return a;
 }
 
-hipError_t launch_scan(const Problem &p, const Workspace &ws, hipStream_t st) {
+hipError_t launch_scan(const Problem &p, const Workspace &ws, hipStream_t st, float *mb) {
   const bool staged = staged_path(p);
   const int64_t units8 = (int64_t(p.n_seqs) * p.H_v + 7) / 8 * 8;
-  const bool narrow = staged && units8 * (p.d_v / 32) < kNarrowBelowBlocks;
+  const int cols = p.d_v + (mb ? p.d_k : 0);  // state columns per unit (transition mode: B and M)
+  const bool narrow = staged && units8 * (cols / 32) < kNarrowBelowBlocks;
   const int width = staged && !narrow ? 32 : 16;
-  const int64_t blocks = units8 * (p.d_v / width);
+  const int64_t blocks = units8 * (cols / width);
   if (blocks == 0) return hipSuccess;
-  if (staged && narrow) {
-    hipLaunchKernelGGL(scan_kernel_staged<1>, dim3(unsigned(blocks)), dim3(64 * 7), 0, st,
-                       scan_args<bf16_t>(p, ws, width));
-  } else if (staged) {
-    hipLaunchKernelGGL(scan_kernel_staged<2>, dim3(unsigned(blocks)), dim3(64 * 8), 0, st,
-                       scan_args<bf16_t>(p, ws, width));
+  if (blocks > 0x7fffffff) return hipErrorInvalidConfiguration;
+  const dim3 grid = dim3(static_cast<unsigned>(blocks));
+  if (staged) {
+    const ScanArgs<bf16_t> a = scan_args<bf16_t>(p, ws, width, mb);
+    if (narrow && mb) hipLaunchKernelGGL((scan_kernel_staged<1, 1>), grid, dim3(64 * 7), 0, st, a);
+    else if (narrow) hipLaunchKernelGGL((scan_kernel_staged<1, 0>), grid, dim3(64 * 7), 0, st, a);
+    else if (mb) hipLaunchKernelGGL((scan_kernel_staged<2, 1>), grid, dim3(64 * 8), 0, st, a);
+    else hipLaunchKernelGGL((scan_kernel_staged<2, 0>), grid, dim3(64 * 8), 0, st, a);
   } else if (p.dtype == 1) {
-    hipLaunchKernelGGL(scan_kernel<bf16_t>, dim3(unsigned(blocks)), dim3(64), 0, st,
-                       scan_args<bf16_t>(p, ws, width));
+    hipLaunchKernelGGL(scan_kernel<bf16_t>, grid, dim3(64), 0, st, scan_args<bf16_t>(p, ws, width, mb));
   } else {
-    hipLaunchKernelGGL(scan_kernel<float>, dim3(unsigned(blocks)), dim3(64), 0, st,
-                       scan_args<float>(p, ws, width));
+    hipLaunchKernelGGL(scan_kernel<float>, grid, dim3(64), 0, st, scan_args<float>(p, ws, width, mb));
   }
   return hipGetLastError();
 }

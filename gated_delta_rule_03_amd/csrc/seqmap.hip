@@ -63,6 +63,64 @@ __global__ __launch_bounds__(256) void chunk_offsets_kernel(SeqGeom geo, int32_t
   }
 }
 
+// Segment map of the segment-parallel path: every sequence is cut into
+// segments of `seg_tokens` tokens (a multiple of the chunk size, so segment
+// boundaries are chunk boundaries and the chunks are those of the whole
+// sequence); its last segment may be shorter.  seg_first[s] = number of
+// segments in sequences 0..s-1; seg_cu[i] = first token of segment i, and
+// entries past the last segment hold the end of the last sequence (empty
+// segments).  The segments then run as a packed batch.
+__global__ __launch_bounds__(256) void segment_map_kernel(SeqGeom geo, int seg_tokens, int n_seg_bound,
+                                                          int32_t *seg_cu, int32_t *seg_first) {
+  __shared__ int32_t sh[256];
+  __shared__ int32_t carry;
+  const int tid = threadIdx.x;
+  if (tid == 0) {
+    seg_first[0] = 0;
+    carry = 0;
+  }
+  __syncthreads();
+  for (int base = 0; base < geo.n_seqs; base += 256) {
+    const int s = base + tid;
+    int cnt = 0, start = 0, end = 0;
+    if (s < geo.n_seqs) {
+      geo.seq_bounds(s, start, end);
+      cnt = (end - start + seg_tokens - 1) / seg_tokens;
+    }
+    sh[tid] = cnt;
+    __syncthreads();
+    for (int d = 1; d < 256; d <<= 1) {
+      const int add = tid >= d ? sh[tid - d] : 0;
+      __syncthreads();
+      sh[tid] += add;
+      __syncthreads();
+    }
+    if (s < geo.n_seqs) {
+      const int first = carry + sh[tid] - cnt;
+      seg_first[s + 1] = first + cnt;
+      for (int j = 0; j < cnt && first + j < n_seg_bound; ++j) seg_cu[first + j] = start + j * seg_tokens;
+    }
+    __syncthreads();
+    if (tid == 255) carry += sh[255];
+    __syncthreads();
+  }
+  // the end of the last sequence closes the last segment and fills the rest
+  int last_end = 0;
+  if (geo.n_seqs > 0) {
+    int start;
+    geo.seq_bounds(geo.n_seqs - 1, start, last_end);
+  }
+  for (int i = min(carry, n_seg_bound) + tid; i <= n_seg_bound; i += 256) seg_cu[i] = last_end;
+}
+
+hipError_t launch_segment_map(const Problem &p, int seg_tokens, int n_seg_bound, int32_t *seg_cu,
+                              int32_t *seg_first, hipStream_t st) {
+  SeqGeom geo = make_geom(p, nullptr);
+  hipLaunchKernelGGL(segment_map_kernel, dim3(1), dim3(256), 0, st, geo, seg_tokens, n_seg_bound, seg_cu,
+                     seg_first);
+  return hipGetLastError();
+}
+
 hipError_t launch_chunk_offsets(const Problem &p, const Workspace &ws, hipStream_t st) {
   if (!p.cu_seqlens) return hipSuccess;
   SeqGeom geo = make_geom(p, &ws);

@@ -99,7 +99,8 @@ int32_t gdn_recurrent_fwd(int32_t B, int32_t T, int32_t H_qk, int32_t H_v, int32
 /*
  * Bytes of device workspace gdn_chunk_fwd needs for these sizes (0 when the
  * arguments are unsupported).  The bound holds for every cu_seqlens with the
- * given T and n_seqs.
+ * given T and n_seqs.  It includes the segment-parallel form's buffers when
+ * gdn_chunk_fwd_plan_segments picks that form for these sizes.
  */
 size_t gdn_chunk_fwd_workspace_bytes(int32_t B, int32_t T, int32_t H_qk, int32_t H_v,
                                      int32_t d_k, int32_t d_v, int32_t dtype, int32_t chunk,
@@ -130,6 +131,46 @@ int32_t gdn_chunk_fwd(int32_t B, int32_t T, int32_t H_qk, int32_t H_v, int32_t d
                       const float *alpha, const float *beta, const int32_t *cu_seqlens,
                       int32_t n_seqs, const float *h0, void *o, float *hT, int32_t chunk,
                       void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * Segment-parallel form of gdn_chunk_fwd (same result, up to rounding).
+ *
+ * The chunk updates of a sequence compose: the effect of a run of chunks on
+ * the state is one affine map S_out = M S_in + B, because the delta rule is
+ * linear in the state and the values ("From KV Cache to a State Matrix:
+ * Linear Attention and DeltaNet", section "Chunkwise training for DeltaNet";
+ * "Attention as Matrix Algebra", section 8).  Each sequence is cut into
+ * segments of `seg_chunks` chunks (its last segment may be shorter); the
+ * segments are scanned as independent units for their maps (B from a zero
+ * state, M from the identity with the values set to zero), the maps are
+ * folded in sequence order in fp32 (the state entering each segment, and the
+ * final state), and the segments are scanned again from those states for the
+ * outputs.  This spreads a problem with few (sequence, value head) units --
+ * a long single sequence -- over the whole GPU, at about three times the
+ * scan work.  gdn_chunk_fwd takes this form by itself when the one-pass scan
+ * would keep fewer than half of the GPU's compute units busy.
+ *
+ * gdn_chunk_fwd_plan_segments: the segment length gdn_chunk_fwd uses for these
+ *   sizes, in chunks (0 = one pass; -1 = unsupported arguments).
+ * gdn_chunk_fwd_segmented_workspace_bytes: workspace bytes of
+ *   gdn_chunk_fwd_segmented for the given seg_chunks (0 = unsupported).
+ *   gdn_chunk_fwd_workspace_bytes is this value for the planned length.
+ * gdn_chunk_fwd_segmented: arguments as gdn_chunk_fwd, plus
+ *   seg_chunks  chunks per segment, >= 0 (0 = one pass, as gdn_chunk_fwd
+ *               without segments).  GDN_ERROR_INVALID_VALUE when negative;
+ *               GDN_ERROR_NOT_SUPPORTED when a segment would exceed 2^31 - 1
+ *               tokens or the batch would need 2^30 segments or more.
+ */
+int32_t gdn_chunk_fwd_plan_segments(int32_t B, int32_t T, int32_t H_qk, int32_t H_v, int32_t d_k,
+                                    int32_t d_v, int32_t dtype, int32_t chunk, int32_t n_seqs);
+size_t gdn_chunk_fwd_segmented_workspace_bytes(int32_t B, int32_t T, int32_t H_qk, int32_t H_v,
+                                               int32_t d_k, int32_t d_v, int32_t dtype, int32_t chunk,
+                                               int32_t n_seqs, int32_t seg_chunks);
+int32_t gdn_chunk_fwd_segmented(int32_t B, int32_t T, int32_t H_qk, int32_t H_v, int32_t d_k, int32_t d_v,
+                                int32_t dtype, const void *q, const void *k, const void *v,
+                                const float *alpha, const float *beta, const int32_t *cu_seqlens,
+                                int32_t n_seqs, const float *h0, void *o, float *hT, int32_t chunk,
+                                int32_t seg_chunks, void *workspace, size_t workspace_bytes, void *stream);
 
 /*
  * gdn_decode_step -- one new token per sequence, state updated in place.

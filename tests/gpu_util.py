@@ -12,16 +12,19 @@ sequence, say):
   * windowed: the same ratio over every 64-token window of a unit's outputs,
     max_w |o - o_ref| / max_w |o_ref|, held to the same bars;
   * elementwise: |o - o_ref| / (|o_ref| + 1e-3 max_s |o_ref|) per element,
-    reported, and held to ELEM_TOL (derived in the design notes: bf16 outputs
-    carry absolute errors of order 2^-9 of the terms that cancel into them, so
-    an element near zero is judged against the 1e-3 floor).
+    reported, and held to ELEM_TOL.  For float32 inputs that is a real bar
+    (errors ~1e-6 of the unit's scale).  With bf16 operands an output carries
+    an absolute error of order 2^-9 of the terms that sum into it, which is
+    about twice the 1e-3 floor, so near-zero elements score O(1) however
+    correct the kernel is; the bf16 bar only catches gross failures, and the
+    windowed metric is the local check.
 """
 import sys
 
 import numpy as np
 
 TOL = {"f32": 1e-4, "bf16": 2e-2}
-ELEM_TOL = {"f32": 1e-2, "bf16": 1.0}
+ELEM_TOL = {"f32": 1e-2, "bf16": 16.0}
 WINDOW = 64
 
 

@@ -166,8 +166,49 @@ def test_host_path_reaches_launch_without_gpu(lib):
     assert lib.gdn_recurrent_fwd(*base, None) == 4
     ws = ctypes.c_void_p(0x100000)
     assert lib.gdn_chunk_fwd(*base, 64, ws, 1 << 30, None) == 4
+    assert lib.gdn_chunk_fwd_segmented(*base, 64, 0, ws, 1 << 30, None) == 4
+    assert lib.gdn_chunk_fwd_segmented(*base, 64, 1, ws, 1 << 30, None) == 4
     assert lib.gdn_decode_step(2, 1, 1, 64, 64, 1, p, p, p, p, p, p, p, None) == 4
     assert lib.gdn_kda_recurrent_fwd(*base, None) == 4
     assert lib.gdn_kda_decode_step(2, 1, 1, 64, 64, 1, p, p, p, p, p, p, p, None) == 4
     assert prologue(lib) == 4
     assert lib.gdn_block_epilogue(1, 8, 1, 64, 0, p, p, None, 1e-6, p, None) == 4
+
+
+def test_segment_plan_and_workspace(lib):
+    bf = gdn.GDN_BF16
+    # a full batch runs in one pass; a few long units are cut into segments
+    assert gdn.chunk_fwd_plan_segments(4, 4096, 16, 16, 128, 128, bf, 64, 0) == 0
+    assert gdn.chunk_fwd_plan_segments(1, 65536, 16, 16, 128, 128, bf, 64, 0) == 0
+    seg = gdn.chunk_fwd_plan_segments(1, 65536, 2, 2, 128, 128, bf, 64, 0)
+    assert 4 <= seg < 1024
+    assert gdn.chunk_fwd_plan_segments(1, 256, 1, 1, 128, 128, bf, 64, 0) == 0   # too short to cut
+    assert lib.gdn_chunk_fwd_plan_segments(1, 64, 1, 1, 48, 64, bf, 64, 0) == -1
+    # gdn_chunk_fwd's query covers the planned form
+    one = gdn.chunk_fwd_segmented_workspace_bytes(1, 65536, 2, 2, 128, 128, bf, 64, 0, 0)
+    planned = gdn.chunk_fwd_segmented_workspace_bytes(1, 65536, 2, 2, 128, 128, bf, 64, 0, seg)
+    assert gdn.chunk_fwd_workspace_bytes(1, 65536, 2, 2, 128, 128, bf, 64, 0) == planned
+    nseg = 1024 // seg + (1024 % seg > 0)
+    # + segment offsets, maps [seg, H, 128, 256] and entry states [seg, H, 128, 128] in fp32
+    assert planned >= one + nseg * 2 * 128 * (256 + 128) * 4
+    assert gdn.chunk_fwd_workspace_bytes(4, 4096, 16, 16, 128, 128, bf, 64, 0) == \
+        gdn.chunk_fwd_segmented_workspace_bytes(4, 4096, 16, 16, 128, 128, bf, 64, 0, 0)
+    # packed: a bound for every cu_seqlens with these totals
+    packed = gdn.chunk_fwd_segmented_workspace_bytes(1, 1000, 2, 4, 64, 32, gdn.GDN_F32, 32, 5, 2)
+    assert packed > gdn.chunk_fwd_segmented_workspace_bytes(1, 1000, 2, 4, 64, 32, gdn.GDN_F32, 32, 5, 0)
+    assert gdn.chunk_fwd_segmented_workspace_bytes(1, 1000, 2, 4, 64, 32, gdn.GDN_F32, 32, 5, -1) == 0
+
+
+def test_segmented_argument_errors(lib):
+    p = ctypes.c_void_p(0x1000)
+    base = [1, 8, 1, 1, 64, 64, 0, p, p, p, p, p, None, 0, None, p, None]
+    assert lib.gdn_chunk_fwd_segmented(*base, 64, -1, p, 1 << 30, None) == 1   # negative length
+    assert lib.gdn_chunk_fwd_segmented(*base, 48, 2, p, 1 << 30, None) == 2    # unsupported chunk
+    assert lib.gdn_chunk_fwd_segmented(*base, 64, 2, None, 1 << 30, None) == 3  # no workspace
+    assert lib.gdn_chunk_fwd_segmented(*base, 64, 2, p, 64, None) == 3          # too small
+    # a segment longer than 2^31 - 1 tokens
+    assert lib.gdn_chunk_fwd_segmented(*base, 64, 1 << 26, p, 1 << 30, None) == 2
+    bad = list(base)
+    bad[2] = 3
+    bad[3] = 4
+    assert lib.gdn_chunk_fwd_segmented(*bad, 64, 2, p, 1 << 30, None) == 2      # H_v not a multiple of H_qk
