@@ -145,11 +145,31 @@ def device_inputs(torch, dev, spec, n_tokens, B, seed):
     return q, k, v, alpha.float().contiguous(), beta.float().contiguous()
 
 
+def timed_calls(args, torch, stream, evict, call):
+    """Median seconds of ``call`` over several calls, each after an eviction."""
+    ms = []
+    for i in range(2 + max(3, args.steps // 4)):
+        evict(4)
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        call()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        if i >= 2:
+            ms.append(e0.elapsed_time(e1))
+    return statistics.median(ms) * 1e-3
+
+
 def extra_workloads(args, gi, gdn, torch, dev, stream, evict):
-    """Chunked-forward throughput on the long-context and variable-length workloads."""
+    """Chunked-forward throughput on the long-context and variable-length
+    workloads.  The long-context workload is also timed through the
+    segment-parallel form, as given (16 heads) and at two heads (one GPU's
+    share of an eight-way head split), next to the one-pass scan."""
     out = {}
-    for key, idx in (("long_context", 4), ("varlen", 5)):
-        spec = gi.config(idx)
+    cases = (("long_context", gi.config(4), None), ("long_context_2heads",
+             gi.config(4, H_qk=2, H_v=2, name="long-2heads"), None), ("varlen", gi.config(5), None))
+    for key, spec, _ in cases:
         if spec.packed_seqs:
             lengths = gi.packed_lengths(spec)
             n_tokens, B = int(sum(lengths)), 1
@@ -161,26 +181,25 @@ def extra_workloads(args, gi, gdn, torch, dev, stream, evict):
         q, k, v, alpha, beta = device_inputs(torch, dev, spec, n_tokens, B, seed=spec.seed)
         o = torch.empty_like(v)
         hT = torch.empty((n_seqs, spec.H_v, spec.d_k, spec.d_v), dtype=torch.float32, device=dev)
-        need = gdn.chunk_fwd_workspace_bytes(B, n_tokens // B, spec.H_qk, spec.H_v, spec.d_k, spec.d_v,
-                                             gdn.GDN_BF16, spec.chunk, n_seqs if cu is not None else 0)
-        ws = torch.empty(need, dtype=torch.uint8, device=dev)
+        n_arg = n_seqs if cu is not None else 0
+        dims = (B, n_tokens // B, spec.H_qk, spec.H_v, spec.d_k, spec.d_v, gdn.GDN_BF16, spec.chunk, n_arg)
+        plan = gdn.chunk_fwd_plan_segments(*dims)
+        # the one-pass scan, the planned form, and (long context) fixed segment lengths
+        forms = [0] if plan == 0 else [0, plan]
+        if key.startswith("long_context"):
+            forms += [s for s in (32, 64, 128) if s not in forms]
+        times = {}
+        for seg in forms:
+            need = gdn.chunk_fwd_segmented_workspace_bytes(*dims, seg)
+            ws = torch.empty(need, dtype=torch.uint8, device=dev)
 
-        def call():
-            gdn.chunk_fwd(q, k, v, alpha, beta, chunk=spec.chunk, cu_seqlens=cu, o=o, hT=hT, workspace=ws,
-                          stream=stream)
+            def call():
+                gdn.chunk_fwd(q, k, v, alpha, beta, chunk=spec.chunk, cu_seqlens=cu, o=o, hT=hT, workspace=ws,
+                              seg_chunks=seg, stream=stream)
 
-        ms = []
-        for i in range(2 + max(3, args.steps // 4)):
-            evict(4)
-            e0 = torch.cuda.Event(enable_timing=True)
-            e1 = torch.cuda.Event(enable_timing=True)
-            e0.record(stream)
-            call()
-            e1.record(stream)
-            torch.cuda.synchronize()
-            if i >= 2:
-                ms.append(e0.elapsed_time(e1))
-        t = statistics.median(ms) * 1e-3
+            times[seg] = timed_calls(args, torch, stream, evict, call)
+            del ws
+        t = times[plan]
         units = n_seqs * spec.H_v
         flops = n_tokens * spec.H_v * PREFILL_FLOPS_PER_TOKEN_UNIT
         byts = n_tokens * (2 * spec.H_qk * spec.d_k * 2 + 2 * spec.H_v * spec.d_v * 2 + 8 * spec.H_v) + \
@@ -189,8 +208,11 @@ def extra_workloads(args, gi, gdn, torch, dev, stream, evict):
                                 f"H_v={spec.H_v} d={spec.d_k} bf16 chunk {spec.chunk}",
                     "tokens_per_s": n_tokens / t, "us_per_call": t * 1e6,
                     "hbm_frac": byts / t / HBM_PEAK, "mfma_frac": flops / t / MFMA_BF16_PEAK,
+                    "segment_chunks": plan,
                     "inputs": "drawn on the device with the generator's shapes and distributions"}
-        del q, k, v, alpha, beta, o, hT, ws
+        if len(forms) > 1:
+            out[key]["us_by_segment_chunks"] = {str(sg): tm * 1e6 for sg, tm in times.items()}
+        del q, k, v, alpha, beta, o, hT
     return out
 
 

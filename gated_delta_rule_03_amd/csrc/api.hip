@@ -110,17 +110,22 @@ static int32_t status_of(hipError_t e) { return e == hipSuccess ? GDN_SUCCESS : 
 // ---------------------------------------------------------------------------
 
 // Chunks per segment for a problem (0: one pass).  Segments pay off when the
-// one-pass scan would keep fewer than half of the 256 compute units busy
-// (units x d_v / 16 blocks of 16 columns); then the segment length is chosen
-// so that the output pass has about 256 blocks of 32 columns, with at least
-// four chunks per segment.
+// one-pass scan has fewer than 128 blocks of 32 value columns (then it runs
+// 16-column blocks, and still leaves CUs idle or waits on one long chain).
+// The segment count aims at about two full rounds of transition-pass blocks
+// (512 blocks of 32 of its d_v + d_k columns), with the segment length kept
+// between 64 and 128 chunks: shorter segments pay more per-segment start-up
+// and fold steps, longer ones leave the passes with too few blocks.
+// Measured on MI355X, long context T = 65536, d = 128, one pass vs segments
+// of 16 / 32 / 64 / 128 / 256 chunks: 16 heads 1,123 vs
+// 1,150 / 957 / 886 / 844 / 921 us; 2 heads 863 vs 319 / 221 / 200 / 271 / 459 us.
 static int32_t plan_segment_chunks(const Problem &p) {
   const int64_t units = int64_t(p.n_seqs) * p.H_v;
   const int64_t max_chunks = ceil_div(p.T, p.chunk);  // the longest sequence's chunks, at most
-  if (units == 0 || units * (p.d_v / 16) >= 128 || max_chunks < 16) return 0;
-  const int64_t blocks32 = units * std::max(1, p.d_v / 32);
-  const int64_t segs = std::max<int64_t>(2, ceil_div(256, blocks32));
-  const int64_t seg = std::max<int64_t>(4, ceil_div(max_chunks, segs));
+  if (units == 0 || units * std::max(1, p.d_v / 32) >= 128) return 0;
+  const int64_t blocks1 = units * std::max(1, (p.d_v + p.d_k) / 32);
+  const int64_t segs = ceil_div(512, blocks1);
+  const int64_t seg = std::min<int64_t>(128, std::max<int64_t>(64, ceil_div(max_chunks, segs)));
   return seg >= max_chunks ? 0 : int32_t(seg);
 }
 

@@ -56,40 +56,56 @@ __global__ __launch_bounds__(512) void fold_kernel(FoldArgs a) {
   const int j1 = min(max(a.seg_first[s + 1], j0), j_end);
   // operands of step j: M row 16 w + r0, columns 16 m + 4 g .. + 3 (contraction
   // order: MFMA 4 m + i of a step takes index 16 m + 4 g + i in both
-  // operands), and B at this lane's accumulator elements
-  f32x4_t Mr[8], Bv;
-  auto load_step = [&](int j) {
+  // operands), and B at this lane's accumulator elements.  Three register
+  // sets: the maps of the next two segments are in flight while one step runs
+  // (the step's products are short next to a map's load latency).
+  struct Ops {
+    f32x4_t m[8], b;
+  };
+  auto load_step = [&](int j, Ops &r) {
     const float *base = a.mb + (int64_t(j) * a.H_v + h) * a.d_k * ld;
     const float *mrow = base + int64_t(16 * w + r0) * ld + a.d_v + 4 * g;
 #pragma unroll
     for (int m = 0; m < 8; ++m)
-      if (m < nk4) Mr[m] = *reinterpret_cast<const f32x4_t *>(mrow + 16 * m);
+      if (m < nk4) r.m[m] = *reinterpret_cast<const f32x4_t *>(mrow + 16 * m);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) Bv[i] = base[int64_t(16 * w + 4 * g + i) * ld + col];
+    for (int i = 0; i < 4; ++i) r.b[i] = base[int64_t(16 * w + 4 * g + i) * ld + col];
   };
-  if (j0 < j1) load_step(j0);
   int buf = 0;
-  for (int j = j0; j < j1; ++j) {
-    // the state entering segment j
+  // S <- M_j S + B_j, after writing out the state entering segment j
+  auto step = [&](int j, const Ops &r) {
     float *sin = a.s_in + (int64_t(j) * a.H_v + h) * a.d_k * a.d_v;
 #pragma unroll
     for (int i = 0; i < 4; ++i) sin[int64_t(16 * w + 4 * g + i) * a.d_v + col] = S[i];
     *reinterpret_cast<f32x4_t *>(&st[buf][r0 * kFoldRow + 16 * w + 4 * g]) = S;
     __syncthreads();
-    f32x4_t M_cur[8], acc = Bv;
-#pragma unroll
-    for (int m = 0; m < 8; ++m) M_cur[m] = Mr[m];
-    if (j + 1 < j1) load_step(j + 1);  // in flight during this step's products
+    f32x4_t acc = r.b;
 #pragma unroll
     for (int m = 0; m < 8; ++m) {
       if (m < nk4) {
         const f32x4_t sv = *reinterpret_cast<const f32x4_t *>(&st[buf][r0 * kFoldRow + 16 * m + 4 * g]);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(M_cur[m][i], sv[i], acc, 0, 0, 0);
+        for (int i = 0; i < 4; ++i) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(r.m[m][i], sv[i], acc, 0, 0, 0);
       }
     }
     S = acc;
     buf ^= 1;  // the next step writes the other buffer: no wave still reads it
+  };
+  Ops r0s, r1s, r2s;
+  if (j0 < j1) load_step(j0, r0s);
+  if (j0 + 1 < j1) load_step(j0 + 1, r1s);
+  if (j0 + 2 < j1) load_step(j0 + 2, r2s);
+  for (int j = j0; j < j1; j += 3) {
+    step(j, r0s);
+    if (j + 3 < j1) load_step(j + 3, r0s);
+    if (j + 1 < j1) {
+      step(j + 1, r1s);
+      if (j + 4 < j1) load_step(j + 4, r1s);
+    }
+    if (j + 2 < j1) {
+      step(j + 2, r2s);
+      if (j + 5 < j1) load_step(j + 5, r2s);
+    }
   }
   if (a.hT) {
 #pragma unroll

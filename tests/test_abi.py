@@ -179,10 +179,11 @@ def test_segment_plan_and_workspace(lib):
     bf = gdn.GDN_BF16
     # a full batch runs in one pass; a few long units are cut into segments
     assert gdn.chunk_fwd_plan_segments(4, 4096, 16, 16, 128, 128, bf, 64, 0) == 0
-    assert gdn.chunk_fwd_plan_segments(1, 65536, 16, 16, 128, 128, bf, 64, 0) == 0
+    assert gdn.chunk_fwd_plan_segments(1, 65536, 16, 16, 128, 128, bf, 64, 0) == 128
     seg = gdn.chunk_fwd_plan_segments(1, 65536, 2, 2, 128, 128, bf, 64, 0)
-    assert 4 <= seg < 1024
-    assert gdn.chunk_fwd_plan_segments(1, 256, 1, 1, 128, 128, bf, 64, 0) == 0   # too short to cut
+    assert seg == 64
+    assert gdn.chunk_fwd_plan_segments(1, 4096, 1, 1, 128, 128, bf, 64, 0) == 0   # too short to cut
+    assert gdn.chunk_fwd_plan_segments(1, 8192, 1, 1, 128, 128, bf, 64, 0) == 64
     assert lib.gdn_chunk_fwd_plan_segments(1, 64, 1, 1, 48, 64, bf, 64, 0) == -1
     # gdn_chunk_fwd's query covers the planned form
     one = gdn.chunk_fwd_segmented_workspace_bytes(1, 65536, 2, 2, 128, 128, bf, 64, 0, 0)

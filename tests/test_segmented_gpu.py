@@ -116,20 +116,23 @@ def test_plan_picks_segments_for_few_long_units(gdn):
     """gdn_chunk_fwd segments a few long units by itself and not a full batch."""
     bf = gdn.GDN_BF16
     assert gdn.chunk_fwd_plan_segments(4, 4096, 16, 16, 128, 128, bf, 64, 0) == 0
-    assert gdn.chunk_fwd_plan_segments(1, 65536, 16, 16, 128, 128, bf, 64, 0) == 0
+    assert gdn.chunk_fwd_plan_segments(1, 65536, 16, 16, 128, 128, bf, 64, 0) > 0
     assert gdn.chunk_fwd_plan_segments(1, 65536, 2, 2, 128, 128, bf, 64, 0) > 0
-    w = small("bf16", 1, 4096, 1, 1, 128, 128, 64, seed=61, log_alpha_scale=0.1)
-    plan = gdn.chunk_fwd_plan_segments(1, 4096, 1, 1, 128, 128, bf, 64, 0)
-    log(f"[plan] B=1 T=4096 H=1: {plan} chunks per segment")
+    w = small("bf16", 1, 8192, 1, 1, 128, 128, 64, seed=61, log_alpha_scale=0.1)
+    plan = gdn.chunk_fwd_plan_segments(1, 8192, 1, 1, 128, 128, bf, 64, 0)
+    log(f"[plan] B=1 T=8192 H=1: {plan} chunks per segment")
     assert plan > 0
     check_seg(gdn, w, None)
 
 
-def test_config4_long_context_segmented_full(gdn):
-    """The long-context workload (B=1, H=16, T=65536) through the segmented
-    form with 64-chunk segments."""
+def test_config4_long_context_other_forms_full(gdn):
+    """The long-context workload (B=1, H=16, T=65536), which gdn_chunk_fwd
+    cuts into 128-chunk segments, through the one-pass scan and through
+    64-chunk segments."""
     w = gi.generate(gi.config(4))
-    check_seg(gdn, w, 64)
+    ref = oracle.forward(w.q, w.k, w.v, w.alpha, w.beta)
+    check_seg(gdn, w, 0, ref=ref)
+    check_seg(gdn, w, 64, ref=ref)
 
 
 def test_config4_two_heads_auto(gdn):
