@@ -24,7 +24,8 @@ __all__ = [
     "GDNError", "lib_path", "load", "version", "status_string", "recurrent_fwd",
     "chunk_fwd", "chunk_fwd_workspace_bytes", "chunk_fwd_plan_segments",
     "chunk_fwd_segmented_workspace_bytes", "decode_step", "block_prologue", "block_epilogue",
-    "kda_recurrent_fwd", "kda_decode_step", "GDN_F32", "GDN_BF16",
+    "kda_recurrent_fwd", "kda_chunk_fwd", "kda_chunk_fwd_workspace_bytes", "kda_decode_step",
+    "GDN_F32", "GDN_BF16",
 ]
 
 GDN_SUCCESS = 0
@@ -38,7 +39,8 @@ _lib: Optional[ctypes.CDLL] = None
 EXPORTS = ["gdn_version", "gdn_status_string", "gdn_recurrent_fwd",
            "gdn_chunk_fwd_workspace_bytes", "gdn_chunk_fwd", "gdn_chunk_fwd_plan_segments",
            "gdn_chunk_fwd_segmented_workspace_bytes", "gdn_chunk_fwd_segmented", "gdn_decode_step",
-           "gdn_block_prologue", "gdn_block_epilogue", "gdn_kda_recurrent_fwd", "gdn_kda_decode_step"]
+           "gdn_block_prologue", "gdn_block_epilogue", "gdn_kda_recurrent_fwd",
+           "gdn_kda_chunk_fwd_workspace_bytes", "gdn_kda_chunk_fwd", "gdn_kda_decode_step"]
 
 
 class GDNError(RuntimeError):
@@ -84,6 +86,10 @@ def load() -> ctypes.CDLL:
     lib.gdn_decode_step.argtypes = [i32] * 6 + [vp, vp, vp, fp, fp, fp, vp, vp]
     lib.gdn_kda_recurrent_fwd.argtypes = fwd + [vp]
     lib.gdn_kda_recurrent_fwd.restype = i32
+    lib.gdn_kda_chunk_fwd_workspace_bytes.argtypes = [i32] * 9
+    lib.gdn_kda_chunk_fwd_workspace_bytes.restype = ctypes.c_size_t
+    lib.gdn_kda_chunk_fwd.argtypes = fwd + [i32, vp, ctypes.c_size_t, vp]
+    lib.gdn_kda_chunk_fwd.restype = i32
     lib.gdn_kda_decode_step.argtypes = [i32] * 6 + [vp, vp, vp, fp, fp, fp, vp, vp]
     lib.gdn_kda_decode_step.restype = i32
     lib.gdn_decode_step.restype = i32
@@ -297,6 +303,35 @@ def kda_recurrent_fwd(q, k, v, alpha, beta, *, cu_seqlens=None, h0=None, o=None,
                                       _stream(stream))
     if st != GDN_SUCCESS:
         raise GDNError(st, "gdn_kda_recurrent_fwd")
+    return o, hT
+
+
+def kda_chunk_fwd_workspace_bytes(B, T, H_qk, H_v, d_k, d_v, dtype_code, chunk=64, n_seqs=0) -> int:
+    return int(load().gdn_kda_chunk_fwd_workspace_bytes(B, T, H_qk, H_v, d_k, d_v, dtype_code, chunk,
+                                                        n_seqs))
+
+
+def kda_chunk_fwd(q, k, v, alpha, beta, *, chunk: int = 64, cu_seqlens=None, h0=None, o=None, hT=None,
+                  workspace=None, output_final_state: bool = True, stream=None) -> Tuple:
+    """Chunked delta rule with one decay rate per key channel: alpha is
+    [B, T, H_v, d_k] float32.  Returns (o, hT)."""
+    torch = _torch()
+    dims, n_seqs, o, hT = _fwd_args(q, k, v, alpha, beta, cu_seqlens, h0, o, hT,
+                                    output_final_state, per_channel=True)
+    need = kda_chunk_fwd_workspace_bytes(*dims, chunk, n_seqs)
+    if need == 0:
+        raise GDNError(2, "gdn_kda_chunk_fwd_workspace_bytes")
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    elif workspace.numel() * workspace.element_size() < need:
+        raise ValueError(f"workspace holds {workspace.numel() * workspace.element_size()} "
+                         f"bytes, {need} needed")
+    st = load().gdn_kda_chunk_fwd(*dims, _ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(beta),
+                                  _ptr(cu_seqlens), n_seqs, _ptr(h0), _ptr(o), _ptr(hT), chunk,
+                                  _ptr(workspace), workspace.numel() * workspace.element_size(),
+                                  _stream(stream))
+    if st != GDN_SUCCESS:
+        raise GDNError(st, "gdn_kda_chunk_fwd")
     return o, hT
 
 

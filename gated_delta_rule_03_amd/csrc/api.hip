@@ -365,6 +365,37 @@ int32_t gdn_kda_recurrent_fwd(int32_t B, int32_t T, int32_t H_qk, int32_t H_v, i
   return status_of(launch_recurrent(p, static_cast<hipStream_t>(stream)));
 }
 
+size_t gdn_kda_chunk_fwd_workspace_bytes(int32_t B, int32_t T, int32_t H_qk, int32_t H_v, int32_t d_k,
+                                         int32_t d_v, int32_t dtype, int32_t chunk, int32_t n_seqs) {
+  if (!query_ok(B, T, H_qk, H_v, d_k, d_v, dtype, chunk, n_seqs)) return 0;
+  Problem p = query_problem(B, T, H_qk, H_v, d_k, d_v, dtype, chunk, n_seqs);
+  p.per_channel = 1;
+  return workspace_layout(p, nullptr, nullptr);
+}
+
+int32_t gdn_kda_chunk_fwd(int32_t B, int32_t T, int32_t H_qk, int32_t H_v, int32_t d_k, int32_t d_v,
+                          int32_t dtype, const void *q, const void *k, const void *v, const float *alpha,
+                          const float *beta, const int32_t *cu_seqlens, int32_t n_seqs, const float *h0,
+                          void *o, float *hT, int32_t chunk, void *workspace, size_t workspace_bytes,
+                          void *stream) {
+  Problem p;
+  int32_t st = make_problem(B, T, H_qk, H_v, d_k, d_v, dtype, q, k, v, alpha, beta, cu_seqlens,
+                            n_seqs, h0, o, hT, &p);
+  if (st != GDN_SUCCESS) return st;
+  if (chunk != 16 && chunk != 32 && chunk != 64) return GDN_ERROR_NOT_SUPPORTED;
+  p.chunk = chunk;
+  p.per_channel = 1;
+  const size_t need = workspace_layout(p, nullptr, nullptr);
+  if (!workspace || workspace_bytes < need) return GDN_ERROR_WORKSPACE;
+  if (reinterpret_cast<uintptr_t>(workspace) & 255) return GDN_ERROR_WORKSPACE;
+  Workspace ws;
+  workspace_layout(p, workspace, &ws);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e = launch_chunk_offsets(p, ws, s);
+  if (e == hipSuccess) e = launch_kda_chunk(p, ws, s);
+  return status_of(e);
+}
+
 int32_t gdn_kda_decode_step(int32_t B, int32_t H_qk, int32_t H_v, int32_t d_k, int32_t d_v,
                             int32_t dtype, const void *q, const void *k, const void *v,
                             const float *alpha, const float *beta, float *state, void *o,

@@ -1,0 +1,359 @@
+// Chunked form of the delta rule with one decay rate per key channel.
+//
+// "Attention as Matrix Algebra: From Softmax to the Delta Rule", section 10,
+// names Kimi Delta Attention: the gated delta rule with its own forget rate
+// for each feature channel.  The channels are the key features (the rows of
+// the keys x values state), so step t decays the state by diag(alpha_t).  The
+// chunk algebra of section 8 of the same page ("Training the delta rule in
+// chunks") carries over with the scalar cumulative gate replaced by a vector
+// one.  Inside a chunk that starts from state S, with G_t = sum_{i<=t}
+// log2 alpha_i (chunk-local, per channel) and Gamma_t = 2^G_t:
+//
+//   A_ti = beta_t sum_c k_tc k_ic 2^(G_tc - G_ic)   (i < t),  T = (I + A)^-1 diag(beta)
+//   P_ti = sum_c q_tc k_ic 2^(G_tc - G_ic)          (i <= t)
+//   Khat_t = Gamma_t . k_t,  Qhat_t = Gamma_t . q_t,  Ktil_i = 2^(G_C - G_i) . k_i
+//   U  = T (V - Khat S)          pseudo-values
+//   O  = Qhat S + P U            the chunk's outputs
+//   S <- diag(Gamma_C) S + Ktil^T U
+//
+// (unrolling u_t = beta_t (v_t - (diag(alpha_t) S_{t-1})^T k_t) through the
+// chunk exactly as for the scalar gate, with every scalar decay product
+// replaced by its diagonal matrix).  Every exponent is a difference G_t - G_i
+// <= 0 for i <= t, or G_t <= 0, so no factor exceeds one.  The exponent of
+// A and P differs per channel, so it cannot be pulled out of the channel sum
+// as the scalar gate's can; the prep kernel evaluates those sums with the
+// exact per-channel factors in fp32.
+//
+// The prep kernel writes, per (chunk slot, value head), T and P and the
+// pre-scaled operands Khat, Qhat (A-operand fragments, rows = tokens) and
+// Ktil^T (A-operand fragments, rows = key channels) in MFMA fragment order,
+// then Gamma_C; the scan walks each unit's chunks in order with the state in
+// accumulator registers, one wave per 16 state columns.
+#include "launch.hpp"
+#include "stage.hpp"
+
+namespace gdn {
+
+// Entry of one (chunk slot, value head), kda_entry_bytes (launch.hpp):
+// fragments of 64 lanes x 8 elements of the operand type -- T (8), P (8),
+// Khat (16: 4 token tiles x 4 contraction blocks of d_k), Qhat (16), Ktil^T
+// (16: 8 channel tiles x 2 token blocks) -- then Gamma_C (128 fp32).
+constexpr int kKdaFragT = 0, kKdaFragP = 8, kKdaFragKh = 16, kKdaFragQh = 32, kKdaFragKt = 48;
+
+template <typename T>
+struct KdaArgs {
+  const T *q, *k, *v;
+  const float *alpha, *beta;  // alpha [tokens, H_v, d_k], beta [tokens, H_v]
+  char *entries;
+  const float *h0;
+  T *o;
+  float *hT;
+  int H_qk, H_v, d_k, d_v, group, n_units, n_colblk;
+  SeqGeom geo;
+};
+
+constexpr int kKRow = 129;  // fp32 row stride of the LDS token x channel tiles (odd: column walks hit every bank)
+
+// ---------------------------------------------------------------------------
+// Prep: one block of 512 threads per (chunk slot, value head).
+// ---------------------------------------------------------------------------
+template <typename T>
+__global__ __launch_bounds__(512) void kda_prep_kernel(KdaArgs<T> a) {
+  const int c = blockIdx.x, h = blockIdx.y;
+  int s, tok0, len;
+  if (!a.geo.locate(c, s, tok0, len)) return;
+  const int hq = h / a.group;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int dk = a.d_k;
+
+  __shared__ float sG[64 * kKRow];   // G_t per channel (log2), padded slots repeat the last token's
+  __shared__ float sK[64 * kKRow];   // k rows, zero past the chunk's end
+  __shared__ float sQ[64 * kKRow];   // q rows
+  __shared__ float sA[64][65];       // A (strictly lower), then the inverse's blocks alias sK / sQ
+  __shared__ float sb[64];
+  float(*sM)[65] = reinterpret_cast<float(*)[65]>(sK);           // M = (I + A)^-1 (after the tiles)
+  float(*sY)[16][17] = reinterpret_cast<float(*)[16][17]>(sQ);  // block products
+
+  const int64_t qk_stride = int64_t(a.H_qk) * dk;
+  const T *kb = a.k + int64_t(tok0) * qk_stride + int64_t(hq) * dk;
+  const T *qb = a.q + int64_t(tok0) * qk_stride + int64_t(hq) * dk;
+  const float *ab = a.alpha + (int64_t(tok0) * a.H_v + h) * dk;
+  const int64_t a_stride = int64_t(a.H_v) * dk;
+
+  // ---- rows of k, q and the clamped log2 rates (zero past the chunk's end) ----
+  for (int idx = tid; idx < 64 * dk; idx += 512) {
+    const int t = idx / dk, ch = idx - t * dk;
+    const bool in = t < len;
+    sK[t * kKRow + ch] = in ? to_f32(kb[int64_t(t) * qk_stride + ch]) : 0.0f;
+    sQ[t * kKRow + ch] = in ? to_f32(qb[int64_t(t) * qk_stride + ch]) : 0.0f;
+    sG[t * kKRow + ch] = in ? clamped_log2(ab[int64_t(t) * a_stride + ch]) : 0.0f;
+  }
+  if (tid < 64) sb[tid] = tid < len ? a.beta[int64_t(tok0 + tid) * a.H_v + h] : 0.0f;
+  lds_barrier();
+  // ---- chunk-local cumulative log gate, one thread per channel ----
+  if (tid < dk) {
+    float g = 0.0f;
+    for (int t = 0; t < 64; ++t) {
+      g += sG[t * kKRow + tid];
+      sG[t * kKRow + tid] = g;
+    }
+  }
+  lds_barrier();
+
+  char *entry = a.entries + (int64_t(c) * a.H_v + h) * kda_entry_bytes<T>();
+  T *frag = reinterpret_cast<T *>(entry);
+  float *gamma_C = reinterpret_cast<float *>(frag + kKdaFrags * kFragElems);
+
+  // ---- pre-scaled operands, A-operand fragments in the kappa convention ----
+  // Khat, Qhat: fragment (rt, kk) holds rows 16 rt + lane mod 16, channels 32 kk + kappa.
+  for (int f = wave; f < 32; f += 8) {
+    const bool isq = f >= 16;
+    const int ff = f & 15, rt = ff >> 2, kk = ff & 3;
+    const int t = 16 * rt + (lane & 15);
+    Frag<T> fr;
+    for (int j = 0; j < 8; ++j) {
+      const int ch = 32 * kk + kappa(lane, j);
+      float x = 0.0f;
+      if (ch < dk) x = fast_exp2(sG[t * kKRow + ch]) * (isq ? sQ : sK)[t * kKRow + ch];
+      fr.set(j, x);
+    }
+    store_frag(frag + ((isq ? kKdaFragQh : kKdaFragKh) + ff) * kFragElems, lane, fr);
+  }
+  // Ktil^T: fragment (rm, kk) holds channel 16 rm + lane mod 16, tokens 32 kk + kappa.
+  for (int f = wave; f < 16; f += 8) {
+    const int rm = f >> 1, kk = f & 1;
+    const int ch = 16 * rm + (lane & 15);
+    Frag<T> fr;
+    for (int j = 0; j < 8; ++j) {
+      const int i = 32 * kk + kappa(lane, j);
+      float x = 0.0f;
+      if (ch < dk) x = fast_exp2(sG[63 * kKRow + ch] - sG[i * kKRow + ch]) * sK[i * kKRow + ch];
+      fr.set(j, x);
+    }
+    store_frag(frag + (kKdaFragKt + f) * kFragElems, lane, fr);
+  }
+  if (tid < 128) gamma_C[tid] = tid < dk ? fast_exp2(sG[63 * kKRow + tid]) : 0.0f;
+
+  // ---- A and P: for every pair i <= t, one exponent per channel serves both
+  // sums.  Thread pairs: 2080 lower-triangle entries (i <= t) over 512 threads.
+  // A is kept in LDS for the inverse; P leaves as A-operand fragments (row t,
+  // contraction i), element (t, i) at fragment (t / 16) * 2 + i / 32, lane
+  // 16 * ((i mod 32 mod 16) / 4) + t mod 16, element 4 * ((i mod 32) / 16) + i mod 4.
+  T *fragP = frag + kKdaFragP * kFragElems;
+  for (int p = tid; p < 64 * 64; p += 512) {
+    const int t = p >> 6, i = p & 63;
+    float acc_a = 0.0f, acc_p = 0.0f;
+    if (i <= t) {
+      const float *gt = sG + t * kKRow, *gi = sG + i * kKRow;
+      const float *kt = sK + t * kKRow, *ki = sK + i * kKRow, *qt = sQ + t * kKRow;
+      for (int ch = 0; ch < dk; ++ch) {
+        const float e = fast_exp2(gt[ch] - gi[ch]) * ki[ch];
+        acc_a += kt[ch] * e;
+        acc_p += qt[ch] * e;
+      }
+    }
+    sA[t][i] = i < t ? sb[t] * acc_a : 0.0f;
+    const int ii = i & 31, kk = i >> 5;
+    const int ln = 16 * ((ii & 15) >> 2) + (t & 15), el = 4 * (ii >> 4) + (ii & 3);
+    fragP[((t >> 4) * 2 + kk) * kFragElems + 8 * ln + el] = from_f32<T>(acc_p);
+  }
+  lds_barrier();  // sK and sQ are dead: the inverse's blocks reuse them
+
+  // ---- M = (I + A)^-1: diagonal 16 x 16 blocks by forward substitution ----
+  if (wave == 0) {
+    const int b = lane >> 4, col = lane & 15;
+    float x[16];
+#pragma unroll
+    for (int t = 0; t < 16; ++t) {
+      float v = (t == col) ? 1.0f : 0.0f;
+#pragma unroll
+      for (int i = 0; i < t; ++i) v -= sA[16 * b + t][16 * b + i] * x[i];
+      x[t] = v;
+    }
+#pragma unroll
+    for (int t = 0; t < 16; ++t) sM[16 * b + t][16 * b + col] = x[t];
+  }
+  lds_barrier();
+  // ---- off-diagonal blocks: M_bc = -M_bb sum_{j=c}^{b-1} A_bj M_jc ----
+  {
+    const int t = (tid >> 4) & 15, col = tid & 15;
+    const bool active = tid < 256;
+    for (int br = 1; br < 4; ++br) {
+      if (active)
+        for (int cb = 0; cb < br; ++cb) {
+          float y = 0.0f;
+          for (int j = cb; j < br; ++j)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) y += sA[16 * br + t][16 * j + i] * sM[16 * j + i][16 * cb + col];
+          sY[cb][t][col] = y;
+        }
+      lds_barrier();
+      if (active)
+        for (int cb = 0; cb < br; ++cb) {
+          float m = 0.0f;
+#pragma unroll
+          for (int i = 0; i < 16; ++i) m -= sM[16 * br + t][16 * br + i] * sY[cb][i][col];
+          sM[16 * br + t][16 * cb + col] = m;
+        }
+      lds_barrier();
+    }
+  }
+  // ---- T = M diag(beta) as A fragments (row t, contraction i) ----
+  for (int f = wave; f < 8; f += 8) {
+    const int rt = f >> 1, kk = f & 1;
+    const int t = 16 * rt + (lane & 15);
+    Frag<T> fr;
+    for (int j = 0; j < 8; ++j) {
+      const int i = 32 * kk + kappa(lane, j);
+      fr.set(j, (i >> 4) <= (t >> 4) ? sM[t][i] * sb[i] : 0.0f);
+    }
+    store_frag(frag + (kKdaFragT + f) * kFragElems, lane, fr);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Scan: one wave per (unit, 16 state columns), chunks in order.
+// ---------------------------------------------------------------------------
+template <typename T>
+__global__ __launch_bounds__(64) void kda_scan_kernel(KdaArgs<T> a) {
+  const int lane = threadIdx.x;
+  int u, cb;
+  decode_block(blockIdx.x, a.n_colblk, u, cb);
+  if (u >= a.n_units) return;
+  const int s = a.geo.ordered(u / a.H_v), h = u % a.H_v;
+  const int g = lane >> 4;
+  const int col = 16 * cb + (lane & 15);
+  const int nkt = a.d_k >> 4;        // 16-row tiles of the state
+  const int nkb = (a.d_k + 31) >> 5; // 32-deep contraction blocks over d_k
+
+  f32x4_t S[8];
+  const int64_t st_base = (int64_t(s) * a.H_v + h) * a.d_k * a.d_v;
+#pragma unroll
+  for (int rt = 0; rt < 8; ++rt) {
+    S[rt] = zero4();
+    if (rt < nkt && a.h0)
+      for (int e = 0; e < 4; ++e) S[rt][e] = a.h0[st_base + int64_t(16 * rt + 4 * g + e) * a.d_v + col];
+  }
+  int start, end;
+  a.geo.seq_bounds(s, start, end);
+  const int n_chunks = (end - start + a.geo.chunk - 1) / a.geo.chunk;
+  const int c_first = a.geo.first_chunk(s);
+  const int64_t v_stride = int64_t(a.H_v) * a.d_v;
+
+  for (int cc = 0; cc < n_chunks; ++cc) {
+    const int c = c_first + cc;
+    if (c >= a.geo.n_slots) break;
+    const int tok0 = start + cc * a.geo.chunk;
+    const int len = min(a.geo.chunk, end - tok0);
+    const T *frag = reinterpret_cast<const T *>(a.entries + (int64_t(c) * a.H_v + h) * kda_entry_bytes<T>());
+    const float *gamma_C = reinterpret_cast<const float *>(frag + kKdaFrags * kFragElems);
+    const T *vb = a.v + int64_t(tok0) * v_stride + int64_t(h) * a.d_v + col;
+
+    Frag<T> Sf[4];
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) Sf[kk] = frag_from_acc<T>(S[2 * kk], S[2 * kk + 1]);
+    // Y = Khat S, OQ = Qhat S
+    f32x4_t Y[4], OQ[4];
+#pragma unroll
+    for (int rt = 0; rt < 4; ++rt) {
+      Y[rt] = zero4();
+      OQ[rt] = zero4();
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk)
+        if (kk < nkb) {
+          Y[rt] = mfma(load_frag(frag + (kKdaFragKh + 4 * rt + kk) * kFragElems, lane), Sf[kk], Y[rt]);
+          OQ[rt] = mfma(load_frag(frag + (kKdaFragQh + 4 * rt + kk) * kFragElems, lane), Sf[kk], OQ[rt]);
+        }
+    }
+    // X = V - Y, U = T X
+    f32x4_t X[4];
+#pragma unroll
+    for (int rt = 0; rt < 4; ++rt)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int t = 16 * rt + 4 * g + e;
+        X[rt][e] = (t < len ? to_f32(vb[int64_t(t) * v_stride]) : 0.0f) - Y[rt][e];
+      }
+    Frag<T> Xf[2] = {frag_from_acc<T>(X[0], X[1]), frag_from_acc<T>(X[2], X[3])};
+    f32x4_t Ua[4];
+#pragma unroll
+    for (int rt = 0; rt < 4; ++rt) {
+      Ua[rt] = zero4();
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk)
+        Ua[rt] = mfma(load_frag(frag + (kKdaFragT + rt * 2 + kk) * kFragElems, lane), Xf[kk], Ua[rt]);
+    }
+    Frag<T> Uf[2] = {frag_from_acc<T>(Ua[0], Ua[1]), frag_from_acc<T>(Ua[2], Ua[3])};
+    // O = Qhat S + P U
+#pragma unroll
+    for (int rt = 0; rt < 4; ++rt) {
+      f32x4_t acc = OQ[rt];
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk)
+        acc = mfma(load_frag(frag + (kKdaFragP + rt * 2 + kk) * kFragElems, lane), Uf[kk], acc);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int t = 16 * rt + 4 * g + e;
+        if (t < len) a.o[int64_t(tok0 + t) * v_stride + int64_t(h) * a.d_v + col] = from_f32<T>(acc[e]);
+      }
+    }
+    // S <- diag(Gamma_C) S + Ktil^T U
+#pragma unroll
+    for (int rm = 0; rm < 8; ++rm) {
+      if (rm < nkt) {
+        const f32x4_t gc = *reinterpret_cast<const f32x4_t *>(gamma_C + 16 * rm + 4 * g);
+        f32x4_t acc = gc * S[rm];
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk)
+          acc = mfma(load_frag(frag + (kKdaFragKt + rm * 2 + kk) * kFragElems, lane), Uf[kk], acc);
+        S[rm] = acc;
+      }
+    }
+  }
+  if (a.hT) {
+#pragma unroll
+    for (int rt = 0; rt < 8; ++rt)
+      if (rt < nkt)
+        for (int e = 0; e < 4; ++e) a.hT[st_base + int64_t(16 * rt + 4 * g + e) * a.d_v + col] = S[rt][e];
+  }
+}
+
+template <typename T>
+static hipError_t launch_kda_chunk_t(const Problem &p, const Workspace &ws, hipStream_t st) {
+  KdaArgs<T> a;
+  a.q = static_cast<const T *>(p.q);
+  a.k = static_cast<const T *>(p.k);
+  a.v = static_cast<const T *>(p.v);
+  a.alpha = p.alpha;
+  a.beta = p.beta;
+  a.entries = static_cast<char *>(ws.entries);
+  a.h0 = p.h0;
+  a.o = static_cast<T *>(p.o);
+  a.hT = p.hT;
+  a.H_qk = p.H_qk;
+  a.H_v = p.H_v;
+  a.d_k = p.d_k;
+  a.d_v = p.d_v;
+  a.group = p.H_v / p.H_qk;
+  a.n_units = p.n_seqs * p.H_v;
+  a.n_colblk = p.d_v / 16;
+  a.geo = make_geom(p, &ws);
+  const int64_t slots = chunk_slots(p);
+  if (slots > 0) {
+    hipLaunchKernelGGL(kda_prep_kernel<T>, dim3(unsigned(slots), unsigned(p.H_v)), dim3(512), 0, st, a);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  const int64_t blocks = (int64_t(p.n_seqs) * p.H_v + 7) / 8 * 8 * (p.d_v / 16);
+  if (blocks == 0) return hipSuccess;
+  hipLaunchKernelGGL(kda_scan_kernel<T>, dim3(unsigned(blocks)), dim3(64), 0, st, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_kda_chunk(const Problem &p, const Workspace &ws, hipStream_t st) {
+  if (p.dtype == 1) return launch_kda_chunk_t<bf16_t>(p, ws, st);
+  return launch_kda_chunk_t<float>(p, ws, st);
+}
+
+}  // namespace gdn

@@ -48,7 +48,14 @@ inline bool staged_path(const Problem &p) { return p.dtype == 1 && p.d_k == 128 
 constexpr int kStagedGateOffset = 5 * 1024;
 constexpr int kStagedGateBytes = 3 * 64 * 4;
 constexpr int64_t kStagedEntryBytes = kStagedGateOffset + kStagedGateBytes;
+// Per-channel gate (kda_chunk.hip): 64 fragments (T, P, Khat, Qhat, Ktil^T)
+// then Gamma_C, 128 fp32.
+constexpr int kKdaFrags = 64;
+template <typename T> constexpr int64_t kda_entry_bytes() {
+  return int64_t(kKdaFrags) * kFragElems * sizeof(T) + 128 * 4;
+}
 inline int64_t entry_stride(const Problem &p) {
+  if (p.per_channel) return p.dtype == 1 ? kda_entry_bytes<uint16_t>() : kda_entry_bytes<float>();
   if (staged_path(p)) return kStagedEntryBytes;
   return p.dtype == 1 ? entry_bytes<uint16_t>() : entry_bytes<float>();
 }
@@ -64,6 +71,7 @@ hipError_t launch_chunk_offsets(const Problem &p, const Workspace &ws, hipStream
 hipError_t launch_prep(const Problem &p, const Workspace &ws, hipStream_t st);
 hipError_t launch_scan(const Problem &p, const Workspace &ws, hipStream_t st, float *mb = nullptr);
 hipError_t launch_recurrent(const Problem &p, hipStream_t st);
+hipError_t launch_kda_chunk(const Problem &p, const Workspace &ws, hipStream_t st);
 // Segment-parallel path (seqmap.hip, fold.hip).
 hipError_t launch_segment_map(const Problem &p, int seg_tokens, int n_seg_bound, int32_t *seg_cu,
                               int32_t *seg_first, hipStream_t st);

@@ -210,6 +210,33 @@ int32_t gdn_kda_recurrent_fwd(int32_t B, int32_t T, int32_t H_qk, int32_t H_v, i
                               int32_t d_v, int32_t dtype, const void *q, const void *k, const void *v,
                               const float *alpha, const float *beta, const int32_t *cu_seqlens,
                               int32_t n_seqs, const float *h0, void *o, float *hT, void *stream);
+
+/*
+ * gdn_kda_chunk_fwd -- the per-channel-gate forward computed chunk by chunk
+ * (the same result as gdn_kda_recurrent_fwd, up to rounding).
+ *
+ * The chunk algebra of "Attention as Matrix Algebra" section 8 with the
+ * scalar cumulative gate replaced by one per key channel: with
+ * G_t = sum_{i<=t} log alpha_i inside the chunk (a vector over channels),
+ *   A_ti = beta_t sum_c k_tc k_ic e^(G_tc - G_ic) (i < t),  T = (I + A)^-1 diag(beta),
+ *   U = T (V - (e^G . K) S),  O = (e^G . Q) S + P U,  P_ti = sum_c q_tc k_ic e^(G_tc - G_ic) (i <= t),
+ *   S <- diag(e^(G_C)) S + (e^(G_C - G) . K)^T U.
+ * Every factor is e to a non-positive power; the channel sums of A and P
+ * take their per-channel factors exactly in fp32.
+ *
+ * Arguments as gdn_kda_recurrent_fwd (alpha [B, T, H_v, d_k] float32,
+ * 16-byte aligned), plus chunk (16, 32 or 64) and a caller-provided
+ * workspace of at least gdn_kda_chunk_fwd_workspace_bytes(...) bytes,
+ * 256-byte aligned (contents on entry do not matter, undefined on return;
+ * concurrent calls need separate workspaces).  Errors as gdn_chunk_fwd.
+ */
+size_t gdn_kda_chunk_fwd_workspace_bytes(int32_t B, int32_t T, int32_t H_qk, int32_t H_v, int32_t d_k,
+                                         int32_t d_v, int32_t dtype, int32_t chunk, int32_t n_seqs);
+int32_t gdn_kda_chunk_fwd(int32_t B, int32_t T, int32_t H_qk, int32_t H_v, int32_t d_k, int32_t d_v,
+                          int32_t dtype, const void *q, const void *k, const void *v, const float *alpha,
+                          const float *beta, const int32_t *cu_seqlens, int32_t n_seqs, const float *h0,
+                          void *o, float *hT, int32_t chunk, void *workspace, size_t workspace_bytes,
+                          void *stream);
 int32_t gdn_kda_decode_step(int32_t B, int32_t H_qk, int32_t H_v, int32_t d_k, int32_t d_v,
                             int32_t dtype, const void *q, const void *k, const void *v,
                             const float *alpha, const float *beta, float *state, void *o,

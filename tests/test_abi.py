@@ -67,7 +67,8 @@ def fwd(lib, fn, B=1, T=8, H_qk=1, H_v=1, d_k=64, d_v=64, dtype=0, ptrs=True, cu
 
 @pytest.mark.parametrize("fn,extra", [("gdn_recurrent_fwd", (None,)),
                                       ("gdn_kda_recurrent_fwd", (None,)),
-                                      ("gdn_chunk_fwd", (64, None, 0, None))])
+                                      ("gdn_chunk_fwd", (64, None, 0, None)),
+                                      ("gdn_kda_chunk_fwd", (64, None, 0, None))])
 def test_argument_errors_are_reported_before_launch(lib, fn, extra):
     # every case below fails validation, so no kernel is launched
     assert fwd(lib, fn, d_k=48, extra=extra) == 2
@@ -170,6 +171,7 @@ def test_host_path_reaches_launch_without_gpu(lib):
     assert lib.gdn_chunk_fwd_segmented(*base, 64, 1, ws, 1 << 30, None) == 4
     assert lib.gdn_decode_step(2, 1, 1, 64, 64, 1, p, p, p, p, p, p, p, None) == 4
     assert lib.gdn_kda_recurrent_fwd(*base, None) == 4
+    assert lib.gdn_kda_chunk_fwd(*base, 64, ws, 1 << 30, None) == 4
     assert lib.gdn_kda_decode_step(2, 1, 1, 64, 64, 1, p, p, p, p, p, p, p, None) == 4
     assert prologue(lib) == 4
     assert lib.gdn_block_epilogue(1, 8, 1, 64, 0, p, p, None, 1e-6, p, None) == 4
@@ -213,3 +215,20 @@ def test_segmented_argument_errors(lib):
     bad[2] = 3
     bad[3] = 4
     assert lib.gdn_chunk_fwd_segmented(*bad, 64, 2, p, 1 << 30, None) == 2      # H_v not a multiple of H_qk
+
+
+def test_kda_chunk_workspace(lib):
+    bf = gdn.GDN_BF16
+    # one entry per (chunk slot, value head): 64 fragments of 512 operand-type
+    # elements (T, P, Khat, Qhat, Ktil^T) + 128 fp32 decay factors
+    entry = 64 * 512 * 2 + 512
+    w = gdn.kda_chunk_fwd_workspace_bytes(4, 4096, 16, 16, 128, 128, bf, 64, 0)
+    assert 4 * 64 * 16 * entry <= w < 4 * 64 * 16 * entry + 4096
+    f32 = gdn.kda_chunk_fwd_workspace_bytes(1, 100, 1, 2, 32, 32, gdn.GDN_F32, 32, 0)
+    assert f32 >= 4 * 2 * (64 * 512 * 4 + 512)
+    assert gdn.kda_chunk_fwd_workspace_bytes(1, 64, 1, 1, 48, 64, bf, 64, 0) == 0
+    p = ctypes.c_void_p(0x1000)
+    args = [1, 8, 1, 1, 64, 64, 0, p, p, p, p, p, None, 0, None, p, None]
+    assert lib.gdn_kda_chunk_fwd(*args, 48, p, 1 << 30, None) == 2
+    assert lib.gdn_kda_chunk_fwd(*args, 64, None, 1 << 30, None) == 3
+    assert lib.gdn_kda_chunk_fwd(*args, 64, p, 64, None) == 3

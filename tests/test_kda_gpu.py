@@ -103,3 +103,81 @@ def test_kda_decode(gdn, dtype, B, H_qk, H_v, d):
     es = rel_err(host_f64(st), rs)
     log(f"    max rel err o={eo:.3e} state={es:.3e}")
     assert eo <= TOL[dtype] and es <= TOL["f32"]
+
+
+# ---------------------------------------------------------------------------
+# The chunked form (gdn_kda_chunk_fwd)
+# ---------------------------------------------------------------------------
+
+CHUNK_CASES = [
+    # dtype, B, T, H_qk, H_v, d_k, d_v, chunk, lengths
+    ("f32", 2, 150, 1, 2, 16, 16, 16, None),
+    ("f32", 1, 200, 2, 2, 64, 32, 32, None),
+    ("f32", 2, 130, 1, 1, 128, 64, 64, None),
+    ("f32", 1, 0, 2, 4, 64, 128, 64, (17, 0, 1, 130, 64)),
+    ("bf16", 2, 300, 2, 4, 128, 128, 64, None),
+    ("bf16", 1, 0, 1, 4, 64, 32, 64, (40, 3, 0, 77, 200)),
+    ("bf16", 1, 190, 2, 2, 128, 64, 32, None),
+]
+
+
+def kda_unit_errors(o, hT, ro, rh, slices):
+    eo = max([rel_err(o[b, s:e].transpose(1, 0, 2), ro[b, s:e].transpose(1, 0, 2))
+              for b, s, e in slices if e > s] or [0.0])
+    return eo, rel_err(hT, rh)
+
+
+@pytest.mark.parametrize("case", CHUNK_CASES, ids=[f"{c[0]}-B{c[1]}T{c[2]}H{c[3]}_{c[4]}d{c[5]}_{c[6]}C{c[7]}"
+                                                   + ("-packed" if c[8] else "") for c in CHUNK_CASES])
+def test_kda_chunk(gdn, case):
+    import torch
+    dtype, B, T, H_qk, H_v, d_k, d_v, chunk, lengths = case
+    seed = 500 + CHUNK_CASES.index(case)
+    w = gi.generate(gi.Spec("kda-chunk", B=B, T=T, H_qk=H_qk, H_v=H_v, d_k=d_k, d_v=d_v, dtype=dtype,
+                            chunk=chunk, lengths=lengths, seed=seed))
+    B, T = w.q.shape[0], w.q.shape[1]
+    a = gi.channel_rates(B, T, H_v, d_k, seed + 50)
+    cu = w.cu_seqlens
+    N = B if cu is None else len(cu) - 1
+    slices = w.seq_slices()
+    args = [dev_tensor(x) for x in (w.q, w.k, w.v)] + [dev_tensor(a), dev_tensor(w.beta)]
+    cu_t = None if cu is None else dev_tensor(cu)
+    for h0 in (None, gi.random_state((N, H_v, d_k, d_v), seed=seed + 60, scale=0.3)):
+        log(f"[kda chunk] {case} h0={h0 is not None}")
+        o, hT = gdn.kda_chunk_fwd(*args, chunk=chunk, cu_seqlens=cu_t, h0=None if h0 is None else dev_tensor(h0))
+        torch.cuda.synchronize()
+        ro, rh = kda.forward(w.q, w.k, w.v, a, w.beta, cu_seqlens=cu, h0=h0)
+        eo, eh = kda_unit_errors(host_f64(o), host_f64(hT), ro, rh, slices)
+        log(f"    max rel err o={eo:.3e} hT={eh:.3e}")
+        assert np.all(np.isfinite(host_f64(o))) and eo <= TOL[dtype] and eh <= TOL[dtype]
+
+
+def test_kda_chunk_equal_rates_match_scalar_chunk(gdn):
+    """Every channel at one rate: the per-channel chunked form gives the
+    scalar-gate chunked forward's results (to rounding)."""
+    import torch
+    w = gi.generate(gi.Spec("kda-eq-chunk", B=2, T=300, H_qk=2, H_v=2, d_k=64, d_v=64, dtype="f32", chunk=64,
+                            gates="tiny", seed=520))
+    a = np.repeat(w.alpha[..., None], 64, axis=-1).astype(np.float32)
+    args = [dev_tensor(x) for x in (w.q, w.k, w.v)]
+    o1, h1 = gdn.kda_chunk_fwd(*args, dev_tensor(a), dev_tensor(w.beta))
+    o2, h2 = gdn.chunk_fwd(*args, dev_tensor(w.alpha), dev_tensor(w.beta))
+    torch.cuda.synchronize()
+    e = max(rel_err(host_f64(o1), host_f64(o2)), rel_err(host_f64(h1), host_f64(h2)))
+    log(f"[kda chunk equal rates] max rel diff vs scalar chunked forward {e:.3e}")
+    assert e <= 1e-5
+
+
+def test_kda_chunk_prefill_shape(gdn):
+    """The prefill shape (B=4, T=4096, H=16, d=128, bf16, chunk 64) with one
+    rate per key channel, every unit checked against the float64 oracle."""
+    import torch
+    w = gi.generate(gi.config(2, name="kda-prefill"))
+    a = gi.channel_rates(4, 4096, 16, 128, 540)
+    log("[kda chunk] prefill shape B=4 T=4096 H=16 d=128 bf16")
+    o, hT = gdn.kda_chunk_fwd(*[dev_tensor(x) for x in (w.q, w.k, w.v)], dev_tensor(a), dev_tensor(w.beta))
+    torch.cuda.synchronize()
+    ro, rh = kda.forward(w.q, w.k, w.v, a, w.beta)
+    eo, eh = kda_unit_errors(host_f64(o), host_f64(hT), ro, rh, w.seq_slices())
+    log(f"    max rel err o={eo:.3e} hT={eh:.3e}")
+    assert eo <= TOL["bf16"] and eh <= TOL["bf16"]
