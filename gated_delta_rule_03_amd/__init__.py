@@ -23,7 +23,7 @@ from typing import Optional, Tuple
 __all__ = [
     "GDNError", "lib_path", "load", "version", "status_string", "recurrent_fwd",
     "chunk_fwd", "chunk_fwd_workspace_bytes", "chunk_fwd_plan_segments",
-    "chunk_fwd_segmented_workspace_bytes", "decode_step", "block_prologue", "block_epilogue",
+    "chunk_fwd_segmented_workspace_bytes", "chunk_fwd_noalloc", "decode_step", "block_prologue", "block_epilogue",
     "kda_recurrent_fwd", "kda_chunk_fwd", "kda_chunk_fwd_workspace_bytes", "kda_decode_step",
     "GDN_F32", "GDN_BF16",
 ]
@@ -38,7 +38,8 @@ _lib: Optional[ctypes.CDLL] = None
 
 EXPORTS = ["gdn_version", "gdn_status_string", "gdn_recurrent_fwd",
            "gdn_chunk_fwd_workspace_bytes", "gdn_chunk_fwd", "gdn_chunk_fwd_plan_segments",
-           "gdn_chunk_fwd_segmented_workspace_bytes", "gdn_chunk_fwd_segmented", "gdn_decode_step",
+           "gdn_chunk_fwd_segmented_workspace_bytes", "gdn_chunk_fwd_segmented", "gdn_chunk_fwd_noalloc",
+           "gdn_decode_step",
            "gdn_block_prologue", "gdn_block_epilogue", "gdn_kda_recurrent_fwd",
            "gdn_kda_chunk_fwd_workspace_bytes", "gdn_kda_chunk_fwd", "gdn_kda_decode_step"]
 
@@ -83,6 +84,8 @@ def load() -> ctypes.CDLL:
     lib.gdn_chunk_fwd_segmented_workspace_bytes.restype = ctypes.c_size_t
     lib.gdn_chunk_fwd_segmented.argtypes = fwd + [i32, i32, vp, ctypes.c_size_t, vp]
     lib.gdn_chunk_fwd_segmented.restype = i32
+    lib.gdn_chunk_fwd_noalloc.argtypes = fwd + [i32, vp]
+    lib.gdn_chunk_fwd_noalloc.restype = i32
     lib.gdn_decode_step.argtypes = [i32] * 6 + [vp, vp, vp, fp, fp, fp, vp, vp]
     lib.gdn_kda_recurrent_fwd.argtypes = fwd + [vp]
     lib.gdn_kda_recurrent_fwd.restype = i32
@@ -263,6 +266,21 @@ def chunk_fwd(q, k, v, alpha, beta, *, chunk: int = 64, cu_seqlens=None, h0=None
         where = "gdn_chunk_fwd_segmented"
     if st != GDN_SUCCESS:
         raise GDNError(st, where)
+    return o, hT
+
+
+def chunk_fwd_noalloc(q, k, v, alpha, beta, *, chunk: int = 64, cu_seqlens=None, h0=None, o=None,
+                      hT=None, output_final_state: bool = True, stream=None) -> Tuple:
+    """chunk_fwd without a workspace: the library's static per-GPU scratch
+    (32 MiB) serves instead.  Calls that overlap on one GPU race on it.
+    Returns (o, hT); ``o`` and ``hT`` are allocated here only when omitted."""
+    dims, n_seqs, o, hT = _fwd_args(q, k, v, alpha, beta, cu_seqlens, h0, o, hT,
+                                    output_final_state)
+    st = load().gdn_chunk_fwd_noalloc(*dims, _ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(beta),
+                                      _ptr(cu_seqlens), n_seqs, _ptr(h0), _ptr(o), _ptr(hT), chunk,
+                                      _stream(stream))
+    if st != GDN_SUCCESS:
+        raise GDNError(st, "gdn_chunk_fwd_noalloc")
     return o, hT
 
 

@@ -77,7 +77,7 @@ static int32_t check_common(int32_t B, int32_t T, int32_t H_qk, int32_t H_v, int
   return GDN_SUCCESS;
 }
 
-static int32_t make_problem(int32_t B, int32_t T, int32_t H_qk, int32_t H_v, int32_t d_k,
+int32_t make_problem(int32_t B, int32_t T, int32_t H_qk, int32_t H_v, int32_t d_k,
                             int32_t d_v, int32_t dtype, const void *q, const void *k,
                             const void *v, const float *alpha, const float *beta,
                             const int32_t *cu_seqlens, int32_t n_seqs, const float *h0,
@@ -119,7 +119,7 @@ static int32_t status_of(hipError_t e) { return e == hipSuccess ? GDN_SUCCESS : 
 // Measured on MI355X, long context T = 65536, d = 128, one pass vs segments
 // of 16 / 32 / 64 / 128 / 256 chunks: 16 heads 1,123 vs
 // 1,150 / 957 / 886 / 844 / 921 us; 2 heads 863 vs 319 / 221 / 200 / 271 / 459 us.
-static int32_t plan_segment_chunks(const Problem &p) {
+int32_t plan_segment_chunks(const Problem &p) {
   const int64_t units = int64_t(p.n_seqs) * p.H_v;
   const int64_t max_chunks = ceil_div(p.T, p.chunk);  // the longest sequence's chunks, at most
   if (units == 0 || units * std::max(1, p.d_v / 32) >= 128) return 0;
@@ -172,7 +172,7 @@ static size_t seg_workspace_layout(const Problem &p, int32_t seg_chunks, void *b
   return cu_bytes + first_bytes + ws_bytes + mb_bytes + sin_bytes;
 }
 
-static size_t chunk_workspace_bytes(const Problem &p, int32_t seg_chunks) {
+size_t chunk_workspace_bytes(const Problem &p, int32_t seg_chunks) {
   return seg_chunks > 0 ? seg_workspace_layout(p, seg_chunks, nullptr, nullptr)
                         : workspace_layout(p, nullptr, nullptr);
 }
@@ -216,8 +216,8 @@ static bool seg_chunks_ok(const Problem &p, int32_t seg_chunks) {
   return bound < (int64_t(1) << 30) && bound * p.H_v * std::max(p.d_v, 32) / 16 < 0x7fffffff;
 }
 
-static int32_t run_chunk_fwd(Problem p, int32_t seg_chunks, void *workspace, size_t workspace_bytes,
-                             hipStream_t s) {
+int32_t run_chunk_fwd(Problem p, int32_t seg_chunks, void *workspace, size_t workspace_bytes,
+                      hipStream_t s) {
   const size_t need = chunk_workspace_bytes(p, seg_chunks);
   if (!workspace || workspace_bytes < need) return GDN_ERROR_WORKSPACE;
   if (reinterpret_cast<uintptr_t>(workspace) & 255) return GDN_ERROR_WORKSPACE;

@@ -99,4 +99,13 @@ hipError_t launch_decode(const Problem &p, float *state, hipStream_t st);
 
 SeqGeom make_geom(const Problem &p, const Workspace *ws);
 
+// Host-side steps of the chunked forward shared by its entry points (api.hip).
+int32_t make_problem(int32_t B, int32_t T, int32_t H_qk, int32_t H_v, int32_t d_k, int32_t d_v, int32_t dtype,
+                     const void *q, const void *k, const void *v, const float *alpha, const float *beta,
+                     const int32_t *cu_seqlens, int32_t n_seqs, const float *h0, void *o, float *hT,
+                     Problem *p);
+int32_t plan_segment_chunks(const Problem &p);
+size_t chunk_workspace_bytes(const Problem &p, int32_t seg_chunks);
+int32_t run_chunk_fwd(Problem p, int32_t seg_chunks, void *workspace, size_t workspace_bytes, hipStream_t s);
+
 }  // namespace gdn

@@ -173,6 +173,28 @@ int32_t gdn_chunk_fwd_segmented(int32_t B, int32_t T, int32_t H_qk, int32_t H_v,
                                 int32_t seg_chunks, void *workspace, size_t workspace_bytes, void *stream);
 
 /*
+ * gdn_chunk_fwd_noalloc -- gdn_chunk_fwd for callers that cannot allocate
+ * device memory around a call (code under HIP graph capture, tight serving
+ * loops, harnesses that forbid allocation): the same arguments without the
+ * workspace, the same result.
+ *
+ * The scratch lives in one static device array of 32 MiB (33,554,432 bytes)
+ * per GPU, held until the process ends; the call allocates and frees
+ * nothing.  A problem whose gdn_chunk_fwd_workspace_bytes(...) exceeds
+ * 32 MiB is rejected with GDN_ERROR_WORKSPACE before anything is launched
+ * (the prefill batch B=4, T=4096, H=16, d=128 needs about 24 MB).  All calls
+ * on one GPU share that array: calls that overlap on one GPU (on different
+ * streams, or from different threads) race on it and must be ordered by the
+ * caller.  The first call on a device looks the array's address up on that
+ * device (the current one).
+ */
+int32_t gdn_chunk_fwd_noalloc(int32_t B, int32_t T, int32_t H_qk, int32_t H_v, int32_t d_k, int32_t d_v,
+                              int32_t dtype, const void *q, const void *k, const void *v,
+                              const float *alpha, const float *beta, const int32_t *cu_seqlens,
+                              int32_t n_seqs, const float *h0, void *o, float *hT, int32_t chunk,
+                              void *stream);
+
+/*
  * gdn_decode_step -- one new token per sequence, state updated in place.
  *
  * The generation step of "Attention as Matrix Algebra" (section 9: about 6rd

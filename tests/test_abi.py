@@ -68,7 +68,8 @@ def fwd(lib, fn, B=1, T=8, H_qk=1, H_v=1, d_k=64, d_v=64, dtype=0, ptrs=True, cu
 @pytest.mark.parametrize("fn,extra", [("gdn_recurrent_fwd", (None,)),
                                       ("gdn_kda_recurrent_fwd", (None,)),
                                       ("gdn_chunk_fwd", (64, None, 0, None)),
-                                      ("gdn_kda_chunk_fwd", (64, None, 0, None))])
+                                      ("gdn_kda_chunk_fwd", (64, None, 0, None)),
+                                      ("gdn_chunk_fwd_noalloc", (64, None))])
 def test_argument_errors_are_reported_before_launch(lib, fn, extra):
     # every case below fails validation, so no kernel is launched
     assert fwd(lib, fn, d_k=48, extra=extra) == 2
@@ -172,6 +173,7 @@ def test_host_path_reaches_launch_without_gpu(lib):
     assert lib.gdn_decode_step(2, 1, 1, 64, 64, 1, p, p, p, p, p, p, p, None) == 4
     assert lib.gdn_kda_recurrent_fwd(*base, None) == 4
     assert lib.gdn_kda_chunk_fwd(*base, 64, ws, 1 << 30, None) == 4
+    assert lib.gdn_chunk_fwd_noalloc(*base, 64, None) == 4   # no device: the scratch has no address
     assert lib.gdn_kda_decode_step(2, 1, 1, 64, 64, 1, p, p, p, p, p, p, p, None) == 4
     assert prologue(lib) == 4
     assert lib.gdn_block_epilogue(1, 8, 1, 64, 0, p, p, None, 1e-6, p, None) == 4
@@ -232,3 +234,13 @@ def test_kda_chunk_workspace(lib):
     assert lib.gdn_kda_chunk_fwd(*args, 48, p, 1 << 30, None) == 2
     assert lib.gdn_kda_chunk_fwd(*args, 64, None, 1 << 30, None) == 3
     assert lib.gdn_kda_chunk_fwd(*args, 64, p, 64, None) == 3
+
+
+def test_noalloc_argument_errors(lib):
+    p = ctypes.c_void_p(0x1000)
+    base = [1, 8, 1, 1, 64, 64, 0, p, p, p, p, p, None, 0, None, p, None]
+    assert lib.gdn_chunk_fwd_noalloc(*base, 48, None) == 2          # unsupported chunk
+    # a problem whose scratch exceeds the 32 MiB array: rejected before any launch
+    big = [8, 4096, 16, 16, 128, 128, 1, p, p, p, p, p, None, 0, None, p, None]
+    assert gdn.chunk_fwd_workspace_bytes(8, 4096, 16, 16, 128, 128, 1, 64, 0) > (32 << 20)
+    assert lib.gdn_chunk_fwd_noalloc(*big, 64, None) == 3
