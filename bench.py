@@ -244,6 +244,38 @@ def kda_decode_workload(args, gdn, torch, dev, stream, evict, Dd, state):
     }}
 
 
+def kda_chunk_workload(args, gdn, gi, torch, dev, stream, evict):
+    """The per-channel-gate chunked forward on the prefill shape (B=4, T=4096,
+    H=16, d=128, bf16, chunk 64): q, k, v, beta as the prefill workload,
+    one decay rate per key channel drawn uniform in [0.8, 1)."""
+    spec = gi.config(2)
+    B, T = spec.B, spec.T
+    q, k, v, _, beta = device_inputs(torch, dev, spec, B * T, B, seed=spec.seed + 7)
+    g = torch.Generator(device=dev)
+    g.manual_seed(92)
+    alpha = 0.8 + 0.2 * torch.rand((B, T, spec.H_v, spec.d_k), generator=g, device=dev)
+    o = torch.empty_like(v)
+    hT = torch.empty((B, spec.H_v, spec.d_k, spec.d_v), dtype=torch.float32, device=dev)
+    ws = torch.empty(gdn.kda_chunk_fwd_workspace_bytes(B, T, spec.H_qk, spec.H_v, spec.d_k, spec.d_v, gdn.GDN_BF16,
+                                                       64, 0), dtype=torch.uint8, device=dev)
+    log("bench: per-channel-gate chunked forward, prefill shape")
+
+    def call():
+        gdn.kda_chunk_fwd(q, k, v, alpha, beta, chunk=64, o=o, hT=hT, workspace=ws, stream=stream)
+
+    t = timed_calls(args, torch, stream, evict, call)
+    tokens, units = B * T, B * spec.H_v
+    # q, k, v, o in bf16, the rates (d_k fp32) and beta per token-unit, the final states
+    nbytes = tokens * spec.H_v * (4 * 128 * 2 + 128 * 4 + 4) + units * 128 * 128 * 4
+    flops = tokens * spec.H_v * PREFILL_FLOPS_PER_TOKEN_UNIT
+    del q, k, v, alpha, beta, o, hT, ws
+    return {"kda_chunk": {
+        "workload": f"per-channel gate chunked forward B={B} T={T} H={spec.H_v} d=128 bf16 chunk 64",
+        "tokens_per_s": tokens / t, "us_per_call": t * 1e6, "bytes": nbytes,
+        "hbm_frac": nbytes / t / HBM_PEAK, "mfma_frac": flops / t / MFMA_BF16_PEAK,
+    }}
+
+
 def decode_graph_workload(args, gdn, torch, dev, stream):
     """A serving loop of 64 decode steps at batch 1 (H=32, d=128, bf16), launched
     eagerly and as one captured HIP graph: the per-step time shows the launch
@@ -483,6 +515,7 @@ def main():
         extra = extra_workloads(args, gi, gdn, torch, dev, stream, evict)
         extra.update(block_workload(args, gdn, torch, dev, stream, evict))
         extra.update(kda_decode_workload(args, gdn, torch, dev, stream, evict, Dd, state))
+        extra.update(kda_chunk_workload(args, gdn, gi, torch, dev, stream, evict))
         extra.update(decode_graph_workload(args, gdn, torch, dev, stream))
 
     tokens = B * T
