@@ -110,17 +110,73 @@ def to_dev(a, torch, dev):
     return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
 
 
-def cpu_baseline(w):
-    """The oracle as it stands, on this host's cores, over the whole prefill batch."""
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
+def cpu_baseline(w, gi):
+    """The oracle as it stands, on this host's cores: the whole prefill batch
+    (the headline), and bounded samples of the other workloads, each timed
+    on the float64 recurrence alone (not input generation).
+
+    long context: all 16 heads over its first 8,192 tokens;
+    packed batch: every head of its first 8 sequences;
+    decode: one step of 32 of the 256 sequences (1,024 of 8,192 units) from a
+    random fp32 state, and the 512-token warm-up forward of the same 1,024
+    units.  Rates are per token of the full workload (a token carries every
+    head) and, for decode, per full-batch step.
+    """
     import oracle
     threads = oracle.cpu_threads()
-    t0 = time.perf_counter()
-    oracle.forward(w.q, w.k, w.v, w.alpha, w.beta, return_o=True, threads=threads)
-    dt = time.perf_counter() - t0
+
+    def timed(fn):
+        t0 = time.perf_counter()
+        fn()
+        return time.perf_counter() - t0
+
+    dt = timed(lambda: oracle.forward(w.q, w.k, w.v, w.alpha, w.beta, return_o=True, threads=threads))
     tokens = w.B * w.T
-    return {"value": tokens / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
-            "sample": f"whole prefill batch (B={w.B}, T={w.T}, H={w.spec.H_v}, d=128; "
-                      f"{tokens * w.spec.H_v} token-units) in {dt:.2f} s, float64"}
+    out = {"value": tokens / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+           "cpu_model": cpu_model(),
+           "sample": f"whole prefill batch (B={w.B}, T={w.T}, H={w.spec.H_v}, d=128; "
+                     f"{tokens * w.spec.H_v} token-units) in {dt:.2f} s, float64"}
+    others = {}
+    # long context, the first 8,192 tokens of all 16 heads
+    wl = gi.generate(gi.config(4, T=8192, name="long-cpu-sample"))
+    dt = timed(lambda: oracle.forward(wl.q, wl.k, wl.v, wl.alpha, wl.beta, return_o=True, threads=threads))
+    units = wl.spec.H_v * wl.T
+    others["long_context"] = {"tokens_per_s": wl.T / dt, "token_units_per_s": units / dt,
+                              "sample": f"first {wl.T} of 65536 tokens, all 16 heads ({units} token-units) "
+                                        f"in {dt:.2f} s"}
+    # packed batch, first 8 sequences, all 32 heads
+    wv = gi.generate(gi.config(5))
+    sel = [(i, j) for i in range(8) for j in range(wv.spec.H_v)]
+    n_tok = int(wv.cu_seqlens[8])
+    dt = timed(lambda: oracle.forward(wv.q, wv.k, wv.v, wv.alpha, wv.beta, cu_seqlens=wv.cu_seqlens,
+                                      units=sel, threads=threads))
+    others["varlen"] = {"tokens_per_s": n_tok / dt, "token_units_per_s": n_tok * wv.spec.H_v / dt,
+                        "sample": f"8 of 32 packed sequences ({n_tok} tokens x 32 heads) in {dt:.2f} s"}
+    # decode: 32 of 256 sequences
+    s3 = gi.config(3, B=32, name="decode-cpu-sample")
+    wd = gi.generate(s3)
+    state = gi.random_state((32, s3.H_v, 128, 128), seed=3, scale=0.3)
+    dt = timed(lambda: oracle.decode(state, wd.q, wd.k, wd.v, wd.alpha, wd.beta, threads=threads))
+    others["decode_step"] = {"steps_per_s": (32 * s3.H_v) / dt / 8192, "units_per_s": 32 * s3.H_v / dt,
+                             "sample": f"one step of 32 of 256 sequences (1,024 units) in {dt:.3f} s"}
+    ww = gi.generate(gi.decode_warmup_spec(s3))
+    dt = timed(lambda: oracle.forward(ww.q, ww.k, ww.v, ww.alpha, ww.beta, return_o=False, threads=threads))
+    others["decode_warmup"] = {"tokens_per_s": 32 * ww.T / dt, "token_units_per_s": 32 * ww.T * s3.H_v / dt,
+                               "sample": f"512-token forward of 32 sequences x 32 heads in {dt:.2f} s"}
+    out["other_workloads"] = others
+    del wl, wv, wd, ww, state
+    return out
 
 
 def device_inputs(torch, dev, spec, n_tokens, B, seed):
@@ -581,7 +637,7 @@ def main():
         result["calibration_copy_GBps"] = copy_gbps
     if not args.no_cpu_baseline:
         log("bench: cpu baseline (float64 oracle on host cores)")
-        result["cpu_baseline"] = cpu_baseline(wp)
+        result["cpu_baseline"] = cpu_baseline(wp, gi)
     print(json.dumps(result), flush=True)
 
 
