@@ -99,6 +99,29 @@ def decode_traffic():
     return rec.get("hbm_bytes_per_launch")
 
 
+CHUNK_COUNTERS_FILE = os.path.join(ROOT, "profiles", "chunk_fwd_B4_H16_T4096_d128.counters.json")
+CHUNK_SOURCES = {n: os.path.join(ROOT, "gated_delta_rule_03_amd", "csrc", n) for n in ("prep.hip", "scan.hip")}
+
+
+def chunk_counters():
+    """Counter figures of the prefill chunked forward's kernels (MFMA busy,
+    MFMA flop, HBM bytes), if taken on the current prep.hip and scan.hip."""
+    try:
+        with open(CHUNK_COUNTERS_FILE) as f:
+            rec = json.load(f)
+        for name, path in CHUNK_SOURCES.items():
+            with open(path, "rb") as f:
+                if rec["source_sha256"].get(name) != hashlib.sha256(f.read()).hexdigest():
+                    return None
+    except (OSError, ValueError, KeyError):
+        return None
+    call = rec["call"]
+    return {"mfma_busy_frac": call["mfma_busy_frac_time_weighted"], "mfma_flop_executed": call["mfma_flop"],
+            "hbm_bytes": call["hbm_bytes"], "traffic_over_algorithmic": call["traffic_over_algorithmic"],
+            "kernel_us": call["kernel_us"],
+            "per_kernel_mfma_busy": {k: v["mfma_busy_frac"] for k, v in rec["kernels"].items()}}
+
+
 def log(msg):
     print(msg, file=sys.stderr, flush=True)
 
@@ -629,6 +652,7 @@ def main():
             "mfma_frac": prefill_flops / chunk_s / MFMA_BF16_PEAK,
             "achieved_GBps": prefill_bytes / chunk_s / 1e9,
             "achieved_TFLOPs": prefill_flops / chunk_s / 1e12,
+            "counters": chunk_counters(),
         },
         "wall_s_timed_region": wall,
     }
