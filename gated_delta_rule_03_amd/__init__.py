@@ -11,8 +11,9 @@ Names follow the C ABI: ``recurrent_fwd``, ``chunk_fwd`` (with
 ``chunk_fwd_workspace_bytes``; ``seg_chunks`` selects the segment-parallel
 form of ``gdn_chunk_fwd_segmented``, with ``chunk_fwd_plan_segments`` and
 ``chunk_fwd_segmented_workspace_bytes``), ``decode_step``, the GDN block's
-``block_prologue`` and ``block_epilogue``, and the per-channel-gate
-``kda_recurrent_fwd`` and ``kda_decode_step``.
+``block_prologue`` and ``block_epilogue``, the per-channel-gate
+``kda_recurrent_fwd``, ``kda_chunk_fwd`` and ``kda_decode_step``, and the
+backward pass ``chunk_bwd`` (with ``chunk_bwd_workspace_bytes``).
 """
 from __future__ import annotations
 
@@ -25,7 +26,7 @@ __all__ = [
     "chunk_fwd", "chunk_fwd_workspace_bytes", "chunk_fwd_plan_segments",
     "chunk_fwd_segmented_workspace_bytes", "chunk_fwd_noalloc", "decode_step", "block_prologue", "block_epilogue",
     "kda_recurrent_fwd", "kda_chunk_fwd", "kda_chunk_fwd_workspace_bytes", "kda_decode_step",
-    "GDN_F32", "GDN_BF16",
+    "chunk_bwd", "chunk_bwd_workspace_bytes", "GDN_F32", "GDN_BF16",
 ]
 
 GDN_SUCCESS = 0
@@ -41,7 +42,8 @@ EXPORTS = ["gdn_version", "gdn_status_string", "gdn_recurrent_fwd",
            "gdn_chunk_fwd_segmented_workspace_bytes", "gdn_chunk_fwd_segmented", "gdn_chunk_fwd_noalloc",
            "gdn_decode_step",
            "gdn_block_prologue", "gdn_block_epilogue", "gdn_kda_recurrent_fwd",
-           "gdn_kda_chunk_fwd_workspace_bytes", "gdn_kda_chunk_fwd", "gdn_kda_decode_step"]
+           "gdn_kda_chunk_fwd_workspace_bytes", "gdn_kda_chunk_fwd", "gdn_kda_decode_step",
+           "gdn_chunk_bwd_workspace_bytes", "gdn_chunk_bwd"]
 
 
 class GDNError(RuntimeError):
@@ -102,6 +104,11 @@ def load() -> ctypes.CDLL:
     lib.gdn_block_prologue.restype = i32
     lib.gdn_block_epilogue.argtypes = [i32] * 5 + [vp, vp, fp, f32, vp, vp]
     lib.gdn_block_epilogue.restype = i32
+    lib.gdn_chunk_bwd_workspace_bytes.argtypes = [i32] * 9
+    lib.gdn_chunk_bwd_workspace_bytes.restype = ctypes.c_size_t
+    lib.gdn_chunk_bwd.argtypes = ([i32] * 7 + [vp, vp, vp, fp, fp, vp, i32, fp, vp, fp]
+                                  + [fp] * 6 + [i32, vp, ctypes.c_size_t, vp])
+    lib.gdn_chunk_bwd.restype = i32
     _lib = lib
     return lib
 
@@ -267,6 +274,49 @@ def chunk_fwd(q, k, v, alpha, beta, *, chunk: int = 64, cu_seqlens=None, h0=None
     if st != GDN_SUCCESS:
         raise GDNError(st, where)
     return o, hT
+
+
+def chunk_bwd_workspace_bytes(B, T, H_qk, H_v, d_k, d_v, dtype_code, chunk=64, n_seqs=0) -> int:
+    return int(load().gdn_chunk_bwd_workspace_bytes(B, T, H_qk, H_v, d_k, d_v, dtype_code, chunk, n_seqs))
+
+
+def chunk_bwd(q, k, v, alpha, beta, d_o, *, chunk: int = 64, cu_seqlens=None, h0=None, dhT=None,
+              want_dh0: bool = True, workspace=None, stream=None) -> Tuple:
+    """Gradients of L = sum <d_o, o> + <dhT, hT> (gdn_chunk_bwd).
+
+    Returns (dq, dk, dv, dalpha, dbeta, dh0), all float32; dq and dk sum over
+    the value heads that read each query/key head; dh0 is None unless
+    ``want_dh0``.
+    """
+    torch = _torch()
+    dims, n_seqs, _, _ = _fwd_args(q, k, v, alpha, beta, cu_seqlens, h0, d_o, None, False)
+    B, T, H_qk, H_v, d_k, d_v, code = dims
+    N = n_seqs if cu_seqlens is not None else B
+    dev = q.device
+    if dhT is not None:
+        _check(dhT, "dhT", (N, H_v, d_k, d_v), torch.float32, dev)
+    f32 = dict(dtype=torch.float32, device=dev)
+    dq = torch.empty((B, T, H_qk, d_k), **f32)
+    dk = torch.empty((B, T, H_qk, d_k), **f32)
+    dv = torch.empty((B, T, H_v, d_v), **f32)
+    dalpha = torch.empty((B, T, H_v), **f32)
+    dbeta = torch.empty((B, T, H_v), **f32)
+    dh0 = torch.empty((N, H_v, d_k, d_v), **f32) if want_dh0 else None
+    need = chunk_bwd_workspace_bytes(*dims, chunk, n_seqs)
+    if need == 0:
+        raise GDNError(2, "gdn_chunk_bwd_workspace_bytes")
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    elif workspace.numel() * workspace.element_size() < need:
+        raise ValueError(f"workspace holds {workspace.numel() * workspace.element_size()} "
+                         f"bytes, {need} needed")
+    st = load().gdn_chunk_bwd(*dims, _ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(beta), _ptr(cu_seqlens),
+                              n_seqs, _ptr(h0), _ptr(d_o), _ptr(dhT), _ptr(dq), _ptr(dk), _ptr(dv),
+                              _ptr(dalpha), _ptr(dbeta), _ptr(dh0), chunk, _ptr(workspace),
+                              workspace.numel() * workspace.element_size(), _stream(stream))
+    if st != GDN_SUCCESS:
+        raise GDNError(st, "gdn_chunk_bwd")
+    return dq, dk, dv, dalpha, dbeta, dh0
 
 
 def chunk_fwd_noalloc(q, k, v, alpha, beta, *, chunk: int = 64, cu_seqlens=None, h0=None, o=None,

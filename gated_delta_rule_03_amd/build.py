@@ -14,7 +14,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libgdn.so")
-SOURCES = ["api.hip", "seqmap.hip", "prep.hip", "scan.hip", "fold.hip", "kda_chunk.hip", "noalloc.hip", "decode.hip", "recurrent.hip", "block.hip"]
+SOURCES = ["api.hip", "seqmap.hip", "prep.hip", "scan.hip", "fold.hip", "kda_chunk.hip", "noalloc.hip", "decode.hip", "recurrent.hip", "block.hip", "bwd.hip"]
 ARCH = os.environ.get("GDN_OFFLOAD_ARCH", "gfx950")
 
 HIPCC_FLAGS = [

@@ -244,6 +244,32 @@ int32_t run_chunk_fwd(Problem p, int32_t seg_chunks, void *workspace, size_t wor
   return status_of(e);
 }
 
+// Workspace of the backward pass: chunk offsets, the chunk-start states, the
+// per-value-head dq and dk, and each unit's fp32 intermediates.
+size_t bwd_workspace_layout(const Problem &p, void *base, BwdProblem *b) {
+  const int64_t tokens = p.n_tokens();
+  const size_t off_bytes = align256(size_t(2 * int64_t(p.n_seqs) + 1) * sizeof(int32_t));
+  const size_t st_bytes = align256(size_t(chunk_slots(p)) * p.H_v * p.d_k * p.d_v * sizeof(float));
+  const size_t part_bytes = align256(size_t(tokens) * p.H_v * p.d_k * sizeof(float));
+  const size_t scr_bytes =
+      align256(size_t(p.n_seqs) * p.H_v * bwd_unit_floats(p.chunk, p.d_k, p.d_v) * sizeof(float));
+  if (b) {
+    char *c = static_cast<char *>(base);
+    b->ws.chunk_off = reinterpret_cast<int32_t *>(c);
+    b->ws.seq_order = b->ws.chunk_off + p.n_seqs + 1;
+    b->ws.entries = nullptr;
+    c += off_bytes;
+    b->states = reinterpret_cast<float *>(c);
+    c += st_bytes;
+    b->dq_part = reinterpret_cast<float *>(c);
+    c += part_bytes;
+    b->dk_part = reinterpret_cast<float *>(c);
+    c += part_bytes;
+    b->scratch = reinterpret_cast<float *>(c);
+  }
+  return off_bytes + st_bytes + 2 * part_bytes + scr_bytes;
+}
+
 }  // namespace gdn
 
 using namespace gdn;
@@ -325,6 +351,49 @@ int32_t gdn_chunk_fwd_segmented(int32_t B, int32_t T, int32_t H_qk, int32_t H_v,
   if (seg_chunks < 0) return GDN_ERROR_INVALID_VALUE;
   if (!seg_chunks_ok(p, seg_chunks)) return GDN_ERROR_NOT_SUPPORTED;
   return run_chunk_fwd(p, seg_chunks, workspace, workspace_bytes, static_cast<hipStream_t>(stream));
+}
+
+size_t gdn_chunk_bwd_workspace_bytes(int32_t B, int32_t T, int32_t H_qk, int32_t H_v, int32_t d_k,
+                                     int32_t d_v, int32_t dtype, int32_t chunk, int32_t n_seqs) {
+  if (!query_ok(B, T, H_qk, H_v, d_k, d_v, dtype, chunk, n_seqs)) return 0;
+  const Problem p = query_problem(B, T, H_qk, H_v, d_k, d_v, dtype, chunk, n_seqs);
+  return bwd_workspace_layout(p, nullptr, nullptr);
+}
+
+int32_t gdn_chunk_bwd(int32_t B, int32_t T, int32_t H_qk, int32_t H_v, int32_t d_k, int32_t d_v, int32_t dtype,
+                      const void *q, const void *k, const void *v, const float *alpha, const float *beta,
+                      const int32_t *cu_seqlens, int32_t n_seqs, const float *h0, const void *d_o,
+                      const float *dhT, float *dq, float *dk, float *dv, float *dalpha, float *dbeta, float *dh0,
+                      int32_t chunk, void *workspace, size_t workspace_bytes, void *stream) {
+  Problem p;
+  // d_o takes the place of o in the forward's checks (required, 16-byte aligned)
+  int32_t st = make_problem(B, T, H_qk, H_v, d_k, d_v, dtype, q, k, v, alpha, beta, cu_seqlens, n_seqs, h0,
+                            const_cast<void *>(d_o), nullptr, &p);
+  if (st != GDN_SUCCESS) return st;
+  if (chunk != 16 && chunk != 32 && chunk != 64) return GDN_ERROR_NOT_SUPPORTED;
+  if (p.n_tokens() > 0 && (!dq || !dk || !dv || !dalpha || !dbeta)) return GDN_ERROR_INVALID_VALUE;
+  if (!aligned16(dhT) || !aligned16(dh0)) return GDN_ERROR_INVALID_VALUE;
+  p.chunk = chunk;
+  p.o = nullptr;
+  const size_t need = bwd_workspace_layout(p, nullptr, nullptr);
+  if (!workspace || workspace_bytes < need) return GDN_ERROR_WORKSPACE;
+  if (reinterpret_cast<uintptr_t>(workspace) & 255) return GDN_ERROR_WORKSPACE;
+  BwdProblem b;
+  b.p = p;
+  bwd_workspace_layout(p, workspace, &b);
+  b.d_o = d_o;
+  b.dhT = dhT;
+  b.dq = dq;
+  b.dk = dk;
+  b.dv = dv;
+  b.dalpha = dalpha;
+  b.dbeta = dbeta;
+  b.dh0 = dh0;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e = launch_chunk_offsets(p, b.ws, s);
+  if (e == hipSuccess) e = launch_recurrent_states(p, b.ws, b.states, s);
+  if (e == hipSuccess) e = launch_chunk_bwd(b, s);
+  return status_of(e);
 }
 
 int32_t gdn_decode_step(int32_t B, int32_t H_qk, int32_t H_v, int32_t d_k, int32_t d_v,

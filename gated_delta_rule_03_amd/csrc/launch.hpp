@@ -71,6 +71,23 @@ hipError_t launch_chunk_offsets(const Problem &p, const Workspace &ws, hipStream
 hipError_t launch_prep(const Problem &p, const Workspace &ws, hipStream_t st);
 hipError_t launch_scan(const Problem &p, const Workspace &ws, hipStream_t st, float *mb = nullptr);
 hipError_t launch_recurrent(const Problem &p, hipStream_t st);
+// The token-by-token forward writing the state that enters every chunk of
+// p.chunk tokens to states [chunk slot, H_v, d_k, d_v] (o and hT may be null).
+hipError_t launch_recurrent_states(const Problem &p, const Workspace &ws, float *states, hipStream_t st);
+
+// Backward pass of the chunked form (bwd.hip).
+struct BwdProblem {
+  Problem p;             // the forward problem (its o and hT are unused)
+  Workspace ws;          // chunk offsets of a packed batch
+  const void *d_o;       // dL/do, [tokens, H_v, d_v] in the input dtype
+  const float *dhT;      // dL/dS_T or null
+  float *states;         // [chunk slots, H_v, d_k, d_v]: chunk-start states
+  float *dq_part, *dk_part;  // [tokens, H_v, d_k]: per value head
+  float *scratch;        // per-unit intermediates, bwd_unit_floats each
+  float *dq, *dk, *dv, *dalpha, *dbeta, *dh0;
+};
+size_t bwd_unit_floats(int chunk, int d_k, int d_v);
+hipError_t launch_chunk_bwd(const BwdProblem &b, hipStream_t st);
 hipError_t launch_kda_chunk(const Problem &p, const Workspace &ws, hipStream_t st);
 // Segment-parallel path (seqmap.hip, fold.hip).
 hipError_t launch_segment_map(const Problem &p, int seg_tokens, int n_seg_bound, int32_t *seg_cu,

@@ -195,6 +195,44 @@ int32_t gdn_chunk_fwd_noalloc(int32_t B, int32_t T, int32_t H_qk, int32_t H_v, i
                               void *stream);
 
 /*
+ * gdn_chunk_bwd -- gradients of the gated delta rule for training in chunks.
+ *
+ * The pages motivate chunked training ("From KV Cache to a State Matrix:
+ * Linear Attention and DeltaNet", section "Chunkwise training for DeltaNet";
+ * "Attention as Matrix Algebra", section 8) and print no gradients; these
+ * are the reverse-mode derivatives of the forward of gdn_recurrent_fwd
+ * ("Linear attention", Eqs. (1)-(4)) for the loss
+ *   L = sum_t <d_o_t, o_t> + <dhT, S_T>   (per sequence and value head),
+ * evaluated chunk by chunk from the chunk-start states of a token-by-token
+ * forward, in fp32.
+ *
+ * Inputs as gdn_chunk_fwd (q, k, v, alpha, beta, cu_seqlens, n_seqs, h0,
+ * chunk, workspace), plus:
+ *   d_o    dL/do, [B, T, H_v, d_v] in the input dtype (required when T > 0).
+ *   dhT    dL/dS_T, [N, H_v, d_k, d_v] fp32, or NULL (zero).
+ * Outputs, all fp32 and written in full:
+ *   dq, dk     [B, T, H_qk, d_k]: summed over the value heads that read each
+ *              query/key head (v head j reads qk head floor(j H_qk / H_v)).
+ *   dv         [B, T, H_v, d_v].
+ *   dalpha     [B, T, H_v]: dL/dalpha, computed as dL/d(ln alpha) / alpha, so
+ *              alpha must be > 0 for a finite result.
+ *   dbeta      [B, T, H_v].
+ *   dh0        [N, H_v, d_k, d_v], or NULL (not written).
+ * gdn_chunk_bwd_workspace_bytes gives the workspace bytes (0 = unsupported
+ * arguments): chunk-start states, per-value-head dq and dk, and per unit
+ * about (8 C^2 + 12 C max(d_k, d_v) + 2 d_k d_v) floats of intermediates.
+ * Errors as gdn_chunk_fwd; GDN_ERROR_INVALID_VALUE when an output is NULL
+ * for a non-empty batch or a pointer is misaligned.
+ */
+size_t gdn_chunk_bwd_workspace_bytes(int32_t B, int32_t T, int32_t H_qk, int32_t H_v, int32_t d_k,
+                                     int32_t d_v, int32_t dtype, int32_t chunk, int32_t n_seqs);
+int32_t gdn_chunk_bwd(int32_t B, int32_t T, int32_t H_qk, int32_t H_v, int32_t d_k, int32_t d_v, int32_t dtype,
+                      const void *q, const void *k, const void *v, const float *alpha, const float *beta,
+                      const int32_t *cu_seqlens, int32_t n_seqs, const float *h0, const void *d_o,
+                      const float *dhT, float *dq, float *dk, float *dv, float *dalpha, float *dbeta, float *dh0,
+                      int32_t chunk, void *workspace, size_t workspace_bytes, void *stream);
+
+/*
  * gdn_decode_step -- one new token per sequence, state updated in place.
  *
  * The generation step of "Attention as Matrix Algebra" (section 9: about 6rd

@@ -173,6 +173,8 @@ def test_host_path_reaches_launch_without_gpu(lib):
     assert lib.gdn_decode_step(2, 1, 1, 64, 64, 1, p, p, p, p, p, p, p, None) == 4
     assert lib.gdn_kda_recurrent_fwd(*base, None) == 4
     assert lib.gdn_kda_chunk_fwd(*base, 64, ws, 1 << 30, None) == 4
+    grads = [p, None, p, p, p, p, p, None]  # d_o, dhT, dq, dk, dv, dalpha, dbeta, dh0
+    assert lib.gdn_chunk_bwd(*base[:15], *grads, 64, ws, 1 << 30, None) == 4
     assert lib.gdn_chunk_fwd_noalloc(*base, 64, None) == 4   # no device: the scratch has no address
     assert lib.gdn_kda_decode_step(2, 1, 1, 64, 64, 1, p, p, p, p, p, p, p, None) == 4
     assert prologue(lib) == 4
@@ -244,3 +246,28 @@ def test_noalloc_argument_errors(lib):
     big = [8, 4096, 16, 16, 128, 128, 1, p, p, p, p, p, None, 0, None, p, None]
     assert gdn.chunk_fwd_workspace_bytes(8, 4096, 16, 16, 128, 128, 1, 64, 0) > (32 << 20)
     assert lib.gdn_chunk_fwd_noalloc(*big, 64, None) == 3
+
+
+def test_backward_workspace_and_argument_errors(lib):
+    """gdn_chunk_bwd: workspace sizes and argument errors, all before any launch."""
+    bf, f32 = gdn.GDN_BF16, gdn.GDN_F32
+    w = gdn.chunk_bwd_workspace_bytes(4, 4096, 16, 16, 128, 128, bf, 64, 0)
+    states = 4 * 64 * 16 * 128 * 128 * 4            # chunk-start states, fp32
+    parts = 2 * 4 * 4096 * 16 * 128 * 4              # per-value-head dq and dk
+    assert states + parts < w < states + parts + 64 * 1024 * 1024
+    packed = gdn.chunk_bwd_workspace_bytes(1, 1000, 2, 4, 64, 32, f32, 32, 5)
+    assert packed >= (32 + 5) * 4 * 64 * 32 * 4 + 2 * 1000 * 4 * 64 * 4
+    assert gdn.chunk_bwd_workspace_bytes(1, 64, 1, 1, 48, 64, bf, 64, 0) == 0
+    assert gdn.chunk_bwd_workspace_bytes(1, 64, 1, 1, 64, 64, bf, 48, 0) == 0
+    p = ctypes.c_void_p(0x1000)
+    ws = ctypes.c_void_p(0x100000)
+    fwd = [1, 8, 1, 1, 64, 64, 0, p, p, p, p, p, None, 0, None]
+    good = [p, None, p, p, p, p, p, None]
+    assert lib.gdn_chunk_bwd(*fwd, None, *good[1:], 64, ws, 1 << 30, None) == 1      # d_o missing
+    assert lib.gdn_chunk_bwd(*fwd, *good[:2], None, *good[3:], 64, ws, 1 << 30, None) == 1  # dq missing
+    assert lib.gdn_chunk_bwd(*fwd, *good, 48, ws, 1 << 30, None) == 2                 # chunk
+    assert lib.gdn_chunk_bwd(*fwd, *good, 64, ws, 16, None) == 3                      # workspace too small
+    assert lib.gdn_chunk_bwd(*fwd, *good, 64, ctypes.c_void_p(0x100010), 1 << 30, None) == 3  # misaligned
+    assert lib.gdn_chunk_bwd(*fwd, *good[:7], ctypes.c_void_p(0x1004), 64, ws, 1 << 30, None) == 1  # dh0
+    bad_dtype = [1, 8, 1, 1, 64, 64, 5] + fwd[7:]
+    assert lib.gdn_chunk_bwd(*bad_dtype, *good, 64, ws, 1 << 30, None) == 2
