@@ -38,6 +38,8 @@ projections drawn on the device, and gives each kernel's algorithmic bytes
 (every input read once, every output written once) as a fraction of HBM
 peak.
 
+``chunk_bwd`` times the backward pass (gdn_chunk_bwd) on the prefill shape.
+
 ``kda_decode`` times the per-channel-gate decode step (one decay rate per key
 channel) on the decode shape, with its HBM fraction.
 
@@ -355,6 +357,31 @@ def kda_chunk_workload(args, gdn, gi, torch, dev, stream, evict):
     }}
 
 
+def chunk_bwd_workload(args, gdn, gi, torch, dev, stream, evict):
+    """The backward pass (gdn_chunk_bwd) on the prefill shape (B=4, T=4096,
+    H=16, d=128, bf16, chunk 64): the prefill workload's inputs and an
+    upstream gradient d_o ~ N(0, 1) in bf16; all gradients in fp32."""
+    spec = gi.config(2)
+    B, T = spec.B, spec.T
+    q, k, v, alpha, beta = device_inputs(torch, dev, spec, B * T, B, seed=spec.seed + 9)
+    g = torch.Generator(device=dev)
+    g.manual_seed(93)
+    d_o = torch.randn((B, T, spec.H_v, spec.d_v), generator=g, device=dev).bfloat16()
+    ws = torch.empty(gdn.chunk_bwd_workspace_bytes(B, T, spec.H_qk, spec.H_v, spec.d_k, spec.d_v, gdn.GDN_BF16,
+                                                   64, 0), dtype=torch.uint8, device=dev)
+    log("bench: backward pass, prefill shape")
+
+    def call():
+        gdn.chunk_bwd(q, k, v, alpha, beta, d_o, chunk=64, workspace=ws, stream=stream)
+
+    t = timed_calls(args, torch, stream, evict, call)
+    del q, k, v, alpha, beta, d_o, ws
+    return {"chunk_bwd": {
+        "workload": f"backward pass B={B} T={T} H={spec.H_v} d=128 bf16 inputs, fp32 gradients, chunk 64",
+        "tokens_per_s": B * T / t, "us_per_call": t * 1e6,
+    }}
+
+
 def decode_graph_workload(args, gdn, torch, dev, stream):
     """A serving loop of 64 decode steps at batch 1 (H=32, d=128, bf16), launched
     eagerly and as one captured HIP graph: the per-step time shows the launch
@@ -595,6 +622,7 @@ def main():
         extra.update(block_workload(args, gdn, torch, dev, stream, evict))
         extra.update(kda_decode_workload(args, gdn, torch, dev, stream, evict, Dd, state))
         extra.update(kda_chunk_workload(args, gdn, gi, torch, dev, stream, evict))
+        extra.update(chunk_bwd_workload(args, gdn, gi, torch, dev, stream, evict))
         extra.update(decode_graph_workload(args, gdn, torch, dev, stream))
 
     tokens = B * T

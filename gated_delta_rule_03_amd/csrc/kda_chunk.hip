@@ -319,6 +319,193 @@ __global__ __launch_bounds__(64) void kda_scan_kernel(KdaArgs<T> a) {
   }
 }
 
+// ---------------------------------------------------------------------------
+// Staged scan (bf16): one block per (sequence, value head) with one wave per
+// 16 state columns.  A chunk's entry (the fragments and Gamma_C) is the same
+// for every column, so it is copied once per block into one of two LDS
+// stages, one chunk ahead of the chunk being computed, by all waves together
+// (16 bytes per lane, straight to LDS).  The chunk's v rows come along into
+// the stage's row area.  A wave reads its 16 columns of v there and writes
+// its outputs back into the same place; once the block has passed the
+// chunk's closing barrier, the rows leave for o with 16-byte stores, before
+// the stage is refilled.  The fragments of T and P above their diagonal
+// blocks (rows 0-31, columns 32-63: fragments 1, 3, 9 and 11) are zero and
+// are neither copied nor multiplied.  Rows past a partial chunk read as zero
+// and are not stored.
+// ---------------------------------------------------------------------------
+constexpr int kKdaStagedFrags = kKdaFrags - 4;           // fragments copied
+constexpr int kKdaStGamma = kKdaStagedFrags * 1024;      // Gamma_C (512 bytes of a 1 KiB slot)
+constexpr int kKdaStRows = kKdaStGamma + 1024;           // 64 rows of v / o, d_v bf16 each (<= 16 KiB)
+constexpr int kKdaStageBytes = kKdaStRows + 64 * 128 * 2;
+__host__ __device__ constexpr int kda_slot(int f) {  // LDS slot of entry fragment f (not 1, 3, 9, 11)
+  return f - (f > 1) - (f > 3) - (f > 9) - (f > 11);
+}
+
+__global__ __launch_bounds__(512) void kda_scan_staged_kernel(KdaArgs<bf16_t> a) {
+  __shared__ __attribute__((aligned(16))) char kda_stage0[kKdaStageBytes];
+  __shared__ __attribute__((aligned(16))) char kda_stage1[kKdaStageBytes];
+  const int u = blockIdx.x;
+  if (u >= a.n_units) return;
+  const int lane = threadIdx.x & 63;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int nw = a.d_v >> 4;  // waves (16 columns each)
+  const int s = a.geo.ordered(u / a.H_v), h = u % a.H_v;
+  const int g = lane >> 4, r0 = lane & 15;
+  const int col = 16 * w + r0;
+  const int nkt = a.d_k >> 4;         // 16-row tiles of the state
+  const int nkb = (a.d_k + 31) >> 5;  // 32-deep contraction blocks over d_k
+
+  f32x4_t S[8];
+  const int64_t st_base = (int64_t(s) * a.H_v + h) * a.d_k * a.d_v;
+#pragma unroll
+  for (int rt = 0; rt < 8; ++rt) {
+    S[rt] = zero4();
+    if (rt < nkt && a.h0)
+      for (int e = 0; e < 4; ++e) S[rt][e] = a.h0[st_base + int64_t(16 * rt + 4 * g + e) * a.d_v + col];
+  }
+  int start, end;
+  a.geo.seq_bounds(s, start, end);
+  const int C = a.geo.chunk;
+  const int c_first = a.geo.first_chunk(s);
+  const int n_chunks = max(0, min((end - start + C - 1) / C, a.geo.n_slots - c_first));
+  const uint32_t row_bytes = uint32_t(2 * a.d_v);                  // one token's v (or o) of this head
+  const uint32_t tok_bytes = uint32_t(2 * int64_t(a.H_v) * a.d_v);  // token stride of v and o
+  const int row_copies = a.d_v / 8;  // row bytes / 1 KiB per copy x 64 rows
+  constexpr int64_t kEntry = kda_entry_bytes<bf16_t>();
+  // this lane's piece of a row copy: rows of row_bytes, 16 bytes per lane
+  const int lanes_per_row = int(row_bytes / 16);
+  const int row_of_lane = lane / lanes_per_row, piece = lane - row_of_lane * lanes_per_row;
+  const int rows_per_copy = 64 / lanes_per_row;
+
+  auto copy_stage = [&](int cc, char *buf) {
+    lds_t *st = lds_ptr(buf);
+    const char *entry = a.entries + (int64_t(c_first + cc) * a.H_v + h) * kEntry;
+    const i32x4_t res = buffer_rsrc(entry, uint32_t(kEntry));
+    for (int i = w; i <= kKdaStagedFrags; i += nw) {
+      if (i < kKdaStagedFrags) {
+        const int f = i + (i >= 1) + (i >= 2) + (i >= 7) + (i >= 8);  // entry fragment of slot i
+        dma16_buf(res, uint32_t(1024 * f + 16 * lane), st + 1024 * i);
+      } else {
+        dma16_buf(res, uint32_t(1024 * kKdaFrags + 16 * lane), st + kKdaStGamma);  // lanes 32-63: zeros
+      }
+    }
+    // row copy j is issued by the wave that stores row piece j (store_rows),
+    // so that its own wait orders the read of the previous rows before it
+    const int tok0 = start + cc * C;
+    const int len = min(C, end - tok0);
+    const char *vb = reinterpret_cast<const char *>(a.v) + int64_t(tok0) * tok_bytes + int64_t(h) * row_bytes;
+    const i32x4_t vres = buffer_rsrc(vb, uint32_t(len - 1) * tok_bytes + row_bytes);
+    for (int j = w; j < row_copies; j += nw) {
+      const int row = j * rows_per_copy + row_of_lane;
+      dma16_buf(vres, uint32_t(row) * tok_bytes + 16 * piece, st + kKdaStRows + 1024 * j);
+    }
+  };
+  // the rows of chunk cc's outputs, from the stage's row area, to o
+  auto store_rows = [&](int cc, char *buf) {
+    const lds_t *st = lds_ptr(buf);
+    const int tok0 = start + cc * C;
+    const int len = min(C, end - tok0);
+    char *ob = reinterpret_cast<char *>(a.o) + int64_t(tok0) * tok_bytes + int64_t(h) * row_bytes;
+    const __amdgpu_buffer_rsrc_t ores =
+        __builtin_amdgcn_make_buffer_rsrc(ob, 0, int((len - 1) * tok_bytes + row_bytes), 0x00020000);
+    for (int j = w; j < row_copies; j += nw) {
+      const u32x4_t x = lds_load<u32x4_t>(st + kKdaStRows + 1024 * j + 16 * lane);
+      const int row = j * rows_per_copy + row_of_lane;
+      __builtin_amdgcn_raw_buffer_store_b128(x, ores, uint32_t(row) * tok_bytes + 16 * piece, 0, 0);
+    }
+  };
+
+  if (n_chunks > 0) copy_stage(0, kda_stage0);
+  wait_vmem();
+  lds_barrier();
+  for (int cc = 0; cc < n_chunks; ++cc) {
+    char *cur = (cc & 1) ? kda_stage1 : kda_stage0;
+    char *nxt = (cc & 1) ? kda_stage0 : kda_stage1;
+    // the previous chunk's outputs leave the other stage before it is
+    // refilled: each wave waits for its own reads of the row pieces it then
+    // refills (lgkmcnt(0))
+    if (cc > 0) store_rows(cc - 1, nxt);
+    if (cc + 1 < n_chunks) {
+      __builtin_amdgcn_s_waitcnt((0xF) | (0x7 << 4) | (0x0 << 8) | (0x3 << 14));
+      copy_stage(cc + 1, nxt);
+    }
+    lds_t *st = lds_ptr(cur);
+    auto frag = [&](int f) {
+      Frag<bf16_t> x;
+      x.v = lds_load<bf16x8_t>(st + 1024 * kda_slot(f) + 16 * lane);
+      return x;
+    };
+    // this wave's column of v and o in the row area: row t at t * row_bytes
+    lds_t *rows = st + kKdaStRows + 2 * col;
+
+    Frag<bf16_t> Sf[4];
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) Sf[kk] = frag_from_acc<bf16_t>(S[2 * kk], S[2 * kk + 1]);
+    // Y = Khat S, OQ = Qhat S
+    f32x4_t Y[4], OQ[4];
+#pragma unroll
+    for (int rt = 0; rt < 4; ++rt) {
+      Y[rt] = zero4();
+      OQ[rt] = zero4();
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk)
+        if (kk < nkb) {
+          Y[rt] = mfma(frag(kKdaFragKh + 4 * rt + kk), Sf[kk], Y[rt]);
+          OQ[rt] = mfma(frag(kKdaFragQh + 4 * rt + kk), Sf[kk], OQ[rt]);
+        }
+    }
+    // X = V - Y, U = T X
+    f32x4_t X[4];
+#pragma unroll
+    for (int rt = 0; rt < 4; ++rt)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int t = 16 * rt + 4 * g + e;
+        X[rt][e] = float(lds_load<__bf16>(rows + t * row_bytes)) - Y[rt][e];
+      }
+    const Frag<bf16_t> Xf[2] = {frag_from_acc<bf16_t>(X[0], X[1]), frag_from_acc<bf16_t>(X[2], X[3])};
+    f32x4_t Ua[4];
+#pragma unroll
+    for (int rt = 0; rt < 4; ++rt) {
+      Ua[rt] = mfma(frag(kKdaFragT + rt * 2), Xf[0], zero4());
+      if (rt >= 2) Ua[rt] = mfma(frag(kKdaFragT + rt * 2 + 1), Xf[1], Ua[rt]);
+    }
+    const Frag<bf16_t> Uf[2] = {frag_from_acc<bf16_t>(Ua[0], Ua[1]), frag_from_acc<bf16_t>(Ua[2], Ua[3])};
+    // O = Qhat S + P U, into the row area (this wave's own column)
+#pragma unroll
+    for (int rt = 0; rt < 4; ++rt) {
+      f32x4_t acc = mfma(frag(kKdaFragP + rt * 2), Uf[0], OQ[rt]);
+      if (rt >= 2) acc = mfma(frag(kKdaFragP + rt * 2 + 1), Uf[1], acc);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) lds_store<__bf16>(rows + (16 * rt + 4 * g + e) * row_bytes, __bf16(acc[e]));
+    }
+    // S <- diag(Gamma_C) S + Ktil^T U
+#pragma unroll
+    for (int rm = 0; rm < 8; ++rm) {
+      if (rm < nkt) {
+        const f32x4_t gc = lds_load<f32x4_t>(st + kKdaStGamma + 4 * (16 * rm + 4 * g));
+        f32x4_t acc = gc * S[rm];
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk) acc = mfma(frag(kKdaFragKt + rm * 2 + kk), Uf[kk], acc);
+        S[rm] = acc;
+      }
+    }
+    // the next stage has landed; every wave's outputs are in the row area
+    wait_vmem();
+    lds_barrier();
+  }
+  if (n_chunks > 0) {
+    store_rows(n_chunks - 1, ((n_chunks - 1) & 1) ? kda_stage1 : kda_stage0);
+    wait_vmem();
+  }
+  if (a.hT) {
+#pragma unroll
+    for (int rt = 0; rt < 8; ++rt)
+      if (rt < nkt)
+        for (int e = 0; e < 4; ++e) a.hT[st_base + int64_t(16 * rt + 4 * g + e) * a.d_v + col] = S[rt][e];
+  }
+}
+
 template <typename T>
 static hipError_t launch_kda_chunk_t(const Problem &p, const Workspace &ws, hipStream_t st) {
   KdaArgs<T> a;
@@ -344,6 +531,12 @@ static hipError_t launch_kda_chunk_t(const Problem &p, const Workspace &ws, hipS
     hipLaunchKernelGGL(kda_prep_kernel<T>, dim3(unsigned(slots), unsigned(p.H_v)), dim3(512), 0, st, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
+  }
+  if constexpr (sizeof(T) == 2) {
+    // bf16: the staged scan, one block per unit
+    if (a.n_units == 0) return hipSuccess;
+    hipLaunchKernelGGL(kda_scan_staged_kernel, dim3(unsigned(a.n_units)), dim3(64 * (p.d_v / 16)), 0, st, a);
+    return hipGetLastError();
   }
   const int64_t blocks = (int64_t(p.n_seqs) * p.H_v + 7) / 8 * 8 * (p.d_v / 16);
   if (blocks == 0) return hipSuccess;

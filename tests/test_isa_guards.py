@@ -23,7 +23,7 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 CSRC = os.path.join(ROOT, "gated_delta_rule_03_amd", "csrc")
 sys.path.insert(0, ROOT)
 
-SOURCES = ["scan.hip", "prep.hip"]
+SOURCES = ["scan.hip", "prep.hip", "kda_chunk.hip"]
 
 
 def _assembly(src, tmp_path):
