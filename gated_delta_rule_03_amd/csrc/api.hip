@@ -451,6 +451,7 @@ int32_t gdn_kda_chunk_fwd(int32_t B, int32_t T, int32_t H_qk, int32_t H_v, int32
   int32_t st = make_problem(B, T, H_qk, H_v, d_k, d_v, dtype, q, k, v, alpha, beta, cu_seqlens,
                             n_seqs, h0, o, hT, &p);
   if (st != GDN_SUCCESS) return st;
+  if (!aligned16(alpha)) return GDN_ERROR_INVALID_VALUE;
   if (chunk != 16 && chunk != 32 && chunk != 64) return GDN_ERROR_NOT_SUPPORTED;
   p.chunk = chunk;
   p.per_channel = 1;

@@ -81,23 +81,26 @@ __global__ __launch_bounds__(512) void kda_prep_kernel(KdaArgs<T> a) {
   const float *ab = a.alpha + (int64_t(tok0) * a.H_v + h) * dk;
   const int64_t a_stride = int64_t(a.H_v) * dk;
 
-  // ---- rows of k, q and the clamped log2 rates (zero past the chunk's end) ----
-  for (int idx = tid; idx < 64 * dk; idx += 512) {
-    const int t = idx / dk, ch = idx - t * dk;
+  // ---- rows of k, q and the clamped log2 rates (zero past the chunk's end),
+  // four channels per load ----
+  for (int idx = tid; idx < 16 * dk; idx += 512) {
+    const int t = idx / (dk / 4), ch = 4 * (idx - t * (dk / 4));
     const bool in = t < len;
-    sK[t * kKRow + ch] = in ? to_f32(kb[int64_t(t) * qk_stride + ch]) : 0.0f;
-    sQ[t * kKRow + ch] = in ? to_f32(qb[int64_t(t) * qk_stride + ch]) : 0.0f;
-    sG[t * kKRow + ch] = in ? clamped_log2(ab[int64_t(t) * a_stride + ch]) : 0.0f;
+    const float4 kv = in ? load4_f32(kb + int64_t(t) * qk_stride + ch) : make_float4(0.f, 0.f, 0.f, 0.f);
+    const float4 qv = in ? load4_f32(qb + int64_t(t) * qk_stride + ch) : make_float4(0.f, 0.f, 0.f, 0.f);
+    const float4 av = in ? *reinterpret_cast<const float4 *>(ab + int64_t(t) * a_stride + ch)
+                         : make_float4(1.f, 1.f, 1.f, 1.f);
+    float *pk = sK + t * kKRow + ch, *pq = sQ + t * kKRow + ch, *pg = sG + t * kKRow + ch;
+    pk[0] = kv.x; pk[1] = kv.y; pk[2] = kv.z; pk[3] = kv.w;
+    pq[0] = qv.x; pq[1] = qv.y; pq[2] = qv.z; pq[3] = qv.w;
+    pg[0] = clamped_log2(av.x); pg[1] = clamped_log2(av.y); pg[2] = clamped_log2(av.z); pg[3] = clamped_log2(av.w);
   }
   if (tid < 64) sb[tid] = tid < len ? a.beta[int64_t(tok0 + tid) * a.H_v + h] : 0.0f;
   lds_barrier();
-  // ---- chunk-local cumulative log gate, one thread per channel ----
-  if (tid < dk) {
-    float g = 0.0f;
-    for (int t = 0; t < 64; ++t) {
-      g += sG[t * kKRow + tid];
-      sG[t * kKRow + tid] = g;
-    }
+  // ---- chunk-local cumulative log gate: a wave per channel, lane = token ----
+  for (int ch = wave; ch < dk; ch += 8) {
+    float *pg = sG + lane * kKRow + ch;
+    *pg = wave_prefix_sum(*pg);
   }
   lds_barrier();
 
@@ -135,28 +138,78 @@ __global__ __launch_bounds__(512) void kda_prep_kernel(KdaArgs<T> a) {
   }
   if (tid < 128) gamma_C[tid] = tid < dk ? fast_exp2(sG[63 * kKRow + tid]) : 0.0f;
 
-  // ---- A and P: for every pair i <= t, one exponent per channel serves both
-  // sums.  Thread pairs: 2080 lower-triangle entries (i <= t) over 512 threads.
-  // A is kept in LDS for the inverse; P leaves as A-operand fragments (row t,
-  // contraction i), element (t, i) at fragment (t / 16) * 2 + i / 32, lane
-  // 16 * ((i mod 32 mod 16) / 4) + t mod 16, element 4 * ((i mod 32) / 16) + i mod 4.
+  // ---- A and P ----
+  // When every cumulative log gate of the chunk lies within [-60, 60], the
+  // exponent of the channel sums factors without overflow:
+  // 2^(G_tc - G_ic) = 2^(G_tc) 2^(-G_ic), both factors in [2^-60, 2^60], so
+  //   A_ti = beta_t (Khat Kinv^T)_ti,  P_ti = (Qhat Kinv^T)_ti,
+  // Khat = 2^G . k, Qhat = 2^G . q, Kinv = 2^-G . k, each a 64 x 64 x d_k
+  // product (fp32 MFMA, the lower tiles only).  Otherwise (a chunk that decays
+  // by more than 2^60, e.g. through alpha = 0) every pair i <= t is summed
+  // with one exact exponent per channel.
   T *fragP = frag + kKdaFragP * kFragElems;
-  for (int p = tid; p < 64 * 64; p += 512) {
-    const int t = p >> 6, i = p & 63;
-    float acc_a = 0.0f, acc_p = 0.0f;
-    if (i <= t) {
-      const float *gt = sG + t * kKRow, *gi = sG + i * kKRow;
-      const float *kt = sK + t * kKRow, *ki = sK + i * kKRow, *qt = sQ + t * kKRow;
-      for (int ch = 0; ch < dk; ++ch) {
-        const float e = fast_exp2(gt[ch] - gi[ch]) * ki[ch];
-        acc_a += kt[ch] * e;
-        acc_p += qt[ch] * e;
-      }
-    }
-    sA[t][i] = i < t ? sb[t] * acc_a : 0.0f;
+  auto put_p = [&](int t, int i, float x) {
     const int ii = i & 31, kk = i >> 5;
     const int ln = 16 * ((ii & 15) >> 2) + (t & 15), el = 4 * (ii >> 4) + (ii & 3);
-    fragP[((t >> 4) * 2 + kk) * kFragElems + 8 * ln + el] = from_f32<T>(acc_p);
+    fragP[((t >> 4) * 2 + kk) * kFragElems + 8 * ln + el] = from_f32<T>(x);
+  };
+  bool far = false;
+  for (int idx = tid; idx < 64 * dk; idx += 512) {
+    const int t = idx / dk, ch = idx - t * dk;
+    far |= fabsf(sG[t * kKRow + ch]) > 60.0f;
+  }
+  lds_barrier();  // every fragment above has read sK, sQ and sG
+  if (!__syncthreads_or(far)) {
+    // scale in place: sK <- 2^G k, sQ <- 2^G q, sG <- 2^-G k
+    for (int idx = tid; idx < 64 * dk; idx += 512) {
+      const int t = idx / dk, ch = idx - t * dk;
+      const int o = t * kKRow + ch;
+      const float gg = sG[o], kv = sK[o];
+      sK[o] = fast_exp2(gg) * kv;
+      sQ[o] = fast_exp2(gg) * sQ[o];
+      sG[o] = fast_exp2(-gg) * kv;
+    }
+    lds_barrier();
+    // 20 tile products (the 10 lower 16 x 16 tiles of A and of P) over the 8 waves
+    const int r0 = lane & 15, kq = lane >> 4;
+    for (int job = wave; job < 20; job += 8) {
+      const bool isP = job >= 10;
+      int idx = isP ? job - 10 : job, rt = 0;
+      while (idx > rt) { idx -= rt + 1; ++rt; }
+      const int ct = idx;  // tile (rt, ct), ct <= rt
+      const float *arow = (isP ? sQ : sK) + (16 * rt + r0) * kKRow + kq;
+      const float *brow = sG + (16 * ct + r0) * kKRow + kq;
+      f32x4_t acc = zero4();
+      for (int c4 = 0; c4 < dk; c4 += 4) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(arow[c4], brow[c4], acc, 0, 0, 0);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int t = 16 * rt + 4 * kq + e, i = 16 * ct + r0;
+        if (isP) put_p(t, i, i <= t ? acc[e] : 0.0f);
+        else sA[t][i] = i < t ? sb[t] * acc[e] : 0.0f;
+      }
+    }
+    // the upper tiles of P's fragments are zero
+    for (int idx = tid; idx < 6 * 256; idx += 512) {
+      const int tile = idx >> 8, e = idx & 255;
+      const int rt = tile < 3 ? 0 : (tile < 5 ? 1 : 2), ct = tile < 3 ? tile + 1 : (tile < 5 ? tile - 1 : 3);
+      put_p(16 * rt + (e >> 4), 16 * ct + (e & 15), 0.0f);
+    }
+  } else {
+    for (int p = tid; p < 64 * 64; p += 512) {
+      const int t = p >> 6, i = p & 63;
+      float acc_a = 0.0f, acc_p = 0.0f;
+      if (i <= t) {
+        const float *gt = sG + t * kKRow, *gi = sG + i * kKRow;
+        const float *kt = sK + t * kKRow, *ki = sK + i * kKRow, *qt = sQ + t * kKRow;
+        for (int ch = 0; ch < dk; ++ch) {
+          const float e = fast_exp2(gt[ch] - gi[ch]) * ki[ch];
+          acc_a += kt[ch] * e;
+          acc_p += qt[ch] * e;
+        }
+      }
+      sA[t][i] = i < t ? sb[t] * acc_a : 0.0f;
+      put_p(t, i, acc_p);
+    }
   }
   lds_barrier();  // sK and sQ are dead: the inverse's blocks reuse them
 

@@ -281,8 +281,11 @@ int32_t gdn_kda_recurrent_fwd(int32_t B, int32_t T, int32_t H_qk, int32_t H_v, i
  *   A_ti = beta_t sum_c k_tc k_ic e^(G_tc - G_ic) (i < t),  T = (I + A)^-1 diag(beta),
  *   U = T (V - (e^G . K) S),  O = (e^G . Q) S + P U,  P_ti = sum_c q_tc k_ic e^(G_tc - G_ic) (i <= t),
  *   S <- diag(e^(G_C)) S + (e^(G_C - G) . K)^T U.
- * Every factor is e to a non-positive power; the channel sums of A and P
- * take their per-channel factors exactly in fp32.
+ * Every factor of the state side is e to a non-positive power.  The channel
+ * sums of A and P are evaluated in fp32: as (e^G . K)(e^-G . K)^T and
+ * (e^G . Q)(e^-G . K)^T on matrix cores when every cumulative log2 gate of
+ * the chunk lies within [-60, 60] (no factor leaves [2^-60, 2^60]), else
+ * pair by pair with the exact factor e^(G_tc - G_ic).
  *
  * Arguments as gdn_kda_recurrent_fwd (alpha [B, T, H_v, d_k] float32,
  * 16-byte aligned), plus chunk (16, 32 or 64) and a caller-provided

@@ -236,6 +236,9 @@ def test_kda_chunk_workspace(lib):
     assert lib.gdn_kda_chunk_fwd(*args, 48, p, 1 << 30, None) == 2
     assert lib.gdn_kda_chunk_fwd(*args, 64, None, 1 << 30, None) == 3
     assert lib.gdn_kda_chunk_fwd(*args, 64, p, 64, None) == 3
+    misaligned = list(args)
+    misaligned[10] = ctypes.c_void_p(0x1004)                    # alpha (read 16 bytes at a time)
+    assert lib.gdn_kda_chunk_fwd(*misaligned, 64, p, 1 << 30, None) == 1
 
 
 def test_noalloc_argument_errors(lib):

@@ -181,3 +181,26 @@ def test_kda_chunk_prefill_shape(gdn):
     eo, eh = kda_unit_errors(host_f64(o), host_f64(hT), ro, rh, w.seq_slices())
     log(f"    max rel err o={eo:.3e} hT={eh:.3e}")
     assert eo <= TOL["bf16"] and eh <= TOL["bf16"]
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_kda_chunk_strong_decay_and_zero_rates(gdn, dtype):
+    """Chunks whose per-channel cumulative decay leaves [2^-60, 2^60] (rates
+    down to 0, some exactly 0) take the exact per-pair path of the chunked
+    form; the others the factored one.  Both against the float64 oracle."""
+    import torch
+    B, T, H_qk, H_v, d_k, d_v = 1, 260, 1, 2, 64, 32
+    w = gi.generate(gi.Spec("kda-decay", B=B, T=T, H_qk=H_qk, H_v=H_v, d_k=d_k, d_v=d_v, dtype=dtype,
+                            chunk=64, seed=560))
+    a = gi.channel_rates(B, T, H_v, d_k, 561)           # head 0: rates in [0.8, 1)
+    a[:, :, 1] = gi.channel_rates(B, T, 1, d_k, 562, lo=0.0)[:, :, 0]  # head 1: rates in [0, 1)
+    a[:, 100:103, 1, :5] = 0.0                           # some rates exactly 0
+    a[:, 200, 0, 7] = 0.0                                # one zero in an otherwise slow-decay head
+    args = [dev_tensor(x) for x in (w.q, w.k, w.v)] + [dev_tensor(a), dev_tensor(w.beta)]
+    log(f"[kda chunk strong decay] {dtype}")
+    o, hT = gdn.kda_chunk_fwd(*args, chunk=64)
+    torch.cuda.synchronize()
+    ro, rh = kda.forward(w.q, w.k, w.v, a, w.beta)
+    eo, eh = kda_unit_errors(host_f64(o), host_f64(hT), ro, rh, w.seq_slices())
+    log(f"    max rel err o={eo:.3e} hT={eh:.3e}")
+    assert np.all(np.isfinite(host_f64(o))) and eo <= TOL[dtype] and eh <= TOL[dtype]
