@@ -244,30 +244,28 @@ int32_t run_chunk_fwd(Problem p, int32_t seg_chunks, void *workspace, size_t wor
   return status_of(e);
 }
 
-// Workspace of the backward pass: chunk offsets, the chunk-start states, the
-// per-value-head dq and dk, and each unit's fp32 intermediates.
+// Workspace of the backward pass: chunk offsets, one entry of fp32
+// intermediates per (chunk slot, value head), and under grouped heads the
+// per-value-head dq and dk.
 size_t bwd_workspace_layout(const Problem &p, void *base, BwdProblem *b) {
   const int64_t tokens = p.n_tokens();
   const size_t off_bytes = align256(size_t(2 * int64_t(p.n_seqs) + 1) * sizeof(int32_t));
-  const size_t st_bytes = align256(size_t(chunk_slots(p)) * p.H_v * p.d_k * p.d_v * sizeof(float));
-  const size_t part_bytes = align256(size_t(tokens) * p.H_v * p.d_k * sizeof(float));
-  const size_t scr_bytes =
-      align256(size_t(p.n_seqs) * p.H_v * bwd_unit_floats(p.chunk, p.d_k, p.d_v) * sizeof(float));
+  const size_t ent_bytes =
+      align256(size_t(chunk_slots(p)) * p.H_v * bwd_entry_floats(p.chunk, p.d_k, p.d_v) * sizeof(float));
+  const size_t part_bytes = p.H_v > p.H_qk ? align256(size_t(tokens) * p.H_v * p.d_k * sizeof(float)) : 0;
   if (b) {
     char *c = static_cast<char *>(base);
     b->ws.chunk_off = reinterpret_cast<int32_t *>(c);
     b->ws.seq_order = b->ws.chunk_off + p.n_seqs + 1;
     b->ws.entries = nullptr;
     c += off_bytes;
-    b->states = reinterpret_cast<float *>(c);
-    c += st_bytes;
-    b->dq_part = reinterpret_cast<float *>(c);
+    b->entries = reinterpret_cast<float *>(c);
+    c += ent_bytes;
+    b->dq_part = part_bytes ? reinterpret_cast<float *>(c) : nullptr;
     c += part_bytes;
-    b->dk_part = reinterpret_cast<float *>(c);
-    c += part_bytes;
-    b->scratch = reinterpret_cast<float *>(c);
+    b->dk_part = part_bytes ? reinterpret_cast<float *>(c) : nullptr;
   }
-  return off_bytes + st_bytes + 2 * part_bytes + scr_bytes;
+  return off_bytes + ent_bytes + 2 * part_bytes;
 }
 
 }  // namespace gdn
@@ -391,7 +389,6 @@ int32_t gdn_chunk_bwd(int32_t B, int32_t T, int32_t H_qk, int32_t H_v, int32_t d
   b.dh0 = dh0;
   hipStream_t s = static_cast<hipStream_t>(stream);
   hipError_t e = launch_chunk_offsets(p, b.ws, s);
-  if (e == hipSuccess) e = launch_recurrent_states(p, b.ws, b.states, s);
   if (e == hipSuccess) e = launch_chunk_bwd(b, s);
   return status_of(e);
 }

@@ -27,346 +27,913 @@
 //            dg_n += gamma_C <S, dS'> + sum_t s_t ds_t,
 //            d alpha_i = (sum_{t >= i} dg_t) / alpha_i.
 //
-// (dA uses M^T dU (diag(beta) X)^T M^T = dY (T X)^T = dY U^T.)
+// (dA uses M^T dU (diag(beta) X)^T M^T = dY (T X)^T = dY U^T.)  The row sums
+// over d_v are taken through d_k-sized products that the gradients need
+// anyway: sum_c dO_tc (Q S)_tc = sum_k Q_tk (dO S^T)_tk, and likewise for
+// dX . K S (through dY S^T) and K dS' . U (through U dS'^T).
 //
-// Kernels: the token-by-token forward writes every chunk's start state
-// (recurrent.hip, states mode); then one workgroup per (sequence, value head)
-// walks that unit's chunks in reverse, carrying dS, with every intermediate
-// of a chunk in fp32 in the unit's own slice of the workspace; then the
-// gradients of each query/key head are summed over the value heads that read
-// it.  All arithmetic is fp32; the products are workgroup-cooperative loops
-// over LDS (the C x C matrices) and the workspace (each output element owned
-// by one thread, so the results are the same run to run).  This is the first, correctness-first GPU backward: its
-// reverse chain has the forward scan's shape, and moving its products onto
-// MFMA with LDS-staged operands is the next step.
+// Only the two state recurrences are sequential: S forward and dS backward.
+// Everything else is independent per chunk.  Three launches:
+//   1. bwd_factor_kernel, one block per (chunk, value head): gates, M by a
+//      blocked triangular inverse, P and Gamma . K K^T, into the chunk's entry.
+//   2. bwd_chain_kernel: per (unit, column block of d_v) one block walks the
+//      chunks forward keeping S (writing each chunk's start state, X and U)
+//      and another walks them backward keeping dS (writing each chunk's end
+//      gradient, dY and dv).  The state sits in MFMA accumulators, and the
+//      next chunk's operands are loaded while the current one is computed.
+//   3. bwd_grad_kernel, one block per (chunk, value head): the products over
+//      d_v (dO S^T, dY S^T, U dS'^T, dO U^T, dY U^T), then dq, dk, dbeta and
+//      dalpha.
+// Under grouped heads a last pass sums dq and dk over the value heads that
+// read each query/key head.  Every product runs on fp32 MFMA
+// (v_mfma_f32_16x16x4f32), and every sum has a fixed order, so results repeat
+// bit for bit from run to run.
 #include "launch.hpp"
+#include "stage.hpp"
 
 namespace gdn {
 
 namespace {
 
-constexpr int kBwdThreads = 512;
+// Floats of one entry (one chunk of one value head) in the workspace.
+struct BwdEntry {
+  int64_t M, P, G, gate, S, dS, X, U, dY, total;
+  __host__ __device__ BwdEntry(int C, int DK, int DV) {
+    int64_t o = 0;
+    M = o;    o += int64_t(C) * C;    // (I + A)^-1, row-major C x C
+    P = o;    o += int64_t(C) * C;    // lower(Gamma . Q K^T)
+    G = o;    o += int64_t(C) * C;    // strict_lower(Gamma . K K^T)
+    gate = o; o += 256;               // gamma_t, s_t, log2 cumulative gate, beta_t (64 each)
+    S = o;    o += int64_t(DK) * DV;  // state entering the chunk
+    dS = o;   o += int64_t(DK) * DV;  // gradient reaching the chunk's end state
+    X = o;    o += int64_t(C) * DV;   // V - diag(gamma) K S
+    U = o;    o += int64_t(C) * DV;   // T X
+    dY = o;   o += int64_t(C) * DV;   // M^T dU
+    total = o;
+  }
+};
+constexpr int kGateGamma = 0, kGateS = 64, kGateLog2 = 128, kGateBeta = 192;
 
 template <typename T>
 struct BwdArgs {
   const T *q, *k, *v, *d_o;
-  const float *alpha, *beta, *dhT;
-  const float *states;      // [slots, H_v, d_k, d_v] chunk-start states
-  float *dq_part, *dk_part; // [tokens, H_v, d_k]
+  const float *alpha, *beta, *h0, *dhT;
+  float *ent;             // [n_slots * H_v] entries of ent_floats
+  int64_t ent_floats;
+  float *dq, *dk;         // [tokens, H_v, d_k]: the gradients themselves when every
+                          // query/key head has one value head, else per-value-head parts
   float *dv, *dalpha, *dbeta, *dh0;
-  float *scratch;
-  int64_t unit_floats;
   int H_qk, H_v, d_k, d_v, group, n_units;
   SeqGeom geo;
 };
 
-// Per-unit scratch layout in global memory, in floats, for chunk C and sizes
-// DK, DV (the chunk's C x C matrices live in LDS).
-struct BwdLayout {
-  int64_t K, Q, V, dO, be, al, gg, ga, sc, dg, KS, QS, X, U, KdS, dU, dY, dX, dS0, dS1, dQ, dK, total;
-  __host__ __device__ BwdLayout(int C, int DK, int DV) {
-    int64_t o = 0;
-    auto take = [&](int64_t n) { const int64_t r = o; o += (n + 63) & ~int64_t(63); return r; };
-    K = take(int64_t(C) * DK); Q = take(int64_t(C) * DK); V = take(int64_t(C) * DV); dO = take(int64_t(C) * DV);
-    be = take(C); al = take(C); gg = take(C); ga = take(C); sc = take(C); dg = take(C);
-    KS = take(int64_t(C) * DV); QS = take(int64_t(C) * DV); X = take(int64_t(C) * DV); U = take(int64_t(C) * DV);
-    KdS = take(int64_t(C) * DV); dU = take(int64_t(C) * DV); dY = take(int64_t(C) * DV); dX = take(int64_t(C) * DV);
-    dS0 = take(int64_t(DK) * DV); dS1 = take(int64_t(DK) * DV);
-    dQ = take(int64_t(C) * DK); dK = take(int64_t(C) * DK);
-    total = o;
-  }
-};
-
-// Four k steps of a thread's 1 x 4 output strip: A(i, k..k+3) and
-// B(k..k+3, j0..j0+3), as 16-byte loads where the operand is contiguous
-// along that index (every array here is 16-byte aligned, with row strides
-// that are multiples of four floats).
-template <bool A_ROW, bool B_ROW>
-__device__ __forceinline__ void strip_step(const float *a, int acs, const float *b, int brs, int bcs, int kk,
-                                           const float *ks, float (&sum)[4]) {
-  float av[4], bv[4][4];
-  if constexpr (A_ROW) {
-    const float4 x = *reinterpret_cast<const float4 *>(a + kk);
-    av[0] = x.x; av[1] = x.y; av[2] = x.z; av[3] = x.w;
-  } else {
-#pragma unroll
-    for (int u = 0; u < 4; ++u) av[u] = a[int64_t(kk + u) * acs];
-  }
-  if (ks) {
-#pragma unroll
-    for (int u = 0; u < 4; ++u) av[u] *= ks[kk + u];
-  }
-#pragma unroll
-  for (int u = 0; u < 4; ++u) {
-    if constexpr (B_ROW) {
-      const float4 y = *reinterpret_cast<const float4 *>(b + int64_t(kk + u) * brs);
-      bv[u][0] = y.x; bv[u][1] = y.y; bv[u][2] = y.z; bv[u][3] = y.w;
-    } else {
-#pragma unroll
-      for (int jj = 0; jj < 4; ++jj) bv[u][jj] = b[int64_t(kk + u) * brs + int64_t(jj) * bcs];
-    }
-  }
-#pragma unroll
-  for (int u = 0; u < 4; ++u)
-#pragma unroll
-    for (int jj = 0; jj < 4; ++jj) sum[jj] += av[u] * bv[u][jj];
+// ---- 16 x 16 fp32 MFMA tiles ----------------------------------------------
+// Lane roles: r = lane & 15, g = lane >> 4.  An accumulator holds D[4g + e][r]
+// (e = 0..3); mm16(xr, yt, acc) adds X Y over a 16-deep slice with
+// xr = X[r][4g .. 4g + 3] and yt = Y[4g .. 4g + 3][r], so an accumulator is
+// itself a valid yt for the next product.
+template <typename P> __device__ __forceinline__ f32x4_t row4(const P *p) {
+  const float4 x = load4_f32(p);
+  return f32x4_t{x.x, x.y, x.z, x.w};
+}
+template <typename P> __device__ __forceinline__ f32x4_t col4(const P *p, int ld) {
+  return f32x4_t{to_f32(p[0]), to_f32(p[ld]), to_f32(p[2 * ld]), to_f32(p[3 * ld])};
 }
 
-template <bool A_ROW, bool B_ROW>
-__device__ void wg_gemm_t(float *C, int ldc, const float *A, int ars, int acs, const float *B, int brs, int bcs,
-                          int m, int n, int K, float alpha, const float *rs, const float *ks, bool acc) {
-  const int nb = (n + 3) >> 2;
-  for (int idx = threadIdx.x; idx < m * nb; idx += kBwdThreads) {
-    const int i = idx / nb, j0 = 4 * (idx - i * nb);
-    const int nj = min(4, n - j0);
-    const float *a = A + int64_t(i) * ars;
-    const float *b = B + int64_t(j0) * bcs;
-    float sum[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-    int kk = 0;
-    if (nj == 4)
-      for (; kk + 4 <= K; kk += 4) strip_step<A_ROW, B_ROW>(a, acs, b, brs, bcs, kk, ks, sum);
-    for (; kk < K; ++kk) {
-      const float x = a[int64_t(kk) * acs] * (ks ? ks[kk] : 1.0f);
-      for (int jj = 0; jj < nj; ++jj) sum[jj] += x * b[int64_t(kk) * brs + int64_t(jj) * bcs];
-    }
-    const float scale = alpha * (rs ? rs[i] : 1.0f);
-    float *c = C + int64_t(i) * ldc + j0;
-    for (int jj = 0; jj < nj; ++jj) c[jj] = acc ? c[jj] + scale * sum[jj] : scale * sum[jj];
-  }
+// Sum of x over aligned groups of w lanes (w a power of two <= 64), fixed order.
+__device__ __forceinline__ float group_sum(float x, int w) {
+  for (int o = 1; o < w; o <<= 1) x += __shfl_xor(x, o);
+  return x;
 }
 
-// C[i][j] = (acc ? C[i][j] : 0) + alpha rs[i] sum_{k<K} A(i, k) ks[k] B(k, j)
-// with A(i, k) = A[i ars + k acs], B(k, j) = B[k brs + j bcs] (rs, ks: 1 when
-// null).  A thread owns four adjacent outputs of a row and walks k four steps
-// at a time; the operands may sit in LDS or in global memory.  Every output
-// is summed in k order by one thread, so the result does not depend on the
-// launch.
-__device__ void wg_gemm(float *C, int ldc, const float *A, int ars, int acs, const float *B, int brs, int bcs,
-                        int m, int n, int K, float alpha = 1.0f, const float *rs = nullptr,
-                        const float *ks = nullptr, bool acc = false) {
-  if (acs == 1 && bcs == 1)
-    wg_gemm_t<true, true>(C, ldc, A, ars, acs, B, brs, bcs, m, n, K, alpha, rs, ks, acc);
-  else if (acs == 1)
-    wg_gemm_t<true, false>(C, ldc, A, ars, acs, B, brs, bcs, m, n, K, alpha, rs, ks, acc);
-  else if (bcs == 1)
-    wg_gemm_t<false, true>(C, ldc, A, ars, acs, B, brs, bcs, m, n, K, alpha, rs, ks, acc);
-  else
-    wg_gemm_t<false, false>(C, ldc, A, ars, acs, B, brs, bcs, m, n, K, alpha, rs, ks, acc);
-}
-
-// Sum over the block of one value per thread (red: kBwdThreads floats of LDS).
-__device__ float wg_sum(float x, float *red) {
-  red[threadIdx.x] = x;
-  __syncthreads();
-  for (int s = kBwdThreads / 2; s > 0; s >>= 1) {
-    if (int(threadIdx.x) < s) red[threadIdx.x] += red[threadIdx.x + s];
-    __syncthreads();
+// The k-th lower 16 x 16 tile (row tile >= column tile), row by row.
+__device__ __forceinline__ void lower_tile(int k, int &rt, int &ct) {
+  rt = 0;
+  while (k > rt) {
+    k -= rt + 1;
+    ++rt;
   }
-  const float r = red[0];
-  __syncthreads();
-  return r;
+  ct = k;
 }
 
 }  // namespace
 
-template <typename T>
-__global__ __launch_bounds__(kBwdThreads) void chunk_bwd_kernel(BwdArgs<T> a) {
-  const int u = blockIdx.x;
-  if (u >= a.n_units) return;
-  const int tid = threadIdx.x;
-  const int s = u / a.H_v, h = u - s * a.H_v, hq = h / a.group;
-  const int C = a.geo.chunk, DK = a.d_k, DV = a.d_v;
-  const BwdLayout L(C, DK, DV);
-  float *w = a.scratch + int64_t(u) * a.unit_floats;
-  float *Kc = w + L.K, *Qc = w + L.Q, *Vc = w + L.V, *dOc = w + L.dO;
-  float *be = w + L.be, *al = w + L.al, *gg = w + L.gg, *ga = w + L.ga, *sc = w + L.sc, *dg = w + L.dg;
-  // the chunk's C x C matrices (C <= 64): Gamma, K K^T, Q K^T, M, T, P, dP, dA
-  __shared__ __attribute__((aligned(16))) float cc[8][64 * 64];
-  float *Gm = cc[0], *KK = cc[1], *QK = cc[2], *Mi = cc[3], *Tm = cc[4], *Pm = cc[5], *dP = cc[6], *dA = cc[7];
-  float *KS = w + L.KS, *QS = w + L.QS, *X = w + L.X, *U = w + L.U, *KdS = w + L.KdS, *dU = w + L.dU;
-  float *dY = w + L.dY, *dX = w + L.dX, *dS = w + L.dS0, *dSn = w + L.dS1, *dQ = w + L.dQ, *dK = w + L.dK;
-  __shared__ float red[kBwdThreads];
+// ---------------------------------------------------------------------------
+// 1. Per (chunk, value head): gates, M = (I + A)^-1, P, Gamma . K K^T.
+// ---------------------------------------------------------------------------
+template <typename T, int C>
+__global__ __launch_bounds__(256) void bwd_factor_kernel(BwdArgs<T> a) {
+  constexpr int NB = C / 16, LD = C + 4, NL = NB * (NB + 1) / 2;
+  const int e = blockIdx.x;
+  const int slot = e / a.H_v, h = e - slot * a.H_v;
+  int s, tok0, n;
+  if (!a.geo.locate(slot, s, tok0, n)) return;
+  const int hq = h / a.group, DK = a.d_k;
+  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, r = lane & 15, g = lane >> 4;
+  __shared__ __attribute__((aligned(16))) float sKK[C * LD], sQK[C * LD], sA[C * LD], sM[C * LD];
+  __shared__ float sg[64], sb[64];
+  float *ent = a.ent + int64_t(e) * a.ent_floats;
+  const BwdEntry L(C, DK, a.d_v);
 
-  const int64_t unit_state = (int64_t(s) * a.H_v + h) * DK * DV;
-  for (int idx = tid; idx < DK * DV; idx += kBwdThreads) dS[idx] = a.dhT ? a.dhT[unit_state + idx] : 0.0f;
-  __syncthreads();
-
-  int start, end;
-  a.geo.seq_bounds(s, start, end);
-  const int n_chunks = (end - start + C - 1) / C;
-  const int c_first = a.geo.first_chunk(s);
-  for (int cc = n_chunks - 1; cc >= 0; --cc) {
-    const int slot = c_first + cc;
-    if (slot >= a.geo.n_slots) continue;  // (never for a well-formed batch)
-    const int tok0 = start + cc * C;
-    const int n = min(C, end - tok0);
-    const float *S = a.states + (int64_t(slot) * a.H_v + h) * DK * DV;
-
-    // ---- the chunk's operands in fp32 ----
-    for (int idx = tid; idx < n * DK; idx += kBwdThreads) {
-      const int t = idx / DK, c = idx - t * DK;
-      const int64_t g = (int64_t(tok0 + t) * a.H_qk + hq) * DK + c;
-      Kc[idx] = to_f32(a.k[g]);
-      Qc[idx] = to_f32(a.q[g]);
+  if (w == 0) {  // chunk-local cumulative log2 gate; padded slots add 0
+    const bool in = lane < n;
+    const int64_t gi = int64_t(tok0 + min(lane, n - 1)) * a.H_v + h;
+    const float g2 = wave_prefix_sum(in ? clamped_log2(a.alpha[gi]) : 0.0f);
+    if (lane < C) {
+      sg[lane] = g2;
+      sb[lane] = in ? a.beta[gi] : 0.0f;
     }
-    for (int idx = tid; idx < n * DV; idx += kBwdThreads) {
-      const int t = idx / DV, c = idx - t * DV;
-      const int64_t g = (int64_t(tok0 + t) * a.H_v + h) * DV + c;
-      Vc[idx] = to_f32(a.v[g]);
-      dOc[idx] = to_f32(a.d_o[g]);
-    }
-    if (tid < n) {
-      const int64_t g = int64_t(tok0 + tid) * a.H_v + h;
-      be[tid] = a.beta[g];
-      al[tid] = a.alpha[g];
-    }
-    __syncthreads();
-    // chunk-local cumulative log gate (ln alpha clamped at -200, as in the
-    // forward: e^-200 is zero in fp32)
-    if (tid == 0) {
-      float g = 0.0f;
-      for (int t = 0; t < n; ++t) {
-        g += fmaxf(logf(al[t]), -200.0f);
-        gg[t] = g;
-      }
-    }
-    __syncthreads();
-    const float g_last = gg[n - 1];
-    const float gC = expf(g_last);
-    if (tid < n) {
-      ga[tid] = expf(gg[tid]);
-      sc[tid] = expf(g_last - gg[tid]);
-    }
-    for (int idx = tid; idx < n * C; idx += kBwdThreads) {
-      const int t = idx / C, i = idx - t * C;
-      Gm[idx] = i <= t && i < n ? expf(gg[t] - gg[i]) : 0.0f;
-    }
-    wg_gemm(KK, C, Kc, DK, 1, Kc, 1, DK, n, n, DK);  // K K^T
-    wg_gemm(QK, C, Qc, DK, 1, Kc, 1, DK, n, n, DK);  // Q K^T
-    __syncthreads();
-    // A (strictly lower) into dA's slot, then M = (I + A)^-1 by forward
-    // substitution, one thread per column
-    for (int idx = tid; idx < n * C; idx += kBwdThreads) {
-      const int t = idx / C, i = idx - t * C;
-      dA[idx] = i < t ? be[t] * Gm[idx] * KK[t * C + i] : 0.0f;
-    }
-    __syncthreads();
-    if (tid < n) {
-      const int j = tid;
-      for (int t = 0; t < n; ++t) {
-        float m = t == j ? 1.0f : 0.0f;
-        if (t > j) {
-          for (int i = j; i < t; ++i) m -= dA[t * C + i] * Mi[i * C + j];
-        }
-        Mi[t * C + j] = m;
-      }
-    }
-    __syncthreads();
-    for (int idx = tid; idx < n * C; idx += kBwdThreads) {
-      const int t = idx / C, i = idx - t * C;
-      Tm[idx] = i < n ? Mi[idx] * be[i] : 0.0f;
-      Pm[idx] = i <= t ? QK[idx] * Gm[idx] : 0.0f;
-    }
-    wg_gemm(KS, DV, Kc, DK, 1, S, DV, 1, n, DV, DK);    // K S
-    wg_gemm(QS, DV, Qc, DK, 1, S, DV, 1, n, DV, DK);    // Q S
-    wg_gemm(KdS, DV, Kc, DK, 1, dS, DV, 1, n, DV, DK);  // K dS'
-    __syncthreads();
-    for (int idx = tid; idx < n * DV; idx += kBwdThreads) X[idx] = Vc[idx] - ga[idx / DV] * KS[idx];
-    __syncthreads();
-    wg_gemm(U, DV, Tm, C, 1, X, DV, 1, n, DV, n);   // U = T X
-    wg_gemm(dU, DV, Pm, 1, C, dOc, DV, 1, n, DV, n);  // P^T dO
-    __syncthreads();
-    for (int idx = tid; idx < n * DV; idx += kBwdThreads) dU[idx] += sc[idx / DV] * KdS[idx];
-    __syncthreads();
-    wg_gemm(dY, DV, Mi, 1, C, dU, DV, 1, n, DV, n);  // M^T dU
-    __syncthreads();
-    for (int idx = tid; idx < n * DV; idx += kBwdThreads) {
-      const int t = idx / DV, c = idx - t * DV;
-      const float x = be[t] * dY[idx];
-      dX[idx] = x;
-      a.dv[(int64_t(tok0 + t) * a.H_v + h) * DV + c] = x;
-    }
-    __syncthreads();
-    // dS to the chunk before: gamma_C dS' + Q^T diag(gamma) dO - K^T diag(gamma) dX
-    wg_gemm(dSn, DV, Qc, 1, DK, dOc, DV, 1, DK, DV, n, 1.0f, nullptr, ga);
-    wg_gemm(dSn, DV, Kc, 1, DK, dX, DV, 1, DK, DV, n, -1.0f, nullptr, ga, true);
-    wg_gemm(dP, C, dOc, DV, 1, U, 1, DV, n, n, DV);          // dO U^T (masked below)
-    wg_gemm(dA, C, dY, DV, 1, U, 1, DV, n, n, DV, -1.0f);    // -dY U^T (masked below)
-    wg_gemm(dQ, DK, dOc, DV, 1, S, 1, DV, n, DK, DV, 1.0f, ga);  // diag(gamma) dO S^T
-    __syncthreads();
-    for (int idx = tid; idx < DK * DV; idx += kBwdThreads) dSn[idx] += gC * dS[idx];
-    for (int idx = tid; idx < n * C; idx += kBwdThreads) {
-      const int t = idx / C, i = idx - t * C;
-      const float p = i <= t ? dP[idx] : 0.0f;
-      const float d = i < t ? dA[idx] : 0.0f;
-      dP[idx] = p;
-      dA[idx] = d;
-      Pm[idx] = p * Gm[idx];           // dP . Gamma
-      Tm[idx] = d * be[t] * Gm[idx];   // dG
-    }
-    __syncthreads();
-    wg_gemm(dQ, DK, Pm, C, 1, Kc, DK, 1, n, DK, n, 1.0f, nullptr, nullptr, true);  // + (dP . Gamma) K
-    wg_gemm(dK, DK, Pm, 1, C, Qc, DK, 1, n, DK, n);                                 // (dP . Gamma)^T Q
-    __syncthreads();
-    wg_gemm(dK, DK, dX, DV, 1, S, 1, DV, n, DK, DV, -1.0f, ga, nullptr, true);      // - diag(gamma) dX S^T
-    __syncthreads();
-    wg_gemm(dK, DK, U, DV, 1, dS, 1, DV, n, DK, DV, 1.0f, sc, nullptr, true);       // + diag(s) U dS'^T
-    __syncthreads();
-    wg_gemm(dK, DK, Tm, C, 1, Kc, DK, 1, n, DK, n, 1.0f, nullptr, nullptr, true);   // + dG K
-    __syncthreads();
-    wg_gemm(dK, DK, Tm, 1, C, Kc, DK, 1, n, DK, n, 1.0f, nullptr, nullptr, true);   // + dG^T K
-    // Gamma . dGamma into Mi's slot (M is no longer needed)
-    for (int idx = tid; idx < n * C; idx += kBwdThreads) {
-      const int t = idx / C, i = idx - t * C;
-      Mi[idx] = i <= t ? Gm[idx] * (dA[idx] * be[t] * KK[idx] + dP[idx] * QK[idx]) : 0.0f;
-    }
-    __syncthreads();
-    // per-token sums: dbeta, dgamma, ds
-    float ds_t = 0.0f;
-    if (tid < n) {
-      const int t = tid;
-      float db = 0.0f, dgam = 0.0f, dss = 0.0f;
-      for (int c = 0; c < DV; ++c) {
-        db += dY[t * DV + c] * X[t * DV + c];
-        dgam += dOc[t * DV + c] * QS[t * DV + c] - dX[t * DV + c] * KS[t * DV + c];
-        dss += KdS[t * DV + c] * U[t * DV + c];
-      }
-      float row = 0.0f, col = 0.0f;
-      for (int i = 0; i < n; ++i) {
-        db += dA[t * C + i] * Gm[t * C + i] * KK[t * C + i];
-        row += Mi[t * C + i];
-        col += Mi[i * C + t];
-      }
-      a.dbeta[int64_t(tok0 + t) * a.H_v + h] = db;
-      dg[t] = ga[t] * dgam + row - col - sc[t] * dss;
-      ds_t = sc[t] * dss;
-    }
-    // gamma_C <S, dS'> + sum_t s_t ds_t joins the last slot's dg
-    float part = 0.0f;
-    for (int idx = tid; idx < DK * DV; idx += kBwdThreads) part += S[idx] * dS[idx];
-    const float sd = wg_sum(part, red);
-    const float sds = wg_sum(ds_t, red);
-    if (tid == 0) {
-      dg[n - 1] += gC * sd + sds;
-      float acc = 0.0f;
-      for (int t = n - 1; t >= 0; --t) {
-        acc += dg[t];
-        a.dalpha[int64_t(tok0 + t) * a.H_v + h] = acc / al[t];
-      }
-    }
-    for (int idx = tid; idx < n * DK; idx += kBwdThreads) {
-      const int t = idx / DK, c = idx - t * DK;
-      const int64_t g = (int64_t(tok0 + t) * a.H_v + h) * DK + c;
-      a.dq_part[g] = dQ[idx];
-      a.dk_part[g] = dK[idx];
-    }
-    __syncthreads();
-    float *tmp = dS;
-    dS = dSn;
-    dSn = tmp;
   }
-  if (a.dh0)
-    for (int idx = tid; idx < DK * DV; idx += kBwdThreads) a.dh0[unit_state + idx] = dS[idx];
+  for (int i = tid; i < C * LD; i += 256) sM[i] = 0.0f;
+  // lower tiles of K K^T and Q K^T (contraction over d_k), operands from global
+  for (int job = w; job < 2 * NL; job += 4) {
+    const int mat = job / NL;
+    int rt, ct;
+    lower_tile(job - mat * NL, rt, ct);
+    const int ta = 16 * rt + r, tb = 16 * ct + r;
+    const T *pa = (mat ? a.q : a.k) + (int64_t(tok0 + min(ta, n - 1)) * a.H_qk + hq) * DK + 4 * g;
+    const T *pb = a.k + (int64_t(tok0 + min(tb, n - 1)) * a.H_qk + hq) * DK + 4 * g;
+    f32x4_t acc = zero4();
+    for (int k0 = 0; k0 < DK; k0 += 16) {
+      const f32x4_t xr = ta < n ? row4(pa + k0) : zero4();
+      const f32x4_t yt = tb < n ? row4(pb + k0) : zero4();
+      acc = mm16(xr, yt, acc);
+    }
+    float *dst = mat ? sQK : sKK;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) dst[(16 * rt + 4 * g + q) * LD + 16 * ct + r] = acc[q];
+  }
+  __syncthreads();
+  for (int idx = tid; idx < C * C; idx += 256) {
+    const int t = idx / C, i = idx - t * C;
+    float gkk = 0.0f, p = 0.0f;
+    if (i <= t) {
+      const float gam = fast_exp2(sg[t] - sg[i]);
+      p = gam * sQK[t * LD + i];
+      if (i < t) gkk = gam * sKK[t * LD + i];
+    }
+    sA[t * LD + i] = sb[t] * gkk;
+    ent[L.P + idx] = p;
+    ent[L.G + idx] = gkk;
+  }
+  if (tid < C) {
+    const float gl = sg[C - 1];
+    ent[L.gate + kGateGamma + tid] = fast_exp2(sg[tid]);
+    ent[L.gate + kGateS + tid] = fast_exp2(gl - sg[tid]);
+    ent[L.gate + kGateLog2 + tid] = sg[tid];
+    ent[L.gate + kGateBeta + tid] = sb[tid];
+  }
+  __syncthreads();
+  // (I + A)^-1 by 16 x 16 blocks: the diagonal blocks by forward substitution
+  // (lane group g inverts block g, lane r owns column r) ...
+  if (w == 0 && g < NB) {
+    const int o = 16 * g;
+    float m[16];
+#pragma unroll
+    for (int t = 0; t < 16; ++t) {
+      float x = t == r ? 1.0f : 0.0f;
+#pragma unroll
+      for (int kk = 0; kk < t; ++kk) x -= sA[(o + t) * LD + o + kk] * m[kk];
+      m[t] = x;
+    }
+#pragma unroll
+    for (int t = 0; t < 16; ++t) sM[(o + t) * LD + o + r] = m[t];
+  }
+  __syncthreads();
+  // ... then the blocks d below the diagonal, one wave per block:
+  // M_ij = -M_ii sum_{j <= k < i} A_ik M_kj
+  for (int d = 1; d < NB; ++d) {
+    const int j = w, i = w + d;
+    if (i < NB) {
+      f32x4_t z = zero4();
+      for (int kb = j; kb < i; ++kb)
+        z = mm16(row4(&sA[(16 * i + r) * LD + 16 * kb + 4 * g]), col4(&sM[(16 * kb + 4 * g) * LD + 16 * j + r], LD),
+                 z);
+      const f32x4_t m = mm16(row4(&sM[(16 * i + r) * LD + 16 * i + 4 * g]), z, zero4());
+#pragma unroll
+      for (int q = 0; q < 4; ++q) sM[(16 * i + 4 * g + q) * LD + 16 * j + r] = -m[q];
+    }
+    __syncthreads();
+  }
+  for (int idx = tid; idx < C * C; idx += 256) {
+    const int t = idx / C, i = idx - t * C;
+    ent[L.M + idx] = sM[t * LD + i];
+  }
+}
+
+// ---------------------------------------------------------------------------
+// 2. The two chains.  Block = (unit, column block of CB = min(32, d_v)
+// columns, direction), 4 waves.  Tiles of a C x CB product: i = w + 4m, row
+// tile i % (C/16), column tile i / (C/16), so a wave keeps one row tile.
+// Tiles of the d_k x CB state: i = w + 4m, row tile i % (d_k/16), column tile
+// i / (d_k/16).
+// ---------------------------------------------------------------------------
+namespace {
+
+constexpr int kChainThreads = 256;
+
+template <typename T, int C> struct ChainLds {
+  static constexpr int LDK = 128 + 16 / sizeof(T);  // K / Q rows (elements of T), d_k <= 128
+  static constexpr int LDB = 32 + 4;                // column-block rows (floats)
+  static constexpr int kTile = C * LDK * sizeof(T);
+  static constexpr int kState = 128 * LDB * 4;
+  static constexpr int kCol = C * LDB * 4;
+  static constexpr int kGate = 3 * 64 * 4;
+  // forward: K, S, Y, diag(s) U, gates; backward: K, Q, dS, dO, dU, diag(gamma) dX, gates
+  static constexpr int kFwd = kTile + kState + 2 * kCol + kGate;
+  static constexpr int kRev = 2 * kTile + kState + 3 * kCol + kGate;
+  static constexpr int kBytes = kFwd > kRev ? kFwd : kRev;
+};
+
+// One chunk's token-row tile (K or Q: C rows x d_k of T) as 16-byte pieces in
+// registers, then in LDS.  Rows at or past n read as zero.
+template <typename T, int C> struct TileLoader {
+  static constexpr int EPP = 16 / sizeof(T);
+  static constexpr int MAXP = (C * 128 / EPP + kChainThreads - 1) / kChainThreads;
+  uint4 v[MAXP];
+  __device__ __forceinline__ void load(const T *base, int64_t row_stride, int n, int DK) {
+    const int ppr = DK / EPP, np = C * ppr;
+#pragma unroll
+    for (int m = 0; m < MAXP; ++m) {
+      const int p = threadIdx.x + kChainThreads * m;
+      v[m] = make_uint4(0, 0, 0, 0);
+      if (p < np) {
+        const int t = p / ppr, c = (p - t * ppr) * EPP;
+        if (t < n) v[m] = *reinterpret_cast<const uint4 *>(base + int64_t(t) * row_stride + c);
+      }
+    }
+  }
+  __device__ __forceinline__ void store(T *lds, int ldk, int DK) const {
+    const int ppr = DK / EPP, np = C * ppr;
+#pragma unroll
+    for (int m = 0; m < MAXP; ++m) {
+      const int p = threadIdx.x + kChainThreads * m;
+      if (p < np) {
+        const int t = p / ppr, c = (p - t * ppr) * EPP;
+        *reinterpret_cast<uint4 *>(lds + t * ldk + c) = v[m];
+      }
+    }
+  }
+};
+
+// One chunk's gamma, s and beta (thread t < C holds token t's).
+struct GateLoader {
+  float gam = 0.0f, sc = 0.0f, be = 0.0f;
+  __device__ __forceinline__ void load(const float *gate) {
+    const int t = threadIdx.x;
+    if (t < 64) {
+      gam = gate[kGateGamma + t];
+      sc = gate[kGateS + t];
+      be = gate[kGateBeta + t];
+    }
+  }
+  __device__ __forceinline__ void store(float *sgate, int C) const {
+    const int t = threadIdx.x;
+    if (t < C) {
+      sgate[t] = gam;
+      sgate[64 + t] = sc;
+      sgate[128 + t] = be;
+    }
+  }
+};
+
+// Unit u's sequence, value head, token range, first chunk slot and chunk count.
+__device__ __forceinline__ void unit_of(const SeqGeom &geo, int H_v, int u, int &s, int &h, int &start, int &end,
+                                        int &c_first, int &n_chunks) {
+  s = geo.ordered(u / H_v);
+  h = u - (u / H_v) * H_v;
+  geo.seq_bounds(s, start, end);
+  n_chunks = (end - start + geo.chunk - 1) / geo.chunk;
+  c_first = geo.first_chunk(s);
+  n_chunks = max(0, min(n_chunks, geo.n_slots - c_first));
+}
+
+template <typename T, int C>
+__device__ void fwd_chain(const BwdArgs<T> &a, int u, int cb, char *smem) {
+  using Lds = ChainLds<T, C>;
+  constexpr int NRT = C / 16, LDK = Lds::LDK, LDB = Lds::LDB;
+  const int DK = a.d_k, DV = a.d_v, CB = min(32, DV), c0 = cb * CB;
+  const int NKT = DK / 16, NCT = CB / 16;
+  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, r = lane & 15, g = lane >> 4;
+  T *sK = reinterpret_cast<T *>(smem);
+  float *sS = reinterpret_cast<float *>(smem + Lds::kTile);
+  float *sY = sS + 128 * LDB;
+  float *sU = sY + C * LDB;
+  float *sgate = sU + C * LDB;  // gamma[64], s[64], beta[64]
+  int s, h, start, end, c_first, n_chunks;
+  unit_of(a.geo, a.H_v, u, s, h, start, end, c_first, n_chunks);
+  const int hq = h / a.group;
+  const BwdEntry L(C, DK, DV);
+  const int64_t krow = int64_t(a.H_qk) * DK, vrow = int64_t(a.H_v) * DV;
+
+  // this wave's C x CB tiles (one row tile, up to two column tiles) and state tiles
+  const int rt = w % NRT;
+  const int nmine = (w < NRT * NCT) ? ((w + 4 < NRT * NCT) ? 2 : 1) : 0;
+  const int nst = NKT * NCT;
+  f32x4_t accS[4];
+#pragma unroll
+  for (int m = 0; m < 4; ++m) {
+    accS[m] = zero4();
+    const int i = w + 4 * m;
+    if (i < nst && a.h0) {
+      const int kt = i % NKT, ct = i / NKT;
+      const float *h0 = a.h0 + (int64_t(s) * a.H_v + h) * DK * DV;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) accS[m][q] = h0[int64_t(16 * kt + 4 * g + q) * DV + c0 + 16 * ct + r];
+    }
+  }
+  if (n_chunks == 0) return;
+
+  TileLoader<T, C> kl;
+  GateLoader gl;
+  f32x4_t vcur[2], mcur[NRT];
+  auto load_chunk = [&](int cc, f32x4_t(&vv)[2], f32x4_t(&mm)[NRT]) {
+    const int tok0 = start + cc * C, n = min(C, end - tok0);
+    const float *ent = a.ent + (int64_t(c_first + cc) * a.H_v + h) * a.ent_floats;
+    kl.load(a.k + int64_t(tok0) * krow + int64_t(hq) * DK, krow, n, DK);
+    gl.load(ent + L.gate);
+#pragma unroll
+    for (int m = 0; m < 2; ++m) {
+      vv[m] = zero4();
+      if (m < nmine) {
+        const int ct = (w + 4 * m) / NRT;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int t = 16 * rt + 4 * g + q;
+          if (t < n) vv[m][q] = to_f32(a.v[int64_t(tok0 + t) * vrow + int64_t(h) * DV + c0 + 16 * ct + r]);
+        }
+      }
+    }
+#pragma unroll
+    for (int kb = 0; kb < NRT; ++kb) mm[kb] = row4(ent + L.M + (16 * rt + r) * C + 16 * kb + 4 * g);
+  };
+  load_chunk(0, vcur, mcur);
+  kl.store(sK, LDK, DK);
+  gl.store(sgate, C);
+
+  for (int cc = 0; cc < n_chunks; ++cc) {
+    float *ent = a.ent + (int64_t(c_first + cc) * a.H_v + h) * a.ent_floats;
+    // the state entering this chunk: to LDS (operand of K S) and to the entry
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+      const int i = w + 4 * m;
+      if (i < nst) {
+        const int kt = i % NKT, ct = i / NKT;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int row = 16 * kt + 4 * g + q, col = 16 * ct + r;
+          sS[row * LDB + col] = accS[m][q];
+          ent[L.S + int64_t(row) * DV + c0 + col] = accS[m][q];
+        }
+      }
+    }
+    f32x4_t vnext[2], mnext[NRT];
+    const bool more = cc + 1 < n_chunks;
+    if (more) load_chunk(cc + 1, vnext, mnext);
+    __syncthreads();
+    // X = V - diag(gamma) K S;  Y = diag(beta) X
+#pragma unroll
+    for (int m = 0; m < 2; ++m) {
+      if (m < nmine) {
+        const int ct = (w + 4 * m) / NRT;
+        f32x4_t acc = zero4();
+        for (int k0 = 0; k0 < DK; k0 += 16)
+          acc = mm16(row4(sK + (16 * rt + r) * LDK + k0 + 4 * g), col4(sS + (k0 + 4 * g) * LDB + 16 * ct + r, LDB),
+                     acc);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int t = 16 * rt + 4 * g + q, col = 16 * ct + r;
+          const float x = vcur[m][q] - sgate[t] * acc[q];
+          ent[L.X + int64_t(t) * DV + c0 + col] = x;
+          sY[t * LDB + col] = sgate[128 + t] * x;
+        }
+      }
+    }
+    __syncthreads();
+    // U = M Y;  diag(s) U for the state update
+#pragma unroll
+    for (int m = 0; m < 2; ++m) {
+      if (m < nmine) {
+        const int ct = (w + 4 * m) / NRT;
+        f32x4_t acc = zero4();
+#pragma unroll
+        for (int kb = 0; kb < NRT; ++kb)
+          acc = mm16(mcur[kb], col4(sY + (16 * kb + 4 * g) * LDB + 16 * ct + r, LDB), acc);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int t = 16 * rt + 4 * g + q, col = 16 * ct + r;
+          ent[L.U + int64_t(t) * DV + c0 + col] = acc[q];
+          sU[t * LDB + col] = sgate[64 + t] * acc[q];
+        }
+      }
+    }
+    __syncthreads();
+    // S <- gamma_C S + K^T diag(s) U
+    const float gC = sgate[C - 1];
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+      const int i = w + 4 * m;
+      if (i < nst) {
+        const int kt = i % NKT, ct = i / NKT;
+        f32x4_t acc = accS[m] * gC;
+#pragma unroll
+        for (int kb = 0; kb < NRT; ++kb)
+          acc = mm16(col4(sK + (16 * kb + 4 * g) * LDK + 16 * kt + r, LDK),
+                     col4(sU + (16 * kb + 4 * g) * LDB + 16 * ct + r, LDB), acc);
+        accS[m] = acc;
+      }
+    }
+    __syncthreads();
+    if (more) {
+      kl.store(sK, LDK, DK);
+      gl.store(sgate, C);
+#pragma unroll
+      for (int m = 0; m < 2; ++m) vcur[m] = vnext[m];
+#pragma unroll
+      for (int kb = 0; kb < NRT; ++kb) mcur[kb] = mnext[kb];
+    }
+  }
+}
+
+template <typename T, int C>
+__device__ void rev_chain(const BwdArgs<T> &a, int u, int cb, char *smem) {
+  using Lds = ChainLds<T, C>;
+  constexpr int NRT = C / 16, LDK = Lds::LDK, LDB = Lds::LDB;
+  const int DK = a.d_k, DV = a.d_v, CB = min(32, DV), c0 = cb * CB;
+  const int NKT = DK / 16, NCT = CB / 16;
+  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, r = lane & 15, g = lane >> 4;
+  T *sK = reinterpret_cast<T *>(smem);
+  T *sQ = reinterpret_cast<T *>(smem + Lds::kTile);
+  float *sdS = reinterpret_cast<float *>(smem + 2 * Lds::kTile);
+  float *sdO = sdS + 128 * LDB;
+  float *sdU = sdO + C * LDB;
+  float *sdX = sdU + C * LDB;  // diag(gamma) dX
+  float *sgate = sdX + C * LDB;
+  int s, h, start, end, c_first, n_chunks;
+  unit_of(a.geo, a.H_v, u, s, h, start, end, c_first, n_chunks);
+  const int hq = h / a.group;
+  const BwdEntry L(C, DK, DV);
+  const int64_t krow = int64_t(a.H_qk) * DK, vrow = int64_t(a.H_v) * DV;
+  const int64_t unit_state = (int64_t(s) * a.H_v + h) * DK * DV;
+
+  const int rt = w % NRT;
+  const int nmine = (w < NRT * NCT) ? ((w + 4 < NRT * NCT) ? 2 : 1) : 0;
+  const int nst = NKT * NCT;
+  f32x4_t accS[4];
+#pragma unroll
+  for (int m = 0; m < 4; ++m) {
+    accS[m] = zero4();
+    const int i = w + 4 * m;
+    if (i < nst && a.dhT) {
+      const int kt = i % NKT, ct = i / NKT;
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        accS[m][q] = a.dhT[unit_state + int64_t(16 * kt + 4 * g + q) * DV + c0 + 16 * ct + r];
+    }
+  }
+
+  if (n_chunks > 0) {
+    TileLoader<T, C> kl, ql;
+    GateLoader gl;
+    // dO column block: C rows x CB columns of T in 16-byte pieces
+    constexpr int EPP = 16 / sizeof(T);
+    constexpr int MAXO = (C * 32 / EPP + kChainThreads - 1) / kChainThreads;
+    const int oppr = CB / EPP;
+    uint4 ocur[MAXO];
+    f32x4_t pcur[NRT], mcur[NRT];  // A fragments of P^T and M^T for this wave's row tile
+    auto load_chunk = [&](int cc, uint4(&oo)[MAXO], f32x4_t(&pp)[NRT], f32x4_t(&mm)[NRT]) {
+      const int tok0 = start + cc * C, n = min(C, end - tok0);
+      const float *ent = a.ent + (int64_t(c_first + cc) * a.H_v + h) * a.ent_floats;
+      kl.load(a.k + int64_t(tok0) * krow + int64_t(hq) * DK, krow, n, DK);
+      ql.load(a.q + int64_t(tok0) * krow + int64_t(hq) * DK, krow, n, DK);
+      gl.load(ent + L.gate);
+#pragma unroll
+      for (int m = 0; m < MAXO; ++m) {
+        const int p = tid + kChainThreads * m;
+        oo[m] = make_uint4(0, 0, 0, 0);
+        if (p < C * oppr) {
+          const int t = p / oppr, c = (p - t * oppr) * EPP;
+          if (t < n)
+            oo[m] = *reinterpret_cast<const uint4 *>(a.d_o + int64_t(tok0 + t) * vrow + int64_t(h) * DV + c0 + c);
+        }
+      }
+#pragma unroll
+      for (int kb = 0; kb < NRT; ++kb) {
+        pp[kb] = col4(ent + L.P + (16 * kb + 4 * g) * C + 16 * rt + r, C);
+        mm[kb] = col4(ent + L.M + (16 * kb + 4 * g) * C + 16 * rt + r, C);
+      }
+    };
+    auto store_do = [&](const uint4(&oo)[MAXO]) {
+#pragma unroll
+      for (int m = 0; m < MAXO; ++m) {
+        const int p = tid + kChainThreads * m;
+        if (p < C * oppr) {
+          const int t = p / oppr, c = (p - t * oppr) * EPP;
+          const T *x = reinterpret_cast<const T *>(&oo[m]);
+#pragma unroll
+          for (int j = 0; j < EPP; ++j) sdO[t * LDB + c + j] = to_f32(x[j]);
+        }
+      }
+    };
+    load_chunk(n_chunks - 1, ocur, pcur, mcur);
+    kl.store(sK, LDK, DK);
+    ql.store(sQ, LDK, DK);
+    gl.store(sgate, C);
+    store_do(ocur);
+
+    for (int cc = n_chunks - 1; cc >= 0; --cc) {
+      const int tok0 = start + cc * C, n = min(C, end - tok0);
+      float *ent = a.ent + (int64_t(c_first + cc) * a.H_v + h) * a.ent_floats;
+      // the gradient at this chunk's end state: to LDS and to the entry
+#pragma unroll
+      for (int m = 0; m < 4; ++m) {
+        const int i = w + 4 * m;
+        if (i < nst) {
+          const int kt = i % NKT, ct = i / NKT;
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const int row = 16 * kt + 4 * g + q, col = 16 * ct + r;
+            sdS[row * LDB + col] = accS[m][q];
+            ent[L.dS + int64_t(row) * DV + c0 + col] = accS[m][q];
+          }
+        }
+      }
+      uint4 onext[MAXO];
+      f32x4_t pnext[NRT], mnext[NRT];
+      const bool more = cc > 0;
+      if (more) load_chunk(cc - 1, onext, pnext, mnext);
+      __syncthreads();
+      // dU = P^T dO + diag(s) K dS'
+#pragma unroll
+      for (int m = 0; m < 2; ++m) {
+        if (m < nmine) {
+          const int ct = (w + 4 * m) / NRT;
+          f32x4_t kds = zero4(), pdo = zero4();
+          for (int k0 = 0; k0 < DK; k0 += 16)
+            kds = mm16(row4(sK + (16 * rt + r) * LDK + k0 + 4 * g), col4(sdS + (k0 + 4 * g) * LDB + 16 * ct + r, LDB),
+                       kds);
+#pragma unroll
+          for (int kb = 0; kb < NRT; ++kb)
+            pdo = mm16(pcur[kb], col4(sdO + (16 * kb + 4 * g) * LDB + 16 * ct + r, LDB), pdo);
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const int t = 16 * rt + 4 * g + q;
+            sdU[t * LDB + 16 * ct + r] = pdo[q] + sgate[64 + t] * kds[q];
+          }
+        }
+      }
+      __syncthreads();
+      // dY = M^T dU;  dv = dX = diag(beta) dY
+#pragma unroll
+      for (int m = 0; m < 2; ++m) {
+        if (m < nmine) {
+          const int ct = (w + 4 * m) / NRT;
+          f32x4_t acc = zero4();
+#pragma unroll
+          for (int kb = 0; kb < NRT; ++kb)
+            acc = mm16(mcur[kb], col4(sdU + (16 * kb + 4 * g) * LDB + 16 * ct + r, LDB), acc);
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const int t = 16 * rt + 4 * g + q, col = 16 * ct + r;
+            const float dx = sgate[128 + t] * acc[q];
+            ent[L.dY + int64_t(t) * DV + c0 + col] = acc[q];
+            if (t < n) a.dv[int64_t(tok0 + t) * vrow + int64_t(h) * DV + c0 + col] = dx;
+            sdX[t * LDB + col] = sgate[t] * dx;
+          }
+        }
+      }
+      __syncthreads();
+      // dS <- gamma_C dS' + Q^T diag(gamma) dO - K^T diag(gamma) dX
+      const float gC = sgate[C - 1];
+#pragma unroll
+      for (int m = 0; m < 4; ++m) {
+        const int i = w + 4 * m;
+        if (i < nst) {
+          const int kt = i % NKT, ct = i / NKT;
+          f32x4_t acc = accS[m] * gC;
+#pragma unroll
+          for (int kb = 0; kb < NRT; ++kb) {
+            const int t0 = 16 * kb + 4 * g;
+            f32x4_t xq = col4(sQ + t0 * LDK + 16 * kt + r, LDK);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) xq[j] *= sgate[t0 + j];
+            acc = mm16(xq, col4(sdO + t0 * LDB + 16 * ct + r, LDB), acc);
+            acc = mm16(-col4(sK + t0 * LDK + 16 * kt + r, LDK), col4(sdX + t0 * LDB + 16 * ct + r, LDB), acc);
+          }
+          accS[m] = acc;
+        }
+      }
+      __syncthreads();
+      if (more) {
+        kl.store(sK, LDK, DK);
+        ql.store(sQ, LDK, DK);
+        gl.store(sgate, C);
+        store_do(onext);
+#pragma unroll
+        for (int kb = 0; kb < NRT; ++kb) {
+          pcur[kb] = pnext[kb];
+          mcur[kb] = mnext[kb];
+        }
+      }
+    }
+  }
+  if (a.dh0) {
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+      const int i = w + 4 * m;
+      if (i < nst) {
+        const int kt = i % NKT, ct = i / NKT;
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+          a.dh0[unit_state + int64_t(16 * kt + 4 * g + q) * DV + c0 + 16 * ct + r] = accS[m][q];
+      }
+    }
+  }
+}
+
+}  // namespace
+
+// Blocks come in groups of 8 units x (2 x column blocks): all blocks of a unit
+// have the same block id mod 8, so they share one XCD's L2 copy of the unit's
+// k and q.  Within a unit, even slots walk forward and odd slots backward.
+template <typename T, int C>
+__global__ __launch_bounds__(kChainThreads) void bwd_chain_kernel(BwdArgs<T> a) {
+  __shared__ __attribute__((aligned(16))) char smem[ChainLds<T, C>::kBytes];
+  const int n_cb = a.d_v / min(32, a.d_v);
+  int u, x;
+  decode_block(blockIdx.x, 2 * n_cb, u, x);
+  if (u >= a.n_units) return;
+  if (x & 1)
+    rev_chain<T, C>(a, u, x >> 1, smem);
+  else
+    fwd_chain<T, C>(a, u, x >> 1, smem);
+}
+
+// ---------------------------------------------------------------------------
+// 3. Per (chunk, value head): the gradients.  8 waves.
+//
+// Phase 1 runs over d_v in slabs of DVS columns staged in LDS (dO, dY, U).
+// The C x d_k products W1 = dO S^T, W2 = dY S^T, W3 = U dS'^T are tiled
+// 16 x 16: wave w owns d_k column tile w % (d_k/16) and the row tiles i with
+// i % (8 / (d_k/16)) == w / (d_k/16), and reads its S and dS' rows straight
+// from the entry (each is read by one wave).  The lower tiles of dO U^T and
+// dY U^T go to the waves in turn.  Phase 2 forms dP . Gamma, dG and
+// Gamma . dGamma in LDS and finishes dq and dk with the products against K and
+// Q (contraction over the chunk).
+// ---------------------------------------------------------------------------
+namespace {
+constexpr int kGradThreads = 512;
+}
+
+template <typename T, int C, int DVS>
+__global__ __launch_bounds__(kGradThreads) void bwd_grad_kernel(BwdArgs<T> a) {
+  constexpr int NRT = C / 16, LD = C + 4, LDV = DVS + 4, NL = NRT * (NRT + 1) / 2;
+  constexpr int kSlabFloats = 3 * C * LDV, kPh2Floats = 3 * C * LD;
+  constexpr int kBig = kSlabFloats > kPh2Floats ? kSlabFloats : kPh2Floats;
+  constexpr int NK = DVS / 16;                                        // 16-deep steps per slab
+  constexpr int WPR = DVS / 4;                                        // float4 pieces per slab row
+  constexpr int NPC = (C * WPR + kGradThreads - 1) / kGradThreads;    // pieces per thread
+  __shared__ __attribute__((aligned(16))) float big[kBig];
+  __shared__ float sPartG[64 * 8], sPartS[64 * 8];
+  __shared__ float sR1[64], sRowE[64], sRowF[64], sColE[64], sSd[8];
+  __shared__ float sGam[64], sSc[64], sG2[64], sBe[64];
+
+  const int e = blockIdx.x;
+  const int slot = e / a.H_v, h = e - slot * a.H_v;
+  int s, tok0, n;
+  if (!a.geo.locate(slot, s, tok0, n)) return;
+  const int hq = h / a.group, DK = a.d_k, DV = a.d_v;
+  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, r = lane & 15, g = lane >> 4;
+  const BwdEntry L(C, DK, DV);
+  const float *ent = a.ent + int64_t(e) * a.ent_floats;
+  const int64_t krow = int64_t(a.H_qk) * DK, vrow = int64_t(a.H_v) * DV;
+
+  if (tid < C) {
+    sGam[tid] = ent[L.gate + kGateGamma + tid];
+    sSc[tid] = ent[L.gate + kGateS + tid];
+    sG2[tid] = ent[L.gate + kGateLog2 + tid];
+    sBe[tid] = ent[L.gate + kGateBeta + tid];
+  }
+
+  // ---- tile ownership ----
+  const int NKT = DK / 16, wpc = 8 / NKT;  // waves per d_k column tile
+  const int ct = w % NKT, rsel = w / NKT;  // d_k column tile, row-tile residue
+  const bool has_rows = rsel < NRT;
+  // lower C x C tiles of this wave: numbers w and w + 8
+  const int np = (w < NL) + (w + 8 < NL);
+  int prt[2], pct[2];
+  lower_tile(min(w, NL - 1), prt[0], pct[0]);
+  lower_tile(min(w + 8, NL - 1), prt[1], pct[1]);
+  f32x4_t W1[NRT], W2[NRT], W3[NRT], aP[2], aA[2];
+#pragma unroll
+  for (int i = 0; i < NRT; ++i) W1[i] = W2[i] = W3[i] = zero4();
+  aP[0] = aP[1] = aA[0] = aA[1] = zero4();
+  float sd = 0.0f;  // <S, dS'> partial (one wave per d_k column tile)
+  float r1acc[NPC];
+#pragma unroll
+  for (int m = 0; m < NPC; ++m) r1acc[m] = 0.0f;
+
+  float *sdO = big, *sdY = big + C * LDV, *sU = big + 2 * C * LDV;
+  const float *Sg = ent + L.S + int64_t(16 * ct + r) * DV + 4 * g;
+  const float *dSg = ent + L.dS + int64_t(16 * ct + r) * DV + 4 * g;
+  for (int dv0 = 0; dv0 < DV; dv0 += DVS) {
+    f32x4_t yS[NK], ydS[NK];
+#pragma unroll
+    for (int kk = 0; kk < NK; ++kk) {
+      yS[kk] = has_rows ? row4(Sg + dv0 + 16 * kk) : zero4();
+      ydS[kk] = has_rows ? row4(dSg + dv0 + 16 * kk) : zero4();
+    }
+    // stage dO, dY, U; sum dY . X on the way
+#pragma unroll
+    for (int m = 0; m < NPC; ++m) {
+      const int p = tid + kGradThreads * m;
+      float part = 0.0f;
+      if (p < C * WPR) {
+        const int t = p / WPR, c = (p - t * WPR) * 4;
+        f32x4_t o = zero4();
+        if (t < n) o = row4(a.d_o + int64_t(tok0 + t) * vrow + int64_t(h) * DV + dv0 + c);
+        const f32x4_t y = row4(ent + L.dY + int64_t(t) * DV + dv0 + c);
+        const f32x4_t uu = row4(ent + L.U + int64_t(t) * DV + dv0 + c);
+        const f32x4_t x = row4(ent + L.X + int64_t(t) * DV + dv0 + c);
+        *reinterpret_cast<f32x4_t *>(sdO + t * LDV + c) = o;
+        *reinterpret_cast<f32x4_t *>(sdY + t * LDV + c) = y;
+        *reinterpret_cast<f32x4_t *>(sU + t * LDV + c) = uu;
+        part = y[0] * x[0] + y[1] * x[1] + y[2] * x[2] + y[3] * x[3];
+      }
+      r1acc[m] += group_sum(part, WPR);
+    }
+    __syncthreads();
+#pragma unroll
+    for (int kk = 0; kk < NK; ++kk) {
+      const int k0 = 16 * kk + 4 * g;
+      if (has_rows) {
+#pragma unroll
+        for (int i = 0; i < NRT; ++i) {
+          if (i % wpc != rsel) continue;
+          const int row = (16 * i + r) * LDV + k0;
+          W1[i] = mm16(row4(sdO + row), yS[kk], W1[i]);
+          W2[i] = mm16(row4(sdY + row), yS[kk], W2[i]);
+          W3[i] = mm16(row4(sU + row), ydS[kk], W3[i]);
+        }
+        if (rsel == 0) {
+          const f32x4_t pr = yS[kk] * ydS[kk];
+          sd += (pr[0] + pr[1]) + (pr[2] + pr[3]);
+        }
+      }
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        if (j < np) {
+          const f32x4_t yu = row4(sU + (16 * pct[j] + r) * LDV + k0);
+          aP[j] = mm16(row4(sdO + (16 * prt[j] + r) * LDV + k0), yu, aP[j]);
+          aA[j] = mm16(row4(sdY + (16 * prt[j] + r) * LDV + k0), yu, aA[j]);
+        }
+      }
+    }
+    __syncthreads();
+  }
+  // row sums of dY . X: the first thread of each row's group holds them
+#pragma unroll
+  for (int m = 0; m < NPC; ++m) {
+    const int p = tid + kGradThreads * m;
+    if (p < C * WPR && (p % WPR) == 0) sR1[p / WPR] = r1acc[m];
+  }
+  {
+    const float sdw = group_sum(sd, 64);
+    if (lane == 0) sSd[w] = sdw;
+  }
+
+  // ---- phase 2: C x C matrices in LDS (the slab area is free) ----
+  float *sdP = big, *sdA = big + C * LD, *sE = big + 2 * C * LD;
+  // tiles above the diagonal are zero; the computed lower tiles carry their masks
+  for (int idx = tid; idx < C * C; idx += kGradThreads) {
+    const int t = idx / C, i = idx - t * C;
+    if ((i >> 4) > (t >> 4)) {
+      sdP[t * LD + i] = 0.0f;
+      sdA[t * LD + i] = 0.0f;
+    }
+  }
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    if (j < np) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int t = 16 * prt[j] + 4 * g + q, i = 16 * pct[j] + r;
+        sdP[t * LD + i] = i <= t ? aP[j][q] : 0.0f;
+        sdA[t * LD + i] = i < t ? -aA[j][q] : 0.0f;
+      }
+    }
+  }
+  // K and Q values of this wave's d_k column tile: kf[i][j] = K[16 i + 4g + j][16 ct + r]
+  // (B fragments of the products over the chunk, and the factors of the d_k row sums)
+  f32x4_t kf[NRT], qf[NRT];
+#pragma unroll
+  for (int i = 0; i < NRT; ++i) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int t = 16 * i + 4 * g + j;
+      const int64_t o = int64_t(tok0 + min(t, n - 1)) * krow + int64_t(hq) * DK + 16 * ct + r;
+      kf[i][j] = t < n ? to_f32(a.k[o]) : 0.0f;
+      qf[i][j] = t < n ? to_f32(a.q[o]) : 0.0f;
+    }
+  }
+  __syncthreads();
+  // elementwise, 8 threads per row: dP . Gamma, dG = dA . diag(beta) Gamma,
+  // E = Gamma . dGamma = diag(beta) dA . (Gamma . KK^T) + dP . P
+  {
+    const int t = tid >> 3, part = tid & 7;
+    float rowE = 0.0f, rowF = 0.0f;
+    if (t < C) {
+      for (int i = part; i < C; i += 8) {
+        const float dp = sdP[t * LD + i], da = sdA[t * LD + i];
+        const float gam = i <= t ? fast_exp2(sG2[t] - sG2[i]) : 0.0f;
+        const float f = da * ent[L.G + t * C + i];
+        const float ev = sBe[t] * f + dp * ent[L.P + t * C + i];
+        rowE += ev;
+        rowF += f;
+        sdP[t * LD + i] = dp * gam;
+        sdA[t * LD + i] = da * sBe[t] * gam;
+        sE[t * LD + i] = ev;
+      }
+    }
+    rowE = group_sum(rowE, 8);
+    rowF = group_sum(rowF, 8);
+    if (t < C && part == 0) {
+      sRowE[t] = rowE;
+      sRowF[t] = rowF;
+    }
+  }
+  __syncthreads();
+  if (tid < C) {
+    float c = 0.0f;
+    for (int i = 0; i < C; ++i) c += sE[i * LD + tid];
+    sColE[tid] = c;
+  }
+  __syncthreads();
+  // H = dG + dG^T, into E's place
+  for (int idx = tid; idx < C * C; idx += kGradThreads) {
+    const int t = idx / C, i = idx - t * C;
+    sE[t * LD + i] = sdA[t * LD + i] + sdA[i * LD + t];
+  }
+  __syncthreads();
+  // dq, dk and the d_k row sums of this wave's tiles
+  if (has_rows) {
+#pragma unroll
+    for (int i = 0; i < NRT; ++i) {
+      if (i % wpc != rsel) continue;
+      f32x4_t aq = zero4(), ak = zero4();
+#pragma unroll
+      for (int kb = 0; kb < NRT; ++kb) {
+        aq = mm16(row4(sdP + (16 * i + r) * LD + 16 * kb + 4 * g), kf[kb], aq);
+        ak = mm16(col4(sdP + (16 * kb + 4 * g) * LD + 16 * i + r, LD), qf[kb], ak);
+        ak = mm16(row4(sE + (16 * i + r) * LD + 16 * kb + 4 * g), kf[kb], ak);
+      }
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int t = 16 * i + 4 * g + q, col = 16 * ct + r;
+        const float dqv = sGam[t] * W1[i][q] + aq[q];
+        const float dkv = ak[q] - sGam[t] * sBe[t] * W2[i][q] + sSc[t] * W3[i][q];
+        const float pg = group_sum(qf[i][q] * W1[i][q] - sBe[t] * kf[i][q] * W2[i][q], 16);
+        const float ps = group_sum(kf[i][q] * W3[i][q], 16);
+        if (r == 0) {
+          sPartG[t * 8 + ct] = pg;
+          sPartS[t * 8 + ct] = ps;
+        }
+        if (t < n) {
+          const int64_t o = (int64_t(tok0 + t) * a.H_v + h) * DK + col;
+          a.dq[o] = dqv;
+          a.dk[o] = dkv;
+        }
+      }
+    }
+  }
+  __syncthreads();
+  // per-token scalars, lane t of wave 0
+  if (w == 0) {
+    const int t = lane;
+    float dg = 0.0f, sds = 0.0f;
+    if (t < n) {
+      float pg = 0.0f, ps = 0.0f;
+      for (int c = 0; c < NKT; ++c) {
+        pg += sPartG[t * 8 + c];
+        ps += sPartS[t * 8 + c];
+      }
+      sds = sSc[t] * ps;
+      dg = sGam[t] * pg + sRowE[t] - sColE[t] - sds;
+      a.dbeta[int64_t(tok0 + t) * a.H_v + h] = sR1[t] + sRowF[t];
+    }
+    const float tot_sds = group_sum(sds, 64);
+    float sdsum = 0.0f;
+    for (int i = 0; i < 8; ++i) sdsum += sSd[i];
+    if (t == n - 1) dg += sGam[C - 1] * sdsum + tot_sds;
+    // suffix sums over t' >= t: a prefix sum over the reversed lanes
+    const float rev = __shfl(dg, max(n - 1 - lane, 0));
+    const float pre = wave_prefix_sum(lane < n ? rev : 0.0f);
+    const float suf = __shfl(pre, max(n - 1 - lane, 0));
+    if (t < n) {
+      const int64_t gi = int64_t(tok0 + t) * a.H_v + h;
+      a.dalpha[gi] = suf / a.alpha[gi];
+    }
+  }
 }
 
 // dq (and dk) of a query/key head: the sum over the value heads that read it.
@@ -383,7 +950,31 @@ __global__ __launch_bounds__(256) void group_sum_kernel(const float *part, float
   }
 }
 
-size_t bwd_unit_floats(int chunk, int d_k, int d_v) { return size_t(BwdLayout(chunk, d_k, d_v).total); }
+size_t bwd_entry_floats(int chunk, int d_k, int d_v) { return size_t(BwdEntry(chunk, d_k, d_v).total); }
+
+template <typename T, int C>
+static hipError_t launch_bwd_c(const BwdProblem &b, const BwdArgs<T> &a, hipStream_t st) {
+  const Problem &p = b.p;
+  const unsigned n_ent = unsigned(int64_t(a.geo.n_slots) * p.H_v);
+  if (n_ent > 0) {
+    hipLaunchKernelGGL((bwd_factor_kernel<T, C>), dim3(n_ent), dim3(256), 0, st, a);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  const int n_cb = p.d_v / std::min(32, p.d_v);
+  const int64_t groups = (int64_t(a.n_units) + 7) / 8;
+  const unsigned chain_blocks = unsigned(groups * 8 * 2 * n_cb);
+  hipLaunchKernelGGL((bwd_chain_kernel<T, C>), dim3(chain_blocks), dim3(kChainThreads), 0, st, a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || n_ent == 0) return e;
+  if (p.d_v >= 64)
+    hipLaunchKernelGGL((bwd_grad_kernel<T, C, 64>), dim3(n_ent), dim3(kGradThreads), 0, st, a);
+  else if (p.d_v == 32)
+    hipLaunchKernelGGL((bwd_grad_kernel<T, C, 32>), dim3(n_ent), dim3(kGradThreads), 0, st, a);
+  else
+    hipLaunchKernelGGL((bwd_grad_kernel<T, C, 16>), dim3(n_ent), dim3(kGradThreads), 0, st, a);
+  return hipGetLastError();
+}
 
 template <typename T>
 static hipError_t launch_chunk_bwd_t(const BwdProblem &b, hipStream_t st) {
@@ -395,34 +986,36 @@ static hipError_t launch_chunk_bwd_t(const BwdProblem &b, hipStream_t st) {
   a.d_o = static_cast<const T *>(b.d_o);
   a.alpha = p.alpha;
   a.beta = p.beta;
+  a.h0 = p.h0;
   a.dhT = b.dhT;
-  a.states = b.states;
-  a.dq_part = b.dq_part;
-  a.dk_part = b.dk_part;
+  a.ent = b.entries;
+  a.ent_floats = int64_t(bwd_entry_floats(p.chunk, p.d_k, p.d_v));
+  const int group = p.H_v / p.H_qk;
+  a.dq = group == 1 ? b.dq : b.dq_part;
+  a.dk = group == 1 ? b.dk : b.dk_part;
   a.dv = b.dv;
   a.dalpha = b.dalpha;
   a.dbeta = b.dbeta;
   a.dh0 = b.dh0;
-  a.scratch = b.scratch;
-  a.unit_floats = int64_t(bwd_unit_floats(p.chunk, p.d_k, p.d_v));
   a.H_qk = p.H_qk;
   a.H_v = p.H_v;
   a.d_k = p.d_k;
   a.d_v = p.d_v;
-  a.group = p.H_v / p.H_qk;
+  a.group = group;
   a.n_units = p.n_seqs * p.H_v;
   a.geo = make_geom(p, &b.ws);
   if (a.n_units == 0) return hipSuccess;
-  hipLaunchKernelGGL(chunk_bwd_kernel<T>, dim3(unsigned(a.n_units)), dim3(kBwdThreads), 0, st, a);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
+  hipError_t e = p.chunk == 16   ? launch_bwd_c<T, 16>(b, a, st)
+                 : p.chunk == 32 ? launch_bwd_c<T, 32>(b, a, st)
+                                 : launch_bwd_c<T, 64>(b, a, st);
+  if (e != hipSuccess || group == 1) return e;
   const int64_t tokens = p.n_tokens();
   const int64_t total = tokens * p.H_qk * p.d_k;
   if (total == 0) return hipSuccess;
   const unsigned blocks = unsigned(std::min<int64_t>((total + 255) / 256, 1 << 16));
-  hipLaunchKernelGGL(group_sum_kernel, dim3(blocks), dim3(256), 0, st, b.dq_part, b.dq, tokens, p.H_qk, a.group,
+  hipLaunchKernelGGL(group_sum_kernel, dim3(blocks), dim3(256), 0, st, b.dq_part, b.dq, tokens, p.H_qk, group,
                      p.d_k);
-  hipLaunchKernelGGL(group_sum_kernel, dim3(blocks), dim3(256), 0, st, b.dk_part, b.dk, tokens, p.H_qk, a.group,
+  hipLaunchKernelGGL(group_sum_kernel, dim3(blocks), dim3(256), 0, st, b.dk_part, b.dk, tokens, p.H_qk, group,
                      p.d_k);
   return hipGetLastError();
 }

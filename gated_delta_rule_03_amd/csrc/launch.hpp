@@ -71,9 +71,6 @@ hipError_t launch_chunk_offsets(const Problem &p, const Workspace &ws, hipStream
 hipError_t launch_prep(const Problem &p, const Workspace &ws, hipStream_t st);
 hipError_t launch_scan(const Problem &p, const Workspace &ws, hipStream_t st, float *mb = nullptr);
 hipError_t launch_recurrent(const Problem &p, hipStream_t st);
-// The token-by-token forward writing the state that enters every chunk of
-// p.chunk tokens to states [chunk slot, H_v, d_k, d_v] (o and hT may be null).
-hipError_t launch_recurrent_states(const Problem &p, const Workspace &ws, float *states, hipStream_t st);
 
 // Backward pass of the chunked form (bwd.hip).
 struct BwdProblem {
@@ -81,12 +78,11 @@ struct BwdProblem {
   Workspace ws;          // chunk offsets of a packed batch
   const void *d_o;       // dL/do, [tokens, H_v, d_v] in the input dtype
   const float *dhT;      // dL/dS_T or null
-  float *states;         // [chunk slots, H_v, d_k, d_v]: chunk-start states
-  float *dq_part, *dk_part;  // [tokens, H_v, d_k]: per value head
-  float *scratch;        // per-unit intermediates, bwd_unit_floats each
+  float *entries;        // [chunk slots * H_v] per-chunk intermediates, bwd_entry_floats each
+  float *dq_part, *dk_part;  // [tokens, H_v, d_k]: per value head (grouped heads only)
   float *dq, *dk, *dv, *dalpha, *dbeta, *dh0;
 };
-size_t bwd_unit_floats(int chunk, int d_k, int d_v);
+size_t bwd_entry_floats(int chunk, int d_k, int d_v);
 hipError_t launch_chunk_bwd(const BwdProblem &b, hipStream_t st);
 hipError_t launch_kda_chunk(const Problem &p, const Workspace &ws, hipStream_t st);
 // Segment-parallel path (seqmap.hip, fold.hip).

@@ -24,9 +24,6 @@ struct RecArgs {
   const float *h0;
   T *o;
   float *hT;
-  // states mode (the backward's forward pass): the state entering every
-  // chunk of geo.chunk tokens, [chunk slot, H_v, d_k, d_v]; o may then be null
-  float *states;
   int H_qk, H_v, d_k, d_v, group, n_units, n_colblk;
   SeqGeom geo;
 };
@@ -90,15 +87,6 @@ __global__ __launch_bounds__(64) void recurrent_kernel(RecArgs<T> a) {
   TokenOps cur, nxt;
   if (start < end) fetch_token<T, PER_CHANNEL>(a, start, hq, h, col, r0, nrow, cur);
   for (int tok = start; tok < end; ++tok) {
-    if (a.states && (tok - start) % a.geo.chunk == 0) {
-      const int slot = a.geo.first_chunk(s) + (tok - start) / a.geo.chunk;
-      if (slot < a.geo.n_slots) {
-        float *dst = a.states + ((int64_t(slot) * a.H_v + h) * a.d_k + r0) * a.d_v + col;
-#pragma unroll
-        for (int i = 0; i < 32; ++i)
-          if (i < nrow) dst[int64_t(i) * a.d_v] = S[i];
-      }
-    }
     if (tok + 1 < end) fetch_token<T, PER_CHANNEL>(a, tok + 1, hq, h, col, r0, nrow, nxt);
     // predict: vhat = (alpha S)^T k  (per-channel: (diag(a) S)^T k)
     float p = 0.0f;
@@ -116,7 +104,7 @@ __global__ __launch_bounds__(64) void recurrent_kernel(RecArgs<T> a) {
     }
     r += __shfl_xor(r, 16);
     r += __shfl_xor(r, 32);
-    if (a.o && lane < 16) a.o[(int64_t(tok) * a.H_v + h) * a.d_v + col] = from_f32<T>(r);
+    if (lane < 16) a.o[(int64_t(tok) * a.H_v + h) * a.d_v + col] = from_f32<T>(r);
     cur = nxt;
   }
   if (a.hT) {
@@ -127,10 +115,8 @@ __global__ __launch_bounds__(64) void recurrent_kernel(RecArgs<T> a) {
 }
 
 template <typename T>
-static hipError_t launch_recurrent_t(const Problem &p, hipStream_t st, const Workspace *ws = nullptr,
-                                     float *states = nullptr) {
+static hipError_t launch_recurrent_t(const Problem &p, hipStream_t st) {
   RecArgs<T> a;
-  a.states = states;
   a.q = static_cast<const T *>(p.q);
   a.k = static_cast<const T *>(p.k);
   a.v = static_cast<const T *>(p.v);
@@ -146,7 +132,7 @@ static hipError_t launch_recurrent_t(const Problem &p, hipStream_t st, const Wor
   a.group = p.H_v / p.H_qk;
   a.n_units = p.n_seqs * p.H_v;
   a.n_colblk = p.d_v / 16;
-  a.geo = make_geom(p, ws);
+  a.geo = make_geom(p, nullptr);
   const int64_t blocks = int64_t(a.n_units) * a.n_colblk;
   if (blocks == 0) return hipSuccess;
   if (p.per_channel)
@@ -158,11 +144,6 @@ static hipError_t launch_recurrent_t(const Problem &p, hipStream_t st, const Wor
 
 hipError_t launch_recurrent(const Problem &p, hipStream_t st) {
   return p.dtype == 1 ? launch_recurrent_t<bf16_t>(p, st) : launch_recurrent_t<float>(p, st);
-}
-
-hipError_t launch_recurrent_states(const Problem &p, const Workspace &ws, float *states, hipStream_t st) {
-  return p.dtype == 1 ? launch_recurrent_t<bf16_t>(p, st, &ws, states)
-                      : launch_recurrent_t<float>(p, st, &ws, states);
 }
 
 }  // namespace gdn

@@ -254,12 +254,18 @@ def test_noalloc_argument_errors(lib):
 def test_backward_workspace_and_argument_errors(lib):
     """gdn_chunk_bwd: workspace sizes and argument errors, all before any launch."""
     bf, f32 = gdn.GDN_BF16, gdn.GDN_F32
+    # one fp32 entry per (chunk slot, value head): M, P and Gamma . K K^T
+    # (C x C each), 256 gate values, the chunk's start state and end gradient
+    # (d_k x d_v each), X, U and dY (C x d_v each)
+    def entry(C, dk, dv):
+        return 4 * (3 * C * C + 256 + 2 * dk * dv + 3 * C * dv)
     w = gdn.chunk_bwd_workspace_bytes(4, 4096, 16, 16, 128, 128, bf, 64, 0)
-    states = 4 * 64 * 16 * 128 * 128 * 4            # chunk-start states, fp32
-    parts = 2 * 4 * 4096 * 16 * 128 * 4              # per-value-head dq and dk
-    assert states + parts < w < states + parts + 64 * 1024 * 1024
+    ents = 4 * 64 * 16 * entry(64, 128, 128)        # no per-value-head parts: one value head per qk head
+    assert ents <= w < ents + 4096
     packed = gdn.chunk_bwd_workspace_bytes(1, 1000, 2, 4, 64, 32, f32, 32, 5)
-    assert packed >= (32 + 5) * 4 * 64 * 32 * 4 + 2 * 1000 * 4 * 64 * 4
+    ents = (32 + 5) * 4 * entry(32, 64, 32)
+    parts = 2 * 1000 * 4 * 64 * 4                    # per-value-head dq and dk under grouped heads
+    assert ents + parts <= packed < ents + parts + 4096
     assert gdn.chunk_bwd_workspace_bytes(1, 64, 1, 1, 48, 64, bf, 64, 0) == 0
     assert gdn.chunk_bwd_workspace_bytes(1, 64, 1, 1, 64, 64, bf, 48, 0) == 0
     p = ctypes.c_void_p(0x1000)
