@@ -106,6 +106,16 @@ __device__ __forceinline__ float group_sum(float x, int w) {
   return x;
 }
 
+// Workgroup barrier for LDS traffic: waits for this wave's LDS operations but
+// not for its outstanding global loads, so the next chunk's operands stay in
+// flight across it (__syncthreads would wait for them).  The empty asm
+// statements keep the compiler from moving memory accesses across it.
+__device__ __forceinline__ void lds_sync() {
+  asm volatile("" ::: "memory");
+  lds_barrier();
+  asm volatile("" ::: "memory");
+}
+
 // The k-th lower 16 x 16 tile (row tile >= column tile), row by row.
 __device__ __forceinline__ void lower_tile(int k, int &rt, int &ct) {
   rt = 0;
@@ -346,28 +356,37 @@ __device__ void fwd_chain(const BwdArgs<T> &a, int u, int cb, char *smem) {
 
   TileLoader<T, C> kl;
   GateLoader gl;
+  // V at this wave's accumulator positions and the A fragments of M for its
+  // row tile: loaded a chunk ahead, right after their last use
   f32x4_t vcur[2], mcur[NRT];
-  auto load_chunk = [&](int cc, f32x4_t(&vv)[2], f32x4_t(&mm)[NRT]) {
+  auto load_v = [&](int cc) {
     const int tok0 = start + cc * C, n = min(C, end - tok0);
-    const float *ent = a.ent + (int64_t(c_first + cc) * a.H_v + h) * a.ent_floats;
-    kl.load(a.k + int64_t(tok0) * krow + int64_t(hq) * DK, krow, n, DK);
-    gl.load(ent + L.gate);
 #pragma unroll
     for (int m = 0; m < 2; ++m) {
-      vv[m] = zero4();
+      vcur[m] = zero4();
       if (m < nmine) {
         const int ct = (w + 4 * m) / NRT;
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
           const int t = 16 * rt + 4 * g + q;
-          if (t < n) vv[m][q] = to_f32(a.v[int64_t(tok0 + t) * vrow + int64_t(h) * DV + c0 + 16 * ct + r]);
+          if (t < n) vcur[m][q] = to_f32(a.v[int64_t(tok0 + t) * vrow + int64_t(h) * DV + c0 + 16 * ct + r]);
         }
       }
     }
-#pragma unroll
-    for (int kb = 0; kb < NRT; ++kb) mm[kb] = row4(ent + L.M + (16 * rt + r) * C + 16 * kb + 4 * g);
   };
-  load_chunk(0, vcur, mcur);
+  auto load_m = [&](int cc) {
+    const float *ent = a.ent + (int64_t(c_first + cc) * a.H_v + h) * a.ent_floats;
+#pragma unroll
+    for (int kb = 0; kb < NRT; ++kb) mcur[kb] = row4(ent + L.M + (16 * rt + r) * C + 16 * kb + 4 * g);
+  };
+  auto load_tiles = [&](int cc) {
+    const int tok0 = start + cc * C, n = min(C, end - tok0);
+    kl.load(a.k + int64_t(tok0) * krow + int64_t(hq) * DK, krow, n, DK);
+    gl.load(a.ent + (int64_t(c_first + cc) * a.H_v + h) * a.ent_floats + L.gate);
+  };
+  load_tiles(0);
+  load_v(0);
+  load_m(0);
   kl.store(sK, LDK, DK);
   gl.store(sgate, C);
 
@@ -387,10 +406,9 @@ __device__ void fwd_chain(const BwdArgs<T> &a, int u, int cb, char *smem) {
         }
       }
     }
-    f32x4_t vnext[2], mnext[NRT];
     const bool more = cc + 1 < n_chunks;
-    if (more) load_chunk(cc + 1, vnext, mnext);
-    __syncthreads();
+    if (more) load_tiles(cc + 1);
+    lds_sync();
     // X = V - diag(gamma) K S;  Y = diag(beta) X
 #pragma unroll
     for (int m = 0; m < 2; ++m) {
@@ -409,7 +427,8 @@ __device__ void fwd_chain(const BwdArgs<T> &a, int u, int cb, char *smem) {
         }
       }
     }
-    __syncthreads();
+    if (more) load_v(cc + 1);
+    lds_sync();
     // U = M Y;  diag(s) U for the state update
 #pragma unroll
     for (int m = 0; m < 2; ++m) {
@@ -427,7 +446,8 @@ __device__ void fwd_chain(const BwdArgs<T> &a, int u, int cb, char *smem) {
         }
       }
     }
-    __syncthreads();
+    if (more) load_m(cc + 1);
+    lds_sync();
     // S <- gamma_C S + K^T diag(s) U
     const float gC = sgate[C - 1];
 #pragma unroll
@@ -443,14 +463,10 @@ __device__ void fwd_chain(const BwdArgs<T> &a, int u, int cb, char *smem) {
         accS[m] = acc;
       }
     }
-    __syncthreads();
+    lds_sync();
     if (more) {
       kl.store(sK, LDK, DK);
       gl.store(sgate, C);
-#pragma unroll
-      for (int m = 0; m < 2; ++m) vcur[m] = vnext[m];
-#pragma unroll
-      for (int kb = 0; kb < NRT; ++kb) mcur[kb] = mnext[kb];
     }
   }
 }
@@ -501,45 +517,52 @@ __device__ void rev_chain(const BwdArgs<T> &a, int u, int cb, char *smem) {
     const int oppr = CB / EPP;
     uint4 ocur[MAXO];
     f32x4_t pcur[NRT], mcur[NRT];  // A fragments of P^T and M^T for this wave's row tile
-    auto load_chunk = [&](int cc, uint4(&oo)[MAXO], f32x4_t(&pp)[NRT], f32x4_t(&mm)[NRT]) {
+    auto load_tiles = [&](int cc) {
       const int tok0 = start + cc * C, n = min(C, end - tok0);
-      const float *ent = a.ent + (int64_t(c_first + cc) * a.H_v + h) * a.ent_floats;
       kl.load(a.k + int64_t(tok0) * krow + int64_t(hq) * DK, krow, n, DK);
       ql.load(a.q + int64_t(tok0) * krow + int64_t(hq) * DK, krow, n, DK);
-      gl.load(ent + L.gate);
+      gl.load(a.ent + (int64_t(c_first + cc) * a.H_v + h) * a.ent_floats + L.gate);
 #pragma unroll
       for (int m = 0; m < MAXO; ++m) {
         const int p = tid + kChainThreads * m;
-        oo[m] = make_uint4(0, 0, 0, 0);
+        ocur[m] = make_uint4(0, 0, 0, 0);
         if (p < C * oppr) {
           const int t = p / oppr, c = (p - t * oppr) * EPP;
           if (t < n)
-            oo[m] = *reinterpret_cast<const uint4 *>(a.d_o + int64_t(tok0 + t) * vrow + int64_t(h) * DV + c0 + c);
+            ocur[m] = *reinterpret_cast<const uint4 *>(a.d_o + int64_t(tok0 + t) * vrow + int64_t(h) * DV + c0 + c);
         }
       }
-#pragma unroll
-      for (int kb = 0; kb < NRT; ++kb) {
-        pp[kb] = col4(ent + L.P + (16 * kb + 4 * g) * C + 16 * rt + r, C);
-        mm[kb] = col4(ent + L.M + (16 * kb + 4 * g) * C + 16 * rt + r, C);
-      }
     };
-    auto store_do = [&](const uint4(&oo)[MAXO]) {
+    // loaded a chunk ahead, right after their last use
+    auto load_p = [&](int cc) {
+      const float *ent = a.ent + (int64_t(c_first + cc) * a.H_v + h) * a.ent_floats;
+#pragma unroll
+      for (int kb = 0; kb < NRT; ++kb) pcur[kb] = col4(ent + L.P + (16 * kb + 4 * g) * C + 16 * rt + r, C);
+    };
+    auto load_m = [&](int cc) {
+      const float *ent = a.ent + (int64_t(c_first + cc) * a.H_v + h) * a.ent_floats;
+#pragma unroll
+      for (int kb = 0; kb < NRT; ++kb) mcur[kb] = col4(ent + L.M + (16 * kb + 4 * g) * C + 16 * rt + r, C);
+    };
+    auto store_do = [&]() {
 #pragma unroll
       for (int m = 0; m < MAXO; ++m) {
         const int p = tid + kChainThreads * m;
         if (p < C * oppr) {
           const int t = p / oppr, c = (p - t * oppr) * EPP;
-          const T *x = reinterpret_cast<const T *>(&oo[m]);
+          const T *x = reinterpret_cast<const T *>(&ocur[m]);
 #pragma unroll
           for (int j = 0; j < EPP; ++j) sdO[t * LDB + c + j] = to_f32(x[j]);
         }
       }
     };
-    load_chunk(n_chunks - 1, ocur, pcur, mcur);
+    load_tiles(n_chunks - 1);
+    load_p(n_chunks - 1);
+    load_m(n_chunks - 1);
     kl.store(sK, LDK, DK);
     ql.store(sQ, LDK, DK);
     gl.store(sgate, C);
-    store_do(ocur);
+    store_do();
 
     for (int cc = n_chunks - 1; cc >= 0; --cc) {
       const int tok0 = start + cc * C, n = min(C, end - tok0);
@@ -558,11 +581,9 @@ __device__ void rev_chain(const BwdArgs<T> &a, int u, int cb, char *smem) {
           }
         }
       }
-      uint4 onext[MAXO];
-      f32x4_t pnext[NRT], mnext[NRT];
       const bool more = cc > 0;
-      if (more) load_chunk(cc - 1, onext, pnext, mnext);
-      __syncthreads();
+      if (more) load_tiles(cc - 1);
+      lds_sync();
       // dU = P^T dO + diag(s) K dS'
 #pragma unroll
       for (int m = 0; m < 2; ++m) {
@@ -582,7 +603,8 @@ __device__ void rev_chain(const BwdArgs<T> &a, int u, int cb, char *smem) {
           }
         }
       }
-      __syncthreads();
+      if (more) load_p(cc - 1);
+      lds_sync();
       // dY = M^T dU;  dv = dX = diag(beta) dY
 #pragma unroll
       for (int m = 0; m < 2; ++m) {
@@ -602,7 +624,8 @@ __device__ void rev_chain(const BwdArgs<T> &a, int u, int cb, char *smem) {
           }
         }
       }
-      __syncthreads();
+      if (more) load_m(cc - 1);
+      lds_sync();
       // dS <- gamma_C dS' + Q^T diag(gamma) dO - K^T diag(gamma) dX
       const float gC = sgate[C - 1];
 #pragma unroll
@@ -623,17 +646,12 @@ __device__ void rev_chain(const BwdArgs<T> &a, int u, int cb, char *smem) {
           accS[m] = acc;
         }
       }
-      __syncthreads();
+      lds_sync();
       if (more) {
         kl.store(sK, LDK, DK);
         ql.store(sQ, LDK, DK);
         gl.store(sgate, C);
-        store_do(onext);
-#pragma unroll
-        for (int kb = 0; kb < NRT; ++kb) {
-          pcur[kb] = pnext[kb];
-          mcur[kb] = mnext[kb];
-        }
+        store_do();
       }
     }
   }
@@ -657,7 +675,7 @@ __device__ void rev_chain(const BwdArgs<T> &a, int u, int cb, char *smem) {
 // have the same block id mod 8, so they share one XCD's L2 copy of the unit's
 // k and q.  Within a unit, even slots walk forward and odd slots backward.
 template <typename T, int C>
-__global__ __launch_bounds__(kChainThreads) void bwd_chain_kernel(BwdArgs<T> a) {
+__global__ __launch_bounds__(kChainThreads, 2) void bwd_chain_kernel(BwdArgs<T> a) {
   __shared__ __attribute__((aligned(16))) char smem[ChainLds<T, C>::kBytes];
   const int n_cb = a.d_v / min(32, a.d_v);
   int u, x;
@@ -670,19 +688,20 @@ __global__ __launch_bounds__(kChainThreads) void bwd_chain_kernel(BwdArgs<T> a) 
 }
 
 // ---------------------------------------------------------------------------
-// 3. Per (chunk, value head): the gradients.  8 waves.
+// 3. Per (chunk, value head): the gradients.  16 waves.
 //
 // Phase 1 runs over d_v in slabs of DVS columns staged in LDS (dO, dY, U).
 // The C x d_k products W1 = dO S^T, W2 = dY S^T, W3 = U dS'^T are tiled
 // 16 x 16: wave w owns d_k column tile w % (d_k/16) and the row tiles i with
-// i % (8 / (d_k/16)) == w / (d_k/16), and reads its S and dS' rows straight
-// from the entry (each is read by one wave).  The lower tiles of dO U^T and
-// dY U^T go to the waves in turn.  Phase 2 forms dP . Gamma, dG and
+// i % (16 / (d_k/16)) == w / (d_k/16), and reads its S and dS' rows straight
+// from the entry.  Each lower tile of dO U^T and dY U^T has a wave of its
+// own.  Phase 2 forms dP . Gamma, dG and
 // Gamma . dGamma in LDS and finishes dq and dk with the products against K and
 // Q (contraction over the chunk).
 // ---------------------------------------------------------------------------
 namespace {
-constexpr int kGradThreads = 512;
+constexpr int kGradThreads = 1024;
+constexpr int kGradWaves = kGradThreads / 64;
 }
 
 template <typename T, int C, int DVS>
@@ -695,7 +714,7 @@ __global__ __launch_bounds__(kGradThreads) void bwd_grad_kernel(BwdArgs<T> a) {
   constexpr int NPC = (C * WPR + kGradThreads - 1) / kGradThreads;    // pieces per thread
   __shared__ __attribute__((aligned(16))) float big[kBig];
   __shared__ float sPartG[64 * 8], sPartS[64 * 8];
-  __shared__ float sR1[64], sRowE[64], sRowF[64], sColE[64], sSd[8];
+  __shared__ float sR1[64], sRowE[64], sRowF[64], sColE[64], sSd[kGradWaves];
   __shared__ float sGam[64], sSc[64], sG2[64], sBe[64];
 
   const int e = blockIdx.x;
@@ -716,18 +735,18 @@ __global__ __launch_bounds__(kGradThreads) void bwd_grad_kernel(BwdArgs<T> a) {
   }
 
   // ---- tile ownership ----
-  const int NKT = DK / 16, wpc = 8 / NKT;  // waves per d_k column tile
+  const int NKT = DK / 16, wpc = kGradWaves / NKT;  // waves per d_k column tile
   const int ct = w % NKT, rsel = w / NKT;  // d_k column tile, row-tile residue
   const bool has_rows = rsel < NRT;
-  // lower C x C tiles of this wave: numbers w and w + 8
-  const int np = (w < NL) + (w + 8 < NL);
-  int prt[2], pct[2];
+  // lower C x C tile of this wave (at most 10 of them: C <= 64)
+  static_assert(NL <= kGradWaves, "one lower tile per wave");
+  const int np = w < NL;
+  int prt[1], pct[1];
   lower_tile(min(w, NL - 1), prt[0], pct[0]);
-  lower_tile(min(w + 8, NL - 1), prt[1], pct[1]);
-  f32x4_t W1[NRT], W2[NRT], W3[NRT], aP[2], aA[2];
+  f32x4_t W1[NRT], W2[NRT], W3[NRT], aP[1], aA[1];
 #pragma unroll
   for (int i = 0; i < NRT; ++i) W1[i] = W2[i] = W3[i] = zero4();
-  aP[0] = aP[1] = aA[0] = aA[1] = zero4();
+  aP[0] = aA[0] = zero4();
   float sd = 0.0f;  // <S, dS'> partial (one wave per d_k column tile)
   float r1acc[NPC];
 #pragma unroll
@@ -781,7 +800,7 @@ __global__ __launch_bounds__(kGradThreads) void bwd_grad_kernel(BwdArgs<T> a) {
         }
       }
 #pragma unroll
-      for (int j = 0; j < 2; ++j) {
+      for (int j = 0; j < 1; ++j) {
         if (j < np) {
           const f32x4_t yu = row4(sU + (16 * pct[j] + r) * LDV + k0);
           aP[j] = mm16(row4(sdO + (16 * prt[j] + r) * LDV + k0), yu, aP[j]);
@@ -813,7 +832,7 @@ __global__ __launch_bounds__(kGradThreads) void bwd_grad_kernel(BwdArgs<T> a) {
     }
   }
 #pragma unroll
-  for (int j = 0; j < 2; ++j) {
+  for (int j = 0; j < 1; ++j) {
     if (j < np) {
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
@@ -923,7 +942,7 @@ __global__ __launch_bounds__(kGradThreads) void bwd_grad_kernel(BwdArgs<T> a) {
     }
     const float tot_sds = group_sum(sds, 64);
     float sdsum = 0.0f;
-    for (int i = 0; i < 8; ++i) sdsum += sSd[i];
+    for (int i = 0; i < kGradWaves; ++i) sdsum += sSd[i];
     if (t == n - 1) dg += sGam[C - 1] * sdsum + tot_sds;
     // suffix sums over t' >= t: a prefix sum over the reversed lanes
     const float rev = __shfl(dg, max(n - 1 - lane, 0));
@@ -967,9 +986,7 @@ static hipError_t launch_bwd_c(const BwdProblem &b, const BwdArgs<T> &a, hipStre
   hipLaunchKernelGGL((bwd_chain_kernel<T, C>), dim3(chain_blocks), dim3(kChainThreads), 0, st, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || n_ent == 0) return e;
-  if (p.d_v >= 64)
-    hipLaunchKernelGGL((bwd_grad_kernel<T, C, 64>), dim3(n_ent), dim3(kGradThreads), 0, st, a);
-  else if (p.d_v == 32)
+  if (p.d_v >= 32)
     hipLaunchKernelGGL((bwd_grad_kernel<T, C, 32>), dim3(n_ent), dim3(kGradThreads), 0, st, a);
   else
     hipLaunchKernelGGL((bwd_grad_kernel<T, C, 16>), dim3(n_ent), dim3(kGradThreads), 0, st, a);
