@@ -38,7 +38,9 @@ projections drawn on the device, and gives each kernel's algorithmic bytes
 (every input read once, every output written once) as a fraction of HBM
 peak.
 
-``chunk_bwd`` times the backward pass (gdn_chunk_bwd) on the prefill shape.
+``chunk_bwd`` times the backward pass (gdn_chunk_bwd) on the prefill shape,
+with its products' flops as a fraction of the fp32 MFMA peak (the backward
+computes in fp32).
 
 ``kda_decode`` times the per-channel-gate decode step (one decay rate per key
 channel) on the decode shape, with its HBM fraction.
@@ -70,6 +72,7 @@ if ROOT not in sys.path:
 
 HBM_PEAK = 8.0e12            # bytes/s, MI355X HBM3E
 MFMA_BF16_PEAK = 2.5e15      # flop/s, dense bf16 MFMA
+MFMA_F32_PEAK = 157.3e12     # flop/s, dense fp32 MFMA
 
 # Algorithmic work (per unit = (sequence, value head); per token-unit):
 # q, k, v, o in bf16 (4 x 128 x 2 bytes) + alpha, beta fp32 (8 bytes).
@@ -376,9 +379,16 @@ def chunk_bwd_workload(args, gdn, gi, torch, dev, stream, evict):
 
     t = timed_calls(args, torch, stream, evict, call)
     del q, k, v, alpha, beta, d_o, ws
+    # products per (chunk of 64, value head), triangular ones at half size:
+    # 8 C d_k d_v (K S, the state update, K dS', the two dS terms, dO S^T,
+    # dY S^T, U dS'^T) + 2.5 C^2 d_v (T X, P^T dO, M^T dU, dO U^T, dY U^T)
+    # + 3 C^2 d_k (K K^T, Q K^T, (dP.Gamma) K, (dP.Gamma)^T Q, (dG + dG^T) K)
+    C, dk, dv = 64, spec.d_k, spec.d_v
+    flops = 2 * (8 * C * dk * dv + 2.5 * C * C * dv + 3 * C * C * dk) * (T // C) * B * spec.H_v
     return {"chunk_bwd": {
         "workload": f"backward pass B={B} T={T} H={spec.H_v} d=128 bf16 inputs, fp32 gradients, chunk 64",
-        "tokens_per_s": B * T / t, "us_per_call": t * 1e6,
+        "tokens_per_s": B * T / t, "us_per_call": t * 1e6, "flops": flops,
+        "mfma_f32_frac": flops / t / MFMA_F32_PEAK,
     }}
 
 

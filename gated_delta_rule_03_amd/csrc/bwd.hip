@@ -256,7 +256,10 @@ template <typename T, int C> struct ChainLds {
 };
 
 // One chunk's token-row tile (K or Q: C rows x d_k of T) as 16-byte pieces in
-// registers, then in LDS.  Rows at or past n read as zero.
+// registers, then in LDS.  Rows at or past n read as zero.  Branch-free (an
+// index past the tile is clamped onto its last piece, which then is loaded
+// and stored twice with the same value), so that the compiler can count the
+// loads still in flight exactly and wait only for these.
 template <typename T, int C> struct TileLoader {
   static constexpr int EPP = 16 / sizeof(T);
   static constexpr int MAXP = (C * 128 / EPP + kChainThreads - 1) / kChainThreads;
@@ -265,45 +268,37 @@ template <typename T, int C> struct TileLoader {
     const int ppr = DK / EPP, np = C * ppr;
 #pragma unroll
     for (int m = 0; m < MAXP; ++m) {
-      const int p = threadIdx.x + kChainThreads * m;
-      v[m] = make_uint4(0, 0, 0, 0);
-      if (p < np) {
-        const int t = p / ppr, c = (p - t * ppr) * EPP;
-        if (t < n) v[m] = *reinterpret_cast<const uint4 *>(base + int64_t(t) * row_stride + c);
-      }
+      const int p = min(int(threadIdx.x) + kChainThreads * m, np - 1);
+      const int t = p / ppr, c = (p - t * ppr) * EPP;
+      const uint4 x = *reinterpret_cast<const uint4 *>(base + int64_t(min(t, n - 1)) * row_stride + c);
+      v[m] = t < n ? x : make_uint4(0, 0, 0, 0);
     }
   }
   __device__ __forceinline__ void store(T *lds, int ldk, int DK) const {
     const int ppr = DK / EPP, np = C * ppr;
 #pragma unroll
     for (int m = 0; m < MAXP; ++m) {
-      const int p = threadIdx.x + kChainThreads * m;
-      if (p < np) {
-        const int t = p / ppr, c = (p - t * ppr) * EPP;
-        *reinterpret_cast<uint4 *>(lds + t * ldk + c) = v[m];
-      }
+      const int p = min(int(threadIdx.x) + kChainThreads * m, np - 1);
+      const int t = p / ppr, c = (p - t * ppr) * EPP;
+      *reinterpret_cast<uint4 *>(lds + t * ldk + c) = v[m];
     }
   }
 };
 
-// One chunk's gamma, s and beta (thread t < C holds token t's).
+// One chunk's gamma, s and beta: thread t holds token (t mod 64)'s.
 struct GateLoader {
   float gam = 0.0f, sc = 0.0f, be = 0.0f;
   __device__ __forceinline__ void load(const float *gate) {
-    const int t = threadIdx.x;
-    if (t < 64) {
-      gam = gate[kGateGamma + t];
-      sc = gate[kGateS + t];
-      be = gate[kGateBeta + t];
-    }
+    const int t = threadIdx.x & 63;
+    gam = gate[kGateGamma + t];
+    sc = gate[kGateS + t];
+    be = gate[kGateBeta + t];
   }
-  __device__ __forceinline__ void store(float *sgate, int C) const {
-    const int t = threadIdx.x;
-    if (t < C) {
-      sgate[t] = gam;
-      sgate[64 + t] = sc;
-      sgate[128 + t] = be;
-    }
+  __device__ __forceinline__ void store(float *sgate) const {
+    const int t = threadIdx.x & 63;
+    sgate[t] = gam;
+    sgate[64 + t] = sc;
+    sgate[128 + t] = be;
   }
 };
 
@@ -363,14 +358,12 @@ __device__ void fwd_chain(const BwdArgs<T> &a, int u, int cb, char *smem) {
     const int tok0 = start + cc * C, n = min(C, end - tok0);
 #pragma unroll
     for (int m = 0; m < 2; ++m) {
-      vcur[m] = zero4();
-      if (m < nmine) {
-        const int ct = (w + 4 * m) / NRT;
+      const int ct = min((w + 4 * m) / NRT, NCT - 1);
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const int t = 16 * rt + 4 * g + q;
-          if (t < n) vcur[m][q] = to_f32(a.v[int64_t(tok0 + t) * vrow + int64_t(h) * DV + c0 + 16 * ct + r]);
-        }
+      for (int q = 0; q < 4; ++q) {
+        const int t = 16 * rt + 4 * g + q;
+        const float x = to_f32(a.v[int64_t(tok0 + min(t, n - 1)) * vrow + int64_t(h) * DV + c0 + 16 * ct + r]);
+        vcur[m][q] = t < n ? x : 0.0f;
       }
     }
   };
@@ -388,7 +381,7 @@ __device__ void fwd_chain(const BwdArgs<T> &a, int u, int cb, char *smem) {
   load_v(0);
   load_m(0);
   kl.store(sK, LDK, DK);
-  gl.store(sgate, C);
+  gl.store(sgate);
 
   for (int cc = 0; cc < n_chunks; ++cc) {
     float *ent = a.ent + (int64_t(c_first + cc) * a.H_v + h) * a.ent_floats;
@@ -406,8 +399,8 @@ __device__ void fwd_chain(const BwdArgs<T> &a, int u, int cb, char *smem) {
         }
       }
     }
-    const bool more = cc + 1 < n_chunks;
-    if (more) load_tiles(cc + 1);
+    const int nx = min(cc + 1, n_chunks - 1);  // the next chunk (the last one reloads itself)
+    load_tiles(nx);
     lds_sync();
     // X = V - diag(gamma) K S;  Y = diag(beta) X
 #pragma unroll
@@ -427,7 +420,7 @@ __device__ void fwd_chain(const BwdArgs<T> &a, int u, int cb, char *smem) {
         }
       }
     }
-    if (more) load_v(cc + 1);
+    load_v(nx);
     lds_sync();
     // U = M Y;  diag(s) U for the state update
 #pragma unroll
@@ -446,7 +439,7 @@ __device__ void fwd_chain(const BwdArgs<T> &a, int u, int cb, char *smem) {
         }
       }
     }
-    if (more) load_m(cc + 1);
+    load_m(nx);
     lds_sync();
     // S <- gamma_C S + K^T diag(s) U
     const float gC = sgate[C - 1];
@@ -464,10 +457,8 @@ __device__ void fwd_chain(const BwdArgs<T> &a, int u, int cb, char *smem) {
       }
     }
     lds_sync();
-    if (more) {
-      kl.store(sK, LDK, DK);
-      gl.store(sgate, C);
-    }
+    kl.store(sK, LDK, DK);
+    gl.store(sgate);
   }
 }
 
@@ -483,7 +474,7 @@ __device__ void rev_chain(const BwdArgs<T> &a, int u, int cb, char *smem) {
   float *sdS = reinterpret_cast<float *>(smem + 2 * Lds::kTile);
   float *sdO = sdS + 128 * LDB;
   float *sdU = sdO + C * LDB;
-  float *sdX = sdU + C * LDB;  // diag(gamma) dX
+  float *sdX = sdU + C * LDB;  // -diag(gamma) dX
   float *sgate = sdX + C * LDB;
   int s, h, start, end, c_first, n_chunks;
   unit_of(a.geo, a.H_v, u, s, h, start, end, c_first, n_chunks);
@@ -524,13 +515,11 @@ __device__ void rev_chain(const BwdArgs<T> &a, int u, int cb, char *smem) {
       gl.load(a.ent + (int64_t(c_first + cc) * a.H_v + h) * a.ent_floats + L.gate);
 #pragma unroll
       for (int m = 0; m < MAXO; ++m) {
-        const int p = tid + kChainThreads * m;
-        ocur[m] = make_uint4(0, 0, 0, 0);
-        if (p < C * oppr) {
-          const int t = p / oppr, c = (p - t * oppr) * EPP;
-          if (t < n)
-            ocur[m] = *reinterpret_cast<const uint4 *>(a.d_o + int64_t(tok0 + t) * vrow + int64_t(h) * DV + c0 + c);
-        }
+        const int p = min(tid + kChainThreads * m, C * oppr - 1);
+        const int t = p / oppr, c = (p - t * oppr) * EPP;
+        const uint4 x =
+            *reinterpret_cast<const uint4 *>(a.d_o + int64_t(tok0 + min(t, n - 1)) * vrow + int64_t(h) * DV + c0 + c);
+        ocur[m] = t < n ? x : make_uint4(0, 0, 0, 0);
       }
     };
     // loaded a chunk ahead, right after their last use
@@ -547,13 +536,11 @@ __device__ void rev_chain(const BwdArgs<T> &a, int u, int cb, char *smem) {
     auto store_do = [&]() {
 #pragma unroll
       for (int m = 0; m < MAXO; ++m) {
-        const int p = tid + kChainThreads * m;
-        if (p < C * oppr) {
-          const int t = p / oppr, c = (p - t * oppr) * EPP;
-          const T *x = reinterpret_cast<const T *>(&ocur[m]);
+        const int p = min(tid + kChainThreads * m, C * oppr - 1);
+        const int t = p / oppr, c = (p - t * oppr) * EPP;
+        const T *x = reinterpret_cast<const T *>(&ocur[m]);
 #pragma unroll
-          for (int j = 0; j < EPP; ++j) sdO[t * LDB + c + j] = to_f32(x[j]);
-        }
+        for (int j = 0; j < EPP; ++j) sdO[t * LDB + c + j] = to_f32(x[j]);
       }
     };
     load_tiles(n_chunks - 1);
@@ -561,7 +548,7 @@ __device__ void rev_chain(const BwdArgs<T> &a, int u, int cb, char *smem) {
     load_m(n_chunks - 1);
     kl.store(sK, LDK, DK);
     ql.store(sQ, LDK, DK);
-    gl.store(sgate, C);
+    gl.store(sgate);
     store_do();
 
     for (int cc = n_chunks - 1; cc >= 0; --cc) {
@@ -581,8 +568,8 @@ __device__ void rev_chain(const BwdArgs<T> &a, int u, int cb, char *smem) {
           }
         }
       }
-      const bool more = cc > 0;
-      if (more) load_tiles(cc - 1);
+      const int nx = max(cc - 1, 0);  // the next chunk back (the first one reloads itself)
+      load_tiles(nx);
       lds_sync();
       // dU = P^T dO + diag(s) K dS'
 #pragma unroll
@@ -603,7 +590,7 @@ __device__ void rev_chain(const BwdArgs<T> &a, int u, int cb, char *smem) {
           }
         }
       }
-      if (more) load_p(cc - 1);
+      load_p(nx);
       lds_sync();
       // dY = M^T dU;  dv = dX = diag(beta) dY
 #pragma unroll
@@ -620,11 +607,11 @@ __device__ void rev_chain(const BwdArgs<T> &a, int u, int cb, char *smem) {
             const float dx = sgate[128 + t] * acc[q];
             ent[L.dY + int64_t(t) * DV + c0 + col] = acc[q];
             if (t < n) a.dv[int64_t(tok0 + t) * vrow + int64_t(h) * DV + c0 + col] = dx;
-            sdX[t * LDB + col] = sgate[t] * dx;
+            sdX[t * LDB + col] = -sgate[t] * dx;
           }
         }
       }
-      if (more) load_m(cc - 1);
+      load_m(nx);
       lds_sync();
       // dS <- gamma_C dS' + Q^T diag(gamma) dO - K^T diag(gamma) dX
       const float gC = sgate[C - 1];
@@ -641,18 +628,16 @@ __device__ void rev_chain(const BwdArgs<T> &a, int u, int cb, char *smem) {
 #pragma unroll
             for (int j = 0; j < 4; ++j) xq[j] *= sgate[t0 + j];
             acc = mm16(xq, col4(sdO + t0 * LDB + 16 * ct + r, LDB), acc);
-            acc = mm16(-col4(sK + t0 * LDK + 16 * kt + r, LDK), col4(sdX + t0 * LDB + 16 * ct + r, LDB), acc);
+            acc = mm16(col4(sK + t0 * LDK + 16 * kt + r, LDK), col4(sdX + t0 * LDB + 16 * ct + r, LDB), acc);
           }
           accS[m] = acc;
         }
       }
       lds_sync();
-      if (more) {
-        kl.store(sK, LDK, DK);
-        ql.store(sQ, LDK, DK);
-        gl.store(sgate, C);
-        store_do();
-      }
+      kl.store(sK, LDK, DK);
+      ql.store(sQ, LDK, DK);
+      gl.store(sgate);
+      store_do();
     }
   }
   if (a.dh0) {
