@@ -126,6 +126,38 @@ __device__ __forceinline__ void lower_tile(int k, int &rt, int &ct) {
   ct = k;
 }
 
+constexpr int kChainThreads = 256;
+
+// One chunk's token-row tile (K or Q: C rows x d_k of T) as 16-byte pieces in
+// registers, then in LDS.  Rows at or past n read as zero.  Branch-free (an
+// index past the tile is clamped onto its last piece, which then is loaded
+// and stored twice with the same value), so that the compiler can count the
+// loads still in flight exactly and wait only for these.
+template <typename T, int C> struct TileLoader {
+  static constexpr int EPP = 16 / sizeof(T);
+  static constexpr int MAXP = (C * 128 / EPP + kChainThreads - 1) / kChainThreads;
+  uint4 v[MAXP];
+  __device__ __forceinline__ void load(const T *base, int64_t row_stride, int n, int DK) {
+    const int ppr = DK / EPP, np = C * ppr;
+#pragma unroll
+    for (int m = 0; m < MAXP; ++m) {
+      const int p = min(int(threadIdx.x) + kChainThreads * m, np - 1);
+      const int t = p / ppr, c = (p - t * ppr) * EPP;
+      const uint4 x = *reinterpret_cast<const uint4 *>(base + int64_t(min(t, n - 1)) * row_stride + c);
+      v[m] = t < n ? x : make_uint4(0, 0, 0, 0);
+    }
+  }
+  __device__ __forceinline__ void store(T *lds, int ldk, int DK) const {
+    const int ppr = DK / EPP, np = C * ppr;
+#pragma unroll
+    for (int m = 0; m < MAXP; ++m) {
+      const int p = min(int(threadIdx.x) + kChainThreads * m, np - 1);
+      const int t = p / ppr, c = (p - t * ppr) * EPP;
+      *reinterpret_cast<uint4 *>(lds + t * ldk + c) = v[m];
+    }
+  }
+};
+
 }  // namespace
 
 // ---------------------------------------------------------------------------
@@ -140,51 +172,69 @@ __global__ __launch_bounds__(256) void bwd_factor_kernel(BwdArgs<T> a) {
   if (!a.geo.locate(slot, s, tok0, n)) return;
   const int hq = h / a.group, DK = a.d_k;
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, r = lane & 15, g = lane >> 4;
-  __shared__ __attribute__((aligned(16))) float sKK[C * LD], sQK[C * LD], sA[C * LD], sM[C * LD];
+  // LDS: A; then the chunk's K and Q rows, whose space M takes once the
+  // products below are done
+  constexpr int LDK = 128 + 16 / sizeof(T);
+  constexpr int kTileBytes = C * LDK * sizeof(T);
+  constexpr int kBufBytes = 2 * kTileBytes > C * LD * 4 ? 2 * kTileBytes : C * LD * 4;
+  __shared__ __attribute__((aligned(16))) float sA[C * LD];
+  __shared__ __attribute__((aligned(16))) char sBuf[kBufBytes];
   __shared__ float sg[64], sb[64];
+  T *sK = reinterpret_cast<T *>(sBuf), *sQ = reinterpret_cast<T *>(sBuf + kTileBytes);
+  float *sM = reinterpret_cast<float *>(sBuf);
   float *ent = a.ent + int64_t(e) * a.ent_floats;
   const BwdEntry L(C, DK, a.d_v);
+  const int64_t krow = int64_t(a.H_qk) * DK;
 
-  if (w == 0) {  // chunk-local cumulative log2 gate; padded slots add 0
-    const bool in = lane < n;
-    const int64_t gi = int64_t(tok0 + min(lane, n - 1)) * a.H_v + h;
-    const float g2 = wave_prefix_sum(in ? clamped_log2(a.alpha[gi]) : 0.0f);
-    if (lane < C) {
-      sg[lane] = g2;
-      sb[lane] = in ? a.beta[gi] : 0.0f;
+  {
+    TileLoader<T, C> kl, ql;
+    kl.load(a.k + int64_t(tok0) * krow + int64_t(hq) * DK, krow, n, DK);
+    ql.load(a.q + int64_t(tok0) * krow + int64_t(hq) * DK, krow, n, DK);
+    if (w == 0) {  // chunk-local cumulative log2 gate; padded slots add 0
+      const bool in = lane < n;
+      const int64_t gi = int64_t(tok0 + min(lane, n - 1)) * a.H_v + h;
+      const float al = a.alpha[gi], be = a.beta[gi];
+      const float g2 = wave_prefix_sum(in ? clamped_log2(al) : 0.0f);
+      if (lane < C) {
+        sg[lane] = g2;
+        sb[lane] = in ? be : 0.0f;
+      }
     }
+    for (int i = tid; i < C * LD; i += 256) sA[i] = 0.0f;
+    for (int idx = tid; idx < C * C; idx += 256) {  // P and Gamma . K K^T are zero above the diagonal tiles
+      const int t = idx / C, i = idx - t * C;
+      if ((i >> 4) > (t >> 4)) {
+        ent[L.P + idx] = 0.0f;
+        ent[L.G + idx] = 0.0f;
+      }
+    }
+    kl.store(sK, LDK, DK);
+    ql.store(sQ, LDK, DK);
   }
-  for (int i = tid; i < C * LD; i += 256) sM[i] = 0.0f;
-  // lower tiles of K K^T and Q K^T (contraction over d_k), operands from global
+  __syncthreads();
+  // lower tiles of K K^T and Q K^T (contraction over d_k); each leaves as
+  // Gamma . K K^T (strict lower; A = diag(beta) times it into LDS) or as
+  // P = Gamma . Q K^T (lower)
   for (int job = w; job < 2 * NL; job += 4) {
     const int mat = job / NL;
     int rt, ct;
     lower_tile(job - mat * NL, rt, ct);
-    const int ta = 16 * rt + r, tb = 16 * ct + r;
-    const T *pa = (mat ? a.q : a.k) + (int64_t(tok0 + min(ta, n - 1)) * a.H_qk + hq) * DK + 4 * g;
-    const T *pb = a.k + (int64_t(tok0 + min(tb, n - 1)) * a.H_qk + hq) * DK + 4 * g;
+    const T *pa = (mat ? sQ : sK) + (16 * rt + r) * LDK + 4 * g;
+    const T *pb = sK + (16 * ct + r) * LDK + 4 * g;
     f32x4_t acc = zero4();
-    for (int k0 = 0; k0 < DK; k0 += 16) {
-      const f32x4_t xr = ta < n ? row4(pa + k0) : zero4();
-      const f32x4_t yt = tb < n ? row4(pb + k0) : zero4();
-      acc = mm16(xr, yt, acc);
-    }
-    float *dst = mat ? sQK : sKK;
+    for (int k0 = 0; k0 < DK; k0 += 16) acc = mm16(row4(pa + k0), row4(pb + k0), acc);
 #pragma unroll
-    for (int q = 0; q < 4; ++q) dst[(16 * rt + 4 * g + q) * LD + 16 * ct + r] = acc[q];
-  }
-  __syncthreads();
-  for (int idx = tid; idx < C * C; idx += 256) {
-    const int t = idx / C, i = idx - t * C;
-    float gkk = 0.0f, p = 0.0f;
-    if (i <= t) {
-      const float gam = fast_exp2(sg[t] - sg[i]);
-      p = gam * sQK[t * LD + i];
-      if (i < t) gkk = gam * sKK[t * LD + i];
+    for (int q = 0; q < 4; ++q) {
+      const int t = 16 * rt + 4 * g + q, i = 16 * ct + r;
+      const float gam = i <= t ? fast_exp2(sg[t] - sg[i]) : 0.0f;
+      if (mat) {
+        ent[L.P + t * C + i] = gam * acc[q];
+      } else {
+        const float gkk = i < t ? gam * acc[q] : 0.0f;
+        ent[L.G + t * C + i] = gkk;
+        sA[t * LD + i] = sb[t] * gkk;
+      }
     }
-    sA[t * LD + i] = sb[t] * gkk;
-    ent[L.P + idx] = p;
-    ent[L.G + idx] = gkk;
   }
   if (tid < C) {
     const float gl = sg[C - 1];
@@ -193,6 +243,8 @@ __global__ __launch_bounds__(256) void bwd_factor_kernel(BwdArgs<T> a) {
     ent[L.gate + kGateLog2 + tid] = sg[tid];
     ent[L.gate + kGateBeta + tid] = sb[tid];
   }
+  __syncthreads();  // K and Q are dead: M takes their space
+  for (int i = tid; i < C * LD; i += 256) sM[i] = 0.0f;
   __syncthreads();
   // (I + A)^-1 by 16 x 16 blocks: the diagonal blocks by forward substitution
   // (lane group g inverts block g, lane r owns column r) ...
@@ -240,8 +292,6 @@ __global__ __launch_bounds__(256) void bwd_factor_kernel(BwdArgs<T> a) {
 // ---------------------------------------------------------------------------
 namespace {
 
-constexpr int kChainThreads = 256;
-
 template <typename T, int C> struct ChainLds {
   static constexpr int LDK = 128 + 16 / sizeof(T);  // K / Q rows (elements of T), d_k <= 128
   static constexpr int LDB = 32 + 4;                // column-block rows (floats)
@@ -253,36 +303,6 @@ template <typename T, int C> struct ChainLds {
   static constexpr int kFwd = kTile + kState + 2 * kCol + kGate;
   static constexpr int kRev = 2 * kTile + kState + 3 * kCol + kGate;
   static constexpr int kBytes = kFwd > kRev ? kFwd : kRev;
-};
-
-// One chunk's token-row tile (K or Q: C rows x d_k of T) as 16-byte pieces in
-// registers, then in LDS.  Rows at or past n read as zero.  Branch-free (an
-// index past the tile is clamped onto its last piece, which then is loaded
-// and stored twice with the same value), so that the compiler can count the
-// loads still in flight exactly and wait only for these.
-template <typename T, int C> struct TileLoader {
-  static constexpr int EPP = 16 / sizeof(T);
-  static constexpr int MAXP = (C * 128 / EPP + kChainThreads - 1) / kChainThreads;
-  uint4 v[MAXP];
-  __device__ __forceinline__ void load(const T *base, int64_t row_stride, int n, int DK) {
-    const int ppr = DK / EPP, np = C * ppr;
-#pragma unroll
-    for (int m = 0; m < MAXP; ++m) {
-      const int p = min(int(threadIdx.x) + kChainThreads * m, np - 1);
-      const int t = p / ppr, c = (p - t * ppr) * EPP;
-      const uint4 x = *reinterpret_cast<const uint4 *>(base + int64_t(min(t, n - 1)) * row_stride + c);
-      v[m] = t < n ? x : make_uint4(0, 0, 0, 0);
-    }
-  }
-  __device__ __forceinline__ void store(T *lds, int ldk, int DK) const {
-    const int ppr = DK / EPP, np = C * ppr;
-#pragma unroll
-    for (int m = 0; m < MAXP; ++m) {
-      const int p = min(int(threadIdx.x) + kChainThreads * m, np - 1);
-      const int t = p / ppr, c = (p - t * ppr) * EPP;
-      *reinterpret_cast<uint4 *>(lds + t * ldk + c) = v[m];
-    }
-  }
 };
 
 // One chunk's gamma, s and beta: thread t holds token (t mod 64)'s.
@@ -754,8 +774,8 @@ __global__ __launch_bounds__(kGradThreads) void bwd_grad_kernel(BwdArgs<T> a) {
       float part = 0.0f;
       if (p < C * WPR) {
         const int t = p / WPR, c = (p - t * WPR) * 4;
-        f32x4_t o = zero4();
-        if (t < n) o = row4(a.d_o + int64_t(tok0 + t) * vrow + int64_t(h) * DV + dv0 + c);
+        const f32x4_t od = row4(a.d_o + int64_t(tok0 + min(t, n - 1)) * vrow + int64_t(h) * DV + dv0 + c);
+        const f32x4_t o = t < n ? od : zero4();
         const f32x4_t y = row4(ent + L.dY + int64_t(t) * DV + dv0 + c);
         const f32x4_t uu = row4(ent + L.U + int64_t(t) * DV + dv0 + c);
         const f32x4_t x = row4(ent + L.X + int64_t(t) * DV + dv0 + c);
@@ -836,8 +856,9 @@ __global__ __launch_bounds__(kGradThreads) void bwd_grad_kernel(BwdArgs<T> a) {
     for (int j = 0; j < 4; ++j) {
       const int t = 16 * i + 4 * g + j;
       const int64_t o = int64_t(tok0 + min(t, n - 1)) * krow + int64_t(hq) * DK + 16 * ct + r;
-      kf[i][j] = t < n ? to_f32(a.k[o]) : 0.0f;
-      qf[i][j] = t < n ? to_f32(a.q[o]) : 0.0f;
+      const float kv = to_f32(a.k[o]), qv = to_f32(a.q[o]);
+      kf[i][j] = t < n ? kv : 0.0f;
+      qf[i][j] = t < n ? qv : 0.0f;
     }
   }
   __syncthreads();
