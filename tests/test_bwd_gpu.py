@@ -8,7 +8,8 @@ input values (bf16 widens exactly), so both dtypes are held to the fp32 bar
 of 1e-4.  Cases: uniform and packed batches (empty and one-token sequences,
 ragged last chunks), grouped heads, h0 and dhT, chunks of 16, 32 and 64, the
 sizes d_k, d_v in {16, ..., 128}, bf16 inputs, and run-to-run bitwise
-equality.
+equality; and the prefill shape at full size (B=4, T=4096, H=16, d=128,
+bf16, chunk 64: the launch the benchmark times), checked on sampled units.
 """
 import numpy as np
 import pytest
@@ -119,3 +120,28 @@ def test_chunk_bwd_chunk_sizes_agree_and_repeat_bitwise(gdn):
     for a, b in zip(outs[2], again):
         assert np.array_equal(a, b)
     torch.cuda.synchronize()
+
+
+def test_chunk_bwd_prefill_shape_sampled_units(gdn):
+    """The prefill workload at full size through one call; three units (first,
+    last and one between, all 64 chunks of each) against the gradient oracle.
+    Units are independent (one value head per query/key head here), so the
+    oracle runs on those units alone."""
+    import torch
+    spec = gi.config(2)
+    w = gi.generate(spec)
+    B, T, H = w.q.shape[0], w.q.shape[1], w.q.shape[2]
+    do32 = gi.random_state((B, T, H, spec.d_v), seed=spec.seed + 11)
+    do_bits = gi.f32_to_bf16_bits(do32)
+    log(f"[bwd] prefill shape B={B} T={T} H={H} d={spec.d_k} bf16 chunk 64")
+    got = gdn.chunk_bwd(dev_tensor(w.q), dev_tensor(w.k), dev_tensor(w.v), dev_tensor(w.alpha),
+                        dev_tensor(w.beta), dev_tensor(do_bits), chunk=64)
+    torch.cuda.synchronize()
+    got = [host_f64(g) for g in got]
+    do_ref = gi.bf16_bits_to_f32(do_bits)
+    for b, h in ((0, 0), (2, 7), (B - 1, H - 1)):
+        sl = (slice(b, b + 1), slice(None), slice(h, h + 1))
+        ref = ograd.backward(w.q[sl], w.k[sl], w.v[sl], w.alpha[sl], w.beta[sl], do_ref[sl], None)
+        mine = [g[sl] for g in got[:5]] + [got[5][b:b + 1, h:h + 1]]
+        log(f"    unit (b={b}, h={h})")
+        check(mine, ref, None)
