@@ -294,16 +294,35 @@ namespace {
 
 template <typename T, int C> struct ChainLds {
   static constexpr int LDK = 128 + 16 / sizeof(T);  // K / Q rows (elements of T), d_k <= 128
-  static constexpr int LDB = 32 + 4;                // column-block rows (floats)
+  static constexpr int LDT = 128 + 4;               // transposed state: [column][d_k] floats
+  static constexpr int LDC = C + 4;                 // transposed C x CB operands: [column][token] floats
   static constexpr int kTile = C * LDK * sizeof(T);
-  static constexpr int kState = 128 * LDB * 4;
-  static constexpr int kCol = C * LDB * 4;
+  static constexpr int kState = 32 * LDT * 4;
+  static constexpr int kCol = 32 * LDC * 4;
   static constexpr int kGate = 3 * 64 * 4;
-  // forward: K, S, Y, diag(s) U, gates; backward: K, Q, dS, dO, dU, diag(gamma) dX, gates
+  // forward: K, S^T, Y^T, (diag(s) U)^T, gates; backward: K, Q, dS^T, dO^T,
+  // dU^T, (-diag(gamma) dX)^T, gates
   static constexpr int kFwd = kTile + kState + 2 * kCol + kGate;
   static constexpr int kRev = 2 * kTile + kState + 3 * kCol + kGate;
   static constexpr int kBytes = kFwd > kRev ? kFwd : kRev;
 };
+
+// A fragment of K^T (or Q^T) from a row-major token-row tile in LDS: lane
+// (r, g) gets tile[t0 + 4g + j][col0 + r], j = 0..3.  For bf16 one
+// ds_read_b64_tr_b16: lane L of each 16-lane group addresses row
+// t0 + 4g + L / 4, columns col0 + 4 (L % 4) .. + 3, and lane r then holds
+// column col0 + r of the four rows.
+template <typename T>
+__device__ __forceinline__ f32x4_t tile_colfrag(const T *tile, int ld, int t0, int col0, int r, int g);
+template <>
+__device__ __forceinline__ f32x4_t tile_colfrag<bf16_t>(const bf16_t *tile, int ld, int t0, int col0, int r, int g) {
+  const bf16_t *p = tile + (t0 + 4 * g + (r >> 2)) * ld + col0 + 4 * (r & 3);
+  return __builtin_convertvector(lds_read_tr16(lds_ptr((void *)p)), f32x4_t);
+}
+template <>
+__device__ __forceinline__ f32x4_t tile_colfrag<float>(const float *tile, int ld, int t0, int col0, int r, int g) {
+  return col4(tile + (t0 + 4 * g) * ld + col0 + r, ld);
+}
 
 // One chunk's gamma, s and beta: thread t holds token (t mod 64)'s.
 struct GateLoader {
@@ -336,22 +355,22 @@ __device__ __forceinline__ void unit_of(const SeqGeom &geo, int H_v, int u, int 
 template <typename T, int C>
 __device__ void fwd_chain(const BwdArgs<T> &a, int u, int cb, char *smem) {
   using Lds = ChainLds<T, C>;
-  constexpr int NRT = C / 16, LDK = Lds::LDK, LDB = Lds::LDB;
+  constexpr int NRT = C / 16, LDK = Lds::LDK, LDT = Lds::LDT, LDC = Lds::LDC;
   const int DK = a.d_k, DV = a.d_v, CB = min(32, DV), c0 = cb * CB;
   const int NKT = DK / 16, NCT = CB / 16;
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, r = lane & 15, g = lane >> 4;
   T *sK = reinterpret_cast<T *>(smem);
-  float *sS = reinterpret_cast<float *>(smem + Lds::kTile);
-  float *sY = sS + 128 * LDB;
-  float *sU = sY + C * LDB;
-  float *sgate = sU + C * LDB;  // gamma[64], s[64], beta[64]
+  float *sSt = reinterpret_cast<float *>(smem + Lds::kTile);  // S^T
+  float *sYt = sSt + 32 * LDT;                                  // (diag(beta) X)^T
+  float *sUt = sYt + 32 * LDC;                                  // (diag(s) U)^T
+  float *sgate = sUt + 32 * LDC;                                // gamma[64], s[64], beta[64]
   int s, h, start, end, c_first, n_chunks;
   unit_of(a.geo, a.H_v, u, s, h, start, end, c_first, n_chunks);
   const int hq = h / a.group;
   const BwdEntry L(C, DK, DV);
   const int64_t krow = int64_t(a.H_qk) * DK, vrow = int64_t(a.H_v) * DV;
 
-  // this wave's C x CB tiles (one row tile, up to two column tiles) and state tiles
+  // this wave's C x CB tiles (one row tile, column tiles ct0 and ct0 + 1) and state tiles
   const int rt = w % NRT;
   const int nmine = (w < NRT * NCT) ? ((w + 4 < NRT * NCT) ? 2 : 1) : 0;
   const int nst = NKT * NCT;
@@ -405,57 +424,61 @@ __device__ void fwd_chain(const BwdArgs<T> &a, int u, int cb, char *smem) {
 
   for (int cc = 0; cc < n_chunks; ++cc) {
     float *ent = a.ent + (int64_t(c_first + cc) * a.H_v + h) * a.ent_floats;
-    // the state entering this chunk: to LDS (operand of K S) and to the entry
+    // the state entering this chunk: to LDS, transposed (operand of K S), and to the entry
 #pragma unroll
     for (int m = 0; m < 4; ++m) {
       const int i = w + 4 * m;
       if (i < nst) {
         const int kt = i % NKT, ct = i / NKT;
+        *reinterpret_cast<f32x4_t *>(sSt + (16 * ct + r) * LDT + 16 * kt + 4 * g) = accS[m];
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const int row = 16 * kt + 4 * g + q, col = 16 * ct + r;
-          sS[row * LDB + col] = accS[m][q];
-          ent[L.S + int64_t(row) * DV + c0 + col] = accS[m][q];
-        }
+        for (int q = 0; q < 4; ++q)
+          ent[L.S + int64_t(16 * kt + 4 * g + q) * DV + c0 + 16 * ct + r] = accS[m][q];
       }
     }
     const int nx = min(cc + 1, n_chunks - 1);  // the next chunk (the last one reloads itself)
     load_tiles(nx);
     lds_sync();
     // X = V - diag(gamma) K S;  Y = diag(beta) X
+    if (nmine > 0) {
+      f32x4_t acc[2] = {zero4(), zero4()};
 #pragma unroll
-    for (int m = 0; m < 2; ++m) {
-      if (m < nmine) {
-        const int ct = (w + 4 * m) / NRT;
-        f32x4_t acc = zero4();
-        for (int k0 = 0; k0 < DK; k0 += 16)
-          acc = mm16(row4(sK + (16 * rt + r) * LDK + k0 + 4 * g), col4(sS + (k0 + 4 * g) * LDB + 16 * ct + r, LDB),
-                     acc);
+      for (int kk = 0; kk < 8; ++kk) {
+        if (16 * kk < DK) {
+          const f32x4_t xr = row4(sK + (16 * rt + r) * LDK + 16 * kk + 4 * g);
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const int t = 16 * rt + 4 * g + q, col = 16 * ct + r;
-          const float x = vcur[m][q] - sgate[t] * acc[q];
-          ent[L.X + int64_t(t) * DV + c0 + col] = x;
-          sY[t * LDB + col] = sgate[128 + t] * x;
+          for (int m = 0; m < 2; ++m)
+            if (m < nmine)
+              acc[m] = mm16(xr, row4(sSt + (16 * ((w + 4 * m) / NRT) + r) * LDT + 16 * kk + 4 * g), acc[m]);
+        }
+      }
+      const f32x4_t gam = row4(sgate + 16 * rt + 4 * g), be = row4(sgate + 128 + 16 * rt + 4 * g);
+#pragma unroll
+      for (int m = 0; m < 2; ++m) {
+        if (m < nmine) {
+          const int col = 16 * ((w + 4 * m) / NRT) + r;
+          const f32x4_t x = vcur[m] - gam * acc[m];
+#pragma unroll
+          for (int q = 0; q < 4; ++q) ent[L.X + int64_t(16 * rt + 4 * g + q) * DV + c0 + col] = x[q];
+          *reinterpret_cast<f32x4_t *>(sYt + col * LDC + 16 * rt + 4 * g) = be * x;
         }
       }
     }
     load_v(nx);
     lds_sync();
     // U = M Y;  diag(s) U for the state update
+    if (nmine > 0) {
+      const f32x4_t sc = row4(sgate + 64 + 16 * rt + 4 * g);
 #pragma unroll
-    for (int m = 0; m < 2; ++m) {
-      if (m < nmine) {
-        const int ct = (w + 4 * m) / NRT;
-        f32x4_t acc = zero4();
+      for (int m = 0; m < 2; ++m) {
+        if (m < nmine) {
+          const int col = 16 * ((w + 4 * m) / NRT) + r;
+          f32x4_t acc = zero4();
 #pragma unroll
-        for (int kb = 0; kb < NRT; ++kb)
-          acc = mm16(mcur[kb], col4(sY + (16 * kb + 4 * g) * LDB + 16 * ct + r, LDB), acc);
+          for (int kb = 0; kb < NRT; ++kb) acc = mm16(mcur[kb], row4(sYt + col * LDC + 16 * kb + 4 * g), acc);
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const int t = 16 * rt + 4 * g + q, col = 16 * ct + r;
-          ent[L.U + int64_t(t) * DV + c0 + col] = acc[q];
-          sU[t * LDB + col] = sgate[64 + t] * acc[q];
+          for (int q = 0; q < 4; ++q) ent[L.U + int64_t(16 * rt + 4 * g + q) * DV + c0 + col] = acc[q];
+          *reinterpret_cast<f32x4_t *>(sUt + col * LDC + 16 * rt + 4 * g) = sc * acc;
         }
       }
     }
@@ -471,8 +494,8 @@ __device__ void fwd_chain(const BwdArgs<T> &a, int u, int cb, char *smem) {
         f32x4_t acc = accS[m] * gC;
 #pragma unroll
         for (int kb = 0; kb < NRT; ++kb)
-          acc = mm16(col4(sK + (16 * kb + 4 * g) * LDK + 16 * kt + r, LDK),
-                     col4(sU + (16 * kb + 4 * g) * LDB + 16 * ct + r, LDB), acc);
+          acc = mm16(tile_colfrag(sK, LDK, 16 * kb, 16 * kt, r, g),
+                     row4(sUt + (16 * ct + r) * LDC + 16 * kb + 4 * g), acc);
         accS[m] = acc;
       }
     }
@@ -485,17 +508,17 @@ __device__ void fwd_chain(const BwdArgs<T> &a, int u, int cb, char *smem) {
 template <typename T, int C>
 __device__ void rev_chain(const BwdArgs<T> &a, int u, int cb, char *smem) {
   using Lds = ChainLds<T, C>;
-  constexpr int NRT = C / 16, LDK = Lds::LDK, LDB = Lds::LDB;
+  constexpr int NRT = C / 16, LDK = Lds::LDK, LDT = Lds::LDT, LDC = Lds::LDC;
   const int DK = a.d_k, DV = a.d_v, CB = min(32, DV), c0 = cb * CB;
   const int NKT = DK / 16, NCT = CB / 16;
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, r = lane & 15, g = lane >> 4;
   T *sK = reinterpret_cast<T *>(smem);
   T *sQ = reinterpret_cast<T *>(smem + Lds::kTile);
-  float *sdS = reinterpret_cast<float *>(smem + 2 * Lds::kTile);
-  float *sdO = sdS + 128 * LDB;
-  float *sdU = sdO + C * LDB;
-  float *sdX = sdU + C * LDB;  // -diag(gamma) dX
-  float *sgate = sdX + C * LDB;
+  float *sdSt = reinterpret_cast<float *>(smem + 2 * Lds::kTile);  // dS'^T
+  float *sdOt = sdSt + 32 * LDT;                                     // dO^T
+  float *sdUt = sdOt + 32 * LDC;                                     // dU^T
+  float *sdXt = sdUt + 32 * LDC;                                     // (-diag(gamma) dX)^T
+  float *sgate = sdXt + 32 * LDC;
   int s, h, start, end, c_first, n_chunks;
   unit_of(a.geo, a.H_v, u, s, h, start, end, c_first, n_chunks);
   const int hq = h / a.group;
@@ -553,14 +576,14 @@ __device__ void rev_chain(const BwdArgs<T> &a, int u, int cb, char *smem) {
 #pragma unroll
       for (int kb = 0; kb < NRT; ++kb) mcur[kb] = col4(ent + L.M + (16 * kb + 4 * g) * C + 16 * rt + r, C);
     };
-    auto store_do = [&]() {
+    auto store_do = [&]() {  // transposed: dO^T[column][token]
 #pragma unroll
       for (int m = 0; m < MAXO; ++m) {
         const int p = min(tid + kChainThreads * m, C * oppr - 1);
         const int t = p / oppr, c = (p - t * oppr) * EPP;
         const T *x = reinterpret_cast<const T *>(&ocur[m]);
 #pragma unroll
-        for (int j = 0; j < EPP; ++j) sdO[t * LDB + c + j] = to_f32(x[j]);
+        for (int j = 0; j < EPP; ++j) sdOt[(c + j) * LDC + t] = to_f32(x[j]);
       }
     };
     load_tiles(n_chunks - 1);
@@ -574,60 +597,67 @@ __device__ void rev_chain(const BwdArgs<T> &a, int u, int cb, char *smem) {
     for (int cc = n_chunks - 1; cc >= 0; --cc) {
       const int tok0 = start + cc * C, n = min(C, end - tok0);
       float *ent = a.ent + (int64_t(c_first + cc) * a.H_v + h) * a.ent_floats;
-      // the gradient at this chunk's end state: to LDS and to the entry
+      // the gradient at this chunk's end state: to LDS, transposed, and to the entry
 #pragma unroll
       for (int m = 0; m < 4; ++m) {
         const int i = w + 4 * m;
         if (i < nst) {
           const int kt = i % NKT, ct = i / NKT;
+          *reinterpret_cast<f32x4_t *>(sdSt + (16 * ct + r) * LDT + 16 * kt + 4 * g) = accS[m];
 #pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            const int row = 16 * kt + 4 * g + q, col = 16 * ct + r;
-            sdS[row * LDB + col] = accS[m][q];
-            ent[L.dS + int64_t(row) * DV + c0 + col] = accS[m][q];
-          }
+          for (int q = 0; q < 4; ++q)
+            ent[L.dS + int64_t(16 * kt + 4 * g + q) * DV + c0 + 16 * ct + r] = accS[m][q];
         }
       }
       const int nx = max(cc - 1, 0);  // the next chunk back (the first one reloads itself)
       load_tiles(nx);
       lds_sync();
       // dU = P^T dO + diag(s) K dS'
+      if (nmine > 0) {
+        f32x4_t kds[2] = {zero4(), zero4()}, pdo[2] = {zero4(), zero4()};
 #pragma unroll
-      for (int m = 0; m < 2; ++m) {
-        if (m < nmine) {
-          const int ct = (w + 4 * m) / NRT;
-          f32x4_t kds = zero4(), pdo = zero4();
-          for (int k0 = 0; k0 < DK; k0 += 16)
-            kds = mm16(row4(sK + (16 * rt + r) * LDK + k0 + 4 * g), col4(sdS + (k0 + 4 * g) * LDB + 16 * ct + r, LDB),
-                       kds);
+        for (int kk = 0; kk < 8; ++kk) {
+          if (16 * kk < DK) {
+            const f32x4_t xr = row4(sK + (16 * rt + r) * LDK + 16 * kk + 4 * g);
 #pragma unroll
-          for (int kb = 0; kb < NRT; ++kb)
-            pdo = mm16(pcur[kb], col4(sdO + (16 * kb + 4 * g) * LDB + 16 * ct + r, LDB), pdo);
-#pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            const int t = 16 * rt + 4 * g + q;
-            sdU[t * LDB + 16 * ct + r] = pdo[q] + sgate[64 + t] * kds[q];
+            for (int m = 0; m < 2; ++m)
+              if (m < nmine)
+                kds[m] = mm16(xr, row4(sdSt + (16 * ((w + 4 * m) / NRT) + r) * LDT + 16 * kk + 4 * g), kds[m]);
           }
         }
+#pragma unroll
+        for (int kb = 0; kb < NRT; ++kb)
+#pragma unroll
+          for (int m = 0; m < 2; ++m)
+            if (m < nmine)
+              pdo[m] = mm16(pcur[kb], row4(sdOt + (16 * ((w + 4 * m) / NRT) + r) * LDC + 16 * kb + 4 * g), pdo[m]);
+        const f32x4_t sc = row4(sgate + 64 + 16 * rt + 4 * g);
+#pragma unroll
+        for (int m = 0; m < 2; ++m)
+          if (m < nmine)
+            *reinterpret_cast<f32x4_t *>(sdUt + (16 * ((w + 4 * m) / NRT) + r) * LDC + 16 * rt + 4 * g) =
+                pdo[m] + sc * kds[m];
       }
       load_p(nx);
       lds_sync();
       // dY = M^T dU;  dv = dX = diag(beta) dY
+      if (nmine > 0) {
+        const f32x4_t gam = row4(sgate + 16 * rt + 4 * g), be = row4(sgate + 128 + 16 * rt + 4 * g);
 #pragma unroll
-      for (int m = 0; m < 2; ++m) {
-        if (m < nmine) {
-          const int ct = (w + 4 * m) / NRT;
-          f32x4_t acc = zero4();
+        for (int m = 0; m < 2; ++m) {
+          if (m < nmine) {
+            const int col = 16 * ((w + 4 * m) / NRT) + r;
+            f32x4_t acc = zero4();
 #pragma unroll
-          for (int kb = 0; kb < NRT; ++kb)
-            acc = mm16(mcur[kb], col4(sdU + (16 * kb + 4 * g) * LDB + 16 * ct + r, LDB), acc);
+            for (int kb = 0; kb < NRT; ++kb) acc = mm16(mcur[kb], row4(sdUt + col * LDC + 16 * kb + 4 * g), acc);
+            const f32x4_t dx = be * acc;
 #pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            const int t = 16 * rt + 4 * g + q, col = 16 * ct + r;
-            const float dx = sgate[128 + t] * acc[q];
-            ent[L.dY + int64_t(t) * DV + c0 + col] = acc[q];
-            if (t < n) a.dv[int64_t(tok0 + t) * vrow + int64_t(h) * DV + c0 + col] = dx;
-            sdX[t * LDB + col] = -sgate[t] * dx;
+            for (int q = 0; q < 4; ++q) {
+              const int t = 16 * rt + 4 * g + q;
+              ent[L.dY + int64_t(t) * DV + c0 + col] = acc[q];
+              if (t < n) a.dv[int64_t(tok0 + t) * vrow + int64_t(h) * DV + c0 + col] = dx[q];
+            }
+            *reinterpret_cast<f32x4_t *>(sdXt + col * LDC + 16 * rt + 4 * g) = -(gam * dx);
           }
         }
       }
@@ -643,12 +673,10 @@ __device__ void rev_chain(const BwdArgs<T> &a, int u, int cb, char *smem) {
           f32x4_t acc = accS[m] * gC;
 #pragma unroll
           for (int kb = 0; kb < NRT; ++kb) {
-            const int t0 = 16 * kb + 4 * g;
-            f32x4_t xq = col4(sQ + t0 * LDK + 16 * kt + r, LDK);
-#pragma unroll
-            for (int j = 0; j < 4; ++j) xq[j] *= sgate[t0 + j];
-            acc = mm16(xq, col4(sdO + t0 * LDB + 16 * ct + r, LDB), acc);
-            acc = mm16(col4(sK + t0 * LDK + 16 * kt + r, LDK), col4(sdX + t0 * LDB + 16 * ct + r, LDB), acc);
+            const f32x4_t xq = tile_colfrag(sQ, LDK, 16 * kb, 16 * kt, r, g) * row4(sgate + 16 * kb + 4 * g);
+            acc = mm16(xq, row4(sdOt + (16 * ct + r) * LDC + 16 * kb + 4 * g), acc);
+            acc = mm16(tile_colfrag(sK, LDK, 16 * kb, 16 * kt, r, g),
+                       row4(sdXt + (16 * ct + r) * LDC + 16 * kb + 4 * g), acc);
           }
           accS[m] = acc;
         }
