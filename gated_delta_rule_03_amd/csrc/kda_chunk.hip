@@ -82,25 +82,63 @@ __global__ __launch_bounds__(512) void kda_prep_kernel(KdaArgs<T> a) {
   const int64_t a_stride = int64_t(a.H_v) * dk;
 
   // ---- rows of k, q and the clamped log2 rates (zero past the chunk's end),
-  // four channels per load ----
-  for (int idx = tid; idx < 16 * dk; idx += 512) {
-    const int t = idx / (dk / 4), ch = 4 * (idx - t * (dk / 4));
-    const bool in = t < len;
-    const float4 kv = in ? load4_f32(kb + int64_t(t) * qk_stride + ch) : make_float4(0.f, 0.f, 0.f, 0.f);
-    const float4 qv = in ? load4_f32(qb + int64_t(t) * qk_stride + ch) : make_float4(0.f, 0.f, 0.f, 0.f);
-    const float4 av = in ? *reinterpret_cast<const float4 *>(ab + int64_t(t) * a_stride + ch)
-                         : make_float4(1.f, 1.f, 1.f, 1.f);
-    float *pk = sK + t * kKRow + ch, *pq = sQ + t * kKRow + ch, *pg = sG + t * kKRow + ch;
-    pk[0] = kv.x; pk[1] = kv.y; pk[2] = kv.z; pk[3] = kv.w;
-    pq[0] = qv.x; pq[1] = qv.y; pq[2] = qv.z; pq[3] = qv.w;
-    pg[0] = clamped_log2(av.x); pg[1] = clamped_log2(av.y); pg[2] = clamped_log2(av.z); pg[3] = clamped_log2(av.w);
+  // four channels per load.  Every load is issued before any is used: rows
+  // past the chunk's end and pieces past d_k are clamped onto valid ones
+  // (the latter rewrite the same values), then zeroed ----
+  {
+    constexpr int kPieces = (16 * 128 + 511) / 512;
+    const int np = 16 * dk;
+    float4 kv[kPieces], qv[kPieces], av[kPieces];
+#pragma unroll
+    for (int m = 0; m < kPieces; ++m) {
+      const int idx = min(tid + 512 * m, np - 1);
+      const int t = idx / (dk / 4), ch = 4 * (idx - t * (dk / 4));
+      const int64_t tc = min(t, len - 1);
+      kv[m] = load4_f32(kb + tc * qk_stride + ch);
+      qv[m] = load4_f32(qb + tc * qk_stride + ch);
+      av[m] = *reinterpret_cast<const float4 *>(ab + tc * a_stride + ch);
+    }
+#pragma unroll
+    for (int m = 0; m < kPieces; ++m) {
+      const int idx = min(tid + 512 * m, np - 1);
+      const int t = idx / (dk / 4), ch = 4 * (idx - t * (dk / 4));
+      const bool in = t < len;
+      float *pk = sK + t * kKRow + ch, *pq = sQ + t * kKRow + ch, *pg = sG + t * kKRow + ch;
+      pk[0] = in ? kv[m].x : 0.0f; pk[1] = in ? kv[m].y : 0.0f; pk[2] = in ? kv[m].z : 0.0f; pk[3] = in ? kv[m].w : 0.0f;
+      pq[0] = in ? qv[m].x : 0.0f; pq[1] = in ? qv[m].y : 0.0f; pq[2] = in ? qv[m].z : 0.0f; pq[3] = in ? qv[m].w : 0.0f;
+      pg[0] = in ? clamped_log2(av[m].x) : 0.0f;
+      pg[1] = in ? clamped_log2(av[m].y) : 0.0f;
+      pg[2] = in ? clamped_log2(av[m].z) : 0.0f;
+      pg[3] = in ? clamped_log2(av[m].w) : 0.0f;
+    }
   }
-  if (tid < 64) sb[tid] = tid < len ? a.beta[int64_t(tok0 + tid) * a.H_v + h] : 0.0f;
+  if (tid < 64) {
+    const float bv = a.beta[int64_t(tok0 + min(tid, len - 1)) * a.H_v + h];
+    sb[tid] = tid < len ? bv : 0.0f;
+  }
   lds_barrier();
   // ---- chunk-local cumulative log gate: a wave per channel, lane = token ----
-  for (int ch = wave; ch < dk; ch += 8) {
+  // (several channels at a time, so their reads are in flight together;
+  // d_k >= 16, so channels ch and ch + 8 always exist)
+  for (int ch = wave; ch < dk; ch += 32) {
     float *pg = sG + lane * kKRow + ch;
-    *pg = wave_prefix_sum(*pg);
+    if (ch + 16 < dk) {
+      float x0 = pg[0], x1 = pg[8], x2 = pg[16], x3 = pg[24];
+      x0 = wave_prefix_sum(x0);
+      x1 = wave_prefix_sum(x1);
+      x2 = wave_prefix_sum(x2);
+      x3 = wave_prefix_sum(x3);
+      pg[0] = x0;
+      pg[8] = x1;
+      pg[16] = x2;
+      pg[24] = x3;
+    } else {
+      float x0 = pg[0], x1 = pg[8];
+      x0 = wave_prefix_sum(x0);
+      x1 = wave_prefix_sum(x1);
+      pg[0] = x0;
+      pg[8] = x1;
+    }
   }
   lds_barrier();
 
