@@ -776,9 +776,11 @@ __global__ __launch_bounds__(kGradThreads) void bwd_grad_kernel(BwdArgs<T> a) {
   const int np = w < NL;
   int prt[1], pct[1];
   lower_tile(min(w, NL - 1), prt[0], pct[0]);
-  f32x4_t W1[NRT], W2[NRT], W3[NRT], aP[1], aA[1];
+  // this wave's row tiles: i = rsel + m wpc (wpc >= 2, so at most RPW of them)
+  constexpr int RPW = (NRT + 1) / 2;
+  f32x4_t W1[RPW], W2[RPW], W3[RPW], aP[1], aA[1];
 #pragma unroll
-  for (int i = 0; i < NRT; ++i) W1[i] = W2[i] = W3[i] = zero4();
+  for (int m = 0; m < RPW; ++m) W1[m] = W2[m] = W3[m] = zero4();
   aP[0] = aA[0] = zero4();
   float sd = 0.0f;  // <S, dS'> partial (one wave per d_k column tile)
   float r1acc[NPC];
@@ -820,12 +822,13 @@ __global__ __launch_bounds__(kGradThreads) void bwd_grad_kernel(BwdArgs<T> a) {
       const int k0 = 16 * kk + 4 * g;
       if (has_rows) {
 #pragma unroll
-        for (int i = 0; i < NRT; ++i) {
-          if (i % wpc != rsel) continue;
+        for (int m = 0; m < RPW; ++m) {
+          const int i = rsel + m * wpc;
+          if (i >= NRT) continue;
           const int row = (16 * i + r) * LDV + k0;
-          W1[i] = mm16(row4(sdO + row), yS[kk], W1[i]);
-          W2[i] = mm16(row4(sdY + row), yS[kk], W2[i]);
-          W3[i] = mm16(row4(sU + row), ydS[kk], W3[i]);
+          W1[m] = mm16(row4(sdO + row), yS[kk], W1[m]);
+          W2[m] = mm16(row4(sdY + row), yS[kk], W2[m]);
+          W3[m] = mm16(row4(sU + row), ydS[kk], W3[m]);
         }
         if (rsel == 0) {
           const f32x4_t pr = yS[kk] * ydS[kk];
@@ -931,8 +934,17 @@ __global__ __launch_bounds__(kGradThreads) void bwd_grad_kernel(BwdArgs<T> a) {
   // dq, dk and the d_k row sums of this wave's tiles
   if (has_rows) {
 #pragma unroll
-    for (int i = 0; i < NRT; ++i) {
-      if (i % wpc != rsel) continue;
+    for (int m = 0; m < RPW; ++m) {
+      const int i = rsel + m * wpc;
+      if (i >= NRT) continue;
+      // K and Q values of row tile i (a runtime index: picked, not indexed)
+      f32x4_t kfi = kf[0], qfi = qf[0];
+#pragma unroll
+      for (int kb = 1; kb < NRT; ++kb)
+        if (kb == i) {
+          kfi = kf[kb];
+          qfi = qf[kb];
+        }
       f32x4_t aq = zero4(), ak = zero4();
 #pragma unroll
       for (int kb = 0; kb < NRT; ++kb) {
@@ -943,10 +955,10 @@ __global__ __launch_bounds__(kGradThreads) void bwd_grad_kernel(BwdArgs<T> a) {
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         const int t = 16 * i + 4 * g + q, col = 16 * ct + r;
-        const float dqv = sGam[t] * W1[i][q] + aq[q];
-        const float dkv = ak[q] - sGam[t] * sBe[t] * W2[i][q] + sSc[t] * W3[i][q];
-        const float pg = group_sum(qf[i][q] * W1[i][q] - sBe[t] * kf[i][q] * W2[i][q], 16);
-        const float ps = group_sum(kf[i][q] * W3[i][q], 16);
+        const float dqv = sGam[t] * W1[m][q] + aq[q];
+        const float dkv = ak[q] - sGam[t] * sBe[t] * W2[m][q] + sSc[t] * W3[m][q];
+        const float pg = group_sum(qfi[q] * W1[m][q] - sBe[t] * kfi[q] * W2[m][q], 16);
+        const float ps = group_sum(kfi[q] * W3[m][q], 16);
         if (r == 0) {
           sPartG[t * 8 + ct] = pg;
           sPartS[t * 8 + ct] = ps;
