@@ -141,7 +141,7 @@ template <typename T, int C> struct TileLoader {
     const int ppr = DK / EPP, np = C * ppr;
 #pragma unroll
     for (int m = 0; m < MAXP; ++m) {
-      const int p = min(int(threadIdx.x) + kChainThreads * m, np - 1);
+      const int p = min(int(threadIdx.x % kChainThreads) + kChainThreads * m, np - 1);
       const int t = p / ppr, c = (p - t * ppr) * EPP;
       const uint4 x = *reinterpret_cast<const uint4 *>(base + int64_t(min(t, n - 1)) * row_stride + c);
       v[m] = t < n ? x : make_uint4(0, 0, 0, 0);
@@ -151,7 +151,7 @@ template <typename T, int C> struct TileLoader {
     const int ppr = DK / EPP, np = C * ppr;
 #pragma unroll
     for (int m = 0; m < MAXP; ++m) {
-      const int p = min(int(threadIdx.x) + kChainThreads * m, np - 1);
+      const int p = min(int(threadIdx.x % kChainThreads) + kChainThreads * m, np - 1);
       const int t = p / ppr, c = (p - t * ppr) * EPP;
       *reinterpret_cast<uint4 *>(lds + t * ldk + c) = v[m];
     }
@@ -305,6 +305,8 @@ template <typename T, int C> struct ChainLds {
   static constexpr int kFwd = kTile + kState + 2 * kCol + kGate;
   static constexpr int kRev = 2 * kTile + kState + 3 * kCol + kGate;
   static constexpr int kBytes = kFwd > kRev ? kFwd : kRev;
+  // one block runs a chain of each direction when both fit in a CU's LDS
+  static constexpr bool kPaired = kFwd + kRev <= 160 * 1024;
 };
 
 // A fragment of K^T (or Q^T) from a row-major token-row tile in LDS: lane
@@ -358,7 +360,7 @@ __device__ void fwd_chain(const BwdArgs<T> &a, int u, int cb, char *smem) {
   constexpr int NRT = C / 16, LDK = Lds::LDK, LDT = Lds::LDT, LDC = Lds::LDC;
   const int DK = a.d_k, DV = a.d_v, CB = min(32, DV), c0 = cb * CB;
   const int NKT = DK / 16, NCT = CB / 16;
-  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, r = lane & 15, g = lane >> 4;
+  const int tid = threadIdx.x % kChainThreads, w = tid >> 6, lane = tid & 63, r = lane & 15, g = lane >> 4;
   T *sK = reinterpret_cast<T *>(smem);
   float *sSt = reinterpret_cast<float *>(smem + Lds::kTile);  // S^T
   float *sYt = sSt + 32 * LDT;                                  // (diag(beta) X)^T
@@ -511,7 +513,7 @@ __device__ void rev_chain(const BwdArgs<T> &a, int u, int cb, char *smem) {
   constexpr int NRT = C / 16, LDK = Lds::LDK, LDT = Lds::LDT, LDC = Lds::LDC;
   const int DK = a.d_k, DV = a.d_v, CB = min(32, DV), c0 = cb * CB;
   const int NKT = DK / 16, NCT = CB / 16;
-  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, r = lane & 15, g = lane >> 4;
+  const int tid = threadIdx.x % kChainThreads, w = tid >> 6, lane = tid & 63, r = lane & 15, g = lane >> 4;
   T *sK = reinterpret_cast<T *>(smem);
   T *sQ = reinterpret_cast<T *>(smem + Lds::kTile);
   float *sdSt = reinterpret_cast<float *>(smem + 2 * Lds::kTile);  // dS'^T
@@ -704,20 +706,38 @@ __device__ void rev_chain(const BwdArgs<T> &a, int u, int cb, char *smem) {
 
 }  // namespace
 
-// Blocks come in groups of 8 units x (2 x column blocks): all blocks of a unit
-// have the same block id mod 8, so they share one XCD's L2 copy of the unit's
-// k and q.  Within a unit, even slots walk forward and odd slots backward.
+// One block per (unit, column block): waves 0-3 walk the chunks forward and
+// waves 4-7 walk them backward, each on its own LDS region.  Both take the
+// same barriers (four per chunk, over the same chunks), so each CU runs one
+// chain of each direction and the two share its matrix units (the backward
+// chain has 1.6 times the forward's products).  Where the two regions do not
+// fit together (fp32 inputs in chunks of 64), a block of four waves runs one
+// direction: even slots of a unit forward, odd ones backward.  Blocks come in
+// groups of 8 units x column blocks: the blocks of a unit have the same block
+// id mod 8, so they share one XCD's L2 copy of its k and q.
 template <typename T, int C>
-__global__ __launch_bounds__(kChainThreads, 2) void bwd_chain_kernel(BwdArgs<T> a) {
-  __shared__ __attribute__((aligned(16))) char smem[ChainLds<T, C>::kBytes];
+__global__ __launch_bounds__(2 * kChainThreads) void bwd_chain_kernel(BwdArgs<T> a) {
+  using Lds = ChainLds<T, C>;
   const int n_cb = a.d_v / min(32, a.d_v);
   int u, x;
-  decode_block(blockIdx.x, 2 * n_cb, u, x);
-  if (u >= a.n_units) return;
-  if (x & 1)
-    rev_chain<T, C>(a, u, x >> 1, smem);
-  else
-    fwd_chain<T, C>(a, u, x >> 1, smem);
+  if constexpr (Lds::kPaired) {
+    __shared__ __attribute__((aligned(16))) char smem_f[Lds::kFwd];
+    __shared__ __attribute__((aligned(16))) char smem_r[Lds::kRev];
+    decode_block(blockIdx.x, n_cb, u, x);
+    if (u >= a.n_units) return;
+    if (threadIdx.x >= kChainThreads)
+      rev_chain<T, C>(a, u, x, smem_r);
+    else
+      fwd_chain<T, C>(a, u, x, smem_f);
+  } else {
+    __shared__ __attribute__((aligned(16))) char smem[Lds::kBytes];
+    decode_block(blockIdx.x, 2 * n_cb, u, x);
+    if (u >= a.n_units) return;
+    if (x & 1)
+      rev_chain<T, C>(a, u, x >> 1, smem);
+    else
+      fwd_chain<T, C>(a, u, x >> 1, smem);
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -1028,8 +1048,10 @@ static hipError_t launch_bwd_c(const BwdProblem &b, const BwdArgs<T> &a, hipStre
   }
   const int n_cb = p.d_v / std::min(32, p.d_v);
   const int64_t groups = (int64_t(a.n_units) + 7) / 8;
-  const unsigned chain_blocks = unsigned(groups * 8 * 2 * n_cb);
-  hipLaunchKernelGGL((bwd_chain_kernel<T, C>), dim3(chain_blocks), dim3(kChainThreads), 0, st, a);
+  if (ChainLds<T, C>::kPaired)
+    hipLaunchKernelGGL((bwd_chain_kernel<T, C>), dim3(unsigned(groups * 8 * n_cb)), dim3(2 * kChainThreads), 0, st, a);
+  else
+    hipLaunchKernelGGL((bwd_chain_kernel<T, C>), dim3(unsigned(groups * 8 * 2 * n_cb)), dim3(kChainThreads), 0, st, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || n_ent == 0) return e;
   if (p.d_v >= 32)
