@@ -281,12 +281,13 @@ def chunk_bwd_workspace_bytes(B, T, H_qk, H_v, d_k, d_v, dtype_code, chunk=64, n
 
 
 def chunk_bwd(q, k, v, alpha, beta, d_o, *, chunk: int = 64, cu_seqlens=None, h0=None, dhT=None,
-              want_dh0: bool = True, workspace=None, stream=None) -> Tuple:
+              want_dh0: bool = True, out=None, workspace=None, stream=None) -> Tuple:
     """Gradients of L = sum <d_o, o> + <dhT, hT> (gdn_chunk_bwd).
 
     Returns (dq, dk, dv, dalpha, dbeta, dh0), all float32; dq and dk sum over
     the value heads that read each query/key head; dh0 is None unless
-    ``want_dh0``.
+    ``want_dh0``.  ``out`` may hold those six tensors (dh0 may be None),
+    written in place; otherwise they are allocated here.
     """
     torch = _torch()
     dims, n_seqs, _, _ = _fwd_args(q, k, v, alpha, beta, cu_seqlens, h0, d_o, None, False)
@@ -295,13 +296,22 @@ def chunk_bwd(q, k, v, alpha, beta, d_o, *, chunk: int = 64, cu_seqlens=None, h0
     dev = q.device
     if dhT is not None:
         _check(dhT, "dhT", (N, H_v, d_k, d_v), torch.float32, dev)
-    f32 = dict(dtype=torch.float32, device=dev)
-    dq = torch.empty((B, T, H_qk, d_k), **f32)
-    dk = torch.empty((B, T, H_qk, d_k), **f32)
-    dv = torch.empty((B, T, H_v, d_v), **f32)
-    dalpha = torch.empty((B, T, H_v), **f32)
-    dbeta = torch.empty((B, T, H_v), **f32)
-    dh0 = torch.empty((N, H_v, d_k, d_v), **f32) if want_dh0 else None
+    shapes = ((B, T, H_qk, d_k), (B, T, H_qk, d_k), (B, T, H_v, d_v), (B, T, H_v), (B, T, H_v),
+              (N, H_v, d_k, d_v))
+    names = ("dq", "dk", "dv", "dalpha", "dbeta", "dh0")
+    if out is None:
+        f32 = dict(dtype=torch.float32, device=dev)
+        out = [torch.empty(sh, **f32) for sh in shapes[:5]]
+        out.append(torch.empty(shapes[5], **f32) if want_dh0 else None)
+    else:
+        if len(out) != 6:
+            raise ValueError("out must hold (dq, dk, dv, dalpha, dbeta, dh0)")
+        for t, sh, nm in zip(out, shapes, names):
+            if t is not None:
+                _check(t, nm, sh, torch.float32, dev)
+        if any(t is None for t in out[:5]):
+            raise ValueError("out: only dh0 may be None")
+    dq, dk, dv, dalpha, dbeta, dh0 = out
     need = chunk_bwd_workspace_bytes(*dims, chunk, n_seqs)
     if need == 0:
         raise GDNError(2, "gdn_chunk_bwd_workspace_bytes")

@@ -4,7 +4,8 @@ hold a sentinel pattern; after each call the bands must be bitwise
 untouched.  Cases: the staged and general chunk kernels on uniform batches
 with a partial last chunk, a packed batch with empty and one-token sequences
 and grouped heads, the segment-parallel form, the per-channel-gate chunked
-and token-by-token forwards, and the decode step."""
+and token-by-token forwards, the decode step, and the backward pass (every
+gradient and its workspace, with h0 and dhT)."""
 import numpy as np
 import pytest
 
@@ -123,3 +124,31 @@ def test_decode_bands_untouched(gdn, per_channel):
     torch.cuda.synchronize()
     log(f"[canary] decode per_channel={per_channel}: bands {'intact' if st.intact() and o.intact() else 'OVERWRITTEN'}")
     assert st.intact() and o.intact()
+
+
+@pytest.mark.parametrize("name,case", CASES, ids=[c[0] for c in CASES])
+def test_backward_bands_untouched(gdn, name, case):
+    import torch
+    dtype, B, T, H_qk, H_v, d_k, d_v, chunk, seed, lengths = case
+    w = small(dtype, B, T, H_qk, H_v, d_k, d_v, chunk, seed, lengths)
+    B, T = w.q.shape[0], w.q.shape[1]
+    cu = None if w.cu_seqlens is None else dev_tensor(w.cu_seqlens)
+    N = B if cu is None else cu.numel() - 1
+    n_seqs = 0 if cu is None else N
+    f32 = torch.float32
+    outs = [Guarded((B, T, H_qk, d_k), f32), Guarded((B, T, H_qk, d_k), f32), Guarded((B, T, H_v, d_v), f32),
+            Guarded((B, T, H_v), f32), Guarded((B, T, H_v), f32), Guarded((N, H_v, d_k, d_v), f32)]
+    code = gdn.GDN_BF16 if dtype == "bf16" else gdn.GDN_F32
+    ws = guarded_ws(gdn.chunk_bwd_workspace_bytes(B, T, H_qk, H_v, d_k, d_v, code, chunk, n_seqs))
+    do32 = gi.random_state((B, T, H_v, d_v), seed=seed + 1)
+    d_o = dev_tensor(gi.f32_to_bf16_bits(do32) if dtype == "bf16" else do32)
+    h0 = dev_tensor(gi.random_state((N, H_v, d_k, d_v), seed=seed + 2, scale=0.3))
+    dhT = dev_tensor(gi.random_state((N, H_v, d_k, d_v), seed=seed + 3, scale=0.5))
+    args = [dev_tensor(x) for x in (w.q, w.k, w.v, w.alpha, w.beta)]
+    gdn.chunk_bwd(*args, d_o, chunk=chunk, cu_seqlens=cu, h0=h0, dhT=dhT, out=[g.t for g in outs],
+                  workspace=ws.t)
+    torch.cuda.synchronize()
+    ok = all(g.intact() for g in outs) and ws.intact()
+    log(f"[canary] {name} chunk_bwd: bands {'intact' if ok else 'OVERWRITTEN'}")
+    assert ok
+    assert all(bool(torch.isfinite(g.t).all()) for g in outs)
