@@ -284,11 +284,12 @@ __global__ __launch_bounds__(256) void bwd_factor_kernel(BwdArgs<T> a) {
 }
 
 // ---------------------------------------------------------------------------
-// 2. The two chains.  Block = (unit, column block of CB = min(32, d_v)
-// columns, direction), 4 waves.  Tiles of a C x CB product: i = w + 4m, row
-// tile i % (C/16), column tile i / (C/16), so a wave keeps one row tile.
-// Tiles of the d_k x CB state: i = w + 4m, row tile i % (d_k/16), column tile
-// i / (d_k/16).
+// 2. The two chains, each on four waves over a column block of
+// CB = min(32, d_v) columns of one unit (the kernel below puts a chain of
+// each direction in one block where LDS allows).  With w the wave within its
+// four: tiles of a C x CB product are i = w + 4m, row tile i % (C/16), column
+// tile i / (C/16), so a wave keeps one row tile; tiles of the d_k x CB state
+// are i = w + 4m, row tile i % (d_k/16), column tile i / (d_k/16).
 // ---------------------------------------------------------------------------
 namespace {
 

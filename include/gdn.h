@@ -203,8 +203,10 @@ int32_t gdn_chunk_fwd_noalloc(int32_t B, int32_t T, int32_t H_qk, int32_t H_v, i
  * are the reverse-mode derivatives of the forward of gdn_recurrent_fwd
  * ("Linear attention", Eqs. (1)-(4)) for the loss
  *   L = sum_t <d_o_t, o_t> + <dhT, S_T>   (per sequence and value head),
- * evaluated chunk by chunk from the chunk-start states of a token-by-token
- * forward, in fp32.
+ * evaluated in the chunk form, in fp32: the chunk-start states and the
+ * gradients reaching each chunk's end are carried chunk to chunk, and every
+ * chunk's gradients then follow independently.  Deterministic (no atomics):
+ * two calls on the same inputs give bitwise equal results.
  *
  * Inputs as gdn_chunk_fwd (q, k, v, alpha, beta, cu_seqlens, n_seqs, h0,
  * chunk, workspace), plus:
@@ -219,8 +221,11 @@ int32_t gdn_chunk_fwd_noalloc(int32_t B, int32_t T, int32_t H_qk, int32_t H_v, i
  *   dbeta      [B, T, H_v].
  *   dh0        [N, H_v, d_k, d_v], or NULL (not written).
  * gdn_chunk_bwd_workspace_bytes gives the workspace bytes (0 = unsupported
- * arguments): chunk-start states, per-value-head dq and dk, and per unit
- * about (8 C^2 + 12 C max(d_k, d_v) + 2 d_k d_v) floats of intermediates.
+ * arguments): per (chunk slot, value head) 3 C^2 + 256 + 2 d_k d_v + 3 C d_v
+ * floats of intermediates (1.09 GiB for B=4, T=4096, H=16, d=128, C=64),
+ * plus the per-value-head dq and dk when H_v > H_qk.  The caller owns the
+ * workspace; it must be 256-byte aligned (else GDN_ERROR_WORKSPACE), and
+ * nothing in it is needed after the call.
  * Errors as gdn_chunk_fwd; GDN_ERROR_INVALID_VALUE when an output is NULL
  * for a non-empty batch or a pointer is misaligned.
  */
