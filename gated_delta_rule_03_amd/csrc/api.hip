@@ -151,6 +151,7 @@ static Problem segment_problem(const Problem &p, int32_t seg_chunks, const SegWo
   ps.cu_seqlens = sw ? sw->seg_cu : &kLayoutOnly;  // selects the packed layout
   ps.h0 = sw ? sw->s_in : nullptr;
   ps.hT = nullptr;  // the fold writes the final states
+  ps.seg_pass = 1;
   return ps;
 }
 static size_t seg_workspace_layout(const Problem &p, int32_t seg_chunks, void *base, SegWorkspace *sw) {
@@ -225,8 +226,12 @@ int32_t run_chunk_fwd(Problem p, int32_t seg_chunks, void *workspace, size_t wor
     Workspace ws;
     workspace_layout(p, workspace, &ws);
     hipError_t e = launch_chunk_offsets(p, ws, s);
-    if (e == hipSuccess) e = launch_prep(p, ws, s);
-    if (e == hipSuccess) e = launch_scan(p, ws, s);
+    if (chain_path(p)) {
+      if (e == hipSuccess) e = launch_chain_fwd(p, ws, s);
+    } else {
+      if (e == hipSuccess) e = launch_prep(p, ws, s);
+      if (e == hipSuccess) e = launch_scan(p, ws, s);
+    }
     return status_of(e);
   }
   SegWorkspace sw;

@@ -62,8 +62,8 @@ struct BwdEntry {
     int64_t o = 0;
     M = o;    o += int64_t(C) * C;    // (I + A)^-1, row-major C x C
     P = o;    o += int64_t(C) * C;    // lower(Gamma . Q K^T)
-    G = o;    o += int64_t(C) * C;    // strict_lower(Gamma . K K^T)
     gate = o; o += 256;               // gamma_t, s_t, log2 cumulative gate, beta_t (64 each)
+    G = o;    o += int64_t(C) * C;    // strict_lower(Gamma . K K^T); the forward's entries end here
     S = o;    o += int64_t(DK) * DV;  // state entering the chunk
     dS = o;   o += int64_t(DK) * DV;  // gradient reaching the chunk's end state
     X = o;    o += int64_t(C) * DV;   // V - diag(gamma) K S
@@ -83,6 +83,9 @@ struct BwdArgs {
   float *dq, *dk;         // [tokens, H_v, d_k]: the gradients themselves when every
                           // query/key head has one value head, else per-value-head parts
   float *dv, *dalpha, *dbeta, *dh0;
+  T *o;                   // the forward: outputs [tokens, H_v, d_v] and final states (or null)
+  float *hT;
+  bool want_g;            // the backward: the factor kernel also writes Gamma . K K^T
   int H_qk, H_v, d_k, d_v, group, n_units;
   SeqGeom geo;
 };
@@ -201,11 +204,15 @@ __global__ __launch_bounds__(256) void bwd_factor_kernel(BwdArgs<T> a) {
       }
     }
     for (int i = tid; i < C * LD; i += 256) sA[i] = 0.0f;
-    for (int idx = tid; idx < C * C; idx += 256) {  // P and Gamma . K K^T are zero above the diagonal tiles
-      const int t = idx / C, i = idx - t * C;
-      if ((i >> 4) > (t >> 4)) {
-        ent[L.P + idx] = 0.0f;
-        ent[L.G + idx] = 0.0f;
+    // P and Gamma . K K^T are zero above the diagonal tiles, for the gradient
+    // kernel (the forward chain reads only the lower tiles of P)
+    if (a.want_g) {
+      for (int idx = tid; idx < C * C; idx += 256) {
+        const int t = idx / C, i = idx - t * C;
+        if ((i >> 4) > (t >> 4)) {
+          ent[L.P + idx] = 0.0f;
+          ent[L.G + idx] = 0.0f;
+        }
       }
     }
     kl.store(sK, LDK, DK);
@@ -231,7 +238,7 @@ __global__ __launch_bounds__(256) void bwd_factor_kernel(BwdArgs<T> a) {
         ent[L.P + t * C + i] = gam * acc[q];
       } else {
         const float gkk = i < t ? gam * acc[q] : 0.0f;
-        ent[L.G + t * C + i] = gkk;
+        if (a.want_g) ent[L.G + t * C + i] = gkk;
         sA[t * LD + i] = sb[t] * gkk;
       }
     }
@@ -308,6 +315,8 @@ template <typename T, int C> struct ChainLds {
   static constexpr int kBytes = kFwd > kRev ? kFwd : kRev;
   // one block runs a chain of each direction when both fit in a CU's LDS
   static constexpr bool kPaired = kFwd + kRev <= 160 * 1024;
+  // the forward pass itself: K, Q, S^T, Y^T, U^T, gates
+  static constexpr int kOut = 2 * kTile + kState + 2 * kCol + kGate;
 };
 
 // A fragment of K^T (or Q^T) from a row-major token-row tile in LDS: lane
@@ -355,7 +364,12 @@ __device__ __forceinline__ void unit_of(const SeqGeom &geo, int H_v, int u, int 
   n_chunks = max(0, min(n_chunks, geo.n_slots - c_first));
 }
 
-template <typename T, int C>
+// The forward chain over one column block of one unit.  For the backward
+// (OUT = false) it stores each chunk's start state, X and U in the chunk's
+// entry.  For the forward pass itself (OUT = true) it stores nothing in the
+// entries: it also stages the chunk's Q rows, forms
+// O = diag(gamma) Q S + P U, and writes O and the last state.
+template <typename T, int C, bool OUT>
 __device__ void fwd_chain(const BwdArgs<T> &a, int u, int cb, char *smem) {
   using Lds = ChainLds<T, C>;
   constexpr int NRT = C / 16, LDK = Lds::LDK, LDT = Lds::LDT, LDC = Lds::LDC;
@@ -363,10 +377,11 @@ __device__ void fwd_chain(const BwdArgs<T> &a, int u, int cb, char *smem) {
   const int NKT = DK / 16, NCT = CB / 16;
   const int tid = threadIdx.x % kChainThreads, w = tid >> 6, lane = tid & 63, r = lane & 15, g = lane >> 4;
   T *sK = reinterpret_cast<T *>(smem);
-  float *sSt = reinterpret_cast<float *>(smem + Lds::kTile);  // S^T
-  float *sYt = sSt + 32 * LDT;                                  // (diag(beta) X)^T
-  float *sUt = sYt + 32 * LDC;                                  // (diag(s) U)^T
-  float *sgate = sUt + 32 * LDC;                                // gamma[64], s[64], beta[64]
+  T *sQ = reinterpret_cast<T *>(smem + Lds::kTile);                           // OUT only
+  float *sSt = reinterpret_cast<float *>(smem + (OUT ? 2 : 1) * Lds::kTile);  // S^T
+  float *sYt = sSt + 32 * LDT;                                                // (diag(beta) X)^T
+  float *sUt = sYt + 32 * LDC;        // (diag(s) U)^T; U^T when OUT (scaled where it is read)
+  float *sgate = sUt + 32 * LDC;      // gamma[64], s[64], beta[64]
   int s, h, start, end, c_first, n_chunks;
   unit_of(a.geo, a.H_v, u, s, h, start, end, c_first, n_chunks);
   const int hq = h / a.group;
@@ -389,13 +404,31 @@ __device__ void fwd_chain(const BwdArgs<T> &a, int u, int cb, char *smem) {
       for (int q = 0; q < 4; ++q) accS[m][q] = h0[int64_t(16 * kt + 4 * g + q) * DV + c0 + 16 * ct + r];
     }
   }
-  if (n_chunks == 0) return;
+  // the state after the last chunk (the entry state for an empty sequence)
+  auto store_final = [&]() {
+    if (!OUT || !a.hT) return;
+    float *hT = a.hT + (int64_t(s) * a.H_v + h) * DK * DV;
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+      const int i = w + 4 * m;
+      if (i < nst) {
+        const int kt = i % NKT, ct = i / NKT;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) hT[int64_t(16 * kt + 4 * g + q) * DV + c0 + 16 * ct + r] = accS[m][q];
+      }
+    }
+  };
+  if (n_chunks == 0) {
+    store_final();
+    return;
+  }
 
-  TileLoader<T, C> kl;
+  TileLoader<T, C> kl, ql;
   GateLoader gl;
-  // V at this wave's accumulator positions and the A fragments of M for its
-  // row tile: loaded a chunk ahead, right after their last use
-  f32x4_t vcur[2], mcur[NRT];
+  // V at this wave's accumulator positions and the A fragments of M (and for
+  // OUT of P, lower tiles only) for its row tile: loaded a chunk ahead, right
+  // after their last use
+  f32x4_t vcur[2], mcur[NRT], pcur[NRT];
   auto load_v = [&](int cc) {
     const int tok0 = start + cc * C, n = min(C, end - tok0);
 #pragma unroll
@@ -414,45 +447,62 @@ __device__ void fwd_chain(const BwdArgs<T> &a, int u, int cb, char *smem) {
 #pragma unroll
     for (int kb = 0; kb < NRT; ++kb) mcur[kb] = row4(ent + L.M + (16 * rt + r) * C + 16 * kb + 4 * g);
   };
+  auto load_p = [&](int cc) {  // tiles right of the diagonal are not used (nor written): re-read a used one
+    const float *ent = a.ent + (int64_t(c_first + cc) * a.H_v + h) * a.ent_floats;
+#pragma unroll
+    for (int kb = 0; kb < NRT; ++kb) pcur[kb] = row4(ent + L.P + (16 * rt + r) * C + 16 * min(kb, rt) + 4 * g);
+  };
   auto load_tiles = [&](int cc) {
     const int tok0 = start + cc * C, n = min(C, end - tok0);
     kl.load(a.k + int64_t(tok0) * krow + int64_t(hq) * DK, krow, n, DK);
+    if constexpr (OUT) ql.load(a.q + int64_t(tok0) * krow + int64_t(hq) * DK, krow, n, DK);
     gl.load(a.ent + (int64_t(c_first + cc) * a.H_v + h) * a.ent_floats + L.gate);
   };
   load_tiles(0);
   load_v(0);
   load_m(0);
+  if constexpr (OUT) load_p(0);
   kl.store(sK, LDK, DK);
+  if constexpr (OUT) ql.store(sQ, LDK, DK);
   gl.store(sgate);
 
   for (int cc = 0; cc < n_chunks; ++cc) {
     float *ent = a.ent + (int64_t(c_first + cc) * a.H_v + h) * a.ent_floats;
-    // the state entering this chunk: to LDS, transposed (operand of K S), and to the entry
+    // the state entering this chunk: to LDS, transposed (operand of K S and Q S), and to the entry
 #pragma unroll
     for (int m = 0; m < 4; ++m) {
       const int i = w + 4 * m;
       if (i < nst) {
         const int kt = i % NKT, ct = i / NKT;
         *reinterpret_cast<f32x4_t *>(sSt + (16 * ct + r) * LDT + 16 * kt + 4 * g) = accS[m];
+        if constexpr (!OUT) {
 #pragma unroll
-        for (int q = 0; q < 4; ++q)
-          ent[L.S + int64_t(16 * kt + 4 * g + q) * DV + c0 + 16 * ct + r] = accS[m][q];
+          for (int q = 0; q < 4; ++q)
+            ent[L.S + int64_t(16 * kt + 4 * g + q) * DV + c0 + 16 * ct + r] = accS[m][q];
+        }
       }
     }
     const int nx = min(cc + 1, n_chunks - 1);  // the next chunk (the last one reloads itself)
     load_tiles(nx);
     lds_sync();
-    // X = V - diag(gamma) K S;  Y = diag(beta) X
+    // X = V - diag(gamma) K S;  Y = diag(beta) X;  for OUT also diag(gamma) Q S
+    f32x4_t oacc[2] = {zero4(), zero4()};
     if (nmine > 0) {
-      f32x4_t acc[2] = {zero4(), zero4()};
+      f32x4_t acc[2] = {zero4(), zero4()}, qacc[2] = {zero4(), zero4()};
 #pragma unroll
       for (int kk = 0; kk < 8; ++kk) {
         if (16 * kk < DK) {
           const f32x4_t xr = row4(sK + (16 * rt + r) * LDK + 16 * kk + 4 * g);
+          f32x4_t qr = zero4();
+          if constexpr (OUT) qr = row4(sQ + (16 * rt + r) * LDK + 16 * kk + 4 * g);
 #pragma unroll
-          for (int m = 0; m < 2; ++m)
-            if (m < nmine)
-              acc[m] = mm16(xr, row4(sSt + (16 * ((w + 4 * m) / NRT) + r) * LDT + 16 * kk + 4 * g), acc[m]);
+          for (int m = 0; m < 2; ++m) {
+            if (m < nmine) {
+              const f32x4_t st = row4(sSt + (16 * ((w + 4 * m) / NRT) + r) * LDT + 16 * kk + 4 * g);
+              acc[m] = mm16(xr, st, acc[m]);
+              if constexpr (OUT) qacc[m] = mm16(qr, st, qacc[m]);
+            }
+          }
         }
       }
       const f32x4_t gam = row4(sgate + 16 * rt + 4 * g), be = row4(sgate + 128 + 16 * rt + 4 * g);
@@ -461,15 +511,19 @@ __device__ void fwd_chain(const BwdArgs<T> &a, int u, int cb, char *smem) {
         if (m < nmine) {
           const int col = 16 * ((w + 4 * m) / NRT) + r;
           const f32x4_t x = vcur[m] - gam * acc[m];
+          if constexpr (!OUT) {
 #pragma unroll
-          for (int q = 0; q < 4; ++q) ent[L.X + int64_t(16 * rt + 4 * g + q) * DV + c0 + col] = x[q];
+            for (int q = 0; q < 4; ++q) ent[L.X + int64_t(16 * rt + 4 * g + q) * DV + c0 + col] = x[q];
+          } else {
+            oacc[m] = gam * qacc[m];
+          }
           *reinterpret_cast<f32x4_t *>(sYt + col * LDC + 16 * rt + 4 * g) = be * x;
         }
       }
     }
     load_v(nx);
     lds_sync();
-    // U = M Y;  diag(s) U for the state update
+    // U = M Y;  diag(s) U for the state update (for OUT, U itself: O needs it too)
     if (nmine > 0) {
       const f32x4_t sc = row4(sgate + 64 + 16 * rt + 4 * g);
 #pragma unroll
@@ -479,9 +533,13 @@ __device__ void fwd_chain(const BwdArgs<T> &a, int u, int cb, char *smem) {
           f32x4_t acc = zero4();
 #pragma unroll
           for (int kb = 0; kb < NRT; ++kb) acc = mm16(mcur[kb], row4(sYt + col * LDC + 16 * kb + 4 * g), acc);
+          if constexpr (!OUT) {
 #pragma unroll
-          for (int q = 0; q < 4; ++q) ent[L.U + int64_t(16 * rt + 4 * g + q) * DV + c0 + col] = acc[q];
-          *reinterpret_cast<f32x4_t *>(sUt + col * LDC + 16 * rt + 4 * g) = sc * acc;
+            for (int q = 0; q < 4; ++q) ent[L.U + int64_t(16 * rt + 4 * g + q) * DV + c0 + col] = acc[q];
+            *reinterpret_cast<f32x4_t *>(sUt + col * LDC + 16 * rt + 4 * g) = sc * acc;
+          } else {
+            *reinterpret_cast<f32x4_t *>(sUt + col * LDC + 16 * rt + 4 * g) = acc;
+          }
         }
       }
     }
@@ -496,16 +554,43 @@ __device__ void fwd_chain(const BwdArgs<T> &a, int u, int cb, char *smem) {
         const int kt = i % NKT, ct = i / NKT;
         f32x4_t acc = accS[m] * gC;
 #pragma unroll
-        for (int kb = 0; kb < NRT; ++kb)
-          acc = mm16(tile_colfrag(sK, LDK, 16 * kb, 16 * kt, r, g),
-                     row4(sUt + (16 * ct + r) * LDC + 16 * kb + 4 * g), acc);
+        for (int kb = 0; kb < NRT; ++kb) {
+          f32x4_t ut = row4(sUt + (16 * ct + r) * LDC + 16 * kb + 4 * g);
+          if constexpr (OUT) ut = ut * row4(sgate + 64 + 16 * kb + 4 * g);
+          acc = mm16(tile_colfrag(sK, LDK, 16 * kb, 16 * kt, r, g), ut, acc);
+        }
         accS[m] = acc;
       }
     }
+    if constexpr (OUT) {
+      // O = diag(gamma) Q S + P U, over the lower tiles of P's row tile
+      if (nmine > 0) {
+        const int tok0 = start + cc * C, n = min(C, end - tok0);
+#pragma unroll
+        for (int m = 0; m < 2; ++m) {
+          if (m < nmine) {
+            const int col = 16 * ((w + 4 * m) / NRT) + r;
+            f32x4_t acc = oacc[m];
+#pragma unroll
+            for (int kb = 0; kb < NRT; ++kb)
+              if (kb <= rt) acc = mm16(pcur[kb], row4(sUt + col * LDC + 16 * kb + 4 * g), acc);
+            T *o = a.o + int64_t(tok0) * vrow + int64_t(h) * DV + c0 + col;
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+              const int t = 16 * rt + 4 * g + q;
+              if (t < n) o[int64_t(t) * vrow] = from_f32<T>(acc[q]);
+            }
+          }
+        }
+      }
+      load_p(nx);
+    }
     lds_sync();
     kl.store(sK, LDK, DK);
+    if constexpr (OUT) ql.store(sQ, LDK, DK);
     gl.store(sgate);
   }
+  store_final();
 }
 
 template <typename T, int C>
@@ -729,7 +814,7 @@ __global__ __launch_bounds__(2 * kChainThreads) void bwd_chain_kernel(BwdArgs<T>
     if (threadIdx.x >= kChainThreads)
       rev_chain<T, C>(a, u, x, smem_r);
     else
-      fwd_chain<T, C>(a, u, x, smem_f);
+      fwd_chain<T, C, false>(a, u, x, smem_f);
   } else {
     __shared__ __attribute__((aligned(16))) char smem[Lds::kBytes];
     decode_block(blockIdx.x, 2 * n_cb, u, x);
@@ -737,8 +822,22 @@ __global__ __launch_bounds__(2 * kChainThreads) void bwd_chain_kernel(BwdArgs<T>
     if (x & 1)
       rev_chain<T, C>(a, u, x >> 1, smem);
     else
-      fwd_chain<T, C>(a, u, x >> 1, smem);
+      fwd_chain<T, C, false>(a, u, x >> 1, smem);
   }
+}
+
+// The forward pass on the chained form: one block of four waves per (unit,
+// column block), in the same XCD-aware order, running the forward chain with
+// outputs.
+template <typename T, int C>
+__global__ __launch_bounds__(kChainThreads, 2) void chain_fwd_kernel(BwdArgs<T> a) {
+  using Lds = ChainLds<T, C>;
+  __shared__ __attribute__((aligned(16))) char smem[Lds::kOut];
+  const int n_cb = a.d_v / min(32, a.d_v);
+  int u, x;
+  decode_block(blockIdx.x, n_cb, u, x);
+  if (u >= a.n_units) return;
+  fwd_chain<T, C, true>(a, u, x, smem);
 }
 
 // ---------------------------------------------------------------------------
@@ -1083,6 +1182,9 @@ static hipError_t launch_chunk_bwd_t(const BwdProblem &b, hipStream_t st) {
   a.dalpha = b.dalpha;
   a.dbeta = b.dbeta;
   a.dh0 = b.dh0;
+  a.o = nullptr;
+  a.hT = nullptr;
+  a.want_g = true;
   a.H_qk = p.H_qk;
   a.H_v = p.H_v;
   a.d_k = p.d_k;
@@ -1108,6 +1210,57 @@ static hipError_t launch_chunk_bwd_t(const BwdProblem &b, hipStream_t st) {
 
 hipError_t launch_chunk_bwd(const BwdProblem &b, hipStream_t st) {
   return b.p.dtype == 1 ? launch_chunk_bwd_t<bf16_t>(b, st) : launch_chunk_bwd_t<float>(b, st);
+}
+
+// ---------------------------------------------------------------------------
+// The chained forward: the factor kernel (M, P and the gates only), then the
+// forward chain with outputs.  Its entries are the first BwdEntry::G floats
+// of a backward entry.
+// ---------------------------------------------------------------------------
+template <typename T, int C>
+static hipError_t launch_chain_fwd_c(const BwdArgs<T> &a, hipStream_t st) {
+  const unsigned n_ent = unsigned(int64_t(a.geo.n_slots) * a.H_v);
+  if (n_ent > 0) {
+    hipLaunchKernelGGL((bwd_factor_kernel<T, C>), dim3(n_ent), dim3(256), 0, st, a);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  const int n_cb = a.d_v / std::min(32, a.d_v);
+  const int64_t groups = (int64_t(a.n_units) + 7) / 8;
+  hipLaunchKernelGGL((chain_fwd_kernel<T, C>), dim3(unsigned(groups * 8 * n_cb)), dim3(kChainThreads), 0, st, a);
+  return hipGetLastError();
+}
+
+template <typename T>
+static hipError_t launch_chain_fwd_t(const Problem &p, const Workspace &ws, hipStream_t st) {
+  BwdArgs<T> a{};
+  a.q = static_cast<const T *>(p.q);
+  a.k = static_cast<const T *>(p.k);
+  a.v = static_cast<const T *>(p.v);
+  a.alpha = p.alpha;
+  a.beta = p.beta;
+  a.h0 = p.h0;
+  a.ent = static_cast<float *>(ws.entries);
+  a.ent_floats = BwdEntry(p.chunk, 0, 0).G;
+  a.o = static_cast<T *>(p.o);
+  a.hT = p.hT;
+  a.want_g = false;
+  a.H_qk = p.H_qk;
+  a.H_v = p.H_v;
+  a.d_k = p.d_k;
+  a.d_v = p.d_v;
+  a.group = p.H_v / p.H_qk;
+  a.n_units = p.n_seqs * p.H_v;
+  a.geo = make_geom(p, &ws);
+  if (a.n_units == 0) return hipSuccess;
+  return p.chunk == 16   ? launch_chain_fwd_c<T, 16>(a, st)
+         : p.chunk == 32 ? launch_chain_fwd_c<T, 32>(a, st)
+                         : launch_chain_fwd_c<T, 64>(a, st);
+}
+
+hipError_t launch_chain_fwd(const Problem &p, const Workspace &ws, hipStream_t st) {
+  if (int64_t(entry_stride(p)) != BwdEntry(p.chunk, 0, 0).G * int64_t(sizeof(float))) return hipErrorInvalidValue;
+  return p.dtype == 1 ? launch_chain_fwd_t<bf16_t>(p, ws, st) : launch_chain_fwd_t<float>(p, ws, st);
 }
 
 }  // namespace gdn

@@ -19,6 +19,7 @@ struct Problem {
   float *hT;
   int32_t chunk;
   int32_t per_channel = 0;  // alpha holds one rate per key channel: [.., H_v, d_k]
+  int32_t seg_pass = 0;     // a segment batch of the segment-parallel form (fragment entries)
   int64_t n_tokens() const { return int64_t(B) * T; }
 };
 
@@ -54,9 +55,16 @@ constexpr int kKdaFrags = 64;
 template <typename T> constexpr int64_t kda_entry_bytes() {
   return int64_t(kKdaFrags) * kFragElems * sizeof(T) + 128 * 4;
 }
+// The chained path (launch_chain_fwd, bwd.hip): every other one-pass chunked
+// forward (fp32 inputs, d_k < 128, or d_v not a multiple of 32).  Its entry
+// holds M = (I + A)^-1 and P in fp32 (C x C each, row-major) and a 256-float
+// gate block: the head of a backward entry.
+inline bool chain_path(const Problem &p) { return !p.per_channel && !staged_path(p) && !p.seg_pass; }
+constexpr int64_t chain_entry_bytes(int C) { return (int64_t(2) * C * C + 256) * 4; }
 inline int64_t entry_stride(const Problem &p) {
   if (p.per_channel) return p.dtype == 1 ? kda_entry_bytes<uint16_t>() : kda_entry_bytes<float>();
   if (staged_path(p)) return kStagedEntryBytes;
+  if (chain_path(p)) return chain_entry_bytes(p.chunk);
   return p.dtype == 1 ? entry_bytes<uint16_t>() : entry_bytes<float>();
 }
 
@@ -84,6 +92,10 @@ struct BwdProblem {
 };
 size_t bwd_entry_floats(int chunk, int d_k, int d_v);
 hipError_t launch_chunk_bwd(const BwdProblem &b, hipStream_t st);
+// The chained one-pass forward (chain_path problems): per-chunk factors, then
+// one block per (unit, 32 columns) walking the chunks with the state on fp32
+// MFMA and writing o (and hT).
+hipError_t launch_chain_fwd(const Problem &p, const Workspace &ws, hipStream_t st);
 hipError_t launch_kda_chunk(const Problem &p, const Workspace &ws, hipStream_t st);
 // Segment-parallel path (seqmap.hip, fold.hip).
 hipError_t launch_segment_map(const Problem &p, int seg_tokens, int n_seg_bound, int32_t *seg_cu,

@@ -40,19 +40,20 @@ def test_version_and_status_strings(lib):
 
 
 def test_workspace_query(lib):
-    # one entry per (chunk slot, value head).  General path: 16 fragments of
-    # 512 elements (1 KiB in bf16, 2 KiB in fp32) + a 1 KiB gate block.
-    # Staged path (bf16, d_k = 128, d_v a multiple of 32): T's non-zero
-    # bf16 fragments (four whole, two half) + gamma, s, g: 5,888 bytes.
-    entry, staged = 16 * 1024 + 1024, 5 * 1024 + 768
+    # one entry per (chunk slot, value head).  Staged path (bf16, d_k = 128,
+    # d_v a multiple of 32): T's non-zero bf16 fragments (four whole, two
+    # half) + gamma, s, g: 5,888 bytes.  Chained path (every other one-pass
+    # problem): M and P in fp32, C x C each, + a 256-float gate block.
+    staged = 5 * 1024 + 768
+    chained = lambda c: (2 * c * c + 256) * 4
     w = gdn.chunk_fwd_workspace_bytes(4, 4096, 16, 16, 128, 128, gdn.GDN_BF16, 64, 0)
     assert 4 * 64 * 16 * staged <= w < 4 * 64 * 16 * staged + 4096
     packed = gdn.chunk_fwd_workspace_bytes(1, 1000, 2, 4, 128, 128, gdn.GDN_BF16, 64, 5)
     assert (16 + 5) * 4 * staged <= packed < (16 + 5) * 4 * staged + 4096
     general = gdn.chunk_fwd_workspace_bytes(1, 1000, 2, 4, 64, 128, gdn.GDN_BF16, 64, 5)
-    assert (16 + 5) * 4 * entry <= general < (16 + 5) * 4 * entry + 4096
+    assert (16 + 5) * 4 * chained(64) <= general < (16 + 5) * 4 * chained(64) + 4096
     f32 = gdn.chunk_fwd_workspace_bytes(1, 64, 1, 1, 16, 16, gdn.GDN_F32, 16, 0)
-    assert f32 >= 4 * (16 * 2048 + 1024)
+    assert 4 * chained(16) <= f32 < 4 * chained(16) + 4096
     assert gdn.chunk_fwd_workspace_bytes(1, 64, 1, 1, 48, 64, gdn.GDN_BF16, 64, 0) == 0
     assert gdn.chunk_fwd_workspace_bytes(1, 64, 1, 1, 64, 64, gdn.GDN_BF16, 48, 0) == 0
     assert gdn.chunk_fwd_workspace_bytes(1, 64, 1, 1, 64, 64, 7, 64, 0) == 0
