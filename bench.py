@@ -38,6 +38,10 @@ projections drawn on the device, and gives each kernel's algorithmic bytes
 (every input read once, every output written once) as a fraction of HBM
 peak.
 
+``chunk_fwd_f32`` times the chunked forward with fp32 inputs on the prefill
+shape (the chained form, every product on fp32 MFMA), with the algorithmic
+flops as a fraction of the fp32 MFMA peak.
+
 ``chunk_bwd`` times the backward pass (gdn_chunk_bwd) on the prefill shape,
 with its products' flops as a fraction of the fp32 MFMA peak (the backward
 computes in fp32).
@@ -360,6 +364,37 @@ def kda_chunk_workload(args, gdn, gi, torch, dev, stream, evict):
     }}
 
 
+def chunk_fwd_f32_workload(args, gdn, gi, torch, dev, stream, evict):
+    """The chunked forward with fp32 inputs on the prefill shape (B=4, T=4096,
+    H=16, d=128, chunk 64): the prefill workload's inputs widened to fp32.
+    Off the bf16 staged path, this runs the chained form (every product on
+    fp32 MFMA)."""
+    spec = gi.config(2)
+    B, T = spec.B, spec.T
+    q, k, v, alpha, beta = device_inputs(torch, dev, spec, B * T, B, seed=spec.seed + 11)
+    q, k, v = q.float(), k.float(), v.float()
+    o = torch.empty_like(v)
+    hT = torch.empty((B, spec.H_v, spec.d_k, spec.d_v), dtype=torch.float32, device=dev)
+    ws = torch.empty(gdn.chunk_fwd_workspace_bytes(B, T, spec.H_qk, spec.H_v, spec.d_k, spec.d_v, gdn.GDN_F32,
+                                                   64, 0), dtype=torch.uint8, device=dev)
+    log("bench: chunked forward, fp32 inputs, prefill shape")
+
+    def call():
+        gdn.chunk_fwd(q, k, v, alpha, beta, chunk=64, o=o, hT=hT, workspace=ws, stream=stream)
+
+    t = timed_calls(args, torch, stream, evict, call)
+    tokens, units = B * T, B * spec.H_v
+    # q, k, v, o in fp32, alpha and beta per token-unit, the final states
+    nbytes = tokens * spec.H_v * (4 * 128 * 4 + 8) + units * 128 * 128 * 4
+    flops = tokens * spec.H_v * PREFILL_FLOPS_PER_TOKEN_UNIT
+    del q, k, v, alpha, beta, o, hT, ws
+    return {"chunk_fwd_f32": {
+        "workload": f"chunked forward B={B} T={T} H={spec.H_v} d=128 fp32 inputs, chunk 64",
+        "tokens_per_s": tokens / t, "us_per_call": t * 1e6, "bytes": nbytes, "flops": flops,
+        "hbm_frac": nbytes / t / HBM_PEAK, "mfma_f32_frac": flops / t / MFMA_F32_PEAK,
+    }}
+
+
 def chunk_bwd_workload(args, gdn, gi, torch, dev, stream, evict):
     """The backward pass (gdn_chunk_bwd) on the prefill shape (B=4, T=4096,
     H=16, d=128, bf16, chunk 64): the prefill workload's inputs and an
@@ -632,6 +667,7 @@ def main():
         extra.update(block_workload(args, gdn, torch, dev, stream, evict))
         extra.update(kda_decode_workload(args, gdn, torch, dev, stream, evict, Dd, state))
         extra.update(kda_chunk_workload(args, gdn, gi, torch, dev, stream, evict))
+        extra.update(chunk_fwd_f32_workload(args, gdn, gi, torch, dev, stream, evict))
         extra.update(chunk_bwd_workload(args, gdn, gi, torch, dev, stream, evict))
         extra.update(decode_graph_workload(args, gdn, torch, dev, stream))
 

@@ -86,6 +86,7 @@ struct BwdArgs {
   T *o;                   // the forward: outputs [tokens, H_v, d_v] and final states (or null)
   float *hT;
   bool want_g;            // the backward: the factor kernel also writes Gamma . K K^T
+  int cols;               // columns of d_v per forward-chain block: 16 or 32 (d_v >= 32), else d_v
   int H_qk, H_v, d_k, d_v, group, n_units;
   SeqGeom geo;
 };
@@ -292,8 +293,9 @@ __global__ __launch_bounds__(256) void bwd_factor_kernel(BwdArgs<T> a) {
 
 // ---------------------------------------------------------------------------
 // 2. The two chains, each on four waves over a column block of
-// CB = min(32, d_v) columns of one unit (the kernel below puts a chain of
-// each direction in one block where LDS allows).  With w the wave within its
+// CB = min(32, d_v) columns of one unit; the kernel below puts a chain of
+// each direction in one block where LDS allows, and the forward pass's own
+// chain also runs 16-column blocks when there are few units.  With w the wave within its
 // four: tiles of a C x CB product are i = w + 4m, row tile i % (C/16), column
 // tile i / (C/16), so a wave keeps one row tile; tiles of the d_k x CB state
 // are i = w + 4m, row tile i % (d_k/16), column tile i / (d_k/16).
@@ -373,7 +375,7 @@ template <typename T, int C, bool OUT>
 __device__ void fwd_chain(const BwdArgs<T> &a, int u, int cb, char *smem) {
   using Lds = ChainLds<T, C>;
   constexpr int NRT = C / 16, LDK = Lds::LDK, LDT = Lds::LDT, LDC = Lds::LDC;
-  const int DK = a.d_k, DV = a.d_v, CB = min(32, DV), c0 = cb * CB;
+  const int DK = a.d_k, DV = a.d_v, CB = a.cols, c0 = cb * CB;
   const int NKT = DK / 16, NCT = CB / 16;
   const int tid = threadIdx.x % kChainThreads, w = tid >> 6, lane = tid & 63, r = lane & 15, g = lane >> 4;
   T *sK = reinterpret_cast<T *>(smem);
@@ -802,7 +804,8 @@ __device__ void rev_chain(const BwdArgs<T> &a, int u, int cb, char *smem) {
 // groups of 8 units x column blocks: the blocks of a unit have the same block
 // id mod 8, so they share one XCD's L2 copy of its k and q.
 template <typename T, int C>
-__global__ __launch_bounds__(2 * kChainThreads) void bwd_chain_kernel(BwdArgs<T> a) {
+__global__ __launch_bounds__((ChainLds<T, C>::kPaired ? 2 * kChainThreads : kChainThreads)) void bwd_chain_kernel(
+    BwdArgs<T> a) {
   using Lds = ChainLds<T, C>;
   const int n_cb = a.d_v / min(32, a.d_v);
   int u, x;
@@ -833,7 +836,7 @@ template <typename T, int C>
 __global__ __launch_bounds__(kChainThreads, 2) void chain_fwd_kernel(BwdArgs<T> a) {
   using Lds = ChainLds<T, C>;
   __shared__ __attribute__((aligned(16))) char smem[Lds::kOut];
-  const int n_cb = a.d_v / min(32, a.d_v);
+  const int n_cb = a.d_v / a.cols;
   int u, x;
   decode_block(blockIdx.x, n_cb, u, x);
   if (u >= a.n_units) return;
@@ -1185,6 +1188,7 @@ static hipError_t launch_chunk_bwd_t(const BwdProblem &b, hipStream_t st) {
   a.o = nullptr;
   a.hT = nullptr;
   a.want_g = true;
+  a.cols = std::min(32, p.d_v);
   a.H_qk = p.H_qk;
   a.H_v = p.H_v;
   a.d_k = p.d_k;
@@ -1225,7 +1229,7 @@ static hipError_t launch_chain_fwd_c(const BwdArgs<T> &a, hipStream_t st) {
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  const int n_cb = a.d_v / std::min(32, a.d_v);
+  const int n_cb = a.d_v / a.cols;
   const int64_t groups = (int64_t(a.n_units) + 7) / 8;
   hipLaunchKernelGGL((chain_fwd_kernel<T, C>), dim3(unsigned(groups * 8 * n_cb)), dim3(kChainThreads), 0, st, a);
   return hipGetLastError();
@@ -1251,6 +1255,9 @@ static hipError_t launch_chain_fwd_t(const Problem &p, const Workspace &ws, hipS
   a.d_v = p.d_v;
   a.group = p.H_v / p.H_qk;
   a.n_units = p.n_seqs * p.H_v;
+  // 16-column blocks where 32-column ones would leave CUs without a chain
+  a.cols = std::min(32, p.d_v);
+  if (a.cols == 32 && int64_t(a.n_units) * (p.d_v / 32) < 256) a.cols = 16;
   a.geo = make_geom(p, &ws);
   if (a.n_units == 0) return hipSuccess;
   return p.chunk == 16   ? launch_chain_fwd_c<T, 16>(a, st)
