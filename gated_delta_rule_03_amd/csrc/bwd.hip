@@ -133,19 +133,19 @@ __device__ __forceinline__ void lower_tile(int k, int &rt, int &ct) {
 constexpr int kChainThreads = 256;
 
 // One chunk's token-row tile (K or Q: C rows x d_k of T) as 16-byte pieces in
-// registers, then in LDS.  Rows at or past n read as zero.  Branch-free (an
+// the registers of NTH threads, then in LDS.  Rows at or past n read as zero.  Branch-free (an
 // index past the tile is clamped onto its last piece, which then is loaded
 // and stored twice with the same value), so that the compiler can count the
 // loads still in flight exactly and wait only for these.
-template <typename T, int C> struct TileLoader {
+template <typename T, int C, int NTH = kChainThreads> struct TileLoader {
   static constexpr int EPP = 16 / sizeof(T);
-  static constexpr int MAXP = (C * 128 / EPP + kChainThreads - 1) / kChainThreads;
+  static constexpr int MAXP = (C * 128 / EPP + NTH - 1) / NTH;
   uint4 v[MAXP];
   __device__ __forceinline__ void load(const T *base, int64_t row_stride, int n, int DK) {
     const int ppr = DK / EPP, np = C * ppr;
 #pragma unroll
     for (int m = 0; m < MAXP; ++m) {
-      const int p = min(int(threadIdx.x % kChainThreads) + kChainThreads * m, np - 1);
+      const int p = min(int(threadIdx.x % NTH) + NTH * m, np - 1);
       const int t = p / ppr, c = (p - t * ppr) * EPP;
       const uint4 x = *reinterpret_cast<const uint4 *>(base + int64_t(min(t, n - 1)) * row_stride + c);
       v[m] = t < n ? x : make_uint4(0, 0, 0, 0);
@@ -155,7 +155,7 @@ template <typename T, int C> struct TileLoader {
     const int ppr = DK / EPP, np = C * ppr;
 #pragma unroll
     for (int m = 0; m < MAXP; ++m) {
-      const int p = min(int(threadIdx.x % kChainThreads) + kChainThreads * m, np - 1);
+      const int p = min(int(threadIdx.x % NTH) + NTH * m, np - 1);
       const int t = p / ppr, c = (p - t * ppr) * EPP;
       *reinterpret_cast<uint4 *>(lds + t * ldk + c) = v[m];
     }
@@ -176,15 +176,15 @@ __global__ __launch_bounds__(256) void bwd_factor_kernel(BwdArgs<T> a) {
   if (!a.geo.locate(slot, s, tok0, n)) return;
   const int hq = h / a.group, DK = a.d_k;
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, r = lane & 15, g = lane >> 4;
-  // LDS: A; then the chunk's K and Q rows, whose space M takes once the
-  // products below are done
+  // LDS: the chunk's K and Q rows.  A takes Q's space once P is formed, and
+  // M takes K's once A is (fp32 inputs: two blocks per CU, bf16: four)
   constexpr int LDK = 128 + 16 / sizeof(T);
   constexpr int kTileBytes = C * LDK * sizeof(T);
-  constexpr int kBufBytes = 2 * kTileBytes > C * LD * 4 ? 2 * kTileBytes : C * LD * 4;
-  __shared__ __attribute__((aligned(16))) float sA[C * LD];
-  __shared__ __attribute__((aligned(16))) char sBuf[kBufBytes];
+  static_assert(kTileBytes >= C * LD * 4, "A and M each fit in a row tile's space");
+  __shared__ __attribute__((aligned(16))) char sBuf[2 * kTileBytes];
   __shared__ float sg[64], sb[64];
   T *sK = reinterpret_cast<T *>(sBuf), *sQ = reinterpret_cast<T *>(sBuf + kTileBytes);
+  float *sA = reinterpret_cast<float *>(sBuf + kTileBytes);
   float *sM = reinterpret_cast<float *>(sBuf);
   float *ent = a.ent + int64_t(e) * a.ent_floats;
   const BwdEntry L(C, DK, a.d_v);
@@ -204,7 +204,6 @@ __global__ __launch_bounds__(256) void bwd_factor_kernel(BwdArgs<T> a) {
         sb[lane] = in ? be : 0.0f;
       }
     }
-    for (int i = tid; i < C * LD; i += 256) sA[i] = 0.0f;
     // P and Gamma . K K^T are zero above the diagonal tiles, for the gradient
     // kernel (the forward chain reads only the lower tiles of P)
     if (a.want_g) {
@@ -220,27 +219,31 @@ __global__ __launch_bounds__(256) void bwd_factor_kernel(BwdArgs<T> a) {
     ql.store(sQ, LDK, DK);
   }
   __syncthreads();
-  // lower tiles of K K^T and Q K^T (contraction over d_k); each leaves as
-  // Gamma . K K^T (strict lower; A = diag(beta) times it into LDS) or as
-  // P = Gamma . Q K^T (lower)
-  for (int job = w; job < 2 * NL; job += 4) {
-    const int mat = job / NL;
-    int rt, ct;
-    lower_tile(job - mat * NL, rt, ct);
-    const T *pa = (mat ? sQ : sK) + (16 * rt + r) * LDK + 4 * g;
-    const T *pb = sK + (16 * ct + r) * LDK + 4 * g;
-    f32x4_t acc = zero4();
-    for (int k0 = 0; k0 < DK; k0 += 16) acc = mm16(row4(pa + k0), row4(pb + k0), acc);
+  // lower tiles of Q K^T and then of K K^T (contraction over d_k); each
+  // leaves as P = Gamma . Q K^T (lower) or as Gamma . K K^T (strict lower;
+  // A = diag(beta) times it into LDS).  Every tile of A that the inverse
+  // reads is written here (the diagonal tiles' upper halves as zeros).
+  for (int pass = 0; pass < 2; ++pass) {
+    const bool mat_q = pass == 0;
+    if (!mat_q) __syncthreads();  // Q is dead: A takes its space
+    for (int job = w; job < NL; job += 4) {
+      int rt, ct;
+      lower_tile(job, rt, ct);
+      const T *pa = (mat_q ? sQ : sK) + (16 * rt + r) * LDK + 4 * g;
+      const T *pb = sK + (16 * ct + r) * LDK + 4 * g;
+      f32x4_t acc = zero4();
+      for (int k0 = 0; k0 < DK; k0 += 16) acc = mm16(row4(pa + k0), row4(pb + k0), acc);
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const int t = 16 * rt + 4 * g + q, i = 16 * ct + r;
-      const float gam = i <= t ? fast_exp2(sg[t] - sg[i]) : 0.0f;
-      if (mat) {
-        ent[L.P + t * C + i] = gam * acc[q];
-      } else {
-        const float gkk = i < t ? gam * acc[q] : 0.0f;
-        if (a.want_g) ent[L.G + t * C + i] = gkk;
-        sA[t * LD + i] = sb[t] * gkk;
+      for (int q = 0; q < 4; ++q) {
+        const int t = 16 * rt + 4 * g + q, i = 16 * ct + r;
+        const float gam = i <= t ? fast_exp2(sg[t] - sg[i]) : 0.0f;
+        if (mat_q) {
+          ent[L.P + t * C + i] = gam * acc[q];
+        } else {
+          const float gkk = i < t ? gam * acc[q] : 0.0f;
+          if (a.want_g) ent[L.G + t * C + i] = gkk;
+          sA[t * LD + i] = sb[t] * gkk;
+        }
       }
     }
   }
@@ -251,7 +254,7 @@ __global__ __launch_bounds__(256) void bwd_factor_kernel(BwdArgs<T> a) {
     ent[L.gate + kGateLog2 + tid] = sg[tid];
     ent[L.gate + kGateBeta + tid] = sb[tid];
   }
-  __syncthreads();  // K and Q are dead: M takes their space
+  __syncthreads();  // K is dead: M takes its space
   for (int i = tid; i < C * LD; i += 256) sM[i] = 0.0f;
   __syncthreads();
   // (I + A)^-1 by 16 x 16 blocks: the diagonal blocks by forward substitution
@@ -371,13 +374,17 @@ __device__ __forceinline__ void unit_of(const SeqGeom &geo, int H_v, int u, int 
 // entry.  For the forward pass itself (OUT = true) it stores nothing in the
 // entries: it also stages the chunk's Q rows, forms
 // O = diag(gamma) Q S + P U, and writes O and the last state.
-template <typename T, int C, bool OUT>
+template <typename T, int C, bool OUT, int NW = 4>
 __device__ void fwd_chain(const BwdArgs<T> &a, int u, int cb, char *smem) {
   using Lds = ChainLds<T, C>;
   constexpr int NRT = C / 16, LDK = Lds::LDK, LDT = Lds::LDT, LDC = Lds::LDC;
+  // NW waves; a wave's C x CB tiles (at most 8 in all) and d_k x CB state
+  // tiles (at most 16) are i = w + NW m
+  constexpr int NTH = 64 * NW, MT = (8 + NW - 1) / NW, MS = (16 + NW - 1) / NW;
+  static_assert(NW % NRT == 0, "a wave keeps one row tile");
   const int DK = a.d_k, DV = a.d_v, CB = a.cols, c0 = cb * CB;
   const int NKT = DK / 16, NCT = CB / 16;
-  const int tid = threadIdx.x % kChainThreads, w = tid >> 6, lane = tid & 63, r = lane & 15, g = lane >> 4;
+  const int tid = threadIdx.x % NTH, w = tid >> 6, lane = tid & 63, r = lane & 15, g = lane >> 4;
   T *sK = reinterpret_cast<T *>(smem);
   T *sQ = reinterpret_cast<T *>(smem + Lds::kTile);                           // OUT only
   float *sSt = reinterpret_cast<float *>(smem + (OUT ? 2 : 1) * Lds::kTile);  // S^T
@@ -390,15 +397,15 @@ __device__ void fwd_chain(const BwdArgs<T> &a, int u, int cb, char *smem) {
   const BwdEntry L(C, DK, DV);
   const int64_t krow = int64_t(a.H_qk) * DK, vrow = int64_t(a.H_v) * DV;
 
-  // this wave's C x CB tiles (one row tile, column tiles ct0 and ct0 + 1) and state tiles
+  // this wave's C x CB tiles (one row tile) and state tiles
   const int rt = w % NRT;
-  const int nmine = (w < NRT * NCT) ? ((w + 4 < NRT * NCT) ? 2 : 1) : 0;
+  const int nmine = (w < NRT * NCT) ? ((MT > 1 && w + NW < NRT * NCT) ? 2 : 1) : 0;
   const int nst = NKT * NCT;
-  f32x4_t accS[4];
+  f32x4_t accS[MS];
 #pragma unroll
-  for (int m = 0; m < 4; ++m) {
+  for (int m = 0; m < MS; ++m) {
     accS[m] = zero4();
-    const int i = w + 4 * m;
+    const int i = w + NW * m;
     if (i < nst && a.h0) {
       const int kt = i % NKT, ct = i / NKT;
       const float *h0 = a.h0 + (int64_t(s) * a.H_v + h) * DK * DV;
@@ -411,8 +418,8 @@ __device__ void fwd_chain(const BwdArgs<T> &a, int u, int cb, char *smem) {
     if (!OUT || !a.hT) return;
     float *hT = a.hT + (int64_t(s) * a.H_v + h) * DK * DV;
 #pragma unroll
-    for (int m = 0; m < 4; ++m) {
-      const int i = w + 4 * m;
+    for (int m = 0; m < MS; ++m) {
+      const int i = w + NW * m;
       if (i < nst) {
         const int kt = i % NKT, ct = i / NKT;
 #pragma unroll
@@ -425,17 +432,17 @@ __device__ void fwd_chain(const BwdArgs<T> &a, int u, int cb, char *smem) {
     return;
   }
 
-  TileLoader<T, C> kl, ql;
+  TileLoader<T, C, NTH> kl, ql;
   GateLoader gl;
   // V at this wave's accumulator positions and the A fragments of M (and for
   // OUT of P, lower tiles only) for its row tile: loaded a chunk ahead, right
   // after their last use
-  f32x4_t vcur[2], mcur[NRT], pcur[NRT];
+  f32x4_t vcur[MT], mcur[NRT], pcur[NRT];
   auto load_v = [&](int cc) {
     const int tok0 = start + cc * C, n = min(C, end - tok0);
 #pragma unroll
-    for (int m = 0; m < 2; ++m) {
-      const int ct = min((w + 4 * m) / NRT, NCT - 1);
+    for (int m = 0; m < MT; ++m) {
+      const int ct = min((w + NW * m) / NRT, NCT - 1);
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         const int t = 16 * rt + 4 * g + q;
@@ -472,8 +479,8 @@ __device__ void fwd_chain(const BwdArgs<T> &a, int u, int cb, char *smem) {
     float *ent = a.ent + (int64_t(c_first + cc) * a.H_v + h) * a.ent_floats;
     // the state entering this chunk: to LDS, transposed (operand of K S and Q S), and to the entry
 #pragma unroll
-    for (int m = 0; m < 4; ++m) {
-      const int i = w + 4 * m;
+    for (int m = 0; m < MS; ++m) {
+      const int i = w + NW * m;
       if (i < nst) {
         const int kt = i % NKT, ct = i / NKT;
         *reinterpret_cast<f32x4_t *>(sSt + (16 * ct + r) * LDT + 16 * kt + 4 * g) = accS[m];
@@ -488,9 +495,13 @@ __device__ void fwd_chain(const BwdArgs<T> &a, int u, int cb, char *smem) {
     load_tiles(nx);
     lds_sync();
     // X = V - diag(gamma) K S;  Y = diag(beta) X;  for OUT also diag(gamma) Q S
-    f32x4_t oacc[2] = {zero4(), zero4()};
+    f32x4_t oacc[MT];
+#pragma unroll
+    for (int m = 0; m < MT; ++m) oacc[m] = zero4();
     if (nmine > 0) {
-      f32x4_t acc[2] = {zero4(), zero4()}, qacc[2] = {zero4(), zero4()};
+      f32x4_t acc[MT], qacc[MT];
+#pragma unroll
+      for (int m = 0; m < MT; ++m) acc[m] = qacc[m] = zero4();
 #pragma unroll
       for (int kk = 0; kk < 8; ++kk) {
         if (16 * kk < DK) {
@@ -498,9 +509,9 @@ __device__ void fwd_chain(const BwdArgs<T> &a, int u, int cb, char *smem) {
           f32x4_t qr = zero4();
           if constexpr (OUT) qr = row4(sQ + (16 * rt + r) * LDK + 16 * kk + 4 * g);
 #pragma unroll
-          for (int m = 0; m < 2; ++m) {
+          for (int m = 0; m < MT; ++m) {
             if (m < nmine) {
-              const f32x4_t st = row4(sSt + (16 * ((w + 4 * m) / NRT) + r) * LDT + 16 * kk + 4 * g);
+              const f32x4_t st = row4(sSt + (16 * ((w + NW * m) / NRT) + r) * LDT + 16 * kk + 4 * g);
               acc[m] = mm16(xr, st, acc[m]);
               if constexpr (OUT) qacc[m] = mm16(qr, st, qacc[m]);
             }
@@ -509,9 +520,9 @@ __device__ void fwd_chain(const BwdArgs<T> &a, int u, int cb, char *smem) {
       }
       const f32x4_t gam = row4(sgate + 16 * rt + 4 * g), be = row4(sgate + 128 + 16 * rt + 4 * g);
 #pragma unroll
-      for (int m = 0; m < 2; ++m) {
+      for (int m = 0; m < MT; ++m) {
         if (m < nmine) {
-          const int col = 16 * ((w + 4 * m) / NRT) + r;
+          const int col = 16 * ((w + NW * m) / NRT) + r;
           const f32x4_t x = vcur[m] - gam * acc[m];
           if constexpr (!OUT) {
 #pragma unroll
@@ -529,9 +540,9 @@ __device__ void fwd_chain(const BwdArgs<T> &a, int u, int cb, char *smem) {
     if (nmine > 0) {
       const f32x4_t sc = row4(sgate + 64 + 16 * rt + 4 * g);
 #pragma unroll
-      for (int m = 0; m < 2; ++m) {
+      for (int m = 0; m < MT; ++m) {
         if (m < nmine) {
-          const int col = 16 * ((w + 4 * m) / NRT) + r;
+          const int col = 16 * ((w + NW * m) / NRT) + r;
           f32x4_t acc = zero4();
 #pragma unroll
           for (int kb = 0; kb < NRT; ++kb) acc = mm16(mcur[kb], row4(sYt + col * LDC + 16 * kb + 4 * g), acc);
@@ -550,8 +561,8 @@ __device__ void fwd_chain(const BwdArgs<T> &a, int u, int cb, char *smem) {
     // S <- gamma_C S + K^T diag(s) U
     const float gC = sgate[C - 1];
 #pragma unroll
-    for (int m = 0; m < 4; ++m) {
-      const int i = w + 4 * m;
+    for (int m = 0; m < MS; ++m) {
+      const int i = w + NW * m;
       if (i < nst) {
         const int kt = i % NKT, ct = i / NKT;
         f32x4_t acc = accS[m] * gC;
@@ -569,9 +580,9 @@ __device__ void fwd_chain(const BwdArgs<T> &a, int u, int cb, char *smem) {
       if (nmine > 0) {
         const int tok0 = start + cc * C, n = min(C, end - tok0);
 #pragma unroll
-        for (int m = 0; m < 2; ++m) {
+        for (int m = 0; m < MT; ++m) {
           if (m < nmine) {
-            const int col = 16 * ((w + 4 * m) / NRT) + r;
+            const int col = 16 * ((w + NW * m) / NRT) + r;
             f32x4_t acc = oacc[m];
 #pragma unroll
             for (int kb = 0; kb < NRT; ++kb)
@@ -832,16 +843,20 @@ __global__ __launch_bounds__((ChainLds<T, C>::kPaired ? 2 * kChainThreads : kCha
 // The forward pass on the chained form: one block of four waves per (unit,
 // column block), in the same XCD-aware order, running the forward chain with
 // outputs.
-template <typename T, int C>
-__global__ __launch_bounds__(kChainThreads, 2) void chain_fwd_kernel(BwdArgs<T> a) {
+template <typename T, int C, int NW>
+__global__ __launch_bounds__(64 * NW, 8 / NW) void chain_fwd_kernel(BwdArgs<T> a) {
   using Lds = ChainLds<T, C>;
   __shared__ __attribute__((aligned(16))) char smem[Lds::kOut];
   const int n_cb = a.d_v / a.cols;
   int u, x;
   decode_block(blockIdx.x, n_cb, u, x);
   if (u >= a.n_units) return;
-  fwd_chain<T, C, true>(a, u, x, smem);
+  fwd_chain<T, C, true, NW>(a, u, x, smem);
 }
+// Waves per forward-pass chain block: fp32 operands fill enough LDS that a CU
+// holds one block, so it gets eight waves (two per SIMD) to hide LDS and
+// barrier waits; a bf16 block has four, and a CU holds two.
+template <typename T> constexpr int chain_fwd_waves() { return sizeof(T) == 4 ? 8 : 4; }
 
 // ---------------------------------------------------------------------------
 // 3. Per (chunk, value head): the gradients.  16 waves.
@@ -1231,7 +1246,8 @@ static hipError_t launch_chain_fwd_c(const BwdArgs<T> &a, hipStream_t st) {
   }
   const int n_cb = a.d_v / a.cols;
   const int64_t groups = (int64_t(a.n_units) + 7) / 8;
-  hipLaunchKernelGGL((chain_fwd_kernel<T, C>), dim3(unsigned(groups * 8 * n_cb)), dim3(kChainThreads), 0, st, a);
+  constexpr int NW = chain_fwd_waves<T>();
+  hipLaunchKernelGGL((chain_fwd_kernel<T, C, NW>), dim3(unsigned(groups * 8 * n_cb)), dim3(64 * NW), 0, st, a);
   return hipGetLastError();
 }
 

@@ -96,6 +96,36 @@ def test_small_uniform(gdn, case, path):
     check(gdn, path, w, h0=h0, chunk=chunk)
 
 
+# Off the staged path (fp32 inputs, d_k < 128, d_v = 16) the chunked forward
+# runs the chained kernels.  Below 256 blocks of 32 value columns they use
+# 16-column blocks (every small case above); these have enough units for
+# 32-column blocks, with grouped heads, packed sequences and every chunk size.
+CHAINED_WIDE = [
+    # dtype, B, T, H_qk, H_v, d_k, d_v, chunk
+    ("f32", 4, 70, 16, 16, 128, 128, 64),
+    ("bf16", 2, 100, 64, 128, 64, 64, 32),
+    ("f32", 8, 40, 32, 32, 32, 32, 16),
+]
+
+
+@pytest.mark.parametrize("case", CHAINED_WIDE, ids=[f"{c[0]}-B{c[1]}T{c[2]}H{c[3]}_{c[4]}d{c[5]}_{c[6]}C{c[7]}"
+                                                    for c in CHAINED_WIDE])
+def test_chained_wide_blocks(gdn, case):
+    dtype, B, T, H_qk, H_v, d_k, d_v, chunk = case
+    assert B * H_v * (d_v // 32) >= 256
+    w = small(dtype, B, T, H_qk, H_v, d_k, d_v, chunk, seed=150 + CHAINED_WIDE.index(case))
+    check(gdn, "chunk", w, chunk=chunk)
+    check(gdn, "chunk", w, h0=gi.random_state((B, H_v, d_k, d_v), seed=13, scale=0.3), chunk=chunk)
+
+
+def test_chained_wide_blocks_packed(gdn):
+    lengths = (0, 1, 63, 64, 65, 130, 7, 200) * 4
+    w = small("f32", 1, 0, 8, 32, 64, 64, 64, seed=160, lengths=lengths)
+    assert len(lengths) * 32 * 2 >= 256
+    check(gdn, "chunk", w)
+    check(gdn, "chunk", w, h0=gi.random_state((len(lengths), 32, 64, 64), seed=14, scale=0.3))
+
+
 # bf16 with d_k = 128 and d_v a multiple of 32 runs the staged kernels: value
 # widths of one and two 32-column blocks, unit counts that are not a
 # multiple of the eight-unit block groups, a single partial chunk, one token,
