@@ -29,6 +29,8 @@
 // Ktil^T (A-operand fragments, rows = key channels) in MFMA fragment order,
 // then Gamma_C; the scan walks each unit's chunks in order with the state in
 // accumulator registers, one wave per 16 state columns.
+#include <type_traits>
+
 #include "launch.hpp"
 #include "stage.hpp"
 
@@ -56,9 +58,20 @@ constexpr int kKRow = 129;  // fp32 row stride of the LDS token x channel tiles 
 
 // ---------------------------------------------------------------------------
 // Prep: one block of 512 threads per (chunk slot, value head).
+//
+// LDS holds k and q rows in the input type and G in fp32; the scaled operands
+// 2^G k, 2^G q and 2^-G k of the A and P products are formed as they are
+// read.  P is formed first, so that A can take q's space and M then k's
+// (bf16 inputs: 66 KiB, two blocks per CU).
 // ---------------------------------------------------------------------------
+template <typename T> struct KdaRows;
+template <> struct KdaRows<bf16_t> { static constexpr int LD = 132; };  // 264-byte rows: 8-byte aligned stores
+template <> struct KdaRows<float> { static constexpr int LD = kKRow; };
+
 template <typename T>
-__global__ __launch_bounds__(512) void kda_prep_kernel(KdaArgs<T> a) {
+__global__ __launch_bounds__(512, (sizeof(T) == 2 ? 4 : 2)) void kda_prep_kernel(KdaArgs<T> a) {
+  constexpr int LDT = KdaRows<T>::LD;
+  static_assert(64 * LDT * sizeof(T) >= 64 * 65 * 4, "A and M fit in a row tile's space");
   const int c = blockIdx.x, h = blockIdx.y;
   int s, tok0, len;
   if (!a.geo.locate(c, s, tok0, len)) return;
@@ -67,13 +80,13 @@ __global__ __launch_bounds__(512) void kda_prep_kernel(KdaArgs<T> a) {
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int dk = a.d_k;
 
-  __shared__ float sG[64 * kKRow];   // G_t per channel (log2), padded slots repeat the last token's
-  __shared__ float sK[64 * kKRow];   // k rows, zero past the chunk's end
-  __shared__ float sQ[64 * kKRow];   // q rows
-  __shared__ float sA[64][65];       // A (strictly lower), then the inverse's blocks alias sK / sQ
+  __shared__ float sG[64 * kKRow];                                 // G_t per channel (log2)
+  __shared__ __attribute__((aligned(16))) T sK[64 * LDT];          // k rows, zero past the chunk's end
+  __shared__ __attribute__((aligned(16))) T sQ[64 * LDT];          // q rows
   __shared__ float sb[64];
-  float(*sM)[65] = reinterpret_cast<float(*)[65]>(sK);           // M = (I + A)^-1 (after the tiles)
-  float(*sY)[16][17] = reinterpret_cast<float(*)[16][17]>(sQ);  // block products
+  float(*sA)[65] = reinterpret_cast<float(*)[65]>(sQ);             // A (strictly lower), once P is formed
+  float(*sM)[65] = reinterpret_cast<float(*)[65]>(sK);             // M = (I + A)^-1, once A is formed
+  float(*sY)[16][17] = reinterpret_cast<float(*)[16][17]>(sG);     // the inverse's block products
 
   const int64_t qk_stride = int64_t(a.H_qk) * dk;
   const T *kb = a.k + int64_t(tok0) * qk_stride + int64_t(hq) * dk;
@@ -87,15 +100,17 @@ __global__ __launch_bounds__(512) void kda_prep_kernel(KdaArgs<T> a) {
   // (the latter rewrite the same values), then zeroed ----
   {
     constexpr int kPieces = (16 * 128 + 511) / 512;
+    using Piece = typename std::conditional<sizeof(T) == 2, uint2, uint4>::type;  // four elements of T
     const int np = 16 * dk;
-    float4 kv[kPieces], qv[kPieces], av[kPieces];
+    Piece kv[kPieces], qv[kPieces];
+    float4 av[kPieces];
 #pragma unroll
     for (int m = 0; m < kPieces; ++m) {
       const int idx = min(tid + 512 * m, np - 1);
       const int t = idx / (dk / 4), ch = 4 * (idx - t * (dk / 4));
       const int64_t tc = min(t, len - 1);
-      kv[m] = load4_f32(kb + tc * qk_stride + ch);
-      qv[m] = load4_f32(qb + tc * qk_stride + ch);
+      kv[m] = *reinterpret_cast<const Piece *>(kb + tc * qk_stride + ch);
+      qv[m] = *reinterpret_cast<const Piece *>(qb + tc * qk_stride + ch);
       av[m] = *reinterpret_cast<const float4 *>(ab + tc * a_stride + ch);
     }
 #pragma unroll
@@ -103,9 +118,20 @@ __global__ __launch_bounds__(512) void kda_prep_kernel(KdaArgs<T> a) {
       const int idx = min(tid + 512 * m, np - 1);
       const int t = idx / (dk / 4), ch = 4 * (idx - t * (dk / 4));
       const bool in = t < len;
-      float *pk = sK + t * kKRow + ch, *pq = sQ + t * kKRow + ch, *pg = sG + t * kKRow + ch;
-      pk[0] = in ? kv[m].x : 0.0f; pk[1] = in ? kv[m].y : 0.0f; pk[2] = in ? kv[m].z : 0.0f; pk[3] = in ? kv[m].w : 0.0f;
-      pq[0] = in ? qv[m].x : 0.0f; pq[1] = in ? qv[m].y : 0.0f; pq[2] = in ? qv[m].z : 0.0f; pq[3] = in ? qv[m].w : 0.0f;
+      const Piece zero{};
+      const Piece kp = in ? kv[m] : zero, qp = in ? qv[m] : zero;
+      if constexpr (sizeof(T) == 2) {  // 8-byte aligned: LDT is a multiple of 4
+        *reinterpret_cast<Piece *>(sK + t * LDT + ch) = kp;
+        *reinterpret_cast<Piece *>(sQ + t * LDT + ch) = qp;
+      } else {  // the odd fp32 row stride allows 4-byte stores only
+        const float *kf = reinterpret_cast<const float *>(&kp), *qf = reinterpret_cast<const float *>(&qp);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          sK[t * LDT + ch + e] = kf[e];
+          sQ[t * LDT + ch + e] = qf[e];
+        }
+      }
+      float *pg = sG + t * kKRow + ch;
       pg[0] = in ? clamped_log2(av[m].x) : 0.0f;
       pg[1] = in ? clamped_log2(av[m].y) : 0.0f;
       pg[2] = in ? clamped_log2(av[m].z) : 0.0f;
@@ -145,6 +171,8 @@ __global__ __launch_bounds__(512) void kda_prep_kernel(KdaArgs<T> a) {
   char *entry = a.entries + (int64_t(c) * a.H_v + h) * kda_entry_bytes<T>();
   T *frag = reinterpret_cast<T *>(entry);
   float *gamma_C = reinterpret_cast<float *>(frag + kKdaFrags * kFragElems);
+  auto kval = [&](int t, int ch) { return to_f32(sK[t * LDT + ch]); };
+  auto qval = [&](int t, int ch) { return to_f32(sQ[t * LDT + ch]); };
 
   // ---- pre-scaled operands, A-operand fragments in the kappa convention ----
   // Khat, Qhat: fragment (rt, kk) holds rows 16 rt + lane mod 16, channels 32 kk + kappa.
@@ -156,7 +184,7 @@ __global__ __launch_bounds__(512) void kda_prep_kernel(KdaArgs<T> a) {
     for (int j = 0; j < 8; ++j) {
       const int ch = 32 * kk + kappa(lane, j);
       float x = 0.0f;
-      if (ch < dk) x = fast_exp2(sG[t * kKRow + ch]) * (isq ? sQ : sK)[t * kKRow + ch];
+      if (ch < dk) x = fast_exp2(sG[t * kKRow + ch]) * (isq ? qval(t, ch) : kval(t, ch));
       fr.set(j, x);
     }
     store_frag(frag + ((isq ? kKdaFragQh : kKdaFragKh) + ff) * kFragElems, lane, fr);
@@ -169,87 +197,82 @@ __global__ __launch_bounds__(512) void kda_prep_kernel(KdaArgs<T> a) {
     for (int j = 0; j < 8; ++j) {
       const int i = 32 * kk + kappa(lane, j);
       float x = 0.0f;
-      if (ch < dk) x = fast_exp2(sG[63 * kKRow + ch] - sG[i * kKRow + ch]) * sK[i * kKRow + ch];
+      if (ch < dk) x = fast_exp2(sG[63 * kKRow + ch] - sG[i * kKRow + ch]) * kval(i, ch);
       fr.set(j, x);
     }
     store_frag(frag + (kKdaFragKt + f) * kFragElems, lane, fr);
   }
   if (tid < 128) gamma_C[tid] = tid < dk ? fast_exp2(sG[63 * kKRow + tid]) : 0.0f;
 
-  // ---- A and P ----
+  // ---- P, then A ----
   // When every cumulative log gate of the chunk lies within [-60, 60], the
   // exponent of the channel sums factors without overflow:
   // 2^(G_tc - G_ic) = 2^(G_tc) 2^(-G_ic), both factors in [2^-60, 2^60], so
   //   A_ti = beta_t (Khat Kinv^T)_ti,  P_ti = (Qhat Kinv^T)_ti,
   // Khat = 2^G . k, Qhat = 2^G . q, Kinv = 2^-G . k, each a 64 x 64 x d_k
-  // product (fp32 MFMA, the lower tiles only).  Otherwise (a chunk that decays
-  // by more than 2^60, e.g. through alpha = 0) every pair i <= t is summed
-  // with one exact exponent per channel.
+  // product (fp32 MFMA, the lower tiles only, operands scaled as they are
+  // read).  Otherwise (a chunk that decays by more than 2^60, e.g. through
+  // alpha = 0) every pair i <= t is summed with one exact exponent per
+  // channel.  P goes first: A then takes q's space.
   T *fragP = frag + kKdaFragP * kFragElems;
   auto put_p = [&](int t, int i, float x) {
     const int ii = i & 31, kk = i >> 5;
     const int ln = 16 * ((ii & 15) >> 2) + (t & 15), el = 4 * (ii >> 4) + (ii & 3);
     fragP[((t >> 4) * 2 + kk) * kFragElems + 8 * ln + el] = from_f32<T>(x);
   };
+  // the upper tiles of P's fragments are zero
+  for (int idx = tid; idx < 6 * 256; idx += 512) {
+    const int tile = idx >> 8, e = idx & 255;
+    const int rt = tile < 3 ? 0 : (tile < 5 ? 1 : 2), ct = tile < 3 ? tile + 1 : (tile < 5 ? tile - 1 : 3);
+    put_p(16 * rt + (e >> 4), 16 * ct + (e & 15), 0.0f);
+  }
   bool far = false;
   for (int idx = tid; idx < 64 * dk; idx += 512) {
     const int t = idx / dk, ch = idx - t * dk;
     far |= fabsf(sG[t * kKRow + ch]) > 60.0f;
   }
-  lds_barrier();  // every fragment above has read sK, sQ and sG
-  if (!__syncthreads_or(far)) {
-    // scale in place: sK <- 2^G k, sQ <- 2^G q, sG <- 2^-G k
-    for (int idx = tid; idx < 64 * dk; idx += 512) {
-      const int t = idx / dk, ch = idx - t * dk;
-      const int o = t * kKRow + ch;
-      const float gg = sG[o], kv = sK[o];
-      sK[o] = fast_exp2(gg) * kv;
-      sQ[o] = fast_exp2(gg) * sQ[o];
-      sG[o] = fast_exp2(-gg) * kv;
-    }
-    lds_barrier();
-    // 20 tile products (the 10 lower 16 x 16 tiles of A and of P) over the 8 waves
-    const int r0 = lane & 15, kq = lane >> 4;
-    for (int job = wave; job < 20; job += 8) {
-      const bool isP = job >= 10;
-      int idx = isP ? job - 10 : job, rt = 0;
-      while (idx > rt) { idx -= rt + 1; ++rt; }
-      const int ct = idx;  // tile (rt, ct), ct <= rt
-      const float *arow = (isP ? sQ : sK) + (16 * rt + r0) * kKRow + kq;
-      const float *brow = sG + (16 * ct + r0) * kKRow + kq;
-      f32x4_t acc = zero4();
-      for (int c4 = 0; c4 < dk; c4 += 4) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(arow[c4], brow[c4], acc, 0, 0, 0);
+  far = __syncthreads_or(far);  // (also: every fragment above has read sK, sQ and sG)
+  const int r0 = lane & 15, kq = lane >> 4;
+  for (int pass = 0; pass < 2; ++pass) {
+    const bool isP = pass == 0;
+    if (!isP) lds_barrier();  // q is dead: A takes its space
+    if (!far) {
+      // 10 lower 16 x 16 tiles over the 8 waves
+      for (int job = wave; job < 10; job += 8) {
+        int idx = job, rt = 0;
+        while (idx > rt) { idx -= rt + 1; ++rt; }
+        const int ct = idx;  // tile (rt, ct), ct <= rt
+        const T *xa = (isP ? sQ : sK) + (16 * rt + r0) * LDT + kq;
+        const float *ga = sG + (16 * rt + r0) * kKRow + kq;
+        const T *xb = sK + (16 * ct + r0) * LDT + kq;
+        const float *gb = sG + (16 * ct + r0) * kKRow + kq;
+        f32x4_t acc = zero4();
+        for (int c4 = 0; c4 < dk; c4 += 4)
+          acc = __builtin_amdgcn_mfma_f32_16x16x4f32(fast_exp2(ga[c4]) * to_f32(xa[c4]),
+                                                      fast_exp2(-gb[c4]) * to_f32(xb[c4]), acc, 0, 0, 0);
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int t = 16 * rt + 4 * kq + e, i = 16 * ct + r0;
-        if (isP) put_p(t, i, i <= t ? acc[e] : 0.0f);
-        else sA[t][i] = i < t ? sb[t] * acc[e] : 0.0f;
-      }
-    }
-    // the upper tiles of P's fragments are zero
-    for (int idx = tid; idx < 6 * 256; idx += 512) {
-      const int tile = idx >> 8, e = idx & 255;
-      const int rt = tile < 3 ? 0 : (tile < 5 ? 1 : 2), ct = tile < 3 ? tile + 1 : (tile < 5 ? tile - 1 : 3);
-      put_p(16 * rt + (e >> 4), 16 * ct + (e & 15), 0.0f);
-    }
-  } else {
-    for (int p = tid; p < 64 * 64; p += 512) {
-      const int t = p >> 6, i = p & 63;
-      float acc_a = 0.0f, acc_p = 0.0f;
-      if (i <= t) {
-        const float *gt = sG + t * kKRow, *gi = sG + i * kKRow;
-        const float *kt = sK + t * kKRow, *ki = sK + i * kKRow, *qt = sQ + t * kKRow;
-        for (int ch = 0; ch < dk; ++ch) {
-          const float e = fast_exp2(gt[ch] - gi[ch]) * ki[ch];
-          acc_a += kt[ch] * e;
-          acc_p += qt[ch] * e;
+        for (int e = 0; e < 4; ++e) {
+          const int t = 16 * rt + 4 * kq + e, i = 16 * ct + r0;
+          if (isP) put_p(t, i, i <= t ? acc[e] : 0.0f);
+          else sA[t][i] = i < t ? sb[t] * acc[e] : 0.0f;
         }
       }
-      sA[t][i] = i < t ? sb[t] * acc_a : 0.0f;
-      put_p(t, i, acc_p);
+    } else {
+      for (int p = tid; p < 64 * 64; p += 512) {
+        const int t = p >> 6, i = p & 63;
+        if ((i >> 4) > (t >> 4)) continue;  // upper tiles: zero above (P) / never read (A)
+        float acc = 0.0f;
+        if (i <= t) {
+          const float *gt = sG + t * kKRow, *gi = sG + i * kKRow;
+          for (int ch = 0; ch < dk; ++ch)
+            acc += (isP ? qval(t, ch) : kval(t, ch)) * (fast_exp2(gt[ch] - gi[ch]) * kval(i, ch));
+        }
+        if (isP) put_p(t, i, acc);
+        else sA[t][i] = i < t ? sb[t] * acc : 0.0f;
+      }
     }
   }
-  lds_barrier();  // sK and sQ are dead: the inverse's blocks reuse them
+  lds_barrier();  // k and G are dead: M and the inverse's block products take their space
 
   // ---- M = (I + A)^-1: diagonal 16 x 16 blocks by forward substitution ----
   if (wave == 0) {
