@@ -181,6 +181,7 @@ __global__ __launch_bounds__(512, (sizeof(T) == 2 ? 4 : 2)) void kda_prep_kernel
     const int ff = f & 15, rt = ff >> 2, kk = ff & 3;
     const int t = 16 * rt + (lane & 15);
     Frag<T> fr;
+#pragma unroll
     for (int j = 0; j < 8; ++j) {
       const int ch = 32 * kk + kappa(lane, j);
       float x = 0.0f;
@@ -194,6 +195,7 @@ __global__ __launch_bounds__(512, (sizeof(T) == 2 ? 4 : 2)) void kda_prep_kernel
     const int rm = f >> 1, kk = f & 1;
     const int ch = 16 * rm + (lane & 15);
     Frag<T> fr;
+#pragma unroll
     for (int j = 0; j < 8; ++j) {
       const int i = 32 * kk + kappa(lane, j);
       float x = 0.0f;
@@ -242,14 +244,31 @@ __global__ __launch_bounds__(512, (sizeof(T) == 2 ? 4 : 2)) void kda_prep_kernel
         int idx = job, rt = 0;
         while (idx > rt) { idx -= rt + 1; ++rt; }
         const int ct = idx;  // tile (rt, ct), ct <= rt
-        const T *xa = (isP ? sQ : sK) + (16 * rt + r0) * LDT + kq;
-        const float *ga = sG + (16 * rt + r0) * kKRow + kq;
-        const T *xb = sK + (16 * ct + r0) * LDT + kq;
-        const float *gb = sG + (16 * ct + r0) * kKRow + kq;
+        const T *xa = (isP ? sQ : sK) + (16 * rt + r0) * LDT;
+        const float *ga = sG + (16 * rt + r0) * kKRow;
+        const T *xb = sK + (16 * ct + r0) * LDT;
+        const float *gb = sG + (16 * ct + r0) * kKRow;
         f32x4_t acc = zero4();
-        for (int c4 = 0; c4 < dk; c4 += 4)
-          acc = __builtin_amdgcn_mfma_f32_16x16x4f32(fast_exp2(ga[c4]) * to_f32(xa[c4]),
-                                                      fast_exp2(-gb[c4]) * to_f32(xb[c4]), acc, 0, 0, 0);
+        // channels in groups of cgw = min(64, d_k): k-slot kq of a product
+        // takes channel cg + (cgw / 4) kq + u, so that the 16 rows x 4 slots
+        // of a G read fall in distinct banks (odd row stride); each step
+        // issues its four products' LDS reads together
+        const int cgw = min(64, dk), per = cgw >> 2;
+        for (int cg = 0; cg < dk; cg += cgw) {
+          const int cb = cg + per * kq;
+#pragma unroll 2
+          for (int u0 = 0; u0 < per; u0 += 4) {
+            float xs[4], ys[4];
+#pragma unroll
+            for (int v = 0; v < 4; ++v) {
+              const int ch = cb + u0 + v;
+              xs[v] = fast_exp2(ga[ch]) * to_f32(xa[ch]);
+              ys[v] = fast_exp2(-gb[ch]) * to_f32(xb[ch]);
+            }
+#pragma unroll
+            for (int v = 0; v < 4; ++v) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(xs[v], ys[v], acc, 0, 0, 0);
+          }
+        }
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int t = 16 * rt + 4 * kq + e, i = 16 * ct + r0;
