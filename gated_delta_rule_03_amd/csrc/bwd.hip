@@ -229,10 +229,25 @@ __global__ __launch_bounds__(256) void bwd_factor_kernel(BwdArgs<T> a) {
     for (int job = w; job < NL; job += 4) {
       int rt, ct;
       lower_tile(job, rt, ct);
-      const T *pa = (mat_q ? sQ : sK) + (16 * rt + r) * LDK + 4 * g;
-      const T *pb = sK + (16 * ct + r) * LDK + 4 * g;
       f32x4_t acc = zero4();
-      for (int k0 = 0; k0 < DK; k0 += 16) acc = mm16(row4(pa + k0), row4(pb + k0), acc);
+      if constexpr (sizeof(T) == 2) {
+        // bf16 inputs: their products are exact in fp32, so the bf16 MFMA
+        // (32 channels a step, lane group g taking channels 8g .. 8g + 7)
+        // gives the same sums; groups past d_k (d_k = 16) read as zero
+        const T *pa = (mat_q ? sQ : sK) + (16 * rt + r) * LDK + 8 * g;
+        const T *pb = sK + (16 * ct + r) * LDK + 8 * g;
+        for (int k0 = 0; k0 < DK; k0 += 32) {
+          const bool in = k0 + 8 * g < DK;
+          const bf16x8_t x = *reinterpret_cast<const bf16x8_t *>(pa + k0);
+          const bf16x8_t y = *reinterpret_cast<const bf16x8_t *>(pb + k0);
+          const bf16x8_t z = {};
+          acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(in ? x : z, in ? y : z, acc, 0, 0, 0);
+        }
+      } else {
+        const T *pa = (mat_q ? sQ : sK) + (16 * rt + r) * LDK + 4 * g;
+        const T *pb = sK + (16 * ct + r) * LDK + 4 * g;
+        for (int k0 = 0; k0 < DK; k0 += 16) acc = mm16(row4(pa + k0), row4(pb + k0), acc);
+      }
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         const int t = 16 * rt + 4 * g + q, i = 16 * ct + r;
