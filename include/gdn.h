@@ -119,6 +119,12 @@ size_t gdn_chunk_fwd_workspace_bytes(int32_t B, int32_t T, int32_t H_qk, int32_t
  * "Chunkwise training for DeltaNet"), with the decay gate of "Linear
  * attention", Eq. (1), carried as chunk-local cumulative log gates.
  *
+ * Precision: bf16 inputs run the chunk products on the bf16 matrix cores
+ * (operands such as the chunk's pseudo-values and the state rounded to bf16
+ * where they enter a product, fp32 sums, the state kept in fp32), except in
+ * the one-pass form with d_k < 128 or d_v = 16, which, like fp32 inputs,
+ * keeps every product in fp32.
+ *
  * Arguments as gdn_recurrent_fwd, plus:
  *   chunk       16, 32 or 64.
  *   workspace   device memory of at least gdn_chunk_fwd_workspace_bytes(...)
