@@ -45,9 +45,13 @@
 //      d_v (dO S^T, dY S^T, U dS'^T, dO U^T, dY U^T), then dq, dk, dbeta and
 //      dalpha.
 // Under grouped heads a last pass sums dq and dk over the value heads that
-// read each query/key head.  Every product runs on fp32 MFMA
-// (v_mfma_f32_16x16x4f32), and every sum has a fixed order, so results repeat
-// bit for bit from run to run.
+// read each query/key head.  The products run on fp32 MFMA
+// (v_mfma_f32_16x16x4f32), except two groups that need no fp32 operand
+// rounding beyond a split: K K^T and Q K^T of bf16 inputs (exact products)
+// on the bf16 MFMA, and for bf16 inputs the backward chain's state update
+// Q^T diag(gamma) dO - K^T diag(gamma) dX, whose fp32 factors are split as
+// x = hi + lo in bf16 (about 16 significant bits).  Every sum has a fixed
+// order, so results repeat bit for bit from run to run.
 #include "launch.hpp"
 #include "stage.hpp"
 
@@ -328,10 +332,18 @@ template <typename T, int C> struct ChainLds {
   static constexpr int kState = 32 * LDT * 4;
   static constexpr int kCol = 32 * LDC * 4;
   static constexpr int kGate = 3 * 64 * 4;
+  // bf16 inputs: the backward chain's state update runs on the bf16 MFMA
+  // with its fp32 operands diag(gamma) dO and -diag(gamma) dX split into
+  // bf16 hi + lo, stored per column as [hi x4 | lo x4] per 4 tokens
+  static constexpr bool kSplitB = sizeof(T) == 2;
+  static constexpr int LDP = 2 * C + 8;             // split rows: bf16 elements
+  static constexpr int kSplit = 32 * LDP * 2;
   // forward: K, S^T, Y^T, (diag(s) U)^T, gates; backward: K, Q, dS^T, dO^T,
-  // dU^T, (-diag(gamma) dX)^T, gates
+  // dU^T, (-diag(gamma) dX)^T (bf16: its split, and the split of
+  // diag(gamma) dO), gates
   static constexpr int kFwd = kTile + kState + 2 * kCol + kGate;
-  static constexpr int kRev = 2 * kTile + kState + 3 * kCol + kGate;
+  static constexpr int kRev = kSplitB ? 2 * kTile + kState + 2 * kCol + 2 * kSplit + kGate
+                                      : 2 * kTile + kState + 3 * kCol + kGate;
   static constexpr int kBytes = kFwd > kRev ? kFwd : kRev;
   // one block runs a chain of each direction when both fit in a CU's LDS
   static constexpr bool kPaired = kFwd + kRev <= 160 * 1024;
@@ -354,6 +366,18 @@ __device__ __forceinline__ f32x4_t tile_colfrag<bf16_t>(const bf16_t *tile, int 
 template <>
 __device__ __forceinline__ f32x4_t tile_colfrag<float>(const float *tile, int ld, int t0, int col0, int r, int g) {
   return col4(tile + (t0 + 4 * g) * ld + col0 + r, ld);
+}
+// The same four bf16 values of a bf16 tile, unconverted.
+__device__ __forceinline__ bf16x4_t tile_colfrag_raw(const bf16_t *tile, int ld, int t0, int col0, int r, int g) {
+  const bf16_t *p = tile + (t0 + 4 * g + (r >> 2)) * ld + col0 + 4 * (r & 3);
+  return lds_read_tr16(lds_ptr((void *)p));
+}
+// x = hi + lo in bf16 (hi = bf16(x), lo = bf16(x - hi): about 16 significant
+// bits), as the 8 elements [hi x4 | lo x4].
+__device__ __forceinline__ bf16x8_t split_hi_lo(f32x4_t x) {
+  const bf16x4_t hi = __builtin_convertvector(x, bf16x4_t);
+  const bf16x4_t lo = __builtin_convertvector(x - __builtin_convertvector(hi, f32x4_t), bf16x4_t);
+  return __builtin_shufflevector(hi, lo, 0, 1, 2, 3, 4, 5, 6, 7);
 }
 
 // One chunk's gamma, s and beta: thread t holds token (t mod 64)'s.
@@ -502,7 +526,7 @@ __device__ void fwd_chain(const BwdArgs<T> &a, int u, int cb, char *smem) {
         if constexpr (!OUT) {
 #pragma unroll
           for (int q = 0; q < 4; ++q)
-            ent[L.S + int64_t(16 * kt + 4 * g + q) * DV + c0 + 16 * ct + r] = accS[m][q];
+            ent[L.S + (16 * kt + 4 * g) * DV + c0 + 16 * ct + r + q * DV] = accS[m][q];
         }
       }
     }
@@ -541,7 +565,7 @@ __device__ void fwd_chain(const BwdArgs<T> &a, int u, int cb, char *smem) {
           const f32x4_t x = vcur[m] - gam * acc[m];
           if constexpr (!OUT) {
 #pragma unroll
-            for (int q = 0; q < 4; ++q) ent[L.X + int64_t(16 * rt + 4 * g + q) * DV + c0 + col] = x[q];
+            for (int q = 0; q < 4; ++q) ent[L.X + (16 * rt + 4 * g) * DV + c0 + col + q * DV] = x[q];
           } else {
             oacc[m] = gam * qacc[m];
           }
@@ -563,7 +587,7 @@ __device__ void fwd_chain(const BwdArgs<T> &a, int u, int cb, char *smem) {
           for (int kb = 0; kb < NRT; ++kb) acc = mm16(mcur[kb], row4(sYt + col * LDC + 16 * kb + 4 * g), acc);
           if constexpr (!OUT) {
 #pragma unroll
-            for (int q = 0; q < 4; ++q) ent[L.U + int64_t(16 * rt + 4 * g + q) * DV + c0 + col] = acc[q];
+            for (int q = 0; q < 4; ++q) ent[L.U + (16 * rt + 4 * g) * DV + c0 + col + q * DV] = acc[q];
             *reinterpret_cast<f32x4_t *>(sUt + col * LDC + 16 * rt + 4 * g) = sc * acc;
           } else {
             *reinterpret_cast<f32x4_t *>(sUt + col * LDC + 16 * rt + 4 * g) = acc;
@@ -633,8 +657,12 @@ __device__ void rev_chain(const BwdArgs<T> &a, int u, int cb, char *smem) {
   float *sdSt = reinterpret_cast<float *>(smem + 2 * Lds::kTile);  // dS'^T
   float *sdOt = sdSt + 32 * LDT;                                     // dO^T
   float *sdUt = sdOt + 32 * LDC;                                     // dU^T
-  float *sdXt = sdUt + 32 * LDC;                                     // (-diag(gamma) dX)^T
-  float *sgate = sdXt + 32 * LDC;
+  float *sdXt = sdUt + 32 * LDC;                                     // (-diag(gamma) dX)^T (fp32 inputs)
+  // bf16 inputs: the splits of -diag(gamma) dX and of diag(gamma) dO, per
+  // column: tokens 16 b + 4 g + j (j < 4) at 32 b + 8 g + j (hi) and + 4 (lo)
+  bf16_t *sXs = reinterpret_cast<bf16_t *>(sdXt);
+  bf16_t *sOs = sXs + 32 * Lds::LDP;
+  float *sgate = Lds::kSplitB ? reinterpret_cast<float *>(sOs + 32 * Lds::LDP) : sdXt + 32 * LDC;
   int s, h, start, end, c_first, n_chunks;
   unit_of(a.geo, a.H_v, u, s, h, start, end, c_first, n_chunks);
   const int hq = h / a.group;
@@ -722,7 +750,7 @@ __device__ void rev_chain(const BwdArgs<T> &a, int u, int cb, char *smem) {
           *reinterpret_cast<f32x4_t *>(sdSt + (16 * ct + r) * LDT + 16 * kt + 4 * g) = accS[m];
 #pragma unroll
           for (int q = 0; q < 4; ++q)
-            ent[L.dS + int64_t(16 * kt + 4 * g + q) * DV + c0 + 16 * ct + r] = accS[m][q];
+            ent[L.dS + (16 * kt + 4 * g) * DV + c0 + 16 * ct + r + q * DV] = accS[m][q];
         }
       }
       const int nx = max(cc - 1, 0);  // the next chunk back (the first one reloads itself)
@@ -754,6 +782,14 @@ __device__ void rev_chain(const BwdArgs<T> &a, int u, int cb, char *smem) {
             *reinterpret_cast<f32x4_t *>(sdUt + (16 * ((w + 4 * m) / NRT) + r) * LDC + 16 * rt + 4 * g) =
                 pdo[m] + sc * kds[m];
       }
+      if constexpr (Lds::kSplitB) {
+        // diag(gamma) dO, split, for the state update
+        for (int it = tid; it < CB * (C / 4); it += kChainThreads) {
+          const int col = it / (C / 4), tq = it - col * (C / 4);
+          const f32x4_t x = row4(sdOt + col * LDC + 4 * tq) * row4(sgate + 4 * tq);
+          *reinterpret_cast<bf16x8_t *>(sOs + col * Lds::LDP + 32 * (tq >> 2) + 8 * (tq & 3)) = split_hi_lo(x);
+        }
+      }
       load_p(nx);
       lds_sync();
       // dY = M^T dU;  dv = dX = diag(beta) dY
@@ -767,13 +803,17 @@ __device__ void rev_chain(const BwdArgs<T> &a, int u, int cb, char *smem) {
 #pragma unroll
             for (int kb = 0; kb < NRT; ++kb) acc = mm16(mcur[kb], row4(sdUt + col * LDC + 16 * kb + 4 * g), acc);
             const f32x4_t dx = be * acc;
+            // dY to the entry; dv = dX to the output (rows past the chunk's end are not stored)
+            float *dvp = a.dv + (int64_t(tok0) + 16 * rt + 4 * g) * vrow + int64_t(h) * DV + c0 + col;
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
-              const int t = 16 * rt + 4 * g + q;
-              ent[L.dY + int64_t(t) * DV + c0 + col] = acc[q];
-              if (t < n) a.dv[int64_t(tok0 + t) * vrow + int64_t(h) * DV + c0 + col] = dx[q];
+              ent[L.dY + (16 * rt + 4 * g) * DV + c0 + col + q * DV] = acc[q];
+              if (16 * rt + 4 * g + q < n) dvp[q * vrow] = dx[q];
             }
-            *reinterpret_cast<f32x4_t *>(sdXt + col * LDC + 16 * rt + 4 * g) = -(gam * dx);
+            if constexpr (Lds::kSplitB)
+              *reinterpret_cast<bf16x8_t *>(sXs + col * Lds::LDP + 32 * rt + 8 * g) = split_hi_lo(-(gam * dx));
+            else
+              *reinterpret_cast<f32x4_t *>(sdXt + col * LDC + 16 * rt + 4 * g) = -(gam * dx);
           }
         }
       }
@@ -787,12 +827,26 @@ __device__ void rev_chain(const BwdArgs<T> &a, int u, int cb, char *smem) {
         if (i < nst) {
           const int kt = i % NKT, ct = i / NKT;
           f32x4_t acc = accS[m] * gC;
+          if constexpr (Lds::kSplitB) {
+            // bf16 MFMA, 16 tokens a step: [Q^T | Q^T] against [hi ; lo]
 #pragma unroll
-          for (int kb = 0; kb < NRT; ++kb) {
-            const f32x4_t xq = tile_colfrag(sQ, LDK, 16 * kb, 16 * kt, r, g) * row4(sgate + 16 * kb + 4 * g);
-            acc = mm16(xq, row4(sdOt + (16 * ct + r) * LDC + 16 * kb + 4 * g), acc);
-            acc = mm16(tile_colfrag(sK, LDK, 16 * kb, 16 * kt, r, g),
-                       row4(sdXt + (16 * ct + r) * LDC + 16 * kb + 4 * g), acc);
+            for (int kb = 0; kb < NRT; ++kb) {
+              const bf16x4_t aq = tile_colfrag_raw(sQ, LDK, 16 * kb, 16 * kt, r, g);
+              const bf16x4_t ak = tile_colfrag_raw(sK, LDK, 16 * kb, 16 * kt, r, g);
+              const int o = (16 * ct + r) * Lds::LDP + 32 * kb + 8 * g;
+              acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_shufflevector(aq, aq, 0, 1, 2, 3, 0, 1, 2, 3),
+                                                            *reinterpret_cast<const bf16x8_t *>(sOs + o), acc, 0, 0, 0);
+              acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_shufflevector(ak, ak, 0, 1, 2, 3, 0, 1, 2, 3),
+                                                            *reinterpret_cast<const bf16x8_t *>(sXs + o), acc, 0, 0, 0);
+            }
+          } else {
+#pragma unroll
+            for (int kb = 0; kb < NRT; ++kb) {
+              const f32x4_t xq = tile_colfrag(sQ, LDK, 16 * kb, 16 * kt, r, g) * row4(sgate + 16 * kb + 4 * g);
+              acc = mm16(xq, row4(sdOt + (16 * ct + r) * LDC + 16 * kb + 4 * g), acc);
+              acc = mm16(tile_colfrag(sK, LDK, 16 * kb, 16 * kt, r, g),
+                         row4(sdXt + (16 * ct + r) * LDC + 16 * kb + 4 * g), acc);
+            }
           }
           accS[m] = acc;
         }
@@ -966,6 +1020,7 @@ __global__ __launch_bounds__(kGradThreads) void bwd_grad_kernel(BwdArgs<T> a) {
         *reinterpret_cast<f32x4_t *>(sdY + t * LDV + c) = y;
         *reinterpret_cast<f32x4_t *>(sU + t * LDV + c) = uu;
         part = y[0] * x[0] + y[1] * x[1] + y[2] * x[2] + y[3] * x[3];
+
       }
       r1acc[m] += group_sum(part, WPR);
     }
