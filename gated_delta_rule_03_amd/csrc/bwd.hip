@@ -336,7 +336,8 @@ template <typename T, int C> struct ChainLds {
   // with its fp32 operands diag(gamma) dO and -diag(gamma) dX split into
   // bf16 hi + lo, stored per column as [hi x4 | lo x4] per 4 tokens
   static constexpr bool kSplitB = sizeof(T) == 2;
-  static constexpr int LDP = 2 * C + 8;             // split rows: bf16 elements
+  static constexpr int LDP = 2 * C + 8;             // split rows over tokens: bf16 elements
+  static constexpr int LDSS = 2 * 128 + 8;          // split rows over d_k (a split state^T: kState bytes)
   static constexpr int kSplit = 32 * LDP * 2;
   // forward: K, S^T, Y^T, (diag(s) U)^T, gates; backward: K, Q, dS^T, dO^T,
   // dU^T, (-diag(gamma) dX)^T (bf16: its split, and the split of
@@ -430,6 +431,12 @@ __device__ void fwd_chain(const BwdArgs<T> &a, int u, int cb, char *smem) {
   float *sYt = sSt + 32 * LDT;                                                // (diag(beta) X)^T
   float *sUt = sYt + 32 * LDC;        // (diag(s) U)^T; U^T when OUT (scaled where it is read)
   float *sgate = sUt + 32 * LDC;      // gamma[64], s[64], beta[64]
+  // the backward's forward chain with bf16 inputs: K S and the state update
+  // on the bf16 MFMA, with S^T and (diag(s) U)^T stored split as hi + lo
+  // ([hi x4 | lo x4] per 4 rows of the contraction) in the same space
+  constexpr bool SPL = Lds::kSplitB && !OUT;
+  bf16_t *sSs = reinterpret_cast<bf16_t *>(sSt);
+  bf16_t *sUs = reinterpret_cast<bf16_t *>(sUt);
   int s, h, start, end, c_first, n_chunks;
   unit_of(a.geo, a.H_v, u, s, h, start, end, c_first, n_chunks);
   const int hq = h / a.group;
@@ -522,7 +529,10 @@ __device__ void fwd_chain(const BwdArgs<T> &a, int u, int cb, char *smem) {
       const int i = w + NW * m;
       if (i < nst) {
         const int kt = i % NKT, ct = i / NKT;
-        *reinterpret_cast<f32x4_t *>(sSt + (16 * ct + r) * LDT + 16 * kt + 4 * g) = accS[m];
+        if constexpr (SPL)
+          *reinterpret_cast<bf16x8_t *>(sSs + (16 * ct + r) * Lds::LDSS + 32 * kt + 8 * g) = split_hi_lo(accS[m]);
+        else
+          *reinterpret_cast<f32x4_t *>(sSt + (16 * ct + r) * LDT + 16 * kt + 4 * g) = accS[m];
         if constexpr (!OUT) {
 #pragma unroll
           for (int q = 0; q < 4; ++q)
@@ -544,15 +554,27 @@ __device__ void fwd_chain(const BwdArgs<T> &a, int u, int cb, char *smem) {
 #pragma unroll
       for (int kk = 0; kk < 8; ++kk) {
         if (16 * kk < DK) {
-          const f32x4_t xr = row4(sK + (16 * rt + r) * LDK + 16 * kk + 4 * g);
-          f32x4_t qr = zero4();
-          if constexpr (OUT) qr = row4(sQ + (16 * rt + r) * LDK + 16 * kk + 4 * g);
+          if constexpr (SPL) {
+            // [K | K] against [S_hi ; S_lo], 16 channels a step
+            const bf16x4_t kr = *reinterpret_cast<const bf16x4_t *>(sK + (16 * rt + r) * LDK + 16 * kk + 4 * g);
+            const bf16x8_t k8 = __builtin_shufflevector(kr, kr, 0, 1, 2, 3, 0, 1, 2, 3);
 #pragma unroll
-          for (int m = 0; m < MT; ++m) {
-            if (m < nmine) {
-              const f32x4_t st = row4(sSt + (16 * ((w + NW * m) / NRT) + r) * LDT + 16 * kk + 4 * g);
-              acc[m] = mm16(xr, st, acc[m]);
-              if constexpr (OUT) qacc[m] = mm16(qr, st, qacc[m]);
+            for (int m = 0; m < MT; ++m)
+              if (m < nmine)
+                acc[m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                    k8, *reinterpret_cast<const bf16x8_t *>(sSs + (16 * ((w + NW * m) / NRT) + r) * Lds::LDSS + 32 * kk + 8 * g),
+                    acc[m], 0, 0, 0);
+          } else {
+            const f32x4_t xr = row4(sK + (16 * rt + r) * LDK + 16 * kk + 4 * g);
+            f32x4_t qr = zero4();
+            if constexpr (OUT) qr = row4(sQ + (16 * rt + r) * LDK + 16 * kk + 4 * g);
+#pragma unroll
+            for (int m = 0; m < MT; ++m) {
+              if (m < nmine) {
+                const f32x4_t st = row4(sSt + (16 * ((w + NW * m) / NRT) + r) * LDT + 16 * kk + 4 * g);
+                acc[m] = mm16(xr, st, acc[m]);
+                if constexpr (OUT) qacc[m] = mm16(qr, st, qacc[m]);
+              }
             }
           }
         }
@@ -588,7 +610,10 @@ __device__ void fwd_chain(const BwdArgs<T> &a, int u, int cb, char *smem) {
           if constexpr (!OUT) {
 #pragma unroll
             for (int q = 0; q < 4; ++q) ent[L.U + (16 * rt + 4 * g) * DV + c0 + col + q * DV] = acc[q];
-            *reinterpret_cast<f32x4_t *>(sUt + col * LDC + 16 * rt + 4 * g) = sc * acc;
+            if constexpr (SPL)
+              *reinterpret_cast<bf16x8_t *>(sUs + col * Lds::LDP + 32 * rt + 8 * g) = split_hi_lo(sc * acc);
+            else
+              *reinterpret_cast<f32x4_t *>(sUt + col * LDC + 16 * rt + 4 * g) = sc * acc;
           } else {
             *reinterpret_cast<f32x4_t *>(sUt + col * LDC + 16 * rt + 4 * g) = acc;
           }
@@ -605,11 +630,22 @@ __device__ void fwd_chain(const BwdArgs<T> &a, int u, int cb, char *smem) {
       if (i < nst) {
         const int kt = i % NKT, ct = i / NKT;
         f32x4_t acc = accS[m] * gC;
+        if constexpr (SPL) {
+          // [K^T | K^T] against [(sU)_hi ; (sU)_lo], 16 tokens a step
 #pragma unroll
-        for (int kb = 0; kb < NRT; ++kb) {
-          f32x4_t ut = row4(sUt + (16 * ct + r) * LDC + 16 * kb + 4 * g);
-          if constexpr (OUT) ut = ut * row4(sgate + 64 + 16 * kb + 4 * g);
-          acc = mm16(tile_colfrag(sK, LDK, 16 * kb, 16 * kt, r, g), ut, acc);
+          for (int kb = 0; kb < NRT; ++kb) {
+            const bf16x4_t ak = tile_colfrag_raw(sK, LDK, 16 * kb, 16 * kt, r, g);
+            acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                __builtin_shufflevector(ak, ak, 0, 1, 2, 3, 0, 1, 2, 3),
+                *reinterpret_cast<const bf16x8_t *>(sUs + (16 * ct + r) * Lds::LDP + 32 * kb + 8 * g), acc, 0, 0, 0);
+          }
+        } else {
+#pragma unroll
+          for (int kb = 0; kb < NRT; ++kb) {
+            f32x4_t ut = row4(sUt + (16 * ct + r) * LDC + 16 * kb + 4 * g);
+            if constexpr (OUT) ut = ut * row4(sgate + 64 + 16 * kb + 4 * g);
+            acc = mm16(tile_colfrag(sK, LDK, 16 * kb, 16 * kt, r, g), ut, acc);
+          }
         }
         accS[m] = acc;
       }
@@ -662,6 +698,7 @@ __device__ void rev_chain(const BwdArgs<T> &a, int u, int cb, char *smem) {
   // column: tokens 16 b + 4 g + j (j < 4) at 32 b + 8 g + j (hi) and + 4 (lo)
   bf16_t *sXs = reinterpret_cast<bf16_t *>(sdXt);
   bf16_t *sOs = sXs + 32 * Lds::LDP;
+  bf16_t *sdSs = reinterpret_cast<bf16_t *>(sdSt);  // bf16 inputs: dS'^T split as hi + lo
   float *sgate = Lds::kSplitB ? reinterpret_cast<float *>(sOs + 32 * Lds::LDP) : sdXt + 32 * LDC;
   int s, h, start, end, c_first, n_chunks;
   unit_of(a.geo, a.H_v, u, s, h, start, end, c_first, n_chunks);
@@ -747,7 +784,10 @@ __device__ void rev_chain(const BwdArgs<T> &a, int u, int cb, char *smem) {
         const int i = w + 4 * m;
         if (i < nst) {
           const int kt = i % NKT, ct = i / NKT;
-          *reinterpret_cast<f32x4_t *>(sdSt + (16 * ct + r) * LDT + 16 * kt + 4 * g) = accS[m];
+          if constexpr (Lds::kSplitB)
+            *reinterpret_cast<bf16x8_t *>(sdSs + (16 * ct + r) * Lds::LDSS + 32 * kt + 8 * g) = split_hi_lo(accS[m]);
+          else
+            *reinterpret_cast<f32x4_t *>(sdSt + (16 * ct + r) * LDT + 16 * kt + 4 * g) = accS[m];
 #pragma unroll
           for (int q = 0; q < 4; ++q)
             ent[L.dS + (16 * kt + 4 * g) * DV + c0 + 16 * ct + r + q * DV] = accS[m][q];
@@ -762,11 +802,25 @@ __device__ void rev_chain(const BwdArgs<T> &a, int u, int cb, char *smem) {
 #pragma unroll
         for (int kk = 0; kk < 8; ++kk) {
           if (16 * kk < DK) {
-            const f32x4_t xr = row4(sK + (16 * rt + r) * LDK + 16 * kk + 4 * g);
+            if constexpr (Lds::kSplitB) {
+              // [K | K] against [dS'_hi ; dS'_lo], 16 channels a step
+              const bf16x4_t kr = *reinterpret_cast<const bf16x4_t *>(sK + (16 * rt + r) * LDK + 16 * kk + 4 * g);
+              const bf16x8_t k8 = __builtin_shufflevector(kr, kr, 0, 1, 2, 3, 0, 1, 2, 3);
 #pragma unroll
-            for (int m = 0; m < 2; ++m)
-              if (m < nmine)
-                kds[m] = mm16(xr, row4(sdSt + (16 * ((w + 4 * m) / NRT) + r) * LDT + 16 * kk + 4 * g), kds[m]);
+              for (int m = 0; m < 2; ++m)
+                if (m < nmine)
+                  kds[m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                      k8,
+                      *reinterpret_cast<const bf16x8_t *>(sdSs + (16 * ((w + 4 * m) / NRT) + r) * Lds::LDSS + 32 * kk +
+                                                          8 * g),
+                      kds[m], 0, 0, 0);
+            } else {
+              const f32x4_t xr = row4(sK + (16 * rt + r) * LDK + 16 * kk + 4 * g);
+#pragma unroll
+              for (int m = 0; m < 2; ++m)
+                if (m < nmine)
+                  kds[m] = mm16(xr, row4(sdSt + (16 * ((w + 4 * m) / NRT) + r) * LDT + 16 * kk + 4 * g), kds[m]);
+            }
           }
         }
 #pragma unroll
