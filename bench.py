@@ -44,7 +44,8 @@ flops as a fraction of the fp32 MFMA peak.
 
 ``chunk_bwd`` times the backward pass (gdn_chunk_bwd) on the prefill shape,
 with its products' flops as a fraction of the fp32 MFMA peak (the backward
-computes in fp32).
+computes in fp32; with bf16 inputs some products run on the bf16 MFMA with
+their fp32 factor split hi + lo, still counted here against the fp32 peak).
 
 ``kda_decode`` times the per-channel-gate decode step (one decay rate per key
 channel) on the decode shape, with its HBM fraction.
