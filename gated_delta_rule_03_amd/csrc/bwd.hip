@@ -380,6 +380,19 @@ __device__ __forceinline__ bf16x8_t split_hi_lo(f32x4_t x) {
   const bf16x4_t lo = __builtin_convertvector(x - __builtin_convertvector(hi, f32x4_t), bf16x4_t);
   return __builtin_shufflevector(hi, lo, 0, 1, 2, 3, 4, 5, 6, 7);
 }
+// The 16 x 16 x 16 step of mm16 (xr, yt as there) on the bf16 MFMA when one
+// factor is exact in bf16: the other split as hi + lo, [x_hi | x_lo] against
+// [y ; y] (mm16_sx: yt exact) or [x ; x] against [y_hi ; y_lo] (mm16_sy:
+// xr exact).
+__device__ __forceinline__ f32x4_t mm16_sx(f32x4_t xr, f32x4_t yt, f32x4_t acc) {
+  const bf16x4_t y = __builtin_convertvector(yt, bf16x4_t);
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(split_hi_lo(xr), __builtin_shufflevector(y, y, 0, 1, 2, 3, 0, 1, 2, 3),
+                                                 acc, 0, 0, 0);
+}
+__device__ __forceinline__ f32x4_t mm16_sy(f32x4_t xr, bf16x8_t ys, f32x4_t acc) {
+  const bf16x4_t x = __builtin_convertvector(xr, bf16x4_t);
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_shufflevector(x, x, 0, 1, 2, 3, 0, 1, 2, 3), ys, acc, 0, 0, 0);
+}
 
 // One chunk's gamma, s and beta: thread t holds token (t mod 64)'s.
 struct GateLoader {
@@ -1006,6 +1019,7 @@ __global__ __launch_bounds__(kGradThreads) void bwd_grad_kernel(BwdArgs<T> a) {
   constexpr int NK = DVS / 16;                                        // 16-deep steps per slab
   constexpr int WPR = DVS / 4;                                        // float4 pieces per slab row
   constexpr int NPC = (C * WPR + kGradThreads - 1) / kGradThreads;    // pieces per thread
+  constexpr bool SPLG = sizeof(T) == 2;  // bf16 inputs: products with dO, k or q on the bf16 MFMA
   __shared__ __attribute__((aligned(16))) float big[kBig];
   __shared__ float sPartG[64 * 8], sPartS[64 * 8];
   __shared__ float sR1[64], sRowE[64], sRowF[64], sColE[64], sSd[kGradWaves];
@@ -1083,12 +1097,19 @@ __global__ __launch_bounds__(kGradThreads) void bwd_grad_kernel(BwdArgs<T> a) {
     for (int kk = 0; kk < NK; ++kk) {
       const int k0 = 16 * kk + 4 * g;
       if (has_rows) {
+        // bf16 inputs: dO is exact in bf16, so dO S^T runs on the bf16 MFMA
+        // with S split hi + lo
+        bf16x8_t ySs{};
+        if constexpr (SPLG) ySs = split_hi_lo(yS[kk]);
 #pragma unroll
         for (int m = 0; m < RPW; ++m) {
           const int i = rsel + m * wpc;
           if (i >= NRT) continue;
           const int row = (16 * i + r) * LDV + k0;
-          W1[m] = mm16(row4(sdO + row), yS[kk], W1[m]);
+          if constexpr (SPLG)
+            W1[m] = mm16_sy(row4(sdO + row), ySs, W1[m]);
+          else
+            W1[m] = mm16(row4(sdO + row), yS[kk], W1[m]);
           W2[m] = mm16(row4(sdY + row), yS[kk], W2[m]);
           W3[m] = mm16(row4(sU + row), ydS[kk], W3[m]);
         }
@@ -1101,7 +1122,10 @@ __global__ __launch_bounds__(kGradThreads) void bwd_grad_kernel(BwdArgs<T> a) {
       for (int j = 0; j < 1; ++j) {
         if (j < np) {
           const f32x4_t yu = row4(sU + (16 * pct[j] + r) * LDV + k0);
-          aP[j] = mm16(row4(sdO + (16 * prt[j] + r) * LDV + k0), yu, aP[j]);
+          if constexpr (SPLG)
+            aP[j] = mm16_sy(row4(sdO + (16 * prt[j] + r) * LDV + k0), split_hi_lo(yu), aP[j]);
+          else
+            aP[j] = mm16(row4(sdO + (16 * prt[j] + r) * LDV + k0), yu, aP[j]);
           aA[j] = mm16(row4(sdY + (16 * prt[j] + r) * LDV + k0), yu, aA[j]);
         }
       }
@@ -1210,9 +1234,15 @@ __global__ __launch_bounds__(kGradThreads) void bwd_grad_kernel(BwdArgs<T> a) {
       f32x4_t aq = zero4(), ak = zero4();
 #pragma unroll
       for (int kb = 0; kb < NRT; ++kb) {
-        aq = mm16(row4(sdP + (16 * i + r) * LD + 16 * kb + 4 * g), kf[kb], aq);
-        ak = mm16(col4(sdP + (16 * kb + 4 * g) * LD + 16 * i + r, LD), qf[kb], ak);
-        ak = mm16(row4(sE + (16 * i + r) * LD + 16 * kb + 4 * g), kf[kb], ak);
+        if constexpr (SPLG) {  // k and q exact in bf16: the C x C factors split
+          aq = mm16_sx(row4(sdP + (16 * i + r) * LD + 16 * kb + 4 * g), kf[kb], aq);
+          ak = mm16_sx(col4(sdP + (16 * kb + 4 * g) * LD + 16 * i + r, LD), qf[kb], ak);
+          ak = mm16_sx(row4(sE + (16 * i + r) * LD + 16 * kb + 4 * g), kf[kb], ak);
+        } else {
+          aq = mm16(row4(sdP + (16 * i + r) * LD + 16 * kb + 4 * g), kf[kb], aq);
+          ak = mm16(col4(sdP + (16 * kb + 4 * g) * LD + 16 * i + r, LD), qf[kb], ak);
+          ak = mm16(row4(sE + (16 * i + r) * LD + 16 * kb + 4 * g), kf[kb], ak);
+        }
       }
 #pragma unroll
       for (int q = 0; q < 4; ++q) {

@@ -212,9 +212,9 @@ int32_t gdn_chunk_fwd_noalloc(int32_t B, int32_t T, int32_t H_qk, int32_t H_v, i
  * evaluated in the chunk form, in fp32: the chunk-start states and the
  * gradients reaching each chunk's end are carried chunk to chunk, and every
  * chunk's gradients then follow independently.  With bf16 inputs the
- * products that carry the states from chunk to chunk take their fp32
- * factor split as hi + lo in bf16 (about 16 significant bits) on the bf16
- * matrix cores; every other product is fp32.  Deterministic (no atomics):
+ * products whose other factor is an input (k, q or d_o, exact in bf16) take
+ * their fp32 factor split as hi + lo in bf16 (about 16 significant bits) on
+ * the bf16 matrix cores; every other product is fp32.  Deterministic (no atomics):
  * two calls on the same inputs give bitwise equal results.
  *
  * Inputs as gdn_chunk_fwd (q, k, v, alpha, beta, cu_seqlens, n_seqs, h0,
