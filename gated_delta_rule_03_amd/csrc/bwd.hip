@@ -1024,6 +1024,11 @@ __global__ __launch_bounds__(kGradThreads) void bwd_grad_kernel(BwdArgs<T> a) {
   __shared__ float sPartG[64 * 8], sPartS[64 * 8];
   __shared__ float sR1[64], sRowE[64], sRowF[64], sColE[64], sSd[kGradWaves];
   __shared__ float sGam[64], sSc[64], sG2[64], sBe[64];
+  // the chunk's K and Q rows (operands of the products over the chunk in
+  // phase 2), staged once at the start
+  constexpr int LDKG = 128 + 16 / sizeof(T);
+  __shared__ __attribute__((aligned(16))) T sKg[C * LDKG];
+  __shared__ __attribute__((aligned(16))) T sQg[C * LDKG];
 
   const int e = blockIdx.x;
   const int slot = e / a.H_v, h = e - slot * a.H_v;
@@ -1034,6 +1039,13 @@ __global__ __launch_bounds__(kGradThreads) void bwd_grad_kernel(BwdArgs<T> a) {
   const BwdEntry L(C, DK, DV);
   const float *ent = a.ent + int64_t(e) * a.ent_floats;
   const int64_t krow = int64_t(a.H_qk) * DK, vrow = int64_t(a.H_v) * DV;
+  {
+    TileLoader<T, C, kGradThreads> kl, ql;
+    kl.load(a.k + int64_t(tok0) * krow + int64_t(hq) * DK, krow, n, DK);
+    ql.load(a.q + int64_t(tok0) * krow + int64_t(hq) * DK, krow, n, DK);
+    kl.store(sKg, LDKG, DK);
+    ql.store(sQg, LDKG, DK);
+  }
 
   if (tid < C) {
     sGam[tid] = ent[L.gate + kGateGamma + tid];
@@ -1164,20 +1176,10 @@ __global__ __launch_bounds__(kGradThreads) void bwd_grad_kernel(BwdArgs<T> a) {
       }
     }
   }
-  // K and Q values of this wave's d_k column tile: kf[i][j] = K[16 i + 4g + j][16 ct + r]
-  // (B fragments of the products over the chunk, and the factors of the d_k row sums)
-  f32x4_t kf[NRT], qf[NRT];
-#pragma unroll
-  for (int i = 0; i < NRT; ++i) {
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int t = 16 * i + 4 * g + j;
-      const int64_t o = int64_t(tok0 + min(t, n - 1)) * krow + int64_t(hq) * DK + 16 * ct + r;
-      const float kv = to_f32(a.k[o]), qv = to_f32(a.q[o]);
-      kf[i][j] = t < n ? kv : 0.0f;
-      qf[i][j] = t < n ? qv : 0.0f;
-    }
-  }
+  // K and Q values of this wave's d_k column tile, from LDS:
+  // kf(i)[j] = K[16 i + 4g + j][16 ct + r] (rows past the chunk's end are zero)
+  auto kf = [&](int i) { return tile_colfrag(sKg, LDKG, 16 * i, 16 * ct, r, g); };
+  auto qf = [&](int i) { return tile_colfrag(sQg, LDKG, 16 * i, 16 * ct, r, g); };
   __syncthreads();
   // elementwise, 8 threads per row: dP . Gamma, dG = dA . diag(beta) Gamma,
   // E = Gamma . dGamma = diag(beta) dA . (Gamma . KK^T) + dP . P
@@ -1223,25 +1225,19 @@ __global__ __launch_bounds__(kGradThreads) void bwd_grad_kernel(BwdArgs<T> a) {
     for (int m = 0; m < RPW; ++m) {
       const int i = rsel + m * wpc;
       if (i >= NRT) continue;
-      // K and Q values of row tile i (a runtime index: picked, not indexed)
-      f32x4_t kfi = kf[0], qfi = qf[0];
-#pragma unroll
-      for (int kb = 1; kb < NRT; ++kb)
-        if (kb == i) {
-          kfi = kf[kb];
-          qfi = qf[kb];
-        }
+      const f32x4_t kfi = kf(i), qfi = qf(i);  // K and Q values of row tile i
       f32x4_t aq = zero4(), ak = zero4();
 #pragma unroll
       for (int kb = 0; kb < NRT; ++kb) {
+        const f32x4_t kk = kf(kb), qq = qf(kb);
         if constexpr (SPLG) {  // k and q exact in bf16: the C x C factors split
-          aq = mm16_sx(row4(sdP + (16 * i + r) * LD + 16 * kb + 4 * g), kf[kb], aq);
-          ak = mm16_sx(col4(sdP + (16 * kb + 4 * g) * LD + 16 * i + r, LD), qf[kb], ak);
-          ak = mm16_sx(row4(sE + (16 * i + r) * LD + 16 * kb + 4 * g), kf[kb], ak);
+          aq = mm16_sx(row4(sdP + (16 * i + r) * LD + 16 * kb + 4 * g), kk, aq);
+          ak = mm16_sx(col4(sdP + (16 * kb + 4 * g) * LD + 16 * i + r, LD), qq, ak);
+          ak = mm16_sx(row4(sE + (16 * i + r) * LD + 16 * kb + 4 * g), kk, ak);
         } else {
-          aq = mm16(row4(sdP + (16 * i + r) * LD + 16 * kb + 4 * g), kf[kb], aq);
-          ak = mm16(col4(sdP + (16 * kb + 4 * g) * LD + 16 * i + r, LD), qf[kb], ak);
-          ak = mm16(row4(sE + (16 * i + r) * LD + 16 * kb + 4 * g), kf[kb], ak);
+          aq = mm16(row4(sdP + (16 * i + r) * LD + 16 * kb + 4 * g), kk, aq);
+          ak = mm16(col4(sdP + (16 * kb + 4 * g) * LD + 16 * i + r, LD), qq, ak);
+          ak = mm16(row4(sE + (16 * i + r) * LD + 16 * kb + 4 * g), kk, ak);
         }
       }
 #pragma unroll
