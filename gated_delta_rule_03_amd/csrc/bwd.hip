@@ -1100,7 +1100,6 @@ __global__ __launch_bounds__(kGradThreads) void bwd_grad_kernel(BwdArgs<T> a) {
         *reinterpret_cast<f32x4_t *>(sdY + t * LDV + c) = y;
         *reinterpret_cast<f32x4_t *>(sU + t * LDV + c) = uu;
         part = y[0] * x[0] + y[1] * x[1] + y[2] * x[2] + y[3] * x[3];
-
       }
       r1acc[m] += group_sum(part, WPR);
     }
