@@ -50,6 +50,10 @@ CASES = [
     ("f32", 2, 100, 2, 4, 128, 128, 64, None, True, False),
     ("bf16", 2, 70, 2, 2, 128, 64, 64, None, False, True),
     ("bf16", 1, 0, 2, 4, 64, 128, 16, (33, 3, 0, 80), True, True),
+    # bf16 in chunks of 32, a 16-column value block and d_k = 16: the split
+    # (hi + lo) operand layouts at their other sizes
+    ("bf16", 2, 90, 1, 2, 16, 16, 32, None, True, True),
+    ("bf16", 1, 75, 2, 2, 32, 64, 32, None, False, True),
 ]
 
 
