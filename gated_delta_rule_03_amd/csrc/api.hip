@@ -119,10 +119,18 @@ static int32_t status_of(hipError_t e) { return e == hipSuccess ? GDN_SUCCESS : 
 // Measured on MI355X, long context T = 65536, d = 128, one pass vs segments
 // of 16 / 32 / 64 / 128 / 256 chunks: 16 heads 1,123 vs
 // 1,150 / 957 / 886 / 844 / 921 us; 2 heads 863 vs 319 / 221 / 200 / 271 / 459 us.
+//
+// Shapes off the staged path run their segment batches on the general
+// fragment-entry kernels, much slower per chunk than their one-pass chained
+// form, so they take segments only for 4 units or fewer.  Measured, T = 65536,
+// chunk 64, one pass vs the planned segments: fp32 d = 128, 2 / 4 / 8 / 16
+// heads 4.2 / 4.5 / 4.7 / 4.9 ms vs 3.7 / 4.7 / 9.2 / 11.1 ms; bf16 d = 64,
+// 2 / 4 / 16 heads 3.2 / 3.2 / 3.5 ms vs 2.1 / 2.4 / 8.0 ms.
 int32_t plan_segment_chunks(const Problem &p) {
   const int64_t units = int64_t(p.n_seqs) * p.H_v;
   const int64_t max_chunks = ceil_div(p.T, p.chunk);  // the longest sequence's chunks, at most
   if (units == 0 || units * std::max(1, p.d_v / 32) >= 128) return 0;
+  if (!staged_path(p) && units > 4) return 0;
   const int64_t blocks1 = units * std::max(1, (p.d_v + p.d_k) / 32);
   const int64_t segs = ceil_div(512, blocks1);
   const int64_t seg = std::min<int64_t>(128, std::max<int64_t>(64, ceil_div(max_chunks, segs)));
