@@ -120,20 +120,22 @@ static int32_t status_of(hipError_t e) { return e == hipSuccess ? GDN_SUCCESS : 
 // of 16 / 32 / 64 / 128 / 256 chunks: 16 heads 1,123 vs
 // 1,150 / 957 / 886 / 844 / 921 us; 2 heads 863 vs 319 / 221 / 200 / 271 / 459 us.
 //
-// Shapes off the staged path run their segment batches on the general
-// fragment-entry kernels, much slower per chunk than their one-pass chained
-// form, so they take segments only for 4 units or fewer.  Measured, T = 65536,
-// chunk 64, one pass vs the planned segments: fp32 d = 128, 2 / 4 / 8 / 16
-// heads 4.2 / 4.5 / 4.7 / 4.9 ms vs 3.7 / 4.7 / 9.2 / 11.1 ms; bf16 d = 64,
-// 2 / 4 / 16 heads 3.2 / 3.2 / 3.5 ms vs 2.1 / 2.4 / 8.0 ms.
+// Shapes off the staged path run both passes on the chained kernels, whose
+// chunk step is longer; there the aim is about four rounds (1,024 blocks)
+// and segments of 32 to 128 chunks.  Measured, T = 65536, chunk 64, one pass
+// vs segments of 32 / 64 / 128 chunks: fp32 d = 128, 2 heads 4,219 vs
+// 715 / 711 / 1,010 us, 4 heads 4,475 vs 1,254 / 1,183 / 1,260, 8 heads
+// 4,669 vs 2,339 / 2,176 / 2,119, 16 heads 4,839 vs 4,317 / 4,172 / 4,114;
+// bf16 d = 64, 2 heads 3,225 vs 291 / 400 / 689, 4 heads 3,238 vs
+// 401 / 482 / 730, 16 heads 3,479 vs 1,208 / 1,185 / 1,294.
 int32_t plan_segment_chunks(const Problem &p) {
   const int64_t units = int64_t(p.n_seqs) * p.H_v;
   const int64_t max_chunks = ceil_div(p.T, p.chunk);  // the longest sequence's chunks, at most
   if (units == 0 || units * std::max(1, p.d_v / 32) >= 128) return 0;
-  if (!staged_path(p) && units > 4) return 0;
+  const bool staged = staged_path(p);
   const int64_t blocks1 = units * std::max(1, (p.d_v + p.d_k) / 32);
-  const int64_t segs = ceil_div(512, blocks1);
-  const int64_t seg = std::min<int64_t>(128, std::max<int64_t>(64, ceil_div(max_chunks, segs)));
+  const int64_t segs = ceil_div(staged ? 512 : 1024, blocks1);
+  const int64_t seg = std::min<int64_t>(128, std::max<int64_t>(staged ? 64 : 32, ceil_div(max_chunks, segs)));
   return seg >= max_chunks ? 0 : int32_t(seg);
 }
 
@@ -159,7 +161,6 @@ static Problem segment_problem(const Problem &p, int32_t seg_chunks, const SegWo
   ps.cu_seqlens = sw ? sw->seg_cu : &kLayoutOnly;  // selects the packed layout
   ps.h0 = sw ? sw->s_in : nullptr;
   ps.hT = nullptr;  // the fold writes the final states
-  ps.seg_pass = 1;
   return ps;
 }
 static size_t seg_workspace_layout(const Problem &p, int32_t seg_chunks, void *base, SegWorkspace *sw) {
@@ -249,11 +250,20 @@ int32_t run_chunk_fwd(Problem p, int32_t seg_chunks, void *workspace, size_t wor
   workspace_layout(ps, sw.base, &ws);
   hipError_t e = launch_segment_map(p, seg_chunks * p.chunk, ps.n_seqs, sw.seg_cu, sw.seg_first, s);
   if (e == hipSuccess) e = launch_chunk_offsets(ps, ws, s);
-  if (e == hipSuccess) e = launch_prep(ps, ws, s);
-  if (e == hipSuccess) e = launch_scan(ps, ws, s, sw.mb);
+  const bool chained = chain_path(ps);
+  if (chained) {  // factors once; the transition pass reads them, and so does the output pass
+    if (e == hipSuccess) e = launch_chain_fwd(ps, ws, s, sw.mb, true);
+  } else {
+    if (e == hipSuccess) e = launch_prep(ps, ws, s);
+    if (e == hipSuccess) e = launch_scan(ps, ws, s, sw.mb);
+  }
   if (e == hipSuccess) e = launch_fold(sw.mb, p.h0, sw.s_in, p.hT, sw.seg_first, p.n_seqs, ps.n_seqs, p.H_v, p.d_k,
                                        p.d_v, s);
-  if (e == hipSuccess) e = launch_scan(ps, ws, s);
+  if (chained) {
+    if (e == hipSuccess) e = launch_chain_fwd(ps, ws, s, nullptr, false);
+  } else {
+    if (e == hipSuccess) e = launch_scan(ps, ws, s);
+  }
   return status_of(e);
 }
 

@@ -89,6 +89,7 @@ struct BwdArgs {
   float *dv, *dalpha, *dbeta, *dh0;
   T *o;                   // the forward: outputs [tokens, H_v, d_v] and final states (or null)
   float *hT;
+  float *mb;              // the transition pass: [units, d_k, d_v + d_k] segment maps (B, then M)
   bool want_g;            // the backward: the factor kernel also writes Gamma . K K^T
   int cols;               // columns of d_v per forward-chain block: 16 or 32 (d_v >= 32), else d_v
   int H_qk, H_v, d_k, d_v, group, n_units;
@@ -427,7 +428,7 @@ __device__ __forceinline__ void unit_of(const SeqGeom &geo, int H_v, int u, int 
 // entry.  For the forward pass itself (OUT = true) it stores nothing in the
 // entries: it also stages the chunk's Q rows, forms
 // O = diag(gamma) Q S + P U, and writes O and the last state.
-template <typename T, int C, bool OUT, int NW = 4>
+template <typename T, int C, bool OUT, int NW = 4, bool TRANS = false>
 __device__ void fwd_chain(const BwdArgs<T> &a, int u, int cb, char *smem) {
   using Lds = ChainLds<T, C>;
   constexpr int NRT = C / 16, LDK = Lds::LDK, LDT = Lds::LDT, LDC = Lds::LDC;
@@ -465,15 +466,36 @@ __device__ void fwd_chain(const BwdArgs<T> &a, int u, int cb, char *smem) {
   for (int m = 0; m < MS; ++m) {
     accS[m] = zero4();
     const int i = w + NW * m;
-    if (i < nst && a.h0) {
+    if constexpr (TRANS) {
+      // the transition pass: B's columns start from zero, M's from the identity
+      const int kt = i % NKT, ct = i / NKT;
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        accS[m][q] = (i < nst && c0 >= DV && 16 * kt + 4 * g + q == c0 - DV + 16 * ct + r) ? 1.0f : 0.0f;
+    } else if (i < nst && a.h0) {
       const int kt = i % NKT, ct = i / NKT;
       const float *h0 = a.h0 + (int64_t(s) * a.H_v + h) * DK * DV;
 #pragma unroll
       for (int q = 0; q < 4; ++q) accS[m][q] = h0[int64_t(16 * kt + 4 * g + q) * DV + c0 + 16 * ct + r];
     }
   }
-  // the state after the last chunk (the entry state for an empty sequence)
+  // the state after the last chunk (the entry state for an empty sequence);
+  // the transition pass writes it as the segment's map
   auto store_final = [&]() {
+    if constexpr (TRANS) {
+      const int ldm = DV + DK;
+      float *mb = a.mb + (int64_t(s) * a.H_v + h) * DK * ldm;
+#pragma unroll
+      for (int m = 0; m < MS; ++m) {
+        const int i = w + NW * m;
+        if (i < nst) {
+          const int kt = i % NKT, ct = i / NKT;
+#pragma unroll
+          for (int q = 0; q < 4; ++q) mb[int64_t(16 * kt + 4 * g + q) * ldm + c0 + 16 * ct + r] = accS[m][q];
+        }
+      }
+      return;
+    }
     if (!OUT || !a.hT) return;
     float *hT = a.hT + (int64_t(s) * a.H_v + h) * DK * DV;
 #pragma unroll
@@ -505,8 +527,10 @@ __device__ void fwd_chain(const BwdArgs<T> &a, int u, int cb, char *smem) {
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         const int t = 16 * rt + 4 * g + q;
-        const float x = to_f32(a.v[int64_t(tok0 + min(t, n - 1)) * vrow + int64_t(h) * DV + c0 + 16 * ct + r]);
-        vcur[m][q] = t < n ? x : 0.0f;
+        // (the transition pass's M columns have no values: read a valid column, use zero)
+        const int col = TRANS ? min(c0 + 16 * ct + r, DV - 1) : c0 + 16 * ct + r;
+        const float x = to_f32(a.v[int64_t(tok0 + min(t, n - 1)) * vrow + int64_t(h) * DV + col]);
+        vcur[m][q] = (t < n && (!TRANS || c0 < DV)) ? x : 0.0f;
       }
     }
   };
@@ -546,7 +570,7 @@ __device__ void fwd_chain(const BwdArgs<T> &a, int u, int cb, char *smem) {
           *reinterpret_cast<bf16x8_t *>(sSs + (16 * ct + r) * Lds::LDSS + 32 * kt + 8 * g) = split_hi_lo(accS[m]);
         else
           *reinterpret_cast<f32x4_t *>(sSt + (16 * ct + r) * LDT + 16 * kt + 4 * g) = accS[m];
-        if constexpr (!OUT) {
+        if constexpr (!OUT && !TRANS) {
 #pragma unroll
           for (int q = 0; q < 4; ++q)
             ent[L.S + (16 * kt + 4 * g) * DV + c0 + 16 * ct + r + q * DV] = accS[m][q];
@@ -598,11 +622,11 @@ __device__ void fwd_chain(const BwdArgs<T> &a, int u, int cb, char *smem) {
         if (m < nmine) {
           const int col = 16 * ((w + NW * m) / NRT) + r;
           const f32x4_t x = vcur[m] - gam * acc[m];
-          if constexpr (!OUT) {
+          if constexpr (OUT) {
+            oacc[m] = gam * qacc[m];
+          } else if constexpr (!TRANS) {
 #pragma unroll
             for (int q = 0; q < 4; ++q) ent[L.X + (16 * rt + 4 * g) * DV + c0 + col + q * DV] = x[q];
-          } else {
-            oacc[m] = gam * qacc[m];
           }
           *reinterpret_cast<f32x4_t *>(sYt + col * LDC + 16 * rt + 4 * g) = be * x;
         }
@@ -621,8 +645,10 @@ __device__ void fwd_chain(const BwdArgs<T> &a, int u, int cb, char *smem) {
 #pragma unroll
           for (int kb = 0; kb < NRT; ++kb) acc = mm16(mcur[kb], row4(sYt + col * LDC + 16 * kb + 4 * g), acc);
           if constexpr (!OUT) {
+            if constexpr (!TRANS) {
 #pragma unroll
-            for (int q = 0; q < 4; ++q) ent[L.U + (16 * rt + 4 * g) * DV + c0 + col + q * DV] = acc[q];
+              for (int q = 0; q < 4; ++q) ent[L.U + (16 * rt + 4 * g) * DV + c0 + col + q * DV] = acc[q];
+            }
             if constexpr (SPL)
               *reinterpret_cast<bf16x8_t *>(sUs + col * Lds::LDP + 32 * rt + 8 * g) = split_hi_lo(sc * acc);
             else
@@ -988,6 +1014,19 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void chain_fwd_kernel(BwdArgs<T> a
   decode_block(blockIdx.x, n_cb, u, x);
   if (u >= a.n_units) return;
   fwd_chain<T, C, true, NW>(a, u, x, smem);
+}
+// The transition pass of the segment-parallel form on the chained form: one
+// block per (segment unit, column block of the d_v + d_k state columns of
+// [B | M]), no outputs; each segment's final [B | M] goes to the map buffer.
+template <typename T, int C, int NW>
+__global__ __launch_bounds__(64 * NW, 8 / NW) void chain_trans_kernel(BwdArgs<T> a) {
+  using Lds = ChainLds<T, C>;
+  __shared__ __attribute__((aligned(16))) char smem[Lds::kFwd];
+  const int n_cb = (a.d_v + a.d_k) / a.cols;
+  int u, x;
+  decode_block(blockIdx.x, n_cb, u, x);
+  if (u >= a.n_units) return;
+  fwd_chain<T, C, false, NW, true>(a, u, x, smem);
 }
 // Waves per forward-pass chain block: fp32 operands fill enough LDS that a CU
 // holds one block, so it gets eight waves (two per SIMD) to hide LDS and
@@ -1382,26 +1421,13 @@ hipError_t launch_chunk_bwd(const BwdProblem &b, hipStream_t st) {
 
 // ---------------------------------------------------------------------------
 // The chained forward: the factor kernel (M, P and the gates only), then the
-// forward chain with outputs.  Its entries are the first BwdEntry::G floats
-// of a backward entry.
+// forward chain with outputs; in the segment-parallel form the factor kernel,
+// the transition pass (each segment's map), the fold, and the forward chain
+// from the folded states.  Its entries are the first BwdEntry::G floats of a
+// backward entry.
 // ---------------------------------------------------------------------------
-template <typename T, int C>
-static hipError_t launch_chain_fwd_c(const BwdArgs<T> &a, hipStream_t st) {
-  const unsigned n_ent = unsigned(int64_t(a.geo.n_slots) * a.H_v);
-  if (n_ent > 0) {
-    hipLaunchKernelGGL((bwd_factor_kernel<T, C>), dim3(n_ent), dim3(256), 0, st, a);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-  }
-  const int n_cb = a.d_v / a.cols;
-  const int64_t groups = (int64_t(a.n_units) + 7) / 8;
-  constexpr int NW = chain_fwd_waves<T>();
-  hipLaunchKernelGGL((chain_fwd_kernel<T, C, NW>), dim3(unsigned(groups * 8 * n_cb)), dim3(64 * NW), 0, st, a);
-  return hipGetLastError();
-}
-
 template <typename T>
-static hipError_t launch_chain_fwd_t(const Problem &p, const Workspace &ws, hipStream_t st) {
+static BwdArgs<T> chain_args(const Problem &p, const Workspace &ws, float *mb) {
   BwdArgs<T> a{};
   a.q = static_cast<const T *>(p.q);
   a.k = static_cast<const T *>(p.k);
@@ -1413,6 +1439,7 @@ static hipError_t launch_chain_fwd_t(const Problem &p, const Workspace &ws, hipS
   a.ent_floats = BwdEntry(p.chunk, 0, 0).G;
   a.o = static_cast<T *>(p.o);
   a.hT = p.hT;
+  a.mb = mb;
   a.want_g = false;
   a.H_qk = p.H_qk;
   a.H_v = p.H_v;
@@ -1420,19 +1447,47 @@ static hipError_t launch_chain_fwd_t(const Problem &p, const Workspace &ws, hipS
   a.d_v = p.d_v;
   a.group = p.H_v / p.H_qk;
   a.n_units = p.n_seqs * p.H_v;
-  // 16-column blocks where 32-column ones would leave CUs without a chain
+  // 16-column blocks where 32-column ones would leave CUs without a chain (or,
+  // in the transition pass, where a 32-column block would straddle B and M)
+  const int cols = p.d_v + (mb ? p.d_k : 0);
   a.cols = std::min(32, p.d_v);
-  if (a.cols == 32 && int64_t(a.n_units) * (p.d_v / 32) < 256) a.cols = 16;
+  if (a.cols == 32 && (int64_t(a.n_units) * (cols / 32) < 256 || (mb && p.d_k % 32 != 0))) a.cols = 16;
   a.geo = make_geom(p, &ws);
-  if (a.n_units == 0) return hipSuccess;
-  return p.chunk == 16   ? launch_chain_fwd_c<T, 16>(a, st)
-         : p.chunk == 32 ? launch_chain_fwd_c<T, 32>(a, st)
-                         : launch_chain_fwd_c<T, 64>(a, st);
+  return a;
 }
 
-hipError_t launch_chain_fwd(const Problem &p, const Workspace &ws, hipStream_t st) {
+template <typename T, int C>
+static hipError_t launch_chain_c(const BwdArgs<T> &a, bool factors, hipStream_t st) {
+  const unsigned n_ent = unsigned(int64_t(a.geo.n_slots) * a.H_v);
+  if (factors && n_ent > 0) {
+    hipLaunchKernelGGL((bwd_factor_kernel<T, C>), dim3(n_ent), dim3(256), 0, st, a);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  if (a.n_units == 0) return hipSuccess;
+  const int64_t groups = (int64_t(a.n_units) + 7) / 8;
+  constexpr int NW = chain_fwd_waves<T>();
+  if (a.mb) {
+    const int n_cb = (a.d_v + a.d_k) / a.cols;
+    hipLaunchKernelGGL((chain_trans_kernel<T, C, NW>), dim3(unsigned(groups * 8 * n_cb)), dim3(64 * NW), 0, st, a);
+  } else {
+    const int n_cb = a.d_v / a.cols;
+    hipLaunchKernelGGL((chain_fwd_kernel<T, C, NW>), dim3(unsigned(groups * 8 * n_cb)), dim3(64 * NW), 0, st, a);
+  }
+  return hipGetLastError();
+}
+
+template <typename T>
+static hipError_t launch_chain_t(const Problem &p, const Workspace &ws, float *mb, bool factors, hipStream_t st) {
+  const BwdArgs<T> a = chain_args<T>(p, ws, mb);
+  return p.chunk == 16   ? launch_chain_c<T, 16>(a, factors, st)
+         : p.chunk == 32 ? launch_chain_c<T, 32>(a, factors, st)
+                         : launch_chain_c<T, 64>(a, factors, st);
+}
+
+hipError_t launch_chain_fwd(const Problem &p, const Workspace &ws, hipStream_t st, float *mb, bool factors) {
   if (int64_t(entry_stride(p)) != BwdEntry(p.chunk, 0, 0).G * int64_t(sizeof(float))) return hipErrorInvalidValue;
-  return p.dtype == 1 ? launch_chain_fwd_t<bf16_t>(p, ws, st) : launch_chain_fwd_t<float>(p, ws, st);
+  return p.dtype == 1 ? launch_chain_t<bf16_t>(p, ws, mb, factors, st) : launch_chain_t<float>(p, ws, mb, factors, st);
 }
 
 }  // namespace gdn

@@ -19,7 +19,6 @@ struct Problem {
   float *hT;
   int32_t chunk;
   int32_t per_channel = 0;  // alpha holds one rate per key channel: [.., H_v, d_k]
-  int32_t seg_pass = 0;     // a segment batch of the segment-parallel form (fragment entries)
   int64_t n_tokens() const { return int64_t(B) * T; }
 };
 
@@ -27,17 +26,14 @@ struct Problem {
 // for any packed layout with the same totals.
 int64_t chunk_slots(const Problem &p);
 
-// One workspace entry per (chunk slot, value head): the intra-chunk factors
-// in MFMA fragment order -- T (8 fragments), P (8 fragments) of 64 lanes x 8
-// elements of the operand type -- followed by a 1 KiB gate block of fp32:
-// gamma_t = 2^g_t for the 64 slots, then s_t = 2^(g_C - g_t), then g_t.
-// (g_t is the chunk-local cumulative log2 gate; padded slots repeat the last
-// token's gate, so gamma_63 = gamma_C and s = 1 there.)
+// One workspace entry per (chunk slot, value head) holds the intra-chunk
+// factors of that chunk; its layout depends on the path (below).  Factors in
+// MFMA fragment order are fragments of 64 lanes x 8 elements of the operand
+// type.  A gate block holds fp32 gamma_t = 2^g_t for the 64 slots, then
+// s_t = 2^(g_C - g_t), then g_t.  (g_t is the chunk-local cumulative log2
+// gate; padded slots repeat the last token's gate, so gamma_63 = gamma_C and
+// s = 1 there.)
 constexpr int kFragElems = 64 * 8;
-constexpr int kGateBlockBytes = 1024;
-template <typename T> constexpr int64_t entry_bytes() {
-  return int64_t(16) * kFragElems * sizeof(T) + kGateBlockBytes;
-}
 
 // The staged path: bf16 operands, d_k = 128, d_v a multiple of 32 (the factor
 // kernel and the staged scan).  The scan forms P itself, and T's zeros are
@@ -55,17 +51,17 @@ constexpr int kKdaFrags = 64;
 template <typename T> constexpr int64_t kda_entry_bytes() {
   return int64_t(kKdaFrags) * kFragElems * sizeof(T) + 128 * 4;
 }
-// The chained path (launch_chain_fwd, bwd.hip): every other one-pass chunked
-// forward (fp32 inputs, d_k < 128, or d_v not a multiple of 32).  Its entry
-// holds M = (I + A)^-1 and P in fp32 (C x C each, row-major) and a 256-float
-// gate block: the head of a backward entry.
-inline bool chain_path(const Problem &p) { return !p.per_channel && !staged_path(p) && !p.seg_pass; }
+// The chained path (launch_chain_fwd, bwd.hip): every scalar-gate chunked
+// forward off the staged path (fp32 inputs, d_k < 128, or d_v not a multiple
+// of 32), one-pass and segmented.  Its entry holds M = (I + A)^-1 and P in
+// fp32 (C x C each, row-major) and a 256-float gate block: the head of a
+// backward entry.
+inline bool chain_path(const Problem &p) { return !p.per_channel && !staged_path(p); }
 constexpr int64_t chain_entry_bytes(int C) { return (int64_t(2) * C * C + 256) * 4; }
 inline int64_t entry_stride(const Problem &p) {
   if (p.per_channel) return p.dtype == 1 ? kda_entry_bytes<uint16_t>() : kda_entry_bytes<float>();
   if (staged_path(p)) return kStagedEntryBytes;
-  if (chain_path(p)) return chain_entry_bytes(p.chunk);
-  return p.dtype == 1 ? entry_bytes<uint16_t>() : entry_bytes<float>();
+  return chain_entry_bytes(p.chunk);
 }
 
 struct Workspace {
@@ -92,10 +88,13 @@ struct BwdProblem {
 };
 size_t bwd_entry_floats(int chunk, int d_k, int d_v);
 hipError_t launch_chunk_bwd(const BwdProblem &b, hipStream_t st);
-// The chained one-pass forward (chain_path problems): per-chunk factors, then
-// one block per (unit, 32 columns) walking the chunks with the state on fp32
-// MFMA and writing o (and hT).
-hipError_t launch_chain_fwd(const Problem &p, const Workspace &ws, hipStream_t st);
+// The chained forward (chain_path problems): with factors, the per-chunk
+// factors first; then one block per (unit, 16 or 32 columns) walking the
+// chunks with the state in MFMA accumulators and writing o (and hT), or, with
+// mb, the transition pass of the segment-parallel form (each unit's [B | M]
+// into mb, [units, d_k, d_v + d_k]).
+hipError_t launch_chain_fwd(const Problem &p, const Workspace &ws, hipStream_t st, float *mb = nullptr,
+                            bool factors = true);
 hipError_t launch_kda_chunk(const Problem &p, const Workspace &ws, hipStream_t st);
 // Segment-parallel path (seqmap.hip, fold.hip).
 hipError_t launch_segment_map(const Problem &p, int seg_tokens, int n_seg_bound, int32_t *seg_cu,

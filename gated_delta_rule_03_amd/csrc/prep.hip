@@ -19,21 +19,17 @@
 //   O    = diag(gamma) Q S + P U,       P_ti = Gamma_ti q_t^T k_i  (i <= t)
 //   S   <- gamma_C S + K^T diag(2^(g_C - g)) U
 //
-// This kernel computes what does not depend on the incoming state -- T, P and
-// the gate factors gamma_t = 2^g_t and s_t = 2^(g_C - g_t) for one (chunk,
-// value head) -- and writes them to the workspace entry (T and P in MFMA
-// fragment order, then the gate block).
-//
-// MFMA: k k^T and k q^T are dense 64 x 64 x d_k contractions (bf16 MFMA for
-// bf16 inputs, fp32 MFMA for fp32 inputs).  The triangular inverse is fp32:
-// four 16 x 16 diagonal blocks by forward substitution (one lane per column),
-// then block forward substitution for the off-diagonal blocks.
+// The factor kernel below computes, for the staged path (bf16 inputs,
+// d_k = 128, d_v a multiple of 32), what does not depend on the incoming
+// state -- T and the gate factors gamma_t = 2^g_t and s_t = 2^(g_C - g_t) for
+// one (chunk, value head) -- and writes them to the workspace entry (T in MFMA
+// fragment order, then the gate block); the staged scan forms P itself.  Every
+// other shape runs the chained form (bwd.hip), whose factor kernel writes M
+// and P in fp32.
 //
 // Padding: a chunk is padded to 64 token slots.  Padded slots carry beta = 0
-// and the last token's gate; their k and q rows (zero, or a copy of the
-// chunk's last row when staged) only ever meet exact zeros: their rows and
-// columns of A and T vanish with beta, and their rows of P only reach outputs
-// that are never stored.
+// and the last token's gate; their k rows (zero) only ever meet exact zeros:
+// their rows and columns of A and T vanish with beta.
 #include "launch.hpp"
 #include "stage.hpp"
 
@@ -47,160 +43,6 @@ struct PrepArgs {
   int H_qk, H_v, d_k, group;
   SeqGeom geo;
 };
-
-// General path (fp32, or d_k != 128): fragments are read from global memory,
-// A and M = (I + A)^-1 live in LDS.
-template <typename T>
-__global__ __launch_bounds__(256) void prep_kernel(PrepArgs<T> a) {
-  const int c = blockIdx.x;
-  const int h = blockIdx.y;
-  int s, tok0, len;
-  if (!a.geo.locate(c, s, tok0, len)) return;
-  const int hq = h / a.group;
-  const int tid = threadIdx.x, lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-
-  constexpr int kLdsMain = 2 * 64 * 65 * 4;
-  __shared__ __attribute__((aligned(16))) char smem[kLdsMain];
-  __shared__ float sY[3][16][17];
-  __shared__ float sg[64], sb[64];
-  float(*sA)[65] = reinterpret_cast<float(*)[65]>(smem);
-  float(*sM)[65] = reinterpret_cast<float(*)[65]>(smem + 64 * 65 * 4);
-
-  const int64_t stride = int64_t(a.H_qk) * a.d_k;
-  const T *kb = a.k + int64_t(tok0) * stride + int64_t(hq) * a.d_k;
-  const T *qb = a.q + int64_t(tok0) * stride + int64_t(hq) * a.d_k;
-  char *entry = a.entries + (int64_t(c) * a.H_v + h) * entry_bytes<T>();
-  T *fragT = reinterpret_cast<T *>(entry);
-  T *fragP = fragT + 8 * kFragElems;
-  float *gate_out = reinterpret_cast<float *>(fragT + 16 * kFragElems);
-
-  // ---- cumulative gate (wave 0): g_t for slot t, padded slots hold g_last ----
-  if (wave == 0) {
-    const int t = lane;
-    const int64_t idx = int64_t(tok0 + min(t, len - 1)) * a.H_v + h;
-    float x = t < len ? clamped_log2(a.alpha[idx]) : 0.0f;
-#pragma unroll
-    for (int d = 1; d < 64; d <<= 1) {
-      const float y = __shfl_up(x, d);
-      if (lane >= d) x += y;
-    }
-    sg[t] = x;
-    sb[t] = t < len ? a.beta[idx] : 0.0f;
-    const float g_last = __shfl(x, 63);
-    gate_out[t] = exp2f(x);             // gamma_t
-    gate_out[64 + t] = exp2f(g_last - x);  // s_t
-  }
-  lds_barrier();
-
-  auto frag = [&](int src, int r, int kk) -> Frag<T> {
-    return load_row_frag(src == 0 ? kb : qb, stride, 16 * r + (lane & 15), len, 32 * kk, a.d_k,
-                         lane);
-  };
-  const int nkb = (a.d_k + 31) / 32;
-
-  // ---- 20 tiles: 10 of A = K K^T (r >= cc), 10 of P^T = K Q^T (r <= cc) ----
-  // This wave's tiles are wave + 4 n (n = 0..4), kept in registers.
-  f32x4_t acc[5];
-  int tr[5], tc[5];
-#pragma unroll
-  for (int n = 0; n < 5; ++n) {
-    const int tile = wave + 4 * n;
-    const bool isA = tile < 10;
-    int idx = isA ? tile : tile - 10, rr = 0;
-    while (idx > rr) { idx -= rr + 1; ++rr; }
-    tr[n] = isA ? rr : idx;
-    tc[n] = isA ? idx : rr;
-    acc[n] = zero4();
-    for (int kk = 0; kk < nkb; ++kk)
-      acc[n] = mfma(frag(0, tr[n], kk), frag(isA ? 0 : 1, tc[n], kk), acc[n]);
-  }
-
-#pragma unroll
-  for (int n = 0; n < 5; ++n) {
-    const int tile = wave + 4 * n;
-    const int r = tr[n], cc = tc[n];
-    const int col = 16 * cc + (lane & 15);
-    if (tile < 10) {
-      // rows t, column i: A_ti for i < t
-      for (int e = 0; e < 4; ++e) {
-        const int t = 16 * r + 4 * (lane >> 4) + e;
-        const float gam = fast_exp2(sg[t] - sg[col <= t ? col : t]);
-        sA[t][col] = col < t ? sb[t] * gam * acc[n][e] : 0.0f;
-      }
-    } else {
-      // P^T tile (rows i = 16 r + ..., column t): its lane layout is the
-      // A-fragment layout of P (row t, contraction i), so its 4 elements go
-      // straight into half of fragment (t-tile, i-block).
-      T *dst = fragP + (cc * 2 + (r >> 1)) * kFragElems + 8 * lane + 4 * (r & 1);
-      for (int e = 0; e < 4; ++e) {
-        const int i = 16 * r + 4 * (lane >> 4) + e;
-        const int t = col;
-        const float gam = fast_exp2(sg[t] - sg[i <= t ? i : t]);
-        dst[e] = from_f32<T>(i <= t ? gam * acc[n][e] : 0.0f);
-      }
-    }
-  }
-  // zero halves of P fragments whose P^T tile lies below the diagonal (ri > ct)
-  for (int z = wave; z < 6; z += 4) {
-    int idx = z, rr = 1;
-    while (idx >= rr) { idx -= rr; ++rr; }
-    const int ri = rr, ct = idx;
-    T *dst = fragP + (ct * 2 + (ri >> 1)) * kFragElems + 8 * lane + 4 * (ri & 1);
-    for (int e = 0; e < 4; ++e) dst[e] = from_f32<T>(0.0f);
-  }
-  lds_barrier();
-
-  // ---- M = (I + A)^-1: diagonal 16 x 16 blocks, one lane per column ----
-  if (wave == 0) {
-    const int b = lane >> 4, col = lane & 15;
-    float x[16];
-#pragma unroll
-    for (int t = 0; t < 16; ++t) {
-      float v = (t == col) ? 1.0f : 0.0f;
-#pragma unroll
-      for (int i = 0; i < t; ++i) v -= sA[16 * b + t][16 * b + i] * x[i];
-      x[t] = v;
-    }
-#pragma unroll
-    for (int t = 0; t < 16; ++t) sM[16 * b + t][16 * b + col] = x[t];
-  }
-  lds_barrier();
-  // ---- off-diagonal blocks: M_bc = -M_bb sum_{j=c}^{b-1} A_bj M_jc ----
-  {
-    const int t = tid >> 4, col = tid & 15;
-    for (int br = 1; br < 4; ++br) {
-      for (int cb = 0; cb < br; ++cb) {
-        float y = 0.0f;
-        for (int j = cb; j < br; ++j)
-#pragma unroll
-          for (int i = 0; i < 16; ++i)
-            y += sA[16 * br + t][16 * j + i] * sM[16 * j + i][16 * cb + col];
-        sY[cb][t][col] = y;
-      }
-      lds_barrier();
-      for (int cb = 0; cb < br; ++cb) {
-        float m = 0.0f;
-#pragma unroll
-        for (int i = 0; i < 16; ++i) m -= sM[16 * br + t][16 * br + i] * sY[cb][i][col];
-        sM[16 * br + t][16 * cb + col] = m;
-      }
-      lds_barrier();
-    }
-  }
-
-  // ---- T = M diag(beta) as A fragments (row t, contraction i) ----
-  for (int f = wave; f < 8; f += 4) {
-    const int rt = f >> 1, kk = f & 1;
-    const int t = 16 * rt + (lane & 15);
-    Frag<T> fr;
-    for (int j = 0; j < 8; ++j) {
-      const int i = 32 * kk + kappa(lane, j);
-      fr.set(j, (i >> 4) <= (t >> 4) ? sM[t][i] * sb[i] : 0.0f);
-    }
-    store_frag(fragT + f * kFragElems, lane, fr);
-  }
-}
 
 // ---------------------------------------------------------------------------
 // Staged path (bf16, d_k = 128, d_v % 32 = 0): the factor kernel.  One
@@ -481,8 +323,11 @@ __global__ __launch_bounds__(128, 4) void factors_kernel(PrepArgs<bf16_t> a) {
   }
 }
 
-template <typename T>
-static hipError_t launch_prep_t(const Problem &p, const Workspace &ws, hipStream_t st) {
+// The staged path's factor kernel; other shapes run the chained form.
+hipError_t launch_prep(const Problem &p, const Workspace &ws, hipStream_t st) {
+  if (chunk_slots(p) == 0) return hipSuccess;
+  if (!staged_path(p)) return hipErrorInvalidValue;
+  using T = bf16_t;
   PrepArgs<T> a;
   a.q = static_cast<const T *>(p.q);
   a.k = static_cast<const T *>(p.k);
@@ -495,22 +340,12 @@ static hipError_t launch_prep_t(const Problem &p, const Workspace &ws, hipStream
   a.group = p.H_v / p.H_qk;
   a.geo = make_geom(p, &ws);
   const int64_t slots = chunk_slots(p);
-  if constexpr (sizeof(T) == 2) {
-    if (staged_path(p)) {
-      const int64_t blocks = 8 * ((slots + 7) / 8) * p.H_v;  // chunk slots rounded up to the XCD count
-      if (blocks > 0x7fffffff) return hipErrorInvalidConfiguration;
-      hipLaunchKernelGGL(factors_kernel, dim3(unsigned(blocks)), dim3(128), 0, st, a);
-      return hipGetLastError();
-    }
-  }
-  hipLaunchKernelGGL((prep_kernel<T>), dim3(unsigned(slots), unsigned(p.H_v)), dim3(256), 0, st, a);
+  const int64_t blocks = 8 * ((slots + 7) / 8) * p.H_v;  // chunk slots rounded up to the XCD count
+  if (blocks > 0x7fffffff) return hipErrorInvalidConfiguration;
+  hipLaunchKernelGGL(factors_kernel, dim3(unsigned(blocks)), dim3(128), 0, st, a);
   return hipGetLastError();
 }
 
-hipError_t launch_prep(const Problem &p, const Workspace &ws, hipStream_t st) {
-  if (chunk_slots(p) == 0) return hipSuccess;
-  if (p.dtype == 1) return launch_prep_t<bf16_t>(p, ws, st);
-  return launch_prep_t<float>(p, ws, st);
-}
+
 
 }  // namespace gdn

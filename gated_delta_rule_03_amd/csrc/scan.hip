@@ -11,7 +11,9 @@
 //   O = diag(gamma) (Q S) + P U  the chunk's outputs
 //   S <- gamma_C S + K^T (diag(s) U)
 //
-// A wavefront owns 16 columns of the state (a d_k x 16 slice, fp32, in MFMA
+// This scan serves the staged path (bf16 inputs, d_k = 128, d_v a multiple
+// of 32); every other shape runs the chained form (bwd.hip).  A chain
+// wavefront owns 16 columns of the state (a d_k x 16 slice, fp32, in MFMA
 // accumulator registers) for one (sequence, value head) and walks that
 // sequence's chunks in order.  The delta-rule update acts on each value
 // column separately ("Attention as Matrix Algebra", section 7.2: each write
@@ -58,161 +60,6 @@ __device__ __forceinline__ float initial_state(const float *h0, int64_t st_base,
   return h0 ? h0[st_base + int64_t(row) * d_v + col] : 0.0f;
 }
 
-
-// ---------------------------------------------------------------------------
-// General path: any supported d_k / d_v, fp32 or bf16.  One 64-lane block per
-// (unit, 16 columns); operands are read from global memory as needed.
-// ---------------------------------------------------------------------------
-template <typename T>
-__global__ __launch_bounds__(64) void scan_kernel(ScanArgs<T> a) {
-  const int lane = threadIdx.x;
-  int u, cb;
-  decode_block(blockIdx.x, a.n_colblk, u, cb);
-  if (u >= a.n_units) return;
-  const int s = a.geo.ordered(u / a.H_v), h = u % a.H_v, hq = h / a.group;
-  const bool is_m = a.mode == 1 && cb >= a.n_colblk_v;       // a column block of M
-  const int col = 16 * (is_m ? cb - a.n_colblk_v : cb) + (lane & 15);  // this lane's state column
-  const int vcol = is_m ? (lane & 15) : col;                  // v column read (M blocks: v = 0)
-  const int nkt = a.d_k >> 4;             // 16-row tiles of the state
-  const int nkb = (a.d_k + 31) >> 5;      // 32-deep contraction blocks over d_k
-
-  // S[rt] holds state rows 16 rt + 4 (lane >> 4) + e of column col
-  f32x4_t S[8];
-  const int64_t st_base = (int64_t(s) * a.H_v + h) * a.d_k * a.d_v;
-#pragma unroll
-  for (int rt = 0; rt < 8; ++rt) {
-    S[rt] = zero4();
-    if (rt < nkt)
-      for (int e = 0; e < 4; ++e)
-        S[rt][e] = initial_state(a.h0, st_base, 16 * rt + 4 * (lane >> 4) + e, col, a.d_v, a.mode, is_m);
-  }
-
-  int start, end;
-  a.geo.seq_bounds(s, start, end);
-  const int n_chunks = (end - start + a.geo.chunk - 1) / a.geo.chunk;
-  const int c_first = a.geo.first_chunk(s);
-  const int64_t qk_stride = int64_t(a.H_qk) * a.d_k;
-  const int64_t v_stride = int64_t(a.H_v) * a.d_v;
-
-  for (int cc = 0; cc < n_chunks; ++cc) {
-    const int c = c_first + cc;
-    if (c >= a.geo.n_slots) break;
-    const int tok0 = start + cc * a.geo.chunk;
-    const int len = min(a.geo.chunk, end - tok0);
-    const T *kb = a.k + int64_t(tok0) * qk_stride + int64_t(hq) * a.d_k;
-    const T *qb = a.q + int64_t(tok0) * qk_stride + int64_t(hq) * a.d_k;
-    const T *vb = a.v + int64_t(tok0) * v_stride + int64_t(h) * a.d_v + vcol;
-    const T *entry = reinterpret_cast<const T *>(a.entries + (int64_t(c) * a.H_v + h) *
-                                                                 entry_bytes<T>());
-    const float *gent = reinterpret_cast<const float *>(entry + 16 * kFragElems);
-
-    const float gam_l = gent[lane], sc_l = gent[64 + lane];  // this lane's slot
-    const float gamma_C = __shfl(gam_l, 63);
-    float gam[4][4], sc[4][4];
-#pragma unroll
-    for (int rt = 0; rt < 4; ++rt)
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        gam[rt][e] = __shfl(gam_l, 16 * rt + 4 * (lane >> 4) + e);
-        sc[rt][e] = __shfl(sc_l, 16 * rt + 4 * (lane >> 4) + e);
-      }
-
-    Frag<T> Sf[4];
-#pragma unroll
-    for (int kk = 0; kk < 4; ++kk) Sf[kk] = frag_from_acc<T>(S[2 * kk], S[2 * kk + 1]);
-
-    // Y = K S, OQ = Q S
-    f32x4_t Y[4], OQ[4];
-#pragma unroll
-    for (int rt = 0; rt < 4; ++rt) {
-      Y[rt] = zero4();
-      OQ[rt] = zero4();
-#pragma unroll
-      for (int kk = 0; kk < 4; ++kk) {
-        if (kk < nkb) {
-          const int row = 16 * rt + (lane & 15);
-          Y[rt] = mfma(load_row_frag(kb, qk_stride, row, len, 32 * kk, a.d_k, lane), Sf[kk], Y[rt]);
-          OQ[rt] = mfma(load_row_frag(qb, qk_stride, row, len, 32 * kk, a.d_k, lane), Sf[kk],
-                        OQ[rt]);
-        }
-      }
-    }
-    // X = V - gamma Y
-    f32x4_t X[4];
-#pragma unroll
-    for (int rt = 0; rt < 4; ++rt)
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int t = 16 * rt + 4 * (lane >> 4) + e;
-        const float vv = t < len && !is_m ? to_f32(vb[int64_t(t) * v_stride]) : 0.0f;
-        X[rt][e] = vv - gam[rt][e] * Y[rt][e];
-      }
-    // U = T X
-    Frag<T> Xf[2] = {frag_from_acc<T>(X[0], X[1]), frag_from_acc<T>(X[2], X[3])};
-    f32x4_t Ua[4];
-#pragma unroll
-    for (int rt = 0; rt < 4; ++rt) {
-      Ua[rt] = zero4();
-#pragma unroll
-      for (int kk = 0; kk < 2; ++kk)
-        Ua[rt] = mfma(load_frag(entry + (rt * 2 + kk) * kFragElems, lane), Xf[kk], Ua[rt]);
-    }
-    Frag<T> Uf[2] = {frag_from_acc<T>(Ua[0], Ua[1]), frag_from_acc<T>(Ua[2], Ua[3])};
-    // O = gamma (Q S) + P U
-#pragma unroll
-    for (int rt = 0; rt < 4; ++rt) {
-      if (a.mode == 1) break;
-      f32x4_t acc;
-      for (int e = 0; e < 4; ++e) acc[e] = gam[rt][e] * OQ[rt][e];
-#pragma unroll
-      for (int kk = 0; kk < 2; ++kk)
-        acc = mfma(load_frag(entry + (8 + rt * 2 + kk) * kFragElems, lane), Uf[kk], acc);
-      for (int e = 0; e < 4; ++e) {
-        const int t = 16 * rt + 4 * (lane >> 4) + e;
-        if (t < len)
-          a.o[int64_t(tok0 + t) * v_stride + int64_t(h) * a.d_v + col] = from_f32<T>(acc[e]);
-      }
-    }
-    // S <- gamma_C S + K^T (s U); K^T fragments gathered from k
-#pragma unroll
-    for (int rt = 0; rt < 4; ++rt)
-      for (int e = 0; e < 4; ++e) Ua[rt][e] *= sc[rt][e];
-    Frag<T> Usf[2] = {frag_from_acc<T>(Ua[0], Ua[1]), frag_from_acc<T>(Ua[2], Ua[3])};
-#pragma unroll
-    for (int rm = 0; rm < 8; ++rm) {
-      if (rm < nkt) {
-        const int m = 16 * rm + (lane & 15);
-        f32x4_t acc;
-        for (int e = 0; e < 4; ++e) acc[e] = gamma_C * S[rm][e];
-#pragma unroll
-        for (int kk = 0; kk < 2; ++kk) {
-          Frag<T> kt;
-          for (int j = 0; j < 8; ++j) {
-            const int i = 32 * kk + kappa(lane, j);
-            kt.set(j, i < len ? to_f32(kb[int64_t(i) * qk_stride + m]) : 0.0f);
-          }
-          acc = mfma(kt, Usf[kk], acc);
-        }
-        S[rm] = acc;
-      }
-    }
-  }
-
-  if (a.mode == 1) {
-    const int ld = a.d_v + a.d_k;
-    float *dst = a.mb + (int64_t(s) * a.H_v + h) * a.d_k * ld + (is_m ? a.d_v : 0) + col;
-#pragma unroll
-    for (int rt = 0; rt < 8; ++rt)
-      if (rt < nkt)
-        for (int e = 0; e < 4; ++e) dst[int64_t(16 * rt + 4 * (lane >> 4) + e) * ld] = S[rt][e];
-  } else if (a.hT) {
-#pragma unroll
-    for (int rt = 0; rt < 8; ++rt)
-      if (rt < nkt)
-        for (int e = 0; e < 4; ++e)
-          a.hT[st_base + int64_t(16 * rt + 4 * (lane >> 4) + e) * a.d_v + col] = S[rt][e];
-  }
-}
 
 // ---------------------------------------------------------------------------
 // Pipelined path: bf16, d_k = 128, d_v a multiple of 32.
@@ -834,26 +681,20 @@ static ScanArgs<T> scan_args(const Problem &p, const Workspace &ws, int colblk_w
 }
 
 hipError_t launch_scan(const Problem &p, const Workspace &ws, hipStream_t st, float *mb) {
-  const bool staged = staged_path(p);
+  if (!staged_path(p)) return hipErrorInvalidValue;  // other shapes run the chained form
   const int64_t units8 = (int64_t(p.n_seqs) * p.H_v + 7) / 8 * 8;
   const int cols = p.d_v + (mb ? p.d_k : 0);  // state columns per unit (transition mode: B and M)
-  const bool narrow = staged && units8 * (cols / 32) < kNarrowBelowBlocks;
-  const int width = staged && !narrow ? 32 : 16;
+  const bool narrow = units8 * (cols / 32) < kNarrowBelowBlocks;
+  const int width = narrow ? 16 : 32;
   const int64_t blocks = units8 * (cols / width);
   if (blocks == 0) return hipSuccess;
   if (blocks > 0x7fffffff) return hipErrorInvalidConfiguration;
   const dim3 grid = dim3(static_cast<unsigned>(blocks));
-  if (staged) {
-    const ScanArgs<bf16_t> a = scan_args<bf16_t>(p, ws, width, mb);
-    if (narrow && mb) hipLaunchKernelGGL((scan_kernel_staged<1, 1>), grid, dim3(64 * 7), 0, st, a);
-    else if (narrow) hipLaunchKernelGGL((scan_kernel_staged<1, 0>), grid, dim3(64 * 7), 0, st, a);
-    else if (mb) hipLaunchKernelGGL((scan_kernel_staged<2, 1>), grid, dim3(64 * 8), 0, st, a);
-    else hipLaunchKernelGGL((scan_kernel_staged<2, 0>), grid, dim3(64 * 8), 0, st, a);
-  } else if (p.dtype == 1) {
-    hipLaunchKernelGGL(scan_kernel<bf16_t>, grid, dim3(64), 0, st, scan_args<bf16_t>(p, ws, width, mb));
-  } else {
-    hipLaunchKernelGGL(scan_kernel<float>, grid, dim3(64), 0, st, scan_args<float>(p, ws, width, mb));
-  }
+  const ScanArgs<bf16_t> a = scan_args<bf16_t>(p, ws, width, mb);
+  if (narrow && mb) hipLaunchKernelGGL((scan_kernel_staged<1, 1>), grid, dim3(64 * 7), 0, st, a);
+  else if (narrow) hipLaunchKernelGGL((scan_kernel_staged<1, 0>), grid, dim3(64 * 7), 0, st, a);
+  else if (mb) hipLaunchKernelGGL((scan_kernel_staged<2, 1>), grid, dim3(64 * 8), 0, st, a);
+  else hipLaunchKernelGGL((scan_kernel_staged<2, 0>), grid, dim3(64 * 8), 0, st, a);
   return hipGetLastError();
 }
 
