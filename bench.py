@@ -216,17 +216,19 @@ def device_inputs(torch, dev, spec, n_tokens, B, seed):
     """Inputs with ``spec``'s shapes and distributions, drawn on the device.
 
     q, k ~ N(0, 1) scaled to unit length per token and head (q then by
-    1/sqrt(d_k)), v ~ N(0, 1), rounded to bf16; log alpha = -softplus(N(0, 1))
+    1/sqrt(d_k)), v ~ N(0, 1), rounded to bf16 (kept in fp32 for an fp32
+    spec); log alpha = -softplus(N(0, 1))
     * A_h * s with A_h = exp(U(-4, 0)) per value head, beta = sigmoid(N(0, 1)).
     """
     g = torch.Generator(device=dev)
     g.manual_seed(seed)
     T = n_tokens // B
     q = torch.randn((B, T, spec.H_qk, spec.d_k), generator=g, device=dev)
-    q = (torch.nn.functional.normalize(q, dim=-1) / spec.d_k ** 0.5).bfloat16()
+    dt = torch.float32 if spec.dtype == "f32" else torch.bfloat16
+    q = (torch.nn.functional.normalize(q, dim=-1) / spec.d_k ** 0.5).to(dt)
     k = torch.nn.functional.normalize(torch.randn((B, T, spec.H_qk, spec.d_k), generator=g, device=dev),
-                                      dim=-1).bfloat16()
-    v = torch.randn((B, T, spec.H_v, spec.d_v), generator=g, device=dev).bfloat16()
+                                      dim=-1).to(dt)
+    v = torch.randn((B, T, spec.H_v, spec.d_v), generator=g, device=dev).to(dt)
     A_h = torch.exp(torch.rand((spec.H_v,), generator=g, device=dev) * 4.0 - 4.0)
     z_a = torch.randn((B, T, spec.H_v), generator=g, device=dev)
     alpha = torch.exp(-torch.nn.functional.softplus(z_a) * A_h * spec.log_alpha_scale)
@@ -254,10 +256,13 @@ def extra_workloads(args, gi, gdn, torch, dev, stream, evict):
     """Chunked-forward throughput on the long-context and variable-length
     workloads.  The long-context workload is also timed through the
     segment-parallel form, as given (16 heads) and at two heads (one GPU's
-    share of an eight-way head split), next to the one-pass scan."""
+    share of an eight-way head split), next to the one-pass scan; at two
+    heads also with fp32 inputs (the chained kernels)."""
     out = {}
     cases = (("long_context", gi.config(4), None), ("long_context_2heads",
-             gi.config(4, H_qk=2, H_v=2, name="long-2heads"), None), ("varlen", gi.config(5), None))
+             gi.config(4, H_qk=2, H_v=2, name="long-2heads"), None),
+             ("long_context_2heads_f32", gi.config(4, H_qk=2, H_v=2, dtype="f32", name="long-2heads-f32"), None),
+             ("varlen", gi.config(5), None))
     for key, spec, _ in cases:
         if spec.packed_seqs:
             lengths = gi.packed_lengths(spec)
@@ -271,7 +276,9 @@ def extra_workloads(args, gi, gdn, torch, dev, stream, evict):
         o = torch.empty_like(v)
         hT = torch.empty((n_seqs, spec.H_v, spec.d_k, spec.d_v), dtype=torch.float32, device=dev)
         n_arg = n_seqs if cu is not None else 0
-        dims = (B, n_tokens // B, spec.H_qk, spec.H_v, spec.d_k, spec.d_v, gdn.GDN_BF16, spec.chunk, n_arg)
+        f32 = spec.dtype == "f32"
+        dims = (B, n_tokens // B, spec.H_qk, spec.H_v, spec.d_k, spec.d_v, gdn.GDN_F32 if f32 else gdn.GDN_BF16,
+                spec.chunk, n_arg)
         plan = gdn.chunk_fwd_plan_segments(*dims)
         # the one-pass scan, the planned form, and (long context) fixed segment lengths
         forms = [0] if plan == 0 else [0, plan]
@@ -291,12 +298,14 @@ def extra_workloads(args, gi, gdn, torch, dev, stream, evict):
         t = times[plan]
         units = n_seqs * spec.H_v
         flops = n_tokens * spec.H_v * PREFILL_FLOPS_PER_TOKEN_UNIT
-        byts = n_tokens * (2 * spec.H_qk * spec.d_k * 2 + 2 * spec.H_v * spec.d_v * 2 + 8 * spec.H_v) + \
+        esz = 4 if f32 else 2
+        byts = n_tokens * (2 * spec.H_qk * spec.d_k * esz + 2 * spec.H_v * spec.d_v * esz + 8 * spec.H_v) + \
             units * spec.d_k * spec.d_v * 4
         out[key] = {"workload": f"{spec.name}: B={B} tokens={n_tokens} sequences={n_seqs} H_qk={spec.H_qk} "
-                                f"H_v={spec.H_v} d={spec.d_k} bf16 chunk {spec.chunk}",
+                                f"H_v={spec.H_v} d={spec.d_k} {'fp32' if f32 else 'bf16'} chunk {spec.chunk}",
                     "tokens_per_s": n_tokens / t, "us_per_call": t * 1e6,
-                    "hbm_frac": byts / t / HBM_PEAK, "mfma_frac": flops / t / MFMA_BF16_PEAK,
+                    "hbm_frac": byts / t / HBM_PEAK,
+                    ("mfma_f32_frac" if f32 else "mfma_frac"): flops / t / (MFMA_F32_PEAK if f32 else MFMA_BF16_PEAK),
                     "segment_chunks": plan,
                     "inputs": "drawn on the device with the generator's shapes and distributions"}
         if len(forms) > 1:

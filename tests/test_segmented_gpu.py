@@ -6,7 +6,7 @@ forward: each sequence is cut into segments whose affine state maps are
 folded in order, then every segment's outputs are computed from its true
 incoming state.  Cases: several segment lengths (one chunk, a length that
 leaves a short last segment, longer than the sequence), fp32 and bf16, the
-staged and the general kernels, packed batches with empty and short
+staged and the chained kernels, packed batches with empty and short
 sequences and grouped heads, h0, and the long-context workload at full size
 (as given, and at the two-head share of one GPU of an eight-way head split).
 """
@@ -64,13 +64,17 @@ def small(dtype, B, T, H_qk, H_v, d_k, d_v, chunk, seed, lengths=None, log_alpha
                                lengths=lengths, log_alpha_scale=log_alpha_scale, seed=seed))
 
 
-# bf16 with d_k = 128 (staged kernels) and the general kernels (fp32, small d)
+# bf16 with d_k = 128 (staged kernels) and the chained kernels (fp32; bf16
+# with d_k < 128 or d_v = 16), including d_k not a multiple of 32 (16-column
+# transition blocks)
 UNIFORM = [
     # dtype, B, T, H_qk, H_v, d_k, d_v, chunk, segment lengths (chunks)
     ("bf16", 2, 1000, 2, 2, 128, 128, 64, (1, 3, 4, 40)),
     ("bf16", 1, 700, 1, 2, 128, 64, 32, (2, 5)),
     ("f32", 1, 300, 1, 1, 32, 64, 32, (1, 2, 7)),
     ("f32", 2, 150, 2, 2, 16, 16, 16, (3,)),
+    ("bf16", 1, 900, 2, 2, 64, 64, 64, (2, 5)),
+    ("bf16", 2, 400, 1, 2, 32, 16, 32, (1, 4)),
 ]
 
 
@@ -142,4 +146,14 @@ def test_config4_two_heads_auto(gdn):
     plan = gdn.chunk_fwd_plan_segments(1, 65536, 2, 2, 128, 128, gdn.GDN_BF16, 64, 0)
     log(f"[plan] long context, 2 heads: {plan} chunks per segment")
     assert plan > 0
+    check_seg(gdn, w, None)
+
+
+def test_long_context_chained_f32_two_heads_auto(gdn):
+    """fp32 inputs run the chained kernels; at the two-head share of the
+    long-context workload gdn_chunk_fwd cuts them into segments too."""
+    w = gi.generate(gi.config(4, H_qk=2, H_v=2, dtype="f32", name="long-2heads-f32"))
+    plan = gdn.chunk_fwd_plan_segments(1, 65536, 2, 2, 128, 128, gdn.GDN_F32, 64, 0)
+    log(f"[plan] long context, fp32, 2 heads: {plan} chunks per segment")
+    assert 0 < plan < 1024
     check_seg(gdn, w, None)
