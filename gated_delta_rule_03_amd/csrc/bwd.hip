@@ -1056,7 +1056,9 @@ constexpr int kGradWaves = kGradThreads / 64;
 
 template <typename T, int C, int DVS>
 __global__ __launch_bounds__(kGradThreads) void bwd_grad_kernel(BwdArgs<T> a) {
-  constexpr int NRT = C / 16, LD = C + 4, LDV = DVS + 4, NL = NRT * (NRT + 1) / 2;
+  // slab rows 32 bytes past a multiple of 128 (LDV): half the LDS bank
+  // conflicts of 16 bytes past, measured
+  constexpr int NRT = C / 16, LD = C + 4, LDV = DVS + 8, NL = NRT * (NRT + 1) / 2;
   constexpr int kSlabFloats = 3 * C * LDV, kPh2Floats = 3 * C * LD;
   constexpr int kBig = kSlabFloats > kPh2Floats ? kSlabFloats : kPh2Floats;
   constexpr int NK = DVS / 16;                                        // 16-deep steps per slab
