@@ -182,8 +182,10 @@ __global__ __launch_bounds__(256) void bwd_factor_kernel(BwdArgs<T> a) {
   const int hq = h / a.group, DK = a.d_k;
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, r = lane & 15, g = lane >> 4;
   // LDS: the chunk's K and Q rows.  A takes Q's space once P is formed, and
-  // M takes K's once A is (fp32 inputs: two blocks per CU, bf16: four)
-  constexpr int LDK = 128 + 16 / sizeof(T);
+  // M takes K's once A is (fp32 inputs: two blocks per CU, bf16: four).
+  // Rows 32 bytes past a multiple of 128: LDS bank conflicts 2-3 % of
+  // LDS-active cycles instead of 26-32 % at 16 bytes past (measured).
+  constexpr int LDK = 128 + 32 / sizeof(T);
   constexpr int kTileBytes = C * LDK * sizeof(T);
   static_assert(kTileBytes >= C * LD * 4, "A and M each fit in a row tile's space");
   __shared__ __attribute__((aligned(16))) char sBuf[2 * kTileBytes];
