@@ -165,7 +165,7 @@ def test_block_prologue_many_short_sequences(gdn):
 
 def test_whole_block_unequal_head_dims(gdn):
     """Prologue (two launches: q/k at d_k = 64, v at d_v = 128) -> chunked
-    recurrence on the general path -> epilogue, packed, float32, against the
+    recurrence on the chained path -> epilogue, packed, float32, against the
     float64 oracle of the same composition."""
     import torch
     x = gi.block_inputs(1, 0, 2, 4, 64, 128, "f32", seed=380, lengths=(90, 1, 0, 130))

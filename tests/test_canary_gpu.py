@@ -1,7 +1,7 @@
 """Guard bands: every output buffer (o, the final state, the workspace, the
 decode state) sits inside a larger allocation whose bytes before and after
 hold a sentinel pattern; after each call the bands must be bitwise
-untouched.  Cases: the staged and general chunk kernels on uniform batches
+untouched.  Cases: the staged and chained chunk kernels on uniform batches
 with a partial last chunk, a packed batch with empty and one-token sequences
 and grouped heads, the segment-parallel form, the per-channel-gate chunked
 and token-by-token forwards, the decode step, and the backward pass (every
@@ -93,8 +93,8 @@ CASES = [
     ("staged uniform, partial chunk", ("bf16", 2, 300, 2, 2, 128, 128, 64, 701, None)),
     ("staged 16-column blocks", ("bf16", 1, 100, 1, 1, 128, 64, 64, 702, None)),
     ("staged packed, grouped heads", ("bf16", 1, 0, 2, 4, 128, 128, 64, 703, (1, 64, 65, 0, 130))),
-    ("general fp32, chunk 32", ("f32", 2, 77, 1, 2, 32, 64, 32, 704, None)),
-    ("general bf16 packed", ("bf16", 1, 0, 1, 2, 64, 32, 16, 705, (0, 17, 3, 40))),
+    ("chained fp32, chunk 32", ("f32", 2, 77, 1, 2, 32, 64, 32, 704, None)),
+    ("chained bf16 packed", ("bf16", 1, 0, 1, 2, 64, 32, 16, 705, (0, 17, 3, 40))),
 ]
 
 
