@@ -37,7 +37,7 @@
 //   1. bwd_factor_kernel, one block per (chunk, value head): gates, M by a
 //      blocked triangular inverse, P and Gamma . K K^T, into the chunk's entry.
 //   2. bwd_chain_kernel: per (unit, column block of d_v) one block walks the
-//      chunks forward keeping S (writing each chunk's start state, X and U)
+//      chunks forward keeping S (writing each chunk's start state and U)
 //      and another walks them backward keeping dS (writing each chunk's end
 //      gradient, dY and dv).  The state sits in MFMA accumulators, and the
 //      next chunk's operands are loaded while the current one is computed.
@@ -61,7 +61,7 @@ namespace {
 
 // Floats of one entry (one chunk of one value head) in the workspace.
 struct BwdEntry {
-  int64_t M, P, G, gate, S, dS, X, U, dY, total;
+  int64_t M, P, G, gate, S, dS, U, dY, total;
   __host__ __device__ BwdEntry(int C, int DK, int DV) {
     int64_t o = 0;
     M = o;    o += int64_t(C) * C;    // (I + A)^-1, row-major C x C
@@ -70,8 +70,7 @@ struct BwdEntry {
     G = o;    o += int64_t(C) * C;    // strict_lower(Gamma . K K^T); the forward's entries end here
     S = o;    o += int64_t(DK) * DV;  // state entering the chunk
     dS = o;   o += int64_t(DK) * DV;  // gradient reaching the chunk's end state
-    X = o;    o += int64_t(C) * DV;   // V - diag(gamma) K S
-    U = o;    o += int64_t(C) * DV;   // T X
+    U = o;    o += int64_t(C) * DV;   // T X, X = V - diag(gamma) K S
     dY = o;   o += int64_t(C) * DV;   // M^T dU
     total = o;
   }
@@ -628,12 +627,7 @@ __device__ void fwd_chain(const BwdArgs<T> &a, int u, int cb, char *smem) {
         if (m < nmine) {
           const int col = 16 * ((w + NW * m) / NRT) + r;
           const f32x4_t x = vcur[m] - gam * acc[m];
-          if constexpr (OUT) {
-            oacc[m] = gam * qacc[m];
-          } else if constexpr (!TRANS) {
-#pragma unroll
-            for (int q = 0; q < 4; ++q) ent[L.X + (16 * rt + 4 * g) * DV + c0 + col + q * DV] = x[q];
-          }
+          if constexpr (OUT) oacc[m] = gam * qacc[m];
           *reinterpret_cast<f32x4_t *>(sYt + col * LDC + 16 * rt + 4 * g) = be * x;
         }
       }
@@ -1068,7 +1062,7 @@ __global__ __launch_bounds__(kGradThreads) void bwd_grad_kernel(BwdArgs<T> a) {
   constexpr int NPC = (C * WPR + kGradThreads - 1) / kGradThreads;    // pieces per thread
   constexpr bool SPLG = sizeof(T) == 2;  // bf16 inputs: products with dO, k or q on the bf16 MFMA
   __shared__ __attribute__((aligned(16))) float big[kBig];
-  __shared__ float sPartG[64 * 8], sPartS[64 * 8];
+  __shared__ float sPartG[64 * 8], sPartS[64 * 8], sPartK[64 * 8];
   __shared__ float sR1[64], sRowE[64], sRowF[64], sColE[64], sSd[kGradWaves];
   __shared__ float sGam[64], sSc[64], sG2[64], sBe[64];
   // the chunk's K and Q rows (operands of the products over the chunk in
@@ -1131,7 +1125,8 @@ __global__ __launch_bounds__(kGradThreads) void bwd_grad_kernel(BwdArgs<T> a) {
       yS[kk] = has_rows ? row4(Sg + dv0 + 16 * kk) : zero4();
       ydS[kk] = has_rows ? row4(dSg + dv0 + 16 * kk) : zero4();
     }
-    // stage dO, dY, U; sum dY . X on the way
+    // stage dO, dY, U; sum dY . V on the way (the dY . X row sums of dbeta
+    // are dY . V - gamma K . (dY S^T), and dY S^T is formed here anyway)
 #pragma unroll
     for (int m = 0; m < NPC; ++m) {
       const int p = tid + kGradThreads * m;
@@ -1142,7 +1137,8 @@ __global__ __launch_bounds__(kGradThreads) void bwd_grad_kernel(BwdArgs<T> a) {
         const f32x4_t o = t < n ? od : zero4();
         const f32x4_t y = row4(ent + L.dY + int64_t(t) * DV + dv0 + c);
         const f32x4_t uu = row4(ent + L.U + int64_t(t) * DV + dv0 + c);
-        const f32x4_t x = row4(ent + L.X + int64_t(t) * DV + dv0 + c);
+        const f32x4_t vx = row4(a.v + int64_t(tok0 + min(t, n - 1)) * vrow + int64_t(h) * DV + dv0 + c);
+        const f32x4_t x = t < n ? vx : zero4();
         *reinterpret_cast<f32x4_t *>(sdO + t * LDV + c) = o;
         *reinterpret_cast<f32x4_t *>(sdY + t * LDV + c) = y;
         *reinterpret_cast<f32x4_t *>(sU + t * LDV + c) = uu;
@@ -1190,7 +1186,7 @@ __global__ __launch_bounds__(kGradThreads) void bwd_grad_kernel(BwdArgs<T> a) {
     }
     __syncthreads();
   }
-  // row sums of dY . X: the first thread of each row's group holds them
+  // row sums of dY . V: the first thread of each row's group holds them
 #pragma unroll
   for (int m = 0; m < NPC; ++m) {
     const int p = tid + kGradThreads * m;
@@ -1293,9 +1289,11 @@ __global__ __launch_bounds__(kGradThreads) void bwd_grad_kernel(BwdArgs<T> a) {
         const float dkv = ak[q] - sGam[t] * sBe[t] * W2[m][q] + sSc[t] * W3[m][q];
         const float pg = group_sum(qfi[q] * W1[m][q] - sBe[t] * kfi[q] * W2[m][q], 16);
         const float ps = group_sum(kfi[q] * W3[m][q], 16);
+        const float pk = group_sum(kfi[q] * W2[m][q], 16);
         if (r == 0) {
           sPartG[t * 8 + ct] = pg;
           sPartS[t * 8 + ct] = ps;
+          sPartK[t * 8 + ct] = pk;
         }
         if (t < n) {
           const int64_t o = (int64_t(tok0 + t) * a.H_v + h) * DK + col;
@@ -1311,14 +1309,15 @@ __global__ __launch_bounds__(kGradThreads) void bwd_grad_kernel(BwdArgs<T> a) {
     const int t = lane;
     float dg = 0.0f, sds = 0.0f;
     if (t < n) {
-      float pg = 0.0f, ps = 0.0f;
+      float pg = 0.0f, ps = 0.0f, pk = 0.0f;
       for (int c = 0; c < NKT; ++c) {
         pg += sPartG[t * 8 + c];
         ps += sPartS[t * 8 + c];
+        pk += sPartK[t * 8 + c];
       }
       sds = sSc[t] * ps;
       dg = sGam[t] * pg + sRowE[t] - sColE[t] - sds;
-      a.dbeta[int64_t(tok0 + t) * a.H_v + h] = sR1[t] + sRowF[t];
+      a.dbeta[int64_t(tok0 + t) * a.H_v + h] = (sR1[t] - sGam[t] * pk) + sRowF[t];
     }
     const float tot_sds = group_sum(sds, 64);
     float sdsum = 0.0f;

@@ -230,8 +230,8 @@ int32_t gdn_chunk_fwd_noalloc(int32_t B, int32_t T, int32_t H_qk, int32_t H_v, i
  *   dbeta      [B, T, H_v].
  *   dh0        [N, H_v, d_k, d_v], or NULL (not written).
  * gdn_chunk_bwd_workspace_bytes gives the workspace bytes (0 = unsupported
- * arguments): per (chunk slot, value head) 3 C^2 + 256 + 2 d_k d_v + 3 C d_v
- * floats of intermediates (1.09 GiB for B=4, T=4096, H=16, d=128, C=64),
+ * arguments): per (chunk slot, value head) 3 C^2 + 256 + 2 d_k d_v + 2 C d_v
+ * floats of intermediates (0.94 GiB for B=4, T=4096, H=16, d=128, C=64),
  * plus the per-value-head dq and dk when H_v > H_qk.  The caller owns the
  * workspace; it must be 256-byte aligned (else GDN_ERROR_WORKSPACE), and
  * nothing in it is needed after the call.

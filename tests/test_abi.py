@@ -257,9 +257,9 @@ def test_backward_workspace_and_argument_errors(lib):
     bf, f32 = gdn.GDN_BF16, gdn.GDN_F32
     # one fp32 entry per (chunk slot, value head): M, P and Gamma . K K^T
     # (C x C each), 256 gate values, the chunk's start state and end gradient
-    # (d_k x d_v each), X, U and dY (C x d_v each)
+    # (d_k x d_v each), U and dY (C x d_v each)
     def entry(C, dk, dv):
-        return 4 * (3 * C * C + 256 + 2 * dk * dv + 3 * C * dv)
+        return 4 * (3 * C * C + 256 + 2 * dk * dv + 2 * C * dv)
     w = gdn.chunk_bwd_workspace_bytes(4, 4096, 16, 16, 128, 128, bf, 64, 0)
     ents = 4 * 64 * 16 * entry(64, 128, 128)        # no per-value-head parts: one value head per qk head
     assert ents <= w < ents + 4096
